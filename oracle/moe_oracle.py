@@ -1,0 +1,514 @@
+"""Plain fp64 CPU restatement of the routed-MoE expert path — test infrastructure only.
+
+Sources (each function cites the page and the item on it that it follows):
+
+* ferrum-kernels ``src/backend/cuda/moe.rs`` (docs.rs) — ``route_topk_softmax``,
+  ``moe_build_pairs_by_token``, ``moe_align_block_size`` /
+  ``moe_align_block_size_pair_ids``, ``moe_combine``, ``weighted_sum_batched``.
+* ferrum-kernels ``src/backend/cuda/triton_fused_moe.rs`` (docs.rs) — module doc
+  (one launch over all (token, expert) pairs, gather through sorted ids, masked
+  sentinels), ``TritonStackedGptqWeight`` (stacked raw GPTQ layout),
+  ``launch_fused_moe_w4a16_triton`` (sentinel = number of valid rows).
+* metrale ``gpu_runtime/cutlass/grouped.rs`` — ``ensure_group_arrays`` and its
+  tests; ``nvfp4_grouped_gate_up_fused`` (group row i reads token
+  ``sorted_token_ids[i]``); ``nvfp4_grouped_down`` (A already in expert order).
+* atlas ``spark_model/layers/ops/moe_lora_grouped.rs`` — module doc (fold math:
+  shrink -> bf16 xa, expand -> bf16 delta, base += scale * fp32(delta)),
+  ``MoeExpertRoute``, ``pack_expert_tables``, ``moe_lora_grouped_down``
+  (windows, local-row scratch, ``moe_row_adapter``), ``grouped_down_wc``,
+  ``grouped_down_windows``, ``MLG_M_TILE``, ``moe_lora_gather_bgmv`` (the
+  router weight multiplies base + delta, i.e. fold before combine).
+
+Arithmetic is fp64 on values widened exactly from their storage types (bf16,
+fp16, fp32, int4).  Where the pages fix a precision the oracle follows it: the
+router outputs fp32 weights, and the LoRA fold rounds its shrink and its expand
+results to bf16.  Readings taken where the pages are silent are listed with
+each function.  No blocking, fusion or reordering beyond the definitions: the
+grouped GEMMs are one library matmul per expert over that expert's rows.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "f16_bits_to_f64", "round_bf16", "round_f32", "silu",
+    "route", "max_padded", "align", "check_group_arrays",
+    "gptq_unpack_q", "gptq_unpack_z", "gptq_dequant_expert",
+    "out_dim", "expert_matrix", "grouped_gate_up", "grouped_down",
+    "pack_expert_tables", "lora_windows", "lora_window_tiles", "lora_fold",
+    "combine", "moe_layer", "moe_tokens",
+]
+
+
+# ----------------------------------------------------------------------------- number formats
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> exact fp64 values (bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns -> exact fp64 values."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def round_bf16(v) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value, ties to even; returned as fp64.
+
+    bf16 keeps 8 significant bits and fp32's exponent range, so a value
+    m * 2**e (0.5 <= |m| < 1) is rounded to a multiple of 2**(e-8), with the
+    subnormal quantum 2**-133 as the floor; results of magnitude >= 2**128
+    overflow to infinity.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(v, -q)), q)
+    big = np.abs(r) >= 2.0 ** 128
+    if np.any(big):
+        r = np.where(big, np.copysign(np.inf, v), r)
+    return r
+
+
+def round_f32(v) -> np.ndarray:
+    """Round fp64 values to the nearest fp32 value (ties to even)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
+    return g / (1.0 + np.exp(-g))
+
+
+# ----------------------------------------------------------------------------- A1 route
+def route(logits: np.ndarray, top_k: int, renormalize: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k softmax router: ferrum ``cuda/moe.rs``, ``route_topk_softmax``.
+
+    Per row t of the fp32 ``logits [T, E]``: softmax over all E experts, keep
+    the k most probable, and with ``norm_topk_prob`` divide the k kept
+    probabilities by their sum.  Outputs are i32 ids and f32 weights ``[T, k]``
+    (the types ``try_gpu_route_topk_into_host`` reads back).
+
+    Readings (the page gives no kernel body):
+      * selection order: descending logit, ties -> lower expert index (softmax
+        is monotone, so this is the order of the probabilities; selection is a
+        comparison of the fp32 logits, exact on every implementation);
+      * probabilities: p_i = exp(l_i - max l) / sum_j exp(l_j - max l), in fp64;
+      * renormalised weight w_j = p_{id_j} / sum_{j'} p_{id_j'} (sum in slot
+        order), then rounded once to fp32.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    ids = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float32)
+    idx = np.arange(E)
+    for t in range(T):
+        l = logits[t].astype(np.float64)
+        order = np.lexsort((idx, -l))          # primary: -l ascending; secondary: index
+        sel = order[:top_k]
+        ex = np.exp(l - l.max())
+        p = ex / ex.sum()
+        ps = p[sel]
+        ws = ps / ps.sum() if renormalize else ps
+        ids[t] = sel
+        w[t] = round_f32(ws)
+    return ids, w
+
+
+# ----------------------------------------------------------------------------- A2 align
+def max_padded(num_pairs: int, num_experts: int, block_size: int) -> int:
+    """Worst-case padded row count: every expert may add up to block_size-1 pad rows.
+
+    ferrum ``cuda/moe.rs``, ``moe_align_block_size`` takes this capacity as
+    ``sorted_max_size`` without giving a formula; the bound below is the
+    smallest that holds for every routing.
+    """
+    bs = block_size
+    return -(-(num_pairs + num_experts * (bs - 1)) // bs) * bs
+
+
+def align(topk_ids: np.ndarray, num_experts: int, block_size: int,
+          max_pad: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Block-size alignment of the flat (token, slot) pairs by expert.
+
+    ferrum ``cuda/moe.rs``: ``moe_build_pairs_by_token`` (per-expert counts,
+    ``expert_offsets``, pair -> packed row map) and ``moe_align_block_size`` /
+    ``moe_align_block_size_pair_ids`` (block-padded ``sorted_token_ids``, one
+    expert id per block, ``total_tokens_post_pad``).  Sentinel value = the
+    number of valid rows (ferrum ``triton_fused_moe.rs``,
+    ``launch_fused_moe_w4a16_triton``); inactive blocks hold a negative id
+    (``maybe_dump_moe_routing`` counts ``expert_id >= 0``).
+
+    Readings: sorted entries are flat pair ids p = t*top_k + j (the
+    ``_pair_ids`` variant); rows of one expert are in ascending p; offsets are
+    block padded (``offsets[E] == total``); unused blocks hold -1; an id outside
+    [0, E) is dropped (not counted, ``inv = -1``).
+
+    Returns counts [E], offsets [E+1], sorted_ids [max_pad], expert_ids
+    [max_pad // bs], total (int), inv [P] — all int32 except total.
+    """
+    ids = np.asarray(topk_ids).reshape(-1).astype(np.int64)
+    P = ids.size
+    E, bs = int(num_experts), int(block_size)
+    if max_pad is None:
+        max_pad = max_padded(P, E, bs)
+    counts = [0] * E
+    for p in range(P):
+        e = ids[p]
+        if 0 <= e < E:
+            counts[e] += 1
+    offsets = [0] * (E + 1)
+    for e in range(E):
+        padded = -(-counts[e] // bs) * bs
+        offsets[e + 1] = offsets[e] + padded
+    total = offsets[E]
+    if total > max_pad:
+        raise ValueError("max_pad too small")
+    sorted_ids = [P] * max_pad
+    expert_ids = [-1] * (max_pad // bs)
+    inv = [-1] * P
+    cursor = offsets[:E]
+    cursor = list(cursor)
+    for p in range(P):
+        e = ids[p]
+        if 0 <= e < E:
+            sorted_ids[cursor[e]] = p
+            inv[p] = cursor[e]
+            cursor[e] += 1
+    for e in range(E):
+        for b in range(offsets[e] // bs, offsets[e + 1] // bs):
+            expert_ids[b] = e
+    i32 = lambda a: np.asarray(a, dtype=np.int32)
+    return {"counts": i32(counts), "offsets": i32(offsets), "sorted_ids": i32(sorted_ids),
+            "expert_ids": i32(expert_ids), "total": int(total), "inv": i32(inv),
+            "num_pairs": P, "block_size": bs, "num_experts": E}
+
+
+def check_group_arrays(num_experts: int, per_expert: Sequence[Tuple[str, int]],
+                       offsets: Sequence[int]) -> Optional[str]:
+    """Group-array invariants: metrale ``cutlass/grouped.rs``, ``ensure_group_arrays``.
+
+    ``offsets`` has num_experts+1 entries, every per-expert array has
+    num_experts entries (the message names the first that does not),
+    offsets[0] >= 0 and offsets never decrease (equal neighbours = an empty
+    expert).  Returns None when all hold, else the message.
+    """
+    if len(offsets) != num_experts + 1:
+        return f"expert_offsets len {len(offsets)} != num_experts+1 {num_experts + 1}"
+    for name, n in per_expert:
+        if n != num_experts:
+            return f"{name} len {n} != num_experts {num_experts}"
+    if offsets[0] < 0:
+        return f"expert_offsets[0] = {offsets[0]} is negative"
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        if b < a:
+            return f"expert_offsets is not non-decreasing ({a} then {b})"
+    return None
+
+
+# ----------------------------------------------------------------------------- GPTQ int4 weights
+def gptq_unpack_q(qweight_e: np.ndarray) -> np.ndarray:
+    """qweight ``[K/8, N]`` int32 -> q ``[K, N]``: K index 8*i + s sits in nibble s of word i.
+
+    Layout from ferrum ``triton_fused_moe.rs`` (module doc,
+    ``TritonStackedGptqWeight``); nibble order (low nibble = lowest K) is the
+    reading taken for the raw GPTQ packing.
+    """
+    u = np.asarray(qweight_e).view(np.uint32)
+    K8, N = u.shape
+    q = np.empty((K8 * 8, N), dtype=np.int64)
+    for s in range(8):
+        q[s::8, :] = (u >> np.uint32(4 * s)) & np.uint32(0xF)
+    return q
+
+
+def gptq_unpack_z(qzeros_e: np.ndarray) -> np.ndarray:
+    """qzeros ``[K/G, N/8]`` int32 -> z ``[K/G, N]``: N index 8*i + s sits in nibble s of word i."""
+    u = np.asarray(qzeros_e).view(np.uint32)
+    Gn, N8 = u.shape
+    z = np.empty((Gn, N8 * 8), dtype=np.int64)
+    for s in range(8):
+        z[:, s::8] = (u >> np.uint32(4 * s)) & np.uint32(0xF)
+    return z
+
+
+def gptq_dequant_expert(w: Dict[str, np.ndarray], e: int) -> np.ndarray:
+    """Dequantised weight of expert e as ``[K, N]`` fp64: W[k, n] = (q[k, n] - z[k//G, n]) * s[k//G, n].
+
+    Stacked per-expert tensors as in ferrum ``triton_fused_moe.rs``
+    (``TritonStackedGptqWeight``: qweight [E,K/8,N], scales [E,K/G,N] fp16,
+    qzeros [E,K/G,N/8]).  Reading: the zero point is used as stored (no +1)
+    and groups are contiguous runs of G along K (no act-order permutation).
+    The product has at most 15 significant bits, so it is exact in fp64.
+    """
+    G = int(w["group_size"])
+    q = gptq_unpack_q(w["qweight"][e])
+    z = gptq_unpack_z(w["qzeros"][e])
+    s = f16_bits_to_f64(w["scales"][e])
+    g = np.arange(q.shape[0]) // G
+    return (q - z[g, :]).astype(np.float64) * s[g, :]
+
+
+def out_dim(w) -> int:
+    """Output width N of a stacked expert weight in either storage format."""
+    return int(w["qweight"].shape[2]) if isinstance(w, dict) else int(w.shape[1])
+
+
+def expert_matrix(w, e: int) -> np.ndarray:
+    """Weight of expert e as ``[N_out, K_in]`` fp64 for either storage format.
+
+    bf16 weights are stored ``[E, N, K]`` (K contiguous, the nn.Linear
+    convention); GPTQ weights are stored K-major and are transposed here.
+    """
+    if isinstance(w, dict):
+        return gptq_dequant_expert(w, e).T
+    return bf16_bits_to_f64(w[e])
+
+
+# ----------------------------------------------------------------------------- A3 / A4 grouped GEMMs
+def _rows_by_expert(al: Dict[str, np.ndarray], rows: Optional[np.ndarray] = None):
+    """Real sorted rows grouped by the expert of their block: {e: rows}."""
+    P, bs = al["num_pairs"], al["block_size"]
+    sid, eid = al["sorted_ids"], al["expert_ids"]
+    r_all = np.arange(int(al["total"])) if rows is None else np.asarray(rows)
+    real = r_all[(sid[r_all] >= 0) & (sid[r_all] < P)]
+    out: Dict[int, np.ndarray] = {}
+    for r in real:
+        e = int(eid[r // bs])
+        if e >= 0:
+            out.setdefault(e, []).append(int(r))
+    return {e: np.asarray(v, dtype=np.int64) for e, v in out.items()}
+
+
+def grouped_gate_up(x_bits: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray], top_k: int,
+                    rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Grouped gate/up GEMM with SiLU(gate) * up, over block-aligned sorted rows.
+
+    For every real sorted row r (sorted id p < P) with token t = p // top_k and
+    expert e = expert_ids[r // block_size]:
+    h[r] = silu(Wg[e] x[t]) * (Wu[e] x[t]).
+
+    Gather through sorted ids: metrale ``cutlass/grouped.rs``,
+    ``nvfp4_grouped_gate_up_fused``; ferrum ``triton_fused_moe.rs`` module doc
+    (``expert_ids[pid_m]`` picks the block's expert, sentinel rows masked).
+    SiLU(gate) * up: atlas ``moe_lora_grouped.rs`` (``moe_lora_gather_bgmv``:
+    the post-SwiGLU activation).  Sentinel / padding rows are left NaN (they are
+    never defined).  ``rows`` restricts the evaluation to a subset.
+    """
+    P = al["num_pairs"]
+    sid = al["sorted_ids"]
+    h = np.full((len(sid), out_dim(w_gate)), np.nan)
+    for e, rr in _rows_by_expert(al, rows).items():
+        t = sid[rr] // top_k
+        X = bf16_bits_to_f64(x_bits[t])
+        g = X @ expert_matrix(w_gate, e).T
+        u = X @ expert_matrix(w_up, e).T
+        h[rr] = silu(g) * u
+    return h
+
+
+def grouped_down(h: np.ndarray, w_down, al: Dict[str, np.ndarray],
+                 rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Grouped down GEMM: y[r] = Wd[e] h[r] for every real sorted row r.
+
+    The input is already in expert order (metrale ``cutlass/grouped.rs``,
+    ``nvfp4_grouped_down``); the output is the sorted ``expert_down_out``
+    (atlas ``moe_lora_grouped.rs`` module doc).  Sentinel rows stay NaN.
+    """
+    y = np.full((h.shape[0], out_dim(w_down)), np.nan)
+    for e, rr in _rows_by_expert(al, rows).items():
+        y[rr] = h[rr] @ expert_matrix(w_down, e).T
+    return y
+
+
+# ----------------------------------------------------------------------------- A5 LoRA fold
+def pack_expert_tables(entries: Iterable[Tuple[int, object, object, float]]):
+    """Dense per-expert tables: atlas ``moe_lora_grouped.rs``, ``pack_expert_tables``.
+
+    ``entries`` = (expert_id, a, b, scale).  Table length n = max id + 1; slots
+    of unadapted experts hold a null handle (None here, address 0 on the
+    device) and scale 0.0; a repeated id keeps its last entry; no entries ->
+    None.  Returns (a_list, b_list, scale_list, n).
+    """
+    entries = list(entries)
+    if not entries:
+        return None
+    n = max(int(e) for e, *_ in entries) + 1
+    a: List[object] = [None] * n
+    b: List[object] = [None] * n
+    s: List[float] = [0.0] * n
+    for e, ea, eb, es in entries:
+        a[int(e)], b[int(e)], s[int(e)] = ea, eb, float(es)
+    return a, b, s, n
+
+
+def lora_window_tiles(row_offset: int, row_end: int, m_tile: int = 64) -> int:
+    """Tiles of one window: max(1, ceil((row_end - row_offset) / 64)).
+
+    atlas ``moe_lora_grouped.rs``, ``grouped_down_wc`` with ``MLG_M_TILE`` = 64
+    (a window that is empty or inverted counts as zero rows).
+    """
+    n = max(0, row_end - row_offset)
+    return max(1, -(-n // m_tile))
+
+
+def lora_windows(total_rows: int, cap: int) -> List[Tuple[int, int]]:
+    """Contiguous [start, end) windows of at most ``cap`` rows covering 0..total_rows.
+
+    atlas ``moe_lora_grouped.rs``, ``grouped_down_windows`` (cap must be > 0).
+    """
+    if cap <= 0:
+        raise ValueError("grouped LoRA scratch capacity must be nonzero")
+    return [(s, min(s + cap, total_rows)) for s in range(0, total_rows, cap)]
+
+
+def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], top_k: int,
+              row_adapter: Optional[np.ndarray] = None, row_offset: int = 0,
+              row_end: Optional[int] = None, bf16_base: bool = True) -> np.ndarray:
+    """Down-projection LoRA fold over sorted rows: atlas ``moe_lora_grouped.rs``.
+
+    For every sorted row r in the window [row_offset, row_end) that is real
+    (sorted id < P), whose expert e (the span [offsets[e], offsets[e+1])
+    holding r) is adapted (e < table length and a non-null table entry), and
+    whose token's ``row_adapter`` entry is >= 0 (or no adapter map is given):
+
+        xa    = bf16(A_e  x[r])      (shrink, [max_rank])
+        delta = bf16(B_e  xa)        (expand, [n_out])
+        y[r] += scale_e * delta
+
+    ``x`` holds the bf16 post-SiLU sorted activations (module doc and
+    ``moe_lora_grouped_down``: x = post-SiLU sorted activations, base =
+    sorted ``expert_down_out``).  With ``bf16_base`` the base rows are bf16
+    and the folded row is bf16(base + scale * delta); otherwise y is kept in
+    fp64.  Rows outside the window, sentinel rows and unadapted rows are left
+    as they are.  ``tables`` = (a_list, b_list, scale_list, n) from
+    ``pack_expert_tables`` with A_e [max_rank, k_in] and B_e [n_out, max_rank]
+    as bf16 bit arrays.  Returns a new array.
+    """
+    a_tab, b_tab, s_tab, n_tab = tables
+    P = al["num_pairs"]
+    sid, off = al["sorted_ids"], al["offsets"]
+    E = len(off) - 1
+    y = np.array(y, dtype=np.float64, copy=True)
+    mats: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+    if row_end is None:
+        row_end = len(sid)
+    for r in range(max(0, row_offset), min(row_end, len(sid))):
+        p = int(sid[r])
+        if p < 0 or p >= P:
+            continue
+        e = next((k for k in range(E) if off[k] <= r < off[k + 1]), None)
+        if e is None or e >= n_tab or a_tab[e] is None or b_tab[e] is None:
+            continue
+        if row_adapter is not None and row_adapter[p // top_k] < 0:
+            continue
+        if e not in mats:
+            mats[e] = (bf16_bits_to_f64(a_tab[e]), bf16_bits_to_f64(b_tab[e]))
+        A, B = mats[e]
+        xa = round_bf16(A @ x[r])
+        delta = round_bf16(B @ xa)
+        if bf16_base:
+            y[r] = round_bf16(y[r] + np.float64(np.float32(s_tab[e])) * delta)
+        else:
+            y[r] = y[r] + np.float64(np.float32(s_tab[e])) * delta
+    return y
+
+
+# ----------------------------------------------------------------------------- A6 combine
+def combine(y: np.ndarray, inv: Optional[np.ndarray], topk_w: np.ndarray, T: int,
+            top_k: int) -> np.ndarray:
+    """Top-k weighted combine: ferrum ``cuda/moe.rs``, ``moe_combine`` / ``weighted_sum_batched``.
+
+    out[t] = sum_{j<k} w[t, j] * y[row(t, j)], j ascending, where row(t, j) =
+    inv[t*k + j] (``moe_combine``'s pair -> packed-row map); a negative entry
+    (a dropped pair) contributes nothing.  With ``inv`` None the rows are
+    slot-major, row(t, j) = t*k + j (``weighted_sum_batched``).  fp64.
+    """
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64).reshape(T, top_k)
+    H = y.shape[1]
+    out = np.zeros((T, H))
+    for t in range(T):
+        for j in range(top_k):
+            row = t * top_k + j if inv is None else int(inv[t * top_k + j])
+            if row < 0:
+                continue
+            out[t] += w[t, j] * y[row]
+    return out
+
+
+# ----------------------------------------------------------------------------- whole layer
+def _lora_tables(d) -> Optional[tuple]:
+    if "lora_ids" not in d:
+        return None
+    return pack_expert_tables(
+        (int(e), d["lora_a"][i], d["lora_b"][i], float(d["lora_scale"][i]))
+        for i, e in enumerate(d["lora_ids"]))
+
+
+def _weights(d):
+    if "wg" in d:
+        return d["wg"], d["wu"], d["wd"]
+    return d["gate"], d["up"], d["down"]
+
+
+def moe_layer(d: Dict[str, object], max_pad: Optional[int] = None) -> Dict[str, object]:
+    """The whole path on the sorted layout: route -> align -> gate/up -> down -> [fold] -> combine.
+
+    The fold (when the inputs carry LoRA tables) runs before the combine, so
+    the router weight multiplies base + delta (atlas ``moe_lora_grouped.rs``,
+    ``moe_lora_gather_bgmv``), on the bf16 post-SiLU activations bf16(h).
+    Intermediates stay fp64 otherwise.
+    """
+    cfg = d["cfg"]
+    ids, w = route(d["logits"], cfg.top_k, cfg.renormalize)
+    al = align(ids, cfg.E, cfg.block_size, max_pad)
+    wg, wu, wd = _weights(d)
+    h = grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
+    y = grouped_down(h, wd, al)
+    tabs = _lora_tables(d)
+    if tabs is not None:
+        y = lora_fold(y, round_bf16(np.nan_to_num(h)), tabs, al, cfg.top_k, bf16_base=False)
+    out = combine(y, al["inv"], w, cfg.T, cfg.top_k)
+    return {"ids": ids, "w": w, "align": al, "h": h, "y": y, "out": out}
+
+
+def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
+               routing: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
+    """The layer output for selected tokens straight from the per-token definition.
+
+    out[t] = sum_j w[t, j] * FFN_{id[t, j]}(x[t]) with
+    FFN_e(x) = Wd[e] (silu(Wg[e] x) * (Wu[e] x)) and, for adapted experts, the
+    fold delta added to FFN_e(x) before weighting.  No sorting or padding:
+    used on sampled tokens of full-size workloads.  Returns [len(tokens), H].
+    """
+    cfg = d["cfg"]
+    ids, w = routing if routing is not None else route(d["logits"], cfg.top_k, cfg.renormalize)
+    wg, wu, wd = _weights(d)
+    tabs = _lora_tables(d)
+    tokens = list(tokens)
+    by_e: Dict[int, List[Tuple[int, int]]] = {}
+    for i, t in enumerate(tokens):
+        for j in range(cfg.top_k):
+            by_e.setdefault(int(ids[t, j]), []).append((i, j))
+    out = np.zeros((len(tokens), cfg.H))
+    contrib = {}
+    for e, lst in sorted(by_e.items()):
+        X = bf16_bits_to_f64(d["x"][[tokens[i] for i, _ in lst]])
+        h = silu(X @ expert_matrix(wg, e).T) * (X @ expert_matrix(wu, e).T)
+        yy = h @ expert_matrix(wd, e).T
+        if tabs is not None and e < tabs[3] and tabs[0][e] is not None:
+            A = bf16_bits_to_f64(tabs[0][e])
+            B = bf16_bits_to_f64(tabs[1][e])
+            xa = round_bf16(round_bf16(h) @ A.T)
+            delta = round_bf16(xa @ B.T)
+            yy = yy + np.float64(np.float32(tabs[2][e])) * delta
+        for (i, j), row in zip(lst, yy):
+            contrib[(i, j)] = row
+    for i, t in enumerate(tokens):
+        for j in range(cfg.top_k):
+            out[i] += np.float64(w[t, j]) * contrib[(i, j)]
+    return out

@@ -1,0 +1,353 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something other
+than itself — the pages' own test cases, hand-worked examples with closed forms,
+independent library routines, textbook special cases, invariants and brute force
+on tiny inputs.  CPU only."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax as scipy_softmax
+
+import oracle
+from moe_synth import CONFIGS, MoeConfig, make_inputs, f32_to_bf16_bits
+from conftest import golden
+
+
+def bf16(a):
+    return f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+# ----------------------------------------------------------------------------- number formats
+def test_round_bf16_against_torch():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+        np.float32([0.0, -0.0, 1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -133, 2 ** -134,
+                    3 * 2 ** -134, 1e-45, 3.3895e38]),
+    ])
+    # every fp32 value that sits exactly on a bf16 tie
+    ties = (np.arange(1, 5000, dtype=np.uint32) << 16 | np.uint32(0x8000)).view(np.float32)
+    v = np.concatenate([v, ties, -ties])
+    ours = oracle.round_bf16(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_round_bf16_hand_values():
+    r = oracle.round_bf16
+    assert r(1 + 2 ** -8) == 1.0                      # tie -> even mantissa
+    assert r(1 + 3 * 2 ** -8) == 1 + 2 ** -6          # tie -> even (up)
+    assert r(1 + 2 ** -8 + 2 ** -30) == 1 + 2 ** -7   # just above the tie
+    assert r(-(1 + 2 ** -8)) == -1.0
+    assert r(255.5) == 256.0 and r(255.0) == 255.0
+    assert r(2.0 ** 128 * 0.999) == np.inf
+
+
+def test_bf16_and_f16_widening_exact():
+    v = np.float32([1.5, -2.75, 3.0e-3, 65504.0])
+    assert np.array_equal(oracle.bf16_bits_to_f64(bf16(v)), torch.tensor(v).bfloat16().double().numpy())
+    h = np.float16([0.005, 0.02, -1.0, 6.1e-5])
+    assert np.array_equal(oracle.f16_bits_to_f64(h.view(np.uint16)), h.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- route
+def test_route_worked_examples():
+    g = golden("route_worked.json")
+    for c in g["cases"]:
+        l = np.float32([float(x) for x in c["logits"]])[None, :]
+        ids, w = oracle.route(l, c["top_k"], c["renormalize"])
+        assert ids[0].tolist() == c["ids"], c
+        assert np.array_equal(w[0], np.float32(c["weights"])), (w, c)
+
+
+def test_route_special_cases():
+    rng = np.random.default_rng(2)
+    # one expert: weight exactly 1
+    ids, w = oracle.route(rng.standard_normal((5, 1)).astype(np.float32), 1)
+    assert (ids == 0).all() and (w == 1.0).all()
+    # k = E with renormalisation = the full softmax, in descending order
+    l = rng.standard_normal((50, 6)).astype(np.float32)
+    ids, w = oracle.route(l, 6, True)
+    full = scipy_softmax(l.astype(np.float64), axis=1)
+    assert np.array_equal(w, np.take_along_axis(full, ids, 1).astype(np.float32))
+    # without renormalisation the weights are the softmax probabilities themselves
+    l = rng.standard_normal((50, 16)).astype(np.float32)
+    ids, w = oracle.route(l, 3, False)
+    assert np.array_equal(w, np.take_along_axis(scipy_softmax(l.astype(np.float64), axis=1), ids, 1)
+                          .astype(np.float32))
+
+
+def test_route_brute_force_ids_and_sum():
+    rng = np.random.default_rng(3)
+    for E, k in [(8, 2), (64, 6), (128, 8), (5, 5)]:
+        l = rng.standard_normal((300, E)).astype(np.float32)
+        l[:10, 1] = l[:10, 3]                          # plant exact ties
+        ids, w = oracle.route(l, k, True)
+        ref = np.argsort(-l, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1) <= k * 2.0 ** -24)
+        # renormalised weights are proportional to exp(logit)
+        lsel = np.take_along_axis(l.astype(np.float64), ids, 1)
+        ref_w = scipy_softmax(lsel, axis=1)
+        assert np.allclose(w, ref_w, rtol=2 ** -23, atol=0)
+
+
+# ----------------------------------------------------------------------------- align
+def _check_align_invariants(ids_flat, E, bs, al):
+    P = len(ids_flat)
+    counts, off, sid, eid, inv = al["counts"], al["offsets"], al["sorted_ids"], al["expert_ids"], al["inv"]
+    assert oracle.check_group_arrays(E, [("counts", len(counts))], off.tolist()) is None
+    valid = (ids_flat >= 0) & (ids_flat < E)
+    assert counts.sum() == valid.sum()
+    assert np.array_equal(counts, np.bincount(ids_flat[valid], minlength=E))
+    assert off[0] == 0 and (off % bs == 0).all() and al["total"] == off[-1] <= len(sid)
+    assert np.array_equal(np.diff(off), -(-counts // bs) * bs)
+    # brute force: a stable sort of the pairs by expert gives the real rows in order
+    order = np.argsort(np.where(valid, ids_flat, E), kind="stable")[: valid.sum()]
+    real_rows = np.concatenate([np.arange(off[e], off[e] + counts[e]) for e in range(E)] or [[]]).astype(int)
+    assert np.array_equal(sid[real_rows], order)
+    # everything else is the sentinel P; inverse map round-trips
+    mask = np.ones(len(sid), bool)
+    mask[real_rows] = False
+    assert (sid[mask] == P).all()
+    assert np.array_equal(inv[order], real_rows)
+    assert (inv[~valid] == -1).all()
+    for b in range(len(eid)):
+        if b * bs < al["total"]:
+            e = np.searchsorted(off, b * bs, side="right") - 1
+            assert eid[b] == e
+        else:
+            assert eid[b] == -1
+
+
+def test_align_worked_examples():
+    for c in golden("align_worked.json")["cases"]:
+        ids = np.asarray(c["topk_ids"])
+        al = oracle.align(ids, c["num_experts"], c["block_size"], c["max_pad"])
+        for key in ("counts", "offsets", "sorted_ids", "expert_ids", "inv"):
+            assert al[key].tolist() == c[key], key
+        assert al["total"] == c["total"]
+        assert oracle.max_padded(ids.size, c["num_experts"], c["block_size"]) == c["max_pad"]
+
+
+@pytest.mark.parametrize("E,k,bs,T", [(8, 2, 16, 64), (128, 8, 64, 300), (64, 6, 16, 16), (3, 1, 128, 7),
+                                      (256, 4, 32, 100), (1, 1, 16, 5)])
+def test_align_invariants_random(E, k, bs, T):
+    rng = np.random.default_rng(E * 1000 + T)
+    ids = rng.integers(0, E, size=(T, k))
+    al = oracle.align(ids, E, bs)
+    assert len(al["sorted_ids"]) == oracle.max_padded(T * k, E, bs)
+    _check_align_invariants(ids.reshape(-1), E, bs, al)
+
+
+def test_align_drops_out_of_range_and_empty():
+    ids = np.array([[0, 5], [-1, 2], [2, 2]])
+    al = oracle.align(ids, 3, 4)
+    _check_align_invariants(ids.reshape(-1), 3, 4, al)
+    assert al["inv"][1] == -1 and al["inv"][2] == -1
+    al0 = oracle.align(np.zeros((0, 2), dtype=np.int32), 4, 16)
+    assert al0["total"] == 0 and (al0["sorted_ids"] == 0).all() and (al0["expert_ids"] == -1).all()
+
+
+def test_align_max_pad_is_tight():
+    # all pairs on distinct experts with one pair each reach the bound exactly
+    E, bs = 10, 16
+    ids = np.arange(E)[:, None]
+    al = oracle.align(ids, E, bs)
+    assert al["total"] == E * bs == oracle.max_padded(E, E, bs)
+
+
+def test_group_arrays_page_cases():
+    for c in golden("group_arrays_cases.json")["cases"]:
+        msg = oracle.check_group_arrays(c["num_experts"], [tuple(x) for x in c["per_expert"]], c["offsets"])
+        assert (msg is None) == c["ok"], (c, msg)
+        if "message_contains" in c:
+            assert c["message_contains"] in msg
+
+
+# ----------------------------------------------------------------------------- GPTQ
+def _pack_reference(q, z):
+    """Independent packer: build each int32 word from its nibbles with Python ints."""
+    K, N = q.shape
+    qw = np.zeros((K // 8, N), dtype=np.int64)
+    for k in range(K):
+        for n in range(N):
+            qw[k // 8, n] |= int(q[k, n]) << (4 * (k % 8))
+    G_, _ = z.shape
+    qz = np.zeros((G_, N // 8), dtype=np.int64)
+    for g in range(G_):
+        for n in range(N):
+            qz[g, n // 8] |= int(z[g, n]) << (4 * (n % 8))
+    to32 = lambda a: a.astype(np.uint32).view(np.int32)
+    return to32(qw), to32(qz)
+
+
+def test_gptq_unpack_and_dequant():
+    rng = np.random.default_rng(4)
+    K, N, G = 64, 16, 32
+    q = rng.integers(0, 16, (K, N))
+    z = rng.integers(0, 16, (K // G, N))
+    s = np.float16(rng.uniform(0.005, 0.02, (K // G, N)))
+    qw, qz = _pack_reference(q, z)
+    assert np.array_equal(oracle.gptq_unpack_q(qw), q)
+    assert np.array_equal(oracle.gptq_unpack_z(qz), z)
+    w = {"qweight": qw[None], "qzeros": qz[None], "scales": s.view(np.uint16)[None], "group_size": G}
+    W = oracle.gptq_dequant_expert(w, 0)
+    for k, n in itertools.product(range(0, K, 7), range(N)):
+        assert W[k, n] == (q[k, n] - z[k // G, n]) * float(s[k // G, n])
+    # q == z gives an exact zero; a power-of-two scale gives exact integers
+    w2 = {"qweight": _pack_reference(q, q[::G][: K // G])[0][None], "qzeros": _pack_reference(q, q[:K // G])[1][None],
+          "scales": np.full((1, K // G, N), np.float16(2.0 ** -3)).view(np.uint16), "group_size": G}
+    q2 = oracle.gptq_unpack_q(w2["qweight"][0])
+    z2 = oracle.gptq_unpack_z(w2["qzeros"][0])
+    W2 = oracle.gptq_dequant_expert(w2, 0)
+    assert np.array_equal(W2 * 8, (q2 - z2[np.arange(K) // G]).astype(np.float64))
+    w3 = dict(w)
+    w3["qzeros"] = _pack_reference(q, np.stack([q[g * G] for g in range(K // G)]))[1][None]
+    W3 = oracle.gptq_dequant_expert(w3, 0)
+    assert all(W3[g * G, n] == 0.0 for g in range(K // G) for n in range(N))
+
+
+def test_gptq_generator_layout_matches_page():
+    cfg = CONFIGS["decode_int4"].with_(T=4, H=256, I=128, E=3)
+    d = make_inputs(cfg)
+    g = d["gate"]
+    assert g["qweight"].shape == (3, 256 // 8, 128) and g["qweight"].dtype == np.int32
+    assert g["scales"].shape == (3, 256 // 128, 128)
+    assert g["qzeros"].shape == (3, 256 // 128, 128 // 8) and g["qzeros"].dtype == np.int32
+    s = oracle.f16_bits_to_f64(g["scales"])
+    assert s.min() >= 0.0049 and s.max() <= 0.0201
+
+
+# ----------------------------------------------------------------------------- GEMMs and the whole layer
+def _dense_brute_force(d, ids, w):
+    """Every token through every expert; the gate weight is zero for unselected experts."""
+    cfg = d["cfg"]
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    X = oracle.bf16_bits_to_f64(d["x"])
+    gate = np.zeros((cfg.T, cfg.E))
+    for t in range(cfg.T):
+        for j in range(cfg.top_k):
+            gate[t, ids[t, j]] += float(w[t, j])
+    out = np.zeros((cfg.T, cfg.H))
+    for e in range(cfg.E):
+        Wg, Wu, Wd = (oracle.expert_matrix(m, e) for m in (wg, wu, wd))
+        a = X @ Wg.T
+        f = ((a * (1 / (1 + np.exp(-a)))) * (X @ Wu.T)) @ Wd.T
+        out += gate[:, e:e + 1] * f
+    return out
+
+
+@pytest.mark.parametrize("E,k,bs", [(1, 1, 16), (2, 1, 16), (8, 2, 16), (8, 2, 64), (4, 4, 32)])
+def test_layer_matches_dense_brute_force(E, k, bs):
+    cfg = MoeConfig("t", T=40, H=64, I=32, E=E, top_k=k, block_size=bs, seed=E * 10 + k)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    ref = _dense_brute_force(d, r["ids"], r["w"])
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+    tok = oracle.moe_tokens(d, range(cfg.T))
+    assert np.allclose(tok, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_layer_int4_matches_dense_brute_force():
+    cfg = MoeConfig("t", T=12, H=256, I=128, E=5, top_k=3, block_size=16, weights="int4_gptq",
+                    group_size=128, seed=9)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    assert np.allclose(r["out"], _dense_brute_force(d, r["ids"], r["w"]), rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_textbook_swiglu():
+    cfg = MoeConfig("t", T=16, H=64, I=48, E=1, top_k=1, block_size=16, seed=5)
+    d = make_inputs(cfg)
+    out = oracle.moe_layer(d)["out"]
+    x = torch.from_numpy(oracle.bf16_bits_to_f64(d["x"]))
+    Wg, Wu, Wd = (torch.from_numpy(oracle.bf16_bits_to_f64(d[k][0])) for k in ("wg", "wu", "wd"))
+    ref = (torch.nn.functional.silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+    assert np.allclose(out, ref.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_grouped_gemm_sentinel_rows_undefined():
+    cfg = CONFIGS["tiny"]
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    sid = r["align"]["sorted_ids"]
+    pad = sid >= cfg.P
+    assert np.isnan(r["h"][pad]).all() and np.isnan(r["y"][pad]).all()
+    assert np.isfinite(r["h"][~pad]).all()
+
+
+# ----------------------------------------------------------------------------- combine
+def test_combine_worked_example():
+    g = golden("combine_worked.json")
+    y = np.asarray(g["y"])
+    out = oracle.combine(y, np.asarray(g["inv"]), np.float32(g["topk_w"]), 2, 2)
+    assert np.array_equal(out, np.asarray(g["out"]))
+    out2 = oracle.combine(y, None, np.float32(g["topk_w"]), 2, 2)
+    assert np.array_equal(out2, np.asarray(g["out_slot_major"]))
+
+
+# ----------------------------------------------------------------------------- LoRA fold
+def _fold_case(c, *, delta_round=True, xa_round=True):
+    """Run the oracle fold on one closed-form case (one row, one adapted expert)."""
+    x = np.asarray(c["x"])[None, :]
+    A = bf16(np.asarray(c["A"]))
+    B = bf16(np.asarray(c["B"]))
+    al = oracle.align(np.array([[0]]), 1, 1)
+    tabs = oracle.pack_expert_tables([(0, A, B, c["scale"])])
+    return oracle.lora_fold(np.asarray(c["base"])[None, :], x, tabs, al, 1)[0]
+
+
+def test_lora_fold_rounding_pins():
+    for c in golden("lora_fold_pins.json")["cases"]:
+        assert np.array_equal(_fold_case(c), np.asarray(c["folded_bf16"])), c["name"]
+
+
+def test_lora_fold_identities_and_windows():
+    cfg = CONFIGS["lora_prefill"].with_(T=96, H=128, I=64, E=8, top_k=2, block_size=16,
+                                        lora_rank=4, lora_max_rank=8)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    al = r["align"]
+    xs = oracle.round_bf16(np.nan_to_num(r["h"]))
+    base = oracle.round_bf16(np.nan_to_num(r["y"]))
+    tabs = oracle.moe_oracle._lora_tables(d)
+    full = oracle.lora_fold(base, xs, tabs, al, cfg.top_k)
+    # chunked windows give the same bits as one call over everything
+    chunked = base.copy()
+    for s, e in oracle.lora_windows(len(al["sorted_ids"]), 40):
+        chunked = oracle.lora_fold(chunked, xs, tabs, al, cfg.top_k, row_offset=s, row_end=e)
+    assert np.array_equal(chunked, full)
+    # only real rows of adapted (even) experts change
+    P = cfg.P
+    changed = np.any(full != base, axis=1)
+    sid = al["sorted_ids"]
+    for rr in range(len(sid)):
+        e = np.searchsorted(al["offsets"], rr, side="right") - 1
+        adapted = sid[rr] < P and e < cfg.E and e % 2 == 0
+        if not adapted:
+            assert not changed[rr]
+    assert changed.sum() > 0
+    # scale 0 leaves every row bit-identical
+    a, b, s, n = tabs
+    z = oracle.lora_fold(base, xs, (a, b, [0.0] * n, n), al, cfg.top_k)
+    assert np.array_equal(z, base)
+    # a per-token adapter map with all entries < 0 skips every row
+    skip = oracle.lora_fold(base, xs, tabs, al, cfg.top_k, row_adapter=-np.ones(cfg.T, np.int32))
+    assert np.array_equal(skip, base)
+
+
+def test_pack_expert_tables_and_windows():
+    assert oracle.pack_expert_tables([]) is None
+    a, b, s, n = oracle.pack_expert_tables([(2, "A2", "B2", 0.5), (0, "A0", "B0", 1.5), (2, "A2b", "B2b", 0.25)])
+    assert n == 3 and a == ["A0", None, "A2b"] and b == ["B0", None, "B2b"] and s == [1.5, 0.0, 0.25]
+    assert oracle.lora_window_tiles(0, 16320) == math.ceil(16320 / 64)
+    assert oracle.lora_window_tiles(100, 100) == 1 and oracle.lora_window_tiles(0, 1) == 1
+    w = oracle.lora_windows(10000, 4096)
+    assert w == [(0, 4096), (4096, 8192), (8192, 10000)]
+    with pytest.raises(ValueError):
+        oracle.lora_windows(10, 0)
