@@ -1,0 +1,160 @@
+"""Benchmark of one routed-MoE expert layer on one MI355X.
+
+One step = the whole path over one batch of synthetic tokens:
+route -> align -> grouped gate/up + SiLU -> grouped down -> [LoRA fold] -> combine.
+
+Prints ONE JSON line (metric = MoE layer tokens/s).  The grouped gate/up GEMM is
+timed on its own with HIP events on the launch stream inside the timed region and
+reported against the bf16 MFMA peak; the CPU oracle is timed on a bounded token
+sample of the same workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(cfg, op: str) -> float:
+    """Algorithmic FLOPs of one grouped GEMM launch: 2*K*N per real (token, expert) pair and projection."""
+    per_pair = {"gate_up": 2 * 2 * cfg.H * cfg.I, "down": 2 * cfg.H * cfg.I}[op]
+    return float(per_pair) * cfg.P
+
+
+def layer_flops(cfg) -> float:
+    return 6.0 * cfg.H * cfg.I * cfg.P
+
+
+def cpu_baseline(cfg, d, budget_tokens: int):
+    """The oracle as it stands, on the first ``budget_tokens`` tokens of the same workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    T = min(cfg.T, budget_tokens)
+    sub = dict(d)
+    sub["cfg"] = cfg.with_(T=T)
+    sub["logits"] = d["logits"][:T]
+    sub["x"] = d["x"][:T]
+    t0 = time.perf_counter()
+    oracle.moe_layer(sub)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {T} of {cfg.T} tokens of {cfg.name}, whole layer (route, align, grouped "
+                      f"GEMMs, combine) in fp64 numpy; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--cpu-tokens", type=int, default=256, help="token sample of the CPU oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures the single-GPU path only; --gpus {args.gpus} is not supported "
+              "(multi-GPU expert/tensor parallel sharding is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mixture_experts_routed_route_amd as m
+    from moe_synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name} inputs")
+    d = make_inputs(cfg)
+    layer = m.MoeLayer.from_arrays(d, dev)
+    b = layer.plan(cfg.T, dev)
+    logits = torch.from_numpy(d["logits"]).to(dev)
+    x = torch.from_numpy(d["x"]).view(torch.bfloat16).to(dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        layer.route_align(logits, b)
+        if ev is not None:
+            ev[0].record()
+        m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, x, layer.gate, layer.up, b.routing, out=b.hs)
+        if ev is not None:
+            ev[1].record()
+        m.moe_grouped_gemm(m.MOE_OP_DOWN, b.hs, layer.down, None, b.routing, out=b.ys)
+        if ev is not None:
+            ev[2].record()
+        if layer.lora is not None:
+            for s, e in m.lora_windows(b.routing.max_pad, b.xa.shape[0]):
+                m.moe_lora_fold(b.hs, b.ys, layer.lora, b.routing, None, b.xa, s, e)
+        layer.combine(b)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    tokens_s = cfg.T / (ms / 1e3)
+    gu_tflops = gemm_flops(cfg, "gate_up") / (gu_ms / 1e3) / 1e12
+    dn_tflops = gemm_flops(cfg, "down") / (dn_ms / 1e3) / 1e12
+    gemm_tflops = (gemm_flops(cfg, "gate_up") + gemm_flops(cfg, "down")) / ((gu_ms + dn_ms) / 1e3) / 1e12
+    log(f"[bench] step {ms:.3f} ms; gate/up {gu_ms:.3f} ms ({gu_tflops:.1f} TFLOP/s); "
+        f"down {dn_ms:.3f} ms ({dn_tflops:.1f} TFLOP/s); grouped GEMMs {gemm_tflops:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(cfg, d, args.cpu_tokens)
+        log(f"[bench] cpu oracle {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "MoE layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA / HBM peak), 1 GPU",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64; random-init expert weights)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
+                   "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
+                   "weights": cfg.weights, "lora_rank": cfg.lora_rank},
+        "grouped_gemm_tflops": gemm_tflops,
+        "grouped_gemm_frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "kernels_ms": {"gate_up": gu_ms, "down": dn_ms},
+        "roofline": {"kernel": "gemm_bf16_kernel<gate_up>", "bound": "mfma", "achieved": gu_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gu_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

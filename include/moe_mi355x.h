@@ -1,0 +1,208 @@
+/*
+ * moe_mi355x.h — C ABI of the routed mixture-of-experts expert path on MI355X (gfx950).
+ *
+ * The path, one layer of a routed MoE FFN on one GPU:
+ *
+ *   moe_route         top-k softmax routing of the router logits
+ *   moe_align         per-expert histogram, block-padded expert_offsets,
+ *                     sorted pair ids with sentinels, one expert id per block
+ *   moe_grouped_gemm  grouped gate/up GEMM with fused SiLU(gate)*up, and the
+ *                     grouped down GEMM (bf16 or GPTQ-int4 expert weights)
+ *   moe_lora_fold     optional per-expert down-projection LoRA fold, in place
+ *   moe_combine       top-k weighted sum of the expert outputs per token
+ *
+ * Sources (cited by page and item; the pages are Rust host code of four
+ * projects):  ferrum-kernels `src/backend/cuda/moe.rs` (route_topk_softmax,
+ * moe_build_pairs_by_token, moe_align_block_size[_pair_ids], moe_combine,
+ * weighted_sum_batched); ferrum-kernels `src/backend/cuda/triton_fused_moe.rs`
+ * (stacked GPTQ layout, one launch over all pairs, sentinel masking); metrale
+ * `gpu_runtime/cutlass/grouped.rs` (grouped gate/up/down roles, gather through
+ * sorted ids, ensure_group_arrays); atlas `spark_model/layers/ops/
+ * moe_lora_grouped.rs` (down-projection LoRA fold, device-side expert spans,
+ * static worst-case grids, windows).
+ *
+ * Conventions for every entry point:
+ *  - Array arguments of device entry points are DEVICE pointers, allocated and
+ *    owned by the caller, 16-byte aligned.  bf16 and fp16 values travel as
+ *    uint16_t bit patterns.  Layouts are row-major and contiguous.
+ *  - The library allocates no memory, never synchronises, never reads device
+ *    data on the host, and enqueues work only on `stream` (a hipStream_t; NULL
+ *    is the null stream).  Every launch grid is fixed by host scalars alone, so
+ *    a sequence of calls can be captured in a HIP graph.
+ *  - Return value: MOE_OK, or a negative moe_status.  Every precondition the
+ *    host can check is checked before anything is enqueued; the failing call
+ *    enqueues nothing and moe_last_error() names the offending argument.
+ *    Device-resident values that the host cannot see (ids, offsets) get
+ *    defined behaviour instead: out-of-range values are skipped, never used to
+ *    address memory.
+ *  - Thread safety: all entry points are re-entrant; moe_last_error() is
+ *    per calling thread.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* a host-checkable argument is invalid               */
+#define MOE_EUNSUPPORTED (-2)  /* valid but outside what the kernels support (E>256)  */
+#define MOE_ELAUNCH (-3)       /* the HIP runtime refused the launch                  */
+
+typedef void* moe_stream; /* hipStream_t */
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t moe_abi_version(void);
+
+/* ============================================================== pure host helpers (no GPU) */
+
+/* Rows the sorted layout needs in the worst case: roundup(P + E*(bs-1), bs).
+ * The capacity `sorted_max_size` of ferrum moe.rs moe_align_block_size, which
+ * that page passes without a formula.  Returns -1 on invalid arguments. */
+int64_t moe_align_max_padded(int64_t num_pairs, int32_t num_experts, int32_t block_size);
+
+/* Bytes of device workspace moe_align needs (per-chunk expert histograms). */
+int64_t moe_align_workspace_bytes(int64_t num_pairs, int32_t num_experts);
+
+/* Group-array check of metrale cutlass/grouped.rs, ensure_group_arrays:
+ * `offsets` (host, `offsets_len` entries) must have num_experts+1 entries,
+ * offsets[0] >= 0 and never decrease; each of the `n_arrays` per-expert host
+ * arrays, whose lengths are `lens[i]` and names `names[i]`, must have
+ * num_experts entries.  MOE_EINVAL with a message naming the first offender. */
+moe_status moe_check_group_arrays(int32_t num_experts, const int64_t* lens, const char* const* names,
+                                  int32_t n_arrays, const int32_t* offsets, int64_t offsets_len);
+
+/* Dense per-expert LoRA tables, atlas moe_lora_grouped.rs pack_expert_tables:
+ * entries (ids[i], a[i], b[i], s[i]) for i < n are scattered into tables of
+ * length n_tab = max id + 1 (written to *n_tab); unadapted slots hold 0 / 0.0;
+ * a repeated id keeps its last entry; n == 0 gives *n_tab = 0 (no route).
+ * Output arrays are host arrays of capacity `cap` entries.  Ids must be in
+ * [0, 65535] (the page keys experts by u16). */
+moe_status moe_lora_pack_tables(const int32_t* ids, const uint64_t* a, const uint64_t* b, const float* s,
+                                int32_t n, uint64_t* a_out, uint64_t* b_out, float* s_out, int32_t cap,
+                                int32_t* n_tab);
+
+/* Row tiles (64 rows each) of one fold window, atlas moe_lora_grouped.rs
+ * grouped_down_wc: max(1, ceil((row_end - row_offset) / 64)). */
+int64_t moe_lora_window_tiles(int64_t row_offset, int64_t row_end);
+
+/* Contiguous [start, end) windows of at most `cap` rows covering 0..total_rows
+ * (atlas moe_lora_grouped.rs grouped_down_windows).  Writes up to
+ * `max_windows` pairs and returns the number of windows, or -1 if cap <= 0. */
+int64_t moe_lora_windows(int64_t total_rows, int64_t cap, int64_t* starts, int64_t* ends,
+                         int64_t max_windows);
+
+/* ============================================================== device entry points */
+
+/* A1 — top-k softmax routing (ferrum moe.rs, route_topk_softmax).
+ *   logits   fp32 [num_tokens, num_experts]
+ *   topk_ids i32  [num_tokens, top_k]   out: selected experts, most probable first
+ *   topk_w   fp32 [num_tokens, top_k]   out: their weights
+ * Per token: probabilities p = softmax over all experts; the top_k experts by
+ * logit (ties: lower index first); with `renormalize` the kept p are divided
+ * by their sum.  Weights are computed in fp64 and rounded once to fp32.
+ * Logits must be finite.  1 <= top_k <= num_experts <= 256.  num_tokens == 0
+ * enqueues nothing. */
+moe_status moe_route(const float* logits, int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                     int32_t renormalize, int32_t* topk_ids, float* topk_w, moe_stream stream);
+
+/* A2 — alignment of the P = num_tokens*top_k (token, slot) pairs by expert
+ * (ferrum moe.rs, moe_build_pairs_by_token + moe_align_block_size_pair_ids).
+ *   topk_ids       i32 [num_pairs]          flat pair p = t*top_k + j -> expert
+ *   counts         i32 [num_experts]        out: real rows per expert
+ *   expert_offsets i32 [num_experts + 1]    out: block-padded exclusive prefix sum;
+ *                                           expert e owns sorted rows [off[e], off[e+1]),
+ *                                           its real rows are the first counts[e]
+ *   sorted_ids     i32 [max_pad]            out: pair id per sorted row, ascending p
+ *                                           within an expert; every other row holds
+ *                                           the sentinel num_pairs
+ *   expert_ids     i32 [max_pad/block_size] out: expert of each block, -1 past the end
+ *   total_padded   i32 [1]                  out: off[num_experts]
+ *   inv_sorted     i32 [num_pairs]          out: sorted row of each pair (-1 if dropped)
+ *   workspace      device, >= moe_align_workspace_bytes(num_pairs, num_experts) bytes
+ * An id outside [0, num_experts) is dropped: not counted, inv_sorted = -1.
+ * max_pad >= moe_align_max_padded(...) and a multiple of block_size;
+ * block_size in {16, 32, 64, 128}; num_experts <= 256 (MOE_EUNSUPPORTED above,
+ * the limit of ferrum's MAX_NUM_EXPERTS). */
+moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_experts, int32_t block_size,
+                     int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                     int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, void* workspace,
+                     int64_t workspace_bytes, moe_stream stream);
+
+/* Expert weights of one projection, K = contraction, N = outputs.
+ *   MOE_W_BF16:      data = bf16 [E, N, K] (K contiguous); scales, qzeros unused.
+ *   MOE_W_INT4_GPTQ: data = int32 qweight [E, K/8, N], K index 8i+s in nibble s of
+ *                    word i; scales = fp16 [E, K/G, N]; qzeros = int32 [E, K/G, N/8],
+ *                    N index 8i+s in nibble s; W[k,n] = (q - z) * s, groups of G
+ *                    consecutive k (ferrum triton_fused_moe.rs, TritonStackedGptqWeight). */
+typedef enum { MOE_W_BF16 = 0, MOE_W_INT4_GPTQ = 1 } moe_wtype;
+typedef struct moe_weight {
+    int32_t type;            /* moe_wtype */
+    int32_t group_size;      /* G (int4 only): multiple of 32, divides K */
+    const void* data;
+    const uint16_t* scales;
+    const int32_t* qzeros;
+} moe_weight;
+
+typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1 } moe_gemm_op;
+
+/* A3/A4 — grouped expert GEMM over the sorted, block-padded rows (one launch
+ * for all experts; metrale cutlass/grouped.rs nvfp4_grouped_gate_up_fused /
+ * nvfp4_grouped_down roles, ferrum triton_fused_moe.rs masking).
+ *   MOE_OP_GATE_UP_SILU: a = x [num_pairs/top_k, K] token-major; sorted row r
+ *                        reads token sorted_ids[r]/top_k; w0 = gate, w1 = up;
+ *                        c[r, :N] = bf16(silu(x Wg^T) * (x Wu^T))
+ *   MOE_OP_DOWN:         a = Hs [max_pad, K] in sorted order; w0 = down, w1 = NULL;
+ *                        c[r, :N] = bf16(Hs[r] Wd^T)
+ * The expert of row r is the block's expert (expert_ids / expert_offsets from
+ * moe_align).  Sentinel and padding rows are neither read as tokens nor
+ * written: c keeps its previous content there.  fp32 accumulation.
+ *   c: bf16 [max_pad, N].  K % 8 == 0, N % 8 == 0 (int4: N % 64 == 0,
+ *   K % group_size == 0).  Both weights must have the same type. */
+moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0, const moe_weight* w1,
+                            uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
+                            const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
+                            int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
+                            moe_stream stream);
+
+/* A5 — down-projection LoRA fold, in place, on one window [row_offset, row_end)
+ * of the sorted rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down).
+ *   x           bf16 [max_pad, k_in]   post-SiLU sorted activations (Hs)
+ *   base        bf16 [max_pad, n_out]  sorted expert_down_out (Ys), folded in place
+ *   a_table     u64  [n_tab] device    address of A_e, bf16 [max_rank, k_in]; 0 = unadapted
+ *   b_table     u64  [n_tab] device    address of B_e, bf16 [n_out, max_rank]; 0 = unadapted
+ *   scale_table f32  [n_tab] device    scale_e
+ *   row_adapter i32  [num_pairs/top_k] or NULL: a token whose entry is < 0 is skipped
+ *   xa          bf16 [cap, max_rank]   scratch, indexed by the local row r - row_offset
+ * For each real row r of an adapted expert e < n_tab in the window:
+ *   xa = bf16(x[r] A_e^T); delta = bf16(xa B_e^T); base[r] = bf16(base[r] + scale_e*delta)
+ * with fp32 sums.  Other rows are not touched.  Windows may be applied one
+ * after the other with the same xa scratch (stream order).  max_rank % 32 == 0,
+ * k_in % 8 == 0, n_out % 8 == 0, cap >= row_end - row_offset, n_tab <= num_experts. */
+moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_table, const uint64_t* b_table,
+                         const float* scale_table, int32_t n_tab, int32_t k_in, int32_t n_out, int32_t max_rank,
+                         const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
+                         int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
+                         int64_t row_offset, int64_t row_end, int64_t max_pad, moe_stream stream);
+
+/* A6 — top-k weighted combine (ferrum moe.rs, moe_combine / weighted_sum_batched).
+ *   ys         bf16 [ys_rows, hidden]
+ *   inv_sorted i32  [num_tokens*top_k] or NULL (slot-major: row t*top_k + j)
+ *   topk_w     fp32 [num_tokens, top_k]
+ *   out        bf16 [num_tokens, hidden]
+ * out[t] = bf16(sum_{j<top_k} topk_w[t,j] * ys[row(t,j)]), fp32, j ascending;
+ * a row outside [0, ys_rows) contributes nothing.  hidden % 8 == 0. */
+moe_status moe_combine(const uint16_t* ys, const int32_t* inv_sorted, const float* topk_w, uint16_t* out,
+                       int32_t num_tokens, int32_t top_k, int32_t hidden, int64_t ys_rows, moe_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

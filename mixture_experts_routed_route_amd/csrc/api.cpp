@@ -1,0 +1,305 @@
+// C ABI of the MoE expert path (declared in include/moe_mi355x.h): host-side argument
+// checks, pure host helpers, and the launches of the gfx950 kernels.
+#include "../../include/moe_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launchers.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+moe_status ok() { return MOE_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                 \
+    do {                                                   \
+        if (!(cond)) return fail(MOE_EINVAL, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(who, p)                                                                 \
+    do {                                                                                    \
+        if ((p) == nullptr) return fail(MOE_EINVAL, "%s: %s is NULL", who, #p);             \
+        if (!aligned16(p)) return fail(MOE_EINVAL, "%s: %s is not 16-byte aligned", who, #p); \
+    } while (0)
+
+moe_status launched(const char* who, hipError_t err) {
+    if (err != hipSuccess) return fail(MOE_ELAUNCH, "%s: launch failed: %s", who, hipGetErrorString(err));
+    return ok();
+}
+
+bool valid_block_size(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
+int64_t max_padded(int64_t P, int64_t E, int64_t bs) { return ((P + E * (bs - 1) + bs - 1) / bs) * bs; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_abi_version(void) { return 1; }
+
+int64_t moe_align_max_padded(int64_t num_pairs, int32_t num_experts, int32_t block_size) {
+    if (num_pairs < 0 || num_experts < 1 || block_size < 1) return -1;
+    return max_padded(num_pairs, num_experts, block_size);
+}
+
+int64_t moe_align_workspace_bytes(int64_t num_pairs, int32_t num_experts) {
+    if (num_pairs < 0 || num_experts < 1) return -1;
+    return static_cast<int64_t>(moe::align_num_chunks(num_pairs)) * num_experts * 4;
+}
+
+moe_status moe_check_group_arrays(int32_t num_experts, const int64_t* lens, const char* const* names,
+                                  int32_t n_arrays, const int32_t* offsets, int64_t offsets_len) {
+    const char* who = "moe_check_group_arrays";
+    REQUIRE(num_experts >= 0, "%s: num_experts %d is negative", who, num_experts);
+    REQUIRE(n_arrays >= 0 && (n_arrays == 0 || (lens && names)), "%s: per-expert arrays not given", who);
+    if (offsets_len != static_cast<int64_t>(num_experts) + 1)
+        return fail(MOE_EINVAL, "expert_offsets len %lld != num_experts+1 %lld", static_cast<long long>(offsets_len),
+                    static_cast<long long>(num_experts) + 1);
+    for (int i = 0; i < n_arrays; ++i)
+        if (lens[i] != num_experts)
+            return fail(MOE_EINVAL, "%s len %lld != num_experts %d", names[i] ? names[i] : "?",
+                        static_cast<long long>(lens[i]), num_experts);
+    REQUIRE(offsets != nullptr, "%s: offsets is NULL", who);
+    if (offsets[0] < 0) return fail(MOE_EINVAL, "expert_offsets[0] = %d is negative", offsets[0]);
+    for (int64_t i = 0; i + 1 < offsets_len; ++i)
+        if (offsets[i + 1] < offsets[i])
+            return fail(MOE_EINVAL,
+                        "expert_offsets is not non-decreasing (%d then %d): a group would have a negative row count",
+                        offsets[i], offsets[i + 1]);
+    return ok();
+}
+
+moe_status moe_lora_pack_tables(const int32_t* ids, const uint64_t* a, const uint64_t* b, const float* s,
+                                int32_t n, uint64_t* a_out, uint64_t* b_out, float* s_out, int32_t cap,
+                                int32_t* n_tab) {
+    const char* who = "moe_lora_pack_tables";
+    REQUIRE(n_tab != nullptr, "%s: n_tab is NULL", who);
+    REQUIRE(n >= 0, "%s: n %d is negative", who, n);
+    if (n == 0) {
+        *n_tab = 0;
+        return ok();
+    }
+    REQUIRE(ids && a && b && s, "%s: an input array is NULL", who);
+    int32_t mx = -1;
+    for (int i = 0; i < n; ++i) {
+        REQUIRE(ids[i] >= 0 && ids[i] <= 65535, "%s: ids[%d] = %d is not a u16 expert id", who, i, ids[i]);
+        mx = ids[i] > mx ? ids[i] : mx;
+    }
+    const int32_t len = mx + 1;
+    REQUIRE(len <= cap, "%s: table length %d exceeds cap %d", who, len, cap);
+    REQUIRE(a_out && b_out && s_out, "%s: an output array is NULL", who);
+    for (int i = 0; i < len; ++i) { a_out[i] = 0; b_out[i] = 0; s_out[i] = 0.0f; }
+    for (int i = 0; i < n; ++i) { a_out[ids[i]] = a[i]; b_out[ids[i]] = b[i]; s_out[ids[i]] = s[i]; }
+    *n_tab = len;
+    return ok();
+}
+
+int64_t moe_lora_window_tiles(int64_t row_offset, int64_t row_end) {
+    const int64_t n = row_end > row_offset ? row_end - row_offset : 0;
+    const int64_t t = (n + 63) / 64;
+    return t < 1 ? 1 : t;
+}
+
+int64_t moe_lora_windows(int64_t total_rows, int64_t cap, int64_t* starts, int64_t* ends, int64_t max_windows) {
+    if (cap <= 0 || total_rows < 0) return -1;
+    int64_t n = 0;
+    for (int64_t s0 = 0; s0 < total_rows; s0 += cap, ++n) {
+        if (n < max_windows && starts && ends) {
+            starts[n] = s0;
+            ends[n] = s0 + cap < total_rows ? s0 + cap : total_rows;
+        }
+    }
+    return n;
+}
+
+moe_status moe_route(const float* logits, int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                     int32_t renormalize, int32_t* topk_ids, float* topk_w, moe_stream stream) {
+    const char* who = "moe_route";
+    REQUIRE(num_tokens >= 0, "%s: num_tokens %d is negative", who, num_tokens);
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256)
+        return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(top_k >= 1 && top_k <= num_experts, "%s: top_k %d not in [1, num_experts=%d]", who, top_k,
+            num_experts);
+    if (num_tokens == 0) return ok();
+    REQUIRE_PTR(who, logits);
+    REQUIRE_PTR(who, topk_ids);
+    REQUIRE_PTR(who, topk_w);
+    return launched(who, moe::launch_route(logits, num_tokens, num_experts, top_k, renormalize ? 1 : 0, topk_ids,
+                                           topk_w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_experts, int32_t block_size,
+                     int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                     int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, void* workspace,
+                     int64_t workspace_bytes, moe_stream stream) {
+    const char* who = "moe_align";
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs %lld out of range", who,
+            static_cast<long long>(num_pairs));
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256)
+        return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d exceeds MAX_NUM_EXPERTS=256", who, num_experts);
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    const int64_t need = max_padded(num_pairs, num_experts, block_size);
+    REQUIRE(max_pad >= need, "%s: max_pad %lld < required %lld", who, static_cast<long long>(max_pad),
+            static_cast<long long>(need));
+    REQUIRE(max_pad % block_size == 0, "%s: max_pad %lld is not a multiple of block_size %d", who,
+            static_cast<long long>(max_pad), block_size);
+    REQUIRE(max_pad < INT32_MAX, "%s: max_pad too large", who);
+    const int64_t ws_need = moe_align_workspace_bytes(num_pairs, num_experts);
+    REQUIRE(workspace_bytes >= ws_need, "%s: workspace_bytes %lld < required %lld", who,
+            static_cast<long long>(workspace_bytes), static_cast<long long>(ws_need));
+    if (num_pairs > 0) {
+        REQUIRE_PTR(who, topk_ids);
+        REQUIRE_PTR(who, inv_sorted);
+    }
+    REQUIRE_PTR(who, counts);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, expert_ids);
+    REQUIRE_PTR(who, total_padded);
+    REQUIRE_PTR(who, workspace);
+    return launched(who, moe::launch_align(topk_ids, static_cast<int>(num_pairs), num_experts, block_size, counts,
+                                           expert_offsets, sorted_ids, expert_ids, total_padded, inv_sorted,
+                                           static_cast<int>(max_pad), static_cast<int32_t*>(workspace),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0, const moe_weight* w1,
+                            uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
+                            const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
+                            int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
+                            moe_stream stream) {
+    const char* who = "moe_grouped_gemm";
+    REQUIRE(op == MOE_OP_GATE_UP_SILU || op == MOE_OP_DOWN, "%s: unknown op %d", who, op);
+    const bool gate_up = op == MOE_OP_GATE_UP_SILU;
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
+    REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
+    REQUIRE(num_pairs % top_k == 0, "%s: num_pairs %lld is not a multiple of top_k %d", who,
+            static_cast<long long>(num_pairs), top_k);
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    REQUIRE(n >= 8 && n % 8 == 0, "%s: n %d must be a positive multiple of 8", who, n);
+    REQUIRE(k >= 8 && k % 8 == 0, "%s: k %d must be a positive multiple of 8", who, k);
+    REQUIRE(max_pad >= max_padded(num_pairs, num_experts, block_size) && max_pad % block_size == 0 &&
+                max_pad < INT32_MAX,
+            "%s: max_pad %lld must be >= %lld and a multiple of block_size", who, static_cast<long long>(max_pad),
+            static_cast<long long>(max_padded(num_pairs, num_experts, block_size)));
+    REQUIRE(w0 != nullptr, "%s: w0 is NULL", who);
+    if (gate_up) REQUIRE(w1 != nullptr, "%s: MOE_OP_GATE_UP_SILU needs w1 (up)", who);
+    else REQUIRE(w1 == nullptr, "%s: MOE_OP_DOWN takes no w1", who);
+    REQUIRE(w0->type == MOE_W_BF16 || w0->type == MOE_W_INT4_GPTQ, "%s: w0 has unknown type %d", who, w0->type);
+    if (w1) REQUIRE(w1->type == w0->type, "%s: w0 and w1 have different types", who);
+    if (num_pairs == 0) return ok();
+    REQUIRE_PTR(who, a);
+    REQUIRE_PTR(who, c);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, w0->data);
+    if (w1) REQUIRE_PTR(who, w1->data);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int P = static_cast<int>(num_pairs);
+    if (w0->type == MOE_W_BF16) {
+        REQUIRE_PTR(who, expert_offsets);
+        return launched(who, moe::launch_gemm_bf16(gate_up, a, static_cast<const uint16_t*>(w0->data),
+                                                   w1 ? static_cast<const uint16_t*>(w1->data) : nullptr, c,
+                                                   sorted_ids, expert_offsets, P, top_k, num_experts, n, k,
+                                                   static_cast<int>(max_pad), s));
+    }
+    const int G = w0->group_size;
+    REQUIRE(G == 32 || G == 64 || G == 128 || G == 256, "%s: group_size %d not in {32,64,128,256}", who, G);
+    if (w1) REQUIRE(w1->group_size == G, "%s: w0 and w1 group sizes differ", who);
+    REQUIRE(k % G == 0, "%s: k %d is not a multiple of group_size %d", who, k, G);
+    REQUIRE(n % 64 == 0, "%s: int4 weights need n %% 64 == 0 (n = %d)", who, n);
+    REQUIRE_PTR(who, expert_ids);
+    REQUIRE_PTR(who, w0->scales);
+    REQUIRE_PTR(who, w0->qzeros);
+    if (w1) {
+        REQUIRE_PTR(who, w1->scales);
+        REQUIRE_PTR(who, w1->qzeros);
+    }
+    return launched(who, moe::launch_gemm_int4(
+                             gate_up, a, static_cast<const int32_t*>(w0->data), w0->scales, w0->qzeros,
+                             w1 ? static_cast<const int32_t*>(w1->data) : nullptr, w1 ? w1->scales : nullptr,
+                             w1 ? w1->qzeros : nullptr, G, c, sorted_ids, expert_ids, P, top_k, num_experts, n, k,
+                             block_size, static_cast<int>(max_pad), s));
+}
+
+moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_table, const uint64_t* b_table,
+                         const float* scale_table, int32_t n_tab, int32_t k_in, int32_t n_out, int32_t max_rank,
+                         const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
+                         int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
+                         int64_t row_offset, int64_t row_end, int64_t max_pad, moe_stream stream) {
+    const char* who = "moe_lora_fold";
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(n_tab >= 0 && n_tab <= num_experts, "%s: n_tab %d not in [0, num_experts=%d]", who, n_tab,
+            num_experts);
+    REQUIRE(k_in >= 8 && k_in % 8 == 0, "%s: k_in %d must be a positive multiple of 8", who, k_in);
+    REQUIRE(n_out >= 8 && n_out % 8 == 0, "%s: n_out %d must be a positive multiple of 8", who, n_out);
+    REQUIRE(max_rank >= 32 && max_rank <= 128 && max_rank % 32 == 0, "%s: max_rank %d not in {32,64,96,128}", who,
+            max_rank);
+    REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX && num_pairs % top_k == 0, "%s: bad num_pairs %lld", who,
+            static_cast<long long>(num_pairs));
+    REQUIRE(max_pad >= 0 && max_pad < INT32_MAX, "%s: bad max_pad", who);
+    REQUIRE(row_offset >= 0 && row_end <= max_pad, "%s: window [%lld, %lld) outside [0, max_pad=%lld)", who,
+            static_cast<long long>(row_offset), static_cast<long long>(row_end), static_cast<long long>(max_pad));
+    REQUIRE(cap >= row_end - row_offset, "%s: cap %lld < window rows %lld", who, static_cast<long long>(cap),
+            static_cast<long long>(row_end - row_offset));
+    if (row_end <= row_offset || n_tab == 0 || num_pairs == 0) return ok();
+    REQUIRE_PTR(who, x);
+    REQUIRE_PTR(who, base);
+    REQUIRE_PTR(who, a_table);
+    REQUIRE_PTR(who, b_table);
+    REQUIRE_PTR(who, scale_table);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, xa);
+    if (row_adapter) REQUIRE_PTR(who, row_adapter);
+    return launched(who, moe::launch_lora_fold(x, base, a_table, b_table, scale_table, n_tab, k_in, n_out, max_rank,
+                                               expert_offsets, num_experts, sorted_ids, static_cast<int>(num_pairs),
+                                               top_k, row_adapter, xa, row_offset, row_end,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine(const uint16_t* ys, const int32_t* inv_sorted, const float* topk_w, uint16_t* out,
+                       int32_t num_tokens, int32_t top_k, int32_t hidden, int64_t ys_rows, moe_stream stream) {
+    const char* who = "moe_combine";
+    REQUIRE(num_tokens >= 0, "%s: num_tokens %d is negative", who, num_tokens);
+    REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
+    REQUIRE(hidden >= 8 && hidden % 8 == 0, "%s: hidden %d must be a positive multiple of 8", who, hidden);
+    REQUIRE(ys_rows >= 0, "%s: ys_rows is negative", who);
+    if (num_tokens == 0) return ok();
+    REQUIRE_PTR(who, ys);
+    REQUIRE_PTR(who, topk_w);
+    REQUIRE_PTR(who, out);
+    if (inv_sorted) REQUIRE_PTR(who, inv_sorted);
+    else REQUIRE(ys_rows >= static_cast<int64_t>(num_tokens) * top_k,
+                 "%s: slot-major combine needs ys_rows >= num_tokens*top_k", who);
+    return launched(who, moe::launch_combine(ys, inv_sorted, topk_w, out, num_tokens, top_k, hidden, ys_rows,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+// Grouped expert GEMM with GPTQ int4 weights (stacked raw GPTQ layout of ferrum-kernels
+// triton_fused_moe.rs: qweight [E,K/8,N] i32, scales [E,K/G,N] fp16, qzeros [E,K/G,N/8]),
+// one launch for all experts.  Built for weight streaming (decode: a block holds a few
+// real rows, so every weight byte is used by at most a handful of rows).
+//
+// Work unit: one workgroup = one 16-row tile of sorted rows (one expert, from expert_ids)
+// x 64 output columns; its 4 waves split the K groups and add their partial sums in LDS.
+//
+// Dequantisation without per-weight float work.  A qweight word holds 8 consecutive k of
+// one column; OR-ing nibble pairs into bf16 0x4300 (= 128.0) gives the exact bf16 values
+// 128+q in two ALU ops per pair, so the MFMA (16x16x32 bf16, fp32 accumulate) computes
+// acc = sum_k x[k]*(128+q[k]) over one quantisation group.  With the group's scale s
+// and zero z fixed per column, the group contributes
+//     s * sum_k x[k]*(q[k]-z) = s * (acc - (128+z) * sum_k x[k]),
+// and sum_k x[k] comes from one more MFMA against a ones matrix.  The pair trick takes
+// nibbles (0,4),(1,5),(2,6),(3,7) of a word, so the x fragment is permuted to the same
+// k order; a sum over k does not depend on the order.
+// Loads: each lane reads 16 B of qweight = the same k-octet of 4 consecutive columns, one
+// column per MFMA, so a wave reads 256 contiguous bytes per k-octet row; the next
+// group's loads are issued before the current group's MFMAs.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace moe {
+namespace {
+
+constexpr int NT = 256;
+constexpr int NCOL = 64;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// x fragment k order (k0..k7) -> (k0,k4,k1,k5,k2,k6,k3,k7), matching the nibble pairs.
+__device__ __forceinline__ u32x4 permute_k(u32x4 a) {
+    u32x4 r;
+    r[0] = (a[0] & 0xffffu) | (a[2] << 16);
+    r[1] = (a[0] >> 16) | (a[2] & 0xffff0000u);
+    r[2] = (a[1] & 0xffffu) | (a[3] << 16);
+    r[3] = (a[1] >> 16) | (a[3] & 0xffff0000u);
+    return r;
+}
+
+// One qweight word (8 nibbles of consecutive k) -> bf16 (128+q) in the permuted k order.
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w) {
+    u32x4 r;
+    r[0] = (w & 0x000f000fu) | 0x43004300u;
+    r[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
+    r[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
+    r[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
+    return r;
+}
+
+// Registers of one quantisation group for one lane (STEPS = G/32 MFMA k-steps).
+template <int NP, int STEPS>
+struct GroupRegs {
+    u32x4 q[NP][STEPS];  // qweight: 16 B = 4 columns x one k-octet, per step
+    u32x4 a[STEPS];      // x fragment (8 bf16) per step
+    uint2 s[NP];         // 4 fp16 scales
+    uint32_t z[NP];      // qzeros word holding the 4 zero points
+};
+
+template <bool GATE_UP, int STEPS>
+__global__ __launch_bounds__(NT) void gemm_int4_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ qw0, const uint16_t* __restrict__ sc0,
+    const int32_t* __restrict__ qz0, const int32_t* __restrict__ qw1, const uint16_t* __restrict__ sc1,
+    const int32_t* __restrict__ qz1, uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ expert_ids, int P, int top_k, int E, int N, int K, int bs, int max_pad) {
+    constexpr int NP = GATE_UP ? 2 : 1;
+    constexpr int G = STEPS * 32;
+    __shared__ int s_row[16];
+    __shared__ int s_any;
+    __shared__ float red[4][NP][4][64][4];  // [wave][proj][v][lane][j]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * 16;
+    const int n0 = blockIdx.y * NCOL;
+    const int e = expert_ids[r0 / bs];
+    if (e < 0 || e >= E) return;
+    if (tid == 0) s_any = 0;
+    __syncthreads();
+    if (tid < 16) {
+        const int r = r0 + tid;
+        int src = -1;
+        if (r < max_pad) {
+            const int p = sorted_ids[r];
+            if (p >= 0 && p < P) src = GATE_UP ? p / top_k : r;
+        }
+        s_row[tid] = src;
+        if (src >= 0) atomicOr(&s_any, 1);
+    }
+    __syncthreads();
+    if (!s_any) return;
+
+    // this wave's quantisation groups (split-K over the 4 waves)
+    const int ngroups = K / G;
+    const int per = (ngroups + 3) / 4;
+    const int g_begin = wave * per;
+    const int g_end = min(ngroups, g_begin + per);
+
+    const int m = lane & 15, kq = lane >> 4;  // A fragment row; k-octet within a k32 step
+    const int arow = s_row[m];
+    const uint16_t* a_ptr = arow >= 0 ? A + static_cast<size_t>(arow) * K + kq * 8 : nullptr;
+    const int ncol = n0 + 4 * m;              // first of this lane's 4 columns
+    const int zshift = 16 * (m & 1);          // nibble of column ncol inside its qzeros word
+
+    const int32_t* qw[NP];
+    const uint16_t* sc[NP];
+    const int32_t* qz[NP];
+    qw[0] = qw0 + static_cast<size_t>(e) * (K / 8) * N;
+    sc[0] = sc0 + static_cast<size_t>(e) * (K / G) * N;
+    qz[0] = qz0 + static_cast<size_t>(e) * (K / G) * (N / 8);
+    if (GATE_UP) {
+        qw[NP - 1] = qw1 + static_cast<size_t>(e) * (K / 8) * N;
+        sc[NP - 1] = sc1 + static_cast<size_t>(e) * (K / G) * N;
+        qz[NP - 1] = qz1 + static_cast<size_t>(e) * (K / G) * (N / 8);
+    }
+
+    auto load_group = [&](int g, GroupRegs<NP, STEPS>& R) {
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int kb = g * G + st * 32;
+            R.a[st] = a_ptr ? *reinterpret_cast<const u32x4*>(a_ptr + kb) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                R.q[p][st] = *reinterpret_cast<const u32x4*>(qw[p] + static_cast<size_t>(kb / 8 + kq) * N + ncol);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            R.s[p] = *reinterpret_cast<const uint2*>(sc[p] + static_cast<size_t>(g) * N + ncol);
+            R.z[p] = static_cast<uint32_t>(qz[p][static_cast<size_t>(g) * (N / 8) + ncol / 8]);
+        }
+    };
+
+    f32x4 out[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[p][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+    GroupRegs<NP, STEPS> nxt;
+    if (g_begin < g_end) load_group(g_begin, nxt);
+    for (int g = g_begin; g < g_end; ++g) {
+        const GroupRegs<NP, STEPS> cur = nxt;
+        if (g + 1 < g_end) load_group(g + 1, nxt);
+        f32x4 acc[NP][4], accx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[p][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const bf16x8 afr = as_bf16x8(permute_k(cur.a[st]));
+            accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, as_bf16x8(ones), accx, 0, 0, 0);
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[p][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        afr, as_bf16x8(dequant_word(cur.q[p][st][j])), acc[p][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sbits = (j < 2 ? cur.s[p].x : cur.s[p].y) >> (16 * (j & 1));
+                const float s = f16_to_f32(static_cast<uint16_t>(sbits & 0xffffu));
+                const float zz = 128.0f + static_cast<float>((cur.z[p] >> (zshift + 4 * j)) & 0xfu);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) out[p][j][v] = fmaf(s, fmaf(-zz, accx[v], acc[p][j][v]), out[p][j][v]);
+            }
+        }
+    }
+
+    // split-K reduction over the 4 waves, then the epilogue: 256 threads = 16 rows x 16 column quads
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wave][p][v][lane][j] = out[p][j][v];
+    __syncthreads();
+    {
+        const int sl = tid & 63, v = tid >> 6;  // source lane and row-in-quad of the C fragment
+        const int row = 4 * (sl >> 4) + v;
+        if (s_row[row] < 0) return;
+        const int col = n0 + 4 * (sl & 15);
+        float res[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                a0 += red[w][0][v][sl][j];
+                if (GATE_UP) a1 += red[w][NP - 1][v][sl][j];
+            }
+            res[j] = GATE_UP ? a0 / (1.0f + __expf(-a0)) * a1 : a0;
+        }
+        uint2 o;
+        o.x = pack_bf16x2(res[0], res[1]);
+        o.y = pack_bf16x2(res[2], res[3]);
+        *reinterpret_cast<uint2*>(C + static_cast<size_t>(r0 + row) * N + col) = o;
+    }
+}
+
+template <int STEPS>
+void launch_int4_steps(bool gate_up, dim3 grid, hipStream_t s, const uint16_t* a, const int32_t* qw0,
+                       const uint16_t* sc0, const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1,
+                       const int32_t* qz1, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids, int P,
+                       int top_k, int E, int N, int K, int bs, int max_pad) {
+    if (gate_up)
+        gemm_int4_kernel<true, STEPS><<<grid, NT, 0, s>>>(a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids,
+                                                          P, top_k, E, N, K, bs, max_pad);
+    else
+        gemm_int4_kernel<false, STEPS><<<grid, NT, 0, s>>>(a, qw0, sc0, qz0, nullptr, nullptr, nullptr, c,
+                                                           sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_int4(bool gate_up, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
+                            const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1, const int32_t* qz1,
+                            int group_size, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
+                            int P, int top_k, int E, int N, int K, int bs, int max_pad, hipStream_t s) {
+    const dim3 grid(max_pad / 16, N / NCOL);
+    switch (group_size) {
+        case 32: launch_int4_steps<1>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 64: launch_int4_steps<2>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 128: launch_int4_steps<4>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 256: launch_int4_steps<8>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

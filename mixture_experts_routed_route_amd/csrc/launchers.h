@@ -1,0 +1,42 @@
+// Host-side launchers of the gfx950 kernels (internal; the C ABI in api.cpp validates
+// arguments and calls these).  Each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// route.hip
+hipError_t launch_route(const float* logits, int T, int E, int top_k, int renorm, int32_t* ids, float* w,
+                        hipStream_t s);
+
+// align.hip
+int align_num_chunks(int64_t num_pairs);
+hipError_t launch_align(const int32_t* topk_ids, int P, int E, int bs, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* total, int32_t* inv, int max_pad,
+                        int32_t* workspace, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w, uint16_t* out, int T, int k,
+                          int H, int64_t ys_rows, hipStream_t s);
+
+// gemm_bf16.hip
+hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
+                            const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
+                            int K, int max_pad, hipStream_t s);
+
+// gemm_int4.hip
+hipError_t launch_gemm_int4(bool gate_up, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
+                            const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1, const int32_t* qz1,
+                            int group_size, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
+                            int P, int top_k, int E, int N, int K, int bs, int max_pad, hipStream_t s);
+
+// lora_fold.hip
+hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_tab, const uint64_t* b_tab,
+                            const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
+                            const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
+                            const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
+                            hipStream_t s);
+
+}  // namespace moe

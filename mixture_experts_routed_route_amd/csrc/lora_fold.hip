@@ -1,0 +1,195 @@
+// Down-projection LoRA fold on the sorted rows (atlas moe_lora_grouped.rs,
+// moe_lora_grouped_down): for each real row r of an adapted expert e in the window,
+//   xa    = bf16(x[r] A_e^T)                      (shrink, max_rank outputs)
+//   delta = bf16(xa B_e^T)                        (expand, n_out outputs)
+//   base[r] = bf16(fp32(base[r]) + scale_e * fp32(delta))   (in place)
+// Two launches like the page: the shrink writes the bf16 xa scratch at the local row
+// r - row_offset, the expand reads it.  The expert of a row is read on the device from
+// expert_offsets (the row's span), so the grid is fixed by host scalars: a window is cut
+// into 64-row tiles aligned to 16-row boundaries (one 16-row sub-tile per wave; block
+// sizes are multiples of 16, so a sub-tile never straddles two experts' spans), and
+// sub-tiles of unadapted experts, sentinel rows and rows outside the window do nothing.
+// Both stages use 16x16x32 bf16 MFMA with fp32 accumulation.  The expand stages its bf16
+// delta tile in LDS and then updates the base rows with 16-byte coalesced accesses.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace moe {
+namespace {
+
+constexpr int NT = 256;
+constexpr int EXP_COLS = 256;     // expand output columns per workgroup
+constexpr int MAX_RANK_BLOCKS = 8;  // max_rank <= 128
+
+struct SubTile {
+    int e;          // expert of the 16-row sub-tile (-1: nothing to do)
+    int span_end;   // end of that expert's padded span
+};
+
+__device__ __forceinline__ SubTile sub_tile_expert(int sub0, const int32_t* off, int E, int n_tab,
+                                                   const uint64_t* a_tab, const uint64_t* b_tab) {
+    SubTile st{-1, 0};
+    // expert spans are read from device memory: clamp the search to what it can address
+    int lo = 0, hi = E;
+    if (off[0] > sub0 || off[E] <= sub0) return st;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= sub0) lo = mid; else hi = mid;
+    }
+    if (lo >= n_tab || a_tab[lo] == 0 || b_tab[lo] == 0) return st;
+    st.e = lo;
+    st.span_end = off[lo + 1];
+    return st;
+}
+
+// Is sorted row r folded?  (inside the window and the expert span, real, adapter allows)
+__device__ __forceinline__ bool row_active(int64_t r, int64_t row_offset, int64_t row_end, int span_end,
+                                           const int32_t* sorted_ids, int P, int top_k,
+                                           const int32_t* row_adapter) {
+    if (r < row_offset || r >= row_end || r >= span_end) return false;
+    const int p = sorted_ids[r];
+    if (p < 0 || p >= P) return false;
+    if (row_adapter && row_adapter[p / top_k] < 0) return false;
+    return true;
+}
+
+__global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restrict__ x, const uint64_t* a_tab,
+                                                         const uint64_t* b_tab, int n_tab, int k_in, int max_rank,
+                                                         const int32_t* __restrict__ off, int E,
+                                                         const int32_t* __restrict__ sorted_ids, int P, int top_k,
+                                                         const int32_t* __restrict__ row_adapter,
+                                                         uint16_t* __restrict__ xa, int64_t row_offset,
+                                                         int64_t row_end, int64_t base16) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.x) * 64 + wave * 16;
+    if (sub0 >= row_end) return;
+    const SubTile st = sub_tile_expert(static_cast<int>(sub0), off, E, n_tab, a_tab, b_tab);
+    if (st.e < 0) return;
+    const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[st.e]);
+
+    const int m = lane & 15, kq = lane >> 4;
+    const int64_t r = sub0 + m;
+    const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
+    if (__ballot(act) == 0) return;
+    const uint16_t* xr = act ? x + r * k_in + kq * 8 : nullptr;
+    const int nb = max_rank / 16;
+
+    f32x4 acc[MAX_RANK_BLOCKS];
+#pragma unroll
+    for (int j = 0; j < MAX_RANK_BLOCKS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < k_in; k0 += 32) {
+        const bool kin = k0 + kq * 8 < k_in;
+        const u32x4 av = (xr && kin) ? *reinterpret_cast<const u32x4*>(xr + k0) : u32x4{0, 0, 0, 0};
+        const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int j = 0; j < MAX_RANK_BLOCKS; ++j) {
+            if (j < nb) {
+                const uint16_t* bp = Ae + static_cast<int64_t>(j * 16 + m) * k_in + k0 + kq * 8;
+                const u32x4 bv = kin ? *reinterpret_cast<const u32x4*>(bp) : u32x4{0, 0, 0, 0};
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bv), acc[j],
+                                                                 0, 0, 0);
+            }
+        }
+    }
+    // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t rr = sub0 + 4 * kq + v;
+        if (!row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter)) continue;
+        uint16_t* dst = xa + (rr - row_offset) * max_rank;
+#pragma unroll
+        for (int j = 0; j < MAX_RANK_BLOCKS; ++j)
+            if (j < nb) dst[j * 16 + m] = f32_to_bf16(acc[j][v]);
+    }
+}
+
+__global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __restrict__ xa,
+                                                              const uint64_t* a_tab, const uint64_t* b_tab,
+                                                              const float* __restrict__ s_tab, int n_tab,
+                                                              int n_out, int max_rank,
+                                                              const int32_t* __restrict__ off, int E,
+                                                              const int32_t* __restrict__ sorted_ids, int P,
+                                                              int top_k, const int32_t* __restrict__ row_adapter,
+                                                              uint16_t* __restrict__ base, int64_t row_offset,
+                                                              int64_t row_end, int64_t base16) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_delta[4][16][EXP_COLS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.y) * 64 + wave * 16;
+    const int n0 = blockIdx.x * EXP_COLS;
+    if (sub0 >= row_end) return;
+    const SubTile st = sub_tile_expert(static_cast<int>(sub0), off, E, n_tab, a_tab, b_tab);
+    if (st.e < 0) return;
+    const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[st.e]);
+    const float scale = s_tab[st.e];
+
+    const int m = lane & 15, kq = lane >> 4;
+    const int64_t r = sub0 + m;
+    const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
+    if (__ballot(act) == 0) return;
+    const uint16_t* xr = act ? xa + (r - row_offset) * max_rank + kq * 8 : nullptr;
+
+    f32x4 acc[EXP_COLS / 16];
+#pragma unroll
+    for (int c = 0; c < EXP_COLS / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < max_rank; k0 += 32) {
+        const u32x4 av = xr ? *reinterpret_cast<const u32x4*>(xr + k0) : u32x4{0, 0, 0, 0};
+        const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int c = 0; c < EXP_COLS / 16; ++c) {
+            const int n = n0 + c * 16 + m;
+            const u32x4 bv = n < n_out ? *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(n) * max_rank + k0 + kq * 8)
+                                       : u32x4{0, 0, 0, 0};
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bv), acc[c], 0, 0, 0);
+        }
+    }
+    // bf16 delta tile to LDS (rows 4*(lane/16)+v, column 16*c + lane%16)
+#pragma unroll
+    for (int c = 0; c < EXP_COLS / 16; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_delta[wave][4 * kq + v][c * 16 + m] = f32_to_bf16(acc[c][v]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    // coalesced fold: 2 rows x 32 lanes x 8 columns per step
+    for (int it = 0; it < 8; ++it) {
+        const int rl = it * 2 + (lane >> 5);
+        const int64_t rr = sub0 + rl;
+        const int col = (lane & 31) * 8;
+        if (n0 + col >= n_out) continue;
+        if (!row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter)) continue;
+        u32x4* bp = reinterpret_cast<u32x4*>(base + rr * n_out + n0 + col);
+        const u32x4 bv = *bp;
+        const u32x4 dv = *reinterpret_cast<const u32x4*>(&s_delta[wave][rl][col]);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float b_lo = __uint_as_float(bv[i] << 16), b_hi = __uint_as_float(bv[i] & 0xffff0000u);
+            const float d_lo = __uint_as_float(dv[i] << 16), d_hi = __uint_as_float(dv[i] & 0xffff0000u);
+            o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
+        }
+        *bp = o;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_tab, const uint64_t* b_tab,
+                            const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
+                            const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
+                            const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
+                            hipStream_t s) {
+    if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
+    const int64_t base16 = (row_offset / 16) * 16;
+    const int64_t tiles = (row_end - base16 + 63) / 64;
+    lora_shrink_kernel<<<dim3(static_cast<unsigned>(tiles)), NT, 0, s>>>(
+        x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, P, top_k, row_adapter, xa, row_offset,
+        row_end, base16);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid((n_out + EXP_COLS - 1) / EXP_COLS, static_cast<unsigned>(tiles));
+    lora_expand_fold_kernel<<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_out, max_rank, offsets, E,
+                                               sorted_ids, P, top_k, row_adapter, base, row_offset, row_end,
+                                               base16);
+    return hipGetLastError();
+}
+
+}  // namespace moe

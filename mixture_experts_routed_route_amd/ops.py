@@ -1,0 +1,256 @@
+"""PyTorch-facing binding of the C ABI: argument checks and marshalling only.
+
+Every step of the path runs in the HIP library; PyTorch supplies device memory and the
+current stream.  Functions take and return ``torch`` tensors on a HIP device.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple, Union
+
+import torch
+
+from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_W_BF16, MOE_W_INT4_GPTQ, MoeWeight, check, lib)
+
+__all__ = [
+    "Bf16Weight", "GptqWeight", "Routing", "LoraTables", "max_padded", "align_workspace_bytes",
+    "moe_route", "moe_align", "moe_grouped_gemm", "moe_lora_fold", "moe_combine", "pack_lora_tables",
+    "lora_windows", "lora_window_tiles", "check_group_arrays",
+]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a HIP device (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# ----------------------------------------------------------------------------- weights
+@dataclass
+class Bf16Weight:
+    """bf16 expert weights ``[E, N, K]`` (K contiguous)."""
+    w: torch.Tensor
+
+    @property
+    def shape(self) -> Tuple[int, int, int]:
+        return tuple(self.w.shape)
+
+    def struct(self) -> MoeWeight:
+        return MoeWeight(MOE_W_BF16, 0, _dev(self.w, torch.bfloat16, "weight"), None, None)
+
+
+@dataclass
+class GptqWeight:
+    """GPTQ int4: qweight ``[E, K/8, N]`` int32, scales ``[E, K/G, N]`` fp16, qzeros ``[E, K/G, N/8]`` int32."""
+    qweight: torch.Tensor
+    scales: torch.Tensor
+    qzeros: torch.Tensor
+    group_size: int
+
+    @property
+    def shape(self) -> Tuple[int, int, int]:
+        E, K8, N = self.qweight.shape
+        return (E, N, K8 * 8)
+
+    def struct(self) -> MoeWeight:
+        return MoeWeight(MOE_W_INT4_GPTQ, int(self.group_size), _dev(self.qweight, torch.int32, "qweight"),
+                         _dev(self.scales, torch.float16, "scales"), _dev(self.qzeros, torch.int32, "qzeros"))
+
+
+Weight = Union[Bf16Weight, GptqWeight]
+
+
+# ----------------------------------------------------------------------------- host helpers
+def max_padded(num_pairs: int, num_experts: int, block_size: int) -> int:
+    v = lib().moe_align_max_padded(num_pairs, num_experts, block_size)
+    if v < 0:
+        raise ValueError("invalid arguments")
+    return int(v)
+
+
+def align_workspace_bytes(num_pairs: int, num_experts: int) -> int:
+    return int(lib().moe_align_workspace_bytes(num_pairs, num_experts))
+
+
+def check_group_arrays(num_experts: int, per_expert: Sequence[Tuple[str, int]], offsets: Sequence[int]) -> None:
+    n = len(per_expert)
+    lens = (ctypes.c_int64 * max(n, 1))(*[int(l) for _, l in per_expert])
+    names = (ctypes.c_char_p * max(n, 1))(*[s.encode() for s, _ in per_expert])
+    off = (ctypes.c_int32 * max(len(offsets), 1))(*[int(o) for o in offsets])
+    check(lib().moe_check_group_arrays(num_experts, lens, names, n, off, len(offsets)))
+
+
+def lora_window_tiles(row_offset: int, row_end: int) -> int:
+    return int(lib().moe_lora_window_tiles(row_offset, row_end))
+
+
+def lora_windows(total_rows: int, cap: int) -> List[Tuple[int, int]]:
+    n = lib().moe_lora_windows(total_rows, cap, None, None, 0)
+    if n < 0:
+        raise ValueError("grouped LoRA scratch capacity must be nonzero")
+    s = (ctypes.c_int64 * max(n, 1))()
+    e = (ctypes.c_int64 * max(n, 1))()
+    lib().moe_lora_windows(total_rows, cap, s, e, n)
+    return [(int(s[i]), int(e[i])) for i in range(n)]
+
+
+# ----------------------------------------------------------------------------- A1 route
+def moe_route(logits: torch.Tensor, top_k: int, renormalize: bool = True,
+              topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None):
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    check(lib().moe_route(_dev(logits, torch.float32, "logits"), T, E, top_k, int(bool(renormalize)),
+                          _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
+                          _stream(logits)))
+    return topk_ids, topk_w
+
+
+# ----------------------------------------------------------------------------- A2 align
+@dataclass
+class Routing:
+    """Outputs of moe_align (device tensors) plus the scalars that describe them."""
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_ids: torch.Tensor
+    expert_ids: torch.Tensor
+    total_padded: torch.Tensor
+    inv_sorted: torch.Tensor
+    workspace: torch.Tensor
+    num_pairs: int
+    top_k: int
+    num_experts: int
+    block_size: int
+    max_pad: int
+
+    @staticmethod
+    def allocate(num_pairs: int, top_k: int, num_experts: int, block_size: int, device,
+                 max_pad: Optional[int] = None) -> "Routing":
+        mp = max_padded(num_pairs, num_experts, block_size) if max_pad is None else int(max_pad)
+        i32 = dict(dtype=torch.int32, device=device)
+        wsb = align_workspace_bytes(num_pairs, num_experts)
+        return Routing(torch.empty(num_experts, **i32), torch.empty(num_experts + 1, **i32),
+                       torch.empty(mp, **i32), torch.empty(mp // block_size, **i32), torch.empty(1, **i32),
+                       torch.empty(max(num_pairs, 1), **i32), torch.empty(max(wsb // 4, 1), **i32),
+                       num_pairs, top_k, num_experts, block_size, mp)
+
+
+def moe_align(topk_ids: torch.Tensor, num_experts: int, block_size: int, max_pad: Optional[int] = None,
+              out: Optional[Routing] = None) -> Routing:
+    P = topk_ids.numel()
+    top_k = topk_ids.shape[-1] if topk_ids.dim() == 2 else 1
+    r = out if out is not None else Routing.allocate(P, top_k, num_experts, block_size, topk_ids.device, max_pad)
+    if r.num_pairs != P or r.num_experts != num_experts or r.block_size != block_size:
+        raise ValueError("preallocated Routing does not match the call")
+    check(lib().moe_align(_dev(topk_ids, torch.int32, "topk_ids"), P, num_experts, block_size,
+                          _dev(r.counts, torch.int32, "counts"), _dev(r.offsets, torch.int32, "offsets"),
+                          _dev(r.sorted_ids, torch.int32, "sorted_ids"),
+                          _dev(r.expert_ids, torch.int32, "expert_ids"),
+                          _dev(r.total_padded, torch.int32, "total_padded"),
+                          _dev(r.inv_sorted, torch.int32, "inv_sorted"), r.max_pad,
+                          _dev(r.workspace, torch.int32, "workspace"), r.workspace.numel() * 4,
+                          _stream(topk_ids)))
+    return r
+
+
+# ----------------------------------------------------------------------------- A3 / A4 grouped GEMM
+def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight], routing: Routing,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """op = MOE_OP_GATE_UP_SILU (a = x [T, K], w0 = gate, w1 = up) or MOE_OP_DOWN (a = Hs [max_pad, K])."""
+    E, N, K = w0.shape
+    if out is None:
+        out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=a.device)
+    s0 = w0.struct()
+    s1 = w1.struct() if w1 is not None else None
+    check(lib().moe_grouped_gemm(op, _dev(a, torch.bfloat16, "a"), ctypes.byref(s0),
+                                 ctypes.byref(s1) if s1 is not None else None, _dev(out, torch.bfloat16, "out"),
+                                 _dev(routing.sorted_ids, torch.int32, "sorted_ids"),
+                                 _dev(routing.expert_ids, torch.int32, "expert_ids"),
+                                 _dev(routing.offsets, torch.int32, "offsets"), routing.num_pairs, routing.top_k,
+                                 routing.num_experts, N, K, routing.block_size, routing.max_pad, _stream(a)))
+    return out
+
+
+# ----------------------------------------------------------------------------- A5 LoRA fold
+@dataclass
+class LoraTables:
+    """Device tables of one adapter's per-expert down-projection LoRA (atlas MoeExpertRoute)."""
+    a_table: torch.Tensor      # int64 [n_tab] addresses (0 = unadapted)
+    b_table: torch.Tensor
+    scale_table: torch.Tensor  # float32 [n_tab]
+    n_tab: int
+    k_in: int
+    n_out: int
+    max_rank: int
+    keep: List[torch.Tensor] = field(default_factory=list)  # owners of the A/B memory
+
+
+def pack_lora_tables(ids: Sequence[int], a: Sequence[torch.Tensor], b: Sequence[torch.Tensor],
+                     scales: Sequence[float], device) -> Optional[LoraTables]:
+    """A_e bf16 [max_rank, k_in], B_e bf16 [n_out, max_rank] on the device; tables via moe_lora_pack_tables."""
+    n = len(ids)
+    if n == 0:
+        return None
+    for t in list(a) + list(b):
+        _dev(t, torch.bfloat16, "lora weight")
+    cap = max(int(i) for i in ids) + 1
+    ids_c = (ctypes.c_int32 * n)(*[int(i) for i in ids])
+    a_c = (ctypes.c_uint64 * n)(*[t.data_ptr() for t in a])
+    b_c = (ctypes.c_uint64 * n)(*[t.data_ptr() for t in b])
+    s_c = (ctypes.c_float * n)(*[float(s) for s in scales])
+    ao, bo, so = (ctypes.c_uint64 * cap)(), (ctypes.c_uint64 * cap)(), (ctypes.c_float * cap)()
+    n_tab = ctypes.c_int32(0)
+    check(lib().moe_lora_pack_tables(ids_c, a_c, b_c, s_c, n, ao, bo, so, cap, ctypes.byref(n_tab)))
+    k = n_tab.value
+    as_i64 = lambda arr: torch.tensor([int(v) - (1 << 64) if int(v) >= (1 << 63) else int(v) for v in arr[:k]],
+                                      dtype=torch.int64)
+    max_rank, k_in = a[0].shape
+    n_out = b[0].shape[0]
+    return LoraTables(as_i64(ao).to(device), as_i64(bo).to(device),
+                      torch.tensor(list(so[:k]), dtype=torch.float32).to(device), k, k_in, n_out, max_rank,
+                      list(a) + list(b))
+
+
+def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routing: Routing,
+                  row_adapter: Optional[torch.Tensor] = None, xa: Optional[torch.Tensor] = None,
+                  row_offset: int = 0, row_end: Optional[int] = None) -> torch.Tensor:
+    """Fold in place into ``base`` over the window [row_offset, row_end) of the sorted rows."""
+    if row_end is None:
+        row_end = routing.max_pad
+    if xa is None:
+        xa = torch.empty((max(row_end - row_offset, 1), tables.max_rank), dtype=torch.bfloat16, device=x.device)
+    check(lib().moe_lora_fold(
+        _dev(x, torch.bfloat16, "x"), _dev(base, torch.bfloat16, "base"), _dev(tables.a_table, torch.int64, "a_table"),
+        _dev(tables.b_table, torch.int64, "b_table"), _dev(tables.scale_table, torch.float32, "scale_table"),
+        tables.n_tab, tables.k_in, tables.n_out, tables.max_rank, _dev(routing.offsets, torch.int32, "offsets"),
+        routing.num_experts, _dev(routing.sorted_ids, torch.int32, "sorted_ids"), routing.num_pairs, routing.top_k,
+        _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
+        _dev(xa, torch.bfloat16, "xa"), xa.shape[0], row_offset, row_end, routing.max_pad, _stream(x)))
+    return base
+
+
+# ----------------------------------------------------------------------------- A6 combine
+def moe_combine(ys: torch.Tensor, inv_sorted: Optional[torch.Tensor], topk_w: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, k = topk_w.shape
+    H = ys.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=ys.device)
+    check(lib().moe_combine(_dev(ys, torch.bfloat16, "ys"),
+                            _dev(inv_sorted, torch.int32, "inv_sorted") if inv_sorted is not None else None,
+                            _dev(topk_w, torch.float32, "topk_w"), _dev(out, torch.bfloat16, "out"), T, k, H,
+                            ys.shape[0], _stream(ys)))
+    return out

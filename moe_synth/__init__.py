@@ -41,7 +41,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-__all__ = ["MoeConfig", "CONFIGS", "make_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32"]
+__all__ = ["MoeConfig", "CONFIGS", "make_inputs", "make_router_logits", "f32_to_bf16_bits", "bf16_bits_to_f32"]
 
 
 @dataclass(frozen=True)
@@ -166,6 +166,12 @@ def make_logits(cfg: MoeConfig, rng: np.random.Generator) -> np.ndarray:
     elif cfg.logits != "normal":
         raise ValueError(cfg.logits)
     return np.ascontiguousarray(z.astype(np.float32))
+
+
+def make_router_logits(cfg: MoeConfig, seed: Optional[int] = None) -> np.ndarray:
+    """Only the router logits of ``make_inputs`` (same stream, same values)."""
+    ss = np.random.SeedSequence(cfg.seed if seed is None else seed).spawn(6)[0]
+    return make_logits(cfg, _rng(ss))
 
 
 def make_inputs(cfg: MoeConfig, seed: Optional[int] = None, threads: int = 8) -> Dict[str, object]:

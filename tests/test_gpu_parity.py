@@ -1,0 +1,372 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Bars: routing and alignment bit-exact; GEMM / fold / combine outputs within 2e-2
+relative error per row (and over the whole tensor) against the fp64 oracle; sentinel
+and padding rows never written.  Small workloads are checked on every row; the full
+workloads are checked on every routing/alignment output and on sampled token rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_synth import CONFIGS, MoeConfig, make_inputs, make_router_logits, f32_to_bf16_bits
+from _util import (assert_close_rows, bf16_dev, bf16_host, bf16_ulp_diff, bits_host, row_rel_err, to_dev)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+CANARY = 0x7FC1  # a quiet-NaN bf16 pattern no kernel ever writes
+
+
+def note(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import mixture_experts_routed_route_amd as m
+    m.lib()  # raises if the library is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def ops():
+    import mixture_experts_routed_route_amd as m
+    return m
+
+
+# small workloads: several tiles, ragged K and N tails, skew, empty experts
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "mixtral_small": MoeConfig("mixtral_small", T=300, H=520, I=904, E=8, top_k=2, block_size=64, seed=1),
+    "finegrained_small": MoeConfig("finegrained_small", T=700, H=256, I=192, E=128, top_k=8, block_size=64,
+                                   logits="zipf", seed=2),
+    "bs32_small": MoeConfig("bs32_small", T=257, H=384, I=136, E=16, top_k=4, block_size=32, seed=3),
+    "bs128_small": MoeConfig("bs128_small", T=129, H=256, I=256, E=4, top_k=2, block_size=128, seed=4),
+    "lora_small": MoeConfig("lora_small", T=200, H=512, I=256, E=16, top_k=6, block_size=64, lora_rank=16,
+                            lora_max_rank=64, seed=5),
+    "decode_int4": CONFIGS["decode_int4"],
+    "int4_prefill_small": MoeConfig("int4_prefill_small", T=100, H=512, I=256, E=8, top_k=2, block_size=32,
+                                    weights="int4_gptq", group_size=128, seed=6),
+    "int4_g64_small": MoeConfig("int4_g64_small", T=40, H=384, I=192, E=6, top_k=3, block_size=16,
+                                weights="int4_gptq", group_size=64, seed=7),
+}
+
+
+# ----------------------------------------------------------------------------- A1 route
+ROUTE_CASES = [(name, cfg) for name, cfg in CONFIGS.items()] + [
+    ("E256_k8", MoeConfig("E256", T=1000, H=8, I=8, E=256, top_k=8, block_size=64, seed=11)),
+    ("E200_k7", MoeConfig("E200", T=333, H=8, I=8, E=200, top_k=7, block_size=64, seed=12)),
+    ("E1", MoeConfig("E1", T=17, H=8, I=8, E=1, top_k=1, block_size=16, seed=13)),
+    ("k_eq_E", MoeConfig("kE", T=50, H=8, I=8, E=6, top_k=6, block_size=16, seed=14)),
+    ("no_renorm", MoeConfig("nr", T=500, H=8, I=8, E=64, top_k=6, block_size=16, renormalize=False, seed=15)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_bit_exact(dev, name, cfg):
+    note(f"route {name} T={cfg.T} E={cfg.E} k={cfg.top_k}")
+    logits = make_router_logits(cfg)
+    if name == "E256_k8":
+        logits[:40, 7] = logits[:40, 3]           # exact ties
+        logits[40:60] = 0.0                       # all equal
+        logits[60:70, :128] = -0.0
+    ids_ref, w_ref = oracle.route(logits, cfg.top_k, cfg.renormalize)
+    ids, w = ops().moe_route(to_dev(logits), cfg.top_k, cfg.renormalize)
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(ids, ids_ref), f"{(ids != ids_ref).sum()} id mismatches"
+    bad = np.flatnonzero(w.view(np.uint32) != w_ref.view(np.uint32))
+    assert bad.size == 0, f"{bad.size} weight mismatches, first at {bad[:5]}: {w.ravel()[bad[:5]]} vs {w_ref.ravel()[bad[:5]]}"
+
+
+# ----------------------------------------------------------------------------- A2 align
+def _align_dev(ids_host, E, bs, max_pad=None):
+    t = to_dev(np.ascontiguousarray(ids_host, dtype=np.int32))
+    r = ops().moe_align(t, E, bs, max_pad)
+    return {"counts": r.counts.cpu().numpy(), "offsets": r.offsets.cpu().numpy(),
+            "sorted_ids": r.sorted_ids.cpu().numpy(), "expert_ids": r.expert_ids.cpu().numpy(),
+            "total": int(r.total_padded.cpu().item()), "inv": r.inv_sorted.cpu().numpy()[: ids_host.size]}, r
+
+
+def _assert_align_equal(got, ref):
+    for key in ("counts", "offsets", "sorted_ids", "expert_ids", "inv"):
+        a, b = got[key], ref[key]
+        assert a.shape == b.shape and np.array_equal(a, b), f"{key}: {(a != b).sum()} mismatches"
+    assert got["total"] == ref["total"]
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_align_bit_exact_configs(dev, name):
+    cfg = CONFIGS[name]
+    note(f"align {name} P={cfg.P} E={cfg.E} bs={cfg.block_size}")
+    ids, _ = oracle.route(make_router_logits(cfg), cfg.top_k)
+    got, _ = _align_dev(ids, cfg.E, cfg.block_size)
+    _assert_align_equal(got, oracle.align(ids, cfg.E, cfg.block_size))
+
+
+ALIGN_EDGE = [
+    ("one_expert_all", lambda r: np.zeros((5000, 4), np.int32), 8, 64),
+    ("chunk_plus_one", lambda r: r.integers(0, 3, (2049, 1)), 3, 16),
+    ("many_chunks", lambda r: r.integers(0, 5, (50001, 4)), 5, 128),
+    ("E256_bs128", lambda r: r.integers(0, 256, (3000, 8)), 256, 128),
+    ("E256_sparse", lambda r: r.integers(0, 256, (7, 3)), 256, 16),
+    ("invalid_ids", lambda r: r.integers(-3, 11, (999, 3)), 8, 32),
+    ("single_pair", lambda r: np.array([[5]]), 6, 16),
+]
+
+
+@pytest.mark.parametrize("name,make,E,bs", ALIGN_EDGE, ids=[c[0] for c in ALIGN_EDGE])
+def test_align_bit_exact_edges(dev, name, make, E, bs):
+    ids = np.asarray(make(np.random.default_rng(sum(map(ord, name)))), dtype=np.int32)
+    note(f"align edge {name} P={ids.size}")
+    got, _ = _align_dev(ids, E, bs)
+    _assert_align_equal(got, oracle.align(ids, E, bs))
+
+
+def test_align_empty_and_oversized_capacity(dev):
+    ids = np.zeros((0, 2), np.int32)
+    got, _ = _align_dev(ids, 4, 16)
+    ref = oracle.align(ids, 4, 16)
+    _assert_align_equal(got, ref)
+    ids = np.random.default_rng(0).integers(0, 8, (100, 2)).astype(np.int32)
+    big = oracle.max_padded(200, 8, 16) + 5 * 16
+    got, _ = _align_dev(ids, 8, 16, big)
+    _assert_align_equal(got, oracle.align(ids, 8, 16, big))
+
+
+# ----------------------------------------------------------------------------- shared stage setup
+def _routing(cfg, d):
+    ids, w = oracle.route(d["logits"], cfg.top_k, cfg.renormalize)
+    al = oracle.align(ids, cfg.E, cfg.block_size)
+    r = ops().moe_align(to_dev(ids.astype(np.int32)), cfg.E, cfg.block_size)  # bit-exact (tested above)
+    return ids, w, al, r
+
+
+def _weights_dev(d):
+    return ops().MoeLayer.from_arrays(d, "cuda")
+
+
+def _canary(rows, cols):
+    import torch
+    t = torch.full((rows, cols), CANARY, dtype=torch.int16, device="cuda")
+    return t.view(torch.bfloat16)
+
+
+def _real(al, P):
+    return np.flatnonzero(al["sorted_ids"] < P)
+
+
+# ----------------------------------------------------------------------------- A3 / A4 grouped GEMMs
+@pytest.mark.parametrize("name", list(SMALL))
+def test_grouped_gemms_small(dev, name):
+    m = ops()
+    cfg = SMALL[name]
+    note(f"gemm {name}")
+    d = make_inputs(cfg)
+    ids, w, al, r = _routing(cfg, d)
+    layer = _weights_dev(d)
+    P = cfg.P
+    real = _real(al, P)
+    # gate/up + SiLU
+    hs = _canary(r.max_pad, cfg.I)
+    m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, bf16_dev(d["x"]), layer.gate, layer.up, r, out=hs)
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    h_ref = oracle.grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
+    hs_b = bits_host(hs)
+    assert (hs_b[np.setdiff1d(np.arange(r.max_pad), real)] == CANARY).all(), "padding rows of Hs written"
+    assert_close_rows(bf16_host(hs)[real], h_ref[real], TOL, "gate/up")
+    # down, fed with the oracle's own h rounded to bf16 (NaN in every padding row)
+    h_in = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
+    h_in[real] = f32_to_bf16_bits(oracle.round_bf16(h_ref[real]).astype(np.float32))
+    ys = _canary(r.max_pad, cfg.H)
+    m.moe_grouped_gemm(m.MOE_OP_DOWN, bf16_dev(h_in), layer.down, None, r, out=ys)
+    y_ref = oracle.grouped_down(oracle.bf16_bits_to_f64(h_in), wd, al)
+    ys_b = bits_host(ys)
+    assert (ys_b[np.setdiff1d(np.arange(r.max_pad), real)] == CANARY).all(), "padding rows of Ys written"
+    assert_close_rows(bf16_host(ys)[real], y_ref[real], TOL, "down")
+
+
+# ----------------------------------------------------------------------------- A6 combine
+@pytest.mark.parametrize("name", ["tiny", "finegrained_small", "mixtral_small"])
+def test_combine(dev, name):
+    m = ops()
+    cfg = SMALL[name]
+    d = make_inputs(cfg)
+    ids, w, al, r = _routing(cfg, d)
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((r.max_pad, cfg.H)).astype(np.float32)
+    y_bits = f32_to_bf16_bits(y)
+    out = m.moe_combine(bf16_dev(y_bits), r.inv_sorted[: cfg.P], to_dev(w))
+    ref = oracle.combine(oracle.bf16_bits_to_f64(y_bits), al["inv"], w, cfg.T, cfg.top_k)
+    assert_close_rows(bf16_host(out), ref, TOL, "combine")
+    ulp = bf16_ulp_diff(bits_host(out), f32_to_bf16_bits(oracle.round_bf16(ref).astype(np.float32)))
+    assert ulp.max() <= 1 and (ulp == 0).mean() > 0.99
+    # slot-major (no inverse map)
+    out2 = m.moe_combine(bf16_dev(y_bits[: cfg.P]), None, to_dev(w))
+    ref2 = oracle.combine(oracle.bf16_bits_to_f64(y_bits[: cfg.P]), None, w, cfg.T, cfg.top_k)
+    assert_close_rows(bf16_host(out2), ref2, TOL, "combine slot-major")
+    # a dropped pair contributes nothing
+    inv = al["inv"].copy()
+    inv[::3] = -1
+    out3 = m.moe_combine(bf16_dev(y_bits), to_dev(inv), to_dev(w))
+    ref3 = oracle.combine(oracle.bf16_bits_to_f64(y_bits), inv, w, cfg.T, cfg.top_k)
+    assert_close_rows(bf16_host(out3), ref3, TOL, "combine dropped")
+
+
+# ----------------------------------------------------------------------------- A5 LoRA fold
+def _fold_setup(cfg, scale_mult=1.0):
+    d = make_inputs(cfg)
+    if scale_mult != 1.0:
+        d["lora_scale"] = (d["lora_scale"] * scale_mult).astype(np.float32)
+    ids, w, al, r = _routing(cfg, d)
+    P = cfg.P
+    real = _real(al, P)
+    rng = np.random.default_rng(21)
+    x = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
+    x[real] = f32_to_bf16_bits(rng.standard_normal((real.size, cfg.I)).astype(np.float32))
+    base = np.full((r.max_pad, cfg.H), CANARY, np.uint16)
+    base[real] = f32_to_bf16_bits((rng.standard_normal((real.size, cfg.H)) * 0.05).astype(np.float32))
+    return d, al, r, real, x, base
+
+
+@pytest.mark.parametrize("scale_mult", [1.0, 100.0])
+def test_lora_fold_stage(dev, scale_mult):
+    m = ops()
+    cfg = SMALL["lora_small"]
+    d, al, r, real, x, base = _fold_setup(cfg, scale_mult)
+    layer = _weights_dev(d)
+    tabs = oracle.moe_oracle._lora_tables(d)
+    ref = oracle.lora_fold(oracle.bf16_bits_to_f64(base), oracle.bf16_bits_to_f64(x), tabs, al, cfg.top_k)
+    ref_bits = np.full_like(base, CANARY)
+    ref_bits[real] = f32_to_bf16_bits(ref[real].astype(np.float32))
+    got = bf16_dev(base)
+    m.moe_lora_fold(bf16_dev(x), got, layer.lora, r)
+    gb = bits_host(got)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    assert (gb[pad] == CANARY).all(), "padding rows of the base written"
+    ulp = bf16_ulp_diff(gb[real], ref_bits[real])
+    note(f"fold x{scale_mult}: exact {(ulp == 0).mean():.5f}, max ulp {ulp.max()}")
+    assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
+    # unadapted experts (odd ids) are bit-identical to the base
+    changed = np.any(gb != base, axis=1)
+    for rr in np.flatnonzero(changed):
+        e = np.searchsorted(al["offsets"], rr, side="right") - 1
+        assert e % 2 == 0, f"row {rr} of unadapted expert {e} changed"
+    assert changed.sum() > 0
+
+
+def test_lora_fold_windows_bit_identical(dev):
+    m = ops()
+    cfg = SMALL["lora_small"]
+    d, al, r, real, x, base = _fold_setup(cfg)
+    layer = _weights_dev(d)
+    one = bf16_dev(base)
+    m.moe_lora_fold(bf16_dev(x), one, layer.lora, r)
+    for cap in (100, 64, 1000, 17):
+        chunked = bf16_dev(base)
+        import torch
+        xa = torch.empty((cap, layer.lora.max_rank), dtype=torch.bfloat16, device="cuda")
+        for s, e in m.lora_windows(r.max_pad, cap):
+            m.moe_lora_fold(bf16_dev(x), chunked, layer.lora, r, xa=xa, row_offset=s, row_end=e)
+        assert np.array_equal(bits_host(chunked), bits_host(one)), f"cap {cap}"
+
+
+def test_lora_fold_row_adapter(dev):
+    m = ops()
+    cfg = SMALL["lora_small"]
+    d, al, r, real, x, base = _fold_setup(cfg)
+    layer = _weights_dev(d)
+    ra = np.where(np.arange(cfg.T) % 3 == 0, -1, 0).astype(np.int32)
+    tabs = oracle.moe_oracle._lora_tables(d)
+    ref = oracle.lora_fold(oracle.bf16_bits_to_f64(base), oracle.bf16_bits_to_f64(x), tabs, al, cfg.top_k,
+                           row_adapter=ra)
+    got = bf16_dev(base)
+    m.moe_lora_fold(bf16_dev(x), got, layer.lora, r, row_adapter=to_dev(ra))
+    gb = bits_host(got)
+    ulp = bf16_ulp_diff(gb[real], f32_to_bf16_bits(ref[real].astype(np.float32)))
+    assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
+    skipped = [rr for rr in real if ra[al["sorted_ids"][rr] // cfg.top_k] < 0]
+    assert np.array_equal(gb[skipped], base[skipped])
+
+
+# ----------------------------------------------------------------------------- whole layer
+def _layer_run(cfg, d):
+    m = ops()
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    b = layer.plan(cfg.T, "cuda")
+    out = layer.forward(to_dev(d["logits"]), bf16_dev(d["x"]), b)
+    return layer, b, out
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_end_to_end_small(dev, name):
+    cfg = SMALL[name]
+    note(f"layer {name}")
+    d = make_inputs(cfg)
+    layer, b, out = _layer_run(cfg, d)
+    ref = oracle.moe_layer(d)
+    assert np.array_equal(b.ids.cpu().numpy(), ref["ids"])
+    assert_close_rows(bf16_host(out), ref["out"], TOL, f"layer {name}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_layer_full_size_sampled(dev, name):
+    cfg = CONFIGS[name]
+    note(f"layer full {name}")
+    d = make_inputs(cfg)
+    layer, b, out = _layer_run(cfg, d)
+    ids, w = oracle.route(d["logits"], cfg.top_k, cfg.renormalize)
+    assert np.array_equal(b.ids.cpu().numpy(), ids)
+    assert np.array_equal(b.w.cpu().numpy().view(np.uint32), w.view(np.uint32))
+    al = oracle.align(ids, cfg.E, cfg.block_size)
+    assert np.array_equal(b.routing.sorted_ids.cpu().numpy(), al["sorted_ids"])
+    # sampled tokens: first, last, and a spread in between (and the busiest expert's rows)
+    rng = np.random.default_rng(0)
+    n = min(cfg.T, 24)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n, replace=False)]))
+    ref = oracle.moe_tokens(d, toks, (ids, w))
+    got = bf16_host(out)[toks]
+    e1, e2 = assert_close_rows(got, ref, TOL, f"layer full {name}")
+    note(f"  worst row rel err {e1:.2e}, tensor {e2:.2e}")
+
+
+def test_layer_graph_replay_matches_eager(dev):
+    import torch
+    m = ops()
+    cfg = SMALL["lora_small"]
+    d = make_inputs(cfg)
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    b = layer.plan(cfg.T, "cuda")
+    logits, x = to_dev(d["logits"]), bf16_dev(d["x"])
+    eager = bits_host(layer.forward(logits, x, b)).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        layer.forward(logits, x, b)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.forward(logits, x, b)
+    torch.cuda.synchronize()
+    for i in range(3):
+        b.out.zero_()
+        b.ys.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(b.out), eager), f"replay {i} differs from eager"
+        layer.forward(logits, x, b)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_layer_deterministic(dev):
+    cfg = SMALL["finegrained_small"]
+    d = make_inputs(cfg)
+    _, _, o1 = _layer_run(cfg, d)
+    _, _, o2 = _layer_run(cfg, d)
+    assert np.array_equal(bits_host(o1), bits_host(o2))
