@@ -27,10 +27,48 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
+
+
 def gemm_flops(cfg, op: str) -> float:
     """Algorithmic FLOPs of one grouped GEMM launch: 2*K*N per real (token, expert) pair and projection."""
     per_pair = {"gate_up": 2 * 2 * cfg.H * cfg.I, "down": 2 * cfg.H * cfg.I}[op]
     return float(per_pair) * cfg.P
+
+
+def expert_weight_bytes(cfg, op: str) -> float:
+    """Bytes of one expert's weights read by one launch (gate+up, or down)."""
+    nproj = 2 if op == "gate_up" else 1
+    if cfg.weights == "bf16":
+        return float(nproj * cfg.H * cfg.I * 2)
+    G = cfg.group_size
+    K, N = (cfg.H, cfg.I) if op == "gate_up" else (cfg.I, cfg.H)
+    per = K // 8 * N * 4 + K // G * N * 2 + K // G * N // 8 * 4   # qweight + fp16 scales + qzeros
+    return float(nproj * per)
+
+
+def gemm_bytes(cfg, op: str, active_experts: int) -> float:
+    """Algorithmic HBM bytes of one grouped GEMM launch: the active experts' weights, the
+    activation rows read once (x for gate/up, Hs for down) and the rows written (Hs / Ys)."""
+    w = active_experts * expert_weight_bytes(cfg, op)
+    if op == "gate_up":
+        act = cfg.T * cfg.H * 2 + cfg.P * cfg.I * 2
+    else:
+        act = cfg.P * cfg.I * 2 + cfg.P * cfg.H * 2
+    return w + act
+
+
+def clone_layer(layer):
+    """Same weights in fresh buffers (so repeated steps cannot be served from the 256 MB MALL)."""
+    import copy
+    import mixture_experts_routed_route_amd as m
+    c = copy.copy(layer)
+    def cw(w):
+        if isinstance(w, m.Bf16Weight):
+            return m.Bf16Weight(w.w.clone())
+        return m.GptqWeight(w.qweight.clone(), w.scales.clone(), w.qzeros.clone(), w.group_size)
+    c.gate, c.up, c.down = cw(layer.gate), cw(layer.up), cw(layer.down)
+    return c
 
 
 def layer_flops(cfg) -> float:
@@ -64,6 +102,10 @@ def main():
     ap.add_argument("--config", default="mixtral_prefill")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="token sample of the CPU oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="independent weight copies cycled through (0: enough for >= 1 GiB of weights, max 4)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures the single-GPU path only; --gpus {args.gpus} is not supported "
@@ -81,11 +123,15 @@ def main():
     d = make_inputs(cfg)
     layer = m.MoeLayer.from_arrays(d, dev)
     b = layer.plan(cfg.T, dev)
+    wbytes = sum(expert_weight_bytes(cfg, op) for op in ("gate_up", "down")) * cfg.E
+    rot = args.rotate or max(1, min(4, int(-(-(1 << 30) // wbytes))))
+    layers = [layer] + [clone_layer(layer) for _ in range(rot - 1)]
     logits = torch.from_numpy(d["logits"]).to(dev)
     x = torch.from_numpy(d["x"]).view(torch.bfloat16).to(dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step(i, ev=None):
+        layer = layers[i % rot]
         layer.route_align(logits, b)
         if ev is not None:
             ev[0].record()
@@ -101,8 +147,8 @@ def main():
         layer.combine(b)
 
     log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -110,18 +156,41 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(i, events[i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     tokens_s = cfg.T / (ms / 1e3)
+    active = int((b.routing.counts > 0).sum().item())
+    gu_bytes = gemm_bytes(cfg, "gate_up", active)
     gu_tflops = gemm_flops(cfg, "gate_up") / (gu_ms / 1e3) / 1e12
     dn_tflops = gemm_flops(cfg, "down") / (dn_ms / 1e3) / 1e12
     gemm_tflops = (gemm_flops(cfg, "gate_up") + gemm_flops(cfg, "down")) / ((gu_ms + dn_ms) / 1e3) / 1e12
     log(f"[bench] step {ms:.3f} ms; gate/up {gu_ms:.3f} ms ({gu_tflops:.1f} TFLOP/s); "
         f"down {dn_ms:.3f} ms ({dn_tflops:.1f} TFLOP/s); grouped GEMMs {gemm_tflops:.1f} TFLOP/s")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB device-to-device copy done")
+
+    ai = gemm_flops(cfg, "gate_up") / gu_bytes
+    if ai >= RIDGE:
+        roof = {"bound": "mfma", "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        gbs = gu_bytes / (gu_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>"
+    roof["algorithmic"] = {"flops": gemm_flops(cfg, "gate_up"), "bytes": gu_bytes, "active_experts": active,
+                           "flop_per_byte": ai}
+    log(f"[bench] gate/up roofline: {roof['bound']} {roof['achieved']:.1f} {roof['unit']} "
+        f"({100 * roof['frac']:.1f}% of peak), AI {ai:.0f} flop/B, {active} active experts, rotate {rot}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -140,7 +209,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if cfg.weights == "bf16" else "int4 weights x bf16, fp32 accumulate",
         "data": "synthetic (seeded numpy PCG64; random-init expert weights)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
@@ -148,9 +217,7 @@ def main():
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
         "kernels_ms": {"gate_up": gu_ms, "down": dn_ms},
-        "roofline": {"kernel": "gemm_bf16_kernel<gate_up>", "bound": "mfma", "achieved": gu_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gu_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -36,9 +36,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
-// Inclusive prefix sum of `v` over a 256-thread block; `scratch` holds >= 4 ints.
+// Inclusive prefix sum of `v` over a block of NW waves; `scratch` holds >= NW ints.
 // Every thread of the block must call it.
-__device__ __forceinline__ int block_inclusive_scan_256(int v, int* scratch) {
+template <int NW>
+__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -51,6 +52,10 @@ __device__ __forceinline__ int block_inclusive_scan_256(int v, int* scratch) {
     for (int w = 0; w < wave; ++w) add += scratch[w];
     __syncthreads();
     return v + add;
+}
+
+__device__ __forceinline__ int block_inclusive_scan_256(int v, int* scratch) {
+    return block_inclusive_scan<4>(v, scratch);
 }
 
 // Largest e in [0, n) with off[e] <= r (off non-decreasing, off[0] <= r).

@@ -2,40 +2,98 @@
 // down roles of metrale cutlass/grouped.rs; gather through sorted ids and sentinel masking
 // as in ferrum-kernels triton_fused_moe.rs).
 //
-// Tiling.  A tile is up to BM = 128 consecutive sorted rows of ONE expert: expert e's
-// padded span [off[e], off[e+1]) is cut into ceil(span/128) tiles.  Each workgroup
-// rebuilds that tile list from expert_offsets (a 256-wide LDS scan of the per-expert tile
-// counts), so the grid is a static worst-case bound (ceil(max_pad/128) + E tiles per
-// column panel) and tiles past the end exit at once.  The weight panel of a tile is
-// BP = 256 weight rows: for gate/up, 128 gate rows and the 128 up rows of the same output
-// columns (so SiLU(gate)*up is formed in registers); for down, 256 output columns.
+// Tiling.  A tile is up to BM consecutive sorted rows of ONE expert: expert e's padded span
+// [off[e], off[e+1]) is cut into ceil(span/BM) tiles.  Each workgroup rebuilds that tile list
+// from expert_offsets (a 256-wide LDS scan of the per-expert tile counts), so the grid is a
+// static worst-case bound (ceil(max_pad/BM) + E row tiles per column panel) and tiles past the
+// end exit at once.  The weight panel of a tile is BP = 256 weight rows: for gate/up the 128
+// gate rows and the 128 up rows of the same output columns (SiLU(gate)*up is formed from the
+// fp32 accumulators), for down 256 output columns.
 //
-// Schedule.  256 threads = 4 waves in a 2x2 grid; each wave owns 64 rows x 128 panel rows
-// (4 x 8 MFMA 16x16x32 bf16 tiles, fp32 accumulators).  K advances 64 at a time through a
-// double-buffered LDS stage (A 16 KB + B 32 KB per stage, rows XOR-swizzled in 16-byte
-// chunks so the 16-byte fragment reads of one MFMA spread over the banks); the global
-// loads of the next stage are issued before the MFMAs of the current one.  Workgroup ids
-// are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs) runs a
-// contiguous range of tiles, and consecutive tiles share a weight panel (row tiles of the
-// same expert and column panel), which then stays in that XCD's L2.
+// Pipeline.  NW waves in a (NW/2) x 2 grid, each owning 64 x 128 of the tile as 32x32x16 bf16
+// MFMA blocks with fp32 accumulators; on gfx950 the 32x32x16 form runs at the full bf16 rate,
+// the 16x16x32 form at about half of it.  256-row tiles use 8 waves, two per SIMD, so one
+// wave's LDS and barrier waits overlap the other's MFMAs.  K advances BK at a time through a ring of
+// STAGES LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4: no VGPR
+// staging, no LDS store instructions; issued from inline asm, see dma16); STAGES-1 stages are in flight while one is computed.
+// Each thread waits on its own loads with an explicit vmcnt, then a bare s_barrier makes the
+// stage visible to all waves (a fenced barrier would drain the later stages' loads too).
+// LDS rows are XOR-swizzled in 16-byte chunks so that the 32-row fragment reads are free of LDS
+// bank conflicts.
+// Fragments of the next K step are read from LDS while the MFMAs of the current one run.  Rows that hold no token
+// (sentinels, padding) load a harmless valid row and are never stored; k past K loads zeros.
+//
+// Schedule.  Workgroup ids are dealt round-robin over the 8 XCDs, so the id is remapped to
+// give each XCD a contiguous range of logical tiles.  Logical tiles run in bands of GM row
+// tiles: within a band, GM row tiles of one column panel are consecutive, so the ~32 tiles an
+// XCD runs at once cover a few panels x GM row tiles and share A tiles and weight panels in
+// that XCD's L2.
+//
+// Epilogue.  The bf16 output tile is staged in LDS and written back with 16-byte row stores.
 #include "device_common.h"
 #include "launchers.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128;
 constexpr int BP = 256;
-constexpr int BK = 64;
-constexpr int NT = 256;
-constexpr int A_CH = BM * BK / 8 / NT;  // 16-byte chunks of A per thread per stage
-constexpr int B_CH = BP * BK / 8 / NT;
+#ifndef MOE_GEMM_BAND_ROWS
+#define MOE_GEMM_BAND_ROWS 2048   // sorted rows per band of the tile schedule
+#endif
+#ifndef MOE_GEMM_XCD_REMAP
+#define MOE_GEMM_XCD_REMAP 1
+#endif
 constexpr int kMaxE = 256;
 
-__device__ __forceinline__ int swz(int row, int c) { return row * BK + ((c ^ (row & 7)) << 3); }
+__device__ __attribute__((aligned(16))) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// 16 bytes per lane from global memory straight into LDS at m0 + lane*16 (one 1 KB row block
+// per wave).  Emitted as inline asm so that the compiler does not treat every later LDS read
+// as dependent on it (it would drain all loads in flight before each read); completion is
+// tracked with explicit vmcnt waits instead.  m0 is written inside the statement itself.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(p))));
+}
+
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
+struct Cfg {
+    static constexpr int NT = 64 * NW;                  // threads
+    static constexpr int WAVES_M = NW / 2;              // wave grid WAVES_M x 2
+    static constexpr int CPR = BK / 8;                  // 16-byte chunks per LDS row
+    static constexpr int RP = 256 / (BK * 2);           // LDS rows per 256-byte line of the 64 banks
+    static constexpr int A_ELEMS = BM * BK;
+    static constexpr int B_ELEMS = BP * BK;
+    static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
+    static constexpr int ROWS_PER_INST = 1024 / (BK * 2);  // rows one wave-wide 1 KB load fills
+    static constexpr int A_INST = BM / ROWS_PER_INST / NW;  // load instructions per wave per stage
+    static constexpr int B_INST = BP / ROWS_PER_INST / NW;
+    static constexpr int LOADS = A_INST + B_INST;
+    static constexpr int WM = BM / WAVES_M;              // rows per wave
+    static constexpr int FI = WM / 32;                   // A fragments (32 rows) per wave
+    static constexpr int NCOL = GATE_UP ? BP / 2 : BP;   // output columns per tile
+    static constexpr int GM = MOE_GEMM_BAND_ROWS / BM;   // row tiles per band
+    static constexpr int SMEM = STAGES * STAGE_ELEMS;    // elements
+};
+
+// 16-byte chunk c of LDS row `row` lives at chunk c ^ ((row / rp) % cpr): measured free of bank
+// conflicts for the 32-row x 2-chunk fragment reads of the 32x32x16 MFMA.
+__device__ __forceinline__ int swz_chunk(int row, int c, int rp, int cpr) { return c ^ ((row / rp) % cpr); }
+
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W0,
                                                           const uint16_t* __restrict__ W1,
                                                           uint16_t* __restrict__ C,
@@ -43,16 +101,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ offsets, int P, int top_k,
                                                           int E, int N, int K, int max_pad, int m_tiles,
                                                           int n_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BP) * BK];
-    __shared__ int s_scan[4];
+    using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
+    constexpr int NT = F::NT;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
+    __shared__ int s_scan[NW];
     __shared__ int s_row[BM];
     __shared__ int s_info[3];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // ---- logical tile: XCD-contiguous ranges, then bands of GM row tiles x all panels
     const int nwg = gridDim.x;
     const int bid = blockIdx.x;
-    const int L = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int n_t = L / m_tiles, m_t = L % m_tiles;
+    const int L = MOE_GEMM_XCD_REMAP ? (bid & 7) * (nwg >> 3) + (bid >> 3) : bid;
+    const int band_tiles = F::GM * n_tiles;
+    const int band = L / band_tiles;
+    const int in_band = L - band * band_tiles;
+    const int gm_b = min(F::GM, m_tiles - band * F::GM);
+    if (gm_b <= 0) return;
+    const int n_t = in_band / gm_b;
+    const int m_t = band * F::GM + (in_band - n_t * gm_b);
     if (n_t >= n_tiles) return;
 
     // ---- which expert and rows this tile covers
@@ -62,7 +130,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const uint16_t* __rest
         hi = min(max(offsets[tid + 1], lo), max_pad);
     }
     const int nt_e = (hi - lo + BM - 1) / BM;
-    const int incl = block_inclusive_scan_256(nt_e, s_scan);
+    const int incl = block_inclusive_scan<NW>(nt_e, s_scan);
     if (tid == 0) s_info[0] = -1;
     __syncthreads();
     if (tid < E && m_t >= incl - nt_e && m_t < incl) {
@@ -85,127 +153,190 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const uint16_t* __rest
         s_row[i] = src;
     }
     __syncthreads();
+    const int n0 = n_t * F::NCOL;
 
-    const int n0 = n_t * (GATE_UP ? BP / 2 : BP);
-
-    // ---- per-thread global source rows (fixed over K)
-    const uint16_t* a_src[A_CH];
-    const uint16_t* b_src[B_CH];
+    // ---- per-lane DMA sources: instruction q of this wave fills ROWS_PER_INST rows
+    const int lrow = lane / F::CPR;   // row within the instruction's block
+    const int pc = lane % F::CPR;     // physical chunk this lane's 16 bytes land in
+    const uint16_t* a_src[F::A_INST];
+    const uint16_t* b_src[F::B_INST];
+    int a_kc[F::A_INST], b_kc[F::B_INST];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + NT * i, row = c >> 3, kc = c & 7;
+    for (int q = 0; q < F::A_INST; ++q) {
+        const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
+        const int kc = swz_chunk(row, pc, F::RP, F::CPR);
         const int src = s_row[row];
-        a_src[i] = src >= 0 ? A + static_cast<size_t>(src) * K + kc * 8 : nullptr;
+        // a sentinel row reads a valid row (token 0 / its own sorted row); it is never stored
+        const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0 + row);
+        a_src[q] = A + static_cast<size_t>(srow) * K + kc * 8;
+        a_kc[q] = kc * 8;
     }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + NT * i, row = c >> 3, kc = c & 7;
+    for (int q = 0; q < F::B_INST; ++q) {
+        const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
+        const int kc = swz_chunk(row, pc, F::RP, F::CPR);
         int n;
         const uint16_t* W;
         if (GATE_UP) { n = n0 + (row & (BP / 2 - 1)); W = row < BP / 2 ? W0 : W1; }
         else { n = n0 + row; W = W0; }
-        b_src[i] = n < N ? W + (static_cast<size_t>(e) * N + n) * K + kc * 8 : nullptr;
+        n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
+        b_src[q] = W + (static_cast<size_t>(e) * N + n) * K + kc * 8;
+        b_kc[q] = kc * 8;
     }
 
-    u32x4 ra[A_CH], rb[B_CH];
-    auto load_stage = [&](int k0) {
+    auto issue = [&](int kt) {
+        const int k0 = kt * BK;
+        uint16_t* st = smem + (kt % STAGES) * F::STAGE_ELEMS;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int kc = (tid + NT * i) & 7;
-            ra[i] = (a_src[i] && k0 + kc * 8 < K) ? *reinterpret_cast<const u32x4*>(a_src[i] + k0)
-                                                  : u32x4{0, 0, 0, 0};
+        for (int q = 0; q < F::A_INST; ++q) {
+            const void* g = (k0 + a_kc[q] < K) ? static_cast<const void*>(a_src[q] + k0)
+                                                : static_cast<const void*>(kZero16);
+            dma16(g, lds_u32(st + (wave * F::A_INST + q) * 512));
         }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int kc = (tid + NT * i) & 7;
-            rb[i] = (b_src[i] && k0 + kc * 8 < K) ? *reinterpret_cast<const u32x4*>(b_src[i] + k0)
-                                                  : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_stage = [&](int buf) {
-        uint16_t* la = lds[buf];
-        uint16_t* lb = lds[buf] + BM * BK;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int c = tid + NT * i, row = c >> 3, kc = c & 7;
-            *reinterpret_cast<u32x4*>(la + swz(row, kc)) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int c = tid + NT * i, row = c >> 3, kc = c & 7;
-            *reinterpret_cast<u32x4*>(lb + swz(row, kc)) = rb[i];
+        for (int q = 0; q < F::B_INST; ++q) {
+            const void* g = (k0 + b_kc[q] < K) ? static_cast<const void*>(b_src[q] + k0)
+                                                : static_cast<const void*>(kZero16);
+            dma16(g, lds_u32(st + F::A_ELEMS + (wave * F::B_INST + q) * 512));
         }
     };
 
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x4 acc[4][8];
+    const int wm = wave >> 1, wn = wave & 1;  // wave grid WAVES_M x 2
+    // 32x32x16 MFMA blocks: each wave holds FI x 4 blocks of 32x32 fp32 accumulators
+    f32x16 acc[F::FI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // fragment LDS offsets (elements) within a stage: lane row fr = lane%32, k-chunk fc = lane/32
+    const int fr = lane & 31, fc = lane >> 5;
+    int a_off[F::FI], b_off[4];
+#pragma unroll
+    for (int i = 0; i < F::FI; ++i) a_off[i] = (wm * F::WM + i * 32 + fr) * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int prow;
+        if (GATE_UP) prow = (j < 2 ? wn * 64 + j * 32 : BP / 2 + wn * 64 + (j - 2) * 32);
+        else prow = wn * 128 + j * 32;
+        b_off[j] = F::A_ELEMS + (prow + fr) * BK;
+    }
+    // every fragment starts on a multiple of 32 rows, so its swizzle depends on the lane only
+    const int fswz = (fr / F::RP) % F::CPR;
 
     const int nk = (K + BK - 1) / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_stage((kt + 1) * BK);
-        const uint16_t* la = lds[buf];
-        const uint16_t* lb = lds[buf] + BM * BK;
+    constexpr int KK = BK / 16;  // 32x32x16 MFMA k-steps per stage (even)
+    bf16x8 fa[2][F::FI], fb[2][4];
+    // fragments of k-step kk of stage s into register set `set`
+    auto read = [&](int s, int kk, int set) {
+        const uint16_t* st = smem + (s % STAGES) * F::STAGE_ELEMS;
+        const int cx = ((kk * 2 + fc) ^ fswz) << 3;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = kk * 4 + (lane >> 4);
-            bf16x8 a[4], b[8];
+        for (int i = 0; i < F::FI; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 64 + i * 16 + (lane & 15);
-                a[i] = *reinterpret_cast<const bf16x8*>(la + swz(row, c));
-            }
+        for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + cx);
+    };
+    auto mfma = [&](int set) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                int prow;
-                if (GATE_UP) prow = (j < 4 ? wn * 64 + j * 16 : BP / 2 + wn * 64 + (j - 4) * 16);
-                else prow = wn * 128 + j * 16;
-                prow += lane & 15;
-                b[j] = *reinterpret_cast<const bf16x8*>(lb + swz(prow, c));
-            }
+        for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+    };
+    // Stage t becomes readable: this thread's loads of t have landed (at most `ahead` later stages
+    // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
+    // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
+    auto ready = [&](int t) {
+        const int ahead = min(STAGES - 2, nk - 1 - t);
+        if constexpr (STAGES >= 4) {
+            if (ahead >= 2) wait_vmcnt<2 * F::LOADS>();
+            else if (ahead == 1) wait_vmcnt<F::LOADS>();
+            else wait_vmcnt<0>();
+        } else if constexpr (STAGES == 3) {
+            if (ahead >= 1) wait_vmcnt<F::LOADS>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
         }
-        if (kt + 1 < nk) store_stage(buf ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
+    };
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s);
+    ready(0);
+    read(0, 0, 0);
+    // Each k-step's MFMAs are issued after the next k-step's fragment reads (and, at a stage
+    // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
+    for (int s = 0; s < nk; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) {
+                read(s, kk + 1, (kk + 1) & 1);
+            } else if (s + 1 < nk) {
+                ready(s + 1);
+                read(s + 1, 0, 0);
+            }
+            mfma(kk & 1);
+        }
     }
 
-    // ---- epilogue: C fragment lane holds rows 4*(lane/16)+v, column lane%16
+    // ---- epilogue: bf16 tile through LDS, 16-byte row stores.  Tile row stride NCOL+8.
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int PASS_COLS = 128;                 // columns staged per pass
+    constexpr int PASSES = F::NCOL / PASS_COLS;    // 1 for gate/up, 2 for down
+    constexpr int LD = PASS_COLS + 8;
+    uint16_t* ct = smem;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int pass = 0; pass < PASSES; ++pass) {
+        if (GATE_UP || wn == pass) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + v;
-            if (s_row[rl] < 0) continue;
-            uint16_t* crow = C + static_cast<size_t>(r0 + rl) * N;
-            if (GATE_UP) {
+            for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-                    if (col < N) {
-                        const float g = acc[i][j][v], u = acc[i][j + 4][v];
-                        crow[col] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                for (int v = 0; v < 16; ++v) {
+                    const int rl = wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3);
+                    if (GATE_UP) {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const float g = acc[i][j][v], u = acc[i][j + 2][v];
+                            ct[rl * LD + wn * 64 + j * 32 + fr] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ct[rl * LD + j * 32 + fr] = f32_to_bf16(acc[i][j][v]);
                     }
                 }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int col = n0 + wn * 128 + j * 16 + (lane & 15);
-                    if (col < N) crow[col] = f32_to_bf16(acc[i][j][v]);
-                }
-            }
         }
+        __syncthreads();
+        constexpr int CH = PASS_COLS / 8;  // 16-byte chunks per row
+        for (int idx = tid; idx < BM * CH; idx += NT) {
+            const int rl = idx / CH, ch = idx - rl * CH;
+            const int col = n0 + pass * PASS_COLS + ch * 8;
+            if (s_row[rl] >= 0 && col < N)
+                *reinterpret_cast<u32x4*>(C + static_cast<size_t>(r0 + rl) * N + col) =
+                    *reinterpret_cast<const u32x4*>(ct + rl * LD + ch * 8);
+        }
+        if (PASSES > 1) __syncthreads();
     }
+}
+
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
+hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
+                      const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
+                      int max_pad, hipStream_t s) {
+    using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
+    const int m_tiles = (max_pad + BM - 1) / BM + E;
+    const int n_tiles = (N + F::NCOL - 1) / F::NCOL;
+    const long long tiles = static_cast<long long>(m_tiles) * n_tiles;
+    const int grid = static_cast<int>((tiles + 7) / 8 * 8);
+    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW><<<grid, F::NT, 0, s>>>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N,
+                                                                 K, max_pad, m_tiles, n_tiles);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -213,18 +344,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const uint16_t* __rest
 hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
                             int K, int max_pad, hipStream_t s) {
-    const int m_tiles = (max_pad + BM - 1) / BM + E;
-    const int ncols = gate_up ? BP / 2 : BP;
-    const int n_tiles = (N + ncols - 1) / ncols;
-    const long long tiles = static_cast<long long>(m_tiles) * n_tiles;
-    const int grid = static_cast<int>((tiles + 7) / 8 * 8);
-    if (gate_up)
-        gemm_bf16_kernel<true><<<grid, NT, 0, s>>>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad,
-                                                   m_tiles, n_tiles);
-    else
-        gemm_bf16_kernel<false><<<grid, NT, 0, s>>>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K,
-                                                    max_pad, m_tiles, n_tiles);
-    return hipGetLastError();
+    // 256-row tiles when experts hold enough rows on average, 128-row tiles otherwise
+    const bool big = static_cast<long long>(P) >= 384LL * E;
+    if (gate_up) {
+        if (big) return launch_cfg<true, 256, 32, 4, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+        return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+    }
+    if (big) return launch_cfg<false, 256, 32, 4, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+    return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
 }
 
 }  // namespace moe
