@@ -166,8 +166,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
         const int kc = swz_chunk(row, pc, F::RP, F::CPR);
         const int src = s_row[row];
-        // a sentinel row reads a valid row (token 0 / its own sorted row); it is never stored
-        const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0 + row);
+        // a row without a token reads a row that is always in bounds (token 0, or the tile's
+        // first sorted row r0 < max_pad); its results are never stored
+        const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0);
         a_src[q] = A + static_cast<size_t>(srow) * K + kc * 8;
         a_kc[q] = kc * 8;
     }

@@ -370,3 +370,32 @@ def test_layer_deterministic(dev):
     _, _, o1 = _layer_run(cfg, d)
     _, _, o2 = _layer_run(cfg, d)
     assert np.array_equal(bits_host(o1), bits_host(o2))
+
+
+def test_grouped_gemms_padded_total_at_capacity(dev):
+    """Regression: every expert holds a multiple of block_size plus one pair, so the padded total
+    equals the sorted capacity and the last 256-row tile of the last expert extends past the
+    end of the buffers; such rows must neither be read out of bounds nor stored."""
+    m = ops()
+    E, bs, per = 2, 64, 8 * 64 + 1
+    cfg = MoeConfig("tight", T=E * per, H=256, I=256, E=E, top_k=1, block_size=bs, seed=21)
+    d = make_inputs(cfg)
+    ids = np.repeat(np.arange(E, dtype=np.int32), per).reshape(-1, 1)
+    al = oracle.align(ids, E, bs)
+    assert al["total"] == len(al["sorted_ids"])  # the padded total reaches the capacity
+    r = m.moe_align(to_dev(ids), E, bs)
+    layer = _weights_dev(d)
+    real = _real(al, cfg.P)
+    hs = _canary(r.max_pad, cfg.I)
+    m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, bf16_dev(d["x"]), layer.gate, layer.up, r, out=hs)
+    h_ref = oracle.grouped_gate_up(d["x"], d["wg"], d["wu"], al, 1)
+    assert_close_rows(bf16_host(hs)[real], h_ref[real], TOL, "gate/up at capacity")
+    # down, fed with the oracle's own h rounded to bf16 (NaN in every padding row)
+    h_in = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
+    h_in[real] = f32_to_bf16_bits(oracle.round_bf16(h_ref[real]).astype(np.float32))
+    ys = _canary(r.max_pad, cfg.H)
+    m.moe_grouped_gemm(m.MOE_OP_DOWN, bf16_dev(h_in), layer.down, None, r, out=ys)
+    y_ref = oracle.grouped_down(oracle.bf16_bits_to_f64(h_in), d["wd"], al)
+    assert_close_rows(bf16_host(ys)[real], y_ref[real], TOL, "down at capacity")
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    assert (bits_host(ys)[pad] == CANARY).all()
