@@ -71,6 +71,28 @@ def clone_layer(layer):
     return c
 
 
+def measured_traffic(workload: str, role: str):
+    """HBM bytes per launch of one grouped GEMM from the committed FETCH_SIZE/WRITE_SIZE summary of
+    this workload (already scaled by the copy calibration), or None when there is none or the
+    kernel's source files have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    files, want = kv.get("source_files", "").split(), kv.get("source_sha256")
+    if not files or not want or f"{role}.traffic_bytes" not in kv:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc", f), "rb").read())
+    return float(kv[f"{role}.traffic_bytes"]) if h.hexdigest() == want else None
+
+
 def layer_flops(cfg) -> float:
     return 6.0 * cfg.H * cfg.I * cfg.P
 
@@ -100,7 +122,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral_prefill")
-    ap.add_argument("--cpu-tokens", type=int, default=256, help="token sample of the CPU oracle leg")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="token sample of the CPU oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0,
                     help="independent weight copies cycled through (0: enough for >= 1 GiB of weights, max 4)")
@@ -185,7 +207,7 @@ def main():
         gbs = gu_bytes / (gu_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, "gate_up")
     roof["kernel"] = ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>"
     roof["algorithmic"] = {"flops": gemm_flops(cfg, "gate_up"), "bytes": gu_bytes, "active_experts": active,
                            "flop_per_byte": ai}

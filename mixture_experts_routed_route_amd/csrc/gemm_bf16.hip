@@ -43,6 +43,12 @@ constexpr int BP = 256;
 #ifndef MOE_GEMM_XCD_REMAP
 #define MOE_GEMM_XCD_REMAP 1
 #endif
+#ifndef MOE_GEMM_BIG_BK
+#define MOE_GEMM_BIG_BK 64       // k per LDS stage of the 256-row tiles
+#endif
+#ifndef MOE_GEMM_BIG_STAGES
+#define MOE_GEMM_BIG_STAGES 2    // LDS stages of the 256-row tiles (stage = 512 rows x BK bf16)
+#endif
 constexpr int kMaxE = 256;
 
 __device__ __attribute__((aligned(16))) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
@@ -348,10 +354,10 @@ hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0,
     // 256-row tiles when experts hold enough rows on average, 128-row tiles otherwise
     const bool big = static_cast<long long>(P) >= 384LL * E;
     if (gate_up) {
-        if (big) return launch_cfg<true, 256, 32, 4, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
         return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
     }
-    if (big) return launch_cfg<false, 256, 32, 4, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+    if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
     return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
 }
 
