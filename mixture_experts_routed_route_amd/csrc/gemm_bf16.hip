@@ -23,6 +23,11 @@
 // Fragments of the next K step are read from LDS while the MFMAs of the current one run.  Rows that hold no token
 // (sentinels, padding) load a harmless valid row and are never stored; k past K loads zeros.
 //
+// Ragged tails.  An expert's last tile usually holds fewer tokens than BM.  Its rows past the last
+// token are sentinels, so each wave counts the 32-row A fragments of its own rows that hold a
+// token (0, 1 or 2) and runs a main loop compiled for that count: empty fragments cost no LDS
+// reads and no MFMAs, and the wave still loads and meets the barriers.
+//
 // Schedule.  Workgroup ids are dealt round-robin over the 8 XCDs, so the id is remapped to
 // give each XCD a contiguous range of logical tiles.  Logical tiles run in bands of GM row
 // tiles: within a band, GM row tiles of one column panel are consecutive, so the ~32 tiles an
@@ -30,6 +35,8 @@
 // that XCD's L2.
 //
 // Epilogue.  The bf16 output tile is staged in LDS and written back with 16-byte row stores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
     __shared__ int s_scan[NW];
     __shared__ int s_row[BM];
-    __shared__ int s_info[3];
+    __shared__ int s_info[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     }
     const int nt_e = (hi - lo + BM - 1) / BM;
     const int incl = block_inclusive_scan<NW>(nt_e, s_scan);
-    if (tid == 0) s_info[0] = -1;
+    if (tid == 0) { s_info[0] = -1; s_info[3] = 0; }
     __syncthreads();
     if (tid < E && m_t >= incl - nt_e && m_t < incl) {
         s_info[0] = tid;
@@ -157,8 +164,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             if (p >= 0 && p < P) src = GATE_UP ? p / top_k : r;
         }
         s_row[i] = src;
+        if (src >= 0) atomicMax(&s_info[3], i + 1);
     }
     __syncthreads();
+    // rows at or past h_rows hold no token (an expert's sentinels follow its tokens), so a wave whose
+    // 32-row fragments all lie there skips their MFMAs
+    const int h_rows = s_info[3];
     const int n0 = n_t * F::NCOL;
 
     // ---- per-lane DMA sources: instruction q of this wave fills ROWS_PER_INST rows
@@ -236,18 +247,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     const int nk = (K + BK - 1) / BK;
     constexpr int KK = BK / 16;  // 32x32x16 MFMA k-steps per stage (even)
     bf16x8 fa[2][F::FI], fb[2][4];
-    // fragments of k-step kk of stage s into register set `set`
-    auto read = [&](int s, int kk, int set) {
-        const uint16_t* st = smem + (s % STAGES) * F::STAGE_ELEMS;
-        const int cx = ((kk * 2 + fc) ^ fswz) << 3;
+    // fragments of k-step kk of stage s into register set `set` (the first NF A fragments)
+    auto read = [&](auto nf_c, int s, int kk, int set) {
+        constexpr int NF = decltype(nf_c)::value;
+        if constexpr (NF > 0) {
+            const uint16_t* st = smem + (s % STAGES) * F::STAGE_ELEMS;
+            const int cx = ((kk * 2 + fc) ^ fswz) << 3;
 #pragma unroll
-        for (int i = 0; i < F::FI; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
+            for (int i = 0; i < NF; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + cx);
+            for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + cx);
+        }
     };
-    auto mfma = [&](int set) {
+    auto mfma = [&](auto nf_c, int set) {
+        constexpr int NF = decltype(nf_c)::value;
 #pragma unroll
-        for (int i = 0; i < F::FI; ++i)
+        for (int i = 0; i < NF; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
@@ -275,22 +290,30 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < nk) issue(s);
-    ready(0);
-    read(0, 0, 0);
     // Each k-step's MFMAs are issued after the next k-step's fragment reads (and, at a stage
     // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
-    for (int s = 0; s < nk; ++s) {
+    // NF = A fragments of this wave that hold tokens; every wave still loads and meets the barriers.
+    auto main_loop = [&](auto nf_c) {
+        ready(0);
+        read(nf_c, 0, 0, 0);
+        for (int s = 0; s < nk; ++s) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 1 < KK) {
-                read(s, kk + 1, (kk + 1) & 1);
-            } else if (s + 1 < nk) {
-                ready(s + 1);
-                read(s + 1, 0, 0);
+            for (int kk = 0; kk < KK; ++kk) {
+                if (kk + 1 < KK) {
+                    read(nf_c, s, kk + 1, (kk + 1) & 1);
+                } else if (s + 1 < nk) {
+                    ready(s + 1);
+                    read(nf_c, s + 1, 0, 0);
+                }
+                mfma(nf_c, kk & 1);
             }
-            mfma(kk & 1);
         }
-    }
+    };
+    static_assert(F::FI == 2, "tail skipping assumes two A fragments per wave");
+    const int nf = __builtin_amdgcn_readfirstlane(min(max((h_rows - wm * F::WM + 31) / 32, 0), F::FI));
+    if (nf == 2) main_loop(std::integral_constant<int, 2>{});
+    else if (nf == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
 
     // ---- epilogue: bf16 tile through LDS, 16-byte row stores.  Tile row stride NCOL+8.
     wait_vmcnt<0>();
