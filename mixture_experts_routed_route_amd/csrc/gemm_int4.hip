@@ -4,7 +4,10 @@
 // real rows, so every weight byte is used by at most a handful of rows).
 //
 // Work unit: one workgroup = one 16-row tile of sorted rows (one expert, from expert_ids)
-// x 64 output columns; its 4 waves split the K groups and add their partial sums in LDS.
+// x 64 output columns.  For gate/up, waves 0-1 compute the gate projection and waves 2-3 the up
+// projection, each pair splitting the K groups in two; for down, the 4 waves split the K groups
+// in four.  Partial sums meet in LDS.  One projection per wave keeps a wave's registers small
+// enough for 4 waves per SIMD, so more weight loads are in flight per CU.
 //
 // Dequantisation without per-weight float work.  A qweight word holds 8 consecutive k of
 // one column; OR-ing nibble pairs into bf16 0x4300 (= 128.0) gives the exact bf16 values
@@ -24,6 +27,10 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_INT4_DEPTH
+#define MOE_INT4_DEPTH 1   // quantisation groups of weights in flight per wave while one is computed
+#endif
+
 constexpr int NT = 256;
 constexpr int NCOL = 64;
 
@@ -39,13 +46,15 @@ __device__ __forceinline__ u32x4 permute_k(u32x4 a) {
     return r;
 }
 
-// One qweight word (8 nibbles of consecutive k) -> bf16 (128+q) in the permuted k order.
-__device__ __forceinline__ u32x4 dequant_word(uint32_t w) {
+// One qweight word (8 nibbles of consecutive k) -> bf16 (128+q) in the permuted k order.  The
+// mask and the bf16 exponent pattern come in registers (opaque to the compiler) so that each
+// pair is one v_and_or_b32: a VOP3 instruction cannot take them as literals.
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, uint32_t mask, uint32_t magic) {
     u32x4 r;
-    r[0] = (w & 0x000f000fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
+    r[0] = (w & mask) | magic;
+    r[1] = ((w >> 4) & mask) | magic;
+    r[2] = ((w >> 8) & mask) | magic;
+    r[3] = ((w >> 12) & mask) | magic;
     return r;
 }
 
@@ -59,16 +68,17 @@ struct GroupRegs {
 };
 
 template <bool GATE_UP, int STEPS>
-__global__ __launch_bounds__(NT) void gemm_int4_kernel(
+__global__ __launch_bounds__(NT, STEPS <= 4 ? (MOE_INT4_DEPTH == 2 ? 3 : 4) : 2) void gemm_int4_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ qw0, const uint16_t* __restrict__ sc0,
     const int32_t* __restrict__ qz0, const int32_t* __restrict__ qw1, const uint16_t* __restrict__ sc1,
     const int32_t* __restrict__ qz1, uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, int P, int top_k, int E, int N, int K, int bs, int max_pad) {
-    constexpr int NP = GATE_UP ? 2 : 1;
+    constexpr int NP = 1;                      // projections per wave
+    constexpr int NSPLIT = GATE_UP ? 2 : 4;    // waves sharing one projection's K groups
     constexpr int G = STEPS * 32;
     __shared__ int s_row[16];
     __shared__ int s_any;
-    __shared__ float red[4][NP][4][64][4];  // [wave][proj][v][lane][j]
+    __shared__ float red[4][4][64][4];  // [wave][v][lane][j]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r0 = blockIdx.x * 16;
@@ -90,10 +100,12 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     __syncthreads();
     if (!s_any) return;
 
-    // this wave's quantisation groups (split-K over the 4 waves)
+    // this wave's projection and quantisation groups
+    const int proj = GATE_UP ? wave >> 1 : 0;
+    const int part = GATE_UP ? wave & 1 : wave;
     const int ngroups = K / G;
-    const int per = (ngroups + 3) / 4;
-    const int g_begin = wave * per;
+    const int per = (ngroups + NSPLIT - 1) / NSPLIT;
+    const int g_begin = part * per;
     const int g_end = min(ngroups, g_begin + per);
 
     const int m = lane & 15, kq = lane >> 4;  // A fragment row; k-octet within a k32 step
@@ -105,14 +117,9 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
     const int32_t* qw[NP];
     const uint16_t* sc[NP];
     const int32_t* qz[NP];
-    qw[0] = qw0 + static_cast<size_t>(e) * (K / 8) * N;
-    sc[0] = sc0 + static_cast<size_t>(e) * (K / G) * N;
-    qz[0] = qz0 + static_cast<size_t>(e) * (K / G) * (N / 8);
-    if (GATE_UP) {
-        qw[NP - 1] = qw1 + static_cast<size_t>(e) * (K / 8) * N;
-        sc[NP - 1] = sc1 + static_cast<size_t>(e) * (K / G) * N;
-        qz[NP - 1] = qz1 + static_cast<size_t>(e) * (K / G) * (N / 8);
-    }
+    qw[0] = (proj ? qw1 : qw0) + static_cast<size_t>(e) * (K / 8) * N;
+    sc[0] = (proj ? sc1 : sc0) + static_cast<size_t>(e) * (K / G) * N;
+    qz[0] = (proj ? qz1 : qz0) + static_cast<size_t>(e) * (K / G) * (N / 8);
 
     auto load_group = [&](int g, GroupRegs<NP, STEPS>& R) {
 #pragma unroll
@@ -136,12 +143,11 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) out[p][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    uint32_t nib_mask, bf16_128;
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib_mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bf16_128));
 
-    GroupRegs<NP, STEPS> nxt;
-    if (g_begin < g_end) load_group(g_begin, nxt);
-    for (int g = g_begin; g < g_end; ++g) {
-        const GroupRegs<NP, STEPS> cur = nxt;
-        if (g + 1 < g_end) load_group(g + 1, nxt);
+    auto compute_group = [&](const GroupRegs<NP, STEPS>& cur) {
         f32x4 acc[NP][4], accx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < NP; ++p)
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[p][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        afr, as_bf16x8(dequant_word(cur.q[p][st][j])), acc[p][j], 0, 0, 0);
+                        afr, as_bf16x8(dequant_word(cur.q[p][st][j], nib_mask, bf16_128)), acc[p][j], 0, 0, 0);
         }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -169,15 +175,38 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
                 for (int v = 0; v < 4; ++v) out[p][j][v] = fmaf(s, fmaf(-zz, accx[v], acc[p][j][v]), out[p][j][v]);
             }
         }
-    }
+    };
 
-    // split-K reduction over the 4 waves, then the epilogue: 256 threads = 16 rows x 16 column quads
+#if MOE_INT4_DEPTH == 2
+    // three register sets in rotation: two groups in flight while one is computed
+    GroupRegs<NP, STEPS> ra, rb, rc;
+    if (g_begin < g_end) load_group(g_begin, ra);
+    if (g_begin + 1 < g_end) load_group(g_begin + 1, rb);
+    for (int g = g_begin; g < g_end; g += 3) {
+        if (g + 2 < g_end) load_group(g + 2, rc);
+        compute_group(ra);
+        if (g + 1 >= g_end) break;
+        if (g + 3 < g_end) load_group(g + 3, ra);
+        compute_group(rb);
+        if (g + 2 >= g_end) break;
+        if (g + 4 < g_end) load_group(g + 4, rb);
+        compute_group(rc);
+    }
+#else
+    GroupRegs<NP, STEPS> nxt;
+    if (g_begin < g_end) load_group(g_begin, nxt);
+    for (int g = g_begin; g < g_end; ++g) {
+        const GroupRegs<NP, STEPS> cur = nxt;
+        if (g + 1 < g_end) load_group(g + 1, nxt);
+        compute_group(cur);
+    }
+#endif
+
+    // split-K reduction over the waves, then the epilogue: 256 threads = 16 rows x 16 column quads
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) red[wave][p][v][lane][j] = out[p][j][v];
+        for (int j = 0; j < 4; ++j) red[wave][v][lane][j] = out[0][j][v];
     __syncthreads();
     {
         const int sl = tid & 63, v = tid >> 6;  // source lane and row-in-quad of the C fragment
@@ -187,13 +216,15 @@ __global__ __launch_bounds__(NT) void gemm_int4_kernel(
         float res[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                a0 += red[w][0][v][sl][j];
-                if (GATE_UP) a1 += red[w][NP - 1][v][sl][j];
+            float res_j;
+            if (GATE_UP) {
+                const float g = red[0][v][sl][j] + red[1][v][sl][j];
+                const float u = red[2][v][sl][j] + red[3][v][sl][j];
+                res_j = g / (1.0f + __expf(-g)) * u;
+            } else {
+                res_j = (red[0][v][sl][j] + red[1][v][sl][j]) + (red[2][v][sl][j] + red[3][v][sl][j]);
             }
-            res[j] = GATE_UP ? a0 / (1.0f + __expf(-a0)) * a1 : a0;
+            res[j] = res_j;
         }
         uint2 o;
         o.x = pack_bf16x2(res[0], res[1]);
