@@ -25,15 +25,19 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a).
+// Two fp32 -> packed pair of bf16 (low half = a), one v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// SiLU(g) * u with a hardware reciprocal (1 ulp) instead of an IEEE division.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Inclusive prefix sum of `v` over a block of NW waves; `scratch` holds >= NW ints.

@@ -328,17 +328,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
 #pragma unroll
             for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
+                for (int v = 0; v < 16; v += 2) {
+                    // accumulator values v and v+1 are rows rl and rl+1 of the same column
                     const int rl = wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3);
                     if (GATE_UP) {
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
-                            const float g = acc[i][j][v], u = acc[i][j + 2][v];
-                            ct[rl * LD + wn * 64 + j * 32 + fr] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                            const uint32_t pr = pack_bf16x2(silu_mul(acc[i][j][v], acc[i][j + 2][v]),
+                                                            silu_mul(acc[i][j][v + 1], acc[i][j + 2][v + 1]));
+                            ct[rl * LD + wn * 64 + j * 32 + fr] = static_cast<uint16_t>(pr);
+                            ct[(rl + 1) * LD + wn * 64 + j * 32 + fr] = static_cast<uint16_t>(pr >> 16);
                         }
                     } else {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) ct[rl * LD + j * 32 + fr] = f32_to_bf16(acc[i][j][v]);
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t pr = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
+                            ct[rl * LD + j * 32 + fr] = static_cast<uint16_t>(pr);
+                            ct[(rl + 1) * LD + j * 32 + fr] = static_cast<uint16_t>(pr >> 16);
+                        }
                     }
                 }
         }

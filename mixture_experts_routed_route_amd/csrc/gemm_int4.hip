@@ -220,7 +220,7 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? (MOE_INT4_DEPTH == 2 ? 3 : 4) : 2)
             if (GATE_UP) {
                 const float g = red[0][v][sl][j] + red[1][v][sl][j];
                 const float u = red[2][v][sl][j] + red[3][v][sl][j];
-                res_j = g / (1.0f + __expf(-g)) * u;
+                res_j = silu_mul(g, u);
             } else {
                 res_j = (red[0][v][sl][j] + red[1][v][sl][j]) + (red[2][v][sl][j] + red[3][v][sl][j]);
             }
