@@ -3,38 +3,41 @@
 // as in ferrum-kernels triton_fused_moe.rs).
 //
 // Tiling.  A tile is up to BM consecutive sorted rows of ONE expert: expert e's padded span
-// [off[e], off[e+1]) is cut into ceil(span/BM) tiles.  Each workgroup rebuilds that tile list
-// from expert_offsets (a 256-wide LDS scan of the per-expert tile counts), so the grid is a
-// static worst-case bound (ceil(max_pad/BM) + E row tiles per column panel) and tiles past the
-// end exit at once.  The weight panel of a tile is BP = 256 weight rows: for gate/up the 128
+// [off[e], off[e+1]) is cut into ceil(span/BM) row tiles.  Each workgroup rebuilds that list from
+// expert_offsets once (a 256-wide LDS scan of the per-expert row-tile counts), so launches depend
+// on host scalars only.  The weight panel of a tile is BP = 256 weight rows: for gate/up the 128
 // gate rows and the 128 up rows of the same output columns (SiLU(gate)*up is formed from the
 // fp32 accumulators), for down 256 output columns.
 //
 // Pipeline.  NW waves in a (NW/2) x 2 grid, each owning 64 x 128 of the tile as 32x32x16 bf16
-// MFMA blocks with fp32 accumulators; on gfx950 the 32x32x16 form runs at the full bf16 rate,
-// the 16x16x32 form at about half of it.  256-row tiles use 8 waves, two per SIMD, so one
-// wave's LDS and barrier waits overlap the other's MFMAs.  K advances BK at a time through a ring of
+// MFMA blocks with fp32 accumulators.  256-row tiles use 8 waves, two per SIMD, so one wave's
+// LDS and barrier waits overlap the other's MFMAs.  K advances BK at a time through a ring of
 // STAGES LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4: no VGPR
-// staging, no LDS store instructions; issued from inline asm, see dma16); STAGES-1 stages are in flight while one is computed.
-// Each thread waits on its own loads with an explicit vmcnt, then a bare s_barrier makes the
-// stage visible to all waves (a fenced barrier would drain the later stages' loads too).
-// LDS rows are XOR-swizzled in 16-byte chunks so that the 32-row fragment reads are free of LDS
-// bank conflicts.
-// Fragments of the next K step are read from LDS while the MFMAs of the current one run.  Rows that hold no token
-// (sentinels, padding) load a harmless valid row and are never stored; k past K loads zeros.
+// staging, no LDS store instructions; issued from inline asm, see dma16); STAGES-1 stages are in
+// flight while one is computed.  Each thread waits on its own loads with an explicit vmcnt, then
+// a bare s_barrier makes the stage visible to all waves (a fenced barrier would drain the later
+// stages' loads too).  LDS rows are XOR-swizzled in 16-byte chunks so that the 32-row fragment
+// reads are free of LDS bank conflicts.  Fragments of the next K step are read from LDS while the
+// MFMAs of the current one run.  Rows that hold no token (sentinels, padding) load a harmless
+// valid row and are never stored; k past K loads zeros.
 //
 // Ragged tails.  An expert's last tile usually holds fewer tokens than BM.  Its rows past the last
 // token are sentinels, so each wave counts the 32-row A fragments of its own rows that hold a
 // token (0, 1 or 2) and runs a main loop compiled for that count: empty fragments cost no LDS
 // reads and no MFMAs, and the wave still loads and meets the barriers.
 //
-// Schedule.  Workgroup ids are dealt round-robin over the 8 XCDs, so the id is remapped to
-// give each XCD a contiguous range of logical tiles.  Logical tiles run in bands of GM row
-// tiles: within a band, GM row tiles of one column panel are consecutive, so the ~32 tiles an
-// XCD runs at once cover a few panels x GM row tiles and share A tiles and weight panels in
-// that XCD's L2.
+// Schedule.  Logical tiles run in bands of GM row tiles: within a band, GM row tiles of one
+// column panel are consecutive.  Workgroup ids are dealt round-robin over the 8 XCDs, so XCD x
+// takes the contiguous range [x*T/8, (x+1)*T/8) of the T real tiles and its workgroups stride
+// through it; the ~32 tiles an XCD runs at once then cover a few panels x GM row tiles and share
+// A tiles and weight panels in that XCD's L2.  With more than 4 tiles per compute unit the grid
+// is persistent (one workgroup per compute unit): before a tile's epilogue the workgroup loads the
+// next tile's rows and issues its first stage into the free LDS buffer, so the next tile's setup
+// and first load latency hide behind this epilogue.  With fewer tiles, one workgroup per tile.
 //
-// Epilogue.  The bf16 output tile is staged in LDS and written back with 16-byte row stores.
+// Epilogue.  Straight from the accumulators, no LDS: neighbouring lanes (columns c, c+1) swap
+// one value through DPP so that each lane holds two adjacent columns of one row, converts them
+// with one v_cvt_pk_bf16_f32 and stores 4 bytes.
 #include <type_traits>
 
 #include "device_common.h"
@@ -46,9 +49,6 @@ namespace {
 constexpr int BP = 256;
 #ifndef MOE_GEMM_BAND_ROWS
 #define MOE_GEMM_BAND_ROWS 2048   // sorted rows per band of the tile schedule
-#endif
-#ifndef MOE_GEMM_XCD_REMAP
-#define MOE_GEMM_XCD_REMAP 1
 #endif
 #ifndef MOE_GEMM_BIG_BK
 #define MOE_GEMM_BIG_BK 64       // k per LDS stage of the 256-row tiles
@@ -105,6 +105,17 @@ struct Cfg {
 // conflicts for the 32-row x 2-chunk fragment reads of the 32x32x16 MFMA.
 __device__ __forceinline__ int swz_chunk(int row, int c, int rp, int cpr) { return c ^ ((row / rp) % cpr); }
 
+// Logical tile L (0 <= L < m_real * n_tiles) -> (row tile, column panel): bands of GM row tiles,
+// row tiles fastest inside a band, so the tiles an XCD runs together share A tiles and panels.
+__device__ __forceinline__ void decode_tile(int L, int gm, int m_real, int n_tiles, int& m_t, int& n_t) {
+    const int band_tiles = gm * n_tiles;
+    const int band = L / band_tiles;
+    const int in_band = L - band * band_tiles;
+    const int gm_b = min(gm, m_real - band * gm);
+    n_t = in_band / gm_b;
+    m_t = band * gm + (in_band - n_t * gm_b);
+}
+
 template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W0,
@@ -112,65 +123,75 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                                                           uint16_t* __restrict__ C,
                                                           const int32_t* __restrict__ sorted_ids,
                                                           const int32_t* __restrict__ offsets, int P, int top_k,
-                                                          int E, int N, int K, int max_pad, int m_tiles,
-                                                          int n_tiles) {
+                                                          int E, int N, int K, int max_pad, int n_tiles) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
     constexpr int NT = F::NT;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
     __shared__ int s_scan[NW];
-    __shared__ int s_row[BM];
-    __shared__ int s_info[4];
+    __shared__ int s_lo[kMaxE], s_hi[kMaxE], s_tb[kMaxE + 1];  // expert span, first row tile
+    __shared__ int s_row[2][BM];                                  // A source row per tile row
+    __shared__ int s_h[2];                                        // rows up to the last token
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // ---- logical tile: XCD-contiguous ranges, then bands of GM row tiles x all panels
-    const int nwg = gridDim.x;
-    const int bid = blockIdx.x;
-    const int L = MOE_GEMM_XCD_REMAP ? (bid & 7) * (nwg >> 3) + (bid >> 3) : bid;
-    const int band_tiles = F::GM * n_tiles;
-    const int band = L / band_tiles;
-    const int in_band = L - band * band_tiles;
-    const int gm_b = min(F::GM, m_tiles - band * F::GM);
-    if (gm_b <= 0) return;
-    const int n_t = in_band / gm_b;
-    const int m_t = band * F::GM + (in_band - n_t * gm_b);
-    if (n_t >= n_tiles) return;
-
-    // ---- which expert and rows this tile covers
-    int lo = 0, hi = 0;
-    if (tid < E) {
-        lo = min(max(offsets[tid], 0), max_pad);
-        hi = min(max(offsets[tid + 1], lo), max_pad);
-    }
-    const int nt_e = (hi - lo + BM - 1) / BM;
-    const int incl = block_inclusive_scan<NW>(nt_e, s_scan);
-    if (tid == 0) { s_info[0] = -1; s_info[3] = 0; }
-    __syncthreads();
-    if (tid < E && m_t >= incl - nt_e && m_t < incl) {
-        s_info[0] = tid;
-        s_info[1] = lo + (m_t - (incl - nt_e)) * BM;
-        s_info[2] = hi;
-    }
-    __syncthreads();
-    const int e = s_info[0];
-    if (e < 0) return;
-    const int r0 = s_info[1];
-    const int r_end = min(r0 + BM, s_info[2]);
-    for (int i = tid; i < BM; i += NT) {
-        const int r = r0 + i;
-        int src = -1;
-        if (r < r_end) {
-            const int p = sorted_ids[r];
-            if (p >= 0 && p < P) src = GATE_UP ? p / top_k : r;
+    // ---- expert spans and their row tiles (once per workgroup)
+    {
+        int lo = 0, hi = 0;
+        if (tid < E) {
+            lo = min(max(offsets[tid], 0), max_pad);
+            hi = min(max(offsets[tid + 1], lo), max_pad);
         }
-        s_row[i] = src;
-        if (src >= 0) atomicMax(&s_info[3], i + 1);
+        const int nt_e = (hi - lo + BM - 1) / BM;
+        const int incl = block_inclusive_scan<NW>(nt_e, s_scan);
+        if (tid < E) { s_lo[tid] = lo; s_hi[tid] = hi; s_tb[tid + 1] = incl; }
+        if (tid == 0) { s_tb[0] = 0; s_h[0] = 0; s_h[1] = 0; }
+        __syncthreads();
     }
+    const int m_real = s_tb[E];
+
+    // ---- this workgroup's logical tiles.  Workgroup ids go round-robin over the 8 XCDs, so XCD x
+    // takes the contiguous range [x*T/8, (x+1)*T/8) and its workgroups stride through it.
+    const long long T = static_cast<long long>(m_real) * n_tiles;
+    const int per_xcd = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int l_hi = static_cast<int>(T * (xcd + 1) / 8);
+    int L = static_cast<int>(T * xcd / 8) + slot;
+    if (slot >= per_xcd || L >= l_hi) return;
+
+    // tile L -> expert e, first sorted row r0, rows end r_end, first output column n0
+    auto locate = [&](int Lt, int& e, int& r0, int& r_end, int& n0) {
+        int m_t, n_t;
+        decode_tile(Lt, F::GM, m_real, n_tiles, m_t, n_t);
+        int a = 0, b = E - 1;  // largest expert whose first row tile is <= m_t
+        while (a < b) {
+            const int mid = (a + b + 1) >> 1;
+            if (s_tb[mid] <= m_t) a = mid; else b = mid - 1;
+        }
+        e = a;
+        r0 = s_lo[e] + (m_t - s_tb[e]) * BM;
+        r_end = min(r0 + BM, s_hi[e]);
+        n0 = n_t * F::NCOL;
+    };
+    // A source rows of a tile into s_row[buf] (rows without a token: -1) and s_h[buf]
+    auto load_rows = [&](int buf, int r0, int r_end) {
+        for (int i = tid; i < BM; i += NT) {
+            const int r = r0 + i;
+            int src = -1;
+            if (r < r_end) {
+                const int p = sorted_ids[r];
+                if (p >= 0 && p < P) src = GATE_UP ? p / top_k : r;
+            }
+            s_row[buf][i] = src;
+            if (src >= 0) atomicMax(&s_h[buf], i + 1);
+        }
+    };
+
+    int e, r0, r_end, n0;
+    locate(L, e, r0, r_end, n0);
+    int buf = 0;
+    load_rows(buf, r0, r_end);
     __syncthreads();
-    // rows at or past h_rows hold no token (an expert's sentinels follow its tokens), so a wave whose
-    // 32-row fragments all lie there skips their MFMAs
-    const int h_rows = s_info[3];
-    const int n0 = n_t * F::NCOL;
 
     // ---- per-lane DMA sources: instruction q of this wave fills ROWS_PER_INST rows
     const int lrow = lane / F::CPR;   // row within the instruction's block
@@ -178,33 +199,39 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     const uint16_t* a_src[F::A_INST];
     const uint16_t* b_src[F::B_INST];
     int a_kc[F::A_INST], b_kc[F::B_INST];
+    auto set_sources = [&](int bf, int e_, int r0_, int n0_) {
 #pragma unroll
-    for (int q = 0; q < F::A_INST; ++q) {
-        const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
-        const int kc = swz_chunk(row, pc, F::RP, F::CPR);
-        const int src = s_row[row];
-        // a row without a token reads a row that is always in bounds (token 0, or the tile's
-        // first sorted row r0 < max_pad); its results are never stored
-        const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0);
-        a_src[q] = A + static_cast<size_t>(srow) * K + kc * 8;
-        a_kc[q] = kc * 8;
-    }
+        for (int q = 0; q < F::A_INST; ++q) {
+            const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
+            const int kc = swz_chunk(row, pc, F::RP, F::CPR);
+            const int src = s_row[bf][row];
+            // a row without a token reads a row that is always in bounds (token 0, or the tile's
+            // first sorted row r0 < max_pad); its results are never stored
+            const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0_);
+            a_src[q] = A + static_cast<size_t>(srow) * K + kc * 8;
+            a_kc[q] = kc * 8;
+        }
 #pragma unroll
-    for (int q = 0; q < F::B_INST; ++q) {
-        const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
-        const int kc = swz_chunk(row, pc, F::RP, F::CPR);
-        int n;
-        const uint16_t* W;
-        if (GATE_UP) { n = n0 + (row & (BP / 2 - 1)); W = row < BP / 2 ? W0 : W1; }
-        else { n = n0 + row; W = W0; }
-        n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
-        b_src[q] = W + (static_cast<size_t>(e) * N + n) * K + kc * 8;
-        b_kc[q] = kc * 8;
-    }
+        for (int q = 0; q < F::B_INST; ++q) {
+            const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
+            const int kc = swz_chunk(row, pc, F::RP, F::CPR);
+            int n;
+            const uint16_t* W;
+            if (GATE_UP) { n = n0_ + (row & (BP / 2 - 1)); W = row < BP / 2 ? W0 : W1; }
+            else { n = n0_ + row; W = W0; }
+            n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
+            b_src[q] = W + (static_cast<size_t>(e_) * N + n) * K + kc * 8;
+            b_kc[q] = kc * 8;
+        }
+    };
+    set_sources(buf, e, r0, n0);
 
+    const int nk = (K + BK - 1) / BK;
+    int sb = 0;  // running stage count: stage t of the current tile lives in LDS buffer (sb + t) % STAGES
+    auto stage_ptr = [&](int t) { return smem + ((sb + t) % STAGES) * F::STAGE_ELEMS; };
     auto issue = [&](int kt) {
         const int k0 = kt * BK;
-        uint16_t* st = smem + (kt % STAGES) * F::STAGE_ELEMS;
+        uint16_t* st = stage_ptr(kt);
 #pragma unroll
         for (int q = 0; q < F::A_INST; ++q) {
             const void* g = (k0 + a_kc[q] < K) ? static_cast<const void*>(a_src[q] + k0)
@@ -222,12 +249,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     const int wm = wave >> 1, wn = wave & 1;  // wave grid WAVES_M x 2
     // 32x32x16 MFMA blocks: each wave holds FI x 4 blocks of 32x32 fp32 accumulators
     f32x16 acc[F::FI][4];
-#pragma unroll
-    for (int i = 0; i < F::FI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     // fragment LDS offsets (elements) within a stage: lane row fr = lane%32, k-chunk fc = lane/32
     const int fr = lane & 31, fc = lane >> 5;
@@ -244,14 +265,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // every fragment starts on a multiple of 32 rows, so its swizzle depends on the lane only
     const int fswz = (fr / F::RP) % F::CPR;
 
-    const int nk = (K + BK - 1) / BK;
     constexpr int KK = BK / 16;  // 32x32x16 MFMA k-steps per stage (even)
     bf16x8 fa[2][F::FI], fb[2][4];
     // fragments of k-step kk of stage s into register set `set` (the first NF A fragments)
     auto read = [&](auto nf_c, int s, int kk, int set) {
         constexpr int NF = decltype(nf_c)::value;
         if constexpr (NF > 0) {
-            const uint16_t* st = smem + (s % STAGES) * F::STAGE_ELEMS;
+            const uint16_t* st = stage_ptr(s);
             const int cx = ((kk * 2 + fc) ^ fswz) << 3;
 #pragma unroll
             for (int i = 0; i < NF; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
@@ -286,10 +306,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         __builtin_amdgcn_s_barrier();
         if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
     };
-
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue(s);
     // Each k-step's MFMAs are issued after the next k-step's fragment reads (and, at a stage
     // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
     // NF = A fragments of this wave that hold tokens; every wave still loads and meets the barriers.
@@ -310,55 +326,83 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         }
     };
     static_assert(F::FI == 2, "tail skipping assumes two A fragments per wave");
-    const int nf = __builtin_amdgcn_readfirstlane(min(max((h_rows - wm * F::WM + 31) / 32, 0), F::FI));
-    if (nf == 2) main_loop(std::integral_constant<int, 2>{});
-    else if (nf == 1) main_loop(std::integral_constant<int, 1>{});
-    else main_loop(std::integral_constant<int, 0>{});
 
-    // ---- epilogue: bf16 tile through LDS, 16-byte row stores.  Tile row stride NCOL+8.
-    wait_vmcnt<0>();
-    __syncthreads();
-    constexpr int PASS_COLS = 128;                 // columns staged per pass
-    constexpr int PASSES = F::NCOL / PASS_COLS;    // 1 for gate/up, 2 for down
-    constexpr int LD = PASS_COLS + 8;
-    uint16_t* ct = smem;
+    // The first tile issues its first STAGES-1 stages here; later tiles find stage 0 already in
+    // flight (issued by the previous tile before its epilogue) and issue stages 1..STAGES-2.
+    for (int t = 0; t < STAGES - 1; ++t)
+        if (t < nk) issue(t);
+
+    while (true) {
+        // rows up to the last token of this tile (an expert's sentinels follow its tokens): a wave
+        // whose 32-row fragments all lie past it skips their MFMAs
+        const int h_rows = s_h[buf];
 #pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-        if (GATE_UP || wn == pass) {
+        for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-            for (int i = 0; i < F::FI; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    // accumulator values v and v+1 are rows rl and rl+1 of the same column
-                    const int rl = wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3);
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        const int nf = __builtin_amdgcn_readfirstlane(min(max((h_rows - wm * F::WM + 31) / 32, 0), F::FI));
+        if (nf == 2) main_loop(std::integral_constant<int, 2>{});
+        else if (nf == 1) main_loop(std::integral_constant<int, 1>{});
+        else main_loop(std::integral_constant<int, 0>{});
+
+        // ---- next tile: its rows, sources and first stage, before this tile's epilogue
+        const int L_next = L + per_xcd;
+        const bool more = L_next < l_hi;
+        int e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
+        if (more) {
+            locate(L_next, e2, r02, r_end2, n02);
+            if (tid == 0) s_h[buf ^ 1] = 0;
+            __syncthreads();  // every wave is past this tile's last stage reads and s_h is reset
+            load_rows(buf ^ 1, r02, r_end2);
+            __syncthreads();
+            set_sources(buf ^ 1, e2, r02, n02);
+            // stage 0 of the next tile goes to buffer (sb + nk) % STAGES, which held stage nk-STAGES+1
+            // .. of this tile at the latest and is no longer read by any wave
+            sb += nk;
+            issue(0);
+            sb -= nk;
+        }
+
+        // ---- epilogue straight from the accumulators: neighbour lanes (columns c, c+1) swap one
+        // value so that each lane stores two adjacent bf16 columns of one row as 4 bytes
+        const bool odd = (lane & 1) != 0;
+        const int ccol = n0 + (fr & ~1);
+#pragma unroll
+        for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const int rl = wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3);  // row of value v
+                const int row_l = rl + (odd ? 1 : 0);
+                const bool ok = s_row[buf][row_l] >= 0;
+                uint16_t* crow = C + static_cast<size_t>(r0 + row_l) * N;
+                constexpr int NJ = GATE_UP ? 2 : 4;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    float h0, h1;  // values v (row rl) and v+1 (row rl+1) of this lane's column
                     if (GATE_UP) {
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const uint32_t pr = pack_bf16x2(silu_mul(acc[i][j][v], acc[i][j + 2][v]),
-                                                            silu_mul(acc[i][j][v + 1], acc[i][j + 2][v + 1]));
-                            ct[rl * LD + wn * 64 + j * 32 + fr] = static_cast<uint16_t>(pr);
-                            ct[(rl + 1) * LD + wn * 64 + j * 32 + fr] = static_cast<uint16_t>(pr >> 16);
-                        }
+                        h0 = silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+                        h1 = silu_mul(acc[i][j][v + 1], acc[i][j + 2][v + 1]);
                     } else {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t pr = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
-                            ct[rl * LD + j * 32 + fr] = static_cast<uint16_t>(pr);
-                            ct[(rl + 1) * LD + j * 32 + fr] = static_cast<uint16_t>(pr >> 16);
-                        }
+                        h0 = acc[i][j][v];
+                        h1 = acc[i][j][v + 1];
                     }
+                    const float send = odd ? h0 : h1;
+                    const float got = __int_as_float(__builtin_amdgcn_update_dpp(
+                        0, __float_as_int(send), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+                    const uint32_t pr = odd ? pack_bf16x2(got, h1) : pack_bf16x2(h0, got);
+                    const int col = ccol + (GATE_UP ? wn * 64 + j * 32 : wn * 128 + j * 32);
+                    if (ok && col < N) *reinterpret_cast<uint32_t*>(crow + col) = pr;
                 }
-        }
-        __syncthreads();
-        constexpr int CH = PASS_COLS / 8;  // 16-byte chunks per row
-        for (int idx = tid; idx < BM * CH; idx += NT) {
-            const int rl = idx / CH, ch = idx - rl * CH;
-            const int col = n0 + pass * PASS_COLS + ch * 8;
-            if (s_row[rl] >= 0 && col < N)
-                *reinterpret_cast<u32x4*>(C + static_cast<size_t>(r0 + rl) * N + col) =
-                    *reinterpret_cast<const u32x4*>(ct + rl * LD + ch * 8);
-        }
-        if (PASSES > 1) __syncthreads();
+            }
+        if (!more) break;
+        L = L_next;
+        e = e2; r0 = r02; r_end = r_end2; n0 = n02;
+        sb += nk;
+        buf ^= 1;
+        for (int t = 1; t < STAGES - 1; ++t)
+            if (t < nk) issue(t);
     }
 }
 
@@ -367,12 +411,29 @@ hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1,
                       const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
                       int max_pad, hipStream_t s) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
-    const int m_tiles = (max_pad + BM - 1) / BM + E;
     const int n_tiles = (N + F::NCOL - 1) / F::NCOL;
-    const long long tiles = static_cast<long long>(m_tiles) * n_tiles;
-    const int grid = static_cast<int>((tiles + 7) / 8 * 8);
-    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW><<<grid, F::NT, 0, s>>>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N,
-                                                                 K, max_pad, m_tiles, n_tiles);
+    // Persistent (one workgroup per compute unit, a multiple of the 8 XCDs) when there are more
+    // than 4 tiles per compute unit at worst.  With fewer, one workgroup per tile lets the hardware
+    // dispatcher hand late tiles to whichever compute unit frees up first, which balances better
+    // than a static share when a few long tiles remain.
+    static int cus[64] = {0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cus[dev] == 0) {
+        int n = 0;
+        err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        cus[dev] = n;
+    }
+    const long long worst = static_cast<long long>((max_pad + BM - 1) / BM + E) * n_tiles;
+    long long grid = cus[dev] / 8 * 8;
+    if (grid < 8) grid = 8;
+    const long long worst8 = (worst + 7) / 8 * 8;
+    if (worst8 <= 4 * grid) grid = worst8;
+    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW><<<static_cast<int>(grid), F::NT, 0, s>>>(
+        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles);
     return hipGetLastError();
 }
 

@@ -63,3 +63,56 @@ def test_every_addressed_row_in_bounds(case):
         for BM in (128, 256):
             for kind, idx, lim in touched_rows(P, top_k, E, 256, al, gate_up, BM):
                 assert 0 <= idx < lim, f"{name} gate_up={gate_up} BM={BM}: {kind} row {idx} outside [0, {lim})"
+
+
+def _decode_tile(L, gm, m_real, n_tiles):
+    """Band decode of a logical tile (restates the kernel's integer arithmetic)."""
+    band_tiles = gm * n_tiles
+    band = L // band_tiles
+    in_band = L - band * band_tiles
+    gm_b = min(gm, m_real - band * gm)
+    n_t = in_band // gm_b
+    return band * gm + (in_band - n_t * gm_b), n_t
+
+
+def _assigned_tiles(m_real, n_tiles, grid, gm):
+    """Every (row tile, panel) that the workgroups of a launch process, in kernel order."""
+    T = m_real * n_tiles
+    per_xcd = grid >> 3
+    out = []
+    for bid in range(grid):
+        xcd, slot = bid & 7, bid >> 3
+        l_hi = T * (xcd + 1) // 8
+        L = T * xcd // 8 + slot
+        while slot < per_xcd and L < l_hi:
+            out.append(_decode_tile(L, gm, m_real, n_tiles))
+            L += per_xcd
+    return out
+
+
+@pytest.mark.parametrize("m_real,n_tiles,grid,gm", [
+    (37, 112, 256, 8), (37, 16, 672, 8), (1, 1, 8, 8), (5, 3, 256, 8), (351, 8, 256, 8),
+    (64, 11, 256, 16), (9, 7, 16, 4), (200, 1, 256, 8), (3, 200, 24, 2)])
+def test_persistent_assignment_covers_each_tile_once(m_real, n_tiles, grid, gm):
+    """The workgroups of a launch (persistent or one per tile) process every (row tile, column
+    panel) of the real tile grid exactly once."""
+    got = _assigned_tiles(m_real, n_tiles, grid, gm)
+    assert len(got) == m_real * n_tiles
+    assert sorted(got) == [(m, n) for m in range(m_real) for n in range(n_tiles)]
+
+
+def test_expert_of_row_tile_binary_search():
+    """Largest expert whose first row tile is <= m_t, with empty experts in between (the kernel's
+    binary search over the inclusive tile scan)."""
+    nt = [0, 3, 0, 0, 2, 0, 1, 0]
+    tb = np.concatenate([[0], np.cumsum(nt)])
+    E = len(nt)
+    for m_t in range(int(tb[-1])):
+        a, b = 0, E - 1
+        while a < b:
+            mid = (a + b + 1) >> 1
+            if tb[mid] <= m_t:
+                a = mid
+            else:
+                b = mid - 1
+        assert tb[a] <= m_t < tb[a + 1] and nt[a] > 0
