@@ -6,6 +6,7 @@
  *   moe_route         top-k softmax routing of the router logits
  *   moe_align         per-expert histogram, block-padded expert_offsets,
  *                     sorted pair ids with sentinels, one expert id per block
+ *   moe_route_align   the two above in one call (one launch for decode batches)
  *   moe_grouped_gemm  grouped gate/up GEMM with fused SiLU(gate)*up, and the
  *                     grouped down GEMM (bf16 or GPTQ-int4 expert weights)
  *   moe_lora_fold     optional per-expert down-projection LoRA fold, in place
@@ -135,6 +136,18 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_exp
                      int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
                      int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, void* workspace,
                      int64_t workspace_bytes, moe_stream stream);
+
+/* A1+A2 — moe_route followed by moe_align on its topk_ids, with the same
+ * arguments, results and error behaviour as the two calls (topk_ids is both the
+ * routing output and the alignment input; num_pairs = num_tokens*top_k).  When
+ * the pairs fit one alignment chunk (num_pairs <= 2048, decode batches) both
+ * steps run in one single-workgroup launch; otherwise it enqueues the launches
+ * of the two calls.  num_tokens == 0 aligns zero pairs (fills the sentinels). */
+moe_status moe_route_align(const float* logits, int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                           int32_t renormalize, int32_t* topk_ids, float* topk_w, int32_t block_size,
+                           int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                           int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, void* workspace,
+                           int64_t workspace_bytes, moe_stream stream);
 
 /* Expert weights of one projection, K = contraction, N = outputs.
  *   MOE_W_BF16:      data = bf16 [E, N, K] (K contiguous); scales, qzeros unused.

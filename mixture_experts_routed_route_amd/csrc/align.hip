@@ -1,7 +1,8 @@
 // Block-size alignment of the (token, slot) pairs by expert (ferrum-kernels cuda/moe.rs:
 // moe_build_pairs_by_token, moe_align_block_size_pair_ids): a stable counting sort.
 //
-// The pairs are cut into chunks of kChunk ids; one 256-thread workgroup owns a chunk.
+// The pairs are cut into chunks of kChunk ids; one 256-thread workgroup owns a chunk.  When
+// all pairs fit one chunk (decode batches), step 1 is folded into step 2: one launch.
 //   1. align_count: each workgroup builds its chunk's expert histogram in LDS and
 //      writes it to the workspace row ws[chunk][0..E).
 //   2. align_scatter: each workgroup reads the whole [chunks, E] table, derives the
@@ -14,6 +15,7 @@
 // Deterministic: no order-dependent atomics (the LDS histogram atomics only count).
 #include "device_common.h"
 #include "launchers.h"
+#include "route_common.h"
 
 namespace moe {
 namespace {
@@ -54,29 +56,58 @@ __device__ __forceinline__ uint64_t peer_mask(int key, bool active) {
     return m;
 }
 
-__global__ __launch_bounds__(kThreads) void align_scatter_kernel(
+// SINGLE: all pairs fit one chunk (G == 1); the workgroup builds the histogram itself, so the
+// alignment is one launch with no workspace round trip.  g = this workgroup's chunk.  NWAVES:
+// waves of the workgroup (4, or 16 in the fused route+align kernel); pairs are held by the first
+// kWaves waves only, the others take part in the scan, the fills and the barriers.
+template <bool SINGLE, int NWAVES = kWaves>
+__device__ __forceinline__ void align_scatter_body(
     const int32_t* __restrict__ ids, int P, int E, int bs, const int32_t* __restrict__ ws, int G,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
-    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad) {
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad,
+    int g) {
     __shared__ int s_off[kMaxE + 1];   // block-padded offsets
     __shared__ int s_cnt[kMaxE];       // real rows per expert
     __shared__ int s_run[kWaves][kMaxE];
-    __shared__ int s_scan[kWaves];
+    __shared__ int s_scan[NWAVES];
+    constexpr int NT = 64 * NWAVES;
+    static_assert(SINGLE || NWAVES == kWaves, "several chunks: 4 waves per workgroup");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = blockIdx.x;
+
+    // this wave's run of pairs, loaded once (expert id, or -1 past the end / out of range); waves
+    // past the first kWaves start past kChunk >= P and hold none
+    const int run0 = g * kChunk + wave * (64 * kIters);
+    int e_reg[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int p = run0 + it * 64 + lane;
+        const int e = p < P ? ids[p] : -1;
+        e_reg[it] = (e >= 0 && e < E) ? e : -1;
+    }
 
     // totals and this chunk's start inside each expert
     int tot = 0, before = 0;
-    if (tid < E) {
-        for (int c = 0; c < G; ++c) {
-            const int v = ws[static_cast<size_t>(c) * E + tid];
-            before += (c < g) ? v : 0;
-            tot += v;
+    if constexpr (SINGLE) {
+        for (int e = tid; e < E; e += NT) s_cnt[e] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kIters; ++it)
+            if (e_reg[it] >= 0) atomicAdd(&s_cnt[e_reg[it]], 1);
+        __syncthreads();
+        if (tid < E) tot = s_cnt[tid];
+        __syncthreads();
+    } else {
+        if (tid < E) {
+            for (int c = 0; c < G; ++c) {
+                const int v = ws[static_cast<size_t>(c) * E + tid];
+                before += (c < g) ? v : 0;
+                tot += v;
+            }
         }
     }
     const int padded = (tid < E) ? ((tot + bs - 1) / bs) * bs : 0;
-    const int incl = block_inclusive_scan_256(padded, s_scan);
+    const int incl = block_inclusive_scan<NWAVES>(padded, s_scan);
     if (tid < E) {
         s_off[tid] = incl - padded;
         s_cnt[tid] = tot;
@@ -95,26 +126,38 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
     // expert_ids for every block, sentinels for every row that no pair will fill
     const int stride = G * kThreads;
     const int nblk = max_pad / bs;
-    for (int b = g * kThreads + tid; b < nblk; b += stride) {
-        const int r = b * bs;
-        expert_ids[b] = (r < total) ? upper_index(s_off, E, r) : -1;
-    }
-    for (int r = g * kThreads + tid; r < max_pad; r += stride) {
-        bool pad = r >= total;
-        if (!pad) {
-            const int e = upper_index(s_off, E, r);
-            pad = r >= s_off[e] + s_cnt[e];
+    if constexpr (SINGLE) {
+        // one thread per expert writes its blocks and its padding rows (at most bs-1); the rows
+        // and blocks past the padded total are shared out
+        if (tid < E) {
+            for (int b = s_off[tid] / bs; b < s_off[tid + 1] / bs; ++b) expert_ids[b] = tid;
+            for (int r = s_off[tid] + s_cnt[tid]; r < s_off[tid + 1]; ++r) sorted_ids[r] = P;
         }
-        if (pad) sorted_ids[r] = P;
+        for (int b = total / bs + tid; b < nblk; b += NT) expert_ids[b] = -1;
+        for (int r = total + tid; r < max_pad; r += NT) sorted_ids[r] = P;
+    } else {
+        for (int b = g * kThreads + tid; b < nblk; b += stride) {
+            const int r = b * bs;
+            expert_ids[b] = (r < total) ? upper_index(s_off, E, r) : -1;
+        }
+        for (int r = g * kThreads + tid; r < max_pad; r += stride) {
+            bool pad = r >= total;
+            if (!pad) {
+                const int e = upper_index(s_off, E, r);
+                pad = r >= s_off[e] + s_cnt[e];
+            }
+            if (pad) sorted_ids[r] = P;
+        }
     }
 
     // pass A: per-wave counts of each expert over the wave's run of pairs
-    const int run0 = g * kChunk + wave * (64 * kIters);
+#pragma unroll
     for (int it = 0; it < kIters; ++it) {
+        if (run0 + it * 64 >= P) break;  // wave-uniform
         const int p = run0 + it * 64 + lane;
         const bool in = p < P;
-        const int e = in ? ids[p] : -1;
-        const bool valid = in && e >= 0 && e < E;
+        const int e = e_reg[it];
+        const bool valid = e >= 0;
         const int key = valid ? e : 511;
         const uint64_t peers = peer_mask(key, in);
         const int rank = __popcll(peers & ((1ull << lane) - 1ull));
@@ -132,11 +175,13 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
     }
     __syncthreads();
     // pass B: place the pairs
+#pragma unroll
     for (int it = 0; it < kIters; ++it) {
+        if (run0 + it * 64 >= P) break;  // wave-uniform
         const int p = run0 + it * 64 + lane;
         const bool in = p < P;
-        const int e = in ? ids[p] : -1;
-        const bool valid = in && e >= 0 && e < E;
+        const int e = e_reg[it];
+        const bool valid = e >= 0;
         const int key = valid ? e : 511;
         const uint64_t peers = peer_mask(key, in);
         const int rank = __popcll(peers & ((1ull << lane) - 1ull));
@@ -151,6 +196,37 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
     }
 }
 
+template <bool SINGLE>
+__global__ __launch_bounds__(kThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int bs, const int32_t* __restrict__ ws, int G,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad) {
+    align_scatter_body<SINGLE>(ids, P, E, bs, ws, G, counts, offsets, sorted_ids, expert_ids, total_out, inv,
+                               max_pad, blockIdx.x);
+}
+
+// Routing and alignment of a small batch (pairs fit one chunk, at most kFusedTokens tokens) in one
+// workgroup and one launch: 16 waves route the tokens (one wave per token, up to four tokens per
+// wave interleaved), then the workgroup aligns the pairs they wrote.
+constexpr int kFusedWaves = 16;
+constexpr int kFusedTokens = 64;
+template <int EPL>
+__global__ __launch_bounds__(64 * kFusedWaves) void route_align_kernel(
+    const float* __restrict__ logits, int T, int E, int top_k, int renorm, int32_t* topk_ids, float* topk_w,
+    int bs, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (T <= kFusedWaves) {
+        if (wave < T) route_tokens<EPL, 1>(logits, wave, 0, T, E, top_k, renorm, topk_ids, topk_w, lane);
+    } else {
+        for (int t = wave; t < T; t += kFusedWaves * 4)
+            route_tokens<EPL, 4>(logits, t, kFusedWaves, T, E, top_k, renorm, topk_ids, topk_w, lane);
+    }
+    __syncthreads();  // the workgroup's id stores are visible to its own loads after the barrier
+    align_scatter_body<true, kFusedWaves>(topk_ids, T * top_k, E, bs, nullptr, 1, counts, offsets, sorted_ids,
+                                          expert_ids, total_out, inv, max_pad, 0);
+}
+
 }  // namespace
 
 int align_num_chunks(int64_t num_pairs) {
@@ -162,11 +238,35 @@ hipError_t launch_align(const int32_t* topk_ids, int P, int E, int bs, int32_t* 
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total, int32_t* inv, int max_pad,
                         int32_t* workspace, hipStream_t s) {
     const int G = align_num_chunks(P);
+    if (G == 1) {
+        align_scatter_kernel<true><<<1, kThreads, 0, s>>>(topk_ids, P, E, bs, workspace, 1, counts, offsets,
+                                                          sorted_ids, expert_ids, total, inv, max_pad);
+        return hipGetLastError();
+    }
     align_count_kernel<<<G, kThreads, 0, s>>>(topk_ids, P, E, workspace);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    align_scatter_kernel<<<G, kThreads, 0, s>>>(topk_ids, P, E, bs, workspace, G, counts, offsets, sorted_ids,
-                                                 expert_ids, total, inv, max_pad);
+    align_scatter_kernel<false><<<G, kThreads, 0, s>>>(topk_ids, P, E, bs, workspace, G, counts, offsets, sorted_ids,
+                                                        expert_ids, total, inv, max_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int renorm, int32_t* ids, float* w,
+                              int bs, int32_t* counts, int32_t* offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                              int32_t* total, int32_t* inv, int max_pad, int32_t* workspace, hipStream_t s) {
+    const int P = T * top_k;
+    if (align_num_chunks(P) > 1 || T > kFusedTokens) {
+        hipError_t err = launch_route(logits, T, E, top_k, renorm, ids, w, s);
+        if (err != hipSuccess) return err;
+        return launch_align(ids, P, E, bs, counts, offsets, sorted_ids, expert_ids, total, inv, max_pad, workspace, s);
+    }
+    const int epl = (E + 63) / 64;
+    switch (epl) {
+        case 1: route_align_kernel<1><<<1, 64 * kFusedWaves, 0, s>>>(logits, T, E, top_k, renorm, ids, w, bs, counts, offsets, sorted_ids, expert_ids, total, inv, max_pad); break;
+        case 2: route_align_kernel<2><<<1, 64 * kFusedWaves, 0, s>>>(logits, T, E, top_k, renorm, ids, w, bs, counts, offsets, sorted_ids, expert_ids, total, inv, max_pad); break;
+        case 3: route_align_kernel<3><<<1, 64 * kFusedWaves, 0, s>>>(logits, T, E, top_k, renorm, ids, w, bs, counts, offsets, sorted_ids, expert_ids, total, inv, max_pad); break;
+        default: route_align_kernel<4><<<1, 64 * kFusedWaves, 0, s>>>(logits, T, E, top_k, renorm, ids, w, bs, counts, offsets, sorted_ids, expert_ids, total, inv, max_pad); break;
+    }
     return hipGetLastError();
 }
 

@@ -186,6 +186,55 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_exp
                                            static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_route_align(const float* logits, int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                           int32_t renormalize, int32_t* topk_ids, float* topk_w, int32_t block_size,
+                           int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                           int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, void* workspace,
+                           int64_t workspace_bytes, moe_stream stream) {
+    const char* who = "moe_route_align";
+    REQUIRE(num_tokens >= 0, "%s: num_tokens %d is negative", who, num_tokens);
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256)
+        return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(top_k >= 1 && top_k <= num_experts, "%s: top_k %d not in [1, num_experts=%d]", who, top_k,
+            num_experts);
+    const int64_t num_pairs = static_cast<int64_t>(num_tokens) * top_k;
+    REQUIRE(num_pairs < INT32_MAX, "%s: num_tokens*top_k %lld out of range", who,
+            static_cast<long long>(num_pairs));
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    const int64_t need = max_padded(num_pairs, num_experts, block_size);
+    REQUIRE(max_pad >= need, "%s: max_pad %lld < required %lld", who, static_cast<long long>(max_pad),
+            static_cast<long long>(need));
+    REQUIRE(max_pad % block_size == 0, "%s: max_pad %lld is not a multiple of block_size %d", who,
+            static_cast<long long>(max_pad), block_size);
+    REQUIRE(max_pad < INT32_MAX, "%s: max_pad too large", who);
+    const int64_t ws_need = moe_align_workspace_bytes(num_pairs, num_experts);
+    REQUIRE(workspace_bytes >= ws_need, "%s: workspace_bytes %lld < required %lld", who,
+            static_cast<long long>(workspace_bytes), static_cast<long long>(ws_need));
+    if (num_tokens > 0) {
+        REQUIRE_PTR(who, logits);
+        REQUIRE_PTR(who, topk_ids);
+        REQUIRE_PTR(who, topk_w);
+        REQUIRE_PTR(who, inv_sorted);
+    }
+    REQUIRE_PTR(who, counts);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, expert_ids);
+    REQUIRE_PTR(who, total_padded);
+    REQUIRE_PTR(who, workspace);
+    if (num_tokens == 0)
+        return launched(who, moe::launch_align(nullptr, 0, num_experts, block_size, counts, expert_offsets,
+                                               sorted_ids, expert_ids, total_padded, inv_sorted,
+                                               static_cast<int>(max_pad), static_cast<int32_t*>(workspace),
+                                               static_cast<hipStream_t>(stream)));
+    return launched(who, moe::launch_route_align(logits, num_tokens, num_experts, top_k, renormalize ? 1 : 0,
+                                                 topk_ids, topk_w, block_size, counts, expert_offsets, sorted_ids,
+                                                 expert_ids, total_padded, inv_sorted, static_cast<int>(max_pad),
+                                                 static_cast<int32_t*>(workspace),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0, const moe_weight* w1,
                             uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,

@@ -27,22 +27,19 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_INT4_DEPTH
-#define MOE_INT4_DEPTH 1   // quantisation groups of weights in flight per wave while one is computed
-#endif
-
 constexpr int NT = 256;
 constexpr int NCOL = 64;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// x fragment k order (k0..k7) -> (k0,k4,k1,k5,k2,k6,k3,k7), matching the nibble pairs.
+// x fragment k order (k0..k7) -> (k0,k4,k1,k5,k2,k6,k3,k7), matching the nibble pairs: one
+// v_perm_b32 per output word (byte selectors 0-3 pick from the second operand, 4-7 the first).
 __device__ __forceinline__ u32x4 permute_k(u32x4 a) {
     u32x4 r;
-    r[0] = (a[0] & 0xffffu) | (a[2] << 16);
-    r[1] = (a[0] >> 16) | (a[2] & 0xffff0000u);
-    r[2] = (a[1] & 0xffffu) | (a[3] << 16);
-    r[3] = (a[1] >> 16) | (a[3] & 0xffff0000u);
+    r[0] = __builtin_amdgcn_perm(a[2], a[0], 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(a[2], a[0], 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(a[3], a[1], 0x05040100u);
+    r[3] = __builtin_amdgcn_perm(a[3], a[1], 0x07060302u);
     return r;
 }
 
@@ -59,21 +56,20 @@ __device__ __forceinline__ u32x4 dequant_word(uint32_t w, uint32_t mask, uint32_
 }
 
 // Registers of one quantisation group for one lane (STEPS = G/32 MFMA k-steps).
-template <int NP, int STEPS>
+template <int STEPS>
 struct GroupRegs {
-    u32x4 q[NP][STEPS];  // qweight: 16 B = 4 columns x one k-octet, per step
-    u32x4 a[STEPS];      // x fragment (8 bf16) per step
-    uint2 s[NP];         // 4 fp16 scales
-    uint32_t z[NP];      // qzeros word holding the 4 zero points
+    u32x4 q[STEPS];  // qweight: 16 B = 4 columns x one k-octet, per step
+    u32x4 a[STEPS];  // x fragment (8 bf16) per step
+    uint2 s;         // 4 fp16 scales
+    uint32_t z;      // qzeros word holding the 4 zero points
 };
 
 template <bool GATE_UP, int STEPS>
-__global__ __launch_bounds__(NT, STEPS <= 4 ? (MOE_INT4_DEPTH == 2 ? 3 : 4) : 2) void gemm_int4_kernel(
+__global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ qw0, const uint16_t* __restrict__ sc0,
     const int32_t* __restrict__ qz0, const int32_t* __restrict__ qw1, const uint16_t* __restrict__ sc1,
     const int32_t* __restrict__ qz1, uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, int P, int top_k, int E, int N, int K, int bs, int max_pad) {
-    constexpr int NP = 1;                      // projections per wave
     constexpr int NSPLIT = GATE_UP ? 2 : 4;    // waves sharing one projection's K groups
     constexpr int G = STEPS * 32;
     __shared__ int s_row[16];
@@ -110,103 +106,80 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? (MOE_INT4_DEPTH == 2 ? 3 : 4) : 2)
 
     const int m = lane & 15, kq = lane >> 4;  // A fragment row; k-octet within a k32 step
     const int arow = s_row[m];
-    const uint16_t* a_ptr = arow >= 0 ? A + static_cast<size_t>(arow) * K + kq * 8 : nullptr;
+    // a row without a token reads a row that is always in bounds (token 0, or the tile's first
+    // sorted row); its results are never stored
+    const int arow_ok = arow >= 0 ? arow : (GATE_UP ? 0 : r0);
     const int ncol = n0 + 4 * m;              // first of this lane's 4 columns
     const int zshift = 16 * (m & 1);          // nibble of column ncol inside its qzeros word
 
-    const int32_t* qw[NP];
-    const uint16_t* sc[NP];
-    const int32_t* qz[NP];
-    qw[0] = (proj ? qw1 : qw0) + static_cast<size_t>(e) * (K / 8) * N;
-    sc[0] = (proj ? sc1 : sc0) + static_cast<size_t>(e) * (K / G) * N;
-    qz[0] = (proj ? qz1 : qz0) + static_cast<size_t>(e) * (K / G) * (N / 8);
-
-    auto load_group = [&](int g, GroupRegs<NP, STEPS>& R) {
+    // per-lane cursors at group g_begin; every group moves them by a fixed stride
+    const uint16_t* a_cur = A + static_cast<size_t>(arow_ok) * K + kq * 8 + static_cast<size_t>(g_begin) * G;
+    const int32_t* q_cur = (proj ? qw1 : qw0) + static_cast<size_t>(e) * (K / 8) * N +
+                           static_cast<size_t>(g_begin * (G / 8) + kq) * N + ncol;
+    const uint16_t* s_cur = (proj ? sc1 : sc0) + static_cast<size_t>(e) * (K / G) * N +
+                            static_cast<size_t>(g_begin) * N + ncol;
+    const int32_t* z_cur = (proj ? qz1 : qz0) + static_cast<size_t>(e) * (K / G) * (N / 8) +
+                           static_cast<size_t>(g_begin) * (N / 8) + ncol / 8;
+    auto load_group = [&](GroupRegs<STEPS>& R) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const int kb = g * G + st * 32;
-            R.a[st] = a_ptr ? *reinterpret_cast<const u32x4*>(a_ptr + kb) : u32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-                R.q[p][st] = *reinterpret_cast<const u32x4*>(qw[p] + static_cast<size_t>(kb / 8 + kq) * N + ncol);
+            R.a[st] = *reinterpret_cast<const u32x4*>(a_cur + st * 32);
+            R.q[st] = *reinterpret_cast<const u32x4*>(q_cur + static_cast<size_t>(st) * 4 * N);
         }
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            R.s[p] = *reinterpret_cast<const uint2*>(sc[p] + static_cast<size_t>(g) * N + ncol);
-            R.z[p] = static_cast<uint32_t>(qz[p][static_cast<size_t>(g) * (N / 8) + ncol / 8]);
-        }
+        R.s = *reinterpret_cast<const uint2*>(s_cur);
+        R.z = static_cast<uint32_t>(*z_cur);
+        a_cur += G;
+        q_cur += static_cast<size_t>(G / 8) * N;
+        s_cur += N;
+        z_cur += N / 8;
     };
 
-    f32x4 out[NP][4];
+    f32x4 out[4];
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) out[p][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) out[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     uint32_t nib_mask, bf16_128;
     asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(nib_mask));
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bf16_128));
 
-    auto compute_group = [&](const GroupRegs<NP, STEPS>& cur) {
-        f32x4 acc[NP][4], accx = {0.f, 0.f, 0.f, 0.f};
+    auto compute_group = [&](const GroupRegs<STEPS>& cur) {
+        f32x4 acc[4], accx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[p][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const bf16x8 afr = as_bf16x8(permute_k(cur.a[st]));
             accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, as_bf16x8(ones), accx, 0, 0, 0);
 #pragma unroll
-            for (int p = 0; p < NP; ++p)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[p][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        afr, as_bf16x8(dequant_word(cur.q[p][st][j], nib_mask, bf16_128)), acc[p][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    afr, as_bf16x8(dequant_word(cur.q[st][j], nib_mask, bf16_128)), acc[j], 0, 0, 0);
         }
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t sbits = (j < 2 ? cur.s.x : cur.s.y) >> (16 * (j & 1));
+            const float sc = f16_to_f32(static_cast<uint16_t>(sbits & 0xffffu));
+            const float zz = 128.0f + static_cast<float>((cur.z >> (zshift + 4 * j)) & 0xfu);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t sbits = (j < 2 ? cur.s[p].x : cur.s[p].y) >> (16 * (j & 1));
-                const float s = f16_to_f32(static_cast<uint16_t>(sbits & 0xffffu));
-                const float zz = 128.0f + static_cast<float>((cur.z[p] >> (zshift + 4 * j)) & 0xfu);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) out[p][j][v] = fmaf(s, fmaf(-zz, accx[v], acc[p][j][v]), out[p][j][v]);
-            }
+            for (int v = 0; v < 4; ++v) out[j][v] = fmaf(sc, fmaf(-zz, accx[v], acc[j][v]), out[j][v]);
         }
     };
 
-#if MOE_INT4_DEPTH == 2
-    // three register sets in rotation: two groups in flight while one is computed
-    GroupRegs<NP, STEPS> ra, rb, rc;
-    if (g_begin < g_end) load_group(g_begin, ra);
-    if (g_begin + 1 < g_end) load_group(g_begin + 1, rb);
-    for (int g = g_begin; g < g_end; g += 3) {
-        if (g + 2 < g_end) load_group(g + 2, rc);
-        compute_group(ra);
-        if (g + 1 >= g_end) break;
-        if (g + 3 < g_end) load_group(g + 3, ra);
-        compute_group(rb);
-        if (g + 2 >= g_end) break;
-        if (g + 4 < g_end) load_group(g + 4, rb);
-        compute_group(rc);
-    }
-#else
-    GroupRegs<NP, STEPS> nxt;
-    if (g_begin < g_end) load_group(g_begin, nxt);
-    for (int g = g_begin; g < g_end; ++g) {
-        const GroupRegs<NP, STEPS> cur = nxt;
-        if (g + 1 < g_end) load_group(g + 1, nxt);
+    // group g+1 loads while group g is computed
+    const int ng = g_end - g_begin;
+    GroupRegs<STEPS> nxt;
+    if (ng > 0) load_group(nxt);
+    for (int i = 0; i < ng; ++i) {
+        const GroupRegs<STEPS> cur = nxt;
+        if (i + 1 < ng) load_group(nxt);
         compute_group(cur);
     }
-#endif
 
     // split-K reduction over the waves, then the epilogue: 256 threads = 16 rows x 16 column quads
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) red[wave][v][lane][j] = out[0][j][v];
+        for (int j = 0; j < 4; ++j) red[wave][v][lane][j] = out[j][v];
     __syncthreads();
     {
         const int sl = tid & 63, v = tid >> 6;  // source lane and row-in-quad of the C fragment

@@ -17,6 +17,11 @@ hipError_t launch_align(const int32_t* topk_ids, int P, int E, int bs, int32_t* 
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total, int32_t* inv, int max_pad,
                         int32_t* workspace, hipStream_t s);
 
+// route + align in one launch when the pairs fit one chunk, else the two above
+hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int renorm, int32_t* ids, float* w,
+                              int bs, int32_t* counts, int32_t* offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                              int32_t* total, int32_t* inv, int max_pad, int32_t* workspace, hipStream_t s);
+
 // combine.hip
 hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w, uint16_t* out, int T, int k,
                           int H, int64_t ys_rows, hipStream_t s);

@@ -1,0 +1,141 @@
+// Per-token top-k softmax routing body, shared by the router kernel and the fused
+// route+align kernel (ferrum-kernels cuda/moe.rs, route_topk_softmax): softmax over all
+// experts, keep the top_k, optionally renormalise over them.
+//
+// One wave64 per token.  Each lane holds up to four logits (E <= 256) in registers.
+// Selection takes top_k rounds of a wave arg-max over a 64-bit key (order-preserving image
+// of the fp32 logit, then the complement of the expert index, so equal logits pick the
+// lower index).  The weights are computed in fp64 and rounded once to fp32.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint32_t order_bits(float v) {
+    v = (v == 0.0f) ? 0.0f : v;  // -0.0 and +0.0 compare equal
+    uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_order_bits(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// Cross-lane reductions over a wave64 without LDS round trips: inside each 16-lane row, DPP
+// row rotations by 1, 2, 4 and 8 leave the row's result in every lane; the four row results
+// are then read from lanes 0, 16, 32 and 48.
+template <int N>
+__device__ __forceinline__ uint64_t row_ror_u64(uint64_t v) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(v)), 0x120 + N, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(v >> 32)), 0x120 + N, 0xF, 0xF, false));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = row_ror_u64<1>(v); v = o > v ? o : v;
+    o = row_ror_u64<2>(v); v = o > v ? o : v;
+    o = row_ror_u64<4>(v); v = o > v ? o : v;
+    o = row_ror_u64<8>(v); v = o > v ? o : v;
+    uint64_t m = readlane_u64(v, 0);
+    o = readlane_u64(v, 16); m = o > m ? o : m;
+    o = readlane_u64(v, 32); m = o > m ? o : m;
+    o = readlane_u64(v, 48); m = o > m ? o : m;
+    return m;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += __builtin_bit_cast(double, row_ror_u64<1>(__builtin_bit_cast(uint64_t, v)));
+    v += __builtin_bit_cast(double, row_ror_u64<2>(__builtin_bit_cast(uint64_t, v)));
+    v += __builtin_bit_cast(double, row_ror_u64<4>(__builtin_bit_cast(uint64_t, v)));
+    v += __builtin_bit_cast(double, row_ror_u64<8>(__builtin_bit_cast(uint64_t, v)));
+    return (__builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, v), 0)) +
+            __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, v), 16))) +
+           (__builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, v), 32)) +
+            __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, v), 48)));
+}
+
+// Route NTOK tokens t0, t0+dt, ... (those below T), called by all 64 lanes of one wave: writes
+// ids/w[t*top_k .. +top_k) of each.  The tokens' selection rounds are independent, so their
+// cross-lane reductions interleave and hide each other's latency.
+template <int EPL, int NTOK>
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int t0, int dt, int T, int E,
+                                             int top_k, int renorm, int32_t* __restrict__ ids,
+                                             float* __restrict__ w, int lane) {
+    float v[NTOK][EPL];
+    uint64_t key[NTOK][EPL];
+#pragma unroll
+    for (int n = 0; n < NTOK; ++n) {
+        const int t = t0 + n * dt;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            if (t < T && e < E) {
+                v[n][i] = logits[static_cast<size_t>(t) * E + e];
+                key[n][i] = (static_cast<uint64_t>(order_bits(v[n][i])) << 32) | static_cast<uint32_t>(0xffff - e);
+            } else {
+                v[n][i] = 0.0f;
+                key[n][i] = 0;  // below every real key
+            }
+        }
+    }
+
+    int my_e[NTOK];
+    float my_l[NTOK], top[NTOK];
+#pragma unroll
+    for (int n = 0; n < NTOK; ++n) { my_e[n] = 0; my_l[n] = 0.0f; top[n] = 0.0f; }
+    for (int j = 0; j < top_k; ++j) {
+        uint64_t best[NTOK];
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+            best[n] = key[n][0];
+#pragma unroll
+            for (int i = 1; i < EPL; ++i) best[n] = key[n][i] > best[n] ? key[n][i] : best[n];
+        }
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) best[n] = wave_max_u64(best[n]);
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+            const int e = 0xffff - static_cast<int>(best[n] & 0xffffu);
+            const float l = from_order_bits(static_cast<uint32_t>(best[n] >> 32));
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (lane + 64 * i == e) key[n][i] = 0;
+            if (j == 0) top[n] = l;
+            if (lane == j) { my_e[n] = e; my_l[n] = l; }
+        }
+    }
+
+#pragma unroll
+    for (int n = 0; n < NTOK; ++n) {
+        const int t = t0 + n * dt;
+        // softmax denominator over every expert, fp64
+        const double m = static_cast<double>(top[n]);
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane + 64 * i < E) part += exp(static_cast<double>(v[n][i]) - m);
+        const double S = wave_sum_f64(part);
+        const double p = exp(static_cast<double>(my_l[n]) - m) / S;
+        double den = 0.0;
+        for (int j = 0; j < top_k; ++j)
+            den += __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, p), j));
+        if (t < T && lane < top_k) {
+            const double wj = renorm ? p / den : p;
+            ids[static_cast<size_t>(t) * top_k + lane] = my_e[n];
+            w[static_cast<size_t>(t) * top_k + lane] = static_cast<float>(wj);
+        }
+    }
+}
+
+}  // namespace moe

@@ -16,7 +16,7 @@ import torch
 
 from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU
 from .ops import (Bf16Weight, GptqWeight, LoraTables, Routing, lora_windows, moe_align, moe_combine,
-                  moe_grouped_gemm, moe_lora_fold, moe_route, pack_lora_tables)
+                  moe_grouped_gemm, moe_lora_fold, moe_route, moe_route_align, pack_lora_tables)
 
 
 @dataclass
@@ -77,8 +77,7 @@ class MoeLayer:
 
     # ------------------------------------------------------------------ forward
     def route_align(self, logits: torch.Tensor, b: Buffers) -> None:
-        moe_route(logits, self.top_k, self.renormalize, b.ids, b.w)
-        moe_align(b.ids, self.E, self.bs, out=b.routing)
+        moe_route_align(logits, self.top_k, self.renormalize, self.bs, b.ids, b.w, b.routing)
 
     def experts(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
         moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs)

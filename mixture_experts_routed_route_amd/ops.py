@@ -15,7 +15,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_W_BF16, MOE_W_INT4_GPTQ
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Routing", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_grouped_gemm", "moe_lora_fold", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "moe_lora_fold", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -163,6 +163,26 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, block_size: int, max_pad
                           _dev(r.inv_sorted, torch.int32, "inv_sorted"), r.max_pad,
                           _dev(r.workspace, torch.int32, "workspace"), r.workspace.numel() * 4,
                           _stream(topk_ids)))
+    return r
+
+
+def moe_route_align(logits: torch.Tensor, top_k: int, renormalize: bool, block_size: int,
+                    topk_ids: torch.Tensor, topk_w: torch.Tensor, out: Routing) -> Routing:
+    """moe_route then moe_align on its ids, as one call (one launch when the pairs fit one chunk)."""
+    T, E = logits.shape
+    r = out
+    if r.num_pairs != T * top_k or r.num_experts != E or r.block_size != block_size:
+        raise ValueError("preallocated Routing does not match the call")
+    check(lib().moe_route_align(_dev(logits, torch.float32, "logits"), T, E, top_k, int(bool(renormalize)),
+                                _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
+                                block_size, _dev(r.counts, torch.int32, "counts"),
+                                _dev(r.offsets, torch.int32, "offsets"),
+                                _dev(r.sorted_ids, torch.int32, "sorted_ids"),
+                                _dev(r.expert_ids, torch.int32, "expert_ids"),
+                                _dev(r.total_padded, torch.int32, "total_padded"),
+                                _dev(r.inv_sorted, torch.int32, "inv_sorted"), r.max_pad,
+                                _dev(r.workspace, torch.int32, "workspace"), r.workspace.numel() * 4,
+                                _stream(logits)))
     return r
 
 

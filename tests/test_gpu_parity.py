@@ -399,3 +399,57 @@ def test_grouped_gemms_padded_total_at_capacity(dev):
     assert_close_rows(bf16_host(ys)[real], y_ref[real], TOL, "down at capacity")
     pad = np.setdiff1d(np.arange(r.max_pad), real)
     assert (bits_host(ys)[pad] == CANARY).all()
+
+
+# ----------------------------------------------------------------------------- A1+A2 fused entry point
+ROUTE_ALIGN_CASES = [
+    ("decode_int4", CONFIGS["decode_int4"]),                        # one launch (96 pairs)
+    ("tiny", CONFIGS["tiny"]),                                      # one launch (128 pairs)
+    ("mixtral_prefill", CONFIGS["mixtral_prefill"]),                # route + two align launches
+    ("E256_k8", MoeConfig("E256", T=200, H=8, I=8, E=256, top_k=8, block_size=64, seed=21)),
+    ("E200_k7_chunk_edge", MoeConfig("E200", T=292, H=8, I=8, E=200, top_k=7, block_size=32, seed=22)),
+    ("E1", MoeConfig("E1", T=17, H=8, I=8, E=1, top_k=1, block_size=16, seed=23)),
+    ("k_eq_E_no_renorm", MoeConfig("kE", T=50, H=8, I=8, E=6, top_k=6, block_size=16, renormalize=False, seed=24)),
+    ("one_chunk_max", MoeConfig("c1", T=256, H=8, I=8, E=64, top_k=8, block_size=128, seed=25)),
+    ("one_over_chunk", MoeConfig("c2", T=2049, H=8, I=8, E=3, top_k=1, block_size=16, seed=26)),
+    ("T40_four_per_wave", MoeConfig("t40", T=40, H=8, I=8, E=128, top_k=8, block_size=32, seed=27)),
+    ("T64_E256", MoeConfig("t64", T=64, H=8, I=8, E=256, top_k=4, block_size=16, seed=28)),
+    ("T65_two_calls", MoeConfig("t65", T=65, H=8, I=8, E=32, top_k=2, block_size=16, seed=29)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", ROUTE_ALIGN_CASES, ids=[c[0] for c in ROUTE_ALIGN_CASES])
+def test_route_align_matches_oracle(dev, name, cfg):
+    """moe_route_align equals the oracle's route followed by its align, bit for bit (single-launch
+    path for batches of at most 2048 pairs, the two-call path above)."""
+    import torch
+    note(f"route_align {name} T={cfg.T} E={cfg.E} k={cfg.top_k} P={cfg.P}")
+    m = ops()
+    logits = make_router_logits(cfg)
+    ids_ref, w_ref = oracle.route(logits, cfg.top_k, cfg.renormalize)
+    ref = oracle.align(ids_ref, cfg.E, cfg.block_size)
+    ids = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    r = m.Routing.allocate(cfg.P, cfg.top_k, cfg.E, cfg.block_size, dev)
+    r.sorted_ids.fill_(-7)   # every row must be written
+    r.expert_ids.fill_(-7)
+    m.moe_route_align(to_dev(logits), cfg.top_k, cfg.renormalize, cfg.block_size, ids, w, r)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+    got = {"counts": r.counts.cpu().numpy(), "offsets": r.offsets.cpu().numpy(),
+           "sorted_ids": r.sorted_ids.cpu().numpy(), "expert_ids": r.expert_ids.cpu().numpy(),
+           "total": int(r.total_padded.cpu().item()), "inv": r.inv_sorted.cpu().numpy()[: cfg.P]}
+    _assert_align_equal(got, ref)
+
+
+def test_route_align_zero_tokens(dev):
+    import torch
+    m = ops()
+    r = m.Routing.allocate(0, 2, 4, 16, dev)
+    r.sorted_ids.fill_(-7)
+    ids = torch.empty((0, 2), dtype=torch.int32, device=dev)
+    w = torch.empty((0, 2), dtype=torch.float32, device=dev)
+    m.moe_route_align(torch.empty((0, 4), dtype=torch.float32, device=dev), 2, True, 16, ids, w, r)
+    ref = oracle.align(np.zeros((0, 2), np.int32), 4, 16)
+    assert np.array_equal(r.sorted_ids.cpu().numpy(), ref["sorted_ids"])
+    assert np.array_equal(r.offsets.cpu().numpy(), ref["offsets"])
