@@ -9,7 +9,8 @@
 // into 64-row tiles aligned to 16-row boundaries (one 16-row sub-tile per wave; block
 // sizes are multiples of 16, so a sub-tile never straddles two experts' spans), and
 // sub-tiles of unadapted experts, sentinel rows and rows outside the window do nothing.
-// Both stages use 16x16x32 bf16 MFMA with fp32 accumulation.  The expand stages its bf16
+// Both stages use 16x16x32 bf16 MFMA with fp32 accumulation.  The shrink gives each 16-row
+// sub-tile a workgroup whose 4 waves split k_in.  The expand stages its bf16
 // delta tile in LDS and then updates the base rows with 16-byte coalesced accesses.
 #include "device_common.h"
 #include "launchers.h"
@@ -53,6 +54,11 @@ __device__ __forceinline__ bool row_active(int64_t r, int64_t row_offset, int64_
     return true;
 }
 
+// Shrink: one workgroup per 16-row sub-tile; its 4 waves take a quarter of k_in each and add
+// their partial sums in LDS, so one row's k loop is split over 4 waves.  NB = rank blocks of 16
+// (max_rank / 16, up to 8); KU k-steps per round: every load of a round is issued before its
+// MFMAs, so a wave waits for one memory round trip per KU steps.
+template <int NB>
 __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restrict__ x, const uint64_t* a_tab,
                                                          const uint64_t* b_tab, int n_tab, int k_in, int max_rank,
                                                          const int32_t* __restrict__ off, int E,
@@ -60,37 +66,52 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ row_adapter,
                                                          uint16_t* __restrict__ xa, int64_t row_offset,
                                                          int64_t row_end, int64_t base16) {
+    constexpr int KU = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
+    __shared__ float red[4][NB][4][64];  // [wave][rank block][v][lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.x) * 64 + wave * 16;
+    const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.x) * 16;
     if (sub0 >= row_end) return;
     const SubTile st = sub_tile_expert(static_cast<int>(sub0), off, E, n_tab, a_tab, b_tab);
-    if (st.e < 0) return;
+    if (st.e < 0) return;  // uniform over the workgroup
     const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[st.e]);
 
     const int m = lane & 15, kq = lane >> 4;
     const int64_t r = sub0 + m;
     const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
-    if (__ballot(act) == 0) return;
+    if (__ballot(act) == 0) return;  // the same rows in every wave: uniform over the workgroup
     const uint16_t* xr = act ? x + r * k_in + kq * 8 : nullptr;
-    const int nb = max_rank / 16;
+    const int kpart = ((k_in + 127) / 128) * 32;  // this wave's k range, a multiple of 32
+    const int kb = wave * kpart, ke = min(k_in, kb + kpart);
 
-    f32x4 acc[MAX_RANK_BLOCKS];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int j = 0; j < MAX_RANK_BLOCKS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < k_in; k0 += 32) {
-        const bool kin = k0 + kq * 8 < k_in;
-        const u32x4 av = (xr && kin) ? *reinterpret_cast<const u32x4*>(xr + k0) : u32x4{0, 0, 0, 0};
-        const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
+    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kb; k0 < ke; k0 += 32 * KU) {
+        u32x4 av[KU], bv[KU][NB];
 #pragma unroll
-        for (int j = 0; j < MAX_RANK_BLOCKS; ++j) {
-            if (j < nb) {
-                const uint16_t* bp = Ae + static_cast<int64_t>(j * 16 + m) * k_in + k0 + kq * 8;
-                const u32x4 bv = kin ? *reinterpret_cast<const u32x4*>(bp) : u32x4{0, 0, 0, 0};
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bv), acc[j],
-                                                                 0, 0, 0);
-            }
+        for (int u = 0; u < KU; ++u) {
+            const int kk = k0 + u * 32;
+            const bool kin = kk + kq * 8 < ke;
+            av[u] = (xr && kin) ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                bv[u][j] = kin ? *reinterpret_cast<const u32x4*>(Ae + static_cast<int64_t>(j * 16 + m) * k_in + kk + kq * 8)
+                               : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const bf16x8 afr = __builtin_bit_cast(bf16x8, av[u]);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bv[u][j]), acc[j], 0, 0, 0);
         }
     }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[j][v];
+    __syncthreads();
+    if (wave != 0) return;
     // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -98,8 +119,9 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
         if (!row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter)) continue;
         uint16_t* dst = xa + (rr - row_offset) * max_rank;
 #pragma unroll
-        for (int j = 0; j < MAX_RANK_BLOCKS; ++j)
-            if (j < nb) dst[j * 16 + m] = f32_to_bf16(acc[j][v]);
+        for (int j = 0; j < NB; ++j)
+            dst[j * 16 + m] = f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
+                                          (red[2][j][v][lane] + red[3][j][v][lane]));
     }
 }
 
@@ -149,15 +171,25 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
         for (int v = 0; v < 4; ++v) s_delta[wave][4 * kq + v][c * 16 + m] = f32_to_bf16(acc[c][v]);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    // coalesced fold: 2 rows x 32 lanes x 8 columns per step
+    // coalesced fold: 2 rows x 32 lanes x 8 columns per step; all 8 steps' base rows are read
+    // before any is written back (one memory round trip per wave)
+    const int col = (lane & 31) * 8;
+    bool ok[8];
+    u32x4 bvs[8];
+#pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int rl = it * 2 + (lane >> 5);
         const int64_t rr = sub0 + rl;
-        const int col = (lane & 31) * 8;
-        if (n0 + col >= n_out) continue;
-        if (!row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter)) continue;
-        u32x4* bp = reinterpret_cast<u32x4*>(base + rr * n_out + n0 + col);
-        const u32x4 bv = *bp;
+        ok[it] = n0 + col < n_out &&
+                 row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
+        bvs[it] = ok[it] ? *reinterpret_cast<const u32x4*>(base + rr * n_out + n0 + col) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        if (!ok[it]) continue;
+        const int rl = it * 2 + (lane >> 5);
+        const int64_t rr = sub0 + rl;
+        const u32x4 bv = bvs[it];
         const u32x4 dv = *reinterpret_cast<const u32x4*>(&s_delta[wave][rl][col]);
         u32x4 o;
 #pragma unroll
@@ -166,7 +198,7 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
             const float d_lo = __uint_as_float(dv[i] << 16), d_hi = __uint_as_float(dv[i] & 0xffff0000u);
             o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
         }
-        *bp = o;
+        *reinterpret_cast<u32x4*>(base + rr * n_out + n0 + col) = o;
     }
 }
 
@@ -180,9 +212,22 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
     const int64_t base16 = (row_offset / 16) * 16;
     const int64_t tiles = (row_end - base16 + 63) / 64;
-    lora_shrink_kernel<<<dim3(static_cast<unsigned>(tiles)), NT, 0, s>>>(
-        x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, P, top_k, row_adapter, xa, row_offset,
-        row_end, base16);
+    const int64_t subs = (row_end - base16 + 15) / 16;
+    const dim3 sgrid(static_cast<unsigned>(subs));
+#define MOE_SHRINK(NB_)                                                                                          \
+    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, \
+                                                 P, top_k, row_adapter, xa, row_offset, row_end, base16)
+    switch (max_rank / 16) {
+        case 1: MOE_SHRINK(1); break;
+        case 2: MOE_SHRINK(2); break;
+        case 3: MOE_SHRINK(3); break;
+        case 4: MOE_SHRINK(4); break;
+        case 5: MOE_SHRINK(5); break;
+        case 6: MOE_SHRINK(6); break;
+        case 7: MOE_SHRINK(7); break;
+        default: MOE_SHRINK(8); break;
+    }
+#undef MOE_SHRINK
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 grid((n_out + EXP_COLS - 1) / EXP_COLS, static_cast<unsigned>(tiles));
