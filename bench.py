@@ -161,10 +161,10 @@ def main():
         layer.route_align(logits, b)
         if ev is not None:
             ev[0].record()
-        m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, x, layer.gate, layer.up, b.routing, out=b.hs)
+        m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, x, layer.gate, layer.up, b.routing, out=b.hs, workspace=b.ws)
         if ev is not None:
             ev[1].record()
-        m.moe_grouped_gemm(m.MOE_OP_DOWN, b.hs, layer.down, None, b.routing, out=b.ys)
+        m.moe_grouped_gemm(m.MOE_OP_DOWN, b.hs, layer.down, None, b.routing, out=b.ys, workspace=b.ws)
         if ev is not None:
             ev[2].record()
         if layer.lora is not None:

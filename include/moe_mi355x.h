@@ -178,12 +178,28 @@ typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1 } moe_gemm_op;
  * moe_align).  Sentinel and padding rows are neither read as tokens nor
  * written: c keeps its previous content there.  fp32 accumulation.
  *   c: bf16 [max_pad, N].  K % 8 == 0, N % 8 == 0 (int4: N % 64 == 0,
- *   K % group_size == 0).  Both weights must have the same type. */
+ *   K % group_size == 0).  Both weights must have the same type.
+ *   workspace: optional device buffer of >= moe_grouped_gemm_workspace_bytes()
+ *   bytes, or NULL.  With it, bf16 launches that have at least as many output
+ *   tiles as workgroups cut the K loops of all tiles, end to end, into equal
+ *   ranges, one per workgroup (stream-K), so no workgroup idles through a
+ *   last partial wave of tiles; a tile cut by a range boundary is computed in
+ *   two halves that meet through fp32 partials and a counter kept there.  It
+ *   must be zero-filled once before its first use; every call leaves its
+ *   counters at zero again.  Calls that share one workspace must not run
+ *   concurrently.  A smaller non-NULL buffer is rejected (MOE_EINVAL).  int4
+ *   launches ignore it.  Results with and without it agree to fp32 summation
+ *   order; with it they are deterministic (a split tile is the exact sum of
+ *   its two halves). */
 moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0, const moe_weight* w1,
                             uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
                             int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
-                            moe_stream stream);
+                            void* workspace, int64_t workspace_bytes, moe_stream stream);
+
+/* Size in bytes of the optional moe_grouped_gemm workspace (fixed; it does not
+ * depend on the problem). */
+int64_t moe_grouped_gemm_workspace_bytes(void);
 
 /* A5 — down-projection LoRA fold, in place, on one window [row_offset, row_end)
  * of the sorted rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down).

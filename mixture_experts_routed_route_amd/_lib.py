@@ -35,7 +35,8 @@ SIGNATURES = {
                                   c_int64, c_void_p]),
     "moe_grouped_gemm": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int64,
-                                   c_void_p]),
+                                   c_void_p, c_int64, c_void_p]),
+    "moe_grouped_gemm_workspace_bytes": (c_int64, []),
     "moe_lora_fold": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                 c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                 c_int64, c_int64, c_int64, c_int64, c_void_p]),

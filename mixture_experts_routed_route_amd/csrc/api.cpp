@@ -63,6 +63,8 @@ int64_t moe_align_max_padded(int64_t num_pairs, int32_t num_experts, int32_t blo
     return max_padded(num_pairs, num_experts, block_size);
 }
 
+int64_t moe_grouped_gemm_workspace_bytes(void) { return moe::gemm_bf16_workspace_bytes(); }
+
 int64_t moe_align_workspace_bytes(int64_t num_pairs, int32_t num_experts) {
     if (num_pairs < 0 || num_experts < 1) return -1;
     return static_cast<int64_t>(moe::align_num_chunks(num_pairs)) * num_experts * 4;
@@ -239,7 +241,7 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
                             uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
                             int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
-                            moe_stream stream) {
+                            void* workspace, int64_t workspace_bytes, moe_stream stream) {
     const char* who = "moe_grouped_gemm";
     REQUIRE(op == MOE_OP_GATE_UP_SILU || op == MOE_OP_DOWN, "%s: unknown op %d", who, op);
     const bool gate_up = op == MOE_OP_GATE_UP_SILU;
@@ -261,6 +263,12 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
     else REQUIRE(w1 == nullptr, "%s: MOE_OP_DOWN takes no w1", who);
     REQUIRE(w0->type == MOE_W_BF16 || w0->type == MOE_W_INT4_GPTQ, "%s: w0 has unknown type %d", who, w0->type);
     if (w1) REQUIRE(w1->type == w0->type, "%s: w0 and w1 have different types", who);
+    if (workspace != nullptr && w0->type == MOE_W_BF16) {
+        const int64_t need = moe_grouped_gemm_workspace_bytes();
+        REQUIRE_PTR(who, workspace);
+        REQUIRE(need > 0 && workspace_bytes >= need, "%s: workspace_bytes %lld < required %lld", who,
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+    }
     if (num_pairs == 0) return ok();
     REQUIRE_PTR(who, a);
     REQUIRE_PTR(who, c);
@@ -274,7 +282,7 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
         return launched(who, moe::launch_gemm_bf16(gate_up, a, static_cast<const uint16_t*>(w0->data),
                                                    w1 ? static_cast<const uint16_t*>(w1->data) : nullptr, c,
                                                    sorted_ids, expert_offsets, P, top_k, num_experts, n, k,
-                                                   static_cast<int>(max_pad), s));
+                                                   static_cast<int>(max_pad), workspace, workspace_bytes, s));
     }
     const int G = w0->group_size;
     REQUIRE(G == 32 || G == 64 || G == 128 || G == 256, "%s: group_size %d not in {32,64,128,256}", who, G);

@@ -35,6 +35,16 @@
 // next tile's rows and issues its first stage into the free LDS buffer, so the next tile's setup
 // and first load latency hide behind this epilogue.  With fewer tiles, one workgroup per tile.
 //
+// Split tail (only with a caller workspace).  When the tiles do not fill a whole number of
+// rounds of the persistent grid, the last partial round would leave most compute units idle
+// for a whole tile.  Instead every workgroup runs the same number of whole tiles and the
+// remaining tiles are cut along K into pieces that together occupy the grid; pieces of one tile
+// run on one XCD and pieces that run together start at the same K step, so they still share A
+// tiles and weight panels in L2.  Pieces meet through fp32 partials in the workspace: each
+// writes its partial with device-coherent stores and counts itself on the tile's counter; the
+// last one sums all partials in piece order (so results do not depend on arrival order),
+// stores the tile and resets the counter.  No workgroup ever waits for another.
+//
 // Epilogue.  Straight from the accumulators, no LDS: neighbouring lanes (columns c, c+1) swap
 // one value through DPP so that each lane holds two adjacent columns of one row, converts them
 // with one v_cvt_pk_bf16_f32 and stores 4 bytes.
@@ -52,6 +62,9 @@ constexpr int BP = 256;
 #endif
 #ifndef MOE_GEMM_BIG_BK
 #define MOE_GEMM_BIG_BK 64       // k per LDS stage of the 256-row tiles
+#endif
+#ifndef MOE_GEMM_SPLIT_MIN_STAGES
+#define MOE_GEMM_SPLIT_MIN_STAGES 8  // K stages per piece of a split tail tile, at least
 #endif
 #ifndef MOE_GEMM_BIG_STAGES
 #define MOE_GEMM_BIG_STAGES 2    // LDS stages of the 256-row tiles (stage = 512 rows x BK bf16)
@@ -123,7 +136,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                                                           uint16_t* __restrict__ C,
                                                           const int32_t* __restrict__ sorted_ids,
                                                           const int32_t* __restrict__ offsets, int P, int top_k,
-                                                          int E, int N, int K, int max_pad, int n_tiles) {
+                                                          int E, int N, int K, int max_pad, int n_tiles,
+                                                          float* __restrict__ sk_part, int32_t* __restrict__ sk_cnt,
+                                                          int sk_on) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
     constexpr int NT = F::NT;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
@@ -131,6 +146,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     __shared__ int s_lo[kMaxE], s_hi[kMaxE], s_tb[kMaxE + 1];  // expert span, first row tile
     __shared__ int s_row[2][BM];                                  // A source row per tile row
     __shared__ int s_h[2];                                        // rows up to the last token
+    __shared__ int s_arrived;                                     // split tile: the other side's count
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -147,17 +163,64 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         if (tid == 0) { s_tb[0] = 0; s_h[0] = 0; s_h[1] = 0; }
         __syncthreads();
     }
-    const int m_real = s_tb[E];
+    // values read from LDS are the same in every lane: readfirstlane keeps them (and everything
+    // derived from them) in scalar registers
+    const int m_real = __builtin_amdgcn_readfirstlane(s_tb[E]);
 
-    // ---- this workgroup's logical tiles.  Workgroup ids go round-robin over the 8 XCDs, so XCD x
-    // takes the contiguous range [x*T/8, (x+1)*T/8) and its workgroups stride through it.
+    // ---- this workgroup's work.  Workgroup ids go round-robin over the 8 XCDs; position
+    // pos = xcd * per_xcd + slot orders the workgroups XCD by XCD.
+    //  * whole tiles: XCD x takes the contiguous range [x*Tw/8, (x+1)*Tw/8) of the first Tw tiles
+    //    and its workgroups stride through it, all at the same K step;
+    //  * split tail (only with a workspace, and only when each XCD's share of the tail can be cut
+    //    at least in two): Tw is the largest multiple of the grid, so every workgroup runs the
+    //    same number of whole tiles, and the remaining T - Tw tiles (less than one round) are
+    //    dealt XCD by XCD, n_x to XCD x, each cut along K into s_x pieces of at least
+    //    MOE_GEMM_SPLIT_MIN_STAGES stages with s_x * n_x <= per_xcd.  Piece j of tail
+    //    tile u runs on slot j * n_x + u of that XCD, so the pieces running together start at
+    //    the same K step.  Every piece writes its fp32 partial accumulators to the workspace
+    //    slot of its position and counts itself on the tile's counter; the last to arrive sums
+    //    the s_x partials in piece order and stores the tile.  Nobody waits for anybody.
     const long long T = static_cast<long long>(m_real) * n_tiles;
+    const int nk = (K + BK - 1) / BK;
     const int per_xcd = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
-    const int l_hi = static_cast<int>(T * (xcd + 1) / 8);
-    int L = static_cast<int>(T * xcd / 8) + slot;
-    if (slot >= per_xcd || L >= l_hi) return;
+    const int pos = xcd * per_xcd + slot;
+    long long Tw = T;
+    if (sk_on) {
+        // split only when every XCD's share of the tail is cut at least in two; otherwise whole
+        // tiles throughout, as without a workspace
+        const long long rounds = T / gridDim.x;
+        const int rest = static_cast<int>(T - rounds * gridDim.x);
+        if (rest > 0 && min(per_xcd / ((rest + 7) / 8), nk / MOE_GEMM_SPLIT_MIN_STAGES) >= 2)
+            Tw = rounds * gridDim.x;
+    }
+    const int tail = static_cast<int>(T - Tw);
+    const int l_hi = static_cast<int>(Tw * (xcd + 1) / 8);
+    int L = static_cast<int>(Tw * xcd / 8) + slot;
+    // this workgroup's tail piece (none: tail_L < 0)
+    int tail_L = -1, tail_kb = 0, tail_ke = nk, tail_s = 1, tail_first = 0, tail_n = 1;
+    if (tail > 0) {
+        const int a_x = tail * xcd / 8;
+        const int n_x = tail * (xcd + 1) / 8 - a_x;
+        if (n_x > 0) {
+            const int s_x = max(1, min(per_xcd / n_x, nk / MOE_GEMM_SPLIT_MIN_STAGES));
+            if (slot < s_x * n_x) {
+                const int u = slot % n_x, j = slot / n_x;
+                tail_L = static_cast<int>(Tw) + a_x + u;
+                tail_kb = j * nk / s_x;
+                tail_ke = (j + 1) * nk / s_x;
+                tail_s = s_x;
+                tail_first = xcd * per_xcd + u;  // position of piece 0; piece j' at + j' * n_x
+                tail_n = n_x;
+            }
+        }
+    }
+    int kb = 0, ke = nk;  // current segment: tile L, stages [kb, ke)
+    if (slot >= per_xcd || L >= l_hi) {
+        if (tail_L < 0) return;
+        L = tail_L; kb = tail_kb; ke = tail_ke;
+    }
 
     // tile L -> expert e, first sorted row r0, rows end r_end, first output column n0
     auto locate = [&](int Lt, int& e, int& r0, int& r_end, int& n0) {
@@ -168,10 +231,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             const int mid = (a + b + 1) >> 1;
             if (s_tb[mid] <= m_t) a = mid; else b = mid - 1;
         }
-        e = a;
-        r0 = s_lo[e] + (m_t - s_tb[e]) * BM;
-        r_end = min(r0 + BM, s_hi[e]);
-        n0 = n_t * F::NCOL;
+        e = __builtin_amdgcn_readfirstlane(a);
+        r0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (m_t - s_tb[e]) * BM);
+        r_end = __builtin_amdgcn_readfirstlane(min(r0 + BM, s_hi[e]));
+        n0 = __builtin_amdgcn_readfirstlane(n_t * F::NCOL);
     };
     // A source rows of a tile into s_row[buf] (rows without a token: -1) and s_h[buf]
     auto load_rows = [&](int buf, int r0, int r_end) {
@@ -198,7 +261,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     const int pc = lane % F::CPR;     // physical chunk this lane's 16 bytes land in
     const uint16_t* a_src[F::A_INST];
     const uint16_t* b_src[F::B_INST];
-    int a_kc[F::A_INST], b_kc[F::B_INST];
     auto set_sources = [&](int bf, int e_, int r0_, int n0_) {
 #pragma unroll
         for (int q = 0; q < F::A_INST; ++q) {
@@ -209,7 +271,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             // first sorted row r0 < max_pad); its results are never stored
             const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0_);
             a_src[q] = A + static_cast<size_t>(srow) * K + kc * 8;
-            a_kc[q] = kc * 8;
         }
 #pragma unroll
         for (int q = 0; q < F::B_INST; ++q) {
@@ -221,30 +282,36 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             else { n = n0_ + row; W = W0; }
             n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
             b_src[q] = W + (static_cast<size_t>(e_) * N + n) * K + kc * 8;
-            b_kc[q] = kc * 8;
         }
     };
     set_sources(buf, e, r0, n0);
 
-    const int nk = (K + BK - 1) / BK;
-    int sb = 0;  // running stage count: stage t of the current tile lives in LDS buffer (sb + t) % STAGES
+    int nseg = ke - kb;  // stages of the current segment
+    int sb = 0;  // running stage count: stage t of the current segment lives in LDS buffer (sb + t) % STAGES
     auto stage_ptr = [&](int t) { return smem + ((sb + t) % STAGES) * F::STAGE_ELEMS; };
-    auto issue = [&](int kt) {
-        const int k0 = kt * BK;
-        uint16_t* st = stage_ptr(kt);
+    // loads of segment stage t (K stage kbase + t) into its LDS buffer
+    // The stage's 16-byte chunk of each lane is k0 + kc*8 with kc = swz_chunk(row, pc): only the
+    // stage that runs past K (uniform test) recomputes kc to load zeros for k >= K.
+    auto issue_at = [&](int t, int kbase) {
+        const int k0 = (kbase + t) * BK;
+        const bool tail = k0 + BK > K;
+        uint16_t* st = stage_ptr(t);
 #pragma unroll
         for (int q = 0; q < F::A_INST; ++q) {
-            const void* g = (k0 + a_kc[q] < K) ? static_cast<const void*>(a_src[q] + k0)
-                                                : static_cast<const void*>(kZero16);
+            const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
+            const bool in = !tail || k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+            const void* g = in ? static_cast<const void*>(a_src[q] + k0) : static_cast<const void*>(kZero16);
             dma16(g, lds_u32(st + (wave * F::A_INST + q) * 512));
         }
 #pragma unroll
         for (int q = 0; q < F::B_INST; ++q) {
-            const void* g = (k0 + b_kc[q] < K) ? static_cast<const void*>(b_src[q] + k0)
-                                                : static_cast<const void*>(kZero16);
+            const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
+            const bool in = !tail || k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+            const void* g = in ? static_cast<const void*>(b_src[q] + k0) : static_cast<const void*>(kZero16);
             dma16(g, lds_u32(st + F::A_ELEMS + (wave * F::B_INST + q) * 512));
         }
     };
+    auto issue = [&](int t) { issue_at(t, kb); };
 
     const int wm = wave >> 1, wn = wave & 1;  // wave grid WAVES_M x 2
     // 32x32x16 MFMA blocks: each wave holds FI x 4 blocks of 32x32 fp32 accumulators
@@ -291,7 +358,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
     // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
     auto ready = [&](int t) {
-        const int ahead = min(STAGES - 2, nk - 1 - t);
+        const int ahead = min(STAGES - 2, nseg - 1 - t);
         if constexpr (STAGES >= 4) {
             if (ahead >= 2) wait_vmcnt<2 * F::LOADS>();
             else if (ahead == 1) wait_vmcnt<F::LOADS>();
@@ -304,7 +371,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        if (t + STAGES - 1 < nk) issue(t + STAGES - 1);
+        if (t + STAGES - 1 < nseg) issue(t + STAGES - 1);
     };
     // Each k-step's MFMAs are issued after the next k-step's fragment reads (and, at a stage
     // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
@@ -312,12 +379,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     auto main_loop = [&](auto nf_c) {
         ready(0);
         read(nf_c, 0, 0, 0);
-        for (int s = 0; s < nk; ++s) {
+        for (int s = 0; s < nseg; ++s) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 if (kk + 1 < KK) {
                     read(nf_c, s, kk + 1, (kk + 1) & 1);
-                } else if (s + 1 < nk) {
+                } else if (s + 1 < nseg) {
                     ready(s + 1);
                     read(nf_c, s + 1, 0, 0);
                 }
@@ -327,10 +394,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     };
     static_assert(F::FI == 2, "tail skipping assumes two A fragments per wave");
 
-    // The first tile issues its first STAGES-1 stages here; later tiles find stage 0 already in
-    // flight (issued by the previous tile before its epilogue) and issue stages 1..STAGES-2.
+    // The first segment issues its first STAGES-1 stages here; later segments find stage 0
+    // already in flight (issued by the previous segment before its epilogue) and issue stages
+    // 1..STAGES-2.
     for (int t = 0; t < STAGES - 1; ++t)
-        if (t < nk) issue(t);
+        if (t < nseg) issue(t);
 
     while (true) {
         // rows up to the last token of this tile (an expert's sentinels follow its tokens): a wave
@@ -347,28 +415,99 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         else if (nf == 1) main_loop(std::integral_constant<int, 1>{});
         else main_loop(std::integral_constant<int, 0>{});
 
-        // ---- next tile: its rows, sources and first stage, before this tile's epilogue
-        const int L_next = L + per_xcd;
-        const bool more = L_next < l_hi;
+        // ---- a piece of a split tail tile: partial accumulators through the workspace.
+        // Partials are written and read with device-coherent (sc1) buffer accesses, the same
+        // accesses agent-scope atomic loads and stores use: a store is visible device-wide once
+        // it has completed (vmcnt), and such a load sees it, so no fence has to write back or
+        // invalidate the whole L2 (which would cost every other workgroup on the XCD its cached
+        // A tiles and weight panels).
+        constexpr int PART = F::NT * F::FI * 4 * 16;  // floats per partial
+        constexpr int kSc1 = 16;                      // cache policy: device scope
+        const bool split = L == tail_L && tail_s > 1;
+        bool store = true;
+        bool keep = true;  // the sum starts from acc ...
+        int np = 0;        // ... plus np partials
+        const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+            sk_part, 0, static_cast<int>(gridDim.x) * PART * 4, 0x00020000);
+        uint32_t off = 0;  // byte offset of this thread's first 16 bytes in partial 0 to add
+        if (split) {
+            // layout [16-byte chunk c][thread]: every store and load instruction is coalesced
+            uint32_t o = (static_cast<uint32_t>(pos) * PART + tid * 4) * 4;
+#pragma unroll
+            for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                      acc[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, part, o, 0, kSc1);
+                        o += F::NT * 16;
+                    }
+            wait_vmcnt<0>();  // this piece's partial is complete, hence visible, before it is counted
+            __syncthreads();
+            if (tid == 0)
+                s_arrived = __hip_atomic_fetch_add(&sk_cnt[L - static_cast<int>(Tw)], 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            store = s_arrived == tail_s - 1;
+            if (store) {
+                keep = false;  // the tile is the sum of all pieces' partials, in piece order
+                off = (static_cast<uint32_t>(tail_first) * PART + tid * 4) * 4;
+                np = tail_s;
+                if (tid == 0)
+                    __hip_atomic_store(&sk_cnt[L - static_cast<int>(Tw)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        // runs for every segment (nothing added when np == 0), so the accumulators are not merged
+        // from two branches, which costs registers
+        const uint32_t pstride = static_cast<uint32_t>(tail_n) * PART * 4;
+#pragma unroll
+        for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 t;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) t[v] = keep ? acc[i][j][4 * q + v] : 0.f;
+                    uint32_t o = off;
+                    for (int jp = 0; jp < np; ++jp) {
+                        t += __builtin_amdgcn_raw_buffer_load_b128(part, o, 0, kSc1);
+                        o += pstride;
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] = t[v];
+                    off += F::NT * 16;
+                }
+
+        // ---- next segment: its rows, sources and first stage, before this segment's epilogue
+        int L_next = L + per_xcd, kb2 = 0, ke2 = nk;
+        bool more = L != tail_L && L_next < l_hi;
+        if (!more && L != tail_L && tail_L >= 0) {
+            more = true;
+            L_next = tail_L; kb2 = tail_kb; ke2 = tail_ke;
+        }
         int e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
         if (more) {
             locate(L_next, e2, r02, r_end2, n02);
             if (tid == 0) s_h[buf ^ 1] = 0;
-            __syncthreads();  // every wave is past this tile's last stage reads and s_h is reset
+            __syncthreads();  // every wave is past this segment's last stage reads and s_h is reset
             load_rows(buf ^ 1, r02, r_end2);
             __syncthreads();
             set_sources(buf ^ 1, e2, r02, n02);
-            // stage 0 of the next tile goes to buffer (sb + nk) % STAGES, which held stage nk-STAGES+1
-            // .. of this tile at the latest and is no longer read by any wave
-            sb += nk;
-            issue(0);
-            sb -= nk;
+            // stage 0 of the next segment goes to buffer (sb + nseg) % STAGES, which held stage
+            // nseg-STAGES+1 .. of this segment at the latest and is no longer read by any wave
+            sb += nseg;
+            issue_at(0, kb2);
+            sb -= nseg;
         }
 
         // ---- epilogue straight from the accumulators: neighbour lanes (columns c, c+1) swap one
         // value so that each lane stores two adjacent bf16 columns of one row as 4 bytes
         const bool odd = (lane & 1) != 0;
         const int ccol = n0 + (fr & ~1);
+        if (store)
 #pragma unroll
         for (int i = 0; i < F::FI; ++i)
 #pragma unroll
@@ -399,57 +538,83 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         if (!more) break;
         L = L_next;
         e = e2; r0 = r02; r_end = r_end2; n0 = n02;
-        sb += nk;
+        sb += nseg;
+        kb = kb2; ke = ke2; nseg = ke - kb;
         buf ^= 1;
         for (int t = 1; t < STAGES - 1; ++t)
-            if (t < nk) issue(t);
+            if (t < nseg) issue(t);
     }
 }
+
+int device_cus(hipError_t& err) {
+    static int cus[64] = {0};
+    int dev = 0;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) return 0;
+    if (dev < 0 || dev >= 64) { err = hipErrorInvalidDevice; return 0; }
+    if (cus[dev] == 0) {
+        int n = 0;
+        err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+constexpr int kMaxGrid = 1024;                          // persistent grid cap
+constexpr int kSkMaxGrid = 256;                         // split-tail grid cap: partial slots in the workspace
+constexpr int64_t kSkCounterBytes = 4096;               // one int32 counter per tail tile (< grid), padded
+constexpr int64_t kSkPartBytes = 512LL * 2 * 64 * 4;    // largest partial: 512 threads x 128 fp32
+constexpr int64_t kSkWorkspaceBytes = kSkCounterBytes + kSkMaxGrid * kSkPartBytes;
+static_assert(kSkMaxGrid * 4 <= kSkCounterBytes, "split-tail counters overflow their area");
 
 template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
 hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                       const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
-                      int max_pad, hipStream_t s) {
+                      int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
+    static_assert(F::NT * F::FI * 64 * 4 <= kSkPartBytes, "partial accumulators larger than their workspace slot");
     const int n_tiles = (N + F::NCOL - 1) / F::NCOL;
-    // Persistent (one workgroup per compute unit, a multiple of the 8 XCDs) when there are more
-    // than 4 tiles per compute unit at worst.  With fewer, one workgroup per tile lets the hardware
-    // dispatcher hand late tiles to whichever compute unit frees up first, which balances better
-    // than a static share when a few long tiles remain.
-    static int cus[64] = {0};
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
+    hipError_t err = hipSuccess;
+    const int cus = device_cus(err);
     if (err != hipSuccess) return err;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cus[dev] == 0) {
-        int n = 0;
-        err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err != hipSuccess) return err;
-        cus[dev] = n;
-    }
-    const long long worst = static_cast<long long>((max_pad + BM - 1) / BM + E) * n_tiles;
-    long long grid = cus[dev] / 8 * 8;
+    long long grid = cus / 8 * 8;
     if (grid < 8) grid = 8;
-    const long long worst8 = (worst + 7) / 8 * 8;
-    if (worst8 <= 4 * grid) grid = worst8;
+    // The split tail needs the persistent grid and a workspace of counters + one partial per
+    // workgroup.
+    const bool sk = ws != nullptr && ws_bytes >= kSkWorkspaceBytes;
+    if (grid > (sk ? kSkMaxGrid : kMaxGrid)) grid = sk ? kSkMaxGrid : kMaxGrid;
+    if (!sk) {
+        // Persistent (one workgroup per compute unit) when there are more than 4 tiles per compute
+        // unit at worst.  With fewer, one workgroup per tile lets the hardware dispatcher hand late
+        // tiles to whichever compute unit frees up first, which balances better than a static
+        // share when a few long tiles remain.
+        const long long worst = static_cast<long long>((max_pad + BM - 1) / BM + E) * n_tiles;
+        const long long worst8 = (worst + 7) / 8 * 8;
+        if (worst8 <= 4 * grid) grid = worst8;
+    }
+    int32_t* cnt = sk ? static_cast<int32_t*>(ws) : nullptr;
+    float* part = sk ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSkCounterBytes) : nullptr;
     gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW><<<static_cast<int>(grid), F::NT, 0, s>>>(
-        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles);
+        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t gemm_bf16_workspace_bytes() { return kSkWorkspaceBytes; }
+
 hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
-                            int K, int max_pad, hipStream_t s) {
+                            int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
     // 256-row tiles when experts hold enough rows on average, 128-row tiles otherwise
     const bool big = static_cast<long long>(P) >= 384LL * E;
     if (gate_up) {
-        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
-        return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
+        return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
     }
-    if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
-    return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+    if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
+    return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
 }
 
 }  // namespace moe

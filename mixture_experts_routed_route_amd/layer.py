@@ -15,8 +15,8 @@ import numpy as np
 import torch
 
 from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU
-from .ops import (Bf16Weight, GptqWeight, LoraTables, Routing, lora_windows, moe_align, moe_combine,
-                  moe_grouped_gemm, moe_lora_fold, moe_route, moe_route_align, pack_lora_tables)
+from .ops import (Bf16Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows, moe_align,
+                  moe_combine, moe_grouped_gemm, moe_lora_fold, moe_route, moe_route_align, pack_lora_tables)
 
 
 @dataclass
@@ -29,6 +29,7 @@ class Buffers:
     ys: torch.Tensor
     out: torch.Tensor
     xa: Optional[torch.Tensor]
+    ws: torch.Tensor
 
 
 class MoeLayer:
@@ -73,15 +74,15 @@ class MoeLayer:
         return Buffers(T, torch.empty((T, self.top_k), dtype=torch.int32, device=device),
                        torch.empty((T, self.top_k), dtype=torch.float32, device=device), r,
                        torch.empty((r.max_pad, self.I), **bf), torch.empty((r.max_pad, self.H), **bf),
-                       torch.empty((T, self.H), **bf), xa)
+                       torch.empty((T, self.H), **bf), xa, gemm_workspace(device))
 
     # ------------------------------------------------------------------ forward
     def route_align(self, logits: torch.Tensor, b: Buffers) -> None:
         moe_route_align(logits, self.top_k, self.renormalize, self.bs, b.ids, b.w, b.routing)
 
     def experts(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
-        moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs)
-        moe_grouped_gemm(MOE_OP_DOWN, b.hs, self.down, None, b.routing, out=b.ys)
+        moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs, workspace=b.ws)
+        moe_grouped_gemm(MOE_OP_DOWN, b.hs, self.down, None, b.routing, out=b.ys, workspace=b.ws)
         if self.lora is not None:
             cap = b.xa.shape[0]
             for s, e in lora_windows(b.routing.max_pad, cap):

@@ -15,7 +15,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_W_BF16, MOE_W_INT4_GPTQ
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Routing", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "moe_lora_fold", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -81,6 +81,12 @@ def max_padded(num_pairs: int, num_experts: int, block_size: int) -> int:
 
 def align_workspace_bytes(num_pairs: int, num_experts: int) -> int:
     return int(lib().moe_align_workspace_bytes(num_pairs, num_experts))
+
+
+def gemm_workspace(device) -> torch.Tensor:
+    """A zero-filled workspace for moe_grouped_gemm's split-K tile balancing (calls leave it zeroed)."""
+    n = int(lib().moe_grouped_gemm_workspace_bytes())
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def check_group_arrays(num_experts: int, per_expert: Sequence[Tuple[str, int]], offsets: Sequence[int]) -> None:
@@ -188,8 +194,11 @@ def moe_route_align(logits: torch.Tensor, top_k: int, renormalize: bool, block_s
 
 # ----------------------------------------------------------------------------- A3 / A4 grouped GEMM
 def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight], routing: Routing,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """op = MOE_OP_GATE_UP_SILU (a = x [T, K], w0 = gate, w1 = up) or MOE_OP_DOWN (a = Hs [max_pad, K])."""
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """op = MOE_OP_GATE_UP_SILU (a = x [T, K], w0 = gate, w1 = up) or MOE_OP_DOWN (a = Hs [max_pad, K]).
+
+    ``workspace`` (from ``gemm_workspace``) lets bf16 launches split the last partial wave of tiles
+    over K; without it every tile is computed by one workgroup."""
     E, N, K = w0.shape
     if out is None:
         out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=a.device)
@@ -200,7 +209,9 @@ def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight],
                                  _dev(routing.sorted_ids, torch.int32, "sorted_ids"),
                                  _dev(routing.expert_ids, torch.int32, "expert_ids"),
                                  _dev(routing.offsets, torch.int32, "offsets"), routing.num_pairs, routing.top_k,
-                                 routing.num_experts, N, K, routing.block_size, routing.max_pad, _stream(a)))
+                                 routing.num_experts, N, K, routing.block_size, routing.max_pad,
+                                 _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
+                                 workspace.numel() if workspace is not None else 0, _stream(a)))
     return out
 
 

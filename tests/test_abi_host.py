@@ -24,7 +24,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     from mixture_experts_routed_route_amd import _lib
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
@@ -111,14 +111,18 @@ def test_argument_validation_rejects_before_launch(L):
     from mixture_experts_routed_route_amd._lib import MoeWeight
     w = MoeWeight(0, 0, 1 << 20, None, None)
     rc, msg = _rc(L, "moe_grouped_gemm", 0, fake, ctypes.byref(w), None, fake, fake, fake, fake, 128, 2, 8, 128,
-                  256, 16, 256, None)
+                  256, 16, 256, None, 0, None)
     assert rc == -1 and "w1" in msg
     rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w), None, fake, fake, fake, fake, 128, 2, 8, 100,
-                  256, 16, 256, None)
+                  256, 16, 256, None, 0, None)
     assert rc == -1 and "n 100" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w), None, fake, fake, fake, fake, 128, 2, 8, 128,
+                  256, 16, 256, fake, 64, None)
+    assert rc == -1 and "workspace_bytes" in msg
+    assert L.moe_grouped_gemm_workspace_bytes() > 0
     w4 = MoeWeight(1, 100, 1 << 20, fake, fake)
     rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w4), None, fake, fake, fake, fake, 128, 2, 8, 128,
-                  256, 16, 256, None)
+                  256, 16, 256, None, 0, None)
     assert rc == -1 and "group_size" in msg
     rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 48, fake, 64, fake, 12288, 6,
                   None, fake, 16320, 0, 16320, 16320, None)

@@ -101,6 +101,67 @@ def test_persistent_assignment_covers_each_tile_once(m_real, n_tiles, grid, gm):
     assert sorted(got) == [(m, n) for m in range(m_real) for n in range(n_tiles)]
 
 
+def _split_tail_segments(T, nk, grid, min_stages=8):
+    """Segments (tile, k_begin, k_end, pos, pieces, slot of piece 0, slot stride) of a launch with
+    a workspace (restates the kernel's integer arithmetic)."""
+    per_xcd = grid >> 3
+    Tw = T
+    rest = T % grid
+    if rest > 0 and min(per_xcd // ((rest + 7) // 8), nk // min_stages) >= 2:
+        Tw = T // grid * grid
+    tail = T - Tw
+    out = []
+    for bid in range(grid):
+        xcd, slot = bid & 7, bid >> 3
+        pos = xcd * per_xcd + slot
+        l_hi = Tw * (xcd + 1) // 8
+        L = Tw * xcd // 8 + slot
+        while slot < per_xcd and L < l_hi:
+            out.append((L, 0, nk, pos, 1, None, None))
+            L += per_xcd
+        if tail > 0:
+            a_x = tail * xcd // 8
+            n_x = tail * (xcd + 1) // 8 - a_x
+            if n_x > 0:
+                s_x = max(1, min(per_xcd // n_x, nk // min_stages))
+                if slot < s_x * n_x:
+                    u, j = slot % n_x, slot // n_x
+                    out.append((Tw + a_x + u, j * nk // s_x, (j + 1) * nk // s_x, pos, s_x,
+                                xcd * per_xcd + u, n_x))
+    return out, Tw
+
+
+@pytest.mark.parametrize("T,nk,grid", [
+    (592, 224, 256), (4032, 64, 256), (299, 45, 256), (276, 25, 256), (272, 17, 256), (128, 17, 256),
+    (80, 16, 256), (192, 34, 256), (1, 300, 256), (257, 8, 256), (384, 40, 256), (255, 100, 256),
+    (17, 64, 16), (0, 10, 256)])
+def test_split_tail_covers_each_stage_once(T, nk, grid):
+    """With a workspace, the whole-tile rounds and the tail pieces cover every (tile, K stage)
+    exactly once; the pieces of a tile share one piece count and sit on slots piece0 + j*stride,
+    all inside the grid's partial slots; tail tile counters stay below the grid size."""
+    segs, Tw = _split_tail_segments(T, nk, grid)
+    cover = np.zeros((T, nk), np.int32)
+    pieces = {}
+    for L, kb, ke, pos, s, first, stride in segs:
+        assert 0 <= L < T and 0 <= kb < ke <= nk and 0 <= pos < grid
+        cover[L, kb:ke] += 1
+        if s > 1:
+            assert L - Tw < grid and ke - kb >= 8
+            pieces.setdefault(L, []).append((kb, pos, s, first, stride))
+    assert (cover == 1).all()
+    for L, ps in pieces.items():
+        ps.sort()
+        s, first, stride = ps[0][2:]
+        assert len(ps) == s and all(p[2:] == (s, first, stride) for p in ps)
+        assert [p[1] for p in ps] == [first + j * stride for j in range(s)]
+    # each workgroup runs whole tiles first, then at most one piece
+    per_pos = {}
+    for seg in segs:
+        per_pos.setdefault(seg[3], []).append(seg)
+    for lst in per_pos.values():
+        assert sum(1 for x in lst if x[4] > 1 or x[0] >= Tw) <= 1
+
+
 def test_expert_of_row_tile_binary_search():
     """Largest expert whose first row tile is <= m_t, with empty experts in between (the kernel's
     binary search over the inclusive tile scan)."""

@@ -190,6 +190,60 @@ def test_grouped_gemms_small(dev, name):
     assert_close_rows(bf16_host(ys)[real], y_ref[real], TOL, "down")
 
 
+# Shapes whose tile counts make a workspace cut the last partial round of tiles along K (the
+# split tail): on a 256-workgroup grid, T tiles leave T mod 256 tail tiles, split s ways when
+# every XCD's share of them fits s times in its 32 workgroups and K holds s pieces of >= 8
+# stages of 64.  Ragged K and N tails throughout.
+SPLIT_K = {
+    # 128-row tiles: gate/up 299 tiles (43 in the tail, 5 pieces), down 276 (20, 3 pieces)
+    "rows128": MoeConfig("sk_128", T=1024, H=2824, I=1544, E=16, top_k=2, block_size=64, seed=31),
+    # 256-row tiles: gate/up 272 tiles (16, 5 pieces); down 192 tiles, less than a round and
+    # too many to split: whole tiles
+    "rows256": MoeConfig("sk_256", T=1536, H=2824, I=2120, E=8, top_k=2, block_size=64, seed=33),
+    # gate/up 144 tiles, not split; down 272 tiles (16 in the tail, 2 pieces of 8-9 stages)
+    "rows256_min_pieces": MoeConfig("sk_256b", T=1536, H=4104, I=1032, E=8, top_k=2, block_size=64, seed=34),
+    # less than a round: every tile is a tail tile, gate/up 128 tiles and down 80, in 2 pieces
+    "all_tail": MoeConfig("sk_tail", T=1536, H=1032, I=1000, E=8, top_k=2, block_size=64, seed=35),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_K))
+def test_grouped_gemms_split_k_workspace(dev, name):
+    """With and without the workspace, both GEMMs match the oracle on every real row; two calls
+    that share the workspace give identical bits (the pieces of a split tile are summed in piece
+    order, whatever their arrival order); the workspace counters are back at zero."""
+    m = ops()
+    cfg = SPLIT_K[name]
+    note(f"gemm split-K {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E}")
+    d = make_inputs(cfg)
+    ids, w, al, r = _routing(cfg, d)
+    layer = _weights_dev(d)
+    real = _real(al, cfg.P)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    ws = m.gemm_workspace("cuda")
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    h_ref = oracle.grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
+    h_in = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
+    h_in[real] = f32_to_bf16_bits(oracle.round_bf16(h_ref[real]).astype(np.float32))
+    y_ref = oracle.grouped_down(oracle.bf16_bits_to_f64(h_in), wd, al)
+    x_dev, h_dev = bf16_dev(d["x"]), bf16_dev(h_in)
+    runs = []
+    for use_ws in (False, True, True):
+        hs = _canary(r.max_pad, cfg.I)
+        m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, x_dev, layer.gate, layer.up, r, out=hs,
+                           workspace=ws if use_ws else None)
+        ys = _canary(r.max_pad, cfg.H)
+        m.moe_grouped_gemm(m.MOE_OP_DOWN, h_dev, layer.down, None, r, out=ys, workspace=ws if use_ws else None)
+        hs_b, ys_b = bits_host(hs), bits_host(ys)
+        tag = "with workspace" if use_ws else "without workspace"
+        assert (hs_b[pad] == CANARY).all() and (ys_b[pad] == CANARY).all(), f"padding rows written ({tag})"
+        assert_close_rows(bf16_host(hs)[real], h_ref[real], TOL, f"gate/up {tag}")
+        assert_close_rows(bf16_host(ys)[real], y_ref[real], TOL, f"down {tag}")
+        runs.append((hs_b, ys_b))
+    assert np.array_equal(runs[1][0], runs[2][0]) and np.array_equal(runs[1][1], runs[2][1])
+    assert not ws[:4096].cpu().numpy().any(), "split-K counters not reset"
+
+
 # ----------------------------------------------------------------------------- A6 combine
 @pytest.mark.parametrize("name", ["tiny", "finegrained_small", "mixtral_small"])
 def test_combine(dev, name):
