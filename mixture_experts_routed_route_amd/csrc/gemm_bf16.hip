@@ -148,7 +148,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     __shared__ int s_h[2];                                        // rows up to the last token
     __shared__ int s_arrived;                                     // split tile: the other side's count
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in a scalar register
 
     // ---- expert spans and their row tiles (once per workgroup)
     {
@@ -289,26 +290,37 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     int nseg = ke - kb;  // stages of the current segment
     int sb = 0;  // running stage count: stage t of the current segment lives in LDS buffer (sb + t) % STAGES
     auto stage_ptr = [&](int t) { return smem + ((sb + t) % STAGES) * F::STAGE_ELEMS; };
-    // loads of segment stage t (K stage kbase + t) into its LDS buffer
-    // The stage's 16-byte chunk of each lane is k0 + kc*8 with kc = swz_chunk(row, pc): only the
-    // stage that runs past K (uniform test) recomputes kc to load zeros for k >= K.
+    // LDS byte address of this wave's first 1 KB block of stage buffer 0 (A part and B part):
+    // scalar, so each load only adds the buffer offset and moves it to m0
+    const uint32_t lds_a = lds_u32(smem) + (wave * F::A_INST) * 1024;
+    const uint32_t lds_b = lds_u32(smem) + F::A_ELEMS * 2 + (wave * F::B_INST) * 1024;
+    // loads of segment stage t (K stage kbase + t) into its LDS buffer.  The stage's 16-byte
+    // chunk of each lane is k0 + kc*8 with kc = swz_chunk(row, pc); only the stage that runs past
+    // K (uniform test) recomputes kc to load zeros for k >= K.
     auto issue_at = [&](int t, int kbase) {
         const int k0 = (kbase + t) * BK;
-        const bool tail = k0 + BK > K;
-        uint16_t* st = stage_ptr(t);
+        const uint32_t sbuf = static_cast<uint32_t>((sb + t) % STAGES) * (F::STAGE_ELEMS * 2);
+        if (k0 + BK <= K) {
 #pragma unroll
-        for (int q = 0; q < F::A_INST; ++q) {
-            const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
-            const bool in = !tail || k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
-            const void* g = in ? static_cast<const void*>(a_src[q] + k0) : static_cast<const void*>(kZero16);
-            dma16(g, lds_u32(st + (wave * F::A_INST + q) * 512));
-        }
+            for (int q = 0; q < F::A_INST; ++q) dma16(a_src[q] + k0, lds_a + sbuf + q * 1024);
 #pragma unroll
-        for (int q = 0; q < F::B_INST; ++q) {
-            const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
-            const bool in = !tail || k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
-            const void* g = in ? static_cast<const void*>(b_src[q] + k0) : static_cast<const void*>(kZero16);
-            dma16(g, lds_u32(st + F::A_ELEMS + (wave * F::B_INST + q) * 512));
+            for (int q = 0; q < F::B_INST; ++q) dma16(b_src[q] + k0, lds_b + sbuf + q * 1024);
+        } else {
+            // the stage that runs past K: chunks at k >= K load zeros
+#pragma unroll
+            for (int q = 0; q < F::A_INST; ++q) {
+                const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
+                const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+                const void* g = in ? static_cast<const void*>(a_src[q] + k0) : static_cast<const void*>(kZero16);
+                dma16(g, lds_a + sbuf + q * 1024);
+            }
+#pragma unroll
+            for (int q = 0; q < F::B_INST; ++q) {
+                const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
+                const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+                const void* g = in ? static_cast<const void*>(b_src[q] + k0) : static_cast<const void*>(kZero16);
+                dma16(g, lds_b + sbuf + q * 1024);
+            }
         }
     };
     auto issue = [&](int t) { issue_at(t, kb); };
