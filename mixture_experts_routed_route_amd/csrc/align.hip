@@ -107,7 +107,7 @@ __device__ __forceinline__ void align_scatter_body(
         }
     }
     const int padded = (tid < E) ? ((tot + bs - 1) / bs) * bs : 0;
-    const int incl = block_inclusive_scan<NWAVES>(padded, s_scan);
+    const int incl = block_inclusive_scan<NWAVES>(padded, s_scan, (E + 63) / 64);
     if (tid < E) {
         s_off[tid] = incl - padded;
         s_cnt[tid] = tot;
@@ -215,15 +215,16 @@ __global__ __launch_bounds__(64 * kFusedWaves) void route_align_kernel(
     const float* __restrict__ logits, int T, int E, int top_k, int renorm, int32_t* topk_ids, float* topk_w,
     int bs, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad) {
+    __shared__ int s_ids[kChunk];  // the routed expert ids, handed to the alignment in LDS
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (T <= kFusedWaves) {
-        if (wave < T) route_tokens<EPL, 1>(logits, wave, 0, T, E, top_k, renorm, topk_ids, topk_w, lane);
+        if (wave < T) route_tokens<EPL, 1>(logits, wave, 0, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
     } else {
         for (int t = wave; t < T; t += kFusedWaves * 4)
-            route_tokens<EPL, 4>(logits, t, kFusedWaves, T, E, top_k, renorm, topk_ids, topk_w, lane);
+            route_tokens<EPL, 4>(logits, t, kFusedWaves, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
     }
-    __syncthreads();  // the workgroup's id stores are visible to its own loads after the barrier
-    align_scatter_body<true, kFusedWaves>(topk_ids, T * top_k, E, bs, nullptr, 1, counts, offsets, sorted_ids,
+    __syncthreads();
+    align_scatter_body<true, kFusedWaves>(s_ids, T * top_k, E, bs, nullptr, 1, counts, offsets, sorted_ids,
                                           expert_ids, total_out, inv, max_pad, 0);
 }
 

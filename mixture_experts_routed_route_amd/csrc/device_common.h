@@ -40,21 +40,38 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-// Inclusive prefix sum of `v` over a block of NW waves; `scratch` holds >= NW ints.
-// Every thread of the block must call it.
+// Inclusive prefix sum of `v` over the 64 lanes of a wave with DPP: shifts by 1, 2, 4 and 8
+// lanes inside each row of 16, then row 0's and row 2's last lane into the rows after them
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).  Lanes without a source add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+    return v;
+}
+
+// Inclusive prefix sum of `v` over the first `active` waves of a block of NW waves (values of
+// later waves are ignored); the result is defined on those waves only.  `scratch` holds >= NW
+// ints.  Every thread of the block must call it with the same `active`.  With one active wave
+// there is no exchange and no barrier; otherwise the barriers order LDS only.
 template <int NW>
-__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch) {
+__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int active = NW) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+    v = wave_inclusive_scan(v);
+    if (active <= 1) return v;
     if (lane == 63) scratch[wave] = v;
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     int add = 0;
-    for (int w = 0; w < wave; ++w) add += scratch[w];
-    __syncthreads();
+    const int nw = wave < active ? wave : 0;
+    for (int w = 0; w < nw; ++w) add += scratch[w];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     return v + add;
 }
 

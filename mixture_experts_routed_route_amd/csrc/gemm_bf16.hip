@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             hi = min(max(offsets[tid + 1], lo), max_pad);
         }
         const int nt_e = (hi - lo + BM - 1) / BM;
-        const int incl = block_inclusive_scan<NW>(nt_e, s_scan);
+        const int incl = block_inclusive_scan<NW>(nt_e, s_scan, (E + 63) / 64);
         if (tid < E) { s_lo[tid] = lo; s_hi[tid] = hi; s_tb[tid + 1] = incl; }
         if (tid == 0) { s_tb[0] = 0; s_h[0] = 0; s_h[1] = 0; }
         __syncthreads();

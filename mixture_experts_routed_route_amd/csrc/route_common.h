@@ -66,12 +66,13 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 // Route NTOK tokens t0, t0+dt, ... (those below T), called by all 64 lanes of one wave: writes
-// ids/w[t*top_k .. +top_k) of each.  The tokens' selection rounds are independent, so their
-// cross-lane reductions interleave and hide each other's latency.
+// ids/w[t*top_k .. +top_k) of each, and the ids also to lds_ids[] when it is given.  The tokens'
+// selection rounds are independent, so their cross-lane reductions interleave and hide each
+// other's latency.
 template <int EPL, int NTOK>
 __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int t0, int dt, int T, int E,
                                              int top_k, int renorm, int32_t* __restrict__ ids,
-                                             float* __restrict__ w, int lane) {
+                                             float* __restrict__ w, int lane, int* lds_ids = nullptr) {
     float v[NTOK][EPL];
     uint64_t key[NTOK][EPL];
 #pragma unroll
@@ -134,6 +135,7 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
             const double wj = renorm ? p / den : p;
             ids[static_cast<size_t>(t) * top_k + lane] = my_e[n];
             w[static_cast<size_t>(t) * top_k + lane] = static_cast<float>(wj);
+            if (lds_ids != nullptr) lds_ids[t * top_k + lane] = my_e[n];
         }
     }
 }
