@@ -180,17 +180,17 @@ typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1 } moe_gemm_op;
  *   c: bf16 [max_pad, N].  K % 8 == 0, N % 8 == 0 (int4: N % 64 == 0,
  *   K % group_size == 0).  Both weights must have the same type.
  *   workspace: optional device buffer of >= moe_grouped_gemm_workspace_bytes()
- *   bytes, or NULL.  With it, bf16 launches that have at least as many output
- *   tiles as workgroups cut the K loops of all tiles, end to end, into equal
- *   ranges, one per workgroup (stream-K), so no workgroup idles through a
- *   last partial wave of tiles; a tile cut by a range boundary is computed in
- *   two halves that meet through fp32 partials and a counter kept there.  It
- *   must be zero-filled once before its first use; every call leaves its
+ *   bytes, or NULL.  With it, a bf16 launch whose output tiles end in a
+ *   partial round of the persistent grid cuts that round's tiles along K into
+ *   pieces spread over the whole grid (split tail), so no compute unit idles
+ *   through a last partial round; the pieces of a tile meet through fp32
+ *   partials and a counter kept there.  It must be zero-filled once before
+ *   its first use; every call leaves its
  *   counters at zero again.  Calls that share one workspace must not run
  *   concurrently.  A smaller non-NULL buffer is rejected (MOE_EINVAL).  int4
- *   launches ignore it.  Results with and without it agree to fp32 summation
- *   order; with it they are deterministic (a split tile is the exact sum of
- *   its two halves). */
+ *   launches check its size but do not use it.  Results with and without it
+ *   agree to fp32 summation order; with it they are deterministic (pieces are
+ *   summed in a fixed order). */
 moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0, const moe_weight* w1,
                             uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,

@@ -263,7 +263,7 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
     else REQUIRE(w1 == nullptr, "%s: MOE_OP_DOWN takes no w1", who);
     REQUIRE(w0->type == MOE_W_BF16 || w0->type == MOE_W_INT4_GPTQ, "%s: w0 has unknown type %d", who, w0->type);
     if (w1) REQUIRE(w1->type == w0->type, "%s: w0 and w1 have different types", who);
-    if (workspace != nullptr && w0->type == MOE_W_BF16) {
+    if (workspace != nullptr) {
         const int64_t need = moe_grouped_gemm_workspace_bytes();
         REQUIRE_PTR(who, workspace);
         REQUIRE(need > 0 && workspace_bytes >= need, "%s: workspace_bytes %lld < required %lld", who,

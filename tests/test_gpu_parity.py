@@ -204,11 +204,22 @@ SPLIT_K = {
     "rows256_min_pieces": MoeConfig("sk_256b", T=1536, H=4104, I=1032, E=8, top_k=2, block_size=64, seed=34),
     # less than a round: every tile is a tail tile, gate/up 128 tiles and down 80, in 2 pieces
     "all_tail": MoeConfig("sk_tail", T=1536, H=1032, I=1000, E=8, top_k=2, block_size=64, seed=35),
+    # GPTQ int4 takes the workspace (size-checked) and does not use it: results as without it
+    "int4_decode_g128": CONFIGS["decode_int4"],
+    "int4_decode_g256": MoeConfig("sk_i4_256", T=16, H=2048, I=1536, E=64, top_k=6, block_size=16,
+                                  weights="int4_gptq", group_size=256, seed=37),
 }
 
 
+@pytest.fixture(scope="module")
+def shared_ws(dev):
+    """One workspace for every split case, bf16 cases first: each call must leave the counters it
+    used at zero, whatever kernel used the workspace before."""
+    return ops().gemm_workspace("cuda")
+
+
 @pytest.mark.parametrize("name", list(SPLIT_K))
-def test_grouped_gemms_split_k_workspace(dev, name):
+def test_grouped_gemms_split_k_workspace(dev, shared_ws, name):
     """With and without the workspace, both GEMMs match the oracle on every real row; two calls
     that share the workspace give identical bits (the pieces of a split tile are summed in piece
     order, whatever their arrival order); the workspace counters are back at zero."""
@@ -220,7 +231,7 @@ def test_grouped_gemms_split_k_workspace(dev, name):
     layer = _weights_dev(d)
     real = _real(al, cfg.P)
     pad = np.setdiff1d(np.arange(r.max_pad), real)
-    ws = m.gemm_workspace("cuda")
+    ws = shared_ws
     wg, wu, wd = oracle.moe_oracle._weights(d)
     h_ref = oracle.grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
     h_in = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
@@ -241,7 +252,7 @@ def test_grouped_gemms_split_k_workspace(dev, name):
         assert_close_rows(bf16_host(ys)[real], y_ref[real], TOL, f"down {tag}")
         runs.append((hs_b, ys_b))
     assert np.array_equal(runs[1][0], runs[2][0]) and np.array_equal(runs[1][1], runs[2][1])
-    assert not ws[:4096].cpu().numpy().any(), "split-K counters not reset"
+    assert not ws[:4096].cpu().numpy().any(), "split counters not reset"
 
 
 # ----------------------------------------------------------------------------- A6 combine
