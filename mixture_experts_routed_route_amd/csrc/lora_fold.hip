@@ -19,7 +19,16 @@ namespace moe {
 namespace {
 
 constexpr int NT = 256;
-constexpr int EXP_COLS = 256;     // expand output columns per workgroup
+#ifndef MOE_LORA_EXP_COLS
+#define MOE_LORA_EXP_COLS 64
+#endif
+// expand output columns per workgroup (32 to 256; 64 measured best: 4 accumulators per wave keep
+// 4 waves per SIMD and the base-row loads in flight)
+constexpr int EXP_COLS = MOE_LORA_EXP_COLS;
+static_assert(EXP_COLS >= 32 && EXP_COLS <= 256 && (EXP_COLS & (EXP_COLS - 1)) == 0, "expand tile width");
+constexpr int FOLD_LPR = EXP_COLS / 8;       // fold: lanes per row (8 columns each)
+constexpr int FOLD_RPS = 64 / FOLD_LPR;      // fold: rows per step
+constexpr int FOLD_STEPS = 16 / FOLD_RPS;    // fold: steps over a 16-row sub-tile
 constexpr int MAX_RANK_BLOCKS = 8;  // max_rank <= 128
 
 struct SubTile {
@@ -150,6 +159,20 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
     if (__ballot(act) == 0) return;
     const uint16_t* xr = act ? xa + (r - row_offset) * max_rank + kq * 8 : nullptr;
 
+    // the base rows this wave folds into (FOLD_RPS rows x FOLD_LPR lanes x 8 columns per step)
+    // are loaded first, so that their memory round trip overlaps the delta's loads and MFMAs
+    const int col = (lane % FOLD_LPR) * 8;
+    bool ok[FOLD_STEPS];
+    u32x4 bvs[FOLD_STEPS];
+#pragma unroll
+    for (int it = 0; it < FOLD_STEPS; ++it) {
+        const int rl = it * FOLD_RPS + lane / FOLD_LPR;
+        const int64_t rr = sub0 + rl;
+        ok[it] = n0 + col < n_out &&
+                 row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
+        bvs[it] = ok[it] ? *reinterpret_cast<const u32x4*>(base + rr * n_out + n0 + col) : u32x4{0, 0, 0, 0};
+    }
+
     f32x4 acc[EXP_COLS / 16];
 #pragma unroll
     for (int c = 0; c < EXP_COLS / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -171,23 +194,11 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
         for (int v = 0; v < 4; ++v) s_delta[wave][4 * kq + v][c * 16 + m] = f32_to_bf16(acc[c][v]);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    // coalesced fold: 2 rows x 32 lanes x 8 columns per step; all 8 steps' base rows are read
-    // before any is written back (one memory round trip per wave)
-    const int col = (lane & 31) * 8;
-    bool ok[8];
-    u32x4 bvs[8];
+    // coalesced fold of the delta into the base rows loaded above
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int rl = it * 2 + (lane >> 5);
-        const int64_t rr = sub0 + rl;
-        ok[it] = n0 + col < n_out &&
-                 row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
-        bvs[it] = ok[it] ? *reinterpret_cast<const u32x4*>(base + rr * n_out + n0 + col) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < FOLD_STEPS; ++it) {
         if (!ok[it]) continue;
-        const int rl = it * 2 + (lane >> 5);
+        const int rl = it * FOLD_RPS + lane / FOLD_LPR;
         const int64_t rr = sub0 + rl;
         const u32x4 bv = bvs[it];
         const u32x4 dv = *reinterpret_cast<const u32x4*>(&s_delta[wave][rl][col]);
