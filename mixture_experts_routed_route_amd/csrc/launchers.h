@@ -26,7 +26,7 @@ hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int 
 hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w, uint16_t* out, int T, int k,
                           int H, int64_t ys_rows, hipStream_t s);
 
-// gemm_bf16.hip (ws: optional stream-K workspace, zero-filled before first use; NULL = none)
+// gemm_bf16.hip (ws: optional split-tail workspace, zero-filled before first use; NULL = none)
 int64_t gemm_bf16_workspace_bytes();
 hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
