@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0,
                     help="independent weight copies cycled through (0: enough for >= 1 GiB of weights, max 4)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time steps replayed from HIP graphs (one captured step per weight copy); the "
+                         "per-kernel figures then come from an eager pass of the same steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -178,13 +181,38 @@ def main():
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    if args.graph:
+        # the path allocates nothing and issues no memset, so a step captures as it runs eagerly
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for i in range(rot):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % rot].replay()
+        torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} graph replays")
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % rot].replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        log("[bench] per-kernel timing: eager pass")
+        for i in range(args.steps):
+            step(i, events[i])
+        torch.cuda.synchronize()
+    else:
+        log(f"[bench] timing {args.steps} steps")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, events[i])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
@@ -239,7 +267,8 @@ def main():
         "data": "synthetic (seeded numpy PCG64; random-init expert weights)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
-                   "weights": cfg.weights, "lora_rank": cfg.lora_rank},
+                   "weights": cfg.weights, "lora_rank": cfg.lora_rank,
+                   "launch": "hip_graph" if args.graph else "eager"},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
         "kernels_ms": {"gate_up": gu_ms, "down": dn_ms},
