@@ -178,7 +178,9 @@ typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1 } moe_gemm_op;
  * moe_align).  Sentinel and padding rows are neither read as tokens nor
  * written: c keeps its previous content there.  fp32 accumulation.
  *   c: bf16 [max_pad, N].  K % 8 == 0, N % 8 == 0 (int4: N % 64 == 0,
- *   K % group_size == 0).  Both weights must have the same type.
+ *   K % group_size == 0).  Both weights must have the same type.  bf16: a
+ *   and each expert's [N, K] matrix must each be under 4 GiB
+ *   (MOE_EUNSUPPORTED otherwise).
  *   workspace: optional device buffer of >= moe_grouped_gemm_workspace_bytes()
  *   bytes, or NULL.  With it, a bf16 launch whose output tiles end in a
  *   partial round of the persistent grid cuts that round's tiles along K into

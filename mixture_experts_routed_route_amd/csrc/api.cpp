@@ -279,6 +279,11 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
     const int P = static_cast<int>(num_pairs);
     if (w0->type == MOE_W_BF16) {
         REQUIRE_PTR(who, expert_offsets);
+        // the kernel addresses a's rows and each expert matrix with 32-bit byte offsets
+        const int64_t a_rows = gate_up ? num_pairs / top_k : max_pad;
+        if (a_rows * k * 2 > INT64_C(0xffffffff) || static_cast<int64_t>(n) * k * 2 > INT64_C(0xffffffff))
+            return fail(MOE_EUNSUPPORTED, "%s: bf16 a (%lld rows) or an expert matrix (%d x %d) exceeds 4 GiB", who,
+                        static_cast<long long>(a_rows), n, k);
         return launched(who, moe::launch_gemm_bf16(gate_up, a, static_cast<const uint16_t*>(w0->data),
                                                    w1 ? static_cast<const uint16_t*>(w1->data) : nullptr, c,
                                                    sorted_ids, expert_offsets, P, top_k, num_experts, n, k,

@@ -11,7 +11,8 @@
 //
 // Pipeline.  NW waves in a (NW/2) x 2 grid, each owning 64 x 128 of the tile as 32x32x16 bf16
 // MFMA blocks with fp32 accumulators.  256-row tiles use 8 waves, two per SIMD, so one wave's
-// LDS and barrier waits overlap the other's MFMAs.  K advances BK at a time through a ring of
+// LDS and barrier waits overlap the other's MFMAs; there waves 0-3 issue all of a stage's loads
+// (see the DMA sources below), so that the address unit stalls only one wave of each SIMD.  K advances BK at a time through a ring of
 // STAGES LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4: no VGPR
 // staging, no LDS store instructions; issued from inline asm, see dma16); STAGES-1 stages are in
 // flight while one is computed.  Each thread waits on its own loads with an explicit vmcnt, then
@@ -63,6 +64,9 @@ constexpr int BP = 256;
 #ifndef MOE_GEMM_BIG_BK
 #define MOE_GEMM_BIG_BK 64       // k per LDS stage of the 256-row tiles
 #endif
+#ifndef MOE_GEMM_ASYM
+#define MOE_GEMM_ASYM 1  // 8 waves, 2 stages: waves 0-3 issue all of a stage's loads
+#endif
 #ifndef MOE_GEMM_SPLIT_MIN_STAGES
 #define MOE_GEMM_SPLIT_MIN_STAGES 8  // K stages per piece of a split tail tile, at least
 #endif
@@ -88,6 +92,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // tracked with explicit vmcnt waits instead.  m0 is written inside the statement itself.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory");
+}
+
+// The same with the source as a scalar base plus a 32-bit per-lane byte offset (saddr form).
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
+                 : "memory");
+}
+
+// A wave-uniform pointer held in scalar registers (a select between two uniform pointers may
+// otherwise be formed in vector registers, which an "s" operand cannot take).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -224,7 +244,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     }
 
     // tile L -> expert e, first sorted row r0, rows end r_end, first output column n0
-    auto locate = [&](int Lt, int& e, int& r0, int& r_end, int& n0) {
+    auto locate = [&](int Lt, int& e, int& r0, int& r_end, int& n0) __attribute__((always_inline)) {
         int m_t, n_t;
         decode_tile(Lt, F::GM, m_real, n_tiles, m_t, n_t);
         int a = 0, b = E - 1;  // largest expert whose first row tile is <= m_t
@@ -238,7 +258,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         n0 = __builtin_amdgcn_readfirstlane(n_t * F::NCOL);
     };
     // A source rows of a tile into s_row[buf] (rows without a token: -1) and s_h[buf]
-    auto load_rows = [&](int buf, int r0, int r_end) {
+    auto load_rows = [&](int buf, int r0, int r_end) __attribute__((always_inline)) {
         for (int i = tid; i < BM; i += NT) {
             const int r = r0 + i;
             int src = -1;
@@ -257,73 +277,122 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     load_rows(buf, r0, r_end);
     __syncthreads();
 
-    // ---- per-lane DMA sources: instruction q of this wave fills ROWS_PER_INST rows
+    // ---- per-lane DMA sources.  Instruction q of a wave's row block fills ROWS_PER_INST rows.
+    // With MOE_GEMM_ASYM (8 waves, 2 stages) waves 0-3, one per SIMD, issue the loads of their own
+    // row block and of wave w+4's, and waves 4-7 issue none: while an issuing wave stalls on the
+    // address unit, the other wave of its SIMD issues MFMAs.  To hold twice the sources in the
+    // same registers, those are byte offsets from scalar bases (A, and the tile's expert
+    // matrices) and each load is a saddr-form instruction; otherwise they are 64-bit pointers.
+    constexpr bool ASYM = MOE_GEMM_ASYM != 0 && NW == 8 && STAGES == 2;
+    constexpr int NBLK = ASYM ? 2 : 1;  // row blocks issued per issuing wave
+    const bool issuer = !ASYM || wave < NW / 2;
     const int lrow = lane / F::CPR;   // row within the instruction's block
     const int pc = lane % F::CPR;     // physical chunk this lane's 16 bytes land in
-    const uint16_t* a_src[F::A_INST];
-    const uint16_t* b_src[F::B_INST];
-    auto set_sources = [&](int bf, int e_, int r0_, int n0_) {
+    using Src = std::conditional_t<ASYM, uint32_t, const uint16_t*>;
+    Src a_o[NBLK][F::A_INST], b_o[NBLK][F::B_INST];
+    const uint16_t* b_base0 = W0;     // the tile's expert matrices (uniform)
+    const uint16_t* b_base1 = W1;
+    auto block_wave = [&](int j) __attribute__((always_inline)) { return wave + j * (NW / 2); };
+    auto set_sources = [&](int bf, int e_, int r0_, int n0_) __attribute__((always_inline)) {
+        b_base0 = W0 + static_cast<size_t>(e_) * N * K;
+        b_base1 = GATE_UP ? W1 + static_cast<size_t>(e_) * N * K : b_base0;
+        if (!issuer) return;
 #pragma unroll
-        for (int q = 0; q < F::A_INST; ++q) {
-            const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
-            const int kc = swz_chunk(row, pc, F::RP, F::CPR);
-            const int src = s_row[bf][row];
-            // a row without a token reads a row that is always in bounds (token 0, or the tile's
-            // first sorted row r0 < max_pad); its results are never stored
-            const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0_);
-            a_src[q] = A + static_cast<size_t>(srow) * K + kc * 8;
-        }
+        for (int j = 0; j < NBLK; ++j) {
+            const int bw = block_wave(j);
 #pragma unroll
-        for (int q = 0; q < F::B_INST; ++q) {
-            const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
-            const int kc = swz_chunk(row, pc, F::RP, F::CPR);
-            int n;
-            const uint16_t* W;
-            if (GATE_UP) { n = n0_ + (row & (BP / 2 - 1)); W = row < BP / 2 ? W0 : W1; }
-            else { n = n0_ + row; W = W0; }
-            n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
-            b_src[q] = W + (static_cast<size_t>(e_) * N + n) * K + kc * 8;
+            for (int q = 0; q < F::A_INST; ++q) {
+                const int row = (bw * F::A_INST + q) * F::ROWS_PER_INST + lrow;
+                const int kc = swz_chunk(row, pc, F::RP, F::CPR);
+                const int src = s_row[bf][row];
+                // a row without a token reads a row that is always in bounds (token 0, or the
+                // tile's first sorted row r0 < max_pad); its results are never stored
+                const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0_);
+                if constexpr (ASYM) a_o[j][q] = (static_cast<uint32_t>(srow) * K + kc * 8) * 2;
+                else a_o[j][q] = A + static_cast<size_t>(srow) * K + kc * 8;
+            }
+#pragma unroll
+            for (int q = 0; q < F::B_INST; ++q) {
+                const int row = (bw * F::B_INST + q) * F::ROWS_PER_INST + lrow;
+                const int kc = swz_chunk(row, pc, F::RP, F::CPR);
+                int n = GATE_UP ? n0_ + (row & (BP / 2 - 1)) : n0_ + row;
+                n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
+                if constexpr (ASYM) {
+                    b_o[j][q] = (static_cast<uint32_t>(n) * K + kc * 8) * 2;
+                } else {
+                    const uint16_t* bb = (GATE_UP && row >= BP / 2) ? b_base1 : b_base0;
+                    b_o[j][q] = bb + static_cast<size_t>(n) * K + kc * 8;
+                }
+            }
         }
     };
     set_sources(buf, e, r0, n0);
 
     int nseg = ke - kb;  // stages of the current segment
     int sb = 0;  // running stage count: stage t of the current segment lives in LDS buffer (sb + t) % STAGES
-    auto stage_ptr = [&](int t) { return smem + ((sb + t) % STAGES) * F::STAGE_ELEMS; };
-    // LDS byte address of this wave's first 1 KB block of stage buffer 0 (A part and B part):
-    // scalar, so each load only adds the buffer offset and moves it to m0
-    const uint32_t lds_a = lds_u32(smem) + (wave * F::A_INST) * 1024;
-    const uint32_t lds_b = lds_u32(smem) + F::A_ELEMS * 2 + (wave * F::B_INST) * 1024;
+    auto stage_ptr = [&](int t) __attribute__((always_inline)) { return smem + ((sb + t) % STAGES) * F::STAGE_ELEMS; };
+    // LDS byte addresses of the A and B parts of stage buffer 0 (scalar)
+    const uint32_t lds_a0 = lds_u32(smem);
+    const uint32_t lds_b0 = lds_a0 + F::A_ELEMS * 2;
     // loads of segment stage t (K stage kbase + t) into its LDS buffer.  The stage's 16-byte
     // chunk of each lane is k0 + kc*8 with kc = swz_chunk(row, pc); only the stage that runs past
     // K (uniform test) recomputes kc to load zeros for k >= K.
-    auto issue_at = [&](int t, int kbase) {
+    // (forced inline: the loads take scalar operands, which an outlined call would not keep)
+    auto issue_at = [&](int t, int kbase) __attribute__((always_inline)) {
+        if (!issuer) return;
         const int k0 = (kbase + t) * BK;
         const uint32_t sbuf = static_cast<uint32_t>((sb + t) % STAGES) * (F::STAGE_ELEMS * 2);
+        // B instruction q of block j: its 8 rows lie on one side of the gate/up boundary
+        auto b_base = [&](int bw, int q) __attribute__((always_inline)) {
+            const int row0 = (bw * F::B_INST + q) * F::ROWS_PER_INST;
+            return uniform_ptr((GATE_UP && row0 >= BP / 2) ? b_base1 : b_base0);
+        };
         if (k0 + BK <= K) {
 #pragma unroll
-            for (int q = 0; q < F::A_INST; ++q) dma16(a_src[q] + k0, lds_a + sbuf + q * 1024);
+            for (int j = 0; j < NBLK; ++j) {
+                const int bw = block_wave(j);
 #pragma unroll
-            for (int q = 0; q < F::B_INST; ++q) dma16(b_src[q] + k0, lds_b + sbuf + q * 1024);
+                for (int q = 0; q < F::A_INST; ++q) {
+                    const uint32_t dst = lds_a0 + sbuf + (bw * F::A_INST + q) * 1024;
+                    if constexpr (ASYM) dma16_s(A + k0, a_o[j][q], dst);
+                    else dma16(a_o[j][q] + k0, dst);
+                }
+#pragma unroll
+                for (int q = 0; q < F::B_INST; ++q) {
+                    const uint32_t dst = lds_b0 + sbuf + (bw * F::B_INST + q) * 1024;
+                    if constexpr (ASYM) dma16_s(b_base(bw, q) + k0, b_o[j][q], dst);
+                    else dma16(b_o[j][q] + k0, dst);
+                }
+            }
         } else {
             // the stage that runs past K: chunks at k >= K load zeros
 #pragma unroll
-            for (int q = 0; q < F::A_INST; ++q) {
-                const int row = (wave * F::A_INST + q) * F::ROWS_PER_INST + lrow;
-                const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
-                const void* g = in ? static_cast<const void*>(a_src[q] + k0) : static_cast<const void*>(kZero16);
-                dma16(g, lds_a + sbuf + q * 1024);
-            }
+            for (int j = 0; j < NBLK; ++j) {
+                const int bw = block_wave(j);
 #pragma unroll
-            for (int q = 0; q < F::B_INST; ++q) {
-                const int row = (wave * F::B_INST + q) * F::ROWS_PER_INST + lrow;
-                const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
-                const void* g = in ? static_cast<const void*>(b_src[q] + k0) : static_cast<const void*>(kZero16);
-                dma16(g, lds_b + sbuf + q * 1024);
+                for (int q = 0; q < F::A_INST; ++q) {
+                    const uint32_t dst = lds_a0 + sbuf + (bw * F::A_INST + q) * 1024;
+                    const int row = (bw * F::A_INST + q) * F::ROWS_PER_INST + lrow;
+                    const void* src;
+                    if constexpr (ASYM) src = reinterpret_cast<const char*>(A + k0) + a_o[j][q];
+                    else src = a_o[j][q] + k0;
+                    const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+                    dma16(in ? src : static_cast<const void*>(kZero16), dst);
+                }
+#pragma unroll
+                for (int q = 0; q < F::B_INST; ++q) {
+                    const uint32_t dst = lds_b0 + sbuf + (bw * F::B_INST + q) * 1024;
+                    const int row = (bw * F::B_INST + q) * F::ROWS_PER_INST + lrow;
+                    const void* src;
+                    if constexpr (ASYM) src = reinterpret_cast<const char*>(b_base(bw, q) + k0) + b_o[j][q];
+                    else src = b_o[j][q] + k0;
+                    const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+                    dma16(in ? src : static_cast<const void*>(kZero16), dst);
+                }
             }
         }
     };
-    auto issue = [&](int t) { issue_at(t, kb); };
+    auto issue = [&](int t) __attribute__((always_inline)) { issue_at(t, kb); };
 
     const int wm = wave >> 1, wn = wave & 1;  // wave grid WAVES_M x 2
     // 32x32x16 MFMA blocks: each wave holds FI x 4 blocks of 32x32 fp32 accumulators
@@ -347,7 +416,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     constexpr int KK = BK / 16;  // 32x32x16 MFMA k-steps per stage (even)
     bf16x8 fa[2][F::FI], fb[2][4];
     // fragments of k-step kk of stage s into register set `set` (the first NF A fragments)
-    auto read = [&](auto nf_c, int s, int kk, int set) {
+    auto read = [&](auto nf_c, int s, int kk, int set) __attribute__((always_inline)) {
         constexpr int NF = decltype(nf_c)::value;
         if constexpr (NF > 0) {
             const uint16_t* st = stage_ptr(s);
@@ -358,7 +427,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + cx);
         }
     };
-    auto mfma = [&](auto nf_c, int set) {
+    auto mfma = [&](auto nf_c, int set) __attribute__((always_inline)) {
         constexpr int NF = decltype(nf_c)::value;
 #pragma unroll
         for (int i = 0; i < NF; ++i)
@@ -369,7 +438,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // Stage t becomes readable: this thread's loads of t have landed (at most `ahead` later stages
     // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
     // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
-    auto ready = [&](int t) {
+    auto ready = [&](int t) __attribute__((always_inline)) {
         const int ahead = min(STAGES - 2, nseg - 1 - t);
         if constexpr (STAGES >= 4) {
             if (ahead >= 2) wait_vmcnt<2 * F::LOADS>();
@@ -388,7 +457,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // Each k-step's MFMAs are issued after the next k-step's fragment reads (and, at a stage
     // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
     // NF = A fragments of this wave that hold tokens; every wave still loads and meets the barriers.
-    auto main_loop = [&](auto nf_c) {
+    auto main_loop = [&](auto nf_c) __attribute__((always_inline)) {
         ready(0);
         read(nf_c, 0, 0, 0);
         for (int s = 0; s < nseg; ++s) {
