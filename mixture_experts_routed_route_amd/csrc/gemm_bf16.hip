@@ -64,6 +64,9 @@ constexpr int BP = 256;
 #ifndef MOE_GEMM_BIG_BK
 #define MOE_GEMM_BIG_BK 64       // k per LDS stage of the 256-row tiles
 #endif
+#ifndef MOE_GEMM_BIG_ROWS
+#define MOE_GEMM_BIG_ROWS 128  // 256-row tiles when experts average at least this many rows
+#endif
 #ifndef MOE_GEMM_ASYM
 #define MOE_GEMM_ASYM 1  // 8 waves, 2 stages: waves 0-3 issue all of a stage's loads
 #endif
@@ -688,8 +691,9 @@ int64_t gemm_bf16_workspace_bytes() { return kSkWorkspaceBytes; }
 hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
                             int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
-    // 256-row tiles when experts hold enough rows on average, 128-row tiles otherwise
-    const bool big = static_cast<long long>(P) >= 384LL * E;
+    // 256-row tiles (8 waves) when experts average at least MOE_GEMM_BIG_ROWS rows, where a 128-row
+    // tiling would read most weight panels twice; 128-row tiles (4 waves) for fewer rows
+    const bool big = static_cast<long long>(P) >= static_cast<long long>(MOE_GEMM_BIG_ROWS) * E;
     if (gate_up) {
         if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
         return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);

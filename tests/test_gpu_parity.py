@@ -195,8 +195,9 @@ def test_grouped_gemms_small(dev, name):
 # every XCD's share of them fits s times in its 32 workgroups and K holds s pieces of >= 8
 # stages of 64.  Ragged K and N tails throughout.
 SPLIT_K = {
-    # 128-row tiles: gate/up 299 tiles (43 in the tail, 5 pieces), down 276 (20, 3 pieces)
-    "rows128": MoeConfig("sk_128", T=1024, H=2824, I=1544, E=16, top_k=2, block_size=64, seed=31),
+    # 128-row tiles (85 rows per expert): gate/up 312 tiles (56 in the tail, 4 pieces), down 288
+    # (32, 3 pieces)
+    "rows128": MoeConfig("sk_128", T=1024, H=2824, I=1544, E=24, top_k=2, block_size=64, seed=31),
     # 256-row tiles: gate/up 272 tiles (16, 5 pieces); down 192 tiles, less than a round and
     # too many to split: whole tiles
     "rows256": MoeConfig("sk_256", T=1536, H=2824, I=2120, E=8, top_k=2, block_size=64, seed=33),
