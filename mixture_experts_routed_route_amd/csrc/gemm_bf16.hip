@@ -67,6 +67,9 @@ constexpr int BP = 256;
 #ifndef MOE_GEMM_BIG_ROWS
 #define MOE_GEMM_BIG_ROWS 128  // 256-row tiles when experts average at least this many rows
 #endif
+#ifndef MOE_GEMM_A_LATE
+#define MOE_GEMM_A_LATE 1  // asymmetric issue: activation-row loads of a stage issued at this k-step
+#endif
 #ifndef MOE_GEMM_ASYM
 #define MOE_GEMM_ASYM 1  // 8 waves, 2 stages: waves 0-3 issue all of a stage's loads
 #endif
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // chunk of each lane is k0 + kc*8 with kc = swz_chunk(row, pc); only the stage that runs past
     // K (uniform test) recomputes kc to load zeros for k >= K.
     // (forced inline: the loads take scalar operands, which an outlined call would not keep)
-    auto issue_at = [&](int t, int kbase) __attribute__((always_inline)) {
+    auto issue_at = [&](int t, int kbase, int parts = 3) __attribute__((always_inline)) {  // 1: A rows, 2: B rows
         if (!issuer) return;
         const int k0 = (kbase + t) * BK;
         const uint32_t sbuf = static_cast<uint32_t>((sb + t) % STAGES) * (F::STAGE_ELEMS * 2);
@@ -356,12 +359,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 const int bw = block_wave(j);
 #pragma unroll
                 for (int q = 0; q < F::A_INST; ++q) {
+                    if (!(parts & 1)) break;
                     const uint32_t dst = lds_a0 + sbuf + (bw * F::A_INST + q) * 1024;
                     if constexpr (ASYM) dma16_s(A + k0, a_o[j][q], dst);
                     else dma16(a_o[j][q] + k0, dst);
                 }
 #pragma unroll
                 for (int q = 0; q < F::B_INST; ++q) {
+                    if (!(parts & 2)) break;
                     const uint32_t dst = lds_b0 + sbuf + (bw * F::B_INST + q) * 1024;
                     if constexpr (ASYM) dma16_s(b_base(bw, q) + k0, b_o[j][q], dst);
                     else dma16(b_o[j][q] + k0, dst);
@@ -374,6 +379,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 const int bw = block_wave(j);
 #pragma unroll
                 for (int q = 0; q < F::A_INST; ++q) {
+                    if (!(parts & 1)) break;
                     const uint32_t dst = lds_a0 + sbuf + (bw * F::A_INST + q) * 1024;
                     const int row = (bw * F::A_INST + q) * F::ROWS_PER_INST + lrow;
                     const void* src;
@@ -384,6 +390,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 }
 #pragma unroll
                 for (int q = 0; q < F::B_INST; ++q) {
+                    if (!(parts & 2)) break;
                     const uint32_t dst = lds_b0 + sbuf + (bw * F::B_INST + q) * 1024;
                     const int row = (bw * F::B_INST + q) * F::ROWS_PER_INST + lrow;
                     const void* src;
@@ -395,7 +402,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             }
         }
     };
-    auto issue = [&](int t) __attribute__((always_inline)) { issue_at(t, kb); };
+    // With the asymmetric issue and MOE_GEMM_A_LATE > 0, a stage's weight-panel loads (the long
+    // ones, from HBM) go out right after the barrier and its activation-row loads (mostly L2
+    // hits) at k-step MOE_GEMM_A_LATE, which halves the burst of loads landing in LDS meanwhile.
+    constexpr bool A_LATE = ASYM && MOE_GEMM_A_LATE > 0 && MOE_GEMM_A_LATE < BK / 16;
+    auto issue = [&](int t) __attribute__((always_inline)) { issue_at(t, kb, A_LATE ? 2 : 3); };
 
     const int wm = wave >> 1, wn = wave & 1;  // wave grid WAVES_M x 2
     // 32x32x16 MFMA blocks: each wave holds FI x 4 blocks of 32x32 fp32 accumulators
@@ -466,6 +477,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         for (int s = 0; s < nseg; ++s) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
+                if (A_LATE && kk == MOE_GEMM_A_LATE && s + 1 < nseg) issue_at(s + 1, kb, 1);
                 if (kk + 1 < KK) {
                     read(nf_c, s, kk + 1, (kk + 1) & 1);
                 } else if (s + 1 < nseg) {
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // already in flight (issued by the previous segment before its epilogue) and issue stages
     // 1..STAGES-2.
     for (int t = 0; t < STAGES - 1; ++t)
-        if (t < nseg) issue(t);
+        if (t < nseg) issue_at(t, kb);
 
     while (true) {
         // rows up to the last token of this tile (an expert's sentinels follow its tokens): a wave
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         kb = kb2; ke = ke2; nseg = ke - kb;
         buf ^= 1;
         for (int t = 1; t < STAGES - 1; ++t)
-            if (t < nseg) issue(t);
+            if (t < nseg) issue_at(t, kb);
     }
 }
 
