@@ -37,7 +37,7 @@ __all__ = [
     "route", "max_padded", "align", "check_group_arrays",
     "gptq_unpack_q", "gptq_unpack_z", "gptq_dequant_expert",
     "out_dim", "expert_matrix", "grouped_gate_up", "grouped_down",
-    "pack_expert_tables", "lora_windows", "lora_window_tiles", "lora_fold",
+    "pack_expert_tables", "lora_windows", "lora_window_tiles", "lora_fold", "lora_gather_fold",
     "combine", "moe_layer", "moe_tokens",
 ]
 
@@ -415,6 +415,49 @@ def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], t
             y[r] = round_bf16(y[r] + np.float64(np.float32(s_tab[e])) * delta)
         else:
             y[r] = y[r] + np.float64(np.float32(s_tab[e])) * delta
+    return y
+
+
+def lora_gather_fold(y: np.ndarray, x: np.ndarray, tables, indices: np.ndarray, top_k: int,
+                     x_gather: bool = False, row_adapter: Optional[np.ndarray] = None,
+                     row_map: Optional[np.ndarray] = None) -> np.ndarray:
+    """Slot-major LoRA fold of decode: atlas ``moe_lora_grouped.rs``, ``moe_lora_gather_bgmv``.
+
+    There is no sorting: flat (token, slot) row s < n_slots = len(indices)
+    takes its expert from ``indices[s]`` and its adapter decision from
+    ``row_adapter[s // top_k]`` (``gather_row_token``; < 0 skips, None folds
+    every row).  The x row is the slot itself for the down fold and the owning
+    token s // top_k with ``x_gather`` (the gate/up fold over token-major x).
+    The arithmetic is that of the grouped fold (module doc):
+
+        xa    = bf16(A_e  x[x row])
+        delta = bf16(B_e  xa)
+        y[s]  = bf16(y[s] + scale_e * delta)
+
+    Readings where the page is silent: an expert id outside [0, table length)
+    or with a null table entry leaves the row as it is (as in the grouped
+    fold).  ``row_map`` (not on the page) lets the same fold run on buffers in
+    another row order: slot s then reads and writes row ``row_map[s]`` of y
+    (and of x without ``x_gather``), and a negative entry skips the slot; None
+    is the page's slot-major layout.  Returns a new array.
+    """
+    a_tab, b_tab, s_tab, n_tab = tables
+    y = np.array(y, dtype=np.float64, copy=True)
+    ids = np.asarray(indices).reshape(-1)
+    for s in range(len(ids)):
+        e = int(ids[s])
+        if e < 0 or e >= n_tab or a_tab[e] is None or b_tab[e] is None:
+            continue
+        if row_adapter is not None and row_adapter[s // top_k] < 0:
+            continue
+        row = s if row_map is None else int(row_map[s])
+        if row < 0:
+            continue
+        xrow = s // top_k if x_gather else row
+        A, B = bf16_bits_to_f64(a_tab[e]), bf16_bits_to_f64(b_tab[e])
+        xa = round_bf16(A @ x[xrow])
+        delta = round_bf16(B @ xa)
+        y[row] = round_bf16(y[row] + np.float64(np.float32(s_tab[e])) * delta)
     return y
 
 

@@ -160,15 +160,57 @@ def fold_no_delta_round(y, x, tables, al, top_k, row_adapter=None, row_offset=0,
         om.round_bf16 = real
 
 
+def gather_x_row_is_slot(y, x, tables, indices, top_k, x_gather=False, row_adapter=None, row_map=None):
+    # the gate/up form reads x row s (clamped into x) instead of the owning token s // top_k
+    if not x_gather:
+        return om._orig_gather(y, x, tables, indices, top_k, False, row_adapter, row_map)
+    n = len(np.ravel(indices))
+    xx = np.stack([x[min(s, len(x) - 1)] for s in range(n)])
+    return om._orig_gather(y, xx, tables, indices, top_k, False, row_adapter, row_map)
+
+
+def gather_adapter_by_slot(y, x, tables, indices, top_k, x_gather=False, row_adapter=None, row_map=None):
+    # the adapter map indexed by slot (clamped into the map) instead of by token
+    if row_adapter is None:
+        return om._orig_gather(y, x, tables, indices, top_k, x_gather, None, row_map)
+    n = len(np.ravel(indices))
+    ra = np.asarray(row_adapter)[np.minimum(np.arange(n), len(row_adapter) - 1)]
+    if not x_gather:
+        return om._orig_gather(y, x, tables, indices, 1, False, ra, row_map)
+    xx = np.stack([x[s // top_k] for s in range(n)])
+    return om._orig_gather(y, xx, tables, indices, 1, False, ra, row_map)
+
+
+def gather_ignores_row_map(y, x, tables, indices, top_k, x_gather=False, row_adapter=None, row_map=None):
+    return om._orig_gather(y, x, tables, indices, top_k, x_gather, row_adapter, None)
+
+
+def gather_no_delta_round(y, x, tables, indices, top_k, x_gather=False, row_adapter=None, row_map=None):
+    real = om.round_bf16
+    calls = {"n": 0}
+
+    def rb(v):
+        calls["n"] += 1
+        return v if calls["n"] % 3 == 2 else real(v)
+    om.round_bf16 = rb
+    try:
+        return om._orig_gather(y, x, tables, indices, top_k, x_gather, row_adapter, row_map)
+    finally:
+        om.round_bf16 = real
+
+
 om._orig_route = om.route
 om._orig_align = om.align
 om._orig_gate_up = om.grouped_gate_up
 om._orig_combine = om.combine
 om._orig_fold = om.lora_fold
+om._orig_gather = om.lora_gather_fold
 
 ROUTE_PINS = [pins.test_route_worked_examples, pins.test_route_special_cases, pins.test_route_brute_force_ids_and_sum]
 ALIGN_PINS = [pins.test_align_worked_examples, lambda: pins.test_align_invariants_random(8, 2, 16, 64)]
 LAYER_PINS = [lambda: pins.test_layer_matches_dense_brute_force(8, 2, 16), pins.test_single_expert_is_textbook_swiglu]
+GATHER_PINS = [pins.test_lora_gather_fold_rounding_pins, pins.test_lora_gather_fold_identity_closed_forms,
+               pins.test_lora_gather_fold_on_sorted_rows_equals_grouped_fold]
 INT4_PINS = [pins.test_gptq_unpack_and_dequant, pins.test_layer_int4_matches_dense_brute_force]
 
 MUTANTS = [
@@ -187,6 +229,10 @@ MUTANTS = [
     ("round_bf16", round_bf16_ties_away, [pins.test_round_bf16_against_torch, pins.test_round_bf16_hand_values]),
     ("lora_fold", fold_no_xa_round, [pins.test_lora_fold_rounding_pins]),
     ("lora_fold", fold_no_delta_round, [pins.test_lora_fold_rounding_pins]),
+    ("lora_gather_fold", gather_x_row_is_slot, GATHER_PINS),
+    ("lora_gather_fold", gather_adapter_by_slot, GATHER_PINS),
+    ("lora_gather_fold", gather_ignores_row_map, GATHER_PINS),
+    ("lora_gather_fold", gather_no_delta_round, GATHER_PINS),
 ]
 
 

@@ -341,6 +341,77 @@ def test_lora_fold_identities_and_windows():
     assert np.array_equal(skip, base)
 
 
+def _gather_case(c, x_gather):
+    """One closed-form fold case through the slot-major gather fold (one slot, expert 0)."""
+    x = np.asarray(c["x"])[None, :]
+    tabs = oracle.pack_expert_tables([(0, bf16(np.asarray(c["A"])), bf16(np.asarray(c["B"])), c["scale"])])
+    return oracle.lora_gather_fold(np.asarray(c["base"])[None, :], x, tabs, np.array([0]), 1,
+                                   x_gather=x_gather)[0]
+
+
+def test_lora_gather_fold_rounding_pins():
+    for c in golden("lora_fold_pins.json")["cases"]:
+        for xg in (False, True):
+            assert np.array_equal(_gather_case(c, xg), np.asarray(c["folded_bf16"])), (c["name"], xg)
+
+
+def test_lora_gather_fold_identity_closed_forms():
+    """A_e = B_e = I and scale_e = 2^-(e+1) on a zero base: slot s ends up holding exactly
+    scale_e * x[x row], which names the expert, the x row and the output row it used."""
+    T, k, R, E = 5, 3, 8, 6
+    n = T * k
+    eye = bf16(np.eye(R))
+    tabs = oracle.pack_expert_tables([(e, eye, eye, 2.0 ** -(e + 1)) for e in range(0, E, 2)])  # odd: unadapted
+    assert tabs[3] == E - 1
+    rng = np.random.default_rng(7)
+    xs = oracle.round_bf16(rng.standard_normal((n, R)))        # bf16 values: the fold is exact
+    ids = rng.integers(0, E, n)
+    ids[[1, 4]] = [-1, E + 3]                                   # outside the table: skipped
+    zero = np.zeros((n, R))
+
+    def expect(xrow_of, rows=None, skip_tok=()):
+        want = np.zeros((n, R))
+        for s in range(n):
+            e = ids[s]
+            if e < 0 or e >= E - 1 or e % 2 or s // k in skip_tok:
+                continue
+            r = s if rows is None else rows[s]
+            if r < 0:
+                continue
+            want[r] = 2.0 ** -(e + 1) * xs[xrow_of(s, r)]
+        return want
+
+    down = oracle.lora_gather_fold(zero, xs, tabs, ids, k)
+    assert np.array_equal(down, expect(lambda s, r: r))
+    gate_up = oracle.lora_gather_fold(zero, xs[:T], tabs, ids, k, x_gather=True)
+    assert np.array_equal(gate_up, expect(lambda s, r: s // k))
+    adapter = np.array([0, -1, 3, -2, 0], np.int32)
+    skipped = oracle.lora_gather_fold(zero, xs, tabs, ids, k, row_adapter=adapter)
+    assert np.array_equal(skipped, expect(lambda s, r: r, skip_tok=(1, 3)))
+    perm = rng.permutation(n).astype(np.int32)
+    perm[[2, 9]] = -1
+    mapped = oracle.lora_gather_fold(zero, xs, tabs, ids, k, row_map=perm)
+    assert np.array_equal(mapped, expect(lambda s, r: r, rows=perm))
+
+
+def test_lora_gather_fold_on_sorted_rows_equals_grouped_fold():
+    """Through the inverse map, the slot-major fold on the sorted buffers is the grouped fold."""
+    cfg = CONFIGS["lora_prefill"].with_(T=40, H=64, I=96, E=6, top_k=3, block_size=16,
+                                        lora_rank=4, lora_max_rank=8)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    al = r["align"]
+    xs = oracle.round_bf16(np.nan_to_num(r["h"]))
+    base = oracle.round_bf16(np.nan_to_num(r["y"]))
+    tabs = oracle.moe_oracle._lora_tables(d)
+    ids = np.asarray(r["ids"]).reshape(-1)
+    adapter = np.where(np.arange(cfg.T) % 5 == 2, -1, 0).astype(np.int32)
+    grouped = oracle.lora_fold(base, xs, tabs, al, cfg.top_k, row_adapter=adapter)
+    gathered = oracle.lora_gather_fold(base, xs, tabs, ids, cfg.top_k, row_adapter=adapter, row_map=al["inv"])
+    assert np.array_equal(gathered, grouped)
+    assert np.any(grouped != base)
+
+
 def test_pack_expert_tables_and_windows():
     assert oracle.pack_expert_tables([]) is None
     a, b, s, n = oracle.pack_expert_tables([(2, "A2", "B2", 0.5), (0, "A0", "B0", 1.5), (2, "A2b", "B2b", 0.25)])
