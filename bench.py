@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time steps replayed from HIP graphs (one captured step per weight copy); the "
                          "per-kernel figures then come from an eager pass of the same steps")
+    ap.add_argument("--fold", default="auto", choices=["auto", "grouped", "gather"],
+                    help="LoRA fold over the sorted rows or slot by slot (auto: by the padding share)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -150,7 +152,7 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] generating {cfg.name} inputs")
     d = make_inputs(cfg)
-    layer = m.MoeLayer.from_arrays(d, dev)
+    layer = m.MoeLayer.from_arrays(d, dev, fold=args.fold)
     b = layer.plan(cfg.T, dev)
     wbytes = sum(expert_weight_bytes(cfg, op) for op in ("gate_up", "down")) * cfg.E
     rot = args.rotate or max(1, min(4, int(-(-(1 << 30) // wbytes))))
@@ -170,9 +172,9 @@ def main():
         m.moe_grouped_gemm(m.MOE_OP_DOWN, b.hs, layer.down, None, b.routing, out=b.ys, workspace=b.ws)
         if ev is not None:
             ev[2].record()
-        if layer.lora is not None:
-            for s, e in m.lora_windows(b.routing.max_pad, b.xa.shape[0]):
-                m.moe_lora_fold(b.hs, b.ys, layer.lora, b.routing, None, b.xa, s, e)
+        layer.lora_fold(b)
+        if ev is not None:
+            ev[3].record()
         layer.combine(b)
 
     log(f"[bench] warmup {args.warmup}")
@@ -180,7 +182,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     if args.graph:
         # the path allocates nothing and issues no memset, so a step captures as it runs eagerly
         cap = torch.cuda.Stream()
@@ -216,6 +218,7 @@ def main():
     ms = dt * 1e3 / args.steps
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if layer.lora is not None else None
     tokens_s = cfg.T / (ms / 1e3)
     active = int((b.routing.counts > 0).sum().item())
     gu_bytes = gemm_bytes(cfg, "gate_up", active)
@@ -223,7 +226,8 @@ def main():
     dn_tflops = gemm_flops(cfg, "down") / (dn_ms / 1e3) / 1e12
     gemm_tflops = (gemm_flops(cfg, "gate_up") + gemm_flops(cfg, "down")) / ((gu_ms + dn_ms) / 1e3) / 1e12
     log(f"[bench] step {ms:.3f} ms; gate/up {gu_ms:.3f} ms ({gu_tflops:.1f} TFLOP/s); "
-        f"down {dn_ms:.3f} ms ({dn_tflops:.1f} TFLOP/s); grouped GEMMs {gemm_tflops:.1f} TFLOP/s")
+        f"down {dn_ms:.3f} ms ({dn_tflops:.1f} TFLOP/s); grouped GEMMs {gemm_tflops:.1f} TFLOP/s"
+        + (f"; LoRA fold ({layer.fold_mode(b)}) {1e3 * fold_ms:.1f} us" if fold_ms is not None else ""))
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
@@ -268,10 +272,12 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
                    "weights": cfg.weights, "lora_rank": cfg.lora_rank,
+                   **({"lora_fold": layer.fold_mode(b)} if layer.lora is not None else {}),
                    "launch": "hip_graph" if args.graph else "eager"},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
-        "kernels_ms": {"gate_up": gu_ms, "down": dn_ms},
+        "kernels_ms": {"gate_up": gu_ms, "down": dn_ms,
+                       **({"lora_fold": fold_ms} if fold_ms is not None else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -10,6 +10,7 @@
  *   moe_grouped_gemm  grouped gate/up GEMM with fused SiLU(gate)*up, and the
  *                     grouped down GEMM (bf16 or GPTQ-int4 expert weights)
  *   moe_lora_fold     optional per-expert down-projection LoRA fold, in place
+ *   moe_lora_gather_fold  the same fold on slot-major rows (decode, no sorting)
  *   moe_combine       top-k weighted sum of the expert outputs per token
  *
  * Sources (cited by page and item; the pages are Rust host code of four
@@ -222,6 +223,40 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                          const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
                          int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
                          int64_t row_offset, int64_t row_end, int64_t max_pad, moe_stream stream);
+
+/* Decode form of the LoRA fold, slot-major, in place (atlas moe_lora_grouped.rs,
+ * moe_lora_gather_bgmv, gather_row_token).  No sorted layout: flat (token, slot)
+ * row s < n_slots (= tokens * top_k) takes its expert e = indices[s] and its
+ * adapter decision from row_adapter[s / top_k] (< 0 skips; NULL folds every row).
+ *   x           bf16 [x_rows, k_in]     x_gather == 0: row = the slot's row (the
+ *                                       post-SiLU activations of the down fold);
+ *                                       x_gather == 1: row s / top_k (token-major
+ *                                       input of the gate/up fold)
+ *   base        bf16 [base_rows, n_out] folded in place at the slot's row
+ *   indices     i32  [n_slots]          expert per slot (the router's topk_ids)
+ *   row_map     i32  [n_slots] or NULL  the slot's row of base (and of x when
+ *                                       x_gather == 0); NULL = s (slot-major, as on
+ *                                       the page); a negative entry skips the slot.
+ *                                       With moe_align's inv_sorted it folds buffers
+ *                                       in sorted order.
+ *   a_table, b_table, scale_table, n_tab: as for moe_lora_fold
+ *   xa          bf16 [n_slots, max_rank] scratch, indexed by s
+ * For each slot whose expert is adapted (e in [0, n_tab), non-zero table
+ * entries): xa = bf16(x[x row] A_e^T); delta = bf16(xa B_e^T);
+ * base[row] = bf16(base[row] + scale_e*delta), fp32 sums.  Other rows are not
+ * touched.  One workgroup per (slot, output chunk): the grid depends on n_slots
+ * only.  Device values that the host cannot check get defined behaviour: an id
+ * outside the tables, a map entry outside [0, base_rows) or an x row outside
+ * [0, x_rows) skips the slot.  Two slots mapped to the same row race (the
+ * caller keeps the map injective; inv_sorted is).  n_slots % top_k == 0;
+ * x_rows >= n_slots / top_k (x_gather == 1) or >= n_slots (x_gather == 0, no
+ * row_map); base_rows >= n_slots without a row_map; max_rank in {32, 64, 96,
+ * 128}; k_in % 8 == 0; n_out % 8 == 0; n_tab <= 65536. */
+moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
+                                const int32_t* indices, int64_t n_slots, int32_t top_k, int32_t x_gather,
+                                const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_table,
+                                const uint64_t* b_table, const float* scale_table, int32_t n_tab, int32_t k_in,
+                                int32_t n_out, int32_t max_rank, uint16_t* xa, moe_stream stream);
 
 /* A6 — top-k weighted combine (ferrum moe.rs, moe_combine / weighted_sum_batched).
  *   ys         bf16 [ys_rows, hidden]

@@ -346,6 +346,44 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                                                static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
+                                const int32_t* indices, int64_t n_slots, int32_t top_k, int32_t x_gather,
+                                const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_table,
+                                const uint64_t* b_table, const float* scale_table, int32_t n_tab, int32_t k_in,
+                                int32_t n_out, int32_t max_rank, uint16_t* xa, moe_stream stream) {
+    const char* who = "moe_lora_gather_fold";
+    REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
+    REQUIRE(n_slots >= 0 && n_slots < INT32_MAX && n_slots % top_k == 0,
+            "%s: n_slots %lld must be in [0, 2^31) and a multiple of top_k=%d", who,
+            static_cast<long long>(n_slots), top_k);
+    REQUIRE(x_gather == 0 || x_gather == 1, "%s: x_gather %d not 0 or 1", who, x_gather);
+    REQUIRE(n_tab >= 0 && n_tab <= 65536, "%s: n_tab %d not in [0, 65536]", who, n_tab);
+    REQUIRE(k_in >= 8 && k_in % 8 == 0, "%s: k_in %d must be a positive multiple of 8", who, k_in);
+    REQUIRE(n_out >= 8 && n_out % 8 == 0, "%s: n_out %d must be a positive multiple of 8", who, n_out);
+    REQUIRE(max_rank >= 32 && max_rank <= 128 && max_rank % 32 == 0, "%s: max_rank %d not in {32,64,96,128}", who,
+            max_rank);
+    REQUIRE(x_rows >= 0 && base_rows >= 0, "%s: negative row count", who);
+    const int64_t need_x = x_gather ? n_slots / top_k : (row_map ? 0 : n_slots);
+    REQUIRE(x_rows >= need_x, "%s: x has %lld rows, needs %lld", who, static_cast<long long>(x_rows),
+            static_cast<long long>(need_x));
+    REQUIRE(row_map || base_rows >= n_slots, "%s: base has %lld rows < n_slots %lld (no row_map)", who,
+            static_cast<long long>(base_rows), static_cast<long long>(n_slots));
+    if (n_slots == 0 || n_tab == 0) return ok();
+    REQUIRE_PTR(who, x);
+    REQUIRE_PTR(who, base);
+    REQUIRE_PTR(who, indices);
+    REQUIRE_PTR(who, a_table);
+    REQUIRE_PTR(who, b_table);
+    REQUIRE_PTR(who, scale_table);
+    REQUIRE_PTR(who, xa);
+    if (row_map) REQUIRE_PTR(who, row_map);
+    if (row_adapter) REQUIRE_PTR(who, row_adapter);
+    return launched(who, moe::launch_lora_gather_fold(x, x_rows, base, base_rows, indices, n_slots, top_k, x_gather,
+                                                      row_map, row_adapter, a_table, b_table, scale_table, n_tab,
+                                                      k_in, n_out, max_rank, xa,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_combine(const uint16_t* ys, const int32_t* inv_sorted, const float* topk_w, uint16_t* out,
                        int32_t num_tokens, int32_t top_k, int32_t hidden, int64_t ys_rows, moe_stream stream) {
     const char* who = "moe_combine";

@@ -44,5 +44,11 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
                             const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
                             hipStream_t s);
+// slot-major gather fold (decode form): one workgroup per (slot, chunk)
+hipError_t launch_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
+                                   const int32_t* indices, int64_t n_slots, int top_k, int x_gather,
+                                   const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_tab,
+                                   const uint64_t* b_tab, const float* s_tab, int n_tab, int k_in, int n_out,
+                                   int max_rank, uint16_t* xa, hipStream_t s);
 
 }  // namespace moe

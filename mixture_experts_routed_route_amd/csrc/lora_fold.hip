@@ -213,6 +213,163 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
     }
 }
 
+// ------------------------------------------------------------------ slot-major gather fold
+// The decode form of the fold (atlas moe_lora_grouped.rs, moe_lora_gather_bgmv): no sorted
+// layout; flat (token, slot) row s takes its expert from indices[s] and its adapter decision
+// from row_adapter[s / top_k].  One workgroup per (slot, output chunk), so the grid is fixed by
+// the slot count alone.  With one row per expert visit these are matrix-vector products, so
+// they run on the vector ALU with coalesced 16-byte loads rather than on MFMA.
+
+struct GatherRow {
+    int e;          // expert (table index)
+    int64_t row;    // row of base (and of x for the down form)
+    int64_t xrow;   // row of x
+};
+
+// Is slot s folded, and where?  Ids, map entries and rows are device data: anything outside
+// the tables or the buffers skips the slot.
+__device__ __forceinline__ bool gather_row(int64_t s, const int32_t* indices, const int32_t* row_map,
+                                           const int32_t* row_adapter, int top_k, int x_gather, int n_tab,
+                                           const uint64_t* a_tab, const uint64_t* b_tab, int64_t x_rows,
+                                           int64_t base_rows, GatherRow& g) {
+    const int e = indices[s];
+    if (e < 0 || e >= n_tab || a_tab[e] == 0 || b_tab[e] == 0) return false;
+    if (row_adapter && row_adapter[s / top_k] < 0) return false;
+    const int64_t row = row_map ? static_cast<int64_t>(row_map[s]) : s;
+    if (row < 0 || row >= base_rows) return false;
+    const int64_t xrow = x_gather ? s / top_k : row;
+    if (xrow >= x_rows) return false;
+    g = GatherRow{e, row, xrow};
+    return true;
+}
+
+// acc + sum of the 8 products of two rows of 8 bf16, in index order, fp32 fma
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+        acc = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Shrink: xa[s, j] = bf16(x[x row] . A_e[j]) for 16 rank rows per workgroup, its 4 waves taking
+// every fourth 128-wide k chunk (so a slot's loads are spread over 4 * max_rank/16 waves and are
+// in flight together).  Lanes 16g..16g+15 read one chunk of row 4p+g, 4 rows per load; each row's
+// partial sum is reduced over its 16 lanes, then the 4 waves' partials are added in LDS in wave
+// order.
+__global__ __launch_bounds__(NT) void gather_shrink_kernel(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ indices,
+                                                           const int32_t* __restrict__ row_map,
+                                                           const int32_t* __restrict__ row_adapter,
+                                                           const uint64_t* a_tab, const uint64_t* b_tab, int n_tab,
+                                                           int top_k, int x_gather, int64_t x_rows,
+                                                           int64_t base_rows, int k_in, int max_rank,
+                                                           uint16_t* __restrict__ xa) {
+    __shared__ float red[4][16];
+    const int64_t s = blockIdx.x;
+    GatherRow gr;
+    if (!gather_row(s, indices, row_map, row_adapter, top_k, x_gather, n_tab, a_tab, b_tab, x_rows, base_rows, gr))
+        return;  // uniform over the workgroup
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int j0 = blockIdx.y * 16;  // < max_rank: the grid has max_rank / 16 rows of workgroups
+    const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[gr.e]) + static_cast<int64_t>(j0 + g) * k_in;
+    const uint16_t* xr = x + gr.xrow * k_in;
+    constexpr int U = 3;  // chunks per wave in flight together
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = wave * 128; q0 < k_in; q0 += 4 * 128 * U) {
+        u32x4 xv[U], av[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = q0 + u * 4 * 128 + c * 8;
+            const bool in = k < k_in;
+            xv[u] = in ? load16(xr + k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                av[u][p] = in ? load16(Ae + static_cast<int64_t>(4 * p) * k_in + k) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) acc[p] = dot8_bf16(xv[u], av[u][p], acc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) acc[p] += __shfl_xor(acc[p], o, 16);
+    }
+    if (c == 0) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) red[wave][4 * p + g] = acc[p];
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int j = threadIdx.x;
+        xa[s * max_rank + j0 + j] = f32_to_bf16((red[0][j] + red[1][j]) + (red[2][j] + red[3][j]));
+    }
+}
+
+// Expand + fold: base[row, n] = bf16(base + scale_e * bf16(xa[s] . B_e[n])) for 256 outputs per
+// workgroup, 64 per wave.  Lanes 8g..8g+7 read one 128-byte run of ranks of row n (8 rows per
+// load); after the sums over those 8 lanes, lane 8g+c holds output n0 + 8c + g, and one
+// cross-lane move gives lane L output n0 + L for a contiguous update of the base row.
+__global__ __launch_bounds__(NT) void gather_expand_kernel(const uint16_t* __restrict__ xa,
+                                                           const int32_t* __restrict__ indices,
+                                                           const int32_t* __restrict__ row_map,
+                                                           const int32_t* __restrict__ row_adapter,
+                                                           const uint64_t* a_tab, const uint64_t* b_tab,
+                                                           const float* __restrict__ s_tab, int n_tab, int top_k,
+                                                           int x_gather, int64_t x_rows, int64_t base_rows,
+                                                           int n_out, int max_rank, uint16_t* __restrict__ base) {
+    const int64_t s = blockIdx.x;
+    GatherRow gr;
+    if (!gather_row(s, indices, row_map, row_adapter, top_k, x_gather, n_tab, a_tab, b_tab, x_rows, base_rows, gr))
+        return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 3, c = lane & 7;
+    const int n0 = blockIdx.y * 256 + wave * 64;
+    if (n0 >= n_out) return;
+    const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[gr.e]);
+    const float scale = s_tab[gr.e];
+    uint16_t* brow = base + gr.row * n_out;
+    const int n_mine = n0 + lane;
+    const uint16_t b_old = n_mine < n_out ? brow[n_mine] : uint16_t(0);
+    // ranks c*8 + 64*i of this lane (max_rank <= 128)
+    u32x4 xv[2];
+    bool rin[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        rin[i] = c * 8 + 64 * i < max_rank;
+        xv[i] = rin[i] ? load16(xa + s * max_rank + c * 8 + 64 * i) : u32x4{0, 0, 0, 0};
+    }
+    u32x4 bv[8][2];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int n = n0 + 8 * p + g;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            bv[p][i] = (rin[i] && n < n_out) ? load16(Be + static_cast<int64_t>(n) * max_rank + c * 8 + 64 * i)
+                                             : u32x4{0, 0, 0, 0};
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        float a = dot8_bf16(xv[0], bv[p][0], 0.f);
+        a = dot8_bf16(xv[1], bv[p][1], a);
+#pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) a += __shfl_xor(a, o, 8);
+        if (c == p) mine = a;
+    }
+    const float v = __shfl(mine, (lane & 7) * 8 + (lane >> 3));
+    if (n_mine < n_out) {
+        const float delta = bf16_to_f32(f32_to_bf16(v));
+        brow[n_mine] = f32_to_bf16(fmaf(scale, delta, bf16_to_f32(b_old)));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_tab, const uint64_t* b_tab,
@@ -245,6 +402,23 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     lora_expand_fold_kernel<<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_out, max_rank, offsets, E,
                                                sorted_ids, P, top_k, row_adapter, base, row_offset, row_end,
                                                base16);
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
+                                   const int32_t* indices, int64_t n_slots, int top_k, int x_gather,
+                                   const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_tab,
+                                   const uint64_t* b_tab, const float* s_tab, int n_tab, int k_in, int n_out,
+                                   int max_rank, uint16_t* xa, hipStream_t s) {
+    if (n_slots <= 0 || n_tab <= 0) return hipSuccess;
+    const dim3 sgrid(static_cast<unsigned>(n_slots), static_cast<unsigned>(max_rank / 16));
+    gather_shrink_kernel<<<sgrid, NT, 0, s>>>(x, indices, row_map, row_adapter, a_tab, b_tab, n_tab, top_k, x_gather,
+                                              x_rows, base_rows, k_in, max_rank, xa);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 egrid(static_cast<unsigned>(n_slots), static_cast<unsigned>((n_out + 255) / 256));
+    gather_expand_kernel<<<egrid, NT, 0, s>>>(xa, indices, row_map, row_adapter, a_tab, b_tab, s_tab, n_tab, top_k,
+                                              x_gather, x_rows, base_rows, n_out, max_rank, base);
     return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_W_BF16, MOE_W_INT4_GPTQ
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Routing", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -270,6 +270,29 @@ def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routi
         routing.num_experts, _dev(routing.sorted_ids, torch.int32, "sorted_ids"), routing.num_pairs, routing.top_k,
         _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
         _dev(xa, torch.bfloat16, "xa"), xa.shape[0], row_offset, row_end, routing.max_pad, _stream(x)))
+    return base
+
+
+def moe_lora_gather_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, indices: torch.Tensor,
+                         top_k: int, x_gather: bool = False, row_map: Optional[torch.Tensor] = None,
+                         row_adapter: Optional[torch.Tensor] = None,
+                         xa: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Slot-major fold in place into ``base``: slot s = flat (token, slot) row of ``indices``."""
+    n_slots = indices.numel()
+    if xa is None:
+        xa = torch.empty((max(n_slots, 1), tables.max_rank), dtype=torch.bfloat16, device=x.device)
+    if xa.shape[0] < n_slots or xa.shape[1] != tables.max_rank:
+        raise ValueError(f"xa must be [>= {n_slots}, {tables.max_rank}] (got {tuple(xa.shape)})")
+    if x.shape[1] != tables.k_in or base.shape[1] != tables.n_out:
+        raise ValueError("x / base widths do not match the LoRA tables")
+    check(lib().moe_lora_gather_fold(
+        _dev(x, torch.bfloat16, "x"), x.shape[0], _dev(base, torch.bfloat16, "base"), base.shape[0],
+        _dev(indices, torch.int32, "indices"), n_slots, top_k, int(bool(x_gather)),
+        _dev(row_map, torch.int32, "row_map") if row_map is not None else None,
+        _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
+        _dev(tables.a_table, torch.int64, "a_table"), _dev(tables.b_table, torch.int64, "b_table"),
+        _dev(tables.scale_table, torch.float32, "scale_table"), tables.n_tab, tables.k_in, tables.n_out,
+        tables.max_rank, _dev(xa, torch.bfloat16, "xa"), _stream(x)))
     return base
 
 

@@ -24,7 +24,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     from mixture_experts_routed_route_amd import _lib
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
@@ -133,6 +133,24 @@ def test_argument_validation_rejects_before_launch(L):
     rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 65, 1408, 4096, 64, fake, 64, fake, 12288, 6,
                   None, fake, 16320, 0, 16320, 16320, None)
     assert rc == -1 and "n_tab" in msg
+    # gather fold: (x, x_rows, base, base_rows, indices, n_slots, top_k, x_gather, row_map, row_adapter,
+    #              a_table, b_table, scale_table, n_tab, k_in, n_out, max_rank, xa, stream)
+    g = lambda **kw: _rc(L, "moe_lora_gather_fold", *[kw.get(k, v) for k, v in (
+        ("x", fake), ("x_rows", 96), ("base", fake), ("base_rows", 96), ("indices", fake), ("n_slots", 96),
+        ("top_k", 6), ("x_gather", 0), ("row_map", None), ("row_adapter", None), ("a", fake), ("b", fake),
+        ("s", fake), ("n_tab", 63), ("k_in", 1408), ("n_out", 2048), ("max_rank", 64), ("xa", fake),
+        ("stream", None))])
+    assert g(x_gather=2)[0] == -1 and "x_gather" in g(x_gather=2)[1]
+    assert g(n_slots=95)[0] == -1 and "n_slots" in g(n_slots=95)[1]
+    assert g(max_rank=48)[0] == -1 and "max_rank" in g(max_rank=48)[1]
+    assert g(n_out=100)[0] == -1 and "n_out" in g(n_out=100)[1]
+    assert g(base_rows=95)[0] == -1 and "base" in g(base_rows=95)[1]
+    assert g(x_rows=95)[0] == -1 and "x has 95 rows" in g(x_rows=95)[1]
+    assert g(x_gather=1, x_rows=15)[0] == -1                       # token-major x needs 16 rows
+    assert g(indices=None)[0] == -1 and "indices" in g(indices=None)[1]
+    assert g(row_map=P((1 << 20) + 4))[0] == -1 and "aligned" in g(row_map=P((1 << 20) + 4))[1]
+    assert g(n_slots=0, x=None, base=None, indices=None)[0] == 0   # no slots: nothing to do
+    assert g(n_tab=0, x=None)[0] == 0                               # no adapted expert: nothing to do
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 100, 8, None)
     assert rc == -1 and "hidden" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 128, 7, None)

@@ -50,6 +50,7 @@ SMALL = {
     "lora_small": MoeConfig("lora_small", T=200, H=512, I=256, E=16, top_k=6, block_size=64, lora_rank=16,
                             lora_max_rank=64, seed=5),
     "decode_int4": CONFIGS["decode_int4"],
+    "decode_lora": CONFIGS["decode_lora"],
     "int4_prefill_small": MoeConfig("int4_prefill_small", T=100, H=512, I=256, E=8, top_k=2, block_size=32,
                                     weights="int4_gptq", group_size=128, seed=6),
     "int4_g64_small": MoeConfig("int4_g64_small", T=40, H=384, I=192, E=6, top_k=3, block_size=16,
@@ -359,6 +360,134 @@ def test_lora_fold_row_adapter(dev):
     assert np.array_equal(gb[skipped], base[skipped])
 
 
+# ----------------------------------------------------------------------------- A5 gather fold (decode form)
+# (name, tokens, top_k, experts, k_in, n_out, max_rank, real rank, x_gather, scale multiplier, adapter map)
+GATHER_CASES = [
+    ("decode_down", 16, 6, 64, 1408, 2048, 64, 16, 0, 1.0, False),
+    ("decode_gate_up", 16, 6, 64, 2048, 1408, 64, 16, 1, 1.0, False),
+    ("decode_down_x100", 16, 6, 64, 1408, 2048, 64, 16, 0, 100.0, False),
+    ("ragged_r32_adapter", 7, 3, 10, 72, 264, 32, 32, 0, 1.0, True),
+    ("ragged_r96_gather", 9, 2, 5, 200, 520, 96, 80, 1, 1.0, True),
+    ("r128_k4", 33, 4, 12, 640, 136, 128, 128, 0, 1.0, False),
+    ("one_slot", 1, 1, 1, 40, 8, 32, 8, 1, 1.0, False),
+]
+
+
+def _gather_setup(T, k, E, k_in, n_out, R, r, scale_mult, seed):
+    """Router ids (with a dropped and an out-of-table id), tables for the even experts, bf16 x and base."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = oracle.route(logits, k)
+    ids = ids.reshape(-1).copy()
+    if ids.size > 5:
+        ids[1], ids[4] = -1, E + 2
+    adapted = list(range(0, E, 2))
+    a_l, b_l, s_l = [], [], []
+    for _ in adapted:
+        a = np.zeros((R, k_in), np.uint16)
+        a[:r] = f32_to_bf16_bits((rng.standard_normal((r, k_in)) * 0.01).astype(np.float32))
+        b = np.zeros((n_out, R), np.uint16)
+        b[:, :r] = f32_to_bf16_bits((rng.standard_normal((n_out, r)) * 0.01).astype(np.float32))
+        a_l.append(a), b_l.append(b), s_l.append(float(np.float32(rng.uniform(0.5, 2.0) * scale_mult)))
+    return rng, ids.astype(np.int32), adapted, a_l, b_l, s_l
+
+
+def _gather_dev_tables(adapted, a_l, b_l, s_l):
+    m = ops()
+    return m.pack_lora_tables(adapted, [bf16_dev(a) for a in a_l], [bf16_dev(b) for b in b_l], s_l, "cuda")
+
+
+def _gather_check(got_bits, ref, scaled_delta, base_bits, rows, what):
+    """At least 99.9% of the folded values bit-exact; every one within 3 bf16 ulps of the largest
+    of |base|, |result| and |scale * delta|.  The kernel sums in fp32 in another order than the
+    oracle, so an xa or delta value next to a rounding boundary may round the other way: a delta
+    one ulp off moves scale * delta by under 2 ulps of itself, and the result rounds once more.
+    Where base and scale * delta cancel, this is many ulps of the small result."""
+    g = oracle.bf16_bits_to_f64(got_bits[rows])
+    r = ref[rows]
+    m = np.maximum(np.maximum(np.abs(oracle.bf16_bits_to_f64(base_bits[rows])), np.abs(r)),
+                   np.abs(scaled_delta[rows]))
+    _, ex = np.frexp(m)
+    ulp_m = np.ldexp(1.0, np.maximum(ex - 8, -133))
+    worst = (np.abs(g - r) / ulp_m).max()
+    exact = (g == r).mean()
+    note(f"{what}: exact {exact:.5f}, max |diff| {worst:.2f} ulp of the largest term")
+    assert worst <= 3 and exact >= 0.999, what
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_lora_gather_fold_slot_major(dev, case):
+    m = ops()
+    name, T, k, E, k_in, n_out, R, r, xg, smult, use_ra = case
+    note(f"gather fold {name}")
+    rng, ids, adapted, a_l, b_l, s_l = _gather_setup(T, k, E, k_in, n_out, R, r, smult, seed=31 + len(name))
+    n = T * k
+    x = f32_to_bf16_bits(rng.standard_normal((T if xg else n, k_in)).astype(np.float32))
+    base = f32_to_bf16_bits((rng.standard_normal((n, n_out)) * 0.05).astype(np.float32))
+    ra = np.where(np.arange(T) % 3 == 1, -1, 0).astype(np.int32) if use_ra else None
+    tabs = oracle.pack_expert_tables([(e, a, b, sc) for e, a, b, sc in zip(adapted, a_l, b_l, s_l)])
+    ref = oracle.lora_gather_fold(oracle.bf16_bits_to_f64(base), oracle.bf16_bits_to_f64(x), tabs, ids, k,
+                                  x_gather=bool(xg), row_adapter=ra)
+    sd = oracle.lora_gather_fold(np.zeros(base.shape), oracle.bf16_bits_to_f64(x), tabs, ids, k,
+                                 x_gather=bool(xg), row_adapter=ra)
+    got = bf16_dev(base)
+    m.moe_lora_gather_fold(bf16_dev(x), got, _gather_dev_tables(adapted, a_l, b_l, s_l), to_dev(ids), k,
+                           x_gather=bool(xg), row_adapter=to_dev(ra) if ra is not None else None)
+    gb = bits_host(got)
+    folded = np.array([0 <= e < tabs[3] and e % 2 == 0 and (ra is None or ra[s // k] >= 0)
+                       for s, e in enumerate(ids)])
+    assert folded.any()
+    assert np.array_equal(gb[~folded], base[~folded]), "a skipped slot changed"
+    _gather_check(gb, ref, sd, base, np.flatnonzero(folded), name)
+
+
+def test_lora_gather_fold_row_map_on_sorted_buffers(dev):
+    """Through the inverse map the gather fold updates the sorted buffers of the grouped path:
+    padding rows and the rows of dropped pairs stay untouched."""
+    m = ops()
+    T, k, E, k_in, n_out, R, r = 24, 6, 16, 256, 512, 64, 16
+    rng, ids, adapted, a_l, b_l, s_l = _gather_setup(T, k, E, k_in, n_out, R, r, 1.0, seed=77)
+    al = oracle.align(ids, E, 16)
+    rows = len(al["sorted_ids"])
+    x = np.full((rows, k_in), CANARY, np.uint16)
+    base = np.full((rows, n_out), CANARY, np.uint16)
+    real = np.flatnonzero(al["sorted_ids"] < ids.size)
+    x[real] = f32_to_bf16_bits(rng.standard_normal((real.size, k_in)).astype(np.float32))
+    base[real] = f32_to_bf16_bits((rng.standard_normal((real.size, n_out)) * 0.05).astype(np.float32))
+    tabs = oracle.pack_expert_tables([(e, a, b, sc) for e, a, b, sc in zip(adapted, a_l, b_l, s_l)])
+    ref = oracle.lora_gather_fold(oracle.bf16_bits_to_f64(base), oracle.bf16_bits_to_f64(x), tabs, ids, k,
+                                  row_map=al["inv"])
+    sd = oracle.lora_gather_fold(np.zeros(base.shape), oracle.bf16_bits_to_f64(x), tabs, ids, k,
+                                 row_map=al["inv"])
+    got = bf16_dev(base)
+    m.moe_lora_gather_fold(bf16_dev(x), got, _gather_dev_tables(adapted, a_l, b_l, s_l), to_dev(ids), k,
+                           row_map=to_dev(al["inv"]))
+    gb = bits_host(got)
+    mapped = np.array([int(al["inv"][s]) for s, e in enumerate(ids) if 0 <= e < tabs[3] and e % 2 == 0])
+    untouched = np.setdiff1d(np.arange(rows), mapped)
+    assert np.array_equal(gb[untouched], base[untouched])
+    _gather_check(gb, ref, sd, base, mapped, "row_map")
+    # the grouped fold on the same buffers gives the oracle's result too
+    import torch
+    routing = m.Routing.allocate(ids.size, k, E, 16, "cuda")
+    m.moe_align(to_dev(ids.reshape(T, k)), E, 16, out=routing)
+    grouped = bf16_dev(base)
+    m.moe_lora_fold(bf16_dev(x), grouped, _gather_dev_tables(adapted, a_l, b_l, s_l), routing)
+    _gather_check(bits_host(grouped), ref, sd, base, mapped, "grouped fold, same rows")
+
+
+def test_lora_gather_fold_no_slots(dev):
+    import torch
+    m = ops()
+    rng, ids, adapted, a_l, b_l, s_l = _gather_setup(2, 2, 4, 64, 64, 32, 8, 1.0, seed=3)
+    base = bf16_dev(f32_to_bf16_bits(np.ones((4, 64), np.float32)))
+    m.moe_lora_gather_fold(bf16_dev(np.zeros((4, 64), np.uint16)), base,
+                           _gather_dev_tables(adapted, a_l, b_l, s_l), torch.empty(0, dtype=torch.int32,
+                                                                                   device="cuda"), 2)
+    torch.cuda.synchronize()
+    assert (bits_host(base) == f32_to_bf16_bits(np.float32(1.0))).all()
+
+
 # ----------------------------------------------------------------------------- whole layer
 def _layer_run(cfg, d):
     m = ops()
@@ -399,6 +528,43 @@ def test_layer_full_size_sampled(dev, name):
     got = bf16_host(out)[toks]
     e1, e2 = assert_close_rows(got, ref, TOL, f"layer full {name}")
     note(f"  worst row rel err {e1:.2e}, tensor {e2:.2e}")
+
+
+@pytest.mark.parametrize("name,fold", [("lora_small", "grouped"), ("lora_small", "gather"),
+                                       ("decode_lora", "grouped"), ("decode_lora", "gather")])
+def test_layer_lora_fold_modes(dev, name, fold):
+    """Both folds inside the layer: the folded Ys rows against the oracle fold of the GPU's own
+    Hs and unfolded Ys (a missing fold is below the end-to-end tolerance), then the output."""
+    import torch
+    m = ops()
+    cfg = SMALL[name]
+    note(f"layer fold {name} {fold}")
+    d = make_inputs(cfg)
+    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold)
+    b = layer.plan(cfg.T, "cuda")
+    assert layer.fold_mode(b) == fold
+    layer.route_align(to_dev(d["logits"]), b)
+    lora, layer.lora = layer.lora, None
+    layer.experts(bf16_dev(d["x"]), b)          # the GEMMs only
+    layer.lora = lora
+    torch.cuda.synchronize()
+    hs, ys0 = bits_host(b.hs), bits_host(b.ys)
+    layer.lora_fold(b)
+    out = layer.combine(b)
+    ref = oracle.moe_layer(d)
+    al = ref["align"]
+    real = _real(al, cfg.P)
+    tabs = oracle.moe_oracle._lora_tables(d)
+    hs_f = np.where(np.isin(np.arange(hs.shape[0]), real)[:, None], oracle.bf16_bits_to_f64(hs), 0.0)
+    ys0_f = oracle.bf16_bits_to_f64(ys0)
+    want = oracle.lora_fold(ys0_f, hs_f, tabs, al, cfg.top_k)
+    sd = oracle.lora_fold(np.zeros(ys0.shape), hs_f, tabs, al, cfg.top_k)
+    adapted_rows = np.array([rr for rr in real
+                             if (np.searchsorted(al["offsets"], rr, side="right") - 1) % 2 == 0])
+    _gather_check(bits_host(b.ys), want, sd, ys0, adapted_rows, f"layer fold {name} {fold}")
+    others = np.setdiff1d(real, adapted_rows)
+    assert np.array_equal(bits_host(b.ys)[others], ys0[others])
+    assert_close_rows(bf16_host(out), ref["out"], TOL, f"layer {name} {fold}")
 
 
 def test_layer_graph_replay_matches_eager(dev):
