@@ -60,6 +60,7 @@ class MoeConfig:
     zipf_beta: float = 1.05
     lora_rank: int = 0             # 0 = no LoRA fold
     lora_max_rank: int = 0
+    lora_gate_up: bool = False     # also LoRA tables for the gate and up projections
     renormalize: bool = True
     seed: int = 0
 
@@ -216,4 +217,14 @@ def make_inputs(cfg: MoeConfig, seed: Optional[int] = None, threads: int = 8) ->
         d["lora_a"] = a
         d["lora_b"] = b
         d["lora_scale"] = scale
+        if cfg.lora_gate_up:
+            # drawn after the down tables, so those stay the same with or without these
+            for proj in ("gate", "up"):
+                ga = np.zeros((n, R, H), dtype=np.uint16)
+                ga[:, :r, :] = _normal_bf16(rng, (n, r, H), 0.01)
+                gb = np.zeros((n, I, R), dtype=np.uint16)
+                gb[:, :, :r] = _normal_bf16(rng, (n, I, r), 0.01)
+                d[f"lora_{proj}_a"] = ga
+                d[f"lora_{proj}_b"] = gb
+                d[f"lora_{proj}_scale"] = rng.uniform(0.5, 2.0, size=n).astype(np.float32)
     return d

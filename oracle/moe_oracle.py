@@ -36,7 +36,7 @@ __all__ = [
     "bf16_bits_to_f64", "f16_bits_to_f64", "round_bf16", "round_f32", "silu",
     "route", "max_padded", "align", "check_group_arrays",
     "gptq_unpack_q", "gptq_unpack_z", "gptq_dequant_expert",
-    "out_dim", "expert_matrix", "grouped_gate_up", "grouped_down",
+    "out_dim", "expert_matrix", "grouped_gate_up", "grouped_gate_up_lora", "grouped_down",
     "pack_expert_tables", "lora_windows", "lora_window_tiles", "lora_fold", "lora_gather_fold",
     "combine", "moe_layer", "moe_tokens",
 ]
@@ -311,6 +311,33 @@ def grouped_gate_up(x_bits: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray],
     return h
 
 
+def grouped_gate_up_lora(x_bits: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray], top_k: int,
+                         tabs_gate, tabs_up) -> np.ndarray:
+    """Gate/up with LoRA folded into each projection before SiLU: atlas ``moe_lora_grouped.rs``,
+    ``moe_lora_grouped_down`` with ``x_gather`` = 1 (token-major input, base = the sorted BF16
+    ``expert_gate_out`` / ``expert_up_out``), then ``moe_lora_gather_bgmv``'s ``moe_silu_mul``
+    into a BF16 buffer.
+
+    For every real sorted row: g = bf16(Wg[e] x[t]), u = bf16(Wu[e] x[t]); each is folded
+    with its own tables (a projection without tables is left as it is); h = bf16(silu(g) * u).
+    Unlike the fused path, gate and up are rounded to bf16 before SiLU, as the page's path
+    materialises them.  Sentinel rows are NaN.
+    """
+    sid = al["sorted_ids"]
+    X = bf16_bits_to_f64(x_bits)
+    g = np.full((len(sid), out_dim(w_gate)), np.nan)
+    u = np.full_like(g, np.nan)
+    for e, rr in _rows_by_expert(al).items():
+        xt = X[sid[rr] // top_k]
+        g[rr] = round_bf16(xt @ expert_matrix(w_gate, e).T)
+        u[rr] = round_bf16(xt @ expert_matrix(w_up, e).T)
+    if tabs_gate is not None:
+        g = lora_fold(g, X, tabs_gate, al, top_k, x_gather=True)
+    if tabs_up is not None:
+        u = lora_fold(u, X, tabs_up, al, top_k, x_gather=True)
+    return round_bf16(silu(g) * u)
+
+
 def grouped_down(h: np.ndarray, w_down, al: Dict[str, np.ndarray],
                  rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Grouped down GEMM: y[r] = Wd[e] h[r] for every real sorted row r.
@@ -368,7 +395,7 @@ def lora_windows(total_rows: int, cap: int) -> List[Tuple[int, int]]:
 
 def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], top_k: int,
               row_adapter: Optional[np.ndarray] = None, row_offset: int = 0,
-              row_end: Optional[int] = None, bf16_base: bool = True) -> np.ndarray:
+              row_end: Optional[int] = None, bf16_base: bool = True, x_gather: bool = False) -> np.ndarray:
     """Down-projection LoRA fold over sorted rows: atlas ``moe_lora_grouped.rs``.
 
     For every sorted row r in the window [row_offset, row_end) that is real
@@ -382,7 +409,9 @@ def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], t
 
     ``x`` holds the bf16 post-SiLU sorted activations (module doc and
     ``moe_lora_grouped_down``: x = post-SiLU sorted activations, base =
-    sorted ``expert_down_out``).  With ``bf16_base`` the base rows are bf16
+    sorted ``expert_down_out``).  With ``x_gather`` (the same launcher's
+    gate/up form) ``x`` is the token-major layer input and row r reads token
+    sorted_ids[r] // top_k; the base is then a sorted gate or up output.  With ``bf16_base`` the base rows are bf16
     and the folded row is bf16(base + scale * delta); otherwise y is kept in
     fp64.  Rows outside the window, sentinel rows and unadapted rows are left
     as they are.  ``tables`` = (a_list, b_list, scale_list, n) from
@@ -409,7 +438,7 @@ def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], t
         if e not in mats:
             mats[e] = (bf16_bits_to_f64(a_tab[e]), bf16_bits_to_f64(b_tab[e]))
         A, B = mats[e]
-        xa = round_bf16(A @ x[r])
+        xa = round_bf16(A @ x[p // top_k if x_gather else r])
         delta = round_bf16(B @ xa)
         if bf16_base:
             y[r] = round_bf16(y[r] + np.float64(np.float32(s_tab[e])) * delta)
@@ -484,7 +513,13 @@ def combine(y: np.ndarray, inv: Optional[np.ndarray], topk_w: np.ndarray, T: int
 
 
 # ----------------------------------------------------------------------------- whole layer
-def _lora_tables(d) -> Optional[tuple]:
+def _lora_tables(d, proj: str = "down") -> Optional[tuple]:
+    if proj != "down":
+        if f"lora_{proj}_a" not in d:
+            return None
+        return pack_expert_tables(
+            (int(e), d[f"lora_{proj}_a"][i], d[f"lora_{proj}_b"][i], float(d[f"lora_{proj}_scale"][i]))
+            for i, e in enumerate(d["lora_ids"]))
     if "lora_ids" not in d:
         return None
     return pack_expert_tables(
@@ -504,13 +539,18 @@ def moe_layer(d: Dict[str, object], max_pad: Optional[int] = None) -> Dict[str, 
     The fold (when the inputs carry LoRA tables) runs before the combine, so
     the router weight multiplies base + delta (atlas ``moe_lora_grouped.rs``,
     ``moe_lora_gather_bgmv``), on the bf16 post-SiLU activations bf16(h).
+    With gate/up tables the gate/up step is ``grouped_gate_up_lora``.
     Intermediates stay fp64 otherwise.
     """
     cfg = d["cfg"]
     ids, w = route(d["logits"], cfg.top_k, cfg.renormalize)
     al = align(ids, cfg.E, cfg.block_size, max_pad)
     wg, wu, wd = _weights(d)
-    h = grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
+    tg, tu = _lora_tables(d, "gate"), _lora_tables(d, "up")
+    if tg is None and tu is None:
+        h = grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
+    else:
+        h = grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu)
     y = grouped_down(h, wd, al)
     tabs = _lora_tables(d)
     if tabs is not None:
@@ -532,6 +572,7 @@ def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
     ids, w = routing if routing is not None else route(d["logits"], cfg.top_k, cfg.renormalize)
     wg, wu, wd = _weights(d)
     tabs = _lora_tables(d)
+    tabs_gu = (_lora_tables(d, "gate"), _lora_tables(d, "up"))
     tokens = list(tokens)
     by_e: Dict[int, List[Tuple[int, int]]] = {}
     for i, t in enumerate(tokens):
@@ -541,7 +582,17 @@ def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
     contrib = {}
     for e, lst in sorted(by_e.items()):
         X = bf16_bits_to_f64(d["x"][[tokens[i] for i, _ in lst]])
-        h = silu(X @ expert_matrix(wg, e).T) * (X @ expert_matrix(wu, e).T)
+        if tabs_gu == (None, None):
+            h = silu(X @ expert_matrix(wg, e).T) * (X @ expert_matrix(wu, e).T)
+        else:
+            gu = []
+            for wm, tb in zip((wg, wu), tabs_gu):
+                v = round_bf16(X @ expert_matrix(wm, e).T)
+                if tb is not None and e < tb[3] and tb[0][e] is not None:
+                    xa = round_bf16(X @ bf16_bits_to_f64(tb[0][e]).T)
+                    v = round_bf16(v + np.float64(np.float32(tb[2][e])) * round_bf16(xa @ bf16_bits_to_f64(tb[1][e]).T))
+                gu.append(v)
+            h = round_bf16(silu(gu[0]) * gu[1])
         yy = h @ expert_matrix(wd, e).T
         if tabs is not None and e < tabs[3] and tabs[0][e] is not None:
             A = bf16_bits_to_f64(tabs[0][e])

@@ -199,18 +199,48 @@ def gather_no_delta_round(y, x, tables, indices, top_k, x_gather=False, row_adap
         om.round_bf16 = real
 
 
+def gate_up_lora_gate_unrounded(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up):
+    real = om.round_bf16
+    calls = {"n": 0}
+
+    def rb(v):
+        calls["n"] += 1
+        return v if calls["n"] == 1 else real(v)  # the first expert's gate values stay unrounded
+    om.round_bf16 = rb
+    try:
+        return om._orig_gate_up_lora(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up)
+    finally:
+        om.round_bf16 = real
+
+
+def gate_up_lora_tables_swapped(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up):
+    return om._orig_gate_up_lora(x_bits, w_gate, w_up, al, top_k, tabs_up, tabs_gate)
+
+
+def fold_x_gather_by_row(y, x, tables, al, top_k, row_adapter=None, row_offset=0, row_end=None, bf16_base=True,
+                         x_gather=False):
+    if not x_gather:
+        return om._orig_fold(y, x, tables, al, top_k, row_adapter, row_offset, row_end, bf16_base)
+    # reads x at the sorted row (clamped into x) instead of at the row's token
+    rows = len(al["sorted_ids"])
+    xx = np.stack([x[min(r, len(x) - 1)] for r in range(rows)])
+    return om._orig_fold(y, xx, tables, al, top_k, row_adapter, row_offset, row_end, bf16_base)
+
+
 om._orig_route = om.route
 om._orig_align = om.align
 om._orig_gate_up = om.grouped_gate_up
 om._orig_combine = om.combine
 om._orig_fold = om.lora_fold
 om._orig_gather = om.lora_gather_fold
+om._orig_gate_up_lora = om.grouped_gate_up_lora
 
 ROUTE_PINS = [pins.test_route_worked_examples, pins.test_route_special_cases, pins.test_route_brute_force_ids_and_sum]
 ALIGN_PINS = [pins.test_align_worked_examples, lambda: pins.test_align_invariants_random(8, 2, 16, 64)]
 LAYER_PINS = [lambda: pins.test_layer_matches_dense_brute_force(8, 2, 16), pins.test_single_expert_is_textbook_swiglu]
 GATHER_PINS = [pins.test_lora_gather_fold_rounding_pins, pins.test_lora_gather_fold_identity_closed_forms,
                pins.test_lora_gather_fold_on_sorted_rows_equals_grouped_fold]
+GATE_UP_LORA_PINS = [pins.test_gate_up_lora_rounding_pin, pins.test_layer_gate_up_lora_matches_dense_brute_force]
 INT4_PINS = [pins.test_gptq_unpack_and_dequant, pins.test_layer_int4_matches_dense_brute_force]
 
 MUTANTS = [
@@ -233,6 +263,9 @@ MUTANTS = [
     ("lora_gather_fold", gather_adapter_by_slot, GATHER_PINS),
     ("lora_gather_fold", gather_ignores_row_map, GATHER_PINS),
     ("lora_gather_fold", gather_no_delta_round, GATHER_PINS),
+    ("grouped_gate_up_lora", gate_up_lora_gate_unrounded, GATE_UP_LORA_PINS),
+    ("grouped_gate_up_lora", gate_up_lora_tables_swapped, GATE_UP_LORA_PINS),
+    ("lora_fold", fold_x_gather_by_row, [pins.test_lora_fold_x_gather_closed_form]),
 ]
 
 

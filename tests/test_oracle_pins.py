@@ -412,6 +412,87 @@ def test_lora_gather_fold_on_sorted_rows_equals_grouped_fold():
     assert np.any(grouped != base)
 
 
+def test_gate_up_lora_rounding_pin():
+    """Gate and up are bf16 values before SiLU on the gate/up LoRA path (closed form)."""
+    for c in golden("gate_up_lora_pins.json")["cases"]:
+        x = bf16(np.asarray(c["x"])[None, :])
+        al = oracle.align(np.array([[0]]), 1, 16)
+        g = bf16(np.asarray(c["gate"]))[None]
+        u = bf16(np.asarray(c["up"]))[None]
+        h = oracle.grouped_gate_up_lora(x, g, u, al, 1, None, None)
+        assert np.array_equal(h[0], np.asarray(c["h_bf16"])), c["name"]
+
+
+def test_lora_fold_x_gather_closed_form():
+    """Gate/up form of the grouped fold: with A = B = I, scale 2^-(e+1) and a zero base, sorted
+    row r ends up holding scale_e * x[token of r] exactly."""
+    T, k, R, E = 6, 2, 8, 4
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    al = oracle.align(ids, E, 16)
+    eye = bf16(np.eye(R))
+    tabs = oracle.pack_expert_tables([(e, eye, eye, 2.0 ** -(e + 1)) for e in (0, 2)])
+    xt = oracle.round_bf16(rng.standard_normal((T, R)))
+    rows = len(al["sorted_ids"])
+    y = oracle.lora_fold(np.zeros((rows, R)), xt, tabs, al, k, x_gather=True)
+    want = np.zeros((rows, R))
+    for r in range(rows):
+        p = al["sorted_ids"][r]
+        if p >= T * k:
+            continue
+        e = ids.reshape(-1)[p]
+        if e in (0, 2):
+            want[r] = 2.0 ** -(e + 1) * xt[p // k]
+    assert np.array_equal(y, want)
+    g = oracle.lora_gather_fold(np.zeros((rows, R)), xt, tabs, ids, k, x_gather=True, row_map=al["inv"])
+    assert np.array_equal(g, want)
+
+
+def _dense_brute_force_gate_up_lora(d, ids, w):
+    """Every token through every expert with the gate/up and down folds, no sorting."""
+    cfg = d["cfg"]
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    X = oracle.bf16_bits_to_f64(d["x"])
+    gate = np.zeros((cfg.T, cfg.E))
+    for t in range(cfg.T):
+        for j in range(cfg.top_k):
+            gate[t, ids[t, j]] += float(w[t, j])
+    rb, f64 = oracle.round_bf16, oracle.bf16_bits_to_f64
+    lids = list(d["lora_ids"])
+    out = np.zeros((cfg.T, cfg.H))
+    for e in range(cfg.E):
+        i = lids.index(e) if e in lids else None
+        proj = []
+        for wm, key in ((wg, "gate"), (wu, "up")):
+            v = rb(X @ oracle.expert_matrix(wm, e).T)
+            if i is not None:
+                xa = rb(X @ f64(d[f"lora_{key}_a"][i]).T)
+                v = rb(v + float(d[f"lora_{key}_scale"][i]) * rb(xa @ f64(d[f"lora_{key}_b"][i]).T))
+            proj.append(v)
+        h = rb(proj[0] / (1 + np.exp(-proj[0])) * proj[1])
+        y = h @ oracle.expert_matrix(wd, e).T
+        if i is not None:
+            y = y + float(d["lora_scale"][i]) * rb(rb(h @ f64(d["lora_a"][i]).T) @ f64(d["lora_b"][i]).T)
+        out += gate[:, e:e + 1] * y
+    return out
+
+
+def test_layer_gate_up_lora_matches_dense_brute_force():
+    cfg = MoeConfig("t", T=30, H=64, I=48, E=6, top_k=2, block_size=16, lora_rank=4, lora_max_rank=8,
+                    lora_gate_up=True, seed=17)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    ref = _dense_brute_force_gate_up_lora(d, r["ids"], r["w"])
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+    tok = oracle.moe_tokens(d, range(cfg.T))
+    assert np.allclose(tok, ref, rtol=1e-12, atol=1e-14)
+    # the gate/up folds change the result (they are not below the comparison)
+    plain = dict(d)
+    for key in ("lora_gate_a", "lora_up_a"):
+        plain.pop(key)
+    assert not np.allclose(oracle.moe_layer(plain)["out"], ref, rtol=1e-6, atol=1e-9)
+
+
 def test_pack_expert_tables_and_windows():
     assert oracle.pack_expert_tables([]) is None
     a, b, s, n = oracle.pack_expert_tables([(2, "A2", "B2", 0.5), (0, "A0", "B0", 1.5), (2, "A2b", "B2b", 0.25)])
