@@ -166,10 +166,10 @@ def main():
         layer.route_align(logits, b)
         if ev is not None:
             ev[0].record()
-        m.moe_grouped_gemm(m.MOE_OP_GATE_UP_SILU, x, layer.gate, layer.up, b.routing, out=b.hs, workspace=b.ws)
+        layer.gate_up_stage(x, b)
         if ev is not None:
             ev[1].record()
-        m.moe_grouped_gemm(m.MOE_OP_DOWN, b.hs, layer.down, None, b.routing, out=b.ys, workspace=b.ws)
+        layer.down_stage(b)
         if ev is not None:
             ev[2].record()
         layer.lora_fold(b)
@@ -219,6 +219,8 @@ def main():
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if layer.lora is not None else None
+    gu_what = ("gate/up stage: 2 gathered GEMMs, 2 LoRA folds, SiLU*up" if layer.gate_up_lora
+               else ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>")
     tokens_s = cfg.T / (ms / 1e3)
     active = int((b.routing.counts > 0).sum().item())
     gu_bytes = gemm_bytes(cfg, "gate_up", active)
@@ -244,7 +246,7 @@ def main():
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(cfg.name, "gate_up")
-    roof["kernel"] = ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>"
+    roof["kernel"] = gu_what
     roof["algorithmic"] = {"flops": gemm_flops(cfg, "gate_up"), "bytes": gu_bytes, "active_experts": active,
                            "flop_per_byte": ai}
     log(f"[bench] gate/up roofline: {roof['bound']} {roof['achieved']:.1f} {roof['unit']} "
@@ -273,6 +275,7 @@ def main():
                    "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
                    "weights": cfg.weights, "lora_rank": cfg.lora_rank,
                    **({"lora_fold": layer.fold_mode(b)} if layer.lora is not None else {}),
+                   **({"lora_gate_up": True} if layer.gate_up_lora else {}),
                    "launch": "hip_graph" if args.graph else "eager"},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,

@@ -7,8 +7,10 @@
  *   moe_align         per-expert histogram, block-padded expert_offsets,
  *                     sorted pair ids with sentinels, one expert id per block
  *   moe_route_align   the two above in one call (one launch for decode batches)
- *   moe_grouped_gemm  grouped gate/up GEMM with fused SiLU(gate)*up, and the
- *                     grouped down GEMM (bf16 or GPTQ-int4 expert weights)
+ *   moe_grouped_gemm  grouped gate/up GEMM with fused SiLU(gate)*up, the grouped
+ *                     down GEMM, and one gathered projection without activation
+ *                     (bf16 or GPTQ-int4 expert weights)
+ *   moe_silu_mul      SiLU(gate)*up when gate and up are folded separately
  *   moe_lora_fold     optional per-expert down-projection LoRA fold, in place
  *   moe_lora_gather_fold  the same fold on slot-major rows (decode, no sorting)
  *   moe_combine       top-k weighted sum of the expert outputs per token
@@ -165,7 +167,7 @@ typedef struct moe_weight {
     const int32_t* qzeros;
 } moe_weight;
 
-typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1 } moe_gemm_op;
+typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1, MOE_OP_GATHER = 2 } moe_gemm_op;
 
 /* A3/A4 — grouped expert GEMM over the sorted, block-padded rows (one launch
  * for all experts; metrale cutlass/grouped.rs nvfp4_grouped_gate_up_fused /
@@ -175,6 +177,12 @@ typedef enum { MOE_OP_GATE_UP_SILU = 0, MOE_OP_DOWN = 1 } moe_gemm_op;
  *                        c[r, :N] = bf16(silu(x Wg^T) * (x Wu^T))
  *   MOE_OP_DOWN:         a = Hs [max_pad, K] in sorted order; w0 = down, w1 = NULL;
  *                        c[r, :N] = bf16(Hs[r] Wd^T)
+ *   MOE_OP_GATHER:       a = x token-major as for GATE_UP_SILU; w0 = one projection,
+ *                        w1 = NULL; c[r, :N] = bf16(x[t] W^T), no activation.  The
+ *                        gate and up outputs that a gate/up LoRA fold works on (atlas
+ *                        moe_lora_grouped.rs: the fold with x_gather = 1 updates the
+ *                        sorted BF16 expert_gate_out / expert_up_out); moe_silu_mul
+ *                        then makes Hs.
  * The expert of row r is the block's expert (expert_ids / expert_offsets from
  * moe_align).  Sentinel and padding rows are neither read as tokens nor
  * written: c keeps its previous content there.  fp32 accumulation.
@@ -204,17 +212,20 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
  * depend on the problem). */
 int64_t moe_grouped_gemm_workspace_bytes(void);
 
-/* A5 — down-projection LoRA fold, in place, on one window [row_offset, row_end)
- * of the sorted rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down).
- *   x           bf16 [max_pad, k_in]   post-SiLU sorted activations (Hs)
- *   base        bf16 [max_pad, n_out]  sorted expert_down_out (Ys), folded in place
+/* A5 — LoRA fold, in place, on one window [row_offset, row_end) of the sorted
+ * rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down).
+ *   x           x_gather == 0 (down):    bf16 [max_pad, k_in], post-SiLU sorted activations (Hs)
+ *               x_gather == 1 (gate/up): bf16 [num_pairs/top_k, k_in], the token-major layer
+ *                                        input; sorted row r reads token sorted_ids[r]/top_k
+ *   base        bf16 [max_pad, n_out]  sorted expert_down_out (Ys), or a sorted gate or up
+ *                                      output (MOE_OP_GATHER) for x_gather == 1; in place
  *   a_table     u64  [n_tab] device    address of A_e, bf16 [max_rank, k_in]; 0 = unadapted
  *   b_table     u64  [n_tab] device    address of B_e, bf16 [n_out, max_rank]; 0 = unadapted
  *   scale_table f32  [n_tab] device    scale_e
  *   row_adapter i32  [num_pairs/top_k] or NULL: a token whose entry is < 0 is skipped
  *   xa          bf16 [cap, max_rank]   scratch, indexed by the local row r - row_offset
  * For each real row r of an adapted expert e < n_tab in the window:
- *   xa = bf16(x[r] A_e^T); delta = bf16(xa B_e^T); base[r] = bf16(base[r] + scale_e*delta)
+ *   xa = bf16(x[x row] A_e^T); delta = bf16(xa B_e^T); base[r] = bf16(base[r] + scale_e*delta)
  * with fp32 sums.  Other rows are not touched.  Windows may be applied one
  * after the other with the same xa scratch (stream order).  max_rank % 32 == 0,
  * k_in % 8 == 0, n_out % 8 == 0, cap >= row_end - row_offset, n_tab <= num_experts. */
@@ -222,7 +233,19 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                          const float* scale_table, int32_t n_tab, int32_t k_in, int32_t n_out, int32_t max_rank,
                          const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
                          int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
-                         int64_t row_offset, int64_t row_end, int64_t max_pad, moe_stream stream);
+                         int64_t row_offset, int64_t row_end, int64_t max_pad, int32_t x_gather,
+                         moe_stream stream);
+
+/* SiLU(gate) * up of the gate/up LoRA path (atlas moe_lora_grouped.rs,
+ * moe_lora_gather_bgmv: the caller's moe_silu_mul writes the BF16 activations
+ * the down projection and its fold read).
+ *   gate, up    bf16 [rows, n]
+ *   out         bf16 [rows, n]   out[r] = bf16(silu(gate[r]) * up[r]), fp32 arithmetic
+ *   sorted_ids  i32 [rows] or NULL: only rows with sorted_ids[r] in [0, num_pairs)
+ *               are written (the real sorted rows); NULL writes every row
+ * n % 8 == 0.  rows == 0 enqueues nothing. */
+moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out, const int32_t* sorted_ids,
+                        int64_t num_pairs, int64_t rows, int32_t n, moe_stream stream);
 
 /* Decode form of the LoRA fold, slot-major, in place (atlas moe_lora_grouped.rs,
  * moe_lora_gather_bgmv, gather_row_token).  No sorted layout: flat (token, slot)

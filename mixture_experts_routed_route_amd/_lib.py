@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 MOE_W_BF16, MOE_W_INT4_GPTQ = 0, 1
-MOE_OP_GATE_UP_SILU, MOE_OP_DOWN = 0, 1
+MOE_OP_GATE_UP_SILU, MOE_OP_DOWN, MOE_OP_GATHER = 0, 1, 2
 
 # every symbol the header declares: name -> (restype, argtypes)
 SIGNATURES = {
@@ -39,7 +39,8 @@ SIGNATURES = {
     "moe_grouped_gemm_workspace_bytes": (c_int64, []),
     "moe_lora_fold": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                 c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
-                                c_int64, c_int64, c_int64, c_int64, c_void_p]),
+                                c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p]),
+    "moe_silu_mul": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p]),
     "moe_lora_gather_fold": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                        c_int32, c_void_p, c_void_p]),

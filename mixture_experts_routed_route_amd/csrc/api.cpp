@@ -56,7 +56,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 int64_t moe_align_max_padded(int64_t num_pairs, int32_t num_experts, int32_t block_size) {
     if (num_pairs < 0 || num_experts < 1 || block_size < 1) return -1;
@@ -243,8 +243,9 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
                             int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
                             void* workspace, int64_t workspace_bytes, moe_stream stream) {
     const char* who = "moe_grouped_gemm";
-    REQUIRE(op == MOE_OP_GATE_UP_SILU || op == MOE_OP_DOWN, "%s: unknown op %d", who, op);
+    REQUIRE(op == MOE_OP_GATE_UP_SILU || op == MOE_OP_DOWN || op == MOE_OP_GATHER, "%s: unknown op %d", who, op);
     const bool gate_up = op == MOE_OP_GATE_UP_SILU;
+    const bool by_token = op != MOE_OP_DOWN;  // a is the token-major x
     REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
     REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
     REQUIRE(num_pairs % top_k == 0, "%s: num_pairs %lld is not a multiple of top_k %d", who,
@@ -260,7 +261,7 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
             static_cast<long long>(max_padded(num_pairs, num_experts, block_size)));
     REQUIRE(w0 != nullptr, "%s: w0 is NULL", who);
     if (gate_up) REQUIRE(w1 != nullptr, "%s: MOE_OP_GATE_UP_SILU needs w1 (up)", who);
-    else REQUIRE(w1 == nullptr, "%s: MOE_OP_DOWN takes no w1", who);
+    else REQUIRE(w1 == nullptr, "%s: op %d takes no w1", who, op);
     REQUIRE(w0->type == MOE_W_BF16 || w0->type == MOE_W_INT4_GPTQ, "%s: w0 has unknown type %d", who, w0->type);
     if (w1) REQUIRE(w1->type == w0->type, "%s: w0 and w1 have different types", who);
     if (workspace != nullptr) {
@@ -280,11 +281,11 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
     if (w0->type == MOE_W_BF16) {
         REQUIRE_PTR(who, expert_offsets);
         // the kernel addresses a's rows and each expert matrix with 32-bit byte offsets
-        const int64_t a_rows = gate_up ? num_pairs / top_k : max_pad;
+        const int64_t a_rows = by_token ? num_pairs / top_k : max_pad;
         if (a_rows * k * 2 > INT64_C(0xffffffff) || static_cast<int64_t>(n) * k * 2 > INT64_C(0xffffffff))
             return fail(MOE_EUNSUPPORTED, "%s: bf16 a (%lld rows) or an expert matrix (%d x %d) exceeds 4 GiB", who,
                         static_cast<long long>(a_rows), n, k);
-        return launched(who, moe::launch_gemm_bf16(gate_up, a, static_cast<const uint16_t*>(w0->data),
+        return launched(who, moe::launch_gemm_bf16(op, a, static_cast<const uint16_t*>(w0->data),
                                                    w1 ? static_cast<const uint16_t*>(w1->data) : nullptr, c,
                                                    sorted_ids, expert_offsets, P, top_k, num_experts, n, k,
                                                    static_cast<int>(max_pad), workspace, workspace_bytes, s));
@@ -302,7 +303,7 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
         REQUIRE_PTR(who, w1->qzeros);
     }
     return launched(who, moe::launch_gemm_int4(
-                             gate_up, a, static_cast<const int32_t*>(w0->data), w0->scales, w0->qzeros,
+                             op, a, static_cast<const int32_t*>(w0->data), w0->scales, w0->qzeros,
                              w1 ? static_cast<const int32_t*>(w1->data) : nullptr, w1 ? w1->scales : nullptr,
                              w1 ? w1->qzeros : nullptr, G, c, sorted_ids, expert_ids, P, top_k, num_experts, n, k,
                              block_size, static_cast<int>(max_pad), s));
@@ -312,8 +313,10 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                          const float* scale_table, int32_t n_tab, int32_t k_in, int32_t n_out, int32_t max_rank,
                          const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
                          int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
-                         int64_t row_offset, int64_t row_end, int64_t max_pad, moe_stream stream) {
+                         int64_t row_offset, int64_t row_end, int64_t max_pad, int32_t x_gather,
+                         moe_stream stream) {
     const char* who = "moe_lora_fold";
+    REQUIRE(x_gather == 0 || x_gather == 1, "%s: x_gather %d not 0 or 1", who, x_gather);
     REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
     if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
     REQUIRE(n_tab >= 0 && n_tab <= num_experts, "%s: n_tab %d not in [0, num_experts=%d]", who, n_tab,
@@ -342,8 +345,23 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
     if (row_adapter) REQUIRE_PTR(who, row_adapter);
     return launched(who, moe::launch_lora_fold(x, base, a_table, b_table, scale_table, n_tab, k_in, n_out, max_rank,
                                                expert_offsets, num_experts, sorted_ids, static_cast<int>(num_pairs),
-                                               top_k, row_adapter, xa, row_offset, row_end,
+                                               top_k, row_adapter, xa, row_offset, row_end, x_gather,
                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out, const int32_t* sorted_ids,
+                        int64_t num_pairs, int64_t rows, int32_t n, moe_stream stream) {
+    const char* who = "moe_silu_mul";
+    REQUIRE(n >= 8 && n % 8 == 0, "%s: n %d must be a positive multiple of 8", who, n);
+    REQUIRE(rows >= 0 && rows < INT32_MAX, "%s: rows %lld out of range", who, static_cast<long long>(rows));
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
+    if (rows == 0) return ok();
+    REQUIRE_PTR(who, gate);
+    REQUIRE_PTR(who, up);
+    REQUIRE_PTR(who, out);
+    if (sorted_ids) REQUIRE_PTR(who, sorted_ids);
+    return launched(who, moe::launch_silu_mul(gate, up, out, sorted_ids, static_cast<int>(num_pairs), rows, n,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                                                           const int32_t* __restrict__ offsets, int P, int top_k,
                                                           int E, int N, int K, int max_pad, int n_tiles,
                                                           float* __restrict__ sk_part, int32_t* __restrict__ sk_cnt,
-                                                          int sk_on) {
+                                                          int sk_on, int a_tok) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
     constexpr int NT = F::NT;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             int src = -1;
             if (r < r_end) {
                 const int p = sorted_ids[r];
-                if (p >= 0 && p < P) src = GATE_UP ? p / top_k : r;
+                if (p >= 0 && p < P) src = (GATE_UP || a_tok) ? p / top_k : r;
             }
             s_row[buf][i] = src;
             if (src >= 0) atomicMax(&s_h[buf], i + 1);
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 const int src = s_row[bf][row];
                 // a row without a token reads a row that is always in bounds (token 0, or the
                 // tile's first sorted row r0 < max_pad); its results are never stored
-                const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0_);
+                const int srow = src >= 0 ? src : ((GATE_UP || a_tok) ? 0 : r0_);
                 if constexpr (ASYM) a_o[j][q] = (static_cast<uint32_t>(srow) * K + kc * 8) * 2;
                 else a_o[j][q] = A + static_cast<size_t>(srow) * K + kc * 8;
             }
@@ -667,7 +667,7 @@ static_assert(kSkMaxGrid * 4 <= kSkCounterBytes, "split-tail counters overflow t
 template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
 hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                       const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
-                      int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
+                      int max_pad, void* ws, int64_t ws_bytes, int a_tok, hipStream_t s) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
     static_assert(F::NT * F::FI * 64 * 4 <= kSkPartBytes, "partial accumulators larger than their workspace slot");
     const int n_tiles = (N + F::NCOL - 1) / F::NCOL;
@@ -692,7 +692,7 @@ hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1,
     int32_t* cnt = sk ? static_cast<int32_t*>(ws) : nullptr;
     float* part = sk ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSkCounterBytes) : nullptr;
     gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW><<<static_cast<int>(grid), F::NT, 0, s>>>(
-        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0);
+        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0, a_tok);
     return hipGetLastError();
 }
 
@@ -700,18 +700,20 @@ hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1,
 
 int64_t gemm_bf16_workspace_bytes() { return kSkWorkspaceBytes; }
 
-hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
+hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
                             int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
     // 256-row tiles (8 waves) when experts average at least MOE_GEMM_BIG_ROWS rows, where a 128-row
     // tiling would read most weight panels twice; 128-row tiles (4 waves) for fewer rows
     const bool big = static_cast<long long>(P) >= static_cast<long long>(MOE_GEMM_BIG_ROWS) * E;
-    if (gate_up) {
-        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
-        return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
+    if (op == kOpGateUpSilu) {
+        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s);
+        return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s);
     }
-    if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
-    return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
+    // one projection, no activation: rows of a in sorted order (down) or by token (gather)
+    const int a_tok = op == kOpGather ? 1 : 0;
+    if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, a_tok, s);
+    return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, a_tok, s);
 }
 
 }  // namespace moe

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ qw0, const uint16_t* __restrict__ sc0,
     const int32_t* __restrict__ qz0, const int32_t* __restrict__ qw1, const uint16_t* __restrict__ sc1,
     const int32_t* __restrict__ qz1, uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ expert_ids, int P, int top_k, int E, int N, int K, int bs, int max_pad) {
+    const int32_t* __restrict__ expert_ids, int P, int top_k, int E, int N, int K, int bs, int max_pad,
+    int a_tok) {
     constexpr int NSPLIT = GATE_UP ? 2 : 4;    // waves sharing one projection's K groups
     constexpr int G = STEPS * 32;
     __shared__ int s_row[16];
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
         int src = -1;
         if (r < max_pad) {
             const int p = sorted_ids[r];
-            if (p >= 0 && p < P) src = GATE_UP ? p / top_k : r;
+            if (p >= 0 && p < P) src = (GATE_UP || a_tok) ? p / top_k : r;
         }
         s_row[tid] = src;
         if (src >= 0) atomicOr(&s_any, 1);
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     const int arow = s_row[m];
     // a row without a token reads a row that is always in bounds (token 0, or the tile's first
     // sorted row); its results are never stored
-    const int arow_ok = arow >= 0 ? arow : (GATE_UP ? 0 : r0);
+    const int arow_ok = arow >= 0 ? arow : ((GATE_UP || a_tok) ? 0 : r0);
     const int ncol = n0 + 4 * m;              // first of this lane's 4 columns
     const int zshift = 16 * (m & 1);          // nibble of column ncol inside its qzeros word
 
@@ -207,30 +208,31 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
 }
 
 template <int STEPS>
-void launch_int4_steps(bool gate_up, dim3 grid, hipStream_t s, const uint16_t* a, const int32_t* qw0,
+void launch_int4_steps(int op, dim3 grid, hipStream_t s, const uint16_t* a, const int32_t* qw0,
                        const uint16_t* sc0, const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1,
                        const int32_t* qz1, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids, int P,
                        int top_k, int E, int N, int K, int bs, int max_pad) {
-    if (gate_up)
+    if (op == kOpGateUpSilu)
         gemm_int4_kernel<true, STEPS><<<grid, NT, 0, s>>>(a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids,
-                                                          P, top_k, E, N, K, bs, max_pad);
-    else
+                                                          P, top_k, E, N, K, bs, max_pad, 1);
+    else  // one projection: rows of a in sorted order (down) or by token (gather)
         gemm_int4_kernel<false, STEPS><<<grid, NT, 0, s>>>(a, qw0, sc0, qz0, nullptr, nullptr, nullptr, c,
-                                                           sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad);
+                                                           sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad,
+                                                           op == kOpGather ? 1 : 0);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_int4(bool gate_up, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
+hipError_t launch_gemm_int4(int op, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
                             const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1, const int32_t* qz1,
                             int group_size, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             int P, int top_k, int E, int N, int K, int bs, int max_pad, hipStream_t s) {
     const dim3 grid(max_pad / 16, N / NCOL);
     switch (group_size) {
-        case 32: launch_int4_steps<1>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
-        case 64: launch_int4_steps<2>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
-        case 128: launch_int4_steps<4>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
-        case 256: launch_int4_steps<8>(gate_up, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 32: launch_int4_steps<1>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 64: launch_int4_steps<2>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 128: launch_int4_steps<4>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 256: launch_int4_steps<8>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -7,6 +7,11 @@
 
 namespace moe {
 
+// grouped GEMM ops (the values of moe_gemm_op in the C header)
+constexpr int kOpGateUpSilu = 0;  // x by token, gate and up, SiLU(gate) * up
+constexpr int kOpDown = 1;        // sorted rows, one projection
+constexpr int kOpGather = 2;      // x by token, one projection, no activation
+
 // route.hip
 hipError_t launch_route(const float* logits, int T, int E, int top_k, int renorm, int32_t* ids, float* w,
                         hipStream_t s);
@@ -28,12 +33,12 @@ hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w
 
 // gemm_bf16.hip (ws: optional split-tail workspace, zero-filled before first use; NULL = none)
 int64_t gemm_bf16_workspace_bytes();
-hipError_t launch_gemm_bf16(bool gate_up, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
+hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
                             int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s);
 
 // gemm_int4.hip
-hipError_t launch_gemm_int4(bool gate_up, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
+hipError_t launch_gemm_int4(int op, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
                             const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1, const int32_t* qz1,
                             int group_size, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             int P, int top_k, int E, int N, int K, int bs, int max_pad, hipStream_t s);
@@ -43,7 +48,10 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
                             const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
                             const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
-                            hipStream_t s);
+                            int x_gather, hipStream_t s);
+// silu_mul.hip: h[r] = bf16(silu(g[r]) * u[r]) on the real sorted rows (all rows without sorted_ids)
+hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint16_t* h, const int32_t* sorted_ids, int P,
+                           int64_t rows, int N, hipStream_t s);
 // slot-major gather fold (decode form): one workgroup per (slot, chunk)
 hipError_t launch_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
                                    const int32_t* indices, int64_t n_slots, int top_k, int x_gather,

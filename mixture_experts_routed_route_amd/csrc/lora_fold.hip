@@ -1,6 +1,8 @@
-// Down-projection LoRA fold on the sorted rows (atlas moe_lora_grouped.rs,
-// moe_lora_grouped_down): for each real row r of an adapted expert e in the window,
-//   xa    = bf16(x[r] A_e^T)                      (shrink, max_rank outputs)
+// LoRA fold on the sorted rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down): for each
+// real row r of an adapted expert e in the window,
+//   xa    = bf16(x[r] A_e^T)                      (shrink, max_rank outputs; with x_gather, the
+//                                                  gate/up form, x is the token-major input and
+//                                                  row r reads its token sorted_ids[r] / top_k)
 //   delta = bf16(xa B_e^T)                        (expand, n_out outputs)
 //   base[r] = bf16(fp32(base[r]) + scale_e * fp32(delta))   (in place)
 // Two launches like the page: the shrink writes the bf16 xa scratch at the local row
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ sorted_ids, int P, int top_k,
                                                          const int32_t* __restrict__ row_adapter,
                                                          uint16_t* __restrict__ xa, int64_t row_offset,
-                                                         int64_t row_end, int64_t base16) {
+                                                         int64_t row_end, int64_t base16, int x_gather) {
     constexpr int KU = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
     __shared__ float red[4][NB][4][64];  // [wave][rank block][v][lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -88,7 +90,9 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
     const int64_t r = sub0 + m;
     const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
     if (__ballot(act) == 0) return;  // the same rows in every wave: uniform over the workgroup
-    const uint16_t* xr = act ? x + r * k_in + kq * 8 : nullptr;
+    // x row: the sorted row (down), or the row's token in the token-major input (gate/up form)
+    const int64_t xrow = act && x_gather ? static_cast<int64_t>(sorted_ids[r] / top_k) : r;
+    const uint16_t* xr = act ? x + xrow * k_in + kq * 8 : nullptr;
     const int kpart = ((k_in + 127) / 128) * 32;  // this wave's k range, a multiple of 32
     const int kb = wave * kpart, ke = min(k_in, kb + kpart);
 
@@ -376,7 +380,7 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
                             const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
                             const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
-                            hipStream_t s) {
+                            int x_gather, hipStream_t s) {
     if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
     const int64_t base16 = (row_offset / 16) * 16;
     const int64_t tiles = (row_end - base16 + 63) / 64;
@@ -384,7 +388,7 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     const dim3 sgrid(static_cast<unsigned>(subs));
 #define MOE_SHRINK(NB_)                                                                                          \
     lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, \
-                                                 P, top_k, row_adapter, xa, row_offset, row_end, base16)
+                                                 P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
     switch (max_rank / 16) {
         case 1: MOE_SHRINK(1); break;
         case 2: MOE_SHRINK(2); break;

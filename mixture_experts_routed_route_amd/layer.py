@@ -3,7 +3,14 @@
     moe_route -> moe_align -> moe_grouped_gemm(gate/up + SiLU) -> moe_grouped_gemm(down)
               -> [LoRA fold] -> moe_combine
 
-The LoRA fold runs either over the sorted rows, window by window (``moe_lora_fold``), or
+With LoRA tables for the gate and up projections, the gate/up step is instead
+
+    moe_grouped_gemm(gather, gate) and (gather, up) -> a fold into each -> moe_silu_mul
+
+because those folds update the gate and up outputs before SiLU, which the fused kernel
+never writes.
+
+A LoRA fold runs either over the sorted rows, window by window (``moe_lora_fold``), or
 slot by slot through the inverse map (``moe_lora_gather_fold``).  The second has a grid of one
 workgroup per (token, slot) pair instead of one per 16 sorted rows of the worst-case layout,
 which is what decode batches want: there the sorted layout is mostly padding.
@@ -19,10 +26,10 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU
+from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER
 from .ops import (Bf16Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows, moe_align,
                   moe_combine, moe_grouped_gemm, moe_lora_fold, moe_lora_gather_fold, moe_route, moe_route_align,
-                  pack_lora_tables)
+                  moe_silu_mul, pack_lora_tables)
 
 FOLD_MODES = ("auto", "grouped", "gather")
 
@@ -36,21 +43,31 @@ class Buffers:
     hs: torch.Tensor
     ys: torch.Tensor
     out: torch.Tensor
-    xa: Optional[torch.Tensor]
+    xa: Optional[torch.Tensor]    # flat bf16 shrink scratch shared by the folds
     ws: torch.Tensor
+    g: Optional[torch.Tensor] = None   # gate and up outputs of the gate/up LoRA path
+    u: Optional[torch.Tensor] = None
 
 
 class MoeLayer:
     def __init__(self, num_experts: int, hidden: int, inter: int, top_k: int, block_size: int, gate, up, down,
                  lora: Optional[LoraTables] = None, renormalize: bool = True, lora_cap: Optional[int] = None,
-                 fold: str = "auto"):
+                 fold: str = "auto", lora_gate: Optional[LoraTables] = None, lora_up: Optional[LoraTables] = None):
         if fold not in FOLD_MODES:
             raise ValueError(f"fold must be one of {FOLD_MODES}")
         self.E, self.H, self.I, self.top_k, self.bs = num_experts, hidden, inter, top_k, block_size
         self.gate, self.up, self.down, self.lora = gate, up, down, lora
+        self.lora_gate, self.lora_up = lora_gate, lora_up
         self.renormalize = renormalize
         self.lora_cap = lora_cap
         self.fold = fold
+
+    @property
+    def gate_up_lora(self) -> bool:
+        return self.lora_gate is not None or self.lora_up is not None
+
+    def _tables(self):
+        return [t for t in (self.lora, self.lora_gate, self.lora_up) if t is not None]
 
     # ------------------------------------------------------------------ construction from host arrays
     @staticmethod
@@ -66,13 +83,19 @@ class MoeLayer:
                                   torch.from_numpy(w["scales"]).view(torch.float16).to(device),
                                   torch.from_numpy(w["qzeros"]).to(device), int(w["group_size"]))
             gate, up, down = gq(d["gate"]), gq(d["up"]), gq(d["down"])
-        lora = None
-        if "lora_ids" in d:
-            a = [bf(d["lora_a"][i]) for i in range(len(d["lora_ids"]))]
-            b = [bf(d["lora_b"][i]) for i in range(len(d["lora_ids"]))]
-            lora = pack_lora_tables(list(d["lora_ids"]), a, b, list(d["lora_scale"]), device)
+
+        def tables(prefix):
+            if f"{prefix}_a" not in d:
+                return None
+            n = len(d["lora_ids"])
+            return pack_lora_tables(list(d["lora_ids"]), [bf(d[f"{prefix}_a"][i]) for i in range(n)],
+                                    [bf(d[f"{prefix}_b"][i]) for i in range(n)], list(d[f"{prefix}_scale"]),
+                                    device)
+        lora = tables("lora") if "lora_ids" in d else None
+        lora_gate = tables("lora_gate") if "lora_ids" in d else None
+        lora_up = tables("lora_up") if "lora_ids" in d else None
         return MoeLayer(cfg.E, cfg.H, cfg.I, cfg.top_k, cfg.block_size, gate, up, down, lora, cfg.renormalize,
-                        lora_cap, fold)
+                        lora_cap, fold, lora_gate, lora_up)
 
     # ------------------------------------------------------------------ buffers
     def plan(self, T: int, device) -> Buffers:
@@ -80,22 +103,42 @@ class MoeLayer:
         r = Routing.allocate(P, self.top_k, self.E, self.bs, device)
         bf = dict(dtype=torch.bfloat16, device=device)
         xa = None
-        if self.lora is not None:
+        if self._tables():
             # rows: the window capacity of the grouped fold, and at least one per slot for the gather fold
             cap = max(self.lora_cap or r.max_pad, P)
-            xa = torch.empty((cap, self.lora.max_rank), **bf)
-        return Buffers(T, torch.empty((T, self.top_k), dtype=torch.int32, device=device),
-                       torch.empty((T, self.top_k), dtype=torch.float32, device=device), r,
-                       torch.empty((r.max_pad, self.I), **bf), torch.empty((r.max_pad, self.H), **bf),
-                       torch.empty((T, self.H), **bf), xa, gemm_workspace(device))
+            xa = torch.empty(cap * max(t.max_rank for t in self._tables()), **bf)
+        b = Buffers(T, torch.empty((T, self.top_k), dtype=torch.int32, device=device),
+                    torch.empty((T, self.top_k), dtype=torch.float32, device=device), r,
+                    torch.empty((r.max_pad, self.I), **bf), torch.empty((r.max_pad, self.H), **bf),
+                    torch.empty((T, self.H), **bf), xa, gemm_workspace(device))
+        if self.gate_up_lora:
+            b.g = torch.empty((r.max_pad, self.I), **bf)
+            b.u = torch.empty((r.max_pad, self.I), **bf)
+        return b
 
     # ------------------------------------------------------------------ forward
     def route_align(self, logits: torch.Tensor, b: Buffers) -> None:
         moe_route_align(logits, self.top_k, self.renormalize, self.bs, b.ids, b.w, b.routing)
 
-    def experts(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
-        moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs, workspace=b.ws)
+    def gate_up_stage(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
+        """Hs from x: the fused kernel, or gathered gate and up, their folds and SiLU * up."""
+        if not self.gate_up_lora:
+            moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs, workspace=b.ws)
+            return
+        moe_grouped_gemm(MOE_OP_GATHER, x, self.gate, None, b.routing, out=b.g, workspace=b.ws)
+        moe_grouped_gemm(MOE_OP_GATHER, x, self.up, None, b.routing, out=b.u, workspace=b.ws)
+        if self.lora_gate is not None:
+            self._fold(self.lora_gate, x, b.g, b, row_adapter, x_gather=True)
+        if self.lora_up is not None:
+            self._fold(self.lora_up, x, b.u, b, row_adapter, x_gather=True)
+        moe_silu_mul(b.g, b.u, b.hs, b.routing)
+
+    def down_stage(self, b: Buffers) -> None:
         moe_grouped_gemm(MOE_OP_DOWN, b.hs, self.down, None, b.routing, out=b.ys, workspace=b.ws)
+
+    def experts(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
+        self.gate_up_stage(x, b, row_adapter)
+        self.down_stage(b)
         self.lora_fold(b, row_adapter)
 
     def fold_mode(self, b: Buffers) -> str:
@@ -105,15 +148,24 @@ class MoeLayer:
             return self.fold
         return "gather" if 2 * b.routing.num_pairs <= b.routing.max_pad else "grouped"
 
-    def lora_fold(self, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
-        if self.lora is None:
-            return
+    def _fold(self, tables: LoraTables, x: torch.Tensor, base: torch.Tensor, b: Buffers,
+              row_adapter: Optional[torch.Tensor], x_gather: bool) -> None:
+        R = tables.max_rank
         if self.fold_mode(b) == "gather":
-            moe_lora_gather_fold(b.hs, b.ys, self.lora, b.ids, self.top_k, row_map=b.routing.inv_sorted,
-                                 row_adapter=row_adapter, xa=b.xa)
+            P = b.routing.num_pairs
+            xa = b.xa[: P * R].view(P, R)
+            moe_lora_gather_fold(x, base, tables, b.ids, self.top_k, x_gather=x_gather,
+                                 row_map=b.routing.inv_sorted, row_adapter=row_adapter, xa=xa)
             return
-        for s, e in lora_windows(b.routing.max_pad, b.xa.shape[0]):
-            moe_lora_fold(b.hs, b.ys, self.lora, b.routing, row_adapter, b.xa, s, e)
+        cap = b.xa.numel() // R
+        xa = b.xa[: cap * R].view(cap, R)
+        for s, e in lora_windows(b.routing.max_pad, cap):
+            moe_lora_fold(x, base, tables, b.routing, row_adapter, xa, s, e, x_gather=x_gather)
+
+    def lora_fold(self, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
+        """The down-projection fold into Ys (none without down tables)."""
+        if self.lora is not None:
+            self._fold(self.lora, b.hs, b.ys, b, row_adapter, x_gather=False)
 
     def combine(self, b: Buffers) -> torch.Tensor:
         return moe_combine(b.ys, b.routing.inv_sorted, b.w, out=b.out)

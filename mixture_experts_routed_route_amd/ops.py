@@ -11,11 +11,12 @@ from typing import List, Optional, Sequence, Tuple, Union
 
 import torch
 
-from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_W_BF16, MOE_W_INT4_GPTQ, MoeWeight, check, lib)
+from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, MOE_W_INT4_GPTQ, MoeWeight, check,
+                   lib)
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Routing", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -195,7 +196,8 @@ def moe_route_align(logits: torch.Tensor, top_k: int, renormalize: bool, block_s
 # ----------------------------------------------------------------------------- A3 / A4 grouped GEMM
 def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight], routing: Routing,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """op = MOE_OP_GATE_UP_SILU (a = x [T, K], w0 = gate, w1 = up) or MOE_OP_DOWN (a = Hs [max_pad, K]).
+    """op = MOE_OP_GATE_UP_SILU (a = x [T, K], w0 = gate, w1 = up), MOE_OP_DOWN (a = Hs [max_pad, K])
+    or MOE_OP_GATHER (a = x [T, K], w0 = one projection, no activation).
 
     ``workspace`` (from ``gemm_workspace``) lets bf16 launches split the last partial wave of tiles
     over K; without it every tile is computed by one workgroup."""
@@ -257,8 +259,9 @@ def pack_lora_tables(ids: Sequence[int], a: Sequence[torch.Tensor], b: Sequence[
 
 def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routing: Routing,
                   row_adapter: Optional[torch.Tensor] = None, xa: Optional[torch.Tensor] = None,
-                  row_offset: int = 0, row_end: Optional[int] = None) -> torch.Tensor:
-    """Fold in place into ``base`` over the window [row_offset, row_end) of the sorted rows."""
+                  row_offset: int = 0, row_end: Optional[int] = None, x_gather: bool = False) -> torch.Tensor:
+    """Fold in place into ``base`` over the window [row_offset, row_end) of the sorted rows.
+    ``x_gather``: x is the token-major layer input and base a sorted gate or up output."""
     if row_end is None:
         row_end = routing.max_pad
     if xa is None:
@@ -269,8 +272,22 @@ def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routi
         tables.n_tab, tables.k_in, tables.n_out, tables.max_rank, _dev(routing.offsets, torch.int32, "offsets"),
         routing.num_experts, _dev(routing.sorted_ids, torch.int32, "sorted_ids"), routing.num_pairs, routing.top_k,
         _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
-        _dev(xa, torch.bfloat16, "xa"), xa.shape[0], row_offset, row_end, routing.max_pad, _stream(x)))
+        _dev(xa, torch.bfloat16, "xa"), xa.shape[0], row_offset, row_end, routing.max_pad, int(bool(x_gather)),
+        _stream(x)))
     return base
+
+
+def moe_silu_mul(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor,
+                 routing: Optional[Routing] = None) -> torch.Tensor:
+    """out[r] = bf16(silu(gate[r]) * up[r]) on the real sorted rows of ``routing`` (every row without)."""
+    if gate.shape != up.shape or gate.shape != out.shape:
+        raise ValueError("gate, up and out must have one shape")
+    rows, n = gate.shape
+    check(lib().moe_silu_mul(_dev(gate, torch.bfloat16, "gate"), _dev(up, torch.bfloat16, "up"),
+                             _dev(out, torch.bfloat16, "out"),
+                             _dev(routing.sorted_ids, torch.int32, "sorted_ids") if routing is not None else None,
+                             routing.num_pairs if routing is not None else 0, rows, n, _stream(gate)))
+    return out
 
 
 def moe_lora_gather_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, indices: torch.Tensor,

@@ -93,6 +93,8 @@ CONFIGS: Dict[str, MoeConfig] = {
                               block_size=64, lora_rank=16, lora_max_rank=64),
     "decode_lora": MoeConfig("decode_lora", T=16, H=2048, I=1408, E=64, top_k=6, block_size=16,
                              weights="int4_gptq", group_size=128, lora_rank=16, lora_max_rank=64),
+    "lora_all_prefill": MoeConfig("lora_all_prefill", T=2048, H=4096, I=1408, E=64, top_k=6,
+                                  block_size=64, lora_rank=16, lora_max_rank=64, lora_gate_up=True),
 }
 
 

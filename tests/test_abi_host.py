@@ -24,11 +24,11 @@ def L():
 def test_exports_every_declared_symbol(L):
     from mixture_experts_routed_route_amd import _lib
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_max_padded_and_workspace(L):
@@ -125,13 +125,13 @@ def test_argument_validation_rejects_before_launch(L):
                   256, 16, 256, None, 0, None)
     assert rc == -1 and "group_size" in msg
     rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 48, fake, 64, fake, 12288, 6,
-                  None, fake, 16320, 0, 16320, 16320, None)
+                  None, fake, 16320, 0, 16320, 16320, 0, None)
     assert rc == -1 and "max_rank" in msg
     rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 64, fake, 64, fake, 12288, 6,
-                  None, fake, 100, 0, 16320, 16320, None)
+                  None, fake, 100, 0, 16320, 16320, 0, None)
     assert rc == -1 and "cap" in msg
     rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 65, 1408, 4096, 64, fake, 64, fake, 12288, 6,
-                  None, fake, 16320, 0, 16320, 16320, None)
+                  None, fake, 16320, 0, 16320, 16320, 0, None)
     assert rc == -1 and "n_tab" in msg
     # gather fold: (x, x_rows, base, base_rows, indices, n_slots, top_k, x_gather, row_map, row_adapter,
     #              a_table, b_table, scale_table, n_tab, k_in, n_out, max_rank, xa, stream)
@@ -151,6 +151,20 @@ def test_argument_validation_rejects_before_launch(L):
     assert g(row_map=P((1 << 20) + 4))[0] == -1 and "aligned" in g(row_map=P((1 << 20) + 4))[1]
     assert g(n_slots=0, x=None, base=None, indices=None)[0] == 0   # no slots: nothing to do
     assert g(n_tab=0, x=None)[0] == 0                               # no adapted expert: nothing to do
+    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 64, fake, 64, fake, 12288, 6,
+                  None, fake, 16320, 0, 16320, 16320, 2, None)
+    assert rc == -1 and "x_gather" in msg
+    rc, msg = _rc(L, "moe_silu_mul", fake, fake, fake, None, 0, 16, 100, None)
+    assert rc == -1 and "n 100" in msg
+    assert _rc(L, "moe_silu_mul", None, None, None, None, 0, 0, 64, None)[0] == 0   # no rows: nothing to do
+    rc, msg = _rc(L, "moe_silu_mul", fake, None, fake, None, 0, 16, 64, None)
+    assert rc == -1 and "up" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm", 3, fake, ctypes.byref(w), None, fake, fake, fake, fake, 128, 2, 8, 128,
+                  256, 16, 256, None, 0, None)
+    assert rc == -1 and "unknown op" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm", 2, fake, ctypes.byref(w), ctypes.byref(w), fake, fake, fake, fake, 128, 2,
+                  8, 128, 256, 16, 256, None, 0, None)
+    assert rc == -1 and "takes no w1" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 100, 8, None)
     assert rc == -1 and "hidden" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 128, 7, None)

@@ -49,6 +49,8 @@ SMALL = {
     "bs128_small": MoeConfig("bs128_small", T=129, H=256, I=256, E=4, top_k=2, block_size=128, seed=4),
     "lora_small": MoeConfig("lora_small", T=200, H=512, I=256, E=16, top_k=6, block_size=64, lora_rank=16,
                             lora_max_rank=64, seed=5),
+    "lora_all_small": MoeConfig("lora_all_small", T=200, H=512, I=256, E=16, top_k=6, block_size=64,
+                                lora_rank=16, lora_max_rank=64, lora_gate_up=True, seed=8),
     "decode_int4": CONFIGS["decode_int4"],
     "decode_lora": CONFIGS["decode_lora"],
     "int4_prefill_small": MoeConfig("int4_prefill_small", T=100, H=512, I=256, E=8, top_k=2, block_size=32,
@@ -255,6 +257,135 @@ def test_grouped_gemms_split_k_workspace(dev, shared_ws, name):
         runs.append((hs_b, ys_b))
     assert np.array_equal(runs[1][0], runs[2][0]) and np.array_equal(runs[1][1], runs[2][1])
     assert not ws[:4096].cpu().numpy().any(), "split counters not reset"
+
+
+# ----------------------------------------------------------------------------- gathered projection + SiLU*up
+GATHER_GEMM = {
+    "bf16_128rows": SMALL["mixtral_small"],                                              # 4-wave tiles
+    "bf16_256rows": MoeConfig("g256", T=1024, H=1032, I=776, E=8, top_k=2, block_size=64, seed=41),  # 8-wave
+    "int4_decode": CONFIGS["decode_int4"],
+    "int4_g64": SMALL["int4_g64_small"],
+}
+
+
+@pytest.mark.parametrize("name", list(GATHER_GEMM))
+def test_gathered_projection_and_silu_mul(dev, shared_ws, name):
+    """MOE_OP_GATHER: gate and up separately, no activation, x read by token; padding rows never
+    written.  Then moe_silu_mul of those bf16 outputs against the oracle's bf16(silu(g) * u)."""
+    m = ops()
+    cfg = GATHER_GEMM[name]
+    note(f"gathered projection {name}")
+    d = make_inputs(cfg)
+    ids, w, al, r = _routing(cfg, d)
+    layer = _weights_dev(d)
+    real = _real(al, cfg.P)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    X = oracle.bf16_bits_to_f64(d["x"])
+    outs = []
+    for wdev, whost, what in ((layer.gate, wg, "gate"), (layer.up, wu, "up")):
+        ref = np.full((r.max_pad, cfg.I), np.nan)
+        for e, rr in oracle.moe_oracle._rows_by_expert(al).items():
+            ref[rr] = X[al["sorted_ids"][rr] // cfg.top_k] @ oracle.expert_matrix(whost, e).T
+        for ws in (None, shared_ws):
+            c = _canary(r.max_pad, cfg.I)
+            m.moe_grouped_gemm(m.MOE_OP_GATHER, bf16_dev(d["x"]), wdev, None, r, out=c, workspace=ws)
+            cb = bits_host(c)
+            assert (cb[pad] == CANARY).all(), f"padding rows of {what} written"
+            assert_close_rows(bf16_host(c)[real], ref[real], TOL, f"{what} (workspace {ws is not None})")
+        outs.append(c)
+    g, u = outs
+    h = _canary(r.max_pad, cfg.I)
+    m.moe_silu_mul(g, u, h, r)
+    hb = bits_host(h)
+    assert (hb[pad] == CANARY).all(), "padding rows of Hs written"
+    gf, uf = bf16_host(g)[real], bf16_host(u)[real]
+    want = f32_to_bf16_bits(oracle.round_bf16(oracle.silu(gf) * uf).astype(np.float32))
+    ulp = bf16_ulp_diff(hb[real], want)
+    note(f"  silu_mul: exact {(ulp == 0).mean():.5f}, max ulp {ulp.max()}")
+    assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
+
+
+def test_silu_mul_every_row(dev):
+    """Without sorted ids every row is written (the slot-major layout), including large |gate|."""
+    import torch
+    m = ops()
+    rng = np.random.default_rng(9)
+    g = f32_to_bf16_bits((rng.standard_normal((37, 264)) * 6).astype(np.float32))
+    g[0, :8] = f32_to_bf16_bits(np.float32([-100, -60, -20, 0, 20, 60, 100, -0.0]))
+    u = f32_to_bf16_bits(rng.standard_normal((37, 264)).astype(np.float32))
+    out = torch.empty((37, 264), dtype=torch.bfloat16, device="cuda")
+    m.moe_silu_mul(bf16_dev(g), bf16_dev(u), out)
+    gf, uf = oracle.bf16_bits_to_f64(g), oracle.bf16_bits_to_f64(u)
+    want = f32_to_bf16_bits(oracle.round_bf16(oracle.silu(gf) * uf).astype(np.float32))
+    ulp = bf16_ulp_diff(bits_host(out), want)
+    assert ulp.max() <= 1 and (ulp == 0).mean() >= 0.999
+
+
+@pytest.mark.parametrize("scale_mult", [1.0, 100.0])
+def test_lora_fold_gate_up_form(dev, scale_mult):
+    """The grouped fold with x_gather: token-major x, base = a sorted gate output."""
+    m = ops()
+    cfg = SMALL["lora_all_small"]
+    d = make_inputs(cfg)
+    d["lora_gate_scale"] = (d["lora_gate_scale"] * scale_mult).astype(np.float32)
+    ids, w, al, r = _routing(cfg, d)
+    real = _real(al, cfg.P)
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    rng = np.random.default_rng(23)
+    base = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
+    base[real] = f32_to_bf16_bits(rng.standard_normal((real.size, cfg.I)).astype(np.float32))
+    tabs = oracle.moe_oracle._lora_tables(d, "gate")
+    X = oracle.bf16_bits_to_f64(d["x"])
+    ref = oracle.lora_fold(oracle.bf16_bits_to_f64(base), X, tabs, al, cfg.top_k, x_gather=True)
+    sd = oracle.lora_fold(np.zeros(base.shape), X, tabs, al, cfg.top_k, x_gather=True)
+    got = bf16_dev(base)
+    m.moe_lora_fold(bf16_dev(d["x"]), got, layer.lora_gate, r, x_gather=True)
+    gb = bits_host(got)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    assert (gb[pad] == CANARY).all()
+    adapted = np.array([rr for rr in real if (np.searchsorted(al["offsets"], rr, side="right") - 1) % 2 == 0])
+    _gather_check(gb, ref, sd, base, adapted, f"gate/up form x{scale_mult}")
+    others = np.setdiff1d(real, adapted)
+    assert np.array_equal(gb[others], base[others])
+
+
+@pytest.mark.parametrize("fold", ["grouped", "gather"])
+def test_layer_gate_up_lora(dev, fold):
+    """The gate/up LoRA path in the layer: Hs from the GPU's own gate and up outputs folded and
+    multiplied, stage by stage against the oracle; then the whole output."""
+    import torch
+    m = ops()
+    cfg = SMALL["lora_all_small"]
+    note(f"layer gate/up lora {fold}")
+    d = make_inputs(cfg)
+    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold)
+    b = layer.plan(cfg.T, "cuda")
+    layer.route_align(to_dev(d["logits"]), b)
+    x = bf16_dev(d["x"])
+    m.moe_grouped_gemm(m.MOE_OP_GATHER, x, layer.gate, None, b.routing, out=b.g)
+    m.moe_grouped_gemm(m.MOE_OP_GATHER, x, layer.up, None, b.routing, out=b.u)
+    torch.cuda.synchronize()
+    g0, u0 = bits_host(b.g), bits_host(b.u)
+    layer.gate_up_stage(x, b)          # the same GEMMs again, then the folds and SiLU * up
+    ref = oracle.moe_layer(d)
+    al = ref["align"]
+    real = _real(al, cfg.P)
+    X = oracle.bf16_bits_to_f64(d["x"])
+    adapted = np.array([rr for rr in real if (np.searchsorted(al["offsets"], rr, side="right") - 1) % 2 == 0])
+    for base0, got, proj in ((g0, b.g, "gate"), (u0, b.u, "up")):
+        tabs = oracle.moe_oracle._lora_tables(d, proj)
+        want = oracle.lora_fold(oracle.bf16_bits_to_f64(base0), X, tabs, al, cfg.top_k, x_gather=True)
+        sd = oracle.lora_fold(np.zeros(base0.shape), X, tabs, al, cfg.top_k, x_gather=True)
+        _gather_check(bits_host(got), want, sd, base0, adapted, f"{proj} fold ({fold})")
+    gf, uf = bf16_host(b.g)[real], bf16_host(b.u)[real]
+    want_h = f32_to_bf16_bits(oracle.round_bf16(oracle.silu(gf) * uf).astype(np.float32))
+    assert bf16_ulp_diff(bits_host(b.hs)[real], want_h).max() <= 1
+    assert_close_rows(bf16_host(b.hs)[real], ref["h"][real], TOL, "Hs against the oracle's")
+    layer.down_stage(b)
+    layer.lora_fold(b)
+    out = layer.combine(b)
+    assert_close_rows(bf16_host(out), ref["out"], TOL, f"layer gate/up lora {fold}")
 
 
 # ----------------------------------------------------------------------------- A6 combine
