@@ -32,6 +32,17 @@ constexpr int FOLD_LPR = EXP_COLS / 8;       // fold: lanes per row (8 columns e
 constexpr int FOLD_RPS = 64 / FOLD_LPR;      // fold: rows per step
 constexpr int FOLD_STEPS = 16 / FOLD_RPS;    // fold: steps over a 16-row sub-tile
 constexpr int MAX_RANK_BLOCKS = 8;  // max_rank <= 128
+#ifndef MOE_LORA_EXP_BLOCKS
+#define MOE_LORA_EXP_BLOCKS 4
+#endif
+constexpr int EXP_BLOCKS = MOE_LORA_EXP_BLOCKS;  // column blocks of EXP_COLS per expand wave
+
+// expert_offsets [E+1] (E <= 256) into LDS, so that each sub-tile's binary search over the
+// expert spans costs LDS reads instead of a chain of dependent global loads
+__device__ __forceinline__ void stage_offsets(const int32_t* off, int E, int* s_off) {
+    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = off[i];
+    __syncthreads();
+}
 
 struct SubTile {
     int e;          // expert of the 16-row sub-tile (-1: nothing to do)
@@ -79,10 +90,12 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                                                          int64_t row_end, int64_t base16, int x_gather) {
     constexpr int KU = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
     __shared__ float red[4][NB][4][64];  // [wave][rank block][v][lane]
+    __shared__ int s_off[257];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.x) * 16;
-    if (sub0 >= row_end) return;
-    const SubTile st = sub_tile_expert(static_cast<int>(sub0), off, E, n_tab, a_tab, b_tab);
+    if (sub0 >= row_end) return;  // uniform over the workgroup
+    stage_offsets(off, E, s_off);
+    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab, a_tab, b_tab);
     if (st.e < 0) return;  // uniform over the workgroup
     const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[st.e]);
 
@@ -138,6 +151,12 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
     }
 }
 
+// Expand + fold: each wave takes one 16-row sub-tile and EXP_COLS * EXP_BLOCKS columns, one
+// block of EXP_COLS at a time.  The row state (which rows fold, their xa fragments) is read once;
+// the base rows and B_e columns of the next block are loaded while the current one is computed
+// and written, so a wave keeps a block's loads in flight instead of paying its row lookups and
+// a memory round trip per EXP_COLS columns.
+template <int NKS>  // k-steps of 32 over max_rank
 __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __restrict__ xa,
                                                               const uint64_t* a_tab, const uint64_t* b_tab,
                                                               const float* __restrict__ s_tab, int n_tab,
@@ -148,11 +167,14 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ base, int64_t row_offset,
                                                               int64_t row_end, int64_t base16) {
     __shared__ __attribute__((aligned(16))) uint16_t s_delta[4][16][EXP_COLS];
+    __shared__ int s_off[257];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.y) * 64 + wave * 16;
-    const int n0 = blockIdx.x * EXP_COLS;
+    const int slab0 = blockIdx.x * (EXP_COLS * EXP_BLOCKS);
+    if (base16 + static_cast<int64_t>(blockIdx.y) * 64 >= row_end) return;  // uniform over the workgroup
+    stage_offsets(off, E, s_off);
     if (sub0 >= row_end) return;
-    const SubTile st = sub_tile_expert(static_cast<int>(sub0), off, E, n_tab, a_tab, b_tab);
+    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab, a_tab, b_tab);
     if (st.e < 0) return;
     const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[st.e]);
     const float scale = s_tab[st.e];
@@ -161,59 +183,82 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
     const int64_t r = sub0 + m;
     const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
     if (__ballot(act) == 0) return;
-    const uint16_t* xr = act ? xa + (r - row_offset) * max_rank + kq * 8 : nullptr;
-
-    // the base rows this wave folds into (FOLD_RPS rows x FOLD_LPR lanes x 8 columns per step)
-    // are loaded first, so that their memory round trip overlaps the delta's loads and MFMAs
+    u32x4 av[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        av[ks] = act ? *reinterpret_cast<const u32x4*>(xa + (r - row_offset) * max_rank + ks * 32 + kq * 8)
+                                   : u32x4{0, 0, 0, 0};
+    // fold rows of this lane (FOLD_RPS rows x FOLD_LPR lanes x 8 columns per step)
     const int col = (lane % FOLD_LPR) * 8;
-    bool ok[FOLD_STEPS];
-    u32x4 bvs[FOLD_STEPS];
+    bool row_ok[FOLD_STEPS];
 #pragma unroll
-    for (int it = 0; it < FOLD_STEPS; ++it) {
-        const int rl = it * FOLD_RPS + lane / FOLD_LPR;
-        const int64_t rr = sub0 + rl;
-        ok[it] = n0 + col < n_out &&
-                 row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
-        bvs[it] = ok[it] ? *reinterpret_cast<const u32x4*>(base + rr * n_out + n0 + col) : u32x4{0, 0, 0, 0};
-    }
+    for (int it = 0; it < FOLD_STEPS; ++it)
+        row_ok[it] = row_active(sub0 + it * FOLD_RPS + lane / FOLD_LPR, row_offset, row_end, st.span_end,
+                                sorted_ids, P, top_k, row_adapter);
 
-    f32x4 acc[EXP_COLS / 16];
+    u32x4 bvs[2][FOLD_STEPS], bw[2][NKS][EXP_COLS / 16];
+    auto load_block = [&](int cb, int set) __attribute__((always_inline)) {
+        const int n0 = slab0 + cb * EXP_COLS;
 #pragma unroll
-    for (int c = 0; c < EXP_COLS / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < max_rank; k0 += 32) {
-        const u32x4 av = xr ? *reinterpret_cast<const u32x4*>(xr + k0) : u32x4{0, 0, 0, 0};
-        const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-        for (int c = 0; c < EXP_COLS / 16; ++c) {
-            const int n = n0 + c * 16 + m;
-            const u32x4 bv = n < n_out ? *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(n) * max_rank + k0 + kq * 8)
-                                       : u32x4{0, 0, 0, 0};
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bv), acc[c], 0, 0, 0);
+        for (int it = 0; it < FOLD_STEPS; ++it) {
+            const int64_t rr = sub0 + it * FOLD_RPS + lane / FOLD_LPR;
+            bvs[set][it] = (row_ok[it] && n0 + col < n_out)
+                               ? *reinterpret_cast<const u32x4*>(base + rr * n_out + n0 + col)
+                               : u32x4{0, 0, 0, 0};
         }
-    }
-    // bf16 delta tile to LDS (rows 4*(lane/16)+v, column 16*c + lane%16)
 #pragma unroll
-    for (int c = 0; c < EXP_COLS / 16; ++c)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s_delta[wave][4 * kq + v][c * 16 + m] = f32_to_bf16(acc[c][v]);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-    // coalesced fold of the delta into the base rows loaded above
+            for (int c = 0; c < EXP_COLS / 16; ++c) {
+                const int n = n0 + c * 16 + m;
+                bw[set][ks][c] = n < n_out
+                                     ? *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(n) * max_rank +
+                                                                       ks * 32 + kq * 8)
+                                     : u32x4{0, 0, 0, 0};
+            }
+    };
+    load_block(0, 0);
 #pragma unroll
-    for (int it = 0; it < FOLD_STEPS; ++it) {
-        if (!ok[it]) continue;
-        const int rl = it * FOLD_RPS + lane / FOLD_LPR;
-        const int64_t rr = sub0 + rl;
-        const u32x4 bv = bvs[it];
-        const u32x4 dv = *reinterpret_cast<const u32x4*>(&s_delta[wave][rl][col]);
-        u32x4 o;
+    for (int cb = 0; cb < EXP_BLOCKS; ++cb) {
+        const int set = cb & 1;
+        const int n0 = slab0 + cb * EXP_COLS;
+        if (cb + 1 < EXP_BLOCKS) load_block(cb + 1, set ^ 1);
+        f32x4 acc[EXP_COLS / 16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float b_lo = __uint_as_float(bv[i] << 16), b_hi = __uint_as_float(bv[i] & 0xffff0000u);
-            const float d_lo = __uint_as_float(dv[i] << 16), d_hi = __uint_as_float(dv[i] & 0xffff0000u);
-            o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
+        for (int c = 0; c < EXP_COLS / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 afr = __builtin_bit_cast(bf16x8, av[ks]);
+#pragma unroll
+            for (int c = 0; c < EXP_COLS / 16; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bw[set][ks][c]),
+                                                                 acc[c], 0, 0, 0);
         }
-        *reinterpret_cast<u32x4*>(base + rr * n_out + n0 + col) = o;
+        // bf16 delta tile to LDS (rows 4*(lane/16)+v, column 16*c + lane%16)
+#pragma unroll
+        for (int c = 0; c < EXP_COLS / 16; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s_delta[wave][4 * kq + v][c * 16 + m] = f32_to_bf16(acc[c][v]);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // coalesced fold of the delta into the base rows
+#pragma unroll
+        for (int it = 0; it < FOLD_STEPS; ++it) {
+            if (!row_ok[it] || n0 + col >= n_out) continue;
+            const int rl = it * FOLD_RPS + lane / FOLD_LPR;
+            const int64_t rr = sub0 + rl;
+            const u32x4 bv = bvs[set][it];
+            const u32x4 dv = *reinterpret_cast<const u32x4*>(&s_delta[wave][rl][col]);
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float b_lo = __uint_as_float(bv[i] << 16), b_hi = __uint_as_float(bv[i] & 0xffff0000u);
+                const float d_lo = __uint_as_float(dv[i] << 16), d_hi = __uint_as_float(dv[i] & 0xffff0000u);
+                o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
+            }
+            *reinterpret_cast<u32x4*>(base + rr * n_out + n0 + col) = o;
+        }
+        __builtin_amdgcn_wave_barrier();  // this block's LDS reads before the next block's writes
     }
 }
 
@@ -402,10 +447,18 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
 #undef MOE_SHRINK
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid((n_out + EXP_COLS - 1) / EXP_COLS, static_cast<unsigned>(tiles));
-    lora_expand_fold_kernel<<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_out, max_rank, offsets, E,
-                                               sorted_ids, P, top_k, row_adapter, base, row_offset, row_end,
-                                               base16);
+    const dim3 grid((n_out + EXP_COLS * EXP_BLOCKS - 1) / (EXP_COLS * EXP_BLOCKS), static_cast<unsigned>(tiles));
+#define MOE_EXPAND(NKS_)                                                                                        \
+    lora_expand_fold_kernel<NKS_><<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_out, max_rank, offsets, E, \
+                                                      sorted_ids, P, top_k, row_adapter, base, row_offset, row_end, \
+                                                      base16)
+    switch (max_rank / 32) {
+        case 1: MOE_EXPAND(1); break;
+        case 2: MOE_EXPAND(2); break;
+        case 3: MOE_EXPAND(3); break;
+        default: MOE_EXPAND(4); break;
+    }
+#undef MOE_EXPAND
     return hipGetLastError();
 }
 
