@@ -53,7 +53,7 @@ class MoeConfig:
     E: int            # experts
     top_k: int
     block_size: int
-    weights: str = "bf16"          # "bf16" | "int4_gptq"
+    weights: str = "bf16"          # "bf16" | "int4_gptq" | "fp8"
     group_size: int = 128          # GPTQ group size along K
     logits: str = "normal"         # "normal" | "zipf"
     zipf_s: float = 1.2
@@ -93,6 +93,8 @@ CONFIGS: Dict[str, MoeConfig] = {
                               block_size=64, lora_rank=16, lora_max_rank=64),
     "decode_lora": MoeConfig("decode_lora", T=16, H=2048, I=1408, E=64, top_k=6, block_size=16,
                              weights="int4_gptq", group_size=128, lora_rank=16, lora_max_rank=64),
+    "fp8_prefill": MoeConfig("fp8_prefill", T=4096, H=4096, I=14336, E=8, top_k=2, block_size=64,
+                             weights="fp8"),
     "lora_all_prefill": MoeConfig("lora_all_prefill", T=2048, H=4096, I=1408, E=64, top_k=6,
                                   block_size=64, lora_rank=16, lora_max_rank=64, lora_gate_up=True),
 }
@@ -142,6 +144,24 @@ def _pack_nibbles(q: np.ndarray, axis: int) -> np.ndarray:
     for i in range(8):
         word |= q[..., i] << np.uint32(4 * i)
     return np.moveaxis(word.view(np.int32), -1, axis)
+
+
+def _fp8(ss: np.random.SeedSequence, E: int, N: int, K: int, threads: int) -> Dict[str, np.ndarray]:
+    """FP8 E4M3 expert weights: codes [E, N, K] (uint8) and one fp32 scale per output channel
+    [E, N].  Codes are drawn directly: random sign, exponent field uniform in 4..10 (magnitudes
+    1/8 .. 15), random 3-bit mantissa, so every code is finite; scales ~ U(0.002, 0.006)."""
+    codes = np.empty((E, N, K), dtype=np.uint8)
+    scales = np.empty((E, N), dtype=np.float32)
+
+    def one(rng, e):
+        sign = rng.integers(0, 2, size=(N, K), dtype=np.uint8) << 7
+        expo = rng.integers(4, 11, size=(N, K), dtype=np.uint8) << 3
+        mant = rng.integers(0, 8, size=(N, K), dtype=np.uint8)
+        codes[e] = sign | expo | mant
+        scales[e] = rng.uniform(0.002, 0.006, size=N).astype(np.float32)
+
+    _per_expert(ss, E, one, threads)
+    return {"codes": codes, "scales": scales}
 
 
 def _gptq(ss: np.random.SeedSequence, E: int, K: int, N: int, G: int,
@@ -201,6 +221,10 @@ def make_inputs(cfg: MoeConfig, seed: Optional[int] = None, threads: int = 8) ->
         d["gate"] = _gptq(ss_gate, E, H, I, G, threads)
         d["up"] = _gptq(ss_up, E, H, I, G, threads)
         d["down"] = _gptq(ss_down, E, I, H, G, threads)
+    elif cfg.weights == "fp8":
+        d["fp8_gate"] = _fp8(ss_gate, E, I, H, threads)
+        d["fp8_up"] = _fp8(ss_up, E, I, H, threads)
+        d["fp8_down"] = _fp8(ss_down, E, H, I, threads)
     else:
         raise ValueError(cfg.weights)
     if cfg.lora_rank:

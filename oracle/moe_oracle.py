@@ -39,6 +39,8 @@ __all__ = [
     "out_dim", "expert_matrix", "grouped_gate_up", "grouped_gate_up_lora", "grouped_down",
     "pack_expert_tables", "lora_windows", "lora_window_tiles", "lora_fold", "lora_gather_fold",
     "combine", "moe_layer", "moe_tokens",
+    "e4m3_to_f64", "e4m3_round", "quantize_rows_fp8", "fp8_expert_matrix", "grouped_gate_up_fp8",
+    "grouped_down_fp8",
 ]
 
 
@@ -80,6 +82,54 @@ def round_f32(v) -> np.ndarray:
 def silu(g: np.ndarray) -> np.ndarray:
     """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
     return g / (1.0 + np.exp(-g))
+
+
+# ----------------------------------------------------------------------------- FP8 E4M3
+# The fp8 prefill variant (atlas ``moe_lora_grouped.rs`` module doc: fp8, like bf16, is a grouped
+# prefill path writing the same sorted BF16 ``expert_down_out``).  The page names no format or
+# scaling; the reading taken: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+# mantissa bits; no infinities; S.1111.111 is NaN), weights with one fp32 scale per output
+# channel, activations quantised per row at run time with scale amax / 448.
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """FP8 E4M3 codes -> exact values (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Round values to the nearest E4M3 code, ties to an even mantissa; magnitudes that round
+    above 448 give the NaN code (no saturation).  -0.0 keeps its sign."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)                    # a = f * 2**ex, 0.5 <= f < 1
+    e = np.maximum(ex - 1, -6)             # unbiased exponent; below 2**-6 the subnormal quantum
+    q = np.rint(np.ldexp(a, 3 - e))        # multiples of 2**(e-3); 8..16 for normals
+    e = np.where(q >= 16, e + 1, e)
+    q = np.where(q >= 16, q / 2, q)        # 16 * 2**(e-3) == 8 * 2**(e-2): carry into the exponent
+    normal = q >= 8
+    field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, q - 8, q).astype(np.int64)
+    code = (field.astype(np.int64) << 3) | mant
+    code = np.where((field > 15) | ((field == 15) & (mant == 7)), 0x7F, code)
+    return (sign | code).astype(np.uint8)
+
+
+def quantize_rows_fp8(x: np.ndarray):
+    """Per-row dynamic FP8 quantisation of bf16 activations: s = fp32(amax) / 448 in fp32
+    (1.0 for an all-zero row), codes = e4m3_round(fp32(x) / s) with the division in fp32, so
+    that every code is decided in the precision the GPU uses.  Returns (codes uint8, s fp32)."""
+    xf = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(xf), axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = e4m3_round((xf / s[:, None]).astype(np.float32))
+    return q, s
 
 
 # ----------------------------------------------------------------------------- A1 route
@@ -352,6 +402,34 @@ def grouped_down(h: np.ndarray, w_down, al: Dict[str, np.ndarray],
     return y
 
 
+def fp8_expert_matrix(w: Dict[str, np.ndarray], e: int) -> np.ndarray:
+    """Dequantised [N, K] matrix of one FP8 expert: value(code) * scale of its output channel."""
+    return e4m3_to_f64(w["codes"][e]) * w["scales"][e].astype(np.float64)[:, None]
+
+
+def grouped_gate_up_fp8(xq: np.ndarray, sx: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray],
+                        top_k: int) -> np.ndarray:
+    """FP8 gate/up with SiLU * up over the sorted rows: for real row r (token t, expert e),
+    g = s_x[t] * sum_k x(t, k) Wg(e, n, k) with x = e4m3 values of the quantised token row and W
+    the dequantised weights; likewise u; h = silu(g) * u.  Sentinel rows are NaN."""
+    sid = al["sorted_ids"]
+    h = np.full((len(sid), w_gate["codes"].shape[1]), np.nan)
+    X = e4m3_to_f64(xq) * np.asarray(sx, np.float64)[:, None]
+    for e, rr in _rows_by_expert(al).items():
+        xt = X[sid[rr] // top_k]
+        h[rr] = silu(xt @ fp8_expert_matrix(w_gate, e).T) * (xt @ fp8_expert_matrix(w_up, e).T)
+    return h
+
+
+def grouped_down_fp8(hq: np.ndarray, sh: np.ndarray, w_down, al: Dict[str, np.ndarray]) -> np.ndarray:
+    """FP8 down over the sorted rows: y[r] = s_h[r] * (values of hq[r]) Wd(e)^T, dequantised."""
+    y = np.full((hq.shape[0], w_down["codes"].shape[1]), np.nan)
+    H = e4m3_to_f64(hq) * np.asarray(sh, np.float64)[:, None]
+    for e, rr in _rows_by_expert(al).items():
+        y[rr] = H[rr] @ fp8_expert_matrix(w_down, e).T
+    return y
+
+
 # ----------------------------------------------------------------------------- A5 LoRA fold
 def pack_expert_tables(entries: Iterable[Tuple[int, object, object, float]]):
     """Dense per-expert tables: atlas ``moe_lora_grouped.rs``, ``pack_expert_tables``.
@@ -545,6 +623,8 @@ def moe_layer(d: Dict[str, object], max_pad: Optional[int] = None) -> Dict[str, 
     cfg = d["cfg"]
     ids, w = route(d["logits"], cfg.top_k, cfg.renormalize)
     al = align(ids, cfg.E, cfg.block_size, max_pad)
+    if "fp8_gate" in d:
+        return _moe_layer_fp8(d, ids, w, al)
     wg, wu, wd = _weights(d)
     tg, tu = _lora_tables(d, "gate"), _lora_tables(d, "up")
     if tg is None and tu is None:
@@ -559,6 +639,47 @@ def moe_layer(d: Dict[str, object], max_pad: Optional[int] = None) -> Dict[str, 
     return {"ids": ids, "w": w, "align": al, "h": h, "y": y, "out": out}
 
 
+def _moe_tokens_fp8(d, tokens, ids, w) -> np.ndarray:
+    """The fp8 layer output for selected tokens, one (token, expert) pair at a time."""
+    cfg = d["cfg"]
+    xq, sx = quantize_rows_fp8(bf16_bits_to_f64(d["x"][tokens]))
+    X = e4m3_to_f64(xq) * sx.astype(np.float64)[:, None]
+    tabs = _lora_tables(d)
+    out = np.zeros((len(tokens), cfg.H))
+    for i in range(len(tokens)):
+        t = tokens[i]
+        for j in range(cfg.top_k):
+            e = int(ids[t, j])
+            h = silu(X[i] @ fp8_expert_matrix(d["fp8_gate"], e).T) * (X[i] @ fp8_expert_matrix(d["fp8_up"], e).T)
+            hs = round_bf16(h)
+            hq, sh = quantize_rows_fp8(hs[None, :])
+            y = (e4m3_to_f64(hq[0]) * np.float64(sh[0])) @ fp8_expert_matrix(d["fp8_down"], e).T
+            if tabs is not None and e < tabs[3] and tabs[0][e] is not None:
+                xa = round_bf16(hs @ bf16_bits_to_f64(tabs[0][e]).T)
+                y = y + np.float64(np.float32(tabs[2][e])) * round_bf16(xa @ bf16_bits_to_f64(tabs[1][e]).T)
+            out[i] += np.float64(w[t, j]) * y
+    return out
+
+
+def _moe_layer_fp8(d, ids, w, al) -> Dict[str, object]:
+    """FP8 prefill: x quantised per token; gate/up + SiLU * up; Hs rounded to bf16 (the buffer
+    the GPU writes) and quantised per sorted row; down; the fold, if any, on bf16 Hs; combine."""
+    cfg = d["cfg"]
+    xq, sx = quantize_rows_fp8(bf16_bits_to_f64(d["x"]))
+    h = grouped_gate_up_fp8(xq, sx, d["fp8_gate"], d["fp8_up"], al, cfg.top_k)
+    hs = round_bf16(np.nan_to_num(h))
+    hq, sh = quantize_rows_fp8(hs)
+    y = grouped_down_fp8(hq, sh, d["fp8_down"], al)
+    real = al["sorted_ids"] < cfg.P
+    y[~real] = np.nan
+    tabs = _lora_tables(d)
+    if tabs is not None:
+        y = lora_fold(y, hs, tabs, al, cfg.top_k, bf16_base=False)
+    out = combine(y, al["inv"], w, cfg.T, cfg.top_k)
+    return {"ids": ids, "w": w, "align": al, "h": np.where(real[:, None], h, np.nan), "y": y, "out": out,
+            "xq": xq, "sx": sx, "hq": hq, "sh": sh}
+
+
 def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
                routing: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
     """The layer output for selected tokens straight from the per-token definition.
@@ -570,6 +691,8 @@ def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
     """
     cfg = d["cfg"]
     ids, w = routing if routing is not None else route(d["logits"], cfg.top_k, cfg.renormalize)
+    if "fp8_gate" in d:
+        return _moe_tokens_fp8(d, list(tokens), ids, w)
     wg, wu, wd = _weights(d)
     tabs = _lora_tables(d)
     tabs_gu = (_lora_tables(d, "gate"), _lora_tables(d, "up"))

@@ -227,6 +227,23 @@ def fold_x_gather_by_row(y, x, tables, al, top_k, row_adapter=None, row_offset=0
     return om._orig_fold(y, xx, tables, al, top_k, row_adapter, row_offset, row_end, bf16_base)
 
 
+def e4m3_bias8(codes):
+    return om._orig_e4m3(codes) / 2.0
+
+
+def quantize_scale_447(x):
+    xf = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(xf), axis=1)
+    sc = np.where(amax > 0, amax / np.float32(447.0), np.float32(1.0)).astype(np.float32)
+    return om.e4m3_round((xf / sc[:, None]).astype(np.float32)), sc
+
+
+def fp8_gate_up_scale_by_column(xq, sx, w_gate, w_up, al, top_k):
+    # the activation scale taken per output column instead of per token row
+    h = om._orig_fp8_gate_up(xq, np.ones_like(sx), w_gate, w_up, al, top_k)
+    return h * np.resize(sx, h.shape[1])[None, :]
+
+
 om._orig_route = om.route
 om._orig_align = om.align
 om._orig_gate_up = om.grouped_gate_up
@@ -234,6 +251,8 @@ om._orig_combine = om.combine
 om._orig_fold = om.lora_fold
 om._orig_gather = om.lora_gather_fold
 om._orig_gate_up_lora = om.grouped_gate_up_lora
+om._orig_e4m3 = om.e4m3_to_f64
+om._orig_fp8_gate_up = om.grouped_gate_up_fp8
 
 ROUTE_PINS = [pins.test_route_worked_examples, pins.test_route_special_cases, pins.test_route_brute_force_ids_and_sum]
 ALIGN_PINS = [pins.test_align_worked_examples, lambda: pins.test_align_invariants_random(8, 2, 16, 64)]
@@ -241,6 +260,8 @@ LAYER_PINS = [lambda: pins.test_layer_matches_dense_brute_force(8, 2, 16), pins.
 GATHER_PINS = [pins.test_lora_gather_fold_rounding_pins, pins.test_lora_gather_fold_identity_closed_forms,
                pins.test_lora_gather_fold_on_sorted_rows_equals_grouped_fold]
 GATE_UP_LORA_PINS = [pins.test_gate_up_lora_rounding_pin, pins.test_layer_gate_up_lora_matches_dense_brute_force]
+FP8_PINS = [pins.test_e4m3_decode_against_torch, pins.test_quantize_rows_fp8_closed_forms,
+            pins.test_fp8_gemms_match_dequantised_definition]
 INT4_PINS = [pins.test_gptq_unpack_and_dequant, pins.test_layer_int4_matches_dense_brute_force]
 
 MUTANTS = [
@@ -266,6 +287,9 @@ MUTANTS = [
     ("grouped_gate_up_lora", gate_up_lora_gate_unrounded, GATE_UP_LORA_PINS),
     ("grouped_gate_up_lora", gate_up_lora_tables_swapped, GATE_UP_LORA_PINS),
     ("lora_fold", fold_x_gather_by_row, [pins.test_lora_fold_x_gather_closed_form]),
+    ("e4m3_to_f64", e4m3_bias8, FP8_PINS),
+    ("quantize_rows_fp8", quantize_scale_447, FP8_PINS),
+    ("grouped_gate_up_fp8", fp8_gate_up_scale_by_column, FP8_PINS),
 ]
 
 

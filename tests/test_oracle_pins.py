@@ -281,6 +281,75 @@ def test_grouped_gemm_sentinel_rows_undefined():
     assert np.isfinite(r["h"][~pad]).all()
 
 
+# ----------------------------------------------------------------------------- fp8 prefill
+def test_e4m3_decode_against_torch():
+    c = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_f64(c)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+    assert oracle.e4m3_to_f64(np.uint8([0x7E, 0x01, 0x08, 0x38]))[[0, 1, 2, 3]].tolist() == [448.0, 2.0 ** -9,
+                                                                                               2.0 ** -6, 1.0]
+
+
+def test_e4m3_round_against_torch():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([(rng.standard_normal(200000) * 40).astype(np.float32),
+                        (rng.standard_normal(20000) * 0.005).astype(np.float32),
+                        np.float32([0.0, -0.0, 448, 463.99, 2 ** -9, 2 ** -10, 3 * 2 ** -10, 1.0625, 1.1875,
+                                    -1.0625, 2 ** -6, 15 * 2 ** -10])])
+    # every value halfway between two neighbouring codes (ties go to the even mantissa)
+    vals = oracle.e4m3_to_f64(np.arange(0x7E, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids])
+    v = v[np.abs(v) < 464]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_round(v), ref)
+
+
+def test_quantize_rows_fp8_closed_forms():
+    x = np.array([[1.0, -0.5, 0.25, 0.0],          # amax 1 -> +-448 for the amax element
+                  [0.0, 0.0, 0.0, 0.0],            # zero row: scale 1, all codes 0
+                  [-3.0, 1.5, 0.75, 3.0]])         # amax 3, reached twice with both signs
+    q, s = oracle.quantize_rows_fp8(x)
+    assert s.dtype == np.float32 and s[1] == 1.0 and (q[1] == 0).all()
+    assert q[0, 0] == 0x7E and q[2, 0] == 0xFE and q[2, 3] == 0x7E
+    assert s[0] == np.float32(1.0) / np.float32(448.0)
+    # halves of the amax are exact powers of two below 448: 224, 112 (and their signs)
+    assert oracle.e4m3_to_f64(q[0]).tolist() == [448.0, -224.0, 112.0, 0.0]
+    back = oracle.e4m3_to_f64(q) * s[:, None].astype(np.float64)
+    assert np.allclose(back, x, rtol=2 ** -4, atol=0)
+
+
+def test_fp8_gemms_match_dequantised_definition():
+    """The fp8 GEMMs are the plain SwiGLU / down products of the values torch decodes from the
+    codes, scaled per token row and per output channel."""
+    cfg = MoeConfig("t", T=24, H=64, I=48, E=3, top_k=2, block_size=16, weights="fp8", seed=21)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    al = r["align"]
+    f64 = lambda c: torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).to(torch.float64)
+    X = f64(r["xq"]) * torch.from_numpy(r["sx"]).double()[:, None]
+    sid = al["sorted_ids"]
+    for rr in np.flatnonzero(sid < cfg.P):
+        t, e = sid[rr] // cfg.top_k, al["expert_ids"][rr // cfg.block_size]
+        Wg = f64(d["fp8_gate"]["codes"][e]) * torch.from_numpy(d["fp8_gate"]["scales"][e]).double()[:, None]
+        Wu = f64(d["fp8_up"]["codes"][e]) * torch.from_numpy(d["fp8_up"]["scales"][e]).double()[:, None]
+        h = torch.nn.functional.silu(Wg @ X[t]) * (Wu @ X[t])
+        assert np.allclose(r["h"][rr], h.numpy(), rtol=1e-12, atol=1e-15)
+        Wd = f64(d["fp8_down"]["codes"][e]) * torch.from_numpy(d["fp8_down"]["scales"][e]).double()[:, None]
+        y = Wd @ (f64(r["hq"][rr]) * float(r["sh"][rr]))
+        assert np.allclose(r["y"][rr], y.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_layer_sorted_equals_per_token():
+    cfg = MoeConfig("t", T=30, H=64, I=32, E=5, top_k=2, block_size=16, weights="fp8", seed=22)
+    d = make_inputs(cfg)
+    r = oracle.moe_layer(d)
+    tok = oracle.moe_tokens(d, range(cfg.T))
+    assert np.allclose(r["out"], tok, rtol=1e-12, atol=1e-14)
+
+
 # ----------------------------------------------------------------------------- combine
 def test_combine_worked_example():
     g = golden("combine_worked.json")
