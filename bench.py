@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -27,7 +28,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
 
 
 def gemm_flops(cfg, op: str) -> float:
@@ -41,6 +41,9 @@ def expert_weight_bytes(cfg, op: str) -> float:
     nproj = 2 if op == "gate_up" else 1
     if cfg.weights == "bf16":
         return float(nproj * cfg.H * cfg.I * 2)
+    if cfg.weights == "fp8":   # codes + one fp32 scale per output channel
+        N = cfg.I if op == "gate_up" else cfg.H
+        return float(nproj * (cfg.H * cfg.I + N * 4))
     G = cfg.group_size
     K, N = (cfg.H, cfg.I) if op == "gate_up" else (cfg.I, cfg.H)
     per = K // 8 * N * 4 + K // G * N * 2 + K // G * N // 8 * 4   # qweight + fp16 scales + qzeros
@@ -49,12 +52,14 @@ def expert_weight_bytes(cfg, op: str) -> float:
 
 def gemm_bytes(cfg, op: str, active_experts: int) -> float:
     """Algorithmic HBM bytes of one grouped GEMM launch: the active experts' weights, the
-    activation rows read once (x for gate/up, Hs for down) and the rows written (Hs / Ys)."""
+    activation rows read once (x for gate/up, Hs for down; 1-byte codes on the fp8 path) and the
+    rows written (Hs / Ys)."""
     w = active_experts * expert_weight_bytes(cfg, op)
+    ab = 1 if cfg.weights == "fp8" else 2
     if op == "gate_up":
-        act = cfg.T * cfg.H * 2 + cfg.P * cfg.I * 2
+        act = cfg.T * cfg.H * ab + cfg.P * cfg.I * 2
     else:
-        act = cfg.P * cfg.I * 2 + cfg.P * cfg.H * 2
+        act = cfg.P * cfg.I * ab + cfg.P * cfg.H * 2
     return w + act
 
 
@@ -66,6 +71,8 @@ def clone_layer(layer):
     def cw(w):
         if isinstance(w, m.Bf16Weight):
             return m.Bf16Weight(w.w.clone())
+        if isinstance(w, m.Fp8Weight):
+            return m.Fp8Weight(w.codes.clone(), w.scales.clone())
         return m.GptqWeight(w.qweight.clone(), w.scales.clone(), w.qzeros.clone(), w.group_size)
     c.gate, c.up, c.down = cw(layer.gate), cw(layer.up), cw(layer.down)
     return c
@@ -220,7 +227,9 @@ def main():
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if layer.lora is not None else None
     gu_what = ("gate/up stage: 2 gathered GEMMs, 2 LoRA folds, SiLU*up" if layer.gate_up_lora
+               else "gate/up stage: x quantisation + gemm_fp8_kernel<gate_up>" if cfg.weights == "fp8"
                else ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>")
+    peak_mfma = PEAK_FP8_TFLOPS if cfg.weights == "fp8" else PEAK_BF16_TFLOPS
     tokens_s = cfg.T / (ms / 1e3)
     active = int((b.routing.counts > 0).sum().item())
     gu_bytes = gemm_bytes(cfg, "gate_up", active)
@@ -239,8 +248,8 @@ def main():
         log("[bench] copy calibration: 1 GiB device-to-device copy done")
 
     ai = gemm_flops(cfg, "gate_up") / gu_bytes
-    if ai >= RIDGE:
-        roof = {"bound": "mfma", "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    if ai >= peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": gu_tflops, "peak": peak_mfma, "unit": "TFLOP/s"}
     else:
         gbs = gu_bytes / (gu_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -269,7 +278,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.weights == "bf16" else "int4 weights x bf16, fp32 accumulate",
+        "dtype": {"bf16": "bf16", "fp8": "fp8 e4m3 x fp8 e4m3, fp32 accumulate"}.get(
+            cfg.weights, "int4 weights x bf16, fp32 accumulate"),
         "data": "synthetic (seeded numpy PCG64; random-init expert weights)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
@@ -278,7 +288,7 @@ def main():
                    **({"lora_gate_up": True} if layer.gate_up_lora else {}),
                    "launch": "hip_graph" if args.graph else "eager"},
         "grouped_gemm_tflops": gemm_tflops,
-        "grouped_gemm_frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "grouped_gemm_frac_mfma_peak": gemm_tflops / peak_mfma,
         "kernels_ms": {"gate_up": gu_ms, "down": dn_ms,
                        **({"lora_fold": fold_ms} if fold_ms is not None else {})},
         "roofline": roof,

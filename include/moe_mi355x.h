@@ -11,6 +11,7 @@
  *                     down GEMM, and one gathered projection without activation
  *                     (bf16 or GPTQ-int4 expert weights)
  *   moe_silu_mul      SiLU(gate)*up when gate and up are folded separately
+ *   moe_quantize_fp8, moe_grouped_gemm_fp8   the fp8 prefill variant of the GEMMs
  *   moe_lora_fold     optional per-expert down-projection LoRA fold, in place
  *   moe_lora_gather_fold  the same fold on slot-major rows (decode, no sorting)
  *   moe_combine       top-k weighted sum of the expert outputs per token
@@ -157,13 +158,16 @@ moe_status moe_route_align(const float* logits, int32_t num_tokens, int32_t num_
  *   MOE_W_INT4_GPTQ: data = int32 qweight [E, K/8, N], K index 8i+s in nibble s of
  *                    word i; scales = fp16 [E, K/G, N]; qzeros = int32 [E, K/G, N/8],
  *                    N index 8i+s in nibble s; W[k,n] = (q - z) * s, groups of G
- *                    consecutive k (ferrum triton_fused_moe.rs, TritonStackedGptqWeight). */
-typedef enum { MOE_W_BF16 = 0, MOE_W_INT4_GPTQ = 1 } moe_wtype;
+ *                    consecutive k (ferrum triton_fused_moe.rs, TritonStackedGptqWeight).
+ *   MOE_W_FP8:       data = uint8 OCP FP8 E4M3 codes [E, N, K] (K contiguous);
+ *                    scales = fp32 [E, N]; W[n,k] = value(code) * scales[e, n].  Used by
+ *                    moe_grouped_gemm_fp8 only. */
+typedef enum { MOE_W_BF16 = 0, MOE_W_INT4_GPTQ = 1, MOE_W_FP8 = 2 } moe_wtype;
 typedef struct moe_weight {
     int32_t type;            /* moe_wtype */
     int32_t group_size;      /* G (int4 only): multiple of 32, divides K */
     const void* data;
-    const uint16_t* scales;
+    const void* scales;      /* int4: fp16 [E, K/G, N]; fp8: fp32 [E, N] */
     const int32_t* qzeros;
 } moe_weight;
 
@@ -211,6 +215,37 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
 /* Size in bytes of the optional moe_grouped_gemm workspace (fixed; it does not
  * depend on the problem). */
 int64_t moe_grouped_gemm_workspace_bytes(void);
+
+/* FP8 prefill (atlas moe_lora_grouped.rs module doc: an fp8 grouped prefill path
+ * that writes the same sorted BF16 expert_down_out; the page fixes no format, so the
+ * reading is OCP FP8 E4M3 with per-row activation and per-channel weight scales).
+ *
+ * moe_quantize_fp8: per-row dynamic quantisation of bf16 rows, in fp32:
+ *   amax = max |x[r]|; scale[r] = amax / 448; q[r] = e4m3(x[r] * (448 / amax)),
+ *   round to nearest even (scale 1 and zero codes for an all-zero row).
+ *   x bf16 [rows, k], q uint8 [rows, k], scale fp32 [rows].  With sorted_ids
+ *   (i32 [rows]) only rows r with sorted_ids[r] in [0, num_pairs) are written (the
+ *   real sorted rows of Hs); NULL writes every row (the token rows of x).
+ *   k % 16 == 0.  rows == 0 enqueues nothing. */
+moe_status moe_quantize_fp8(const uint16_t* x, int64_t rows, int32_t k, const int32_t* sorted_ids,
+                            int64_t num_pairs, uint8_t* q, float* scale, moe_stream stream);
+
+/* moe_grouped_gemm_fp8: the grouped GEMMs with fp8 operands; arguments as for
+ * moe_grouped_gemm, plus
+ *   a        uint8 e4m3 codes: GATE_UP_SILU x [num_pairs/top_k, K] by token; DOWN Hs
+ *            [max_pad, K] in sorted order (moe_quantize_fp8 outputs)
+ *   a_scale  fp32 per row of a ([num_pairs/top_k] or [max_pad])
+ *   w0, w1   MOE_W_FP8 weights (gate and up, or down)
+ *   c        bf16 [max_pad, N]: GATE_UP_SILU silu(g)*u, DOWN y, where
+ *            g[r, n] = a_scale[row] * scales[e, n] * sum_k a(row, k) W(n, k)
+ *            (exact fp8 products, fp32 sums)
+ * Sentinel and padding rows are not written.  op is MOE_OP_GATE_UP_SILU or
+ * MOE_OP_DOWN; K % 16 == 0; N % 8 == 0. */
+moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_scale, const moe_weight* w0,
+                                const moe_weight* w1, uint16_t* c, const int32_t* sorted_ids,
+                                const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
+                                int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
+                                moe_stream stream);
 
 /* A5 — LoRA fold, in place, on one window [row_offset, row_end) of the sorted
  * rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down).

@@ -11,7 +11,7 @@ from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_uint64, c_voi
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libmoe_mi355x.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
-MOE_W_BF16, MOE_W_INT4_GPTQ = 0, 1
+MOE_W_BF16, MOE_W_INT4_GPTQ, MOE_W_FP8 = 0, 1, 2
 MOE_OP_GATE_UP_SILU, MOE_OP_DOWN, MOE_OP_GATHER = 0, 1, 2
 
 # every symbol the header declares: name -> (restype, argtypes)
@@ -40,6 +40,10 @@ SIGNATURES = {
     "moe_lora_fold": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                 c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                 c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p]),
+    "moe_quantize_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
+    "moe_grouped_gemm_fp8": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int64,
+                                       c_void_p]),
     "moe_silu_mul": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p]),
     "moe_lora_gather_fold": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,

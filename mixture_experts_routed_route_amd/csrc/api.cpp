@@ -262,7 +262,8 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
     REQUIRE(w0 != nullptr, "%s: w0 is NULL", who);
     if (gate_up) REQUIRE(w1 != nullptr, "%s: MOE_OP_GATE_UP_SILU needs w1 (up)", who);
     else REQUIRE(w1 == nullptr, "%s: op %d takes no w1", who, op);
-    REQUIRE(w0->type == MOE_W_BF16 || w0->type == MOE_W_INT4_GPTQ, "%s: w0 has unknown type %d", who, w0->type);
+    REQUIRE(w0->type == MOE_W_BF16 || w0->type == MOE_W_INT4_GPTQ, "%s: w0 has unsupported type %d", who,
+            w0->type);
     if (w1) REQUIRE(w1->type == w0->type, "%s: w0 and w1 have different types", who);
     if (workspace != nullptr) {
         const int64_t need = moe_grouped_gemm_workspace_bytes();
@@ -303,8 +304,9 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
         REQUIRE_PTR(who, w1->qzeros);
     }
     return launched(who, moe::launch_gemm_int4(
-                             op, a, static_cast<const int32_t*>(w0->data), w0->scales, w0->qzeros,
-                             w1 ? static_cast<const int32_t*>(w1->data) : nullptr, w1 ? w1->scales : nullptr,
+                             op, a, static_cast<const int32_t*>(w0->data), static_cast<const uint16_t*>(w0->scales),
+                             w0->qzeros, w1 ? static_cast<const int32_t*>(w1->data) : nullptr,
+                             w1 ? static_cast<const uint16_t*>(w1->scales) : nullptr,
                              w1 ? w1->qzeros : nullptr, G, c, sorted_ids, expert_ids, P, top_k, num_experts, n, k,
                              block_size, static_cast<int>(max_pad), s));
 }
@@ -347,6 +349,67 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                                                expert_offsets, num_experts, sorted_ids, static_cast<int>(num_pairs),
                                                top_k, row_adapter, xa, row_offset, row_end, x_gather,
                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize_fp8(const uint16_t* x, int64_t rows, int32_t k, const int32_t* sorted_ids,
+                            int64_t num_pairs, uint8_t* q, float* scale, moe_stream stream) {
+    const char* who = "moe_quantize_fp8";
+    REQUIRE(k >= 16 && k % 16 == 0, "%s: k %d must be a positive multiple of 16", who, k);
+    REQUIRE(rows >= 0 && rows < INT32_MAX, "%s: rows %lld out of range", who, static_cast<long long>(rows));
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
+    if (rows == 0) return ok();
+    REQUIRE_PTR(who, x);
+    REQUIRE_PTR(who, q);
+    REQUIRE_PTR(who, scale);
+    if (sorted_ids) REQUIRE_PTR(who, sorted_ids);
+    return launched(who, moe::launch_quantize_fp8(x, rows, k, sorted_ids, static_cast<int>(num_pairs), q, scale,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_scale, const moe_weight* w0,
+                                const moe_weight* w1, uint16_t* c, const int32_t* sorted_ids,
+                                const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
+                                int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
+                                moe_stream stream) {
+    const char* who = "moe_grouped_gemm_fp8";
+    REQUIRE(op == MOE_OP_GATE_UP_SILU || op == MOE_OP_DOWN, "%s: op %d not GATE_UP_SILU or DOWN", who, op);
+    const bool gate_up = op == MOE_OP_GATE_UP_SILU;
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
+    REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
+    REQUIRE(num_pairs % top_k == 0, "%s: num_pairs %lld is not a multiple of top_k %d", who,
+            static_cast<long long>(num_pairs), top_k);
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    REQUIRE(n >= 8 && n % 8 == 0, "%s: n %d must be a positive multiple of 8", who, n);
+    REQUIRE(k >= 16 && k % 16 == 0, "%s: k %d must be a positive multiple of 16", who, k);
+    REQUIRE(max_pad >= max_padded(num_pairs, num_experts, block_size) && max_pad % block_size == 0 &&
+                max_pad < INT32_MAX,
+            "%s: max_pad %lld must be >= %lld and a multiple of block_size", who, static_cast<long long>(max_pad),
+            static_cast<long long>(max_padded(num_pairs, num_experts, block_size)));
+    REQUIRE(w0 != nullptr, "%s: w0 is NULL", who);
+    if (gate_up) REQUIRE(w1 != nullptr, "%s: MOE_OP_GATE_UP_SILU needs w1 (up)", who);
+    else REQUIRE(w1 == nullptr, "%s: op %d takes no w1", who, op);
+    REQUIRE(w0->type == MOE_W_FP8, "%s: w0 must be MOE_W_FP8 (type %d)", who, w0->type);
+    if (w1) REQUIRE(w1->type == MOE_W_FP8, "%s: w1 must be MOE_W_FP8 (type %d)", who, w1->type);
+    if (num_pairs == 0) return ok();
+    REQUIRE_PTR(who, a);
+    REQUIRE_PTR(who, a_scale);
+    REQUIRE_PTR(who, c);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, w0->data);
+    REQUIRE_PTR(who, w0->scales);
+    if (w1) {
+        REQUIRE_PTR(who, w1->data);
+        REQUIRE_PTR(who, w1->scales);
+    }
+    return launched(who, moe::launch_gemm_fp8(
+                             gate_up, a, a_scale, static_cast<const uint8_t*>(w0->data),
+                             static_cast<const float*>(w0->scales), w1 ? static_cast<const uint8_t*>(w1->data) : nullptr,
+                             w1 ? static_cast<const float*>(w1->scales) : nullptr, c, sorted_ids, expert_offsets,
+                             static_cast<int>(num_pairs), top_k, num_experts, n, k, static_cast<int>(max_pad),
+                             static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out, const int32_t* sorted_ids,

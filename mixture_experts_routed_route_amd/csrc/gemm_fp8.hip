@@ -1,0 +1,343 @@
+// FP8 prefill variant of the grouped expert GEMMs (atlas moe_lora_grouped.rs module doc: fp8,
+// like bf16, is a grouped prefill path that writes the same sorted BF16 expert_down_out).  The
+// page fixes no format, so the reading is: OCP FP8 E4M3 weights [E, N, K] with one fp32 scale
+// per output channel [E, N], and activations quantised per row at run time:
+//   quantize_fp8_kernel   amax of a bf16 row; s = amax / 448 (dequantisation scale) and
+//                         f = 448 / amax in fp32; codes = e4m3(x * f), round to nearest even
+//   gemm_fp8_kernel       acc = sum_k a(r, k) w(n, k) over the e4m3 values (products exact, fp32
+//                         sums) on the CDNA4 32x32x64 fp8 MFMA; out = acc * s_a[row] * s_w[n],
+//                         then SiLU(gate) * up (gate/up) or the plain value (down), to bf16
+//
+// GEMM tiling.  A tile is up to 128 consecutive sorted rows of one expert (an expert's padded
+// span is cut into ceil(span / 128) tiles; the list is rebuilt from expert_offsets by each
+// workgroup with an LDS scan) x a 128-row weight panel (gate/up: 64 gate and 64 up rows of the
+// same output columns, so SiLU * up is formed in the epilogue).  One workgroup per tile, 4
+// waves in a 2 x 2 grid, each owning 64 x 64 of the tile as 2 x 2 blocks of 32 x 32 fp32
+// accumulators.  K advances 128 bytes at a time through a 2-stage LDS ring filled by direct
+// global->LDS loads (16 bytes per lane, no VGPR staging); chunks past K load zeros.  LDS rows are
+// 128 bytes with the 16-byte chunk c of row r stored at c ^ ((r / 2) % 8), so the 32-row x
+// 16-byte fragment reads are free of bank conflicts.  An MFMA's operand is 32 bytes per lane
+// (two chunks); A and B fragments use the same lane -> k mapping, so every product pairs the
+// same k.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace moe {
+namespace {
+
+constexpr int F8_BM = 128;                          // sorted rows per tile
+constexpr int F8_BP = 128;                          // weight rows per tile
+constexpr int F8_BK = 128;                          // k (bytes = elements) per stage
+constexpr int F8_STAGES = 2;
+constexpr int F8_NW = 4;
+constexpr int F8_NT = 64 * F8_NW;
+constexpr int F8_CPR = F8_BK / 16;                  // 16-byte chunks per LDS row
+constexpr int F8_RPI = 1024 / F8_BK;                // rows one wave-wide 1 KB load fills
+constexpr int F8_A_INST = F8_BM / F8_RPI / F8_NW;   // load instructions per wave per stage
+constexpr int F8_B_INST = F8_BP / F8_RPI / F8_NW;
+constexpr int F8_STAGE_BYTES = (F8_BM + F8_BP) * F8_BK;
+constexpr int kMaxE8 = 256;
+static_assert(F8_A_INST * F8_NW * F8_RPI == F8_BM && F8_B_INST * F8_NW * F8_RPI == F8_BP, "load cover");
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// 16 bytes per lane from global memory into LDS at m0 + lane*16 (see gemm_bf16.hip: inline asm
+// keeps the compiler from draining the loads before every LDS read; completion is tracked with
+// explicit vmcnt waits)
+__device__ __forceinline__ void dma16_f8(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory");
+}
+
+__device__ __forceinline__ int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// ------------------------------------------------------------------ per-row quantisation
+constexpr int kQThreads = 256;
+
+__global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t* __restrict__ x,
+                                                                 uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                                 const int32_t* __restrict__ sorted_ids, int P,
+                                                                 int K) {
+    __shared__ float s_max[kQThreads / 64];
+    const int64_t r = blockIdx.x;
+    if (sorted_ids) {
+        const int p = sorted_ids[r];
+        if (p < 0 || p >= P) return;  // uniform over the workgroup
+    }
+    const uint16_t* xr = x + r * K;
+    float amax = 0.f;
+    for (int c = threadIdx.x * 8; c < K; c += kQThreads * 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    const float f = amax > 0.f ? 448.0f / amax : 1.0f;
+    if (threadIdx.x == 0) scale[r] = amax > 0.f ? amax / 448.0f : 1.0f;
+    uint8_t* qr = q + r * K;
+    for (int c = threadIdx.x * 8; c < K; c += kQThreads * 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // codes of elements 4h .. 4h+3, element 4h in the lowest byte
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(v[2 * h] << 16) * f,
+                                                     __uint_as_float(v[2 * h] & 0xffff0000u) * f, 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(v[2 * h + 1] << 16) * f,
+                                                 __uint_as_float(v[2 * h + 1] & 0xffff0000u) * f, pk, true);
+            w[h] = static_cast<uint32_t>(pk);
+        }
+        *reinterpret_cast<uint2*>(qr + c) = make_uint2(w[0], w[1]);
+    }
+}
+
+// ------------------------------------------------------------------ grouped GEMM
+template <bool GATE_UP>
+__global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __restrict__ A,
+                                                            const float* __restrict__ a_scale,
+                                                            const uint8_t* __restrict__ W0,
+                                                            const float* __restrict__ ws0,
+                                                            const uint8_t* __restrict__ W1,
+                                                            const float* __restrict__ ws1, uint16_t* __restrict__ C,
+                                                            const int32_t* __restrict__ sorted_ids,
+                                                            const int32_t* __restrict__ offsets, int P, int top_k,
+                                                            int E, int N, int K, int max_pad, int m_bound,
+                                                            int n_tiles) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_STAGES * F8_STAGE_BYTES];
+    __shared__ int s_scan[F8_NW];
+    __shared__ int s_lo[kMaxE8], s_hi[kMaxE8], s_tb[kMaxE8 + 1];
+    __shared__ int s_row[F8_BM];
+    __shared__ float s_as[F8_BM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations are scalar
+
+    // ---- expert spans and their row tiles
+    {
+        int lo = 0, hi = 0;
+        if (tid < E) {
+            lo = min(max(offsets[tid], 0), max_pad);
+            hi = min(max(offsets[tid + 1], lo), max_pad);
+        }
+        const int nt_e = (hi - lo + F8_BM - 1) / F8_BM;
+        const int incl = block_inclusive_scan<F8_NW>(nt_e, s_scan, (E + 63) / 64);
+        if (tid < E) { s_lo[tid] = lo; s_hi[tid] = hi; s_tb[tid + 1] = incl; }
+        if (tid == 0) s_tb[0] = 0;
+        __syncthreads();
+    }
+    const int m_real = __builtin_amdgcn_readfirstlane(s_tb[E]);
+    const int n_t = blockIdx.x / m_bound;
+    const int m_t = blockIdx.x - n_t * m_bound;
+    if (m_t >= m_real || n_t >= n_tiles) return;  // uniform over the workgroup
+    int lo_e = 0, hi_e = E - 1;                   // largest expert whose first row tile is <= m_t
+    while (lo_e < hi_e) {
+        const int mid = (lo_e + hi_e + 1) >> 1;
+        if (s_tb[mid] <= m_t) lo_e = mid; else hi_e = mid - 1;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(lo_e);
+    const int r0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (m_t - s_tb[e]) * F8_BM);
+    const int r_end = __builtin_amdgcn_readfirstlane(min(r0 + F8_BM, s_hi[e]));
+    constexpr int NCOL = GATE_UP ? F8_BP / 2 : F8_BP;  // output columns per tile
+    const int n0 = n_t * NCOL;
+
+    // ---- the tile's A rows (token rows for gate/up, sorted rows for down) and their scales
+    if (tid < F8_BM) {
+        const int r = r0 + tid;
+        int src = -1;
+        float sc = 0.f;
+        if (r < r_end) {
+            const int p = sorted_ids[r];
+            if (p >= 0 && p < P) {
+                src = GATE_UP ? p / top_k : r;
+                sc = a_scale[src];
+            }
+        }
+        s_row[tid] = src;
+        s_as[tid] = sc;
+    }
+    __syncthreads();
+
+    // ---- per-lane load sources: instruction q of this wave fills LDS rows
+    // (wave * INST + q) * F8_RPI .. + F8_RPI - 1; this lane's 16 bytes are physical chunk pc of
+    // row lrow, which holds logical chunk swz8(row, pc).  A row without a token reads a row that
+    // is always in bounds (token 0, or the tile's first sorted row); its results are never stored.
+    const int lrow = lane / F8_CPR, pc = lane % F8_CPR;
+    const uint8_t* a_src[F8_A_INST];
+    const uint8_t* b_src[F8_B_INST];
+    int a_kc[F8_A_INST], b_kc[F8_B_INST];
+#pragma unroll
+    for (int q = 0; q < F8_A_INST; ++q) {
+        const int row = (wave * F8_A_INST + q) * F8_RPI + lrow;
+        const int kc = swz8(row, pc);
+        const int src = s_row[row];
+        const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0);
+        a_src[q] = A + static_cast<size_t>(srow) * K + kc * 16;
+        a_kc[q] = kc;
+    }
+    const uint8_t* wb0 = W0 + static_cast<size_t>(e) * N * K;
+    const uint8_t* wb1 = GATE_UP ? W1 + static_cast<size_t>(e) * N * K : wb0;
+#pragma unroll
+    for (int q = 0; q < F8_B_INST; ++q) {
+        const int row = (wave * F8_B_INST + q) * F8_RPI + lrow;
+        const int kc = swz8(row, pc);
+        int n = GATE_UP ? n0 + (row & (F8_BP / 2 - 1)) : n0 + row;
+        n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
+        const uint8_t* base = (GATE_UP && row >= F8_BP / 2) ? wb1 : wb0;
+        b_src[q] = base + static_cast<size_t>(n) * K + kc * 16;
+        b_kc[q] = kc;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)smem)));
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * F8_BK;
+        const uint32_t sb = lds0 + static_cast<uint32_t>(t % F8_STAGES) * F8_STAGE_BYTES;
+        const bool full = k0 + F8_BK <= K;
+#pragma unroll
+        for (int q = 0; q < F8_A_INST; ++q) {
+            const void* g = a_src[q] + k0;
+            if (!full && k0 + a_kc[q] * 16 >= K) g = kZeroChunk;
+            dma16_f8(g, sb + (wave * F8_A_INST + q) * 1024);
+        }
+#pragma unroll
+        for (int q = 0; q < F8_B_INST; ++q) {
+            const void* g = b_src[q] + k0;
+            if (!full && k0 + b_kc[q] * 16 >= K) g = kZeroChunk;
+            dma16_f8(g, sb + F8_BM * F8_BK + (wave * F8_B_INST + q) * 1024);
+        }
+    };
+
+    // ---- main loop
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31, fh = lane >> 5;  // fragment row / column, 32-byte k half
+    int a_row[2], b_row[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a_row[i] = wm * 64 + i * 32 + fr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        b_row[j] = F8_BM + (GATE_UP ? (j == 0 ? wn * 32 : F8_BP / 2 + wn * 32) : wn * 64 + j * 32) + fr;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = (K + F8_BK - 1) / F8_BK;
+    issue(0);
+    for (int s = 0; s < nk; ++s) {
+        // this thread's loads of stage s have landed and every wave is past stage s - 1, whose
+        // buffer is refilled with stage s + 1
+        __builtin_amdgcn_s_waitcnt(0x0070 | (15 << 8));  // vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (s + 1 < nk) issue(s + 1);
+        const uint8_t* st = smem + (s % F8_STAGES) * F8_STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < F8_BK / 64; ++ks) {
+            const int c0 = ks * 4 + fh * 2;
+            i32x8 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint8_t* rp = st + a_row[i] * F8_BK;
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + swz8(a_row[i], c0) * 16);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + swz8(a_row[i], c0 + 1) * 16);
+                fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                              (int)hi[3]};
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint8_t* rp = st + b_row[j] * F8_BK;
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + swz8(b_row[j], c0) * 16);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + swz8(b_row[j], c0 + 1) * 16);
+                fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                              (int)hi[3]};
+            }
+            // format 0 (E4M3) for both operands; block scales 127 (2^0): plain fp8 products
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
+                                                                               127, 0, 127);
+        }
+    }
+
+    // ---- epilogue: scales, SiLU * up for gate/up; neighbour lanes (columns c, c+1) swap one
+    // value so that each lane stores two adjacent bf16 columns of one row as 4 bytes
+    const bool odd = (lane & 1) != 0;
+    constexpr int NJ = GATE_UP ? 1 : 2;
+    float wsc[2];
+    int colj[2];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        colj[j] = n0 + (GATE_UP ? wn * 32 : wn * 64 + j * 32) + fr;  // this lane's column
+        const int cc = min(colj[j], N - 1);
+        wsc[j] = ws0[static_cast<size_t>(e) * N + cc];
+    }
+    const float wsu = GATE_UP ? ws1[static_cast<size_t>(e) * N + min(colj[0], N - 1)] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            const int rl = wm * 64 + i * 32 + (v >> 2) * 8 + fh * 4 + (v & 3);  // row of value v
+            const float sa0 = s_as[rl], sa1 = s_as[rl + 1];
+            const int row_l = rl + (odd ? 1 : 0);
+            const bool ok = s_row[row_l] >= 0;
+            uint16_t* crow = C + static_cast<size_t>(r0 + row_l) * N;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                float h0, h1;  // values v (row rl) and v+1 (row rl+1) of this lane's column
+                if (GATE_UP) {
+                    h0 = silu_mul(acc[i][0][v] * sa0 * wsc[0], acc[i][1][v] * sa0 * wsu);
+                    h1 = silu_mul(acc[i][0][v + 1] * sa1 * wsc[0], acc[i][1][v + 1] * sa1 * wsu);
+                } else {
+                    h0 = acc[i][j][v] * sa0 * wsc[j];
+                    h1 = acc[i][j][v + 1] * sa1 * wsc[j];
+                }
+                const float send = odd ? h0 : h1;
+                const float got = __int_as_float(__builtin_amdgcn_update_dpp(
+                    0, __float_as_int(send), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+                const uint32_t pr = odd ? pack_bf16x2(got, h1) : pack_bf16x2(h0, got);
+                const int col = colj[j] & ~1;
+                if (ok && col < N) *reinterpret_cast<uint32_t*>(crow + col) = pr;
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int K, const int32_t* sorted_ids, int P,
+                               uint8_t* q, float* scale, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    quantize_fp8_kernel<<<static_cast<unsigned>(rows), kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(bool gate_up, const uint8_t* a, const float* a_scale, const uint8_t* w0,
+                           const float* ws0, const uint8_t* w1, const float* ws1, uint16_t* c,
+                           const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
+                           int K, int max_pad, hipStream_t s) {
+    const int ncol = gate_up ? F8_BP / 2 : F8_BP;
+    const int n_tiles = (N + ncol - 1) / ncol;
+    const int m_bound = (max_pad + F8_BM - 1) / F8_BM + E;  // row tiles of any routing, at most
+    const long long grid = static_cast<long long>(m_bound) * n_tiles;
+    if (grid <= 0) return hipSuccess;
+    if (gate_up)
+        gemm_fp8_kernel<true><<<static_cast<unsigned>(grid), F8_NT, 0, s>>>(
+            a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound, n_tiles);
+    else
+        gemm_fp8_kernel<false><<<static_cast<unsigned>(grid), F8_NT, 0, s>>>(
+            a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound,
+            n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -27,9 +27,9 @@ import numpy as np
 import torch
 
 from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER
-from .ops import (Bf16Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows, moe_align,
-                  moe_combine, moe_grouped_gemm, moe_lora_fold, moe_lora_gather_fold, moe_route, moe_route_align,
-                  moe_silu_mul, pack_lora_tables)
+from .ops import (Bf16Weight, Fp8Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows,
+                  moe_align, moe_combine, moe_grouped_gemm, moe_grouped_gemm_fp8, moe_lora_fold, moe_lora_gather_fold,
+                  moe_quantize_fp8, moe_route, moe_route_align, moe_silu_mul, pack_lora_tables)
 
 FOLD_MODES = ("auto", "grouped", "gather")
 
@@ -47,6 +47,10 @@ class Buffers:
     ws: torch.Tensor
     g: Optional[torch.Tensor] = None   # gate and up outputs of the gate/up LoRA path
     u: Optional[torch.Tensor] = None
+    xq: Optional[torch.Tensor] = None  # fp8 path: e4m3 codes and per-row scales of x and of Hs
+    sx: Optional[torch.Tensor] = None
+    hq: Optional[torch.Tensor] = None
+    sh: Optional[torch.Tensor] = None
 
 
 class MoeLayer:
@@ -55,12 +59,18 @@ class MoeLayer:
                  fold: str = "auto", lora_gate: Optional[LoraTables] = None, lora_up: Optional[LoraTables] = None):
         if fold not in FOLD_MODES:
             raise ValueError(f"fold must be one of {FOLD_MODES}")
+        if isinstance(gate, Fp8Weight) and (lora_gate is not None or lora_up is not None):
+            raise ValueError("gate/up LoRA tables are not supported with fp8 weights")
         self.E, self.H, self.I, self.top_k, self.bs = num_experts, hidden, inter, top_k, block_size
         self.gate, self.up, self.down, self.lora = gate, up, down, lora
         self.lora_gate, self.lora_up = lora_gate, lora_up
         self.renormalize = renormalize
         self.lora_cap = lora_cap
         self.fold = fold
+
+    @property
+    def fp8(self) -> bool:
+        return isinstance(self.gate, Fp8Weight)
 
     @property
     def gate_up_lora(self) -> bool:
@@ -77,6 +87,10 @@ class MoeLayer:
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
         if "wg" in d:
             gate, up, down = Bf16Weight(bf(d["wg"])), Bf16Weight(bf(d["wu"])), Bf16Weight(bf(d["wd"]))
+        elif "fp8_gate" in d:
+            def f8(w):
+                return Fp8Weight(torch.from_numpy(w["codes"]).to(device), torch.from_numpy(w["scales"]).to(device))
+            gate, up, down = f8(d["fp8_gate"]), f8(d["fp8_up"]), f8(d["fp8_down"])
         else:
             def gq(w):
                 return GptqWeight(torch.from_numpy(w["qweight"]).to(device),
@@ -114,6 +128,10 @@ class MoeLayer:
         if self.gate_up_lora:
             b.g = torch.empty((r.max_pad, self.I), **bf)
             b.u = torch.empty((r.max_pad, self.I), **bf)
+        if self.fp8:
+            u8, f32 = dict(dtype=torch.uint8, device=device), dict(dtype=torch.float32, device=device)
+            b.xq, b.sx = torch.empty((T, self.H), **u8), torch.empty(max(T, 1), **f32)
+            b.hq, b.sh = torch.empty((r.max_pad, self.I), **u8), torch.empty(r.max_pad, **f32)
         return b
 
     # ------------------------------------------------------------------ forward
@@ -121,7 +139,12 @@ class MoeLayer:
         moe_route_align(logits, self.top_k, self.renormalize, self.bs, b.ids, b.w, b.routing)
 
     def gate_up_stage(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
-        """Hs from x: the fused kernel, or gathered gate and up, their folds and SiLU * up."""
+        """Hs from x: the fused kernel, or gathered gate and up, their folds and SiLU * up; with fp8
+        weights, x quantised per token and the fp8 fused kernel."""
+        if self.fp8:
+            moe_quantize_fp8(x, b.xq, b.sx)
+            moe_grouped_gemm_fp8(MOE_OP_GATE_UP_SILU, b.xq, b.sx, self.gate, self.up, b.routing, out=b.hs)
+            return
         if not self.gate_up_lora:
             moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs, workspace=b.ws)
             return
@@ -134,6 +157,10 @@ class MoeLayer:
         moe_silu_mul(b.g, b.u, b.hs, b.routing)
 
     def down_stage(self, b: Buffers) -> None:
+        if self.fp8:  # the real rows of Hs quantised per row, then the fp8 down GEMM
+            moe_quantize_fp8(b.hs, b.hq, b.sh, b.routing)
+            moe_grouped_gemm_fp8(MOE_OP_DOWN, b.hq, b.sh, self.down, None, b.routing, out=b.ys)
+            return
         moe_grouped_gemm(MOE_OP_DOWN, b.hs, self.down, None, b.routing, out=b.ys, workspace=b.ws)
 
     def experts(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:

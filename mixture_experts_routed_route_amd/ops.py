@@ -11,11 +11,11 @@ from typing import List, Optional, Sequence, Tuple, Union
 
 import torch
 
-from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, MOE_W_INT4_GPTQ, MoeWeight, check,
-                   lib)
+from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, MOE_W_FP8, MOE_W_INT4_GPTQ,
+                   MoeWeight, check, lib)
 
 __all__ = [
-    "Bf16Weight", "GptqWeight", "Routing", "LoraTables", "max_padded", "align_workspace_bytes",
+    "Bf16Weight", "GptqWeight", "Fp8Weight", "Routing", "moe_quantize_fp8", "moe_grouped_gemm_fp8", "LoraTables", "max_padded", "align_workspace_bytes",
     "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
@@ -69,7 +69,22 @@ class GptqWeight:
                          _dev(self.scales, torch.float16, "scales"), _dev(self.qzeros, torch.int32, "qzeros"))
 
 
-Weight = Union[Bf16Weight, GptqWeight]
+@dataclass
+class Fp8Weight:
+    """FP8 E4M3 expert weights: codes ``[E, N, K]`` uint8, one fp32 scale per output channel ``[E, N]``."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+    @property
+    def shape(self) -> Tuple[int, int, int]:
+        return tuple(self.codes.shape)
+
+    def struct(self) -> MoeWeight:
+        return MoeWeight(MOE_W_FP8, 0, _dev(self.codes, torch.uint8, "codes"),
+                         _dev(self.scales, torch.float32, "scales"), None)
+
+
+Weight = Union[Bf16Weight, GptqWeight, Fp8Weight]
 
 
 # ----------------------------------------------------------------------------- host helpers
@@ -214,6 +229,34 @@ def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight],
                                  routing.num_experts, N, K, routing.block_size, routing.max_pad,
                                  _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
                                  workspace.numel() if workspace is not None else 0, _stream(a)))
+    return out
+
+
+# ----------------------------------------------------------------------------- fp8 prefill
+def moe_quantize_fp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
+                     routing: Optional[Routing] = None) -> None:
+    """Per-row e4m3 codes and scales of bf16 rows; with ``routing`` only the real sorted rows."""
+    rows, k = x.shape
+    check(lib().moe_quantize_fp8(_dev(x, torch.bfloat16, "x"), rows, k,
+                                 _dev(routing.sorted_ids, torch.int32, "sorted_ids") if routing is not None else None,
+                                 routing.num_pairs if routing is not None else 0, _dev(q, torch.uint8, "q"),
+                                 _dev(scale, torch.float32, "scale"), _stream(x)))
+
+
+def moe_grouped_gemm_fp8(op: int, a: torch.Tensor, a_scale: torch.Tensor, w0: Fp8Weight, w1: Optional[Fp8Weight],
+                         routing: Routing, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """op = MOE_OP_GATE_UP_SILU (a = x codes [T, K] by token) or MOE_OP_DOWN (a = Hs codes [max_pad, K])."""
+    E, N, K = w0.shape
+    if out is None:
+        out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=a.device)
+    s0 = w0.struct()
+    s1 = w1.struct() if w1 is not None else None
+    check(lib().moe_grouped_gemm_fp8(op, _dev(a, torch.uint8, "a"), _dev(a_scale, torch.float32, "a_scale"),
+                                     ctypes.byref(s0), ctypes.byref(s1) if s1 is not None else None,
+                                     _dev(out, torch.bfloat16, "out"),
+                                     _dev(routing.sorted_ids, torch.int32, "sorted_ids"),
+                                     _dev(routing.offsets, torch.int32, "offsets"), routing.num_pairs, routing.top_k,
+                                     routing.num_experts, N, K, routing.block_size, routing.max_pad, _stream(a)))
     return out
 
 

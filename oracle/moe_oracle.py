@@ -122,13 +122,17 @@ def e4m3_round(v) -> np.ndarray:
 
 
 def quantize_rows_fp8(x: np.ndarray):
-    """Per-row dynamic FP8 quantisation of bf16 activations: s = fp32(amax) / 448 in fp32
-    (1.0 for an all-zero row), codes = e4m3_round(fp32(x) / s) with the division in fp32, so
-    that every code is decided in the precision the GPU uses.  Returns (codes uint8, s fp32)."""
+    """Per-row dynamic FP8 quantisation of bf16 activations.  In fp32, as the GPU computes it:
+    amax = max |x|; the dequantisation scale s = amax / 448 and the quantisation factor
+    f = 448 / amax (both 1 for an all-zero row); codes = e4m3_round(x * f).  Every code is
+    decided from the same fp32 product on both sides.  Returns (codes uint8, s fp32)."""
     xf = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(xf), axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
-    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    q = e4m3_round((xf / s[:, None]).astype(np.float32))
+    pos = amax > 0
+    safe = np.where(pos, amax, np.float32(1.0)).astype(np.float32)
+    s = np.where(pos, safe / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    f = np.where(pos, np.float32(448.0) / safe, np.float32(1.0)).astype(np.float32)
+    q = e4m3_round((xf * f[:, None]).astype(np.float32))
     return q, s
 
 
@@ -402,9 +406,16 @@ def grouped_down(h: np.ndarray, w_down, al: Dict[str, np.ndarray],
     return y
 
 
+_E4M3_VALUES: Optional[np.ndarray] = None
+
+
 def fp8_expert_matrix(w: Dict[str, np.ndarray], e: int) -> np.ndarray:
-    """Dequantised [N, K] matrix of one FP8 expert: value(code) * scale of its output channel."""
-    return e4m3_to_f64(w["codes"][e]) * w["scales"][e].astype(np.float64)[:, None]
+    """Dequantised [N, K] matrix of one FP8 expert: value(code) * scale of its output channel
+    (the values of all 256 codes are decoded once and looked up)."""
+    global _E4M3_VALUES
+    if _E4M3_VALUES is None:
+        _E4M3_VALUES = e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    return _E4M3_VALUES[w["codes"][e]] * w["scales"][e].astype(np.float64)[:, None]
 
 
 def grouped_gate_up_fp8(xq: np.ndarray, sx: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray],
@@ -640,24 +651,28 @@ def moe_layer(d: Dict[str, object], max_pad: Optional[int] = None) -> Dict[str, 
 
 
 def _moe_tokens_fp8(d, tokens, ids, w) -> np.ndarray:
-    """The fp8 layer output for selected tokens, one (token, expert) pair at a time."""
+    """The fp8 layer output for selected tokens, per (token, expert) pair (pairs grouped by
+    expert only so that each expert's matrices are dequantised once)."""
     cfg = d["cfg"]
     xq, sx = quantize_rows_fp8(bf16_bits_to_f64(d["x"][tokens]))
     X = e4m3_to_f64(xq) * sx.astype(np.float64)[:, None]
     tabs = _lora_tables(d)
-    out = np.zeros((len(tokens), cfg.H))
-    for i in range(len(tokens)):
-        t = tokens[i]
+    by_e: Dict[int, List[Tuple[int, int]]] = {}
+    for i, t in enumerate(tokens):
         for j in range(cfg.top_k):
-            e = int(ids[t, j])
-            h = silu(X[i] @ fp8_expert_matrix(d["fp8_gate"], e).T) * (X[i] @ fp8_expert_matrix(d["fp8_up"], e).T)
+            by_e.setdefault(int(ids[t, j]), []).append((i, j))
+    out = np.zeros((len(tokens), cfg.H))
+    for e, lst in sorted(by_e.items()):
+        Wg, Wu, Wd = (fp8_expert_matrix(d[k], e) for k in ("fp8_gate", "fp8_up", "fp8_down"))
+        for i, j in lst:
+            h = silu(Wg @ X[i]) * (Wu @ X[i])
             hs = round_bf16(h)
             hq, sh = quantize_rows_fp8(hs[None, :])
-            y = (e4m3_to_f64(hq[0]) * np.float64(sh[0])) @ fp8_expert_matrix(d["fp8_down"], e).T
+            y = Wd @ (e4m3_to_f64(hq[0]) * np.float64(sh[0]))
             if tabs is not None and e < tabs[3] and tabs[0][e] is not None:
                 xa = round_bf16(hs @ bf16_bits_to_f64(tabs[0][e]).T)
                 y = y + np.float64(np.float32(tabs[2][e])) * round_bf16(xa @ bf16_bits_to_f64(tabs[1][e]).T)
-            out[i] += np.float64(w[t, j]) * y
+            out[i] += np.float64(w[tokens[i], j]) * y
     return out
 
 

@@ -24,7 +24,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     from mixture_experts_routed_route_amd import _lib
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
@@ -165,6 +165,22 @@ def test_argument_validation_rejects_before_launch(L):
     rc, msg = _rc(L, "moe_grouped_gemm", 2, fake, ctypes.byref(w), ctypes.byref(w), fake, fake, fake, fake, 128, 2,
                   8, 128, 256, 16, 256, None, 0, None)
     assert rc == -1 and "takes no w1" in msg
+    rc, msg = _rc(L, "moe_quantize_fp8", fake, 16, 24, None, 0, fake, fake, None)
+    assert rc == -1 and "multiple of 16" in msg
+    assert _rc(L, "moe_quantize_fp8", None, 0, 64, None, 0, None, None, None)[0] == 0   # no rows
+    w8 = MoeWeight(2, 0, 1 << 20, fake, None)
+    rc, msg = _rc(L, "moe_grouped_gemm_fp8", 2, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8, 128,
+                  256, 16, 256, None)
+    assert rc == -1 and "op 2" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w), None, fake, fake, fake, 128, 2, 8, 128,
+                  256, 16, 256, None)
+    assert rc == -1 and "MOE_W_FP8" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8, 128,
+                  264, 16, 256, None)
+    assert rc == -1 and "multiple of 16" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w8), None, fake, fake, fake, fake, 128, 2, 8, 128,
+                  256, 16, 256, None, 0, None)
+    assert rc == -1 and "unsupported type" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 100, 8, None)
     assert rc == -1 and "hidden" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 128, 7, None)

@@ -388,6 +388,112 @@ def test_layer_gate_up_lora(dev, fold):
     assert_close_rows(bf16_host(out), ref["out"], TOL, f"layer gate/up lora {fold}")
 
 
+# ----------------------------------------------------------------------------- fp8 prefill
+FP8_SMALL = {
+    # ragged K and N against the 128-wide tiles, one expert over several row tiles, empty experts
+    "fp8_small": MoeConfig("fp8_small", T=300, H=528, I=912, E=8, top_k=2, block_size=64, weights="fp8", seed=51),
+    "fp8_skewed": MoeConfig("fp8_skewed", T=500, H=256, I=384, E=32, top_k=4, block_size=32, weights="fp8",
+                            logits="zipf", seed=52),
+}
+
+
+def test_quantize_fp8_bit_exact(dev):
+    """Codes and scales equal the oracle's bit for bit (every code is decided from the same fp32
+    product); with sorted ids only real rows are written."""
+    import torch
+    m = ops()
+    rng = np.random.default_rng(61)
+    rows, k = 77, 1040
+    x = f32_to_bf16_bits((rng.standard_normal((rows, k)) * np.exp(rng.uniform(-8, 8, (rows, 1)))).astype(np.float32))
+    x[3] = 0                                        # all-zero row
+    x[5, :] = f32_to_bf16_bits(np.float32(1.5))     # constant row: every code is +448
+    x[6, ::7] = f32_to_bf16_bits(np.float32(-2.0 ** -120))
+    q = torch.empty((rows, k), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    m.moe_quantize_fp8(bf16_dev(x), q, sc)
+    want_q, want_s = oracle.quantize_rows_fp8(oracle.bf16_bits_to_f64(x))
+    got_q = q.cpu().numpy()
+    note(f"quantize: {(got_q != want_q).sum()} codes differ")
+    assert np.array_equal(got_q, want_q)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    # sorted rows: sentinel rows keep their canary bytes and scales
+    cfg = FP8_SMALL["fp8_skewed"]
+    d = make_inputs(cfg)
+    ids, w, al, r = _routing(cfg, d)
+    real = _real(al, cfg.P)
+    hs = f32_to_bf16_bits(rng.standard_normal((r.max_pad, 96)).astype(np.float32))
+    q2 = torch.full((r.max_pad, 96), 0xA5, dtype=torch.uint8, device="cuda")
+    s2 = torch.full((r.max_pad,), -7.0, dtype=torch.float32, device="cuda")
+    m.moe_quantize_fp8(bf16_dev(hs), q2, s2, r)
+    wq, ws = oracle.quantize_rows_fp8(oracle.bf16_bits_to_f64(hs[real]))
+    gq, gs = q2.cpu().numpy(), s2.cpu().numpy()
+    assert np.array_equal(gq[real], wq) and np.array_equal(gs[real], ws)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    assert (gq[pad] == 0xA5).all() and (gs[pad] == -7.0).all()
+
+
+@pytest.mark.parametrize("name", list(FP8_SMALL))
+def test_grouped_gemm_fp8(dev, name):
+    """Both fp8 GEMMs against the oracle on the oracle's own codes and scales (so only the GEMM
+    is compared); sentinel and padding rows are never written."""
+    import torch
+    m = ops()
+    cfg = FP8_SMALL[name]
+    note(f"gemm fp8 {name}")
+    d = make_inputs(cfg)
+    ids, w, al, r = _routing(cfg, d)
+    layer = _weights_dev(d)
+    real = _real(al, cfg.P)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    ref = oracle.moe_layer(d)
+    xq, sx = ref["xq"], ref["sx"]
+    hs = _canary(r.max_pad, cfg.I)
+    m.moe_grouped_gemm_fp8(m.MOE_OP_GATE_UP_SILU, to_dev(xq), to_dev(sx), layer.gate, layer.up, r, out=hs)
+    hb = bits_host(hs)
+    assert (hb[pad] == CANARY).all(), "padding rows of Hs written"
+    e1, e2 = assert_close_rows(bf16_host(hs)[real], ref["h"][real], TOL, "fp8 gate/up")
+    note(f"  gate/up worst row {e1:.2e}")
+    hq = np.zeros((r.max_pad, cfg.I), np.uint8)
+    sh = np.ones(r.max_pad, np.float32)
+    hq[real], sh[real] = ref["hq"][real], ref["sh"][real]
+    ys = _canary(r.max_pad, cfg.H)
+    m.moe_grouped_gemm_fp8(m.MOE_OP_DOWN, to_dev(hq), to_dev(sh), layer.down, None, r, out=ys)
+    yb = bits_host(ys)
+    assert (yb[pad] == CANARY).all(), "padding rows of Ys written"
+    e1, e2 = assert_close_rows(bf16_host(ys)[real], ref["y"][real], TOL, "fp8 down")
+    note(f"  down worst row {e1:.2e}")
+
+
+@pytest.mark.parametrize("name", list(FP8_SMALL))
+def test_layer_fp8_end_to_end(dev, name):
+    """The fp8 layer stage by stage on the GPU's own intermediates (each stage to the usual
+    bar: codes bit-exact, GEMMs and combine within 2e-2 per row), then against the independent
+    oracle at 5e-2.  The wider end-to-end bar is that of a 3-bit mantissa: where the GPU's bf16
+    Hs differs from the oracle's in the last bit, an e4m3 code can round the other way and move
+    its element by one fp8 step (1/16 to 1/8 of its size)."""
+    cfg = FP8_SMALL[name]
+    d = make_inputs(cfg)
+    layer, b, out = _layer_run(cfg, d)
+    ref = oracle.moe_layer(d)
+    al = ref["align"]
+    real = _real(al, cfg.P)
+    assert np.array_equal(b.ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(b.xq.cpu().numpy(), ref["xq"]) and np.array_equal(b.sx.cpu().numpy(), ref["sx"])
+    assert_close_rows(bf16_host(b.hs)[real], ref["h"][real], TOL, f"{name} Hs")
+    hs_gpu = bf16_host(b.hs)
+    hq, sh = oracle.quantize_rows_fp8(hs_gpu[real])
+    assert np.array_equal(b.hq.cpu().numpy()[real], hq) and np.array_equal(b.sh.cpu().numpy()[real], sh)
+    hq_full = np.zeros((len(al["sorted_ids"]), cfg.I), np.uint8)
+    sh_full = np.ones(len(al["sorted_ids"]), np.float32)
+    hq_full[real], sh_full[real] = hq, sh
+    y_chain = oracle.grouped_down_fp8(hq_full, sh_full, d["fp8_down"], al)
+    assert_close_rows(bf16_host(b.ys)[real], y_chain[real], TOL, f"{name} Ys on the GPU's codes")
+    out_chain = oracle.combine(bf16_host(b.ys), al["inv"], ref["w"], cfg.T, cfg.top_k)
+    assert_close_rows(bf16_host(out), out_chain, TOL, f"{name} combine")
+    e1, e2 = assert_close_rows(bf16_host(out), ref["out"], 5e-2, f"layer {name} against the oracle")
+    note(f"layer fp8 {name}: against the independent oracle worst row {e1:.2e}, tensor {e2:.2e}")
+
+
 # ----------------------------------------------------------------------------- A6 combine
 @pytest.mark.parametrize("name", ["tiny", "finegrained_small", "mixtral_small"])
 def test_combine(dev, name):
@@ -657,7 +763,8 @@ def test_layer_full_size_sampled(dev, name):
     toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n, replace=False)]))
     ref = oracle.moe_tokens(d, toks, (ids, w))
     got = bf16_host(out)[toks]
-    e1, e2 = assert_close_rows(got, ref, TOL, f"layer full {name}")
+    tol = 5e-2 if cfg.weights == "fp8" else TOL  # fp8: the 3-bit-mantissa bar of the fp8 layer test
+    e1, e2 = assert_close_rows(got, ref, tol, f"layer full {name}")
     note(f"  worst row rel err {e1:.2e}, tensor {e2:.2e}")
 
 

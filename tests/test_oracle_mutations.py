@@ -235,7 +235,8 @@ def quantize_scale_447(x):
     xf = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(xf), axis=1)
     sc = np.where(amax > 0, amax / np.float32(447.0), np.float32(1.0)).astype(np.float32)
-    return om.e4m3_round((xf / sc[:, None]).astype(np.float32)), sc
+    f = np.where(amax > 0, np.float32(447.0) / np.maximum(amax, np.float32(1e-30)), np.float32(1.0))
+    return om.e4m3_round((xf * f[:, None].astype(np.float32)).astype(np.float32)), sc
 
 
 def fp8_gate_up_scale_by_column(xq, sx, w_gate, w_up, al, top_k):
