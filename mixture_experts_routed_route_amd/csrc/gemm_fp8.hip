@@ -8,12 +8,12 @@
 //                         sums) on the CDNA4 32x32x64 fp8 MFMA; out = acc * s_a[row] * s_w[n],
 //                         then SiLU(gate) * up (gate/up) or the plain value (down), to bf16
 //
-// GEMM tiling.  A tile is up to 128 consecutive sorted rows of one expert (an expert's padded
-// span is cut into ceil(span / 128) tiles; the list is rebuilt from expert_offsets by each
-// workgroup with an LDS scan) x a 128-row weight panel (gate/up: 64 gate and 64 up rows of the
-// same output columns, so SiLU * up is formed in the epilogue).  One workgroup per tile, 4
-// waves in a 2 x 2 grid, each owning 64 x 64 of the tile as 2 x 2 blocks of 32 x 32 fp32
-// accumulators.  K advances 128 bytes at a time through a 2-stage LDS ring filled by direct
+// GEMM tiling.  A tile is up to BM (256, or 128 when experts average fewer than 128 rows)
+// consecutive sorted rows of one expert (an expert's padded span is cut into ceil(span / BM)
+// tiles; the list is rebuilt from expert_offsets by each workgroup with an LDS scan) x a BM-row
+// weight panel (gate/up: BM/2 gate and BM/2 up rows of the same output columns, so SiLU * up is
+// formed in the epilogue).  One workgroup per tile, BM/32 waves in a (BM/64) x 2 grid, each
+// owning 64 rows x BM/2 panel rows as 32 x 32 blocks of fp32 accumulators.  K advances 128 bytes at a time through a 2-stage LDS ring filled by direct
 // global->LDS loads (16 bytes per lane, no VGPR staging); chunks past K load zeros.  LDS rows are
 // 128 bytes with the 16-byte chunk c of row r stored at c ^ ((r / 2) % 8), so the 32-row x
 // 16-byte fragment reads are free of bank conflicts.  An MFMA's operand is 32 bytes per lane
@@ -25,19 +25,27 @@
 namespace moe {
 namespace {
 
-constexpr int F8_BM = 128;                          // sorted rows per tile
-constexpr int F8_BP = 128;                          // weight rows per tile
 constexpr int F8_BK = 128;                          // k (bytes = elements) per stage
 constexpr int F8_STAGES = 2;
-constexpr int F8_NW = 4;
-constexpr int F8_NT = 64 * F8_NW;
 constexpr int F8_CPR = F8_BK / 16;                  // 16-byte chunks per LDS row
 constexpr int F8_RPI = 1024 / F8_BK;                // rows one wave-wide 1 KB load fills
-constexpr int F8_A_INST = F8_BM / F8_RPI / F8_NW;   // load instructions per wave per stage
-constexpr int F8_B_INST = F8_BP / F8_RPI / F8_NW;
-constexpr int F8_STAGE_BYTES = (F8_BM + F8_BP) * F8_BK;
 constexpr int kMaxE8 = 256;
-static_assert(F8_A_INST * F8_NW * F8_RPI == F8_BM && F8_B_INST * F8_NW * F8_RPI == F8_BP, "load cover");
+
+// A tile of BM sorted rows x a BM-row weight panel, NW waves in a (NW/2) x 2 grid; each wave
+// owns 64 rows (two 32-row blocks) x BM/2 panel rows (NJ 32-wide blocks).
+template <int BM, int NW>
+struct F8Cfg {
+    static constexpr int NT = 64 * NW;
+    static constexpr int BP = BM;
+    static constexpr int WAVES_M = NW / 2;
+    static constexpr int WM = BM / WAVES_M;
+    static constexpr int NJ = BP / 2 / 32;
+    static constexpr int A_INST = BM / F8_RPI / NW;  // load instructions per wave per stage
+    static constexpr int B_INST = BP / F8_RPI / NW;
+    static constexpr int STAGE_BYTES = (BM + BP) * F8_BK;
+    static_assert(WM == 64, "two 32-row A blocks per wave");
+    static_assert(A_INST * NW * F8_RPI == BM && B_INST * NW * F8_RPI == BP, "load cover");
+};
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
@@ -100,22 +108,19 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t*
 }
 
 // ------------------------------------------------------------------ grouped GEMM
-template <bool GATE_UP>
-__global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __restrict__ A,
-                                                            const float* __restrict__ a_scale,
-                                                            const uint8_t* __restrict__ W0,
-                                                            const float* __restrict__ ws0,
-                                                            const uint8_t* __restrict__ W1,
-                                                            const float* __restrict__ ws1, uint16_t* __restrict__ C,
-                                                            const int32_t* __restrict__ sorted_ids,
-                                                            const int32_t* __restrict__ offsets, int P, int top_k,
-                                                            int E, int N, int K, int max_pad, int m_bound,
-                                                            int n_tiles) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_STAGES * F8_STAGE_BYTES];
-    __shared__ int s_scan[F8_NW];
+template <bool GATE_UP, int BM, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ a_scale, const uint8_t* __restrict__ W0,
+    const float* __restrict__ ws0, const uint8_t* __restrict__ W1, const float* __restrict__ ws1,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ offsets, int P,
+    int top_k, int E, int N, int K, int max_pad, int m_bound, int n_tiles) {
+    using F = F8Cfg<BM, NW>;
+    constexpr int BP = F::BP, NJ = F::NJ;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_STAGES * F::STAGE_BYTES];
+    __shared__ int s_scan[NW];
     __shared__ int s_lo[kMaxE8], s_hi[kMaxE8], s_tb[kMaxE8 + 1];
-    __shared__ int s_row[F8_BM];
-    __shared__ float s_as[F8_BM];
+    __shared__ int s_row[BM];
+    __shared__ float s_as[BM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations are scalar
 
@@ -126,8 +131,8 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
             lo = min(max(offsets[tid], 0), max_pad);
             hi = min(max(offsets[tid + 1], lo), max_pad);
         }
-        const int nt_e = (hi - lo + F8_BM - 1) / F8_BM;
-        const int incl = block_inclusive_scan<F8_NW>(nt_e, s_scan, (E + 63) / 64);
+        const int nt_e = (hi - lo + BM - 1) / BM;
+        const int incl = block_inclusive_scan<NW>(nt_e, s_scan, (E + 63) / 64);
         if (tid < E) { s_lo[tid] = lo; s_hi[tid] = hi; s_tb[tid + 1] = incl; }
         if (tid == 0) s_tb[0] = 0;
         __syncthreads();
@@ -142,13 +147,13 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
         if (s_tb[mid] <= m_t) lo_e = mid; else hi_e = mid - 1;
     }
     const int e = __builtin_amdgcn_readfirstlane(lo_e);
-    const int r0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (m_t - s_tb[e]) * F8_BM);
-    const int r_end = __builtin_amdgcn_readfirstlane(min(r0 + F8_BM, s_hi[e]));
-    constexpr int NCOL = GATE_UP ? F8_BP / 2 : F8_BP;  // output columns per tile
+    const int r0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (m_t - s_tb[e]) * BM);
+    const int r_end = __builtin_amdgcn_readfirstlane(min(r0 + BM, s_hi[e]));
+    constexpr int NCOL = GATE_UP ? BP / 2 : BP;  // output columns per tile
     const int n0 = n_t * NCOL;
 
     // ---- the tile's A rows (token rows for gate/up, sorted rows for down) and their scales
-    if (tid < F8_BM) {
+    if (tid < BM) {
         const int r = r0 + tid;
         int src = -1;
         float sc = 0.f;
@@ -169,12 +174,12 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
     // row lrow, which holds logical chunk swz8(row, pc).  A row without a token reads a row that
     // is always in bounds (token 0, or the tile's first sorted row); its results are never stored.
     const int lrow = lane / F8_CPR, pc = lane % F8_CPR;
-    const uint8_t* a_src[F8_A_INST];
-    const uint8_t* b_src[F8_B_INST];
-    int a_kc[F8_A_INST], b_kc[F8_B_INST];
+    const uint8_t* a_src[F::A_INST];
+    const uint8_t* b_src[F::B_INST];
+    int a_kc[F::A_INST], b_kc[F::B_INST];
 #pragma unroll
-    for (int q = 0; q < F8_A_INST; ++q) {
-        const int row = (wave * F8_A_INST + q) * F8_RPI + lrow;
+    for (int q = 0; q < F::A_INST; ++q) {
+        const int row = (wave * F::A_INST + q) * F8_RPI + lrow;
         const int kc = swz8(row, pc);
         const int src = s_row[row];
         const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0);
@@ -184,12 +189,12 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
     const uint8_t* wb0 = W0 + static_cast<size_t>(e) * N * K;
     const uint8_t* wb1 = GATE_UP ? W1 + static_cast<size_t>(e) * N * K : wb0;
 #pragma unroll
-    for (int q = 0; q < F8_B_INST; ++q) {
-        const int row = (wave * F8_B_INST + q) * F8_RPI + lrow;
+    for (int q = 0; q < F::B_INST; ++q) {
+        const int row = (wave * F::B_INST + q) * F8_RPI + lrow;
         const int kc = swz8(row, pc);
-        int n = GATE_UP ? n0 + (row & (F8_BP / 2 - 1)) : n0 + row;
+        int n = GATE_UP ? n0 + (row & (BP / 2 - 1)) : n0 + row;
         n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
-        const uint8_t* base = (GATE_UP && row >= F8_BP / 2) ? wb1 : wb0;
+        const uint8_t* base = (GATE_UP && row >= BP / 2) ? wb1 : wb0;
         b_src[q] = base + static_cast<size_t>(n) * K + kc * 16;
         b_kc[q] = kc;
     }
@@ -197,39 +202,48 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)smem)));
     auto issue = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * F8_BK;
-        const uint32_t sb = lds0 + static_cast<uint32_t>(t % F8_STAGES) * F8_STAGE_BYTES;
+        const uint32_t sb = lds0 + static_cast<uint32_t>(t % F8_STAGES) * F::STAGE_BYTES;
         const bool full = k0 + F8_BK <= K;
 #pragma unroll
-        for (int q = 0; q < F8_A_INST; ++q) {
+        for (int q = 0; q < F::A_INST; ++q) {
             const void* g = a_src[q] + k0;
             if (!full && k0 + a_kc[q] * 16 >= K) g = kZeroChunk;
-            dma16_f8(g, sb + (wave * F8_A_INST + q) * 1024);
+            dma16_f8(g, sb + (wave * F::A_INST + q) * 1024);
         }
 #pragma unroll
-        for (int q = 0; q < F8_B_INST; ++q) {
+        for (int q = 0; q < F::B_INST; ++q) {
             const void* g = b_src[q] + k0;
             if (!full && k0 + b_kc[q] * 16 >= K) g = kZeroChunk;
-            dma16_f8(g, sb + F8_BM * F8_BK + (wave * F8_B_INST + q) * 1024);
+            dma16_f8(g, sb + BM * F8_BK + (wave * F::B_INST + q) * 1024);
         }
     };
 
     // ---- main loop
     const int wm = wave >> 1, wn = wave & 1;
     const int fr = lane & 31, fh = lane >> 5;  // fragment row / column, 32-byte k half
-    int a_row[2], b_row[2];
+    int a_row[2], b_row[NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i) a_row[i] = wm * 64 + i * 32 + fr;
+    // panel rows of this wave's column blocks: down, BP/2 consecutive rows; gate/up, BP/4 gate rows
+    // (blocks 0 .. NJ/2-1) and the up rows of the same columns (blocks NJ/2 ..)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        b_row[j] = F8_BM + (GATE_UP ? (j == 0 ? wn * 32 : F8_BP / 2 + wn * 32) : wn * 64 + j * 32) + fr;
-    f32x16 acc[2][2];
+    for (int j = 0; j < NJ; ++j)
+        b_row[j] = BM + (GATE_UP ? (j < NJ / 2 ? wn * (BP / 4) + j * 32 : BP / 2 + wn * (BP / 4) + (j - NJ / 2) * 32)
+                                 : wn * (BP / 2) + j * 32) + fr;
+    f32x16 acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+    auto frag = [&](const uint8_t* st, int row, int c0) __attribute__((always_inline)) {
+        const uint8_t* rp = st + row * F8_BK;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + swz8(row, c0) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + swz8(row, c0 + 1) * 16);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
     const int nk = (K + F8_BK - 1) / F8_BK;
     issue(0);
     for (int s = 0; s < nk; ++s) {
@@ -239,32 +253,20 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         if (s + 1 < nk) issue(s + 1);
-        const uint8_t* st = smem + (s % F8_STAGES) * F8_STAGE_BYTES;
+        const uint8_t* st = smem + (s % F8_STAGES) * F::STAGE_BYTES;
 #pragma unroll
         for (int ks = 0; ks < F8_BK / 64; ++ks) {
             const int c0 = ks * 4 + fh * 2;
-            i32x8 fa[2], fb[2];
+            i32x8 fa[2], fb[NJ];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint8_t* rp = st + a_row[i] * F8_BK;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + swz8(a_row[i], c0) * 16);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + swz8(a_row[i], c0 + 1) * 16);
-                fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
-                              (int)hi[3]};
-            }
+            for (int i = 0; i < 2; ++i) fa[i] = frag(st, a_row[i], c0);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint8_t* rp = st + b_row[j] * F8_BK;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + swz8(b_row[j], c0) * 16);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + swz8(b_row[j], c0 + 1) * 16);
-                fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
-                              (int)hi[3]};
-            }
+            for (int j = 0; j < NJ; ++j) fb[j] = frag(st, b_row[j], c0);
             // format 0 (E4M3) for both operands; block scales 127 (2^0): plain fp8 products
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
                                                                                127, 0, 127);
         }
@@ -273,16 +275,16 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
     // ---- epilogue: scales, SiLU * up for gate/up; neighbour lanes (columns c, c+1) swap one
     // value so that each lane stores two adjacent bf16 columns of one row as 4 bytes
     const bool odd = (lane & 1) != 0;
-    constexpr int NJ = GATE_UP ? 1 : 2;
-    float wsc[2];
-    int colj[2];
+    constexpr int NO = GATE_UP ? NJ / 2 : NJ;  // output column blocks of this wave
+    float wsc[NO], wsu[NO];
+    int colj[NO];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        colj[j] = n0 + (GATE_UP ? wn * 32 : wn * 64 + j * 32) + fr;  // this lane's column
+    for (int j = 0; j < NO; ++j) {
+        colj[j] = n0 + (GATE_UP ? wn * (BP / 4) : wn * (BP / 2)) + j * 32 + fr;  // this lane's column
         const int cc = min(colj[j], N - 1);
         wsc[j] = ws0[static_cast<size_t>(e) * N + cc];
+        wsu[j] = GATE_UP ? ws1[static_cast<size_t>(e) * N + cc] : 0.f;
     }
-    const float wsu = GATE_UP ? ws1[static_cast<size_t>(e) * N + min(colj[0], N - 1)] : 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -293,11 +295,11 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
             const bool ok = s_row[row_l] >= 0;
             uint16_t* crow = C + static_cast<size_t>(r0 + row_l) * N;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+            for (int j = 0; j < NO; ++j) {
                 float h0, h1;  // values v (row rl) and v+1 (row rl+1) of this lane's column
                 if (GATE_UP) {
-                    h0 = silu_mul(acc[i][0][v] * sa0 * wsc[0], acc[i][1][v] * sa0 * wsu);
-                    h1 = silu_mul(acc[i][0][v + 1] * sa1 * wsc[0], acc[i][1][v + 1] * sa1 * wsu);
+                    h0 = silu_mul(acc[i][j][v] * sa0 * wsc[j], acc[i][j + NO][v] * sa0 * wsu[j]);
+                    h1 = silu_mul(acc[i][j][v + 1] * sa1 * wsc[j], acc[i][j + NO][v + 1] * sa1 * wsu[j]);
                 } else {
                     h0 = acc[i][j][v] * sa0 * wsc[j];
                     h1 = acc[i][j][v + 1] * sa1 * wsc[j];
@@ -310,6 +312,19 @@ __global__ __launch_bounds__(F8_NT, 2) void gemm_fp8_kernel(const uint8_t* __res
                 if (ok && col < N) *reinterpret_cast<uint32_t*>(crow + col) = pr;
             }
         }
+}
+
+template <bool GATE_UP, int BM, int NW>
+void launch_fp8_cfg(const uint8_t* a, const float* a_scale, const uint8_t* w0, const float* ws0, const uint8_t* w1,
+                    const float* ws1, uint16_t* c, const int32_t* sorted_ids, const int32_t* offsets, int P,
+                    int top_k, int E, int N, int K, int max_pad, hipStream_t s) {
+    const int ncol = GATE_UP ? BM / 2 : BM;
+    const int n_tiles = (N + ncol - 1) / ncol;
+    const int m_bound = (max_pad + BM - 1) / BM + E;  // row tiles of any routing, at most
+    const long long grid = static_cast<long long>(m_bound) * n_tiles;
+    if (grid <= 0) return;
+    gemm_fp8_kernel<GATE_UP, BM, NW><<<static_cast<unsigned>(grid), 64 * NW, 0, s>>>(
+        a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound, n_tiles);
 }
 
 }  // namespace
@@ -325,18 +340,16 @@ hipError_t launch_gemm_fp8(bool gate_up, const uint8_t* a, const float* a_scale,
                            const float* ws0, const uint8_t* w1, const float* ws1, uint16_t* c,
                            const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
                            int K, int max_pad, hipStream_t s) {
-    const int ncol = gate_up ? F8_BP / 2 : F8_BP;
-    const int n_tiles = (N + ncol - 1) / ncol;
-    const int m_bound = (max_pad + F8_BM - 1) / F8_BM + E;  // row tiles of any routing, at most
-    const long long grid = static_cast<long long>(m_bound) * n_tiles;
-    if (grid <= 0) return hipSuccess;
-    if (gate_up)
-        gemm_fp8_kernel<true><<<static_cast<unsigned>(grid), F8_NT, 0, s>>>(
-            a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound, n_tiles);
-    else
-        gemm_fp8_kernel<false><<<static_cast<unsigned>(grid), F8_NT, 0, s>>>(
-            a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound,
-            n_tiles);
+    // 256-row tiles (8 waves, two per SIMD) when experts average at least 128 rows; 128-row
+    // tiles (4 waves) for fewer
+    const bool big = static_cast<long long>(P) >= 128LL * E;
+    if (gate_up) {
+        if (big) launch_fp8_cfg<true, 256, 8>(a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+        else launch_fp8_cfg<true, 128, 4>(a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+    } else {
+        if (big) launch_fp8_cfg<false, 256, 8>(a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+        else launch_fp8_cfg<false, 128, 4>(a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+    }
     return hipGetLastError();
 }
 

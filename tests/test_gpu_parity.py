@@ -394,6 +394,8 @@ FP8_SMALL = {
     "fp8_small": MoeConfig("fp8_small", T=300, H=528, I=912, E=8, top_k=2, block_size=64, weights="fp8", seed=51),
     "fp8_skewed": MoeConfig("fp8_skewed", T=500, H=256, I=384, E=32, top_k=4, block_size=32, weights="fp8",
                             logits="zipf", seed=52),
+    # >= 128 rows per expert on average: 256-row tiles with 8 waves
+    "fp8_big": MoeConfig("fp8_big", T=1024, H=528, I=912, E=4, top_k=2, block_size=64, weights="fp8", seed=53),
 }
 
 
