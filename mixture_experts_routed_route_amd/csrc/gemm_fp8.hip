@@ -30,6 +30,9 @@ constexpr int F8_STAGES = 2;
 constexpr int F8_CPR = F8_BK / 16;                  // 16-byte chunks per LDS row
 constexpr int F8_RPI = 1024 / F8_BK;                // rows one wave-wide 1 KB load fills
 constexpr int kMaxE8 = 256;
+#ifndef MOE_FP8_ASYM
+#define MOE_FP8_ASYM 1  // 8 waves: waves 0-3 issue all of a stage's loads
+#endif
 
 // A tile of BM sorted rows x a BM-row weight panel, NW waves in a (NW/2) x 2 grid; each wave
 // owns 64 rows (two 32-row blocks) x BM/2 panel rows (NJ 32-wide blocks).
@@ -138,9 +141,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
         __syncthreads();
     }
     const int m_real = __builtin_amdgcn_readfirstlane(s_tb[E]);
-    const int n_t = blockIdx.x / m_bound;
-    const int m_t = blockIdx.x - n_t * m_bound;
-    if (m_t >= m_real || n_t >= n_tiles) return;  // uniform over the workgroup
+    // Workgroup ids go round-robin over the 8 XCDs: XCD x takes the contiguous range
+    // [x*T/8, (x+1)*T/8) of the T real tiles (row tiles fastest), so the workgroups an XCD runs
+    // together share weight panels in its L2.  The grid (a multiple of 8) bounds T from above.
+    const int T = m_real * n_tiles;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int L = static_cast<int>(static_cast<long long>(T) * xcd / 8) + slot;
+    if (L >= static_cast<int>(static_cast<long long>(T) * (xcd + 1) / 8)) return;  // uniform
+    const int n_t = L / m_real;
+    const int m_t = L - n_t * m_real;
     int lo_e = 0, hi_e = E - 1;                   // largest expert whose first row tile is <= m_t
     while (lo_e < hi_e) {
         const int mid = (lo_e + hi_e + 1) >> 1;
@@ -174,47 +183,62 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
     // row lrow, which holds logical chunk swz8(row, pc).  A row without a token reads a row that
     // is always in bounds (token 0, or the tile's first sorted row); its results are never stored.
     const int lrow = lane / F8_CPR, pc = lane % F8_CPR;
-    const uint8_t* a_src[F::A_INST];
-    const uint8_t* b_src[F::B_INST];
-    int a_kc[F::A_INST], b_kc[F::B_INST];
-#pragma unroll
-    for (int q = 0; q < F::A_INST; ++q) {
-        const int row = (wave * F::A_INST + q) * F8_RPI + lrow;
-        const int kc = swz8(row, pc);
-        const int src = s_row[row];
-        const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0);
-        a_src[q] = A + static_cast<size_t>(srow) * K + kc * 16;
-        a_kc[q] = kc;
-    }
+    // With 8 waves (two per SIMD), waves 0-3 issue the loads of their own row blocks and of
+    // waves 4-7's, which issue none: while an issuing wave stalls on the address unit, the other
+    // wave of its SIMD issues MFMAs.  Block j of an issuing wave is that of wave + j * NW/2.
+    constexpr bool ASYM = MOE_FP8_ASYM != 0 && NW == 8;
+    constexpr int NBLK = ASYM ? 2 : 1;
+    const bool issuer = !ASYM || wave < NW / 2;
+    const uint8_t* a_src[NBLK][F::A_INST];
+    const uint8_t* b_src[NBLK][F::B_INST];
+    int a_kc[NBLK][F::A_INST], b_kc[NBLK][F::B_INST];
     const uint8_t* wb0 = W0 + static_cast<size_t>(e) * N * K;
     const uint8_t* wb1 = GATE_UP ? W1 + static_cast<size_t>(e) * N * K : wb0;
 #pragma unroll
-    for (int q = 0; q < F::B_INST; ++q) {
-        const int row = (wave * F::B_INST + q) * F8_RPI + lrow;
-        const int kc = swz8(row, pc);
-        int n = GATE_UP ? n0 + (row & (BP / 2 - 1)) : n0 + row;
-        n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
-        const uint8_t* base = (GATE_UP && row >= BP / 2) ? wb1 : wb0;
-        b_src[q] = base + static_cast<size_t>(n) * K + kc * 16;
-        b_kc[q] = kc;
+    for (int j = 0; j < NBLK; ++j) {
+        const int bw = wave + j * (NW / 2);
+#pragma unroll
+        for (int q = 0; q < F::A_INST; ++q) {
+            const int row = (bw * F::A_INST + q) * F8_RPI + lrow;
+            const int kc = swz8(row, pc);
+            const int src = s_row[row];
+            const int srow = src >= 0 ? src : (GATE_UP ? 0 : r0);
+            a_src[j][q] = A + static_cast<size_t>(srow) * K + kc * 16;
+            a_kc[j][q] = kc;
+        }
+#pragma unroll
+        for (int q = 0; q < F::B_INST; ++q) {
+            const int row = (bw * F::B_INST + q) * F8_RPI + lrow;
+            const int kc = swz8(row, pc);
+            int n = GATE_UP ? n0 + (row & (BP / 2 - 1)) : n0 + row;
+            n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
+            const uint8_t* base = (GATE_UP && row >= BP / 2) ? wb1 : wb0;
+            b_src[j][q] = base + static_cast<size_t>(n) * K + kc * 16;
+            b_kc[j][q] = kc;
+        }
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)smem)));
     auto issue = [&](int t) __attribute__((always_inline)) {
+        if (!issuer) return;
         const int k0 = t * F8_BK;
         const uint32_t sb = lds0 + static_cast<uint32_t>(t % F8_STAGES) * F::STAGE_BYTES;
         const bool full = k0 + F8_BK <= K;
 #pragma unroll
-        for (int q = 0; q < F::A_INST; ++q) {
-            const void* g = a_src[q] + k0;
-            if (!full && k0 + a_kc[q] * 16 >= K) g = kZeroChunk;
-            dma16_f8(g, sb + (wave * F::A_INST + q) * 1024);
-        }
+        for (int j = 0; j < NBLK; ++j) {
+            const int bw = wave + j * (NW / 2);
 #pragma unroll
-        for (int q = 0; q < F::B_INST; ++q) {
-            const void* g = b_src[q] + k0;
-            if (!full && k0 + b_kc[q] * 16 >= K) g = kZeroChunk;
-            dma16_f8(g, sb + BM * F8_BK + (wave * F::B_INST + q) * 1024);
+            for (int q = 0; q < F::B_INST; ++q) {
+                const void* g = b_src[j][q] + k0;
+                if (!full && k0 + b_kc[j][q] * 16 >= K) g = kZeroChunk;
+                dma16_f8(g, sb + BM * F8_BK + (bw * F::B_INST + q) * 1024);
+            }
+#pragma unroll
+            for (int q = 0; q < F::A_INST; ++q) {
+                const void* g = a_src[j][q] + k0;
+                if (!full && k0 + a_kc[j][q] * 16 >= K) g = kZeroChunk;
+                dma16_f8(g, sb + (bw * F::A_INST + q) * 1024);
+            }
         }
     };
 
@@ -321,7 +345,8 @@ void launch_fp8_cfg(const uint8_t* a, const float* a_scale, const uint8_t* w0, c
     const int ncol = GATE_UP ? BM / 2 : BM;
     const int n_tiles = (N + ncol - 1) / ncol;
     const int m_bound = (max_pad + BM - 1) / BM + E;  // row tiles of any routing, at most
-    const long long grid = static_cast<long long>(m_bound) * n_tiles;
+    // each XCD's share of the tiles, rounded up, times 8
+    const long long grid = (static_cast<long long>(m_bound) * n_tiles + 7) / 8 * 8 + 8;
     if (grid <= 0) return;
     gemm_fp8_kernel<GATE_UP, BM, NW><<<static_cast<unsigned>(grid), 64 * NW, 0, s>>>(
         a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound, n_tiles);
