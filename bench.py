@@ -142,6 +142,8 @@ def main():
                          "per-kernel figures then come from an eager pass of the same steps")
     ap.add_argument("--fold", default="auto", choices=["auto", "grouped", "gather"],
                     help="LoRA fold over the sorted rows or slot by slot (auto: by the padding share)")
+    ap.add_argument("--gate-up-lora", default="fused", choices=["fused", "unfused"],
+                    help="gate/up LoRA folded in the gate/up GEMM's epilogue, or the page's unfused order")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -159,7 +161,7 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] generating {cfg.name} inputs")
     d = make_inputs(cfg)
-    layer = m.MoeLayer.from_arrays(d, dev, fold=args.fold)
+    layer = m.MoeLayer.from_arrays(d, dev, fold=args.fold, gate_up_fused=args.gate_up_lora == "fused")
     b = layer.plan(cfg.T, dev)
     wbytes = sum(expert_weight_bytes(cfg, op) for op in ("gate_up", "down")) * cfg.E
     rot = args.rotate or max(1, min(4, int(-(-(1 << 30) // wbytes))))
@@ -226,7 +228,9 @@ def main():
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if layer.lora is not None else None
-    gu_what = ("gate/up stage: 2 gathered GEMMs, 2 LoRA folds, SiLU*up" if layer.gate_up_lora
+    gu_what = ("gemm_bf16_kernel<gate_up> with the gate/up LoRA epilogue (+ 2 shrinks)"
+               if layer.gate_up_lora and layer.gate_up_fused
+               else "gate/up stage: 2 gathered GEMMs, 2 LoRA folds, SiLU*up" if layer.gate_up_lora
                else "gate/up stage: x quantisation + gemm_fp8_kernel<gate_up>" if cfg.weights == "fp8"
                else ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>")
     peak_mfma = PEAK_FP8_TFLOPS if cfg.weights == "fp8" else PEAK_BF16_TFLOPS
@@ -285,7 +289,7 @@ def main():
                    "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
                    "weights": cfg.weights, "lora_rank": cfg.lora_rank,
                    **({"lora_fold": layer.fold_mode(b)} if layer.lora is not None else {}),
-                   **({"lora_gate_up": True} if layer.gate_up_lora else {}),
+                   **({"lora_gate_up": "fused" if layer.gate_up_fused else "unfused"} if layer.gate_up_lora else {}),
                    "launch": "hip_graph" if args.graph else "eager"},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_mfma_peak": gemm_tflops / peak_mfma,

@@ -271,6 +271,33 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                          int64_t row_offset, int64_t row_end, int64_t max_pad, int32_t x_gather,
                          moe_stream stream);
 
+/* The gate/up LoRA fused into the gate/up GEMM (bf16 weights): the same
+ * result as MOE_OP_GATHER for gate and up, moe_lora_fold with x_gather = 1 on
+ * each, and moe_silu_mul, in one GEMM whose epilogue folds a rank-r product
+ * (atlas moe_lora_grouped.rs: the gate/up fold over token-major x on the sorted
+ * BF16 expert_gate_out / expert_up_out before SiLU).  For each real sorted row
+ * r of expert e (token t = sorted_ids[r] / top_k):
+ *   g = bf16(x[t] Wg[e]^T); if the gate tables adapt e (and row_adapter[t] >= 0
+ *   or no map): g = bf16(g + s_gate[e] * bf16(bf16(x[t] A_gate[e]^T) B_gate[e]^T));
+ *   u likewise with the up tables; hs[r] = bf16(silu(g) * u).
+ *   x, w_gate, w_up, hs, sorted ids ... max_pad, workspace: as moe_grouped_gemm
+ *   with MOE_OP_GATE_UP_SILU (n = intermediate, k = hidden)
+ *   a_*, b_*, s_*, n_tab_*: tables as for moe_lora_fold (A [max_rank, k],
+ *   B [n, max_rank]); n_tab 0 = no tables for that projection
+ *   row_adapter  i32 [num_pairs/top_k] or NULL
+ *   xa           bf16 [2, max_pad, max_rank] scratch (the gate and up shrinks)
+ * Launches the two shrinks and the GEMM.  MOE_EUNSUPPORTED for int4 weights.
+ * max_rank in {32, 64, 96, 128}. */
+moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_gate, const moe_weight* w_up,
+                                         uint16_t* hs, const int32_t* sorted_ids, const int32_t* expert_offsets,
+                                         int64_t num_pairs, int32_t top_k, int32_t num_experts, int32_t n, int32_t k,
+                                         int32_t block_size, int64_t max_pad, const uint64_t* a_gate,
+                                         const uint64_t* b_gate, const float* s_gate, int32_t n_tab_gate,
+                                         const uint64_t* a_up, const uint64_t* b_up, const float* s_up,
+                                         int32_t n_tab_up, int32_t max_rank, const int32_t* row_adapter,
+                                         uint16_t* xa, void* workspace, int64_t workspace_bytes,
+                                         moe_stream stream);
+
 /* SiLU(gate) * up of the gate/up LoRA path (atlas moe_lora_grouped.rs,
  * moe_lora_gather_bgmv: the caller's moe_silu_mul writes the BF16 activations
  * the down projection and its fold read).

@@ -351,6 +351,91 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
                                                static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_gate, const moe_weight* w_up,
+                                         uint16_t* hs, const int32_t* sorted_ids, const int32_t* expert_offsets,
+                                         int64_t num_pairs, int32_t top_k, int32_t num_experts, int32_t n, int32_t k,
+                                         int32_t block_size, int64_t max_pad, const uint64_t* a_gate,
+                                         const uint64_t* b_gate, const float* s_gate, int32_t n_tab_gate,
+                                         const uint64_t* a_up, const uint64_t* b_up, const float* s_up,
+                                         int32_t n_tab_up, int32_t max_rank, const int32_t* row_adapter,
+                                         uint16_t* xa, void* workspace, int64_t workspace_bytes,
+                                         moe_stream stream) {
+    const char* who = "moe_grouped_gemm_gate_up_lora";
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
+    REQUIRE(top_k >= 1 && num_pairs % top_k == 0, "%s: num_pairs %lld is not a multiple of top_k %d", who,
+            static_cast<long long>(num_pairs), top_k);
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    REQUIRE(n >= 8 && n % 8 == 0, "%s: n %d must be a positive multiple of 8", who, n);
+    REQUIRE(k >= 8 && k % 8 == 0, "%s: k %d must be a positive multiple of 8", who, k);
+    REQUIRE(max_pad >= max_padded(num_pairs, num_experts, block_size) && max_pad % block_size == 0 &&
+                max_pad < INT32_MAX,
+            "%s: max_pad %lld must be >= %lld and a multiple of block_size", who, static_cast<long long>(max_pad),
+            static_cast<long long>(max_padded(num_pairs, num_experts, block_size)));
+    REQUIRE(w_gate != nullptr && w_up != nullptr, "%s: w_gate and w_up are required", who);
+    if (w_gate->type != MOE_W_BF16 || w_up->type != MOE_W_BF16)
+        return fail(MOE_EUNSUPPORTED, "%s: the fused gate/up LoRA takes bf16 weights only", who);
+    REQUIRE(max_rank >= 32 && max_rank <= 128 && max_rank % 32 == 0, "%s: max_rank %d not in {32,64,96,128}", who,
+            max_rank);
+    REQUIRE(n_tab_gate >= 0 && n_tab_gate <= num_experts && n_tab_up >= 0 && n_tab_up <= num_experts,
+            "%s: table lengths must be in [0, num_experts=%d]", who, num_experts);
+    if (workspace != nullptr) {
+        const int64_t need = moe_grouped_gemm_workspace_bytes();
+        REQUIRE_PTR(who, workspace);
+        REQUIRE(workspace_bytes >= need, "%s: workspace_bytes %lld < required %lld", who,
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+    }
+    if (num_pairs == 0) return ok();
+    REQUIRE_PTR(who, x);
+    REQUIRE_PTR(who, hs);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, w_gate->data);
+    REQUIRE_PTR(who, w_up->data);
+    REQUIRE_PTR(who, xa);
+    if (n_tab_gate > 0) {
+        REQUIRE_PTR(who, a_gate);
+        REQUIRE_PTR(who, b_gate);
+        REQUIRE_PTR(who, s_gate);
+    }
+    if (n_tab_up > 0) {
+        REQUIRE_PTR(who, a_up);
+        REQUIRE_PTR(who, b_up);
+        REQUIRE_PTR(who, s_up);
+    }
+    if (row_adapter) REQUIRE_PTR(who, row_adapter);
+    const int64_t a_rows = num_pairs / top_k;
+    if (a_rows * k * 2 > INT64_C(0xffffffff) || static_cast<int64_t>(n) * k * 2 > INT64_C(0xffffffff))
+        return fail(MOE_EUNSUPPORTED, "%s: x or an expert matrix exceeds 4 GiB", who);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int P = static_cast<int>(num_pairs);
+    uint16_t* xa_up = xa + max_pad * max_rank;
+    hipError_t err = moe::launch_lora_shrink(x, a_gate, b_gate, n_tab_gate, k, max_rank, expert_offsets, num_experts,
+                                             sorted_ids, P, top_k, row_adapter, xa, 0, max_pad, 1, s);
+    if (err == hipSuccess)
+        err = moe::launch_lora_shrink(x, a_up, b_up, n_tab_up, k, max_rank, expert_offsets, num_experts, sorted_ids,
+                                      P, top_k, row_adapter, xa_up, 0, max_pad, 1, s);
+    if (err != hipSuccess) return launched(who, err);
+    moe::GateUpLora lora{};
+    lora.xa[0] = xa;
+    lora.xa[1] = xa_up;
+    lora.a_tab[0] = a_gate;
+    lora.a_tab[1] = a_up;
+    lora.b_tab[0] = b_gate;
+    lora.b_tab[1] = b_up;
+    lora.s_tab[0] = s_gate;
+    lora.s_tab[1] = s_up;
+    lora.n_tab[0] = n_tab_gate;
+    lora.n_tab[1] = n_tab_up;
+    lora.rank = max_rank;
+    lora.row_adapter = row_adapter;
+    return launched(who, moe::launch_gemm_bf16(moe::kOpGateUpSilu, x, static_cast<const uint16_t*>(w_gate->data),
+                                               static_cast<const uint16_t*>(w_up->data), hs, sorted_ids,
+                                               expert_offsets, P, top_k, num_experts, n, k,
+                                               static_cast<int>(max_pad), workspace, workspace_bytes, s, &lora));
+}
+
 moe_status moe_quantize_fp8(const uint16_t* x, int64_t rows, int32_t k, const int32_t* sorted_ids,
                             int64_t num_pairs, uint8_t* q, float* scale, moe_stream stream) {
     const char* who = "moe_quantize_fp8";

@@ -155,7 +155,7 @@ __device__ __forceinline__ void decode_tile(int L, int gm, int m_real, int n_til
     m_t = band * gm + (in_band - n_t * gm_b);
 }
 
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, bool LORA = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W0,
                                                           const uint16_t* __restrict__ W1,
@@ -164,7 +164,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                                                           const int32_t* __restrict__ offsets, int P, int top_k,
                                                           int E, int N, int K, int max_pad, int n_tiles,
                                                           float* __restrict__ sk_part, int32_t* __restrict__ sk_cnt,
-                                                          int sk_on, int a_tok) {
+                                                          int sk_on, int a_tok, GateUpLora lora) {
+    static_assert(!LORA || GATE_UP, "the LoRA epilogue is the gate/up one");
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
     constexpr int NT = F::NT;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
@@ -599,6 +600,57 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
             sb -= nseg;
         }
 
+        // ---- gate/up LoRA (the page's order: bf16 gate and up outputs, each folded, then SiLU * up):
+        // every accumulator becomes a bf16 value, bf16(bf16(acc) + scale * bf16(xa . B_e^T)) where
+        // the row is folded.  The delta blocks are 32x32x16 MFMAs over the rank, with the xa and
+        // B_e fragments read straight from memory.
+        if constexpr (LORA) {
+            if (store) {
+                auto bf16r = [](float x) __attribute__((always_inline)) {
+                    return __uint_as_float(static_cast<uint32_t>(f32_to_bf16(x)) << 16);
+                };
+#pragma unroll
+                for (int i = 0; i < F::FI; ++i) {
+                    // this lane's xa row (clamped: rows past the span are computed and never stored)
+                    const int rowf = min(r0 + wm * F::WM + i * 32 + fr, max_pad - 1);
+#pragma unroll
+                    for (int pj = 0; pj < 2; ++pj) {  // 0: gate (blocks 0, 1), 1: up (blocks 2, 3)
+                        const bool adapted = e < lora.n_tab[pj] && lora.a_tab[pj][e] != 0 && lora.b_tab[pj][e] != 0;
+                        if (!adapted) {
+#pragma unroll
+                            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) acc[i][pj * 2 + jj][v] = bf16r(acc[i][pj * 2 + jj][v]);
+                            continue;
+                        }
+                        const uint16_t* xr = lora.xa[pj] + static_cast<size_t>(rowf) * lora.rank + fc * 8;
+                        const uint16_t* Be = reinterpret_cast<const uint16_t*>(lora.b_tab[pj][e]);
+                        const float sc = lora.s_tab[pj][e];
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {  // one 32x32 delta block at a time
+                            const int col = min(n0 + wn * 64 + jj * 32 + fr, N - 1);
+                            const uint16_t* br = Be + static_cast<size_t>(col) * lora.rank + fc * 8;
+                            f32x16 d;
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) d[v] = 0.f;
+                            for (int k0 = 0; k0 < lora.rank; k0 += 16)
+                                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(xr + k0),
+                                                                            *reinterpret_cast<const bf16x8*>(br + k0),
+                                                                            d, 0, 0, 0);
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) {
+                                const int rl = wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3);
+                                const int tok = s_row[buf][rl];
+                                const bool fold = tok >= 0 && (!lora.row_adapter || lora.row_adapter[tok] >= 0);
+                                const float g = bf16r(acc[i][pj * 2 + jj][v]);
+                                acc[i][pj * 2 + jj][v] = fold ? bf16r(fmaf(sc, bf16r(d[v]), g)) : g;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
         // ---- epilogue straight from the accumulators: neighbour lanes (columns c, c+1) swap one
         // value so that each lane stores two adjacent bf16 columns of one row as 4 bytes
         const bool odd = (lane & 1) != 0;
@@ -664,10 +716,11 @@ constexpr int64_t kSkPartBytes = 512LL * 2 * 64 * 4;    // largest partial: 512 
 constexpr int64_t kSkWorkspaceBytes = kSkCounterBytes + kSkMaxGrid * kSkPartBytes;
 static_assert(kSkMaxGrid * 4 <= kSkCounterBytes, "split-tail counters overflow their area");
 
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, bool LORA = false>
 hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                       const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
-                      int max_pad, void* ws, int64_t ws_bytes, int a_tok, hipStream_t s) {
+                      int max_pad, void* ws, int64_t ws_bytes, int a_tok, hipStream_t s,
+                      const GateUpLora& lora = GateUpLora{}) {
     using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
     static_assert(F::NT * F::FI * 64 * 4 <= kSkPartBytes, "partial accumulators larger than their workspace slot");
     const int n_tiles = (N + F::NCOL - 1) / F::NCOL;
@@ -691,8 +744,8 @@ hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1,
     }
     int32_t* cnt = sk ? static_cast<int32_t*>(ws) : nullptr;
     float* part = sk ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSkCounterBytes) : nullptr;
-    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW><<<static_cast<int>(grid), F::NT, 0, s>>>(
-        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0, a_tok);
+    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW, LORA><<<static_cast<int>(grid), F::NT, 0, s>>>(
+        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0, a_tok, lora);
     return hipGetLastError();
 }
 
@@ -702,10 +755,14 @@ int64_t gemm_bf16_workspace_bytes() { return kSkWorkspaceBytes; }
 
 hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
-                            int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
+                            int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s, const GateUpLora* lora) {
     // 256-row tiles (8 waves) when experts average at least MOE_GEMM_BIG_ROWS rows, where a 128-row
     // tiling would read most weight panels twice; 128-row tiles (4 waves) for fewer rows
     const bool big = static_cast<long long>(P) >= static_cast<long long>(MOE_GEMM_BIG_ROWS) * E;
+    if (op == kOpGateUpSilu && lora) {
+        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, true>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
+        return launch_cfg<true, 128, 64, 3, 4, true>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
+    }
     if (op == kOpGateUpSilu) {
         if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s);
         return launch_cfg<true, 128, 64, 3, 4>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s);

@@ -31,11 +31,26 @@ hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int 
 hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w, uint16_t* out, int T, int k,
                           int H, int64_t ys_rows, hipStream_t s);
 
-// gemm_bf16.hip (ws: optional split-tail workspace, zero-filled before first use; NULL = none)
+// LoRA of the gate and up projections folded in the bf16 gate/up GEMM's epilogue.  For each
+// projection p (0 gate, 1 up): xa[p] = bf16 shrink results [max_pad, rank] of the sorted rows, and
+// the expert tables (n_tab[p] == 0: no tables, the projection is only rounded to bf16).
+struct GateUpLora {
+    const uint16_t* xa[2];
+    const uint64_t* a_tab[2];
+    const uint64_t* b_tab[2];
+    const float* s_tab[2];
+    int n_tab[2];
+    int rank;
+    const int32_t* row_adapter;  // [tokens] (< 0: no fold) or NULL
+};
+
+// gemm_bf16.hip (ws: optional split-tail workspace, zero-filled before first use; NULL = none;
+// lora: gate/up op only, NULL = plain SiLU(gate) * up)
 int64_t gemm_bf16_workspace_bytes();
 hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
-                            int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s);
+                            int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s,
+                            const GateUpLora* lora = nullptr);
 
 // gemm_int4.hip
 hipError_t launch_gemm_int4(int op, const uint16_t* a, const int32_t* qw0, const uint16_t* sc0,
@@ -49,6 +64,11 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
                             const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
                             int x_gather, hipStream_t s);
+// the shrink alone: xa[r - row_offset] = bf16(x[row] A_e^T) for the folded rows of the window
+hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int k_in,
+                              int max_rank, const int32_t* offsets, int E, const int32_t* sorted_ids, int P,
+                              int top_k, const int32_t* row_adapter, uint16_t* xa, int64_t row_offset,
+                              int64_t row_end, int x_gather, hipStream_t s);
 // gemm_fp8.hip: per-row fp8 quantisation of bf16 rows (only real sorted rows with sorted_ids), and
 // the fp8 grouped GEMM (gate/up + SiLU, or down) with per-row and per-channel scales
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int K, const int32_t* sorted_ids, int P,

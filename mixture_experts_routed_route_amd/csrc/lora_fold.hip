@@ -421,6 +421,31 @@ __global__ __launch_bounds__(NT) void gather_expand_kernel(const uint16_t* __res
 
 }  // namespace
 
+hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int k_in,
+                              int max_rank, const int32_t* offsets, int E, const int32_t* sorted_ids, int P,
+                              int top_k, const int32_t* row_adapter, uint16_t* xa, int64_t row_offset,
+                              int64_t row_end, int x_gather, hipStream_t s) {
+    if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
+    const int64_t base16 = (row_offset / 16) * 16;
+    const int64_t subs = (row_end - base16 + 15) / 16;
+    const dim3 sgrid(static_cast<unsigned>(subs));
+#define MOE_SHRINK(NB_)                                                                                          \
+    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, \
+                                                 P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
+    switch (max_rank / 16) {
+        case 1: MOE_SHRINK(1); break;
+        case 2: MOE_SHRINK(2); break;
+        case 3: MOE_SHRINK(3); break;
+        case 4: MOE_SHRINK(4); break;
+        case 5: MOE_SHRINK(5); break;
+        case 6: MOE_SHRINK(6); break;
+        case 7: MOE_SHRINK(7); break;
+        default: MOE_SHRINK(8); break;
+    }
+#undef MOE_SHRINK
+    return hipGetLastError();
+}
+
 hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_tab, const uint64_t* b_tab,
                             const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,

@@ -29,7 +29,8 @@ import torch
 from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER
 from .ops import (Bf16Weight, Fp8Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows,
                   moe_align, moe_combine, moe_grouped_gemm, moe_grouped_gemm_fp8, moe_lora_fold, moe_lora_gather_fold,
-                  moe_quantize_fp8, moe_route, moe_route_align, moe_silu_mul, pack_lora_tables)
+                  moe_quantize_fp8, moe_route, moe_route_align, moe_silu_mul, pack_lora_tables,
+                  moe_grouped_gemm_gate_up_lora)
 
 FOLD_MODES = ("auto", "grouped", "gather")
 
@@ -56,7 +57,8 @@ class Buffers:
 class MoeLayer:
     def __init__(self, num_experts: int, hidden: int, inter: int, top_k: int, block_size: int, gate, up, down,
                  lora: Optional[LoraTables] = None, renormalize: bool = True, lora_cap: Optional[int] = None,
-                 fold: str = "auto", lora_gate: Optional[LoraTables] = None, lora_up: Optional[LoraTables] = None):
+                 fold: str = "auto", lora_gate: Optional[LoraTables] = None, lora_up: Optional[LoraTables] = None,
+                 gate_up_fused: bool = True):
         if fold not in FOLD_MODES:
             raise ValueError(f"fold must be one of {FOLD_MODES}")
         if isinstance(gate, Fp8Weight) and (lora_gate is not None or lora_up is not None):
@@ -67,6 +69,9 @@ class MoeLayer:
         self.renormalize = renormalize
         self.lora_cap = lora_cap
         self.fold = fold
+        # gate/up LoRA folded in the gate/up GEMM's epilogue (bf16 weights), else the page's order:
+        # gathered gate and up, a fold into each, SiLU * up
+        self.gate_up_fused = gate_up_fused and isinstance(gate, Bf16Weight)
 
     @property
     def fp8(self) -> bool:
@@ -81,7 +86,8 @@ class MoeLayer:
 
     # ------------------------------------------------------------------ construction from host arrays
     @staticmethod
-    def from_arrays(d: Dict[str, object], device, lora_cap: Optional[int] = None, fold: str = "auto") -> "MoeLayer":
+    def from_arrays(d: Dict[str, object], device, lora_cap: Optional[int] = None, fold: str = "auto",
+                    gate_up_fused: bool = True) -> "MoeLayer":
         """Build from host numpy arrays (bf16 / fp16 as uint16 bit patterns, GPTQ words as int32)."""
         cfg = d["cfg"]
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
@@ -109,7 +115,7 @@ class MoeLayer:
         lora_gate = tables("lora_gate") if "lora_ids" in d else None
         lora_up = tables("lora_up") if "lora_ids" in d else None
         return MoeLayer(cfg.E, cfg.H, cfg.I, cfg.top_k, cfg.block_size, gate, up, down, lora, cfg.renormalize,
-                        lora_cap, fold, lora_gate, lora_up)
+                        lora_cap, fold, lora_gate, lora_up, gate_up_fused)
 
     # ------------------------------------------------------------------ buffers
     def plan(self, T: int, device) -> Buffers:
@@ -125,7 +131,10 @@ class MoeLayer:
                     torch.empty((T, self.top_k), dtype=torch.float32, device=device), r,
                     torch.empty((r.max_pad, self.I), **bf), torch.empty((r.max_pad, self.H), **bf),
                     torch.empty((T, self.H), **bf), xa, gemm_workspace(device))
-        if self.gate_up_lora:
+        if self.gate_up_lora and self.gate_up_fused:
+            rank = max(t.max_rank for t in (self.lora_gate, self.lora_up) if t is not None)
+            b.g = torch.empty((2, r.max_pad, rank), **bf)  # the two shrinks of the fused path
+        elif self.gate_up_lora:
             b.g = torch.empty((r.max_pad, self.I), **bf)
             b.u = torch.empty((r.max_pad, self.I), **bf)
         if self.fp8:
@@ -147,6 +156,10 @@ class MoeLayer:
             return
         if not self.gate_up_lora:
             moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs, workspace=b.ws)
+            return
+        if self.gate_up_fused:
+            moe_grouped_gemm_gate_up_lora(x, self.gate, self.up, b.routing, self.lora_gate, self.lora_up, b.g,
+                                          out=b.hs, row_adapter=row_adapter, workspace=b.ws)
             return
         moe_grouped_gemm(MOE_OP_GATHER, x, self.gate, None, b.routing, out=b.g, workspace=b.ws)
         moe_grouped_gemm(MOE_OP_GATHER, x, self.up, None, b.routing, out=b.u, workspace=b.ws)

@@ -16,7 +16,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, 
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Fp8Weight", "Routing", "moe_quantize_fp8", "moe_grouped_gemm_fp8", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -318,6 +318,43 @@ def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routi
         _dev(xa, torch.bfloat16, "xa"), xa.shape[0], row_offset, row_end, routing.max_pad, int(bool(x_gather)),
         _stream(x)))
     return base
+
+
+def moe_grouped_gemm_gate_up_lora(x: torch.Tensor, gate: Bf16Weight, up: Bf16Weight, routing: Routing,
+                                  lora_gate: Optional[LoraTables], lora_up: Optional[LoraTables],
+                                  xa: torch.Tensor, out: Optional[torch.Tensor] = None,
+                                  row_adapter: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Hs with the gate and up LoRA folded in the gate/up GEMM's epilogue; xa: bf16 [2, max_pad, rank]."""
+    E, N, K = gate.shape
+    tabs = [t for t in (lora_gate, lora_up) if t is not None]
+    if not tabs:
+        raise ValueError("at least one of lora_gate, lora_up is needed")
+    rank = tabs[0].max_rank
+    if any(t.max_rank != rank or t.k_in != K or t.n_out != N for t in tabs):
+        raise ValueError("gate and up tables must share max_rank and match the weights")
+    if tuple(xa.shape) != (2, routing.max_pad, rank):
+        raise ValueError(f"xa must be [2, {routing.max_pad}, {rank}]")
+    if out is None:
+        out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=x.device)
+    sg, su = gate.struct(), up.struct()
+
+    def tab(t):
+        if t is None:
+            return None, None, None, 0
+        return (_dev(t.a_table, torch.int64, "a_table"), _dev(t.b_table, torch.int64, "b_table"),
+                _dev(t.scale_table, torch.float32, "scale_table"), t.n_tab)
+    ag, bg, cg, ng = tab(lora_gate)
+    au, bu, cu, nu = tab(lora_up)
+    check(lib().moe_grouped_gemm_gate_up_lora(
+        _dev(x, torch.bfloat16, "x"), ctypes.byref(sg), ctypes.byref(su), _dev(out, torch.bfloat16, "out"),
+        _dev(routing.sorted_ids, torch.int32, "sorted_ids"), _dev(routing.offsets, torch.int32, "offsets"),
+        routing.num_pairs, routing.top_k, routing.num_experts, N, K, routing.block_size, routing.max_pad,
+        ag, bg, cg, ng, au, bu, cu, nu, rank,
+        _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
+        _dev(xa, torch.bfloat16, "xa"), _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream(x)))
+    return out
 
 
 def moe_silu_mul(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor,

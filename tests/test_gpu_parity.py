@@ -350,6 +350,54 @@ def test_lora_fold_gate_up_form(dev, scale_mult):
     assert np.array_equal(gb[others], base[others])
 
 
+@pytest.mark.parametrize("case", ["lora_all_small", "lora_all_256rows", "x100", "adapter"])
+def test_gate_up_lora_fused_epilogue(dev, shared_ws, case):
+    """The gate/up LoRA folded in the GEMM's epilogue against the oracle and against the
+    unfused GPU path (gathered gate and up, folds, SiLU * up) on the same inputs."""
+    import torch
+    m = ops()
+    cfg = SMALL["lora_all_small"]
+    if case == "lora_all_256rows":   # >= 128 rows per expert: the 8-wave 256-row kernel
+        cfg = cfg.with_(T=1100, E=8, top_k=2, seed=9)
+    note(f"gate/up lora fused {case}")
+    d = make_inputs(cfg)
+    if case == "x100":
+        for proj in ("gate", "up"):
+            d[f"lora_{proj}_scale"] = (d[f"lora_{proj}_scale"] * 100).astype(np.float32)
+    ra = np.where(np.arange(cfg.T) % 4 == 1, -1, 0).astype(np.int32) if case == "adapter" else None
+    ids, w, al, r = _routing(cfg, d)
+    real = _real(al, cfg.P)
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    unf = m.MoeLayer.from_arrays(d, "cuda", gate_up_fused=False)
+    outs = {}
+    for name, lay in (("fused", layer), ("unfused", unf)):
+        b = lay.plan(cfg.T, "cuda")
+        lay.route_align(to_dev(d["logits"]), b)
+        b.hs.view(torch.int16).fill_(CANARY)
+        lay.gate_up_stage(bf16_dev(d["x"]), b, to_dev(ra) if ra is not None else None)
+        torch.cuda.synchronize()
+        outs[name] = bits_host(b.hs)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    assert (outs["fused"][pad] == CANARY).all(), "padding rows of Hs written"
+    tg, tu = oracle.moe_oracle._lora_tables(d, "gate"), oracle.moe_oracle._lora_tables(d, "up")
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    fused = oracle.bf16_bits_to_f64(outs["fused"][real])
+    unfused = oracle.bf16_bits_to_f64(outs["unfused"][real])
+    assert_close_rows(fused, unfused, 1e-2, f"fused vs unfused ({case})")
+    exact = (outs["fused"][real] == outs["unfused"][real]).mean()
+    note(f"  fused == unfused bits on {exact:.4f} of the values")
+    if ra is None:
+        h = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu)
+        assert_close_rows(fused, h[real], TOL, f"fused vs oracle ({case})")
+    else:
+        # tokens whose adapter entry is < 0 get the unfolded (bf16 gate and up) result
+        h0 = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, None, None)
+        h1 = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu)
+        skip = np.array([ra[al["sorted_ids"][rr] // cfg.top_k] < 0 for rr in real])
+        want = np.where(skip[:, None], h0[real], h1[real])
+        assert_close_rows(fused, want, TOL, f"fused vs oracle ({case})")
+
+
 @pytest.mark.parametrize("fold", ["grouped", "gather"])
 def test_layer_gate_up_lora(dev, fold):
     """The gate/up LoRA path in the layer: Hs from the GPU's own gate and up outputs folded and
@@ -359,7 +407,7 @@ def test_layer_gate_up_lora(dev, fold):
     cfg = SMALL["lora_all_small"]
     note(f"layer gate/up lora {fold}")
     d = make_inputs(cfg)
-    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold)
+    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold, gate_up_fused=False)
     b = layer.plan(cfg.T, "cuda")
     layer.route_align(to_dev(d["logits"]), b)
     x = bf16_dev(d["x"])
