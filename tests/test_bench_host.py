@@ -43,6 +43,16 @@ def test_algorithmic_bytes_of_gptq_weights():
     assert bench.expert_weight_bytes(cfg, "down") == K // 8 * N * 4 + K // G * N * 2 + K // G * N // 8 * 4
 
 
+def test_algorithmic_work_of_the_fp8_workload():
+    cfg = CONFIGS["fp8_prefill"]              # mixtral_prefill's shape, E4M3 weights
+    P = 4096 * 2
+    assert bench.gemm_flops(cfg, "gate_up") == 2 * 2 * 4096 * 14336 * P
+    # codes (1 byte) + one fp32 scale per output channel; activations read as 1-byte codes
+    w = 8 * 2 * (4096 * 14336 + 14336 * 4)
+    assert bench.gemm_bytes(cfg, "gate_up", 8) == w + 4096 * 4096 * 1 + P * 14336 * 2
+    assert bench.expert_weight_bytes(cfg, "down") == 4096 * 14336 + 4096 * 4
+
+
 def _write_traffic(tmp, src_files, sha, value):
     os.makedirs(os.path.join(tmp, "profiles"))
     with open(os.path.join(tmp, "profiles", "traffic_w.txt"), "w") as f:
