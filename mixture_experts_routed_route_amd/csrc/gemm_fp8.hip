@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ a_scale, const uint8_t* __restrict__ W0,
     const float* __restrict__ ws0, const uint8_t* __restrict__ W1, const float* __restrict__ ws1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ offsets, int P,
-    int top_k, int E, int N, int K, int max_pad, int m_bound, int n_tiles) {
+    int top_k, int E, int N, int K, int max_pad, int n_tiles) {
     using F = F8Cfg<BM, NW>;
     constexpr int BP = F::BP, NJ = F::NJ;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_STAGES * F::STAGE_BYTES];
@@ -349,7 +349,7 @@ void launch_fp8_cfg(const uint8_t* a, const float* a_scale, const uint8_t* w0, c
     const long long grid = (static_cast<long long>(m_bound) * n_tiles + 7) / 8 * 8 + 8;
     if (grid <= 0) return;
     gemm_fp8_kernel<GATE_UP, BM, NW><<<static_cast<unsigned>(grid), 64 * NW, 0, s>>>(
-        a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, m_bound, n_tiles);
+        a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles);
 }
 
 }  // namespace

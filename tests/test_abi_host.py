@@ -181,6 +181,15 @@ def test_argument_validation_rejects_before_launch(L):
     rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w8), None, fake, fake, fake, fake, 128, 2, 8, 128,
                   256, 16, 256, None, 0, None)
     assert rc == -1 and "unsupported type" in msg
+    # fused gate/up LoRA: (x, w_gate, w_up, hs, sorted_ids, offsets, P, top_k, E, n, k, bs, max_pad,
+    #                      a_g, b_g, s_g, n_g, a_u, b_u, s_u, n_u, max_rank, row_adapter, xa, ws, ws_bytes, stream)
+    lg = lambda wg, rank: _rc(L, "moe_grouped_gemm_gate_up_lora", fake, ctypes.byref(wg), ctypes.byref(wg), fake, fake,
+                              fake, 128, 2, 8, 128, 256, 16, 256, fake, fake, fake, 8, fake, fake, fake, 8, rank, None,
+                              fake, None, 0, None)
+    rc, msg = lg(w4, 64)
+    assert rc == -2 and "bf16" in msg
+    rc, msg = lg(w, 48)
+    assert rc == -1 and "max_rank" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 100, 8, None)
     assert rc == -1 and "hidden" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 128, 7, None)
