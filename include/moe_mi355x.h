@@ -240,12 +240,14 @@ moe_status moe_quantize_fp8(const uint16_t* x, int64_t rows, int32_t k, const in
  *            g[r, n] = a_scale[row] * scales[e, n] * sum_k a(row, k) W(n, k)
  *            (exact fp8 products, fp32 sums)
  * Sentinel and padding rows are not written.  op is MOE_OP_GATE_UP_SILU or
- * MOE_OP_DOWN; K % 16 == 0; N % 8 == 0. */
+ * MOE_OP_DOWN; K % 16 == 0; N % 8 == 0.  workspace: as for moe_grouped_gemm (the
+ * same buffer serves both; the tiles of a last partial round are split along K,
+ * with results deterministic and equal to those without it up to fp32 order). */
 moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_scale, const moe_weight* w0,
                                 const moe_weight* w1, uint16_t* c, const int32_t* sorted_ids,
                                 const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
                                 int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
-                                moe_stream stream);
+                                void* workspace, int64_t workspace_bytes, moe_stream stream);
 
 /* A5 — LoRA fold, in place, on one window [row_offset, row_end) of the sorted
  * rows (atlas moe_lora_grouped.rs, moe_lora_grouped_down).

@@ -47,7 +47,7 @@ SIGNATURES = {
     "moe_quantize_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
     "moe_grouped_gemm_fp8": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int64,
-                                       c_void_p]),
+                                       c_void_p, c_int64, c_void_p]),
     "moe_silu_mul": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p]),
     "moe_lora_gather_fold": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,

@@ -455,7 +455,7 @@ moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_sca
                                 const moe_weight* w1, uint16_t* c, const int32_t* sorted_ids,
                                 const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,
                                 int32_t num_experts, int32_t n, int32_t k, int32_t block_size, int64_t max_pad,
-                                moe_stream stream) {
+                                void* workspace, int64_t workspace_bytes, moe_stream stream) {
     const char* who = "moe_grouped_gemm_fp8";
     REQUIRE(op == MOE_OP_GATE_UP_SILU || op == MOE_OP_DOWN, "%s: op %d not GATE_UP_SILU or DOWN", who, op);
     const bool gate_up = op == MOE_OP_GATE_UP_SILU;
@@ -477,6 +477,12 @@ moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_sca
     else REQUIRE(w1 == nullptr, "%s: op %d takes no w1", who, op);
     REQUIRE(w0->type == MOE_W_FP8, "%s: w0 must be MOE_W_FP8 (type %d)", who, w0->type);
     if (w1) REQUIRE(w1->type == MOE_W_FP8, "%s: w1 must be MOE_W_FP8 (type %d)", who, w1->type);
+    if (workspace != nullptr) {
+        const int64_t need = moe_grouped_gemm_workspace_bytes();
+        REQUIRE_PTR(who, workspace);
+        REQUIRE(workspace_bytes >= need, "%s: workspace_bytes %lld < required %lld", who,
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+    }
     if (num_pairs == 0) return ok();
     REQUIRE_PTR(who, a);
     REQUIRE_PTR(who, a_scale);
@@ -494,7 +500,7 @@ moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_sca
                              static_cast<const float*>(w0->scales), w1 ? static_cast<const uint8_t*>(w1->data) : nullptr,
                              w1 ? static_cast<const float*>(w1->scales) : nullptr, c, sorted_ids, expert_offsets,
                              static_cast<int>(num_pairs), top_k, num_experts, n, k, static_cast<int>(max_pad),
-                             static_cast<hipStream_t>(stream)));
+                             workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out, const int32_t* sorted_ids,

@@ -30,6 +30,12 @@ constexpr int F8_STAGES = 2;
 constexpr int F8_CPR = F8_BK / 16;                  // 16-byte chunks per LDS row
 constexpr int F8_RPI = 1024 / F8_BK;                // rows one wave-wide 1 KB load fills
 constexpr int kMaxE8 = 256;
+#ifndef MOE_FP8_SPLIT_MIN_STAGES
+#define MOE_FP8_SPLIT_MIN_STAGES 8  // K stages of 128 per piece of a split tail tile, at least
+#endif
+#ifndef MOE_FP8_SPLIT_MAX_ROUNDS
+#define MOE_FP8_SPLIT_MAX_ROUNDS 4  // split the tail only of launches with fewer rounds of tiles
+#endif
 #ifndef MOE_FP8_ASYM
 #define MOE_FP8_ASYM 1  // 8 waves: waves 0-3 issue all of a stage's loads
 #endif
@@ -111,12 +117,13 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t*
 }
 
 // ------------------------------------------------------------------ grouped GEMM
-template <bool GATE_UP, int BM, int NW>
+template <bool GATE_UP, int BM, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ a_scale, const uint8_t* __restrict__ W0,
     const float* __restrict__ ws0, const uint8_t* __restrict__ W1, const float* __restrict__ ws1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ offsets, int P,
-    int top_k, int E, int N, int K, int max_pad, int n_tiles) {
+    int top_k, int E, int N, int K, int max_pad, int n_tiles, float* __restrict__ sk_part,
+    int32_t* __restrict__ sk_cnt, int sk_slots) {
     using F = F8Cfg<BM, NW>;
     constexpr int BP = F::BP, NJ = F::NJ;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_STAGES * F::STAGE_BYTES];
@@ -124,6 +131,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
     __shared__ int s_lo[kMaxE8], s_hi[kMaxE8], s_tb[kMaxE8 + 1];
     __shared__ int s_row[BM];
     __shared__ float s_as[BM];
+    __shared__ int s_arrived;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations are scalar
 
@@ -141,13 +149,41 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
         __syncthreads();
     }
     const int m_real = __builtin_amdgcn_readfirstlane(s_tb[E]);
+    const int nk = (K + F8_BK - 1) / F8_BK;
     // Workgroup ids go round-robin over the 8 XCDs: XCD x takes the contiguous range
-    // [x*T/8, (x+1)*T/8) of the T real tiles (row tiles fastest), so the workgroups an XCD runs
-    // together share weight panels in its L2.  The grid (a multiple of 8) bounds T from above.
+    // [x*Tw/8, (x+1)*Tw/8) of the first Tw tiles (row tiles fastest), so the workgroups an XCD
+    // runs together share weight panels in its L2.
+    // Split tail (with a workspace, sk_slots > 0 = workgroups resident at once, and fewer than
+    // MOE_FP8_SPLIT_MAX_ROUNDS rounds of tiles: over more rounds, the last partial one costs less
+    // than the pieces' partials): the rest = T mod
+    // sk_slots tiles of the last partial round are cut along K into s pieces of at least
+    // MOE_FP8_SPLIT_MIN_STAGES stages (rest * s <= sk_slots), which run after the whole tiles on
+    // the workgroups past each XCD's range.  Each piece writes its fp32 partial accumulators to
+    // the workspace slot of its number and counts itself on the tile's counter; the last to
+    // arrive adds the s partials in piece order (so results do not depend on arrival order),
+    // stores the tile and resets the counter.
     const int T = m_real * n_tiles;
+    int Tw = T, split = 1;
+    if (SPLIT && sk_slots > 0 && T < MOE_FP8_SPLIT_MAX_ROUNDS * sk_slots) {
+        const int rest = T % sk_slots;
+        const int s_max = rest > 0 ? min(sk_slots / rest, nk / MOE_FP8_SPLIT_MIN_STAGES) : 1;
+        if (s_max >= 2) { Tw = T - rest; split = s_max; }
+    }
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int L = static_cast<int>(static_cast<long long>(T) * xcd / 8) + slot;
-    if (L >= static_cast<int>(static_cast<long long>(T) * (xcd + 1) / 8)) return;  // uniform
+    const int lo_x = static_cast<int>(static_cast<long long>(Tw) * xcd / 8);
+    const int share = static_cast<int>(static_cast<long long>(Tw) * (xcd + 1) / 8) - lo_x;
+    int L, kb = 0, ke = nk, piece = -1, tail_u = 0;
+    if (slot < share) {
+        L = lo_x + slot;
+    } else {
+        piece = (slot - share) * 8 + xcd;  // distinct over XCDs (piece mod 8 == xcd)
+        if (piece >= (T - Tw) * split) return;  // uniform over the workgroup
+        tail_u = piece / split;
+        const int j = piece - tail_u * split;
+        L = Tw + tail_u;
+        kb = j * nk / split;
+        ke = (j + 1) * nk / split;
+    }
     const int n_t = L / m_real;
     const int m_t = L - n_t * m_real;
     int lo_e = 0, hi_e = E - 1;                   // largest expert whose first row tile is <= m_t
@@ -268,15 +304,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
         const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + swz8(row, c0 + 1) * 16);
         return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
-    const int nk = (K + F8_BK - 1) / F8_BK;
-    issue(0);
-    for (int s = 0; s < nk; ++s) {
+    issue(kb);
+    for (int s = kb; s < ke; ++s) {
         // this thread's loads of stage s have landed and every wave is past stage s - 1, whose
         // buffer is refilled with stage s + 1
         __builtin_amdgcn_s_waitcnt(0x0070 | (15 << 8));  // vmcnt(0)
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        if (s + 1 < nk) issue(s + 1);
+        if (s + 1 < ke) issue(s + 1);
         const uint8_t* st = smem + (s % F8_STAGES) * F::STAGE_BYTES;
 #pragma unroll
         for (int ks = 0; ks < F8_BK / 64; ++ks) {
@@ -294,6 +329,47 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
                                                                                127, 0, 127);
         }
+    }
+
+    // ---- a piece of a split tail tile: partials through the workspace, with device-coherent
+    // (sc1) buffer accesses (see gemm_bf16.hip: no fence writes back or invalidates the L2)
+    if (SPLIT && piece >= 0) {
+        constexpr int PART = 64 * NW * 2 * NJ * 16;  // floats per partial
+        constexpr int kSc1 = 16;
+        const __amdgpu_buffer_rsrc_t part =
+            __builtin_amdgcn_make_buffer_rsrc(sk_part, 0, sk_slots * PART * 4, 0x00020000);
+        uint32_t o = (static_cast<uint32_t>(piece) * PART + tid * 4) * 4;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, part, o, 0, kSc1);
+                    o += 64 * NW * 16;
+                }
+        __builtin_amdgcn_s_waitcnt(0x0070 | (15 << 8));  // vmcnt(0): the partial is visible before it is counted
+        __syncthreads();
+        if (tid == 0)
+            s_arrived = __hip_atomic_fetch_add(&sk_cnt[tail_u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_arrived != split - 1) return;  // uniform: another piece stores the tile
+        uint32_t base = (static_cast<uint32_t>(tail_u * split) * PART + tid * 4) * 4;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 t{0.f, 0.f, 0.f, 0.f};
+                    for (int jp = 0; jp < split; ++jp)
+                        t += __builtin_amdgcn_raw_buffer_load_b128(part, base + jp * PART * 4, 0, kSc1);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] = t[v];
+                    base += 64 * NW * 16;
+                }
+        if (tid == 0) __hip_atomic_store(&sk_cnt[tail_u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- epilogue: scales, SiLU * up for gate/up; neighbour lanes (columns c, c+1) swap one
@@ -338,18 +414,58 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
         }
 }
 
+int device_cus8(hipError_t& err) {
+    static int cus[64] = {0};
+    int dev = 0;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) return 0;
+    if (dev < 0 || dev >= 64) { err = hipErrorInvalidDevice; return 0; }
+    if (cus[dev] == 0) {
+        int n = 0;
+        err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// workspace layout shared with the bf16 GEMM: 4 KB of int32 counters, then partial slots
+constexpr int64_t kF8CounterBytes = 4096;
+constexpr int64_t kF8PartBytes = 512LL * 2 * 64 * 4;   // largest partial: 512 threads x 128 fp32
+constexpr int kF8MaxSlots = 256;
+
 template <bool GATE_UP, int BM, int NW>
-void launch_fp8_cfg(const uint8_t* a, const float* a_scale, const uint8_t* w0, const float* ws0, const uint8_t* w1,
-                    const float* ws1, uint16_t* c, const int32_t* sorted_ids, const int32_t* offsets, int P,
-                    int top_k, int E, int N, int K, int max_pad, hipStream_t s) {
+hipError_t launch_fp8_cfg(const uint8_t* a, const float* a_scale, const uint8_t* w0, const float* ws0,
+                          const uint8_t* w1, const float* ws1, uint16_t* c, const int32_t* sorted_ids,
+                          const int32_t* offsets, int P, int top_k, int E, int N, int K, int max_pad, void* ws,
+                          int64_t ws_bytes, hipStream_t s) {
+    static_assert(64 * NW * 2 * F8Cfg<BM, NW>::NJ * 16 * 4 <= kF8PartBytes, "partial larger than its slot");
     const int ncol = GATE_UP ? BM / 2 : BM;
     const int n_tiles = (N + ncol - 1) / ncol;
     const int m_bound = (max_pad + BM - 1) / BM + E;  // row tiles of any routing, at most
-    // each XCD's share of the tiles, rounded up, times 8
-    const long long grid = (static_cast<long long>(m_bound) * n_tiles + 7) / 8 * 8 + 8;
-    if (grid <= 0) return;
-    gemm_fp8_kernel<GATE_UP, BM, NW><<<static_cast<unsigned>(grid), 64 * NW, 0, s>>>(
-        a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles);
+    // workgroups resident at once: one per compute unit (256-row tiles), two (128-row tiles)
+    int slots = 0;
+    if (ws != nullptr && ws_bytes >= kF8CounterBytes + kF8MaxSlots * kF8PartBytes) {
+        hipError_t err = hipSuccess;
+        slots = device_cus8(err) * (NW == 4 ? 2 : 1);
+        if (err != hipSuccess) return err;
+        slots = min(slots, kF8MaxSlots);
+    }
+    // each XCD's share of the whole tiles (rounded up) plus its pieces of a split tail, times 8
+    const long long grid = ((static_cast<long long>(m_bound) * n_tiles + 7) / 8 + 1 + (slots + 7) / 8) * 8;
+    int32_t* cnt = slots > 0 ? static_cast<int32_t*>(ws) : nullptr;
+    float* part = slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + kF8CounterBytes) : nullptr;
+    // the split-tail code is compiled only into the kernel of launches that can have few rounds of
+    // tiles (it costs the others about 1% through their register allocation)
+    if (slots > 0 && static_cast<long long>(m_bound) * n_tiles < static_cast<long long>(MOE_FP8_SPLIT_MAX_ROUNDS) * slots)
+        gemm_fp8_kernel<GATE_UP, BM, NW, true><<<static_cast<unsigned>(grid), 64 * NW, 0, s>>>(
+            a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt,
+            slots);
+    else
+        gemm_fp8_kernel<GATE_UP, BM, NW, false><<<static_cast<unsigned>(grid), 64 * NW, 0, s>>>(
+            a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, nullptr,
+            nullptr, 0);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -364,18 +480,16 @@ hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int K, const int
 hipError_t launch_gemm_fp8(bool gate_up, const uint8_t* a, const float* a_scale, const uint8_t* w0,
                            const float* ws0, const uint8_t* w1, const float* ws1, uint16_t* c,
                            const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
-                           int K, int max_pad, hipStream_t s) {
+                           int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
     // 256-row tiles (8 waves, two per SIMD) when experts average at least 128 rows; 128-row
     // tiles (4 waves) for fewer
     const bool big = static_cast<long long>(P) >= 128LL * E;
     if (gate_up) {
-        if (big) launch_fp8_cfg<true, 256, 8>(a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
-        else launch_fp8_cfg<true, 128, 4>(a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
-    } else {
-        if (big) launch_fp8_cfg<false, 256, 8>(a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
-        else launch_fp8_cfg<false, 128, 4>(a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, s);
+        if (big) return launch_fp8_cfg<true, 256, 8>(a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
+        return launch_fp8_cfg<true, 128, 4>(a, a_scale, w0, ws0, w1, ws1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
     }
-    return hipGetLastError();
+    if (big) return launch_fp8_cfg<false, 256, 8>(a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
+    return launch_fp8_cfg<false, 128, 4>(a, a_scale, w0, ws0, nullptr, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, s);
 }
 
 }  // namespace moe

@@ -76,7 +76,7 @@ hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int K, const int
 hipError_t launch_gemm_fp8(bool gate_up, const uint8_t* a, const float* a_scale, const uint8_t* w0,
                            const float* ws0, const uint8_t* w1, const float* ws1, uint16_t* c,
                            const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
-                           int K, int max_pad, hipStream_t s);
+                           int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s);
 // silu_mul.hip: h[r] = bf16(silu(g[r]) * u[r]) on the real sorted rows (all rows without sorted_ids)
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint16_t* h, const int32_t* sorted_ids, int P,
                            int64_t rows, int N, hipStream_t s);

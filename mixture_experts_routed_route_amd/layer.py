@@ -152,7 +152,8 @@ class MoeLayer:
         weights, x quantised per token and the fp8 fused kernel."""
         if self.fp8:
             moe_quantize_fp8(x, b.xq, b.sx)
-            moe_grouped_gemm_fp8(MOE_OP_GATE_UP_SILU, b.xq, b.sx, self.gate, self.up, b.routing, out=b.hs)
+            moe_grouped_gemm_fp8(MOE_OP_GATE_UP_SILU, b.xq, b.sx, self.gate, self.up, b.routing, out=b.hs,
+                                 workspace=b.ws)
             return
         if not self.gate_up_lora:
             moe_grouped_gemm(MOE_OP_GATE_UP_SILU, x, self.gate, self.up, b.routing, out=b.hs, workspace=b.ws)
@@ -172,7 +173,7 @@ class MoeLayer:
     def down_stage(self, b: Buffers) -> None:
         if self.fp8:  # the real rows of Hs quantised per row, then the fp8 down GEMM
             moe_quantize_fp8(b.hs, b.hq, b.sh, b.routing)
-            moe_grouped_gemm_fp8(MOE_OP_DOWN, b.hq, b.sh, self.down, None, b.routing, out=b.ys)
+            moe_grouped_gemm_fp8(MOE_OP_DOWN, b.hq, b.sh, self.down, None, b.routing, out=b.ys, workspace=b.ws)
             return
         moe_grouped_gemm(MOE_OP_DOWN, b.hs, self.down, None, b.routing, out=b.ys, workspace=b.ws)
 

@@ -244,7 +244,8 @@ def moe_quantize_fp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
 
 
 def moe_grouped_gemm_fp8(op: int, a: torch.Tensor, a_scale: torch.Tensor, w0: Fp8Weight, w1: Optional[Fp8Weight],
-                         routing: Routing, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         routing: Routing, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """op = MOE_OP_GATE_UP_SILU (a = x codes [T, K] by token) or MOE_OP_DOWN (a = Hs codes [max_pad, K])."""
     E, N, K = w0.shape
     if out is None:
@@ -256,7 +257,9 @@ def moe_grouped_gemm_fp8(op: int, a: torch.Tensor, a_scale: torch.Tensor, w0: Fp
                                      _dev(out, torch.bfloat16, "out"),
                                      _dev(routing.sorted_ids, torch.int32, "sorted_ids"),
                                      _dev(routing.offsets, torch.int32, "offsets"), routing.num_pairs, routing.top_k,
-                                     routing.num_experts, N, K, routing.block_size, routing.max_pad, _stream(a)))
+                                     routing.num_experts, N, K, routing.block_size, routing.max_pad,
+                                     _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
+                                     workspace.numel() if workspace is not None else 0, _stream(a)))
     return out
 
 

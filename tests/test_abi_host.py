@@ -170,14 +170,17 @@ def test_argument_validation_rejects_before_launch(L):
     assert _rc(L, "moe_quantize_fp8", None, 0, 64, None, 0, None, None, None)[0] == 0   # no rows
     w8 = MoeWeight(2, 0, 1 << 20, fake, None)
     rc, msg = _rc(L, "moe_grouped_gemm_fp8", 2, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8, 128,
-                  256, 16, 256, None)
+                  256, 16, 256, None, 0, None)
     assert rc == -1 and "op 2" in msg
     rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w), None, fake, fake, fake, 128, 2, 8, 128,
-                  256, 16, 256, None)
+                  256, 16, 256, None, 0, None)
     assert rc == -1 and "MOE_W_FP8" in msg
     rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8, 128,
-                  264, 16, 256, None)
+                  264, 16, 256, None, 0, None)
     assert rc == -1 and "multiple of 16" in msg
+    rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8, 128,
+                  256, 16, 256, fake, 64, None)
+    assert rc == -1 and "workspace_bytes" in msg
     rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w8), None, fake, fake, fake, fake, 128, 2, 8, 128,
                   256, 16, 256, None, 0, None)
     assert rc == -1 and "unsupported type" in msg

@@ -444,6 +444,13 @@ FP8_SMALL = {
                             logits="zipf", seed=52),
     # >= 128 rows per expert on average: 256-row tiles with 8 waves
     "fp8_big": MoeConfig("fp8_big", T=1024, H=528, I=912, E=4, top_k=2, block_size=64, weights="fp8", seed=53),
+    # less than a round of tiles, K of 17 stages of 128: with the workspace every tile is a tail
+    # tile cut in 2 pieces (gate/up here: 9 column panels, K = 2176)
+    "fp8_split_gate_up": MoeConfig("fp8_split_gu", T=1024, H=2176, I=1040, E=4, top_k=2, block_size=64,
+                                   weights="fp8", seed=54),
+    # ... and down here (5 column panels of 256, K = 2176)
+    "fp8_split_down": MoeConfig("fp8_split_dn", T=1024, H=1040, I=2176, E=4, top_k=2, block_size=64,
+                                weights="fp8", seed=55),
 }
 
 
@@ -483,9 +490,10 @@ def test_quantize_fp8_bit_exact(dev):
 
 
 @pytest.mark.parametrize("name", list(FP8_SMALL))
-def test_grouped_gemm_fp8(dev, name):
+def test_grouped_gemm_fp8(dev, shared_ws, name):
     """Both fp8 GEMMs against the oracle on the oracle's own codes and scales (so only the GEMM
-    is compared); sentinel and padding rows are never written."""
+    is compared), without and with the split-tail workspace; sentinel and padding rows are never
+    written; two calls with the workspace give the same bits; its counters end at zero."""
     import torch
     m = ops()
     cfg = FP8_SMALL[name]
@@ -497,21 +505,28 @@ def test_grouped_gemm_fp8(dev, name):
     pad = np.setdiff1d(np.arange(r.max_pad), real)
     ref = oracle.moe_layer(d)
     xq, sx = ref["xq"], ref["sx"]
-    hs = _canary(r.max_pad, cfg.I)
-    m.moe_grouped_gemm_fp8(m.MOE_OP_GATE_UP_SILU, to_dev(xq), to_dev(sx), layer.gate, layer.up, r, out=hs)
-    hb = bits_host(hs)
-    assert (hb[pad] == CANARY).all(), "padding rows of Hs written"
-    e1, e2 = assert_close_rows(bf16_host(hs)[real], ref["h"][real], TOL, "fp8 gate/up")
-    note(f"  gate/up worst row {e1:.2e}")
     hq = np.zeros((r.max_pad, cfg.I), np.uint8)
     sh = np.ones(r.max_pad, np.float32)
     hq[real], sh[real] = ref["hq"][real], ref["sh"][real]
-    ys = _canary(r.max_pad, cfg.H)
-    m.moe_grouped_gemm_fp8(m.MOE_OP_DOWN, to_dev(hq), to_dev(sh), layer.down, None, r, out=ys)
-    yb = bits_host(ys)
-    assert (yb[pad] == CANARY).all(), "padding rows of Ys written"
-    e1, e2 = assert_close_rows(bf16_host(ys)[real], ref["y"][real], TOL, "fp8 down")
-    note(f"  down worst row {e1:.2e}")
+    runs = []
+    for ws in (None, shared_ws, shared_ws):
+        tag = "with workspace" if ws is not None else "without workspace"
+        hs = _canary(r.max_pad, cfg.I)
+        m.moe_grouped_gemm_fp8(m.MOE_OP_GATE_UP_SILU, to_dev(xq), to_dev(sx), layer.gate, layer.up, r, out=hs,
+                               workspace=ws)
+        hb = bits_host(hs)
+        assert (hb[pad] == CANARY).all(), f"padding rows of Hs written ({tag})"
+        e1, e2 = assert_close_rows(bf16_host(hs)[real], ref["h"][real], TOL, f"fp8 gate/up ({tag})")
+        note(f"  gate/up worst row {e1:.2e} ({tag})")
+        ys = _canary(r.max_pad, cfg.H)
+        m.moe_grouped_gemm_fp8(m.MOE_OP_DOWN, to_dev(hq), to_dev(sh), layer.down, None, r, out=ys, workspace=ws)
+        yb = bits_host(ys)
+        assert (yb[pad] == CANARY).all(), f"padding rows of Ys written ({tag})"
+        e1, e2 = assert_close_rows(bf16_host(ys)[real], ref["y"][real], TOL, f"fp8 down ({tag})")
+        note(f"  down worst row {e1:.2e} ({tag})")
+        runs.append((hb, yb))
+    assert np.array_equal(runs[1][0], runs[2][0]) and np.array_equal(runs[1][1], runs[2][1])
+    assert not shared_ws[:4096].cpu().numpy().any(), "split counters not reset"
 
 
 @pytest.mark.parametrize("name", list(FP8_SMALL))
