@@ -559,6 +559,39 @@ def test_layer_fp8_end_to_end(dev, name):
     note(f"layer fp8 {name}: against the independent oracle worst row {e1:.2e}, tensor {e2:.2e}")
 
 
+def test_layer_fp8_with_down_lora(dev):
+    """fp8 experts with a down-projection LoRA (the fold reads the bf16 Hs the fp8 gate/up wrote):
+    the folded Ys rows against the oracle fold of the GPU's own Hs and unfolded Ys, and the
+    output against the independent oracle at the fp8 bar."""
+    import torch
+    m = ops()
+    cfg = MoeConfig("fp8_lora", T=200, H=512, I=256, E=16, top_k=6, block_size=64, weights="fp8", lora_rank=16,
+                    lora_max_rank=64, seed=56)
+    d = make_inputs(cfg)
+    d["lora_scale"] = (d["lora_scale"] * 20).astype(np.float32)   # a fold well above the fp8 noise
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    b = layer.plan(cfg.T, "cuda")
+    layer.route_align(to_dev(d["logits"]), b)
+    lora, layer.lora = layer.lora, None
+    layer.experts(bf16_dev(d["x"]), b)
+    layer.lora = lora
+    torch.cuda.synchronize()
+    hs, ys0 = bits_host(b.hs), bits_host(b.ys)
+    layer.lora_fold(b)
+    out = layer.combine(b)
+    ref = oracle.moe_layer(d)
+    al = ref["align"]
+    real = _real(al, cfg.P)
+    tabs = oracle.moe_oracle._lora_tables(d)
+    hs_f = np.where(np.isin(np.arange(hs.shape[0]), real)[:, None], oracle.bf16_bits_to_f64(hs), 0.0)
+    want = oracle.lora_fold(oracle.bf16_bits_to_f64(ys0), hs_f, tabs, al, cfg.top_k)
+    sd = oracle.lora_fold(np.zeros(ys0.shape), hs_f, tabs, al, cfg.top_k)
+    adapted = np.array([rr for rr in real if (np.searchsorted(al["offsets"], rr, side="right") - 1) % 2 == 0])
+    _gather_check(bits_host(b.ys), want, sd, ys0, adapted, "fp8 layer down fold")
+    e1, e2 = assert_close_rows(bf16_host(out), ref["out"], 5e-2, "fp8 layer with LoRA")
+    note(f"fp8 + LoRA layer: worst row {e1:.2e}")
+
+
 # ----------------------------------------------------------------------------- A6 combine
 @pytest.mark.parametrize("name", ["tiny", "finegrained_small", "mixtral_small"])
 def test_combine(dev, name):
