@@ -74,28 +74,21 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     constexpr int NSPLIT = GATE_UP ? 2 : 4;    // waves sharing one projection's K groups
     constexpr int G = STEPS * 32;
     __shared__ int s_row[16];
-    __shared__ int s_any;
     __shared__ float red[4][4][64][4];  // [wave][v][lane][j]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r0 = blockIdx.x * 16;
     const int n0 = blockIdx.y * NCOL;
+    const int m = lane & 15, kq = lane >> 4;  // A fragment row; k-octet within a k32 step
+
+    // The tile's rows: every wave reads the 16 sorted ids itself (no barrier before the first
+    // loads).  The id load is issued before the weight loads, so waiting for it does not wait for
+    // them: vector loads complete in issue order.
+    // (loads without branches around them, so the wait for the id can count the later loads)
+    int p = sorted_ids[min(r0 + m, max_pad - 1)];
+    if (r0 + m >= max_pad) p = -1;
     const int e = expert_ids[r0 / bs];
     if (e < 0 || e >= E) return;
-    if (tid == 0) s_any = 0;
-    __syncthreads();
-    if (tid < 16) {
-        const int r = r0 + tid;
-        int src = -1;
-        if (r < max_pad) {
-            const int p = sorted_ids[r];
-            if (p >= 0 && p < P) src = (GATE_UP || a_tok) ? p / top_k : r;
-        }
-        s_row[tid] = src;
-        if (src >= 0) atomicOr(&s_any, 1);
-    }
-    __syncthreads();
-    if (!s_any) return;
 
     // this wave's projection and quantisation groups
     const int proj = GATE_UP ? wave >> 1 : 0;
@@ -104,36 +97,51 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     const int per = (ngroups + NSPLIT - 1) / NSPLIT;
     const int g_begin = part * per;
     const int g_end = min(ngroups, g_begin + per);
-
-    const int m = lane & 15, kq = lane >> 4;  // A fragment row; k-octet within a k32 step
-    const int arow = s_row[m];
-    // a row without a token reads a row that is always in bounds (token 0, or the tile's first
-    // sorted row); its results are never stored
-    const int arow_ok = arow >= 0 ? arow : ((GATE_UP || a_tok) ? 0 : r0);
     const int ncol = n0 + 4 * m;              // first of this lane's 4 columns
     const int zshift = 16 * (m & 1);          // nibble of column ncol inside its qzeros word
 
-    // per-lane cursors at group g_begin; every group moves them by a fixed stride
-    const uint16_t* a_cur = A + static_cast<size_t>(arow_ok) * K + kq * 8 + static_cast<size_t>(g_begin) * G;
+    // per-lane weight cursors at group g_begin (clamped to the last group for a wave without
+    // groups, whose loads are then unused); every group moves them by a fixed stride
+    const int g0 = min(g_begin, ngroups - 1);
     const int32_t* q_cur = (proj ? qw1 : qw0) + static_cast<size_t>(e) * (K / 8) * N +
-                           static_cast<size_t>(g_begin * (G / 8) + kq) * N + ncol;
+                           static_cast<size_t>(g0 * (G / 8) + kq) * N + ncol;
     const uint16_t* s_cur = (proj ? sc1 : sc0) + static_cast<size_t>(e) * (K / G) * N +
-                            static_cast<size_t>(g_begin) * N + ncol;
+                            static_cast<size_t>(g0) * N + ncol;
     const int32_t* z_cur = (proj ? qz1 : qz0) + static_cast<size_t>(e) * (K / G) * (N / 8) +
-                           static_cast<size_t>(g_begin) * (N / 8) + ncol / 8;
-    auto load_group = [&](GroupRegs<STEPS>& R) {
+                           static_cast<size_t>(g0) * (N / 8) + ncol / 8;
+    auto load_w = [&](GroupRegs<STEPS>& R) {
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            R.a[st] = *reinterpret_cast<const u32x4*>(a_cur + st * 32);
+        for (int st = 0; st < STEPS; ++st)
             R.q[st] = *reinterpret_cast<const u32x4*>(q_cur + static_cast<size_t>(st) * 4 * N);
-        }
         R.s = *reinterpret_cast<const uint2*>(s_cur);
         R.z = static_cast<uint32_t>(*z_cur);
-        a_cur += G;
         q_cur += static_cast<size_t>(G / 8) * N;
         s_cur += N;
         z_cur += N / 8;
     };
+    // the first group's weights depend only on the expert: they stream while the rows resolve
+    const int ng = g_end - g_begin;
+    GroupRegs<STEPS> nxt;
+    load_w(nxt);
+
+    const int src = (p >= 0 && p < P) ? ((GATE_UP || a_tok) ? p / top_k : r0 + m) : -1;
+    if (wave == 0 && lane < 16) s_row[lane] = src;  // read by the epilogue after the reduction barrier
+    if (!__any(src >= 0)) return;  // the same 16 rows in every wave: the whole workgroup leaves
+
+    // a row without a token reads a row that is always in bounds (token 0, or the tile's first
+    // sorted row); its results are never stored
+    const int arow_ok = src >= 0 ? src : ((GATE_UP || a_tok) ? 0 : r0);
+    const uint16_t* a_cur = A + static_cast<size_t>(arow_ok) * K + kq * 8 + static_cast<size_t>(g0) * G;
+    auto load_a = [&](GroupRegs<STEPS>& R) {
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) R.a[st] = *reinterpret_cast<const u32x4*>(a_cur + st * 32);
+        a_cur += G;
+    };
+    auto load_group = [&](GroupRegs<STEPS>& R) {
+        load_w(R);
+        load_a(R);
+    };
+    load_a(nxt);
 
     f32x4 out[4];
 #pragma unroll
@@ -167,9 +175,6 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     };
 
     // group g+1 loads while group g is computed
-    const int ng = g_end - g_begin;
-    GroupRegs<STEPS> nxt;
-    if (ng > 0) load_group(nxt);
     for (int i = 0; i < ng; ++i) {
         const GroupRegs<STEPS> cur = nxt;
         if (i + 1 < ng) load_group(nxt);
