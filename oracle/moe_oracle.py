@@ -167,7 +167,13 @@ def route(logits: np.ndarray, top_k: int, renormalize: bool = True) -> Tuple[np.
         ex = np.exp(l - l.max())
         p = ex / ex.sum()
         ps = p[sel]
-        ws = ps / ps.sum() if renormalize else ps
+        if renormalize:
+            kept = 0.0
+            for j in range(top_k):         # the kept probabilities summed in slot order
+                kept += ps[j]
+            ws = ps / kept
+        else:
+            ws = ps
         ids[t] = sel
         w[t] = round_f32(ws)
     return ids, w

@@ -245,6 +245,19 @@ def fp8_gate_up_scale_by_column(xq, sx, w_gate, w_up, al, top_k):
     return h * np.resize(sx, h.shape[1])[None, :]
 
 
+def expert_matrix_always_first(w, e):
+    return om._orig_expert_matrix(w, 0)
+
+
+def expert_matrix_next_expert(w, e):
+    E = w["qweight"].shape[0] if isinstance(w, dict) else w.shape[0]
+    return om._orig_expert_matrix(w, (e + 1) % E)
+
+
+def gptq_dequant_always_first(w, e):
+    return om._orig_gptq_dequant(w, 0)
+
+
 om._orig_route = om.route
 om._orig_align = om.align
 om._orig_gate_up = om.grouped_gate_up
@@ -254,6 +267,8 @@ om._orig_gather = om.lora_gather_fold
 om._orig_gate_up_lora = om.grouped_gate_up_lora
 om._orig_e4m3 = om.e4m3_to_f64
 om._orig_fp8_gate_up = om.grouped_gate_up_fp8
+om._orig_expert_matrix = om.expert_matrix
+om._orig_gptq_dequant = om.gptq_dequant_expert
 
 ROUTE_PINS = [pins.test_route_worked_examples, pins.test_route_special_cases, pins.test_route_brute_force_ids_and_sum]
 ALIGN_PINS = [pins.test_align_worked_examples, lambda: pins.test_align_invariants_random(8, 2, 16, 64)]
@@ -264,6 +279,9 @@ GATE_UP_LORA_PINS = [pins.test_gate_up_lora_rounding_pin, pins.test_layer_gate_u
 FP8_PINS = [pins.test_e4m3_decode_against_torch, pins.test_quantize_rows_fp8_closed_forms,
             pins.test_fp8_gemms_match_dequantised_definition]
 INT4_PINS = [pins.test_gptq_unpack_and_dequant, pins.test_layer_int4_matches_dense_brute_force]
+# pins that build the stacked expert slabs by hand and never read them through the oracle
+SELECTION_PINS = [lambda: pins.test_expert_selection_bf16_hand_built_stacks(5, 2),
+                  pins.test_expert_selection_int4_hand_built_stacks]
 
 MUTANTS = [
     ("route", route_ties_high_first, ROUTE_PINS),
@@ -274,6 +292,9 @@ MUTANTS = [
     ("align", align_sentinel_minus_one, ALIGN_PINS),
     ("gptq_dequant_expert", gptq_zero_plus_one, INT4_PINS),
     ("gptq_unpack_q", unpack_q_reversed, INT4_PINS),
+    ("expert_matrix", expert_matrix_always_first, SELECTION_PINS),
+    ("expert_matrix", expert_matrix_next_expert, SELECTION_PINS),
+    ("gptq_dequant_expert", gptq_dequant_always_first, SELECTION_PINS),
     ("grouped_gate_up", gate_up_token_mod, LAYER_PINS),
     ("grouped_gate_up", gate_up_swapped, LAYER_PINS),
     ("combine", combine_ignores_inv, [pins.test_combine_worked_example] + LAYER_PINS),

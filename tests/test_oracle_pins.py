@@ -572,3 +572,90 @@ def test_pack_expert_tables_and_windows():
     assert w == [(0, 4096), (4096, 8192), (8192, 10000)]
     with pytest.raises(ValueError):
         oracle.lora_windows(10, 0)
+
+
+# ----------------------------------------------------------------------------- expert selection, pinned by hand-built stacks
+# The brute forces above read each expert's matrix through the oracle's own readers.  These two
+# build the stacked [E, N, K] bf16 slabs and the [E, K/8, N] GPTQ slabs from per-expert matrices
+# they hold themselves, and evaluate the layer from those matrices, so a reader that picks the
+# wrong slab (always expert 0, a neighbour) cannot agree with them.  Routing here is also
+# recomputed independently: a stable argsort for the ids and scipy's softmax for the weights.
+
+def _exact_bf16_bits(v):
+    """bf16 bit patterns of values that bf16 holds exactly (asserted: the low fp32 half is zero)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32)
+    assert not np.any(u & np.uint32(0xFFFF)), "value not exact in bf16"
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _independent_routing(logits, k):
+    l = np.asarray(logits, np.float32)
+    ids = np.argsort(-l, axis=1, kind="stable")[:, :k]
+    p = scipy_softmax(l.astype(np.float64), axis=1)
+    ps = np.take_along_axis(p, ids, 1)
+    w = (ps / ps.sum(1, keepdims=True)).astype(np.float32).astype(np.float64)
+    return ids, w
+
+
+def _layer_from_matrices(x, ids, w, Wg, Wu, Wd):
+    """out[t] = sum_j w[t,j] Wd[e] (silu(Wg[e] x_t) * (Wu[e] x_t)), e = ids[t,j]; matrices [E, N, K]."""
+    T, k = ids.shape
+    out = np.zeros((T, Wd.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            g, u = Wg[e] @ x[t], Wu[e] @ x[t]
+            out[t] += w[t, j] * (Wd[e] @ (g / (1.0 + np.exp(-g)) * u))
+    return out
+
+
+@pytest.mark.parametrize("E,k", [(3, 1), (5, 2), (8, 3)])
+def test_expert_selection_bf16_hand_built_stacks(E, k):
+    T, H, I = 20, 32, 16
+    rng = np.random.default_rng(100 + E)
+    # small integers / 64: at most 4 significant bits, exact in bf16; each expert also gets its
+    # own offset (e + 1) / 64 on every entry so no two experts' matrices coincide
+    mats = [rng.integers(-6, 7, (E, n, m)) / 64.0 + (np.arange(E) + 1)[:, None, None] / 64.0
+            for n, m in ((I, H), (I, H), (H, I))]
+    x = rng.integers(-4, 5, (T, H)) / 8.0
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    cfg = MoeConfig("t", T=T, H=H, I=I, E=E, top_k=k, block_size=16)
+    d = {"cfg": cfg, "logits": logits, "x": _exact_bf16_bits(x),
+         "wg": _exact_bf16_bits(mats[0]), "wu": _exact_bf16_bits(mats[1]), "wd": _exact_bf16_bits(mats[2])}
+    ids, w = _independent_routing(logits, k)
+    ref = _layer_from_matrices(x, ids, w, *mats)
+    assert len(np.unique(ids)) >= 2          # several experts are in play, including e > 0
+    r = oracle.moe_layer(d)
+    assert np.array_equal(r["ids"], ids)
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(oracle.moe_tokens(d, range(T)), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_expert_selection_int4_hand_built_stacks():
+    T, H, I, E, k, G = 12, 64, 32, 4, 2, 32
+    rng = np.random.default_rng(77)
+
+    def proj(K, N):
+        # per expert: nibbles q, zero points z and power-of-two scales (exact in fp16), packed with
+        # the independent packer; the dense matrix [N, K] is formed here from q, z, s directly
+        q = rng.integers(0, 16, (E, K, N))
+        z = rng.integers(0, 16, (E, K // G, N))
+        s = np.float16(2.0) ** rng.integers(-7, -3, (E, K // G, N)).astype(np.float16)
+        qw = np.stack([_pack_reference(q[e], z[e])[0] for e in range(E)])
+        qz = np.stack([_pack_reference(q[e], z[e])[1] for e in range(E)])
+        dense = np.stack([((q[e] - np.repeat(z[e], G, axis=0)) * np.repeat(s[e].astype(np.float64), G, axis=0)).T
+                          for e in range(E)])
+        return {"qweight": qw, "qzeros": qz, "scales": s.view(np.uint16), "group_size": G}, dense
+
+    (wg, Wg), (wu, Wu), (wd, Wd) = proj(H, I), proj(H, I), proj(I, H)
+    assert not np.allclose(Wg[0], Wg[1])
+    x = rng.integers(-4, 5, (T, H)) / 8.0
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    cfg = MoeConfig("t", T=T, H=H, I=I, E=E, top_k=k, block_size=16, weights="int4_gptq", group_size=G)
+    d = {"cfg": cfg, "logits": logits, "x": _exact_bf16_bits(x), "gate": wg, "up": wu, "down": wd}
+    ids, w = _independent_routing(logits, k)
+    ref = _layer_from_matrices(x, ids, w, Wg, Wu, Wd)
+    assert len(np.unique(ids)) >= 2
+    r = oracle.moe_layer(d)
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(oracle.moe_tokens(d, range(T)), ref, rtol=1e-12, atol=1e-12)
