@@ -220,8 +220,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) void route_align_kernel(
     if (T <= kFusedWaves) {
         if (wave < T) route_tokens<EPL, 1>(logits, wave, 0, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
     } else {
-        for (int t = wave; t < T; t += kFusedWaves * 4)
-            route_tokens<EPL, 4>(logits, t, kFusedWaves, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
+        // four tokens per wave interleaved; two when each lane holds four logits (registers)
+        constexpr int NTOK = EPL >= 4 ? 2 : 4;
+        for (int t = wave; t < T; t += kFusedWaves * NTOK)
+            route_tokens<EPL, NTOK>(logits, t, kFusedWaves, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
     }
     __syncthreads();
     align_scatter_body<true, kFusedWaves>(s_ids, T * top_k, E, bs, nullptr, 1, counts, offsets, sorted_ids,

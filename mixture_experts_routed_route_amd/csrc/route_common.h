@@ -5,7 +5,8 @@
 // One wave64 per token.  Each lane holds up to four logits (E <= 256) in registers.
 // Selection takes top_k rounds of a wave arg-max over a 64-bit key (order-preserving image
 // of the fp32 logit, then the complement of the expert index, so equal logits pick the
-// lower index).  The weights are computed in fp64 and rounded once to fp32.
+// lower index).  Selection j is kept by lane j % 64 in its slot j / 64, so top_k may reach
+// E (up to 256).  The weights are computed in fp64 and rounded once to fp32.
 #pragma once
 
 #include "device_common.h"
@@ -91,10 +92,15 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
         }
     }
 
-    int my_e[NTOK];
-    float my_l[NTOK], top[NTOK];
+    // selection j lives in lane j % 64, slot j / 64 (top_k <= E <= 64 * EPL)
+    int my_e[NTOK][EPL];
+    float my_l[NTOK][EPL], top[NTOK];
 #pragma unroll
-    for (int n = 0; n < NTOK; ++n) { my_e[n] = 0; my_l[n] = 0.0f; top[n] = 0.0f; }
+    for (int n = 0; n < NTOK; ++n) {
+        top[n] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) { my_e[n][i] = 0; my_l[n][i] = 0.0f; }
+    }
     for (int j = 0; j < top_k; ++j) {
         uint64_t best[NTOK];
 #pragma unroll
@@ -113,7 +119,9 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
             for (int i = 0; i < EPL; ++i)
                 if (lane + 64 * i == e) key[n][i] = 0;
             if (j == 0) top[n] = l;
-            if (lane == j) { my_e[n] = e; my_l[n] = l; }
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (lane + 64 * i == j) { my_e[n][i] = e; my_l[n][i] = l; }
         }
     }
 
@@ -127,15 +135,24 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
         for (int i = 0; i < EPL; ++i)
             if (lane + 64 * i < E) part += exp(static_cast<double>(v[n][i]) - m);
         const double S = wave_sum_f64(part);
-        const double p = exp(static_cast<double>(my_l[n]) - m) / S;
+        double p[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) p[i] = exp(static_cast<double>(my_l[n][i]) - m) / S;
+        // the kept probabilities summed in slot order j = 0 .. top_k-1
         double den = 0.0;
-        for (int j = 0; j < top_k; ++j)
-            den += __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, p), j));
-        if (t < T && lane < top_k) {
-            const double wj = renorm ? p / den : p;
-            ids[static_cast<size_t>(t) * top_k + lane] = my_e[n];
-            w[static_cast<size_t>(t) * top_k + lane] = static_cast<float>(wj);
-            if (lds_ids != nullptr) lds_ids[t * top_k + lane] = my_e[n];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            for (int l = 0; l < 64 && 64 * i + l < top_k; ++l)
+                den += __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, p[i]), l));
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int j = lane + 64 * i;
+            if (t < T && j < top_k) {
+                const double wj = renorm ? p[i] / den : p[i];
+                ids[static_cast<size_t>(t) * top_k + j] = my_e[n][i];
+                w[static_cast<size_t>(t) * top_k + j] = static_cast<float>(wj);
+                if (lds_ids != nullptr) lds_ids[t * top_k + j] = my_e[n][i];
+            }
         }
     }
 }

@@ -25,6 +25,32 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _need(ok: bool, msg: str) -> None:
+    """Shape checks run before any pointer is taken: the C ABI sees no tensor sizes, so a buffer
+    smaller than the call implies must be refused here, before a kernel could read or write past it."""
+    if not ok:
+        raise ValueError(msg)
+
+
+def _rows_at_least(t: Optional[torch.Tensor], rows: int, name: str) -> None:
+    if t is not None:
+        _need(t.dim() >= 1 and t.shape[0] >= rows, f"{name} has {tuple(t.shape)}; needs >= {rows} rows")
+
+
+def _numel_at_least(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    if t is not None:
+        _need(t.numel() >= n, f"{name} has {t.numel()} elements; needs >= {n}")
+
+
+def _check_routing(r: "Routing") -> None:
+    _numel_at_least(r.counts, r.num_experts, "routing.counts")
+    _numel_at_least(r.offsets, r.num_experts + 1, "routing.offsets")
+    _numel_at_least(r.sorted_ids, r.max_pad, "routing.sorted_ids")
+    _numel_at_least(r.expert_ids, r.max_pad // r.block_size, "routing.expert_ids")
+    _numel_at_least(r.total_padded, 1, "routing.total_padded")
+    _numel_at_least(r.inv_sorted, r.num_pairs, "routing.inv_sorted")
+
+
 def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -135,6 +161,8 @@ def moe_route(logits: torch.Tensor, top_k: int, renormalize: bool = True,
         topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
     if topk_w is None:
         topk_w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _numel_at_least(topk_ids, T * top_k, "topk_ids")
+    _numel_at_least(topk_w, T * top_k, "topk_w")
     check(lib().moe_route(_dev(logits, torch.float32, "logits"), T, E, top_k, int(bool(renormalize)),
                           _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
                           _stream(logits)))
@@ -177,6 +205,7 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, block_size: int, max_pad
     r = out if out is not None else Routing.allocate(P, top_k, num_experts, block_size, topk_ids.device, max_pad)
     if r.num_pairs != P or r.num_experts != num_experts or r.block_size != block_size:
         raise ValueError("preallocated Routing does not match the call")
+    _check_routing(r)
     check(lib().moe_align(_dev(topk_ids, torch.int32, "topk_ids"), P, num_experts, block_size,
                           _dev(r.counts, torch.int32, "counts"), _dev(r.offsets, torch.int32, "offsets"),
                           _dev(r.sorted_ids, torch.int32, "sorted_ids"),
@@ -195,6 +224,9 @@ def moe_route_align(logits: torch.Tensor, top_k: int, renormalize: bool, block_s
     r = out
     if r.num_pairs != T * top_k or r.num_experts != E or r.block_size != block_size:
         raise ValueError("preallocated Routing does not match the call")
+    _check_routing(r)
+    _numel_at_least(topk_ids, T * top_k, "topk_ids")
+    _numel_at_least(topk_w, T * top_k, "topk_w")
     check(lib().moe_route_align(_dev(logits, torch.float32, "logits"), T, E, top_k, int(bool(renormalize)),
                                 _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_w, torch.float32, "topk_w"),
                                 block_size, _dev(r.counts, torch.int32, "counts"),
@@ -209,6 +241,20 @@ def moe_route_align(logits: torch.Tensor, top_k: int, renormalize: bool, block_s
 
 
 # ----------------------------------------------------------------------------- A3 / A4 grouped GEMM
+def _check_gemm_shapes(op: int, a: torch.Tensor, w0, w1, routing: "Routing", out: torch.Tensor, who: str) -> None:
+    E, N, K = w0.shape
+    _need(E == routing.num_experts, f"{who}: the weights hold {E} experts, the routing {routing.num_experts}")
+    if op == MOE_OP_GATE_UP_SILU:
+        _need(w1 is not None and tuple(w1.shape) == tuple(w0.shape),
+              f"{who}: gate and up weights must have one shape")
+    _need(a.dim() == 2 and a.shape[1] == K, f"{who}: a is {tuple(a.shape)}; its width must be K={K}")
+    rows = routing.max_pad if op == MOE_OP_DOWN else routing.num_pairs // routing.top_k
+    _rows_at_least(a, rows, f"{who}: a")
+    _need(out.dim() == 2 and out.shape[1] == N and out.shape[0] >= routing.max_pad,
+          f"{who}: out is {tuple(out.shape)}; needs [>= {routing.max_pad}, {N}]")
+    _check_routing(routing)
+
+
 def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight], routing: Routing,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """op = MOE_OP_GATE_UP_SILU (a = x [T, K], w0 = gate, w1 = up), MOE_OP_DOWN (a = Hs [max_pad, K])
@@ -219,6 +265,7 @@ def moe_grouped_gemm(op: int, a: torch.Tensor, w0: Weight, w1: Optional[Weight],
     E, N, K = w0.shape
     if out is None:
         out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=a.device)
+    _check_gemm_shapes(op, a, w0, w1, routing, out, "moe_grouped_gemm")
     s0 = w0.struct()
     s1 = w1.struct() if w1 is not None else None
     check(lib().moe_grouped_gemm(op, _dev(a, torch.bfloat16, "a"), ctypes.byref(s0),
@@ -237,6 +284,10 @@ def moe_quantize_fp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
                      routing: Optional[Routing] = None) -> None:
     """Per-row e4m3 codes and scales of bf16 rows; with ``routing`` only the real sorted rows."""
     rows, k = x.shape
+    _need(tuple(q.shape) == (rows, k), f"moe_quantize_fp8: q is {tuple(q.shape)}; needs {(rows, k)}")
+    _numel_at_least(scale, rows, "moe_quantize_fp8: scale")
+    if routing is not None:
+        _numel_at_least(routing.sorted_ids, rows, "moe_quantize_fp8: routing.sorted_ids")
     check(lib().moe_quantize_fp8(_dev(x, torch.bfloat16, "x"), rows, k,
                                  _dev(routing.sorted_ids, torch.int32, "sorted_ids") if routing is not None else None,
                                  routing.num_pairs if routing is not None else 0, _dev(q, torch.uint8, "q"),
@@ -250,6 +301,8 @@ def moe_grouped_gemm_fp8(op: int, a: torch.Tensor, a_scale: torch.Tensor, w0: Fp
     E, N, K = w0.shape
     if out is None:
         out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=a.device)
+    _check_gemm_shapes(op, a, w0, w1, routing, out, "moe_grouped_gemm_fp8")
+    _numel_at_least(a_scale, a.shape[0], "moe_grouped_gemm_fp8: a_scale")
     s0 = w0.struct()
     s1 = w1.struct() if w1 is not None else None
     check(lib().moe_grouped_gemm_fp8(op, _dev(a, torch.uint8, "a"), _dev(a_scale, torch.float32, "a_scale"),
@@ -312,6 +365,14 @@ def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routi
         row_end = routing.max_pad
     if xa is None:
         xa = torch.empty((max(row_end - row_offset, 1), tables.max_rank), dtype=torch.bfloat16, device=x.device)
+    who = "moe_lora_fold"
+    _need(x.dim() == 2 and x.shape[1] == tables.k_in, f"{who}: x is {tuple(x.shape)}; width must be {tables.k_in}")
+    _rows_at_least(x, routing.num_pairs // routing.top_k if x_gather else routing.max_pad, f"{who}: x")
+    _need(base.dim() == 2 and base.shape[1] == tables.n_out and base.shape[0] >= routing.max_pad,
+          f"{who}: base is {tuple(base.shape)}; needs [>= {routing.max_pad}, {tables.n_out}]")
+    _need(xa.dim() == 2 and xa.shape[1] == tables.max_rank, f"{who}: xa must be [cap, {tables.max_rank}]")
+    _numel_at_least(row_adapter, routing.num_pairs // routing.top_k, f"{who}: row_adapter")
+    _check_routing(routing)
     check(lib().moe_lora_fold(
         _dev(x, torch.bfloat16, "x"), _dev(base, torch.bfloat16, "base"), _dev(tables.a_table, torch.int64, "a_table"),
         _dev(tables.b_table, torch.int64, "b_table"), _dev(tables.scale_table, torch.float32, "scale_table"),
@@ -340,6 +401,8 @@ def moe_grouped_gemm_gate_up_lora(x: torch.Tensor, gate: Bf16Weight, up: Bf16Wei
         raise ValueError(f"xa must be [2, {routing.max_pad}, {rank}]")
     if out is None:
         out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=x.device)
+    _check_gemm_shapes(MOE_OP_GATE_UP_SILU, x, gate, up, routing, out, "moe_grouped_gemm_gate_up_lora")
+    _numel_at_least(row_adapter, routing.num_pairs // routing.top_k, "moe_grouped_gemm_gate_up_lora: row_adapter")
     sg, su = gate.struct(), up.struct()
 
     def tab(t):
@@ -385,6 +448,8 @@ def moe_lora_gather_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables
         raise ValueError(f"xa must be [>= {n_slots}, {tables.max_rank}] (got {tuple(xa.shape)})")
     if x.shape[1] != tables.k_in or base.shape[1] != tables.n_out:
         raise ValueError("x / base widths do not match the LoRA tables")
+    _numel_at_least(row_map, n_slots, "moe_lora_gather_fold: row_map")
+    _numel_at_least(row_adapter, n_slots // max(top_k, 1), "moe_lora_gather_fold: row_adapter")
     check(lib().moe_lora_gather_fold(
         _dev(x, torch.bfloat16, "x"), x.shape[0], _dev(base, torch.bfloat16, "base"), base.shape[0],
         _dev(indices, torch.int32, "indices"), n_slots, top_k, int(bool(x_gather)),
@@ -403,6 +468,8 @@ def moe_combine(ys: torch.Tensor, inv_sorted: Optional[torch.Tensor], topk_w: to
     H = ys.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=ys.device)
+    _need(out.dim() == 2 and tuple(out.shape) == (T, H), f"moe_combine: out is {tuple(out.shape)}; needs {(T, H)}")
+    _numel_at_least(inv_sorted, T * k, "moe_combine: inv_sorted")
     check(lib().moe_combine(_dev(ys, torch.bfloat16, "ys"),
                             _dev(inv_sorted, torch.int32, "inv_sorted") if inv_sorted is not None else None,
                             _dev(topk_w, torch.float32, "topk_w"), _dev(out, torch.bfloat16, "out"), T, k, H,

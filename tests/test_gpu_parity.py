@@ -67,6 +67,12 @@ ROUTE_CASES = [(name, cfg) for name, cfg in CONFIGS.items()] + [
     ("E1", MoeConfig("E1", T=17, H=8, I=8, E=1, top_k=1, block_size=16, seed=13)),
     ("k_eq_E", MoeConfig("kE", T=50, H=8, I=8, E=6, top_k=6, block_size=16, seed=14)),
     ("no_renorm", MoeConfig("nr", T=500, H=8, I=8, E=64, top_k=6, block_size=16, renormalize=False, seed=15)),
+    # top_k above one wave's 64 lanes: selections 64.. live in the lanes' later slots
+    ("E256_k96", MoeConfig("E256k96", T=70, H=8, I=8, E=256, top_k=96, block_size=64, seed=16)),
+    ("E200_k130_no_renorm", MoeConfig("E200k130", T=33, H=8, I=8, E=200, top_k=130, block_size=16,
+                                      renormalize=False, seed=17)),
+    ("E256_k256", MoeConfig("E256k256", T=9, H=8, I=8, E=256, top_k=256, block_size=16, seed=18)),
+    ("E128_k65", MoeConfig("E128k65", T=40, H=8, I=8, E=128, top_k=65, block_size=32, seed=19)),
 ]
 
 
@@ -1016,6 +1022,8 @@ ROUTE_ALIGN_CASES = [
     ("T40_four_per_wave", MoeConfig("t40", T=40, H=8, I=8, E=128, top_k=8, block_size=32, seed=27)),
     ("T64_E256", MoeConfig("t64", T=64, H=8, I=8, E=256, top_k=4, block_size=16, seed=28)),
     ("T65_two_calls", MoeConfig("t65", T=65, H=8, I=8, E=32, top_k=2, block_size=16, seed=29)),
+    ("E256_k96_one_launch", MoeConfig("k96", T=20, H=8, I=8, E=256, top_k=96, block_size=16, seed=30)),
+    ("E192_k100_two_calls", MoeConfig("k100", T=30, H=8, I=8, E=192, top_k=100, block_size=16, seed=31)),
 ]
 
 
