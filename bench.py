@@ -3,14 +3,21 @@
 One step = the whole path over one batch of synthetic tokens:
 route -> align -> grouped gate/up + SiLU -> grouped down -> [LoRA fold] -> combine.
 
-Prints ONE JSON line (metric = MoE layer tokens/s).  The grouped gate/up GEMM is
-timed on its own with HIP events on the launch stream inside the timed region and
-reported against the bf16 MFMA peak; the CPU oracle is timed on a bounded token
-sample of the same workload on the host's cores.
+By default the five workloads the metric is quoted on run one after the other (tiny,
+mixtral_prefill, finegrained_skewed, decode_int4, lora_prefill), and ONE JSON line is printed:
+``value`` is the tokens/s of mixtral_prefill (the largest prefill workload), ``roofline`` is its
+dominant kernel (the grouped gate/up GEMM), and ``configs`` holds every workload's own figures:
+tokens/s, per-kernel times, a roofline object per GEMM (and per LoRA fold), and the CPU oracle
+timed on a bounded token sample of that workload on the host's cores.  ``--config NAME`` runs a
+single workload (used for the rocprofv3 runs whose summaries sit in profiles/).
+
+Each kernel is timed with HIP events recorded on the stream it is launched on (the current
+torch stream, which the binding passes to every call), inside the timed region.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -23,13 +30,19 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+WORKLOADS = ["tiny", "mixtral_prefill", "finegrained_skewed", "decode_int4", "lora_prefill"]
+HEADLINE = "mixtral_prefill"
+# token sample of the CPU oracle per workload, and the host seconds it is repeated for (bounded so the
+# five samples together take well under a minute)
+CPU_SAMPLE = {"tiny": (64, 2.0), "mixtral_prefill": (4096, 8.0), "finegrained_skewed": (2048, 4.0),
+              "decode_int4": (16, 3.0), "lora_prefill": (1024, 4.0)}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-
-
+# ----------------------------------------------------------------------------- algorithmic work
 def gemm_flops(cfg, op: str) -> float:
     """Algorithmic FLOPs of one grouped GEMM launch: 2*K*N per real (token, expert) pair and projection."""
     per_pair = {"gate_up": 2 * 2 * cfg.H * cfg.I, "down": 2 * cfg.H * cfg.I}[op]
@@ -63,11 +76,43 @@ def gemm_bytes(cfg, op: str, active_experts: int) -> float:
     return w + act
 
 
+def fold_work(cfg, counts, lora_ids):
+    """Algorithmic work of the down-projection LoRA fold: per adapted real row, the Hs row read,
+    the Ys row read and written and the bf16 xa row written and read back (at the padded rank the
+    kernels run), plus the A_e and B_e of every adapted expert that has rows; FLOPs at the real
+    rank (2 * rank * (I + H) per adapted real row)."""
+    R, r = cfg.lora_max_rank, cfg.lora_rank
+    ad = [int(e) for e in lora_ids if int(e) < len(counts) and counts[int(e)] > 0]
+    rows = int(sum(int(counts[e]) for e in ad))
+    bytes_ = rows * (cfg.I * 2 + 2 * cfg.H * 2 + 2 * R * 2) + len(ad) * (R * cfg.I * 2 + cfg.H * R * 2)
+    return float(2 * r * (cfg.I + cfg.H) * rows), float(bytes_), rows
+
+
+def roofline(flops: float, bytes_: float, ms: float, peak_mfma: float, kernel: str, traffic=None):
+    """Roofline object of one kernel: the bound is chosen from its arithmetic intensity against the
+    ridge of the MFMA peak and HBM."""
+    ai = flops / bytes_ if bytes_ else float("inf")
+    if ai >= peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
+        ach = flops / (ms / 1e3) / 1e12
+        r = {"bound": "mfma", "achieved": ach, "peak": peak_mfma, "unit": "TFLOP/s"}
+    else:
+        ach = bytes_ / (ms / 1e3) / 1e9
+        r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = traffic
+    r["kernel"] = kernel
+    r["ms"] = ms
+    r["algorithmic"] = {"flops": flops, "bytes": bytes_, "flop_per_byte": ai}
+    return r
+
+
+# ----------------------------------------------------------------------------- helpers
 def clone_layer(layer):
     """Same weights in fresh buffers (so repeated steps cannot be served from the 256 MB MALL)."""
     import copy
     import mixture_experts_routed_route_amd as m
     c = copy.copy(layer)
+
     def cw(w):
         if isinstance(w, m.Bf16Weight):
             return m.Bf16Weight(w.w.clone())
@@ -79,7 +124,7 @@ def clone_layer(layer):
 
 
 def measured_traffic(workload: str, role: str):
-    """HBM bytes per launch of one grouped GEMM from the committed FETCH_SIZE/WRITE_SIZE summary of
+    """HBM bytes per launch of one kernel from the committed FETCH_SIZE/WRITE_SIZE summary of
     this workload (already scaled by the copy calibration), or None when there is none or the
     kernel's source files have changed since the counters were taken."""
     import hashlib
@@ -96,20 +141,27 @@ def measured_traffic(workload: str, role: str):
         return None
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc", f), "rb").read())
+        p = os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc", f)
+        if not os.path.exists(p):
+            return None
+        h.update(open(p, "rb").read())
     return float(kv[f"{role}.traffic_bytes"]) if h.hexdigest() == want else None
 
 
-def layer_flops(cfg) -> float:
-    return 6.0 * cfg.H * cfg.I * cfg.P
+def host_cores() -> int:
+    """Host cores this process may run on (the CPU oracle's BLAS uses up to that many threads)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
-def cpu_baseline(cfg, d, budget_tokens: int, min_seconds: float = 10.0, max_runs: int = 8):
-    """The oracle as it stands, on the first ``budget_tokens`` tokens of the same workload, run
-    repeatedly until at least ``min_seconds`` of host time have passed (at most ``max_runs`` runs)."""
+def cpu_baseline(cfg, d, tokens: int, min_seconds: float, max_runs: int = 200):
+    """The oracle as it stands, on the first ``tokens`` tokens of the same workload, run repeatedly
+    until at least ``min_seconds`` of host time have passed (at most ``max_runs`` runs)."""
     import oracle
     from threadpoolctl import threadpool_info
-    T = min(cfg.T, budget_tokens)
+    T = min(cfg.T, tokens)
     sub = dict(d)
     sub["cfg"] = cfg.with_(T=T)
     sub["logits"] = d["logits"][:T]
@@ -121,45 +173,72 @@ def cpu_baseline(cfg, d, budget_tokens: int, min_seconds: float = 10.0, max_runs
         dt = time.perf_counter() - t0
         if dt >= min_seconds or runs >= max_runs:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": runs * T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    cores = host_cores()
+    blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": runs * T / dt, "unit": "tokens/s", "cores": min(cores, blas), "kind": "oracle",
             "sample": f"{runs} run(s) of the first {T} of {cfg.T} tokens of {cfg.name}, whole layer (route, "
-                      f"align, grouped GEMMs, combine) in fp64 numpy; {dt:.1f} s in total"}
+                      f"align, grouped GEMMs, {'LoRA fold, ' if cfg.lora_rank else ''}combine) in fp64 numpy; "
+                      f"{dt:.1f} s in total; {cores} host cores available, BLAS threads {blas}"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="mixtral_prefill")
-    ap.add_argument("--cpu-tokens", type=int, default=4096, help="token sample of the CPU oracle leg")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rotate", type=int, default=0,
-                    help="independent weight copies cycled through (0: enough for >= 1 GiB of weights, max 4)")
-    ap.add_argument("--graph", action="store_true",
-                    help="time steps replayed from HIP graphs (one captured step per weight copy); the "
-                         "per-kernel figures then come from an eager pass of the same steps")
-    ap.add_argument("--fold", default="auto", choices=["auto", "grouped", "gather"],
-                    help="LoRA fold over the sorted rows or slot by slot (auto: by the padding share)")
-    ap.add_argument("--gate-up-lora", default="fused", choices=["fused", "unfused"],
-                    help="gate/up LoRA folded in the gate/up GEMM's epilogue, or the page's unfused order")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures the single-GPU path only; --gpus {args.gpus} is not supported "
-              "(multi-GPU expert/tensor parallel sharding is not part of this build)", file=sys.stderr)
-        sys.exit(2)
+# ----------------------------------------------------------------------------- measured ceilings
+def measure_ceilings(dev) -> dict:
+    """What this chip delivers, measured beside the datasheet peaks: a 1 GiB device copy (torch's
+    copy kernel; read + write bytes), a 2 GiB streaming read and a register-only bf16 MFMA loop
+    (include/moe_probes.h).  Each is the best of five timed launches after one warm-up."""
+    import torch
+    import mixture_experts_routed_route_amd as m
+    from mixture_experts_routed_route_amd._lib import check, lib
 
+    def best(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts)
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    copy_ms = best(lambda: dst.copy_(src))
+    del dst
+    big = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(5)
+    blocks = 256 * 8
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    read_ms = best(lambda: check(lib().moe_probe_stream_read(big.data_ptr(), big.numel(), sink.data_ptr(), blocks,
+                                                             stream)))
+    del big, src
+    iters, mblocks = 20000, 512          # 2 workgroups of 4 waves per compute unit
+    fsink = torch.empty(mblocks * 256, dtype=torch.float32, device=dev)
+    mfma_ms = best(lambda: check(lib().moe_probe_mfma_bf16(iters, fsink.data_ptr(), mblocks, stream)))
+    mfma_flops = mblocks * 4 * iters * 8 * 32768
+    torch.cuda.synchronize()
+    res = {"copy_GBs": 2 * (1 << 30) / (copy_ms / 1e3) / 1e9,
+           "stream_read_GBs": (2 << 30) / (read_ms / 1e3) / 1e9,
+           "mfma_bf16_TFLOPs": mfma_flops / (mfma_ms / 1e3) / 1e12,
+           "how": "best of 5: 1 GiB torch device copy (read+write bytes); 2 GiB streaming read "
+                  "(moe_probe_stream_read, 2048 workgroups); register-only 32x32x16 bf16 MFMA loop "
+                  "(moe_probe_mfma_bf16, 2 workgroups of 4 waves per CU, pseudo-random operands)"}
+    log(f"[bench] ceilings: copy {res['copy_GBs']:.0f} GB/s, stream read {res['stream_read_GBs']:.0f} GB/s, "
+        f"MFMA bf16 {res['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
+    return res
+
+
+# ----------------------------------------------------------------------------- one workload
+def run_workload(name: str, args, dev) -> dict:
     import numpy as np
     import torch
     import mixture_experts_routed_route_amd as m
     from moe_synth import CONFIGS, make_inputs
 
-    cfg = CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    log(f"[bench] generating {cfg.name} inputs")
+    cfg = CONFIGS[name]
+    log(f"[bench] {name}: generating inputs")
     d = make_inputs(cfg)
     layer = m.MoeLayer.from_arrays(d, dev, fold=args.fold, gate_up_fused=args.gate_up_lora == "fused")
     b = layer.plan(cfg.T, dev)
@@ -169,24 +248,25 @@ def main():
     logits = torch.from_numpy(d["logits"]).to(dev)
     x = torch.from_numpy(d["x"]).view(torch.bfloat16).to(dev)
     torch.cuda.synchronize()
+    has_fold = layer.lora is not None
 
     def step(i, ev=None):
-        layer = layers[i % rot]
-        layer.route_align(logits, b)
+        ly = layers[i % rot]
+        ly.route_align(logits, b)
         if ev is not None:
             ev[0].record()
-        layer.gate_up_stage(x, b)
+        ly.gate_up_stage(x, b)
         if ev is not None:
             ev[1].record()
-        layer.down_stage(b)
+        ly.down_stage(b)
         if ev is not None:
             ev[2].record()
-        layer.lora_fold(b)
+        ly.lora_fold(b)
         if ev is not None:
             ev[3].record()
-        layer.combine(b)
+        ly.combine(b)
 
-    log(f"[bench] warmup {args.warmup}")
+    log(f"[bench] {name}: warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -206,18 +286,18 @@ def main():
         for i in range(args.warmup):
             graphs[i % rot].replay()
         torch.cuda.synchronize()
-        log(f"[bench] timing {args.steps} graph replays")
+        log(f"[bench] {name}: timing {args.steps} graph replays")
         t0 = time.perf_counter()
         for i in range(args.steps):
             graphs[i % rot].replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-        log("[bench] per-kernel timing: eager pass")
+        log(f"[bench] {name}: per-kernel timing from an eager pass")
         for i in range(args.steps):
             step(i, events[i])
         torch.cuda.synchronize()
     else:
-        log(f"[bench] timing {args.steps} steps")
+        log(f"[bench] {name}: timing {args.steps} steps")
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -227,76 +307,140 @@ def main():
     ms = dt * 1e3 / args.steps
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if layer.lora is not None else None
+    fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if has_fold else None
+
+    wt = {"bf16": "gemm_bf16_kernel", "fp8": "gemm_fp8_kernel", "int4_gptq": "gemm_int4_kernel"}[cfg.weights]
     gu_what = ("gemm_bf16_kernel<gate_up> with the gate/up LoRA epilogue (+ 2 shrinks)"
                if layer.gate_up_lora and layer.gate_up_fused
                else "gate/up stage: 2 gathered GEMMs, 2 LoRA folds, SiLU*up" if layer.gate_up_lora
                else "gate/up stage: x quantisation + gemm_fp8_kernel<gate_up>" if cfg.weights == "fp8"
-               else ("gemm_bf16_kernel" if cfg.weights == "bf16" else "gemm_int4_kernel") + "<gate_up>")
+               else f"{wt}<gate_up>")
+    dn_what = ("down stage: Hs quantisation + gemm_fp8_kernel<down>" if cfg.weights == "fp8" else f"{wt}<down>")
     peak_mfma = PEAK_FP8_TFLOPS if cfg.weights == "fp8" else PEAK_BF16_TFLOPS
-    tokens_s = cfg.T / (ms / 1e3)
-    active = int((b.routing.counts > 0).sum().item())
-    gu_bytes = gemm_bytes(cfg, "gate_up", active)
-    gu_tflops = gemm_flops(cfg, "gate_up") / (gu_ms / 1e3) / 1e12
-    dn_tflops = gemm_flops(cfg, "down") / (dn_ms / 1e3) / 1e12
+    counts = b.routing.counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    roofs = {
+        "gate_up": roofline(gemm_flops(cfg, "gate_up"), gemm_bytes(cfg, "gate_up", active), gu_ms, peak_mfma,
+                            gu_what, measured_traffic(cfg.name, "gate_up")),
+        "down": roofline(gemm_flops(cfg, "down"), gemm_bytes(cfg, "down", active), dn_ms, peak_mfma, dn_what,
+                         measured_traffic(cfg.name, "down")),
+    }
+    if has_fold:
+        ff, fb, frows = fold_work(cfg, counts, d["lora_ids"])
+        mode = layer.fold_mode(b)
+        roofs["lora_fold"] = roofline(ff, fb, fold_ms, peak_mfma,
+                                      "lora_shrink_kernel + lora_expand_fold_kernel" if mode == "grouped"
+                                      else "gather_shrink_kernel + gather_expand_kernel",
+                                      measured_traffic(cfg.name, "lora_fold"))
+        roofs["lora_fold"]["adapted_rows"] = frows
     gemm_tflops = (gemm_flops(cfg, "gate_up") + gemm_flops(cfg, "down")) / ((gu_ms + dn_ms) / 1e3) / 1e12
-    log(f"[bench] step {ms:.3f} ms; gate/up {gu_ms:.3f} ms ({gu_tflops:.1f} TFLOP/s); "
-        f"down {dn_ms:.3f} ms ({dn_tflops:.1f} TFLOP/s); grouped GEMMs {gemm_tflops:.1f} TFLOP/s"
+    log(f"[bench] {name}: step {ms:.3f} ms ({cfg.T / (ms / 1e3):.4g} tokens/s); gate/up {gu_ms:.3f} ms; "
+        f"down {dn_ms:.3f} ms; grouped GEMMs {gemm_tflops:.1f} TFLOP/s"
         + (f"; LoRA fold ({layer.fold_mode(b)}) {1e3 * fold_ms:.1f} us" if fold_ms is not None else ""))
+    for k, r in roofs.items():
+        log(f"[bench] {name}: {k} roofline {r['bound']} {r['achieved']:.1f} {r['unit']} "
+            f"({100 * r['frac']:.1f}% of peak), AI {r['algorithmic']['flop_per_byte']:.1f} flop/B")
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         log("[bench] copy calibration: 1 GiB device-to-device copy done")
 
-    ai = gemm_flops(cfg, "gate_up") / gu_bytes
-    if ai >= peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": gu_tflops, "peak": peak_mfma, "unit": "TFLOP/s"}
-    else:
-        gbs = gu_bytes / (gu_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(cfg.name, "gate_up")
-    roof["kernel"] = gu_what
-    roof["algorithmic"] = {"flops": gemm_flops(cfg, "gate_up"), "bytes": gu_bytes, "active_experts": active,
-                           "flop_per_byte": ai}
-    log(f"[bench] gate/up roofline: {roof['bound']} {roof['achieved']:.1f} {roof['unit']} "
-        f"({100 * roof['frac']:.1f}% of peak), AI {ai:.0f} flop/B, {active} active experts, rotate {rot}")
-
-    cpu = None
+    res = {
+        "workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
+        "top_k": cfg.top_k, "block_size": cfg.block_size, "weights": cfg.weights, "lora_rank": cfg.lora_rank,
+        **({"lora_fold": layer.fold_mode(b)} if has_fold else {}),
+        **({"lora_gate_up": "fused" if layer.gate_up_fused else "unfused"} if layer.gate_up_lora else {}),
+        "launch": "hip_graph" if args.graph else "eager", "weight_copies_rotated": rot,
+        "active_experts": active,
+        "tokens_per_s": cfg.T / (ms / 1e3), "ms_per_step": ms,
+        "kernels_ms": {"gate_up": gu_ms, "down": dn_ms, **({"lora_fold": fold_ms} if has_fold else {})},
+        "grouped_gemm_tflops": gemm_tflops,
+        "roofline": roofs,
+        "cpu_baseline": None,
+    }
+    del layers, layer, b, logits, x
+    gc.collect()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu oracle on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(cfg, d, args.cpu_tokens)
-        log(f"[bench] cpu oracle {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+        tok, secs = CPU_SAMPLE.get(name, (args.cpu_tokens or 1024, 4.0))
+        if args.cpu_tokens:
+            tok = args.cpu_tokens
+        log(f"[bench] {name}: cpu oracle on {min(tok, cfg.T)} tokens")
+        res["cpu_baseline"] = cpu_baseline(cfg, d, tok, secs)
+        log(f"[bench] {name}: cpu oracle {res['cpu_baseline']['value']:.2f} tokens/s")
+    del d
+    gc.collect()
+    return res
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="all", help="'all' (the five workloads, mixtral_prefill headline) or one name")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="token sample of the CPU oracle leg (0: per workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="independent weight copies cycled through (0: enough for >= 1 GiB of weights, max 4)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time steps replayed from HIP graphs (one captured step per weight copy); the "
+                         "per-kernel figures then come from an eager pass of the same steps")
+    ap.add_argument("--fold", default="auto", choices=["auto", "grouped", "gather"],
+                    help="LoRA fold over the sorted rows or slot by slot (auto: by the padding share)")
+    ap.add_argument("--gate-up-lora", default="fused", choices=["fused", "unfused"],
+                    help="gate/up LoRA folded in the gate/up GEMM's epilogue, or the page's unfused order")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / stream-read / MFMA-loop ceilings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference for the FETCH_SIZE/WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures the single-GPU path only; --gpus {args.gpus} is not supported "
+              "(multi-GPU expert/tensor parallel sharding is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_synth import CONFIGS
+    names = WORKLOADS if args.config == "all" else [args.config]
+    for n in names:
+        if n not in CONFIGS:
+            sys.exit(f"unknown workload {n}; known: {', '.join(CONFIGS)}")
+    dev = torch.device("cuda:0")
+    ceilings = None if args.no_ceilings else measure_ceilings(dev)
+    results = {}
+    for n in names:
+        results[n] = run_workload(n, args, dev)
+    head = results[HEADLINE] if HEADLINE in results else results[names[0]]
+    peak = PEAK_FP8_TFLOPS if head["weights"] == "fp8" else PEAK_BF16_TFLOPS
+    gu = head["roofline"]["gate_up"]
     line = {
         "metric": "MoE layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA / HBM peak), 1 GPU",
-        "value": tokens_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8 e4m3 x fp8 e4m3, fp32 accumulate"}.get(
-            cfg.weights, "int4 weights x bf16, fp32 accumulate"),
+            head["weights"], "int4 weights x bf16, fp32 accumulate"),
         "data": "synthetic (seeded numpy PCG64; random-init expert weights)",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
-                   "experts": cfg.E, "top_k": cfg.top_k, "block_size": cfg.block_size,
-                   "weights": cfg.weights, "lora_rank": cfg.lora_rank,
-                   **({"lora_fold": layer.fold_mode(b)} if layer.lora is not None else {}),
-                   **({"lora_gate_up": "fused" if layer.gate_up_fused else "unfused"} if layer.gate_up_lora else {}),
-                   "launch": "hip_graph" if args.graph else "eager"},
-        "grouped_gemm_tflops": gemm_tflops,
-        "grouped_gemm_frac_mfma_peak": gemm_tflops / peak_mfma,
-        "kernels_ms": {"gate_up": gu_ms, "down": dn_ms,
-                       **({"lora_fold": fold_ms} if fold_ms is not None else {})},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": {k: head[k] for k in ("workload", "tokens", "hidden", "intermediate", "experts", "top_k",
+                                         "block_size", "weights", "lora_rank", "launch")},
+        "grouped_gemm_tflops": head["grouped_gemm_tflops"],
+        "grouped_gemm_frac_mfma_peak": head["grouped_gemm_tflops"] / peak,
+        "kernels_ms": head["kernels_ms"],
+        "roofline": {k: gu[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                        "algorithmic")},
+        "cpu_baseline": head["cpu_baseline"],
+        "ceilings": ceilings,
+        "configs": results,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,4 +1,5 @@
-"""ctypes view of the C ABI in ``include/moe_mi355x.h`` (``_lib/libmoe_mi355x.so``).
+"""ctypes view of the C ABI in ``include/moe_mi355x.h`` and ``include/moe_probes.h``
+(``_lib/libmoe_mi355x.so``).
 
 No fallback: if the library is missing, loading raises and nothing runs.
 """
@@ -54,6 +55,9 @@ SIGNATURES = {
                                        c_int32, c_void_p, c_void_p]),
     "moe_combine": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int64,
                               c_void_p]),
+    # include/moe_probes.h: ceiling probes, not steps of the path
+    "moe_probe_stream_read": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_void_p]),
+    "moe_probe_mfma_bf16": (c_int32, [c_int64, c_void_p, c_int32, c_void_p]),
 }
 
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libmoe_mi355x.so")
 OBJ_DIR = os.path.join(REPO, "_build")
 
 SOURCES = ["route.hip", "align.hip", "combine.hip", "gemm_bf16.hip", "gemm_int4.hip", "lora_fold.hip",
-           "silu_mul.hip", "gemm_fp8.hip", "api.cpp"]
+           "silu_mul.hip", "gemm_fp8.hip", "probes.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed-fp32 VALU forms are kept out of the generated code (plain fp32 VALU only)

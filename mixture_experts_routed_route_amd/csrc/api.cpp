@@ -1,6 +1,7 @@
 // C ABI of the MoE expert path (declared in include/moe_mi355x.h): host-side argument
 // checks, pure host helpers, and the launches of the gfx950 kernels.
 #include "../../include/moe_mi355x.h"
+#include "../../include/moe_probes.h"
 
 #include <hip/hip_runtime.h>
 
@@ -572,6 +573,25 @@ moe_status moe_combine(const uint16_t* ys, const int32_t* inv_sorted, const floa
                  "%s: slot-major combine needs ys_rows >= num_tokens*top_k", who);
     return launched(who, moe::launch_combine(ys, inv_sorted, topk_w, out, num_tokens, top_k, hidden, ys_rows,
                                              static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ ceiling probes (moe_probes.h)
+moe_status moe_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, moe_stream stream) {
+    const char* who = "moe_probe_stream_read";
+    REQUIRE_PTR(who, src);
+    REQUIRE_PTR(who, sink);
+    REQUIRE(bytes > 0 && bytes % 16 == 0, "%s: bytes %lld must be a positive multiple of 16", who,
+            static_cast<long long>(bytes));
+    REQUIRE(blocks >= 1 && blocks <= (1 << 20), "%s: blocks %d not in [1, 2^20]", who, blocks);
+    return launched(who, moe::launch_probe_stream_read(src, bytes, sink, blocks, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_probe_mfma_bf16(int64_t iters, float* sink, int32_t blocks, moe_stream stream) {
+    const char* who = "moe_probe_mfma_bf16";
+    REQUIRE_PTR(who, sink);
+    REQUIRE(iters >= 1, "%s: iters %lld < 1", who, static_cast<long long>(iters));
+    REQUIRE(blocks >= 1 && blocks <= (1 << 20), "%s: blocks %d not in [1, 2^20]", who, blocks);
+    return launched(who, moe::launch_probe_mfma_bf16(iters, sink, blocks, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -87,4 +87,8 @@ hipError_t launch_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* 
                                    const uint64_t* b_tab, const float* s_tab, int n_tab, int k_in, int n_out,
                                    int max_rank, uint16_t* xa, hipStream_t s);
 
+// probes.hip (ceiling probes, not steps of the path)
+hipError_t launch_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks, hipStream_t s);
+hipError_t launch_probe_mfma_bf16(int64_t iters, float* sink, int blocks, hipStream_t s);
+
 }  // namespace moe

@@ -9,8 +9,9 @@ HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
 
 
 def header_functions():
-    """Names of the functions ``include/moe_mi355x.h`` declares."""
-    src = open(HEADER).read()
+    """Names of the functions the headers under ``include/`` declare."""
+    import glob
+    src = "\n".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
 

@@ -31,7 +31,24 @@ def test_algorithmic_work_of_the_mixtral_workload():
     w = 8 * 2 * 4096 * 14336 * 2
     assert bench.gemm_bytes(cfg, "gate_up", 8) == w + 4096 * 4096 * 2 + P * 14336 * 2
     assert bench.gemm_bytes(cfg, "down", 8) == w / 2 + P * 14336 * 2 + P * 4096 * 2
-    assert bench.layer_flops(cfg) == bench.gemm_flops(cfg, "gate_up") + bench.gemm_flops(cfg, "down")
+
+
+def test_algorithmic_work_of_the_lora_fold():
+    cfg = CONFIGS["lora_prefill"]             # I=1408, H=4096, rank 16 padded to 64
+    counts = [10, 7, 0, 3]                    # expert 2 adapted but idle, expert 1 not adapted
+    flops, bytes_, rows = bench.fold_work(cfg, counts, [0, 2, 3])
+    assert rows == 13
+    assert flops == 2 * 16 * (1408 + 4096) * 13
+    per_row = 1408 * 2 + 2 * 4096 * 2 + 2 * 64 * 2
+    assert bytes_ == 13 * per_row + 2 * (64 * 1408 * 2 + 4096 * 64 * 2)
+
+
+def test_roofline_bound_follows_the_ridge():
+    r = bench.roofline(1e12, 1e9, 1.0, 2500.0, "k")       # 1000 flop/B > ridge 312.5
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and abs(r["achieved"] - 1000.0) < 1e-9
+    assert abs(r["frac"] - 0.4) < 1e-12
+    r = bench.roofline(1e10, 1e9, 1.0, 2500.0, "k")       # 10 flop/B
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and abs(r["achieved"] - 1000.0) < 1e-9
 
 
 def test_algorithmic_bytes_of_gptq_weights():
@@ -81,8 +98,8 @@ def test_traffic_figure_only_for_the_profiled_sources(tmp_path, monkeypatch):
 def test_cpu_baseline_object():
     cfg = MoeConfig("bench_tiny", T=48, H=64, I=32, E=4, top_k=2, block_size=16, seed=3)
     d = make_inputs(cfg)
-    cpu = bench.cpu_baseline(cfg, d, budget_tokens=32, min_seconds=0.0, max_runs=2)
+    cpu = bench.cpu_baseline(cfg, d, tokens=32, min_seconds=0.0, max_runs=2)
     assert set(cpu) == {"value", "unit", "cores", "kind", "sample"}
     assert cpu["kind"] == "oracle" and cpu["unit"] == "tokens/s"
-    assert cpu["value"] > 0 and cpu["cores"] >= 1
+    assert cpu["value"] > 0 and 1 <= cpu["cores"] <= len(os.sched_getaffinity(0))
     assert "32 of 48 tokens" in cpu["sample"]
