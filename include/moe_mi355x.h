@@ -6,6 +6,7 @@
  *   moe_route         top-k softmax routing of the router logits
  *   moe_align         per-expert histogram, block-padded expert_offsets,
  *                     sorted pair ids with sentinels, one expert id per block
+ *   moe_align_noalloc moe_align without a workspace (static table; callers that cannot allocate)
  *   moe_route_align   the two above in one call (one launch for decode batches)
  *   moe_grouped_gemm  grouped gate/up GEMM with fused SiLU(gate)*up, the grouped
  *                     down GEMM, and one gathered projection without activation
@@ -32,7 +33,8 @@
  *    uint16_t bit patterns.  Layouts are row-major and contiguous.
  *  - The library allocates no memory, never synchronises, never reads device
  *    data on the host, and enqueues work only on `stream` (a hipStream_t; NULL
- *    is the null stream).  Every launch grid is fixed by host scalars alone, so
+ *    is the null stream).  Its one piece of device memory of its own is the
+ *    static 1 MiB table of moe_align_noalloc, part of the loaded code object.  Every launch grid is fixed by host scalars alone, so
  *    a sequence of calls can be captured in a HIP graph.
  *  - Return value: MOE_OK, or a negative moe_status.  Every precondition the
  *    host can check is checked before anything is enqueued; the failing call
@@ -140,6 +142,20 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_exp
                      int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
                      int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, void* workspace,
                      int64_t workspace_bytes, moe_stream stream);
+
+/* A2 without a workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * error behaviour as moe_align, minus workspace/workspace_bytes: the per-chunk histogram table
+ * lives in a static device array of the library (1 MiB per GPU, 2^18 int32 cells, held until the
+ * process ends).  ceil(num_pairs / 2048) * num_experts must not exceed 2^18 (for example 2^21
+ * pairs at 256 experts); above that the call returns MOE_EUNSUPPORTED before anything is enqueued.
+ * The call allocates nothing.  Every call on one GPU uses that GPU's one table and overwrites the
+ * cells it reads, so calls ordered on one stream are independent, while calls that overlap on one
+ * GPU (concurrent streams) race.  The first call on a device looks up the table's address; make it
+ * outside graph capture. */
+moe_status moe_align_noalloc(const int32_t* topk_ids, int64_t num_pairs, int32_t num_experts, int32_t block_size,
+                             int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                             int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, moe_stream stream);
 
 /* A1+A2 — moe_route followed by moe_align on its topk_ids, with the same
  * arguments, results and error behaviour as the two calls (topk_ids is both the

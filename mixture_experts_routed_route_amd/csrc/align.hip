@@ -13,6 +13,8 @@
 //      masks) plus per-wave LDS counters, so the order within an expert is ascending
 //      pair id.  All workgroups also share the sentinel and expert_ids fills.
 // Deterministic: no order-dependent atomics (the LDS histogram atomics only count).
+#include <mutex>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "route_common.h"
@@ -230,7 +232,34 @@ __global__ __launch_bounds__(64 * kFusedWaves) void route_align_kernel(
                                           expert_ids, total_out, inv, max_pad, 0);
 }
 
+// Static histogram table of moe_align_noalloc: the [chunks, E] per-chunk counts live here instead
+// of in a caller workspace.  Every call overwrites the cells it reads (align_count_kernel writes all
+// E counts of each of its chunks before align_scatter_kernel reads them), so the table needs no
+// clearing between calls.  Each device holds its own copy for the life of the process.
+static __device__ __align__(256) __attribute__((used)) int32_t scratch[kAlignScratchCells];
+
 }  // namespace
+
+hipError_t align_scratch_ptr(int32_t** out) {
+    // The array's device address, looked up once per device with that device current.  In host
+    // code the name `scratch` is only a stand-in: kernels get this address, never the name.
+    static std::mutex mu;
+    static int32_t* ptrs[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        ptrs[dev] = static_cast<int32_t*>(p);
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
 
 int align_num_chunks(int64_t num_pairs) {
     const int64_t g = (num_pairs + kChunk - 1) / kChunk;

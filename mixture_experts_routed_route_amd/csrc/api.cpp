@@ -57,7 +57,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 int64_t moe_align_max_padded(int64_t num_pairs, int32_t num_experts, int32_t block_size) {
     if (num_pairs < 0 || num_experts < 1 || block_size < 1) return -1;
@@ -187,6 +187,46 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_exp
                                            expert_offsets, sorted_ids, expert_ids, total_padded, inv_sorted,
                                            static_cast<int>(max_pad), static_cast<int32_t*>(workspace),
                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_align_noalloc(const int32_t* topk_ids, int64_t num_pairs, int32_t num_experts, int32_t block_size,
+                             int32_t* counts, int32_t* expert_offsets, int32_t* sorted_ids, int32_t* expert_ids,
+                             int32_t* total_padded, int32_t* inv_sorted, int64_t max_pad, moe_stream stream) {
+    const char* who = "moe_align_noalloc";
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs %lld out of range", who,
+            static_cast<long long>(num_pairs));
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256)
+        return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d exceeds MAX_NUM_EXPERTS=256", who, num_experts);
+    const int64_t cells = static_cast<int64_t>(moe::align_num_chunks(num_pairs)) * num_experts;
+    if (cells > moe::kAlignScratchCells)
+        return fail(MOE_EUNSUPPORTED,
+                    "%s: ceil(num_pairs/2048)*num_experts = %lld histogram cells exceed the static table of %lld "
+                    "(use moe_align with a workspace)",
+                    who, static_cast<long long>(cells), static_cast<long long>(moe::kAlignScratchCells));
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    const int64_t need = max_padded(num_pairs, num_experts, block_size);
+    REQUIRE(max_pad >= need, "%s: max_pad %lld < required %lld", who, static_cast<long long>(max_pad),
+            static_cast<long long>(need));
+    REQUIRE(max_pad % block_size == 0, "%s: max_pad %lld is not a multiple of block_size %d", who,
+            static_cast<long long>(max_pad), block_size);
+    REQUIRE(max_pad < INT32_MAX, "%s: max_pad too large", who);
+    if (num_pairs > 0) {
+        REQUIRE_PTR(who, topk_ids);
+        REQUIRE_PTR(who, inv_sorted);
+    }
+    REQUIRE_PTR(who, counts);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, expert_ids);
+    REQUIRE_PTR(who, total_padded);
+    int32_t* table = nullptr;
+    const hipError_t err = moe::align_scratch_ptr(&table);
+    if (err != hipSuccess)
+        return fail(MOE_ELAUNCH, "%s: static histogram table not found on this device: %s", who, hipGetErrorString(err));
+    return launched(who, moe::launch_align(topk_ids, static_cast<int>(num_pairs), num_experts, block_size, counts,
+                                           expert_offsets, sorted_ids, expert_ids, total_padded, inv_sorted,
+                                           static_cast<int>(max_pad), table, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_route_align(const float* logits, int32_t num_tokens, int32_t num_experts, int32_t top_k,

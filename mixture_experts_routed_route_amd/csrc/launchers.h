@@ -18,6 +18,11 @@ hipError_t launch_route(const float* logits, int T, int E, int top_k, int renorm
 
 // align.hip
 int align_num_chunks(int64_t num_pairs);
+// moe_align_noalloc: the per-chunk histogram table in a static device array of kAlignScratchCells
+// int32 (1 MiB per device); align_scratch_ptr gives this device's copy (looked up on first use)
+constexpr int64_t kAlignScratchCells = 1 << 18;
+constexpr int kMaxDevices = 64;
+hipError_t align_scratch_ptr(int32_t** out);
 hipError_t launch_align(const int32_t* topk_ids, int P, int E, int bs, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total, int32_t* inv, int max_pad,
                         int32_t* workspace, hipStream_t s);

@@ -16,7 +16,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, 
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Fp8Weight", "Routing", "moe_quantize_fp8", "moe_grouped_gemm_fp8", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_align_noalloc", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -214,6 +214,23 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, block_size: int, max_pad
                           _dev(r.inv_sorted, torch.int32, "inv_sorted"), r.max_pad,
                           _dev(r.workspace, torch.int32, "workspace"), r.workspace.numel() * 4,
                           _stream(topk_ids)))
+    return r
+
+
+def moe_align_noalloc(topk_ids: torch.Tensor, num_experts: int, block_size: int, out: Routing) -> Routing:
+    """moe_align into preallocated ``out`` with the library's static histogram table instead of a
+    workspace (for callers that cannot allocate; calls that overlap on one GPU race)."""
+    P = topk_ids.numel()
+    r = out
+    if r.num_pairs != P or r.num_experts != num_experts or r.block_size != block_size:
+        raise ValueError("preallocated Routing does not match the call")
+    _check_routing(r)
+    check(lib().moe_align_noalloc(_dev(topk_ids, torch.int32, "topk_ids"), P, num_experts, block_size,
+                                  _dev(r.counts, torch.int32, "counts"), _dev(r.offsets, torch.int32, "offsets"),
+                                  _dev(r.sorted_ids, torch.int32, "sorted_ids"),
+                                  _dev(r.expert_ids, torch.int32, "expert_ids"),
+                                  _dev(r.total_padded, torch.int32, "total_padded"),
+                                  _dev(r.inv_sorted, torch.int32, "inv_sorted"), r.max_pad, _stream(topk_ids)))
     return r
 
 

@@ -24,11 +24,11 @@ def L():
 def test_exports_every_declared_symbol(L):
     from mixture_experts_routed_route_amd import _lib
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_max_padded_and_workspace(L):
