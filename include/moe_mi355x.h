@@ -272,18 +272,26 @@ moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_sca
  *                                        input; sorted row r reads token sorted_ids[r]/top_k
  *   base        bf16 [max_pad, n_out]  sorted expert_down_out (Ys), or a sorted gate or up
  *                                      output (MOE_OP_GATHER) for x_gather == 1; in place
- *   a_table     u64  [n_tab] device    address of A_e, bf16 [max_rank, k_in]; 0 = unadapted
- *   b_table     u64  [n_tab] device    address of B_e, bf16 [n_out, max_rank]; 0 = unadapted
- *   scale_table f32  [n_tab] device    scale_e
- *   row_adapter i32  [num_pairs/top_k] or NULL: a token whose entry is < 0 is skipped
+ *   a_table     u64  [n_adapters, n_tab] device  address of A_e of adapter a at [a, e],
+ *                                      bf16 [max_rank, k_in]; 0 = e not adapted by a
+ *   b_table     u64  [n_adapters, n_tab] device  address of B_e, bf16 [n_out, max_rank]; 0 = unadapted
+ *   scale_table f32  [n_adapters, n_tab] device  scale_e of adapter a
+ *   n_adapters  adapters installed (>= 1): the rows of the tables
+ *   row_adapter i32  [num_pairs/top_k] or NULL: the adapter of each token (atlas: a mixed batch's
+ *                                      adapter identity comes from this per-row map, not from the
+ *                                      tables); < 0 = base (not folded), an id >= n_adapters is not
+ *                                      folded either; NULL = adapter 0 for every token
  *   xa          bf16 [cap, max_rank]   scratch, indexed by the local row r - row_offset
- * For each real row r of an adapted expert e < n_tab in the window:
+ * For each real row r in the window whose token's adapter a adapts the row's expert e (e < n_tab,
+ * non-zero table entries at [a, e]):
  *   xa = bf16(x[x row] A_e^T); delta = bf16(xa B_e^T); base[r] = bf16(base[r] + scale_e*delta)
- * with fp32 sums.  Other rows are not touched.  Windows may be applied one
- * after the other with the same xa scratch (stream order).  max_rank % 32 == 0,
- * k_in % 8 == 0, n_out % 8 == 0, cap >= row_end - row_offset, n_tab <= num_experts. */
+ * with fp32 sums and adapter a's A_e, B_e, scale_e.  Other rows are not touched.  Windows may be
+ * applied one after the other with the same xa scratch (stream order).  max_rank % 32 == 0,
+ * k_in % 8 == 0, n_out % 8 == 0, cap >= row_end - row_offset, n_tab <= num_experts,
+ * 1 <= n_adapters <= 65536. */
 moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_table, const uint64_t* b_table,
-                         const float* scale_table, int32_t n_tab, int32_t k_in, int32_t n_out, int32_t max_rank,
+                         const float* scale_table, int32_t n_tab, int32_t n_adapters, int32_t k_in, int32_t n_out,
+                         int32_t max_rank,
                          const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
                          int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
                          int64_t row_offset, int64_t row_end, int64_t max_pad, int32_t x_gather,
@@ -295,14 +303,14 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
  * (atlas moe_lora_grouped.rs: the gate/up fold over token-major x on the sorted
  * BF16 expert_gate_out / expert_up_out before SiLU).  For each real sorted row
  * r of expert e (token t = sorted_ids[r] / top_k):
- *   g = bf16(x[t] Wg[e]^T); if the gate tables adapt e (and row_adapter[t] >= 0
- *   or no map): g = bf16(g + s_gate[e] * bf16(bf16(x[t] A_gate[e]^T) B_gate[e]^T));
+ *   g = bf16(x[t] Wg[e]^T); if the gate tables of the token's adapter a (row_adapter[t],
+ *   0 without a map) adapt e: g = bf16(g + s_gate[a,e] * bf16(bf16(x[t] A_gate[a,e]^T) B_gate[a,e]^T));
  *   u likewise with the up tables; hs[r] = bf16(silu(g) * u).
  *   x, w_gate, w_up, hs, sorted ids ... max_pad, workspace: as moe_grouped_gemm
  *   with MOE_OP_GATE_UP_SILU (n = intermediate, k = hidden)
- *   a_*, b_*, s_*, n_tab_*: tables as for moe_lora_fold (A [max_rank, k],
+ *   a_*, b_*, s_*, n_tab_*: tables as for moe_lora_fold, [n_adapters, n_tab_*] (A [max_rank, k],
  *   B [n, max_rank]); n_tab 0 = no tables for that projection
- *   row_adapter  i32 [num_pairs/top_k] or NULL
+ *   row_adapter  i32 [num_pairs/top_k] or NULL, as for moe_lora_fold
  *   xa           bf16 [2, max_pad, max_rank] scratch (the gate and up shrinks)
  * Launches the two shrinks and the GEMM.  MOE_EUNSUPPORTED for int4 weights.
  * max_rank in {32, 64, 96, 128}. */
@@ -312,7 +320,8 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
                                          int32_t block_size, int64_t max_pad, const uint64_t* a_gate,
                                          const uint64_t* b_gate, const float* s_gate, int32_t n_tab_gate,
                                          const uint64_t* a_up, const uint64_t* b_up, const float* s_up,
-                                         int32_t n_tab_up, int32_t max_rank, const int32_t* row_adapter,
+                                         int32_t n_tab_up, int32_t n_adapters, int32_t max_rank,
+                                         const int32_t* row_adapter,
                                          uint16_t* xa, void* workspace, int64_t workspace_bytes,
                                          moe_stream stream);
 
@@ -330,7 +339,7 @@ moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out,
 /* Decode form of the LoRA fold, slot-major, in place (atlas moe_lora_grouped.rs,
  * moe_lora_gather_bgmv, gather_row_token).  No sorted layout: flat (token, slot)
  * row s < n_slots (= tokens * top_k) takes its expert e = indices[s] and its
- * adapter decision from row_adapter[s / top_k] (< 0 skips; NULL folds every row).
+ * adapter a = row_adapter[s / top_k] (< 0 or >= n_adapters skips; NULL = adapter 0).
  *   x           bf16 [x_rows, k_in]     x_gather == 0: row = the slot's row (the
  *                                       post-SiLU activations of the down fold);
  *                                       x_gather == 1: row s / top_k (token-major
@@ -342,10 +351,10 @@ moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out,
  *                                       the page); a negative entry skips the slot.
  *                                       With moe_align's inv_sorted it folds buffers
  *                                       in sorted order.
- *   a_table, b_table, scale_table, n_tab: as for moe_lora_fold
+ *   a_table, b_table, scale_table, n_tab, n_adapters: as for moe_lora_fold, [n_adapters, n_tab]
  *   xa          bf16 [n_slots, max_rank] scratch, indexed by s
- * For each slot whose expert is adapted (e in [0, n_tab), non-zero table
- * entries): xa = bf16(x[x row] A_e^T); delta = bf16(xa B_e^T);
+ * For each slot whose adapter a adapts its expert (e in [0, n_tab), non-zero table
+ * entries at [a, e]): xa = bf16(x[x row] A_e^T); delta = bf16(xa B_e^T);
  * base[row] = bf16(base[row] + scale_e*delta), fp32 sums.  Other rows are not
  * touched.  One workgroup per (slot, output chunk): the grid depends on n_slots
  * only.  Device values that the host cannot check get defined behaviour: an id
@@ -358,8 +367,8 @@ moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out,
 moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
                                 const int32_t* indices, int64_t n_slots, int32_t top_k, int32_t x_gather,
                                 const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_table,
-                                const uint64_t* b_table, const float* scale_table, int32_t n_tab, int32_t k_in,
-                                int32_t n_out, int32_t max_rank, uint16_t* xa, moe_stream stream);
+                                const uint64_t* b_table, const float* scale_table, int32_t n_tab, int32_t n_adapters,
+                                int32_t k_in, int32_t n_out, int32_t max_rank, uint16_t* xa, moe_stream stream);
 
 /* A6 — top-k weighted combine (ferrum moe.rs, moe_combine / weighted_sum_batched).
  *   ys         bf16 [ys_rows, hidden]

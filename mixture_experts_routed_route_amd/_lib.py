@@ -41,12 +41,12 @@ SIGNATURES = {
                                    c_void_p, c_int64, c_void_p]),
     "moe_grouped_gemm_workspace_bytes": (c_int64, []),
     "moe_lora_fold": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
-                                c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+                                c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                 c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p]),
     "moe_grouped_gemm_gate_up_lora": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                                 c_int32, c_int32, c_int32, c_int32, c_int32, c_int64, c_void_p,
                                                 c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
-                                                c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
+                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
     "moe_quantize_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
     "moe_grouped_gemm_fp8": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int64,
@@ -54,7 +54,7 @@ SIGNATURES = {
     "moe_silu_mul": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p]),
     "moe_lora_gather_fold": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
-                                       c_int32, c_void_p, c_void_p]),
+                                       c_int32, c_int32, c_void_p, c_void_p]),
     "moe_combine": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int64,
                               c_void_p]),
     # include/moe_probes.h: ceiling probes, not steps of the path

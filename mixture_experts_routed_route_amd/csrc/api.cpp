@@ -353,8 +353,8 @@ moe_status moe_grouped_gemm(int32_t op, const uint16_t* a, const moe_weight* w0,
 }
 
 moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_table, const uint64_t* b_table,
-                         const float* scale_table, int32_t n_tab, int32_t k_in, int32_t n_out, int32_t max_rank,
-                         const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
+                         const float* scale_table, int32_t n_tab, int32_t n_adapters, int32_t k_in, int32_t n_out,
+                         int32_t max_rank, const int32_t* expert_offsets, int32_t num_experts, const int32_t* sorted_ids,
                          int64_t num_pairs, int32_t top_k, const int32_t* row_adapter, uint16_t* xa, int64_t cap,
                          int64_t row_offset, int64_t row_end, int64_t max_pad, int32_t x_gather,
                          moe_stream stream) {
@@ -364,6 +364,7 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
     if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
     REQUIRE(n_tab >= 0 && n_tab <= num_experts, "%s: n_tab %d not in [0, num_experts=%d]", who, n_tab,
             num_experts);
+    REQUIRE(n_adapters >= 1 && n_adapters <= 65536, "%s: n_adapters %d not in [1, 65536]", who, n_adapters);
     REQUIRE(k_in >= 8 && k_in % 8 == 0, "%s: k_in %d must be a positive multiple of 8", who, k_in);
     REQUIRE(n_out >= 8 && n_out % 8 == 0, "%s: n_out %d must be a positive multiple of 8", who, n_out);
     REQUIRE(max_rank >= 32 && max_rank <= 128 && max_rank % 32 == 0, "%s: max_rank %d not in {32,64,96,128}", who,
@@ -386,7 +387,8 @@ moe_status moe_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_ta
     REQUIRE_PTR(who, sorted_ids);
     REQUIRE_PTR(who, xa);
     if (row_adapter) REQUIRE_PTR(who, row_adapter);
-    return launched(who, moe::launch_lora_fold(x, base, a_table, b_table, scale_table, n_tab, k_in, n_out, max_rank,
+    return launched(who, moe::launch_lora_fold(x, base, a_table, b_table, scale_table, n_tab, n_adapters, k_in, n_out,
+                                               max_rank,
                                                expert_offsets, num_experts, sorted_ids, static_cast<int>(num_pairs),
                                                top_k, row_adapter, xa, row_offset, row_end, x_gather,
                                                static_cast<hipStream_t>(stream)));
@@ -398,7 +400,8 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
                                          int32_t block_size, int64_t max_pad, const uint64_t* a_gate,
                                          const uint64_t* b_gate, const float* s_gate, int32_t n_tab_gate,
                                          const uint64_t* a_up, const uint64_t* b_up, const float* s_up,
-                                         int32_t n_tab_up, int32_t max_rank, const int32_t* row_adapter,
+                                         int32_t n_tab_up, int32_t n_adapters, int32_t max_rank,
+                                         const int32_t* row_adapter,
                                          uint16_t* xa, void* workspace, int64_t workspace_bytes,
                                          moe_stream stream) {
     const char* who = "moe_grouped_gemm_gate_up_lora";
@@ -421,6 +424,7 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
             max_rank);
     REQUIRE(n_tab_gate >= 0 && n_tab_gate <= num_experts && n_tab_up >= 0 && n_tab_up <= num_experts,
             "%s: table lengths must be in [0, num_experts=%d]", who, num_experts);
+    REQUIRE(n_adapters >= 1 && n_adapters <= 65536, "%s: n_adapters %d not in [1, 65536]", who, n_adapters);
     if (workspace != nullptr) {
         const int64_t need = moe_grouped_gemm_workspace_bytes();
         REQUIRE_PTR(who, workspace);
@@ -452,11 +456,11 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int P = static_cast<int>(num_pairs);
     uint16_t* xa_up = xa + max_pad * max_rank;
-    hipError_t err = moe::launch_lora_shrink(x, a_gate, b_gate, n_tab_gate, k, max_rank, expert_offsets, num_experts,
-                                             sorted_ids, P, top_k, row_adapter, xa, 0, max_pad, 1, s);
+    hipError_t err = moe::launch_lora_shrink(x, a_gate, b_gate, n_tab_gate, n_adapters, k, max_rank, expert_offsets,
+                                             num_experts, sorted_ids, P, top_k, row_adapter, xa, 0, max_pad, 1, s);
     if (err == hipSuccess)
-        err = moe::launch_lora_shrink(x, a_up, b_up, n_tab_up, k, max_rank, expert_offsets, num_experts, sorted_ids,
-                                      P, top_k, row_adapter, xa_up, 0, max_pad, 1, s);
+        err = moe::launch_lora_shrink(x, a_up, b_up, n_tab_up, n_adapters, k, max_rank, expert_offsets, num_experts,
+                                      sorted_ids, P, top_k, row_adapter, xa_up, 0, max_pad, 1, s);
     if (err != hipSuccess) return launched(who, err);
     moe::GateUpLora lora{};
     lora.xa[0] = xa;
@@ -469,6 +473,7 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
     lora.s_tab[1] = s_up;
     lora.n_tab[0] = n_tab_gate;
     lora.n_tab[1] = n_tab_up;
+    lora.n_ad = n_adapters;
     lora.rank = max_rank;
     lora.row_adapter = row_adapter;
     return launched(who, moe::launch_gemm_bf16(moe::kOpGateUpSilu, x, static_cast<const uint16_t*>(w_gate->data),
@@ -562,8 +567,8 @@ moe_status moe_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out,
 moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
                                 const int32_t* indices, int64_t n_slots, int32_t top_k, int32_t x_gather,
                                 const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_table,
-                                const uint64_t* b_table, const float* scale_table, int32_t n_tab, int32_t k_in,
-                                int32_t n_out, int32_t max_rank, uint16_t* xa, moe_stream stream) {
+                                const uint64_t* b_table, const float* scale_table, int32_t n_tab, int32_t n_adapters,
+                                int32_t k_in, int32_t n_out, int32_t max_rank, uint16_t* xa, moe_stream stream) {
     const char* who = "moe_lora_gather_fold";
     REQUIRE(top_k >= 1, "%s: top_k %d < 1", who, top_k);
     REQUIRE(n_slots >= 0 && n_slots < INT32_MAX && n_slots % top_k == 0,
@@ -571,6 +576,7 @@ moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* bas
             static_cast<long long>(n_slots), top_k);
     REQUIRE(x_gather == 0 || x_gather == 1, "%s: x_gather %d not 0 or 1", who, x_gather);
     REQUIRE(n_tab >= 0 && n_tab <= 65536, "%s: n_tab %d not in [0, 65536]", who, n_tab);
+    REQUIRE(n_adapters >= 1 && n_adapters <= 65536, "%s: n_adapters %d not in [1, 65536]", who, n_adapters);
     REQUIRE(k_in >= 8 && k_in % 8 == 0, "%s: k_in %d must be a positive multiple of 8", who, k_in);
     REQUIRE(n_out >= 8 && n_out % 8 == 0, "%s: n_out %d must be a positive multiple of 8", who, n_out);
     REQUIRE(max_rank >= 32 && max_rank <= 128 && max_rank % 32 == 0, "%s: max_rank %d not in {32,64,96,128}", who,
@@ -593,7 +599,7 @@ moe_status moe_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* bas
     if (row_adapter) REQUIRE_PTR(who, row_adapter);
     return launched(who, moe::launch_lora_gather_fold(x, x_rows, base, base_rows, indices, n_slots, top_k, x_gather,
                                                       row_map, row_adapter, a_table, b_table, scale_table, n_tab,
-                                                      k_in, n_out, max_rank, xa,
+                                                      n_adapters, k_in, n_out, max_rank, xa,
                                                       static_cast<hipStream_t>(stream)));
 }
 

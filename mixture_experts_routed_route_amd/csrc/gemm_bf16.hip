@@ -155,7 +155,11 @@ __device__ __forceinline__ void decode_tile(int L, int gm, int m_real, int n_til
     m_t = band * gm + (in_band - n_t * gm_b);
 }
 
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW, bool LORA = false>
+// LORA: 0 no gate/up LoRA; 1 one adapter (every folded row is adapter 0); 2 several adapters (the
+// rows of one fragment may belong to different adapters: one pass per adapter present).  The
+// one-adapter form is the common case and keeps the lean epilogue, which the loop of the general
+// form would cost registers in the main loop.
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W0,
                                                           const uint16_t* __restrict__ W1,
@@ -172,6 +176,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     __shared__ int s_scan[NW];
     __shared__ int s_lo[kMaxE], s_hi[kMaxE], s_tb[kMaxE + 1];  // expert span, first row tile
     __shared__ int s_row[2][BM];                                  // A source row per tile row
+    __shared__ int s_rad[LORA ? 2 : 1][LORA ? BM : 1];            // LoRA: adapter id per tile row (-1: none)
     __shared__ int s_h[2];                                        // rows up to the last token
     __shared__ int s_arrived;                                     // split tile: the other side's count
 
@@ -274,6 +279,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 if (p >= 0 && p < P) src = (GATE_UP || a_tok) ? p / top_k : r;
             }
             s_row[buf][i] = src;
+            if constexpr (LORA) {
+                // the token's adapter (atlas: a mixed batch's adapter comes from the per-row map); 0
+                // without a map; -1 for rows without a token or with an id outside [0, n_ad)
+                int a = src >= 0 ? (lora.row_adapter ? lora.row_adapter[src] : 0) : -1;
+                s_rad[buf][i] = (a >= 0 && a < lora.n_ad) ? a : -1;
+            }
             if (src >= 0) atomicMax(&s_h[buf], i + 1);
         }
     };
@@ -615,36 +626,54 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                     const int rowf = min(r0 + wm * F::WM + i * 32 + fr, max_pad - 1);
 #pragma unroll
                     for (int pj = 0; pj < 2; ++pj) {  // 0: gate (blocks 0, 1), 1: up (blocks 2, 3)
-                        const bool adapted = e < lora.n_tab[pj] && lora.a_tab[pj][e] != 0 && lora.b_tab[pj][e] != 0;
-                        if (!adapted) {
 #pragma unroll
-                            for (int jj = 0; jj < 2; ++jj)
+                        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                                for (int v = 0; v < 16; ++v) acc[i][pj * 2 + jj][v] = bf16r(acc[i][pj * 2 + jj][v]);
-                            continue;
-                        }
-                        const uint16_t* xr = lora.xa[pj] + static_cast<size_t>(rowf) * lora.rank + fc * 8;
-                        const uint16_t* Be = reinterpret_cast<const uint16_t*>(lora.b_tab[pj][e]);
-                        const float sc = lora.s_tab[pj][e];
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {  // one 32x32 delta block at a time
-                            const int col = min(n0 + wn * 64 + jj * 32 + fr, N - 1);
-                            const uint16_t* br = Be + static_cast<size_t>(col) * lora.rank + fc * 8;
-                            f32x16 d;
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) d[v] = 0.f;
-                            for (int k0 = 0; k0 < lora.rank; k0 += 16)
-                                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(xr + k0),
-                                                                            *reinterpret_cast<const bf16x8*>(br + k0),
-                                                                            d, 0, 0, 0);
-#pragma unroll
+                            for (int v = 0; v < 16; ++v) acc[i][pj * 2 + jj][v] = bf16r(acc[i][pj * 2 + jj][v]);
+                        if (e >= lora.n_tab[pj]) continue;  // past every adapter's table: not adapted
+                        // adapter id of the row of value v (-1: not folded)
+                        auto row_ad = [&](int v) __attribute__((always_inline)) {
+                            return s_rad[buf][wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3)];
+                        };
+                        // the adapters present among the 32 rows, smallest first: one pass each
+                        auto next_ad = [&](int after) __attribute__((always_inline)) {
+                            int m = 0x7fffffff;
                             for (int v = 0; v < 16; ++v) {
-                                const int rl = wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3);
-                                const int tok = s_row[buf][rl];
-                                const bool fold = tok >= 0 && (!lora.row_adapter || lora.row_adapter[tok] >= 0);
-                                const float g = bf16r(acc[i][pj * 2 + jj][v]);
-                                acc[i][pj * 2 + jj][v] = fold ? bf16r(fmaf(sc, bf16r(d[v]), g)) : g;
+                                const int a = row_ad(v);
+                                if (a > after && a < m) m = a;
                             }
+#pragma unroll
+                            for (int o = 32; o >= 1; o >>= 1) m = min(m, __shfl_xor(m, o));
+                            return m;
+                        };
+                        const uint16_t* xr = lora.xa[pj] + static_cast<size_t>(rowf) * lora.rank + fc * 8;
+                        // one pass per adapter: the delta of adapter `cur`, folded into its rows
+                        auto pass = [&](int cur) __attribute__((always_inline)) {
+                            const int64_t tix = static_cast<int64_t>(cur) * lora.n_tab[pj] + e;
+                            if (lora.a_tab[pj][tix] == 0 || lora.b_tab[pj][tix] == 0) return;  // e not adapted
+                            const uint16_t* Be = reinterpret_cast<const uint16_t*>(lora.b_tab[pj][tix]);
+                            const float sc = lora.s_tab[pj][tix];
+#pragma unroll
+                            for (int jj = 0; jj < 2; ++jj) {  // one 32x32 delta block at a time
+                                const int col = min(n0 + wn * 64 + jj * 32 + fr, N - 1);
+                                const uint16_t* br = Be + static_cast<size_t>(col) * lora.rank + fc * 8;
+                                f32x16 d;
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) d[v] = 0.f;
+                                for (int k0 = 0; k0 < lora.rank; k0 += 16)
+                                    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                        *reinterpret_cast<const bf16x8*>(xr + k0), *reinterpret_cast<const bf16x8*>(br + k0),
+                                        d, 0, 0, 0);
+#pragma unroll
+                                for (int v = 0; v < 16; ++v)
+                                    if (row_ad(v) == cur)
+                                        acc[i][pj * 2 + jj][v] = bf16r(fmaf(sc, bf16r(d[v]), acc[i][pj * 2 + jj][v]));
+                            }
+                        };
+                        if constexpr (LORA == 1) {
+                            pass(0);
+                        } else {
+                            for (int cur = next_ad(-1); cur != 0x7fffffff; cur = next_ad(cur)) pass(cur);
                         }
                     }
                 }
@@ -716,7 +745,7 @@ constexpr int64_t kSkPartBytes = 512LL * 2 * 64 * 4;    // largest partial: 512 
 constexpr int64_t kSkWorkspaceBytes = kSkCounterBytes + kSkMaxGrid * kSkPartBytes;
 static_assert(kSkMaxGrid * 4 <= kSkCounterBytes, "split-tail counters overflow their area");
 
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW, bool LORA = false>
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0>
 hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                       const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
                       int max_pad, void* ws, int64_t ws_bytes, int a_tok, hipStream_t s,
@@ -759,9 +788,13 @@ hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const
     // 256-row tiles (8 waves) when experts average at least MOE_GEMM_BIG_ROWS rows, where a 128-row
     // tiling would read most weight panels twice; 128-row tiles (4 waves) for fewer rows
     const bool big = static_cast<long long>(P) >= static_cast<long long>(MOE_GEMM_BIG_ROWS) * E;
+    if (op == kOpGateUpSilu && lora && lora->n_ad == 1) {
+        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, 1>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
+        return launch_cfg<true, 128, 64, 3, 4, 1>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
+    }
     if (op == kOpGateUpSilu && lora) {
-        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, true>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
-        return launch_cfg<true, 128, 64, 3, 4, true>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
+        if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, 2>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
+        return launch_cfg<true, 128, 64, 3, 4, 2>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
     }
     if (op == kOpGateUpSilu) {
         if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s);

@@ -38,15 +38,17 @@ hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w
 
 // LoRA of the gate and up projections folded in the bf16 gate/up GEMM's epilogue.  For each
 // projection p (0 gate, 1 up): xa[p] = bf16 shrink results [max_pad, rank] of the sorted rows, and
-// the expert tables (n_tab[p] == 0: no tables, the projection is only rounded to bf16).
+// the expert tables, n_ad rows of n_tab[p] entries, row a for the tokens of adapter a (n_tab[p] == 0:
+// no tables, the projection is only rounded to bf16).
 struct GateUpLora {
     const uint16_t* xa[2];
     const uint64_t* a_tab[2];
     const uint64_t* b_tab[2];
     const float* s_tab[2];
     int n_tab[2];
+    int n_ad;
     int rank;
-    const int32_t* row_adapter;  // [tokens] (< 0: no fold) or NULL
+    const int32_t* row_adapter;  // [tokens]: the token's adapter (< 0 or >= n_ad: no fold); NULL = adapter 0
 };
 
 // gemm_bf16.hip (ws: optional split-tail workspace, zero-filled before first use; NULL = none;
@@ -65,12 +67,12 @@ hipError_t launch_gemm_int4(int op, const uint16_t* a, const int32_t* qw0, const
 
 // lora_fold.hip
 hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_tab, const uint64_t* b_tab,
-                            const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
+                            const float* s_tab, int n_tab, int n_ad, int k_in, int n_out, int max_rank,
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
                             const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
                             int x_gather, hipStream_t s);
 // the shrink alone: xa[r - row_offset] = bf16(x[row] A_e^T) for the folded rows of the window
-hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int k_in,
+hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int n_ad, int k_in,
                               int max_rank, const int32_t* offsets, int E, const int32_t* sorted_ids, int P,
                               int top_k, const int32_t* row_adapter, uint16_t* xa, int64_t row_offset,
                               int64_t row_end, int x_gather, hipStream_t s);
@@ -89,7 +91,7 @@ hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint16_t* h, co
 hipError_t launch_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
                                    const int32_t* indices, int64_t n_slots, int top_k, int x_gather,
                                    const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_tab,
-                                   const uint64_t* b_tab, const float* s_tab, int n_tab, int k_in, int n_out,
+                                   const uint64_t* b_tab, const float* s_tab, int n_tab, int n_ad, int k_in, int n_out,
                                    int max_rank, uint16_t* xa, hipStream_t s);
 
 // probes.hip (ceiling probes, not steps of the path)

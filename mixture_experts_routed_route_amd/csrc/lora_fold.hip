@@ -5,6 +5,11 @@
 //                                                  row r reads its token sorted_ids[r] / top_k)
 //   delta = bf16(xa B_e^T)                        (expand, n_out outputs)
 //   base[r] = bf16(fp32(base[r]) + scale_e * fp32(delta))   (in place)
+// Adapters (atlas MoeExpertRoute: adapter identity of a mixed batch comes from the per-row
+// moe_row_adapter, not from the tables): the tables hold n_adapters rows of n_tab entries, and a row
+// of token t uses row a = row_adapter[t] (0 without a map; < 0 or >= n_adapters folds nothing).  The
+// rows of one sub-tile may belong to several adapters: the kernels take the adapters present one at
+// a time (a uniform loop, usually one pass) and write only that adapter's rows in each pass.
 // Two launches like the page: the shrink writes the bf16 xa scratch at the local row
 // r - row_offset, the expand reads it.  The expert of a row is read on the device from
 // expert_offsets (the row's span), so the grid is fixed by host scalars: a window is cut
@@ -49,8 +54,7 @@ struct SubTile {
     int span_end;   // end of that expert's padded span
 };
 
-__device__ __forceinline__ SubTile sub_tile_expert(int sub0, const int32_t* off, int E, int n_tab,
-                                                   const uint64_t* a_tab, const uint64_t* b_tab) {
+__device__ __forceinline__ SubTile sub_tile_expert(int sub0, const int32_t* off, int E, int n_tab) {
     SubTile st{-1, 0};
     // expert spans are read from device memory: clamp the search to what it can address
     int lo = 0, hi = E;
@@ -59,21 +63,40 @@ __device__ __forceinline__ SubTile sub_tile_expert(int sub0, const int32_t* off,
         const int mid = (lo + hi) >> 1;
         if (off[mid] <= sub0) lo = mid; else hi = mid;
     }
-    if (lo >= n_tab || a_tab[lo] == 0 || b_tab[lo] == 0) return st;
+    if (lo >= n_tab) return st;  // past every adapter's table: unadapted
     st.e = lo;
     st.span_end = off[lo + 1];
     return st;
 }
 
-// Is sorted row r folded?  (inside the window and the expert span, real, adapter allows)
-__device__ __forceinline__ bool row_active(int64_t r, int64_t row_offset, int64_t row_end, int span_end,
-                                           const int32_t* sorted_ids, int P, int top_k,
-                                           const int32_t* row_adapter) {
-    if (r < row_offset || r >= row_end || r >= span_end) return false;
+constexpr int kNoAdapter = 0x7fffffff;  // "no adapter" key: above every real adapter id
+
+// Adapter of sorted row r if it is folded (inside the window and the expert span, real, its token's
+// adapter in [0, n_ad) and that adapter adapts expert e), else kNoAdapter.
+__device__ __forceinline__ int row_adapter_of(int64_t r, int64_t row_offset, int64_t row_end, int span_end,
+                                              const int32_t* sorted_ids, int P, int top_k,
+                                              const int32_t* row_adapter, int n_ad, int n_tab, int e,
+                                              const uint64_t* a_tab, const uint64_t* b_tab) {
+    if (r < row_offset || r >= row_end || r >= span_end) return kNoAdapter;
     const int p = sorted_ids[r];
-    if (p < 0 || p >= P) return false;
-    if (row_adapter && row_adapter[p / top_k] < 0) return false;
-    return true;
+    if (p < 0 || p >= P) return kNoAdapter;
+    const int a = row_adapter ? row_adapter[p / top_k] : 0;
+    if (a < 0 || a >= n_ad) return kNoAdapter;
+    const int64_t ix = static_cast<int64_t>(a) * n_tab + e;
+    if (a_tab[ix] == 0 || b_tab[ix] == 0) return kNoAdapter;
+    return a;
+}
+
+// Smallest adapter id above `after` held by any lane of the wave (kNoAdapter if none); the result is
+// the same in every lane.
+__device__ __forceinline__ int wave_next_adapter(int mine, int after) {
+    int v = mine > after ? mine : kNoAdapter;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const int w = __shfl_xor(v, o);
+        v = w < v ? w : v;
+    }
+    return v;
 }
 
 // Shrink: one workgroup per 16-row sub-tile; its 4 waves take a quarter of k_in each and add
@@ -82,7 +105,8 @@ __device__ __forceinline__ bool row_active(int64_t r, int64_t row_offset, int64_
 // MFMAs, so a wave waits for one memory round trip per KU steps.
 template <int NB>
 __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restrict__ x, const uint64_t* a_tab,
-                                                         const uint64_t* b_tab, int n_tab, int k_in, int max_rank,
+                                                         const uint64_t* b_tab, int n_tab, int n_ad, int k_in,
+                                                         int max_rank,
                                                          const int32_t* __restrict__ off, int E,
                                                          const int32_t* __restrict__ sorted_ids, int P, int top_k,
                                                          const int32_t* __restrict__ row_adapter,
@@ -95,19 +119,23 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
     const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.x) * 16;
     if (sub0 >= row_end) return;  // uniform over the workgroup
     stage_offsets(off, E, s_off);
-    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab, a_tab, b_tab);
+    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
     if (st.e < 0) return;  // uniform over the workgroup
-    const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[st.e]);
 
     const int m = lane & 15, kq = lane >> 4;
     const int64_t r = sub0 + m;
-    const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
-    if (__ballot(act) == 0) return;  // the same rows in every wave: uniform over the workgroup
+    const int ad = row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter, n_ad,
+                                  n_tab, st.e, a_tab, b_tab);
+    const bool act = ad != kNoAdapter;
     // x row: the sorted row (down), or the row's token in the token-major input (gate/up form)
     const int64_t xrow = act && x_gather ? static_cast<int64_t>(sorted_ids[r] / top_k) : r;
     const uint16_t* xr = act ? x + xrow * k_in + kq * 8 : nullptr;
     const int kpart = ((k_in + 127) / 128) * 32;  // this wave's k range, a multiple of 32
     const int kb = wave * kpart, ke = min(k_in, kb + kpart);
+    // the rows' adapters, one pass each (every wave holds the same 16 rows: the passes are uniform over
+    // the workgroup); a row of another adapter is computed with this pass's A and not stored
+    for (int cur = wave_next_adapter(ad, -1); cur != kNoAdapter; cur = wave_next_adapter(ad, cur)) {
+    const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[static_cast<int64_t>(cur) * n_tab + st.e]);
 
     f32x4 acc[NB];
 #pragma unroll
@@ -137,17 +165,22 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[j][v];
     __syncthreads();
-    if (wave != 0) return;
-    // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
+    if (wave == 0) {
+        // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int64_t rr = sub0 + 4 * kq + v;
-        if (!row_active(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter)) continue;
-        uint16_t* dst = xa + (rr - row_offset) * max_rank;
+        for (int v = 0; v < 4; ++v) {
+            const int64_t rr = sub0 + 4 * kq + v;
+            if (row_adapter_of(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter, n_ad, n_tab,
+                               st.e, a_tab, b_tab) != cur)
+                continue;
+            uint16_t* dst = xa + (rr - row_offset) * max_rank;
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-            dst[j * 16 + m] = f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
-                                          (red[2][j][v][lane] + red[3][j][v][lane]));
+            for (int j = 0; j < NB; ++j)
+                dst[j * 16 + m] = f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
+                                              (red[2][j][v][lane] + red[3][j][v][lane]));
+        }
+    }
+    __syncthreads();  // red[] is rewritten by the next pass
     }
 }
 
@@ -160,7 +193,7 @@ template <int NKS>  // k-steps of 32 over max_rank
 __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __restrict__ xa,
                                                               const uint64_t* a_tab, const uint64_t* b_tab,
                                                               const float* __restrict__ s_tab, int n_tab,
-                                                              int n_out, int max_rank,
+                                                              int n_ad, int n_out, int max_rank,
                                                               const int32_t* __restrict__ off, int E,
                                                               const int32_t* __restrict__ sorted_ids, int P,
                                                               int top_k, const int32_t* __restrict__ row_adapter,
@@ -174,14 +207,14 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
     if (base16 + static_cast<int64_t>(blockIdx.y) * 64 >= row_end) return;  // uniform over the workgroup
     stage_offsets(off, E, s_off);
     if (sub0 >= row_end) return;
-    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab, a_tab, b_tab);
+    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
     if (st.e < 0) return;
-    const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[st.e]);
-    const float scale = s_tab[st.e];
 
     const int m = lane & 15, kq = lane >> 4;
     const int64_t r = sub0 + m;
-    const bool act = row_active(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter);
+    const int ad = row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter, n_ad, n_tab,
+                                  st.e, a_tab, b_tab);
+    const bool act = ad != kNoAdapter;
     if (__ballot(act) == 0) return;
     u32x4 av[NKS];
 #pragma unroll
@@ -190,11 +223,20 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
                                    : u32x4{0, 0, 0, 0};
     // fold rows of this lane (FOLD_RPS rows x FOLD_LPR lanes x 8 columns per step)
     const int col = (lane % FOLD_LPR) * 8;
-    bool row_ok[FOLD_STEPS];
+    int row_ad[FOLD_STEPS];
 #pragma unroll
     for (int it = 0; it < FOLD_STEPS; ++it)
-        row_ok[it] = row_active(sub0 + it * FOLD_RPS + lane / FOLD_LPR, row_offset, row_end, st.span_end,
-                                sorted_ids, P, top_k, row_adapter);
+        row_ad[it] = row_adapter_of(sub0 + it * FOLD_RPS + lane / FOLD_LPR, row_offset, row_end, st.span_end,
+                                    sorted_ids, P, top_k, row_adapter, n_ad, n_tab, st.e, a_tab, b_tab);
+    // one pass per adapter present in the sub-tile (every row's xa already holds its own adapter's
+    // shrink): the pass computes the delta with that adapter's B_e and folds only its rows
+    for (int cur = wave_next_adapter(ad, -1); cur != kNoAdapter; cur = wave_next_adapter(ad, cur)) {
+    const int64_t tix = static_cast<int64_t>(cur) * n_tab + st.e;
+    const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[tix]);
+    const float scale = s_tab[tix];
+    bool row_ok[FOLD_STEPS];
+#pragma unroll
+    for (int it = 0; it < FOLD_STEPS; ++it) row_ok[it] = row_ad[it] == cur;
 
     u32x4 bvs[2][FOLD_STEPS], bw[2][NKS][EXP_COLS / 16];
     auto load_block = [&](int cb, int set) __attribute__((always_inline)) {
@@ -260,6 +302,7 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
         }
         __builtin_amdgcn_wave_barrier();  // this block's LDS reads before the next block's writes
     }
+    }
 }
 
 // ------------------------------------------------------------------ slot-major gather fold
@@ -270,7 +313,7 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
 // they run on the vector ALU with coalesced 16-byte loads rather than on MFMA.
 
 struct GatherRow {
-    int e;          // expert (table index)
+    int64_t e;      // table entry: adapter * n_tab + expert
     int64_t row;    // row of base (and of x for the down form)
     int64_t xrow;   // row of x
 };
@@ -279,16 +322,19 @@ struct GatherRow {
 // the tables or the buffers skips the slot.
 __device__ __forceinline__ bool gather_row(int64_t s, const int32_t* indices, const int32_t* row_map,
                                            const int32_t* row_adapter, int top_k, int x_gather, int n_tab,
-                                           const uint64_t* a_tab, const uint64_t* b_tab, int64_t x_rows,
-                                           int64_t base_rows, GatherRow& g) {
+                                           int n_ad, const uint64_t* a_tab, const uint64_t* b_tab,
+                                           int64_t x_rows, int64_t base_rows, GatherRow& g) {
     const int e = indices[s];
-    if (e < 0 || e >= n_tab || a_tab[e] == 0 || b_tab[e] == 0) return false;
-    if (row_adapter && row_adapter[s / top_k] < 0) return false;
+    if (e < 0 || e >= n_tab) return false;
+    const int a = row_adapter ? row_adapter[s / top_k] : 0;  // the token's adapter (0 without a map)
+    if (a < 0 || a >= n_ad) return false;
+    const int64_t ix = static_cast<int64_t>(a) * n_tab + e;
+    if (a_tab[ix] == 0 || b_tab[ix] == 0) return false;
     const int64_t row = row_map ? static_cast<int64_t>(row_map[s]) : s;
     if (row < 0 || row >= base_rows) return false;
     const int64_t xrow = x_gather ? s / top_k : row;
     if (xrow >= x_rows) return false;
-    g = GatherRow{e, row, xrow};
+    g = GatherRow{ix, row, xrow};
     return true;
 }
 
@@ -314,13 +360,14 @@ __global__ __launch_bounds__(NT) void gather_shrink_kernel(const uint16_t* __res
                                                            const int32_t* __restrict__ row_map,
                                                            const int32_t* __restrict__ row_adapter,
                                                            const uint64_t* a_tab, const uint64_t* b_tab, int n_tab,
-                                                           int top_k, int x_gather, int64_t x_rows,
+                                                           int n_ad, int top_k, int x_gather, int64_t x_rows,
                                                            int64_t base_rows, int k_in, int max_rank,
                                                            uint16_t* __restrict__ xa) {
     __shared__ float red[4][16];
     const int64_t s = blockIdx.x;
     GatherRow gr;
-    if (!gather_row(s, indices, row_map, row_adapter, top_k, x_gather, n_tab, a_tab, b_tab, x_rows, base_rows, gr))
+    if (!gather_row(s, indices, row_map, row_adapter, top_k, x_gather, n_tab, n_ad, a_tab, b_tab, x_rows, base_rows,
+                    gr))
         return;  // uniform over the workgroup
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -370,12 +417,13 @@ __global__ __launch_bounds__(NT) void gather_expand_kernel(const uint16_t* __res
                                                            const int32_t* __restrict__ row_map,
                                                            const int32_t* __restrict__ row_adapter,
                                                            const uint64_t* a_tab, const uint64_t* b_tab,
-                                                           const float* __restrict__ s_tab, int n_tab, int top_k,
-                                                           int x_gather, int64_t x_rows, int64_t base_rows,
+                                                           const float* __restrict__ s_tab, int n_tab, int n_ad,
+                                                           int top_k, int x_gather, int64_t x_rows, int64_t base_rows,
                                                            int n_out, int max_rank, uint16_t* __restrict__ base) {
     const int64_t s = blockIdx.x;
     GatherRow gr;
-    if (!gather_row(s, indices, row_map, row_adapter, top_k, x_gather, n_tab, a_tab, b_tab, x_rows, base_rows, gr))
+    if (!gather_row(s, indices, row_map, row_adapter, top_k, x_gather, n_tab, n_ad, a_tab, b_tab, x_rows, base_rows,
+                    gr))
         return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 3, c = lane & 7;
@@ -421,7 +469,7 @@ __global__ __launch_bounds__(NT) void gather_expand_kernel(const uint16_t* __res
 
 }  // namespace
 
-hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int k_in,
+hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int n_ad, int k_in,
                               int max_rank, const int32_t* offsets, int E, const int32_t* sorted_ids, int P,
                               int top_k, const int32_t* row_adapter, uint16_t* xa, int64_t row_offset,
                               int64_t row_end, int x_gather, hipStream_t s) {
@@ -430,7 +478,7 @@ hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const ui
     const int64_t subs = (row_end - base16 + 15) / 16;
     const dim3 sgrid(static_cast<unsigned>(subs));
 #define MOE_SHRINK(NB_)                                                                                          \
-    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, \
+    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, sorted_ids, \
                                                  P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
     switch (max_rank / 16) {
         case 1: MOE_SHRINK(1); break;
@@ -447,7 +495,7 @@ hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const ui
 }
 
 hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a_tab, const uint64_t* b_tab,
-                            const float* s_tab, int n_tab, int k_in, int n_out, int max_rank,
+                            const float* s_tab, int n_tab, int n_ad, int k_in, int n_out, int max_rank,
                             const int32_t* offsets, int E, const int32_t* sorted_ids, int P, int top_k,
                             const int32_t* row_adapter, uint16_t* xa, int64_t row_offset, int64_t row_end,
                             int x_gather, hipStream_t s) {
@@ -457,7 +505,7 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     const int64_t subs = (row_end - base16 + 15) / 16;
     const dim3 sgrid(static_cast<unsigned>(subs));
 #define MOE_SHRINK(NB_)                                                                                          \
-    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, k_in, max_rank, offsets, E, sorted_ids, \
+    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, sorted_ids, \
                                                  P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
     switch (max_rank / 16) {
         case 1: MOE_SHRINK(1); break;
@@ -474,7 +522,7 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     if (err != hipSuccess) return err;
     const dim3 grid((n_out + EXP_COLS * EXP_BLOCKS - 1) / (EXP_COLS * EXP_BLOCKS), static_cast<unsigned>(tiles));
 #define MOE_EXPAND(NKS_)                                                                                        \
-    lora_expand_fold_kernel<NKS_><<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_out, max_rank, offsets, E, \
+    lora_expand_fold_kernel<NKS_><<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_ad, n_out, max_rank, offsets, E, \
                                                       sorted_ids, P, top_k, row_adapter, base, row_offset, row_end, \
                                                       base16)
     switch (max_rank / 32) {
@@ -490,16 +538,16 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
 hipError_t launch_lora_gather_fold(const uint16_t* x, int64_t x_rows, uint16_t* base, int64_t base_rows,
                                    const int32_t* indices, int64_t n_slots, int top_k, int x_gather,
                                    const int32_t* row_map, const int32_t* row_adapter, const uint64_t* a_tab,
-                                   const uint64_t* b_tab, const float* s_tab, int n_tab, int k_in, int n_out,
-                                   int max_rank, uint16_t* xa, hipStream_t s) {
+                                   const uint64_t* b_tab, const float* s_tab, int n_tab, int n_ad, int k_in,
+                                   int n_out, int max_rank, uint16_t* xa, hipStream_t s) {
     if (n_slots <= 0 || n_tab <= 0) return hipSuccess;
     const dim3 sgrid(static_cast<unsigned>(n_slots), static_cast<unsigned>(max_rank / 16));
-    gather_shrink_kernel<<<sgrid, NT, 0, s>>>(x, indices, row_map, row_adapter, a_tab, b_tab, n_tab, top_k, x_gather,
+    gather_shrink_kernel<<<sgrid, NT, 0, s>>>(x, indices, row_map, row_adapter, a_tab, b_tab, n_tab, n_ad, top_k, x_gather,
                                               x_rows, base_rows, k_in, max_rank, xa);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 egrid(static_cast<unsigned>(n_slots), static_cast<unsigned>((n_out + 255) / 256));
-    gather_expand_kernel<<<egrid, NT, 0, s>>>(xa, indices, row_map, row_adapter, a_tab, b_tab, s_tab, n_tab, top_k,
+    gather_expand_kernel<<<egrid, NT, 0, s>>>(xa, indices, row_map, row_adapter, a_tab, b_tab, s_tab, n_tab, n_ad, top_k,
                                               x_gather, x_rows, base_rows, n_out, max_rank, base);
     return hipGetLastError();
 }

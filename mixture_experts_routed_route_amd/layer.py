@@ -29,7 +29,7 @@ import torch
 from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER
 from .ops import (Bf16Weight, Fp8Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows,
                   moe_align, moe_combine, moe_grouped_gemm, moe_grouped_gemm_fp8, moe_lora_fold, moe_lora_gather_fold,
-                  moe_quantize_fp8, moe_route, moe_route_align, moe_silu_mul, pack_lora_tables,
+                  moe_quantize_fp8, moe_route, moe_route_align, moe_silu_mul, pack_lora_tables, stack_lora_tables,
                   moe_grouped_gemm_gate_up_lora)
 
 FOLD_MODES = ("auto", "grouped", "gather")
@@ -104,16 +104,24 @@ class MoeLayer:
                                   torch.from_numpy(w["qzeros"]).to(device), int(w["group_size"]))
             gate, up, down = gq(d["gate"]), gq(d["up"]), gq(d["down"])
 
-        def tables(prefix):
-            if f"{prefix}_a" not in d:
+        def one(ad, prefix):
+            if f"{prefix}_a" not in ad:
                 return None
-            n = len(d["lora_ids"])
-            return pack_lora_tables(list(d["lora_ids"]), [bf(d[f"{prefix}_a"][i]) for i in range(n)],
-                                    [bf(d[f"{prefix}_b"][i]) for i in range(n)], list(d[f"{prefix}_scale"]),
+            n = len(ad["lora_ids"])
+            return pack_lora_tables(list(ad["lora_ids"]), [bf(ad[f"{prefix}_a"][i]) for i in range(n)],
+                                    [bf(ad[f"{prefix}_b"][i]) for i in range(n)], list(ad[f"{prefix}_scale"]),
                                     device)
-        lora = tables("lora") if "lora_ids" in d else None
-        lora_gate = tables("lora_gate") if "lora_ids" in d else None
-        lora_up = tables("lora_up") if "lora_ids" in d else None
+
+        def tables(prefix):
+            # one adapter's tables, or several adapters' stacked by adapter id (a mixed batch names
+            # each token's adapter in its row_adapter map)
+            if "lora_adapters" in d:
+                per = [one(ad, prefix) for ad in d["lora_adapters"]]
+                return stack_lora_tables(per, device) if any(t is not None for t in per) else None
+            return one(d, prefix) if "lora_ids" in d else None
+        lora = tables("lora")
+        lora_gate = tables("lora_gate")
+        lora_up = tables("lora_up")
         return MoeLayer(cfg.E, cfg.H, cfg.I, cfg.top_k, cfg.block_size, gate, up, down, lora, cfg.renormalize,
                         lora_cap, fold, lora_gate, lora_up, gate_up_fused)
 

@@ -16,7 +16,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, 
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Fp8Weight", "Routing", "moe_quantize_fp8", "moe_grouped_gemm_fp8", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_align_noalloc", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_align_noalloc", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "stack_lora_tables", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -336,14 +336,17 @@ def moe_grouped_gemm_fp8(op: int, a: torch.Tensor, a_scale: torch.Tensor, w0: Fp
 # ----------------------------------------------------------------------------- A5 LoRA fold
 @dataclass
 class LoraTables:
-    """Device tables of one adapter's per-expert down-projection LoRA (atlas MoeExpertRoute)."""
-    a_table: torch.Tensor      # int64 [n_tab] addresses (0 = unadapted)
+    """Device tables of the per-expert LoRA of one projection (atlas MoeExpertRoute), for
+    ``n_adapters`` installed adapters: row a of the [n_adapters, n_tab] tables belongs to adapter a,
+    whose tokens the per-token ``row_adapter`` map names (NULL map: adapter 0)."""
+    a_table: torch.Tensor      # int64 [n_adapters * n_tab] addresses (0 = unadapted)
     b_table: torch.Tensor
-    scale_table: torch.Tensor  # float32 [n_tab]
+    scale_table: torch.Tensor  # float32 [n_adapters * n_tab]
     n_tab: int
     k_in: int
     n_out: int
     max_rank: int
+    n_adapters: int = 1
     keep: List[torch.Tensor] = field(default_factory=list)  # owners of the A/B memory
 
 
@@ -370,7 +373,33 @@ def pack_lora_tables(ids: Sequence[int], a: Sequence[torch.Tensor], b: Sequence[
     n_out = b[0].shape[0]
     return LoraTables(as_i64(ao).to(device), as_i64(bo).to(device),
                       torch.tensor(list(so[:k]), dtype=torch.float32).to(device), k, k_in, n_out, max_rank,
-                      list(a) + list(b))
+                      keep=list(a) + list(b))
+
+
+def stack_lora_tables(adapters: Sequence[Optional[LoraTables]], device) -> LoraTables:
+    """The tables of several adapters as one [n_adapters, n_tab] set (adapter id = position; None =
+    an id with no tables for this projection).  n_tab is the longest table; shorter ones are padded
+    with unadapted entries."""
+    real = [t for t in adapters if t is not None]
+    if not real:
+        raise ValueError("no adapter has tables")
+    t0 = real[0]
+    if any((t.k_in, t.n_out, t.max_rank, t.n_adapters) != (t0.k_in, t0.n_out, t0.max_rank, 1) for t in real):
+        raise ValueError("stacked adapters must be single-adapter tables with one k_in, n_out and max_rank")
+    n_tab = max(t.n_tab for t in real)
+    n = len(adapters)
+    a = torch.zeros(n * n_tab, dtype=torch.int64, device=device)
+    b = torch.zeros_like(a)
+    sc = torch.zeros(n * n_tab, dtype=torch.float32, device=device)
+    keep: List[torch.Tensor] = []
+    for i, t in enumerate(adapters):
+        if t is None:
+            continue
+        a[i * n_tab: i * n_tab + t.n_tab] = t.a_table
+        b[i * n_tab: i * n_tab + t.n_tab] = t.b_table
+        sc[i * n_tab: i * n_tab + t.n_tab] = t.scale_table
+        keep += t.keep
+    return LoraTables(a, b, sc, n_tab, t0.k_in, t0.n_out, t0.max_rank, n_adapters=n, keep=keep)
 
 
 def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routing: Routing,
@@ -393,7 +422,8 @@ def moe_lora_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables, routi
     check(lib().moe_lora_fold(
         _dev(x, torch.bfloat16, "x"), _dev(base, torch.bfloat16, "base"), _dev(tables.a_table, torch.int64, "a_table"),
         _dev(tables.b_table, torch.int64, "b_table"), _dev(tables.scale_table, torch.float32, "scale_table"),
-        tables.n_tab, tables.k_in, tables.n_out, tables.max_rank, _dev(routing.offsets, torch.int32, "offsets"),
+        tables.n_tab, tables.n_adapters, tables.k_in, tables.n_out, tables.max_rank,
+        _dev(routing.offsets, torch.int32, "offsets"),
         routing.num_experts, _dev(routing.sorted_ids, torch.int32, "sorted_ids"), routing.num_pairs, routing.top_k,
         _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
         _dev(xa, torch.bfloat16, "xa"), xa.shape[0], row_offset, row_end, routing.max_pad, int(bool(x_gather)),
@@ -414,6 +444,9 @@ def moe_grouped_gemm_gate_up_lora(x: torch.Tensor, gate: Bf16Weight, up: Bf16Wei
     rank = tabs[0].max_rank
     if any(t.max_rank != rank or t.k_in != K or t.n_out != N for t in tabs):
         raise ValueError("gate and up tables must share max_rank and match the weights")
+    n_ad = tabs[0].n_adapters
+    if any(t.n_adapters != n_ad for t in tabs):
+        raise ValueError("gate and up tables must hold the same adapters")
     if tuple(xa.shape) != (2, routing.max_pad, rank):
         raise ValueError(f"xa must be [2, {routing.max_pad}, {rank}]")
     if out is None:
@@ -433,7 +466,7 @@ def moe_grouped_gemm_gate_up_lora(x: torch.Tensor, gate: Bf16Weight, up: Bf16Wei
         _dev(x, torch.bfloat16, "x"), ctypes.byref(sg), ctypes.byref(su), _dev(out, torch.bfloat16, "out"),
         _dev(routing.sorted_ids, torch.int32, "sorted_ids"), _dev(routing.offsets, torch.int32, "offsets"),
         routing.num_pairs, routing.top_k, routing.num_experts, N, K, routing.block_size, routing.max_pad,
-        ag, bg, cg, ng, au, bu, cu, nu, rank,
+        ag, bg, cg, ng, au, bu, cu, nu, n_ad, rank,
         _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
         _dev(xa, torch.bfloat16, "xa"), _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream(x)))
@@ -473,8 +506,8 @@ def moe_lora_gather_fold(x: torch.Tensor, base: torch.Tensor, tables: LoraTables
         _dev(row_map, torch.int32, "row_map") if row_map is not None else None,
         _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
         _dev(tables.a_table, torch.int64, "a_table"), _dev(tables.b_table, torch.int64, "b_table"),
-        _dev(tables.scale_table, torch.float32, "scale_table"), tables.n_tab, tables.k_in, tables.n_out,
-        tables.max_rank, _dev(xa, torch.bfloat16, "xa"), _stream(x)))
+        _dev(tables.scale_table, torch.float32, "scale_table"), tables.n_tab, tables.n_adapters, tables.k_in,
+        tables.n_out, tables.max_rank, _dev(xa, torch.bfloat16, "xa"), _stream(x)))
     return base
 
 

@@ -33,6 +33,12 @@ below.
   adapted expert A_e ``[rank, I]`` then B_e ``[H, rank]`` ~ N(0, 0.01) in bf16
   (all A's are drawn before all B's), then scale_e ~ U(0.5, 2.0).  The real
   rank is zero-padded to ``max_rank``: A rows and B columns past ``rank`` are 0.
+* Several adapters (``lora_adapters`` > 1, a mixed batch): adapter 0 is the
+  one above; adapter j >= 1 adapts the experts e with (e + j) % 3 == 0, its
+  tables drawn the same way, after everything above (so adapter 0 is the same
+  with or without the others).  Then each token's adapter id is drawn
+  uniformly from {-1 (base, no fold), 0, .., lora_adapters - 1}.  The adapters
+  are ``d["lora_adapters"]`` (one dict per id) and the map ``d["row_adapter"]``.
 """
 from __future__ import annotations
 
@@ -61,6 +67,7 @@ class MoeConfig:
     lora_rank: int = 0             # 0 = no LoRA fold
     lora_max_rank: int = 0
     lora_gate_up: bool = False     # also LoRA tables for the gate and up projections
+    lora_adapters: int = 1         # adapters installed; > 1 draws a per-token adapter map
     renormalize: bool = True
     seed: int = 0
 
@@ -253,4 +260,22 @@ def make_inputs(cfg: MoeConfig, seed: Optional[int] = None, threads: int = 8) ->
                 d[f"lora_{proj}_a"] = ga
                 d[f"lora_{proj}_b"] = gb
                 d[f"lora_{proj}_scale"] = rng.uniform(0.5, 2.0, size=n).astype(np.float32)
+        if cfg.lora_adapters > 1:
+            keys = [k for k in d if k.startswith("lora_")]
+            adapters = [{k: d[k] for k in keys}]
+            for j in range(1, cfg.lora_adapters):
+                ids_j = np.array([e for e in range(E) if (e + j) % 3 == 0], dtype=np.int32)
+                nj = len(ids_j)
+                ad = {"lora_ids": ids_j}
+                projs = [("lora", I, H)] + ([("lora_gate", H, I), ("lora_up", H, I)] if cfg.lora_gate_up else [])
+                for pre, k_in, n_out in projs:
+                    aa = np.zeros((nj, R, k_in), dtype=np.uint16)
+                    aa[:, :r, :] = _normal_bf16(rng, (nj, r, k_in), 0.01)
+                    bb = np.zeros((nj, n_out, R), dtype=np.uint16)
+                    bb[:, :, :r] = _normal_bf16(rng, (nj, n_out, r), 0.01)
+                    ad[f"{pre}_a"], ad[f"{pre}_b"] = aa, bb
+                    ad[f"{pre}_scale"] = rng.uniform(0.5, 2.0, size=nj).astype(np.float32)
+                adapters.append(ad)
+            d["lora_adapters"] = adapters
+            d["row_adapter"] = rng.integers(-1, cfg.lora_adapters, size=T).astype(np.int32)
     return d

@@ -37,7 +37,8 @@ __all__ = [
     "route", "max_padded", "align", "check_group_arrays",
     "gptq_unpack_q", "gptq_unpack_z", "gptq_dequant_expert",
     "out_dim", "expert_matrix", "grouped_gate_up", "grouped_gate_up_lora", "grouped_down",
-    "pack_expert_tables", "lora_windows", "lora_window_tiles", "lora_fold", "lora_gather_fold",
+    "pack_expert_tables", "adapter_tables", "token_adapter", "lora_windows", "lora_window_tiles", "lora_fold",
+    "lora_gather_fold",
     "combine", "moe_layer", "moe_tokens",
     "e4m3_to_f64", "e4m3_round", "quantize_rows_fp8", "fp8_expert_matrix", "grouped_gate_up_fp8",
     "grouped_down_fp8",
@@ -372,14 +373,15 @@ def grouped_gate_up(x_bits: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray],
 
 
 def grouped_gate_up_lora(x_bits: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray], top_k: int,
-                         tabs_gate, tabs_up) -> np.ndarray:
+                         tabs_gate, tabs_up, row_adapter: Optional[np.ndarray] = None) -> np.ndarray:
     """Gate/up with LoRA folded into each projection before SiLU: atlas ``moe_lora_grouped.rs``,
     ``moe_lora_grouped_down`` with ``x_gather`` = 1 (token-major input, base = the sorted BF16
     ``expert_gate_out`` / ``expert_up_out``), then ``moe_lora_gather_bgmv``'s ``moe_silu_mul``
     into a BF16 buffer.
 
     For every real sorted row: g = bf16(Wg[e] x[t]), u = bf16(Wu[e] x[t]); each is folded
-    with its own tables (a projection without tables is left as it is); h = bf16(silu(g) * u).
+    with its own tables (a projection without tables is left as it is; ``row_adapter`` picks the
+    adapter of each token as in ``lora_fold``); h = bf16(silu(g) * u).
     Unlike the fused path, gate and up are rounded to bf16 before SiLU, as the page's path
     materialises them.  Sentinel rows are NaN.
     """
@@ -392,9 +394,9 @@ def grouped_gate_up_lora(x_bits: np.ndarray, w_gate, w_up, al: Dict[str, np.ndar
         g[rr] = round_bf16(xt @ expert_matrix(w_gate, e).T)
         u[rr] = round_bf16(xt @ expert_matrix(w_up, e).T)
     if tabs_gate is not None:
-        g = lora_fold(g, X, tabs_gate, al, top_k, x_gather=True)
+        g = lora_fold(g, X, tabs_gate, al, top_k, row_adapter, x_gather=True)
     if tabs_up is not None:
-        u = lora_fold(u, X, tabs_up, al, top_k, x_gather=True)
+        u = lora_fold(u, X, tabs_up, al, top_k, row_adapter, x_gather=True)
     return round_bf16(silu(g) * u)
 
 
@@ -468,6 +470,25 @@ def pack_expert_tables(entries: Iterable[Tuple[int, object, object, float]]):
     return a, b, s, n
 
 
+def adapter_tables(tables, a: int):
+    """The per-expert tables adapter ``a`` folds with, or None.
+
+    atlas ``moe_lora_grouped.rs``, ``MoeExpertRoute``: the per-expert tables are built at adapter
+    install, and the adapter of a mixed batch's token comes from the per-row ``moe_row_adapter``
+    (< 0 = base, no fold), not from the tables.  Reading: ``tables`` is either one adapter's
+    (a, b, scale, n) tuple, which is adapter 0 (the page's single-adapter path with a null map), or
+    a list of such tuples (or None) indexed by adapter id; any other id folds nothing.
+    """
+    if isinstance(tables, list):
+        return tables[a] if 0 <= a < len(tables) else None
+    return tables if a == 0 else None
+
+
+def token_adapter(row_adapter: Optional[np.ndarray], t: int) -> int:
+    """Adapter id of token t: row_adapter[t], or 0 without a map (the single-adapter path)."""
+    return 0 if row_adapter is None else int(row_adapter[t])
+
+
 def lora_window_tiles(row_offset: int, row_end: int, m_tile: int = 64) -> int:
     """Tiles of one window: max(1, ceil((row_end - row_offset) / 64)).
 
@@ -494,9 +515,10 @@ def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], t
     """Down-projection LoRA fold over sorted rows: atlas ``moe_lora_grouped.rs``.
 
     For every sorted row r in the window [row_offset, row_end) that is real
-    (sorted id < P), whose expert e (the span [offsets[e], offsets[e+1])
-    holding r) is adapted (e < table length and a non-null table entry), and
-    whose token's ``row_adapter`` entry is >= 0 (or no adapter map is given):
+    (sorted id < P), whose token t has adapter a = row_adapter[t] >= 0 (a = 0
+    without a map), and whose expert e (the span [offsets[e], offsets[e+1])
+    holding r) is adapted by that adapter (``adapter_tables(tables, a)`` exists,
+    e < its length and its entry is non-null):
 
         xa    = bf16(A_e  x[r])      (shrink, [max_rank])
         delta = bf16(B_e  xa)        (expand, [n_out])
@@ -511,9 +533,9 @@ def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], t
     fp64.  Rows outside the window, sentinel rows and unadapted rows are left
     as they are.  ``tables`` = (a_list, b_list, scale_list, n) from
     ``pack_expert_tables`` with A_e [max_rank, k_in] and B_e [n_out, max_rank]
-    as bf16 bit arrays.  Returns a new array.
+    as bf16 bit arrays, or a list of those, one per adapter id.  Returns a new
+    array.
     """
-    a_tab, b_tab, s_tab, n_tab = tables
     P = al["num_pairs"]
     sid, off = al["sorted_ids"], al["offsets"]
     E = len(off) - 1
@@ -526,13 +548,16 @@ def lora_fold(y: np.ndarray, x: np.ndarray, tables, al: Dict[str, np.ndarray], t
         if p < 0 or p >= P:
             continue
         e = next((k for k in range(E) if off[k] <= r < off[k + 1]), None)
-        if e is None or e >= n_tab or a_tab[e] is None or b_tab[e] is None:
+        a = token_adapter(row_adapter, p // top_k)
+        tab = adapter_tables(tables, a) if a >= 0 else None
+        if e is None or tab is None:
             continue
-        if row_adapter is not None and row_adapter[p // top_k] < 0:
+        a_tab, b_tab, s_tab, n_tab = tab
+        if e >= n_tab or a_tab[e] is None or b_tab[e] is None:
             continue
-        if e not in mats:
-            mats[e] = (bf16_bits_to_f64(a_tab[e]), bf16_bits_to_f64(b_tab[e]))
-        A, B = mats[e]
+        if (a, e) not in mats:
+            mats[(a, e)] = (bf16_bits_to_f64(a_tab[e]), bf16_bits_to_f64(b_tab[e]))
+        A, B = mats[(a, e)]
         xa = round_bf16(A @ x[p // top_k if x_gather else r])
         delta = round_bf16(B @ xa)
         if bf16_base:
@@ -548,9 +573,9 @@ def lora_gather_fold(y: np.ndarray, x: np.ndarray, tables, indices: np.ndarray, 
     """Slot-major LoRA fold of decode: atlas ``moe_lora_grouped.rs``, ``moe_lora_gather_bgmv``.
 
     There is no sorting: flat (token, slot) row s < n_slots = len(indices)
-    takes its expert from ``indices[s]`` and its adapter decision from
-    ``row_adapter[s // top_k]`` (``gather_row_token``; < 0 skips, None folds
-    every row).  The x row is the slot itself for the down fold and the owning
+    takes its expert from ``indices[s]`` and its adapter from
+    ``row_adapter[s // top_k]`` (``gather_row_token``; < 0 skips, None is
+    adapter 0 for every row; ``tables`` as in ``lora_fold``).  The x row is the slot itself for the down fold and the owning
     token s // top_k with ``x_gather`` (the gate/up fold over token-major x).
     The arithmetic is that of the grouped fold (module doc):
 
@@ -565,14 +590,16 @@ def lora_gather_fold(y: np.ndarray, x: np.ndarray, tables, indices: np.ndarray, 
     (and of x without ``x_gather``), and a negative entry skips the slot; None
     is the page's slot-major layout.  Returns a new array.
     """
-    a_tab, b_tab, s_tab, n_tab = tables
     y = np.array(y, dtype=np.float64, copy=True)
     ids = np.asarray(indices).reshape(-1)
     for s in range(len(ids)):
         e = int(ids[s])
-        if e < 0 or e >= n_tab or a_tab[e] is None or b_tab[e] is None:
+        a = token_adapter(row_adapter, s // top_k)
+        tab = adapter_tables(tables, a) if a >= 0 else None
+        if tab is None:
             continue
-        if row_adapter is not None and row_adapter[s // top_k] < 0:
+        a_tab, b_tab, s_tab, n_tab = tab
+        if e < 0 or e >= n_tab or a_tab[e] is None or b_tab[e] is None:
             continue
         row = s if row_map is None else int(row_map[s])
         if row < 0:
@@ -608,18 +635,30 @@ def combine(y: np.ndarray, inv: Optional[np.ndarray], topk_w: np.ndarray, T: int
 
 
 # ----------------------------------------------------------------------------- whole layer
-def _lora_tables(d, proj: str = "down") -> Optional[tuple]:
-    if proj != "down":
-        if f"lora_{proj}_a" not in d:
-            return None
-        return pack_expert_tables(
-            (int(e), d[f"lora_{proj}_a"][i], d[f"lora_{proj}_b"][i], float(d[f"lora_{proj}_scale"][i]))
-            for i, e in enumerate(d["lora_ids"]))
-    if "lora_ids" not in d:
+def _adapter_dicts(d) -> List[Dict[str, object]]:
+    """The installed adapters: ``d["lora_adapters"]`` (one dict per adapter id) when the inputs carry
+    several, else the inputs themselves when they carry one adapter's tables, else none."""
+    if "lora_adapters" in d:
+        return list(d["lora_adapters"])
+    return [d] if "lora_ids" in d else []
+
+
+def _pack_one(ad, proj: str):
+    pre = "lora" if proj == "down" else f"lora_{proj}"
+    if f"{pre}_a" not in ad:
         return None
-    return pack_expert_tables(
-        (int(e), d["lora_a"][i], d["lora_b"][i], float(d["lora_scale"][i]))
-        for i, e in enumerate(d["lora_ids"]))
+    return pack_expert_tables((int(e), ad[f"{pre}_a"][i], ad[f"{pre}_b"][i], float(ad[f"{pre}_scale"][i]))
+                              for i, e in enumerate(ad["lora_ids"]))
+
+
+def _lora_tables(d, proj: str = "down"):
+    """Tables of one projection: one adapter's tuple, a list indexed by adapter id (several
+    adapters), or None when no adapter has tables for it."""
+    ads = _adapter_dicts(d)
+    tabs = [_pack_one(ad, proj) for ad in ads]
+    if all(t is None for t in tabs):
+        return None
+    return tabs if "lora_adapters" in d else tabs[0]
 
 
 def _weights(d):
@@ -643,17 +682,28 @@ def moe_layer(d: Dict[str, object], max_pad: Optional[int] = None) -> Dict[str, 
     if "fp8_gate" in d:
         return _moe_layer_fp8(d, ids, w, al)
     wg, wu, wd = _weights(d)
+    ra = d.get("row_adapter")
     tg, tu = _lora_tables(d, "gate"), _lora_tables(d, "up")
     if tg is None and tu is None:
         h = grouped_gate_up(d["x"], wg, wu, al, cfg.top_k)
     else:
-        h = grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu)
+        h = grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu, ra)
     y = grouped_down(h, wd, al)
     tabs = _lora_tables(d)
     if tabs is not None:
-        y = lora_fold(y, round_bf16(np.nan_to_num(h)), tabs, al, cfg.top_k, bf16_base=False)
+        y = lora_fold(y, round_bf16(np.nan_to_num(h)), tabs, al, cfg.top_k, ra, bf16_base=False)
     out = combine(y, al["inv"], w, cfg.T, cfg.top_k)
     return {"ids": ids, "w": w, "align": al, "h": h, "y": y, "out": out}
+
+
+def _token_delta(tables, a: int, e: int, xin: np.ndarray) -> Optional[np.ndarray]:
+    """scale * bf16(B bf16(A xin)) of adapter a's expert e for one activation row, or None when that
+    adapter does not adapt e (or a < 0, the base)."""
+    tab = adapter_tables(tables, a) if (tables is not None and a >= 0) else None
+    if tab is None or e >= tab[3] or tab[0][e] is None or tab[1][e] is None:
+        return None
+    xa = round_bf16(xin @ bf16_bits_to_f64(tab[0][e]).T)
+    return np.float64(np.float32(tab[2][e])) * round_bf16(xa @ bf16_bits_to_f64(tab[1][e]).T)
 
 
 def _moe_tokens_fp8(d, tokens, ids, w) -> np.ndarray:
@@ -675,9 +725,9 @@ def _moe_tokens_fp8(d, tokens, ids, w) -> np.ndarray:
             hs = round_bf16(h)
             hq, sh = quantize_rows_fp8(hs[None, :])
             y = Wd @ (e4m3_to_f64(hq[0]) * np.float64(sh[0]))
-            if tabs is not None and e < tabs[3] and tabs[0][e] is not None:
-                xa = round_bf16(hs @ bf16_bits_to_f64(tabs[0][e]).T)
-                y = y + np.float64(np.float32(tabs[2][e])) * round_bf16(xa @ bf16_bits_to_f64(tabs[1][e]).T)
+            dl = _token_delta(tabs, token_adapter(d.get("row_adapter"), tokens[i]), e, hs)
+            if dl is not None:
+                y = y + dl
             out[i] += np.float64(w[tokens[i], j]) * y
     return out
 
@@ -695,7 +745,7 @@ def _moe_layer_fp8(d, ids, w, al) -> Dict[str, object]:
     y[~real] = np.nan
     tabs = _lora_tables(d)
     if tabs is not None:
-        y = lora_fold(y, hs, tabs, al, cfg.top_k, bf16_base=False)
+        y = lora_fold(y, hs, tabs, al, cfg.top_k, d.get("row_adapter"), bf16_base=False)
     out = combine(y, al["inv"], w, cfg.T, cfg.top_k)
     return {"ids": ids, "w": w, "align": al, "h": np.where(real[:, None], h, np.nan), "y": y, "out": out,
             "xq": xq, "sx": sx, "hq": hq, "sh": sh}
@@ -718,6 +768,7 @@ def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
     tabs = _lora_tables(d)
     tabs_gu = (_lora_tables(d, "gate"), _lora_tables(d, "up"))
     tokens = list(tokens)
+    ra = d.get("row_adapter")
     by_e: Dict[int, List[Tuple[int, int]]] = {}
     for i, t in enumerate(tokens):
         for j in range(cfg.top_k):
@@ -726,24 +777,24 @@ def moe_tokens(d: Dict[str, object], tokens: Sequence[int],
     contrib = {}
     for e, lst in sorted(by_e.items()):
         X = bf16_bits_to_f64(d["x"][[tokens[i] for i, _ in lst]])
+        adapters = [token_adapter(ra, tokens[i]) for i, _ in lst]
         if tabs_gu == (None, None):
             h = silu(X @ expert_matrix(wg, e).T) * (X @ expert_matrix(wu, e).T)
         else:
             gu = []
             for wm, tb in zip((wg, wu), tabs_gu):
                 v = round_bf16(X @ expert_matrix(wm, e).T)
-                if tb is not None and e < tb[3] and tb[0][e] is not None:
-                    xa = round_bf16(X @ bf16_bits_to_f64(tb[0][e]).T)
-                    v = round_bf16(v + np.float64(np.float32(tb[2][e])) * round_bf16(xa @ bf16_bits_to_f64(tb[1][e]).T))
+                for q, a in enumerate(adapters):
+                    dl = _token_delta(tb, a, e, X[q])
+                    if dl is not None:
+                        v[q] = round_bf16(v[q] + dl)
                 gu.append(v)
             h = round_bf16(silu(gu[0]) * gu[1])
         yy = h @ expert_matrix(wd, e).T
-        if tabs is not None and e < tabs[3] and tabs[0][e] is not None:
-            A = bf16_bits_to_f64(tabs[0][e])
-            B = bf16_bits_to_f64(tabs[1][e])
-            xa = round_bf16(round_bf16(h) @ A.T)
-            delta = round_bf16(xa @ B.T)
-            yy = yy + np.float64(np.float32(tabs[2][e])) * delta
+        for q, a in enumerate(adapters):
+            dl = _token_delta(tabs, a, e, round_bf16(h[q]))
+            if dl is not None:
+                yy[q] = yy[q] + dl
         for (i, j), row in zip(lst, yy):
             contrib[(i, j)] = row
     for i, t in enumerate(tokens):

@@ -124,21 +124,21 @@ def test_argument_validation_rejects_before_launch(L):
     rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w4), None, fake, fake, fake, fake, 128, 2, 8, 128,
                   256, 16, 256, None, 0, None)
     assert rc == -1 and "group_size" in msg
-    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 48, fake, 64, fake, 12288, 6,
+    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1, 1408, 4096, 48, fake, 64, fake, 12288, 6,
                   None, fake, 16320, 0, 16320, 16320, 0, None)
     assert rc == -1 and "max_rank" in msg
-    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 64, fake, 64, fake, 12288, 6,
+    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1, 1408, 4096, 64, fake, 64, fake, 12288, 6,
                   None, fake, 100, 0, 16320, 16320, 0, None)
     assert rc == -1 and "cap" in msg
-    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 65, 1408, 4096, 64, fake, 64, fake, 12288, 6,
+    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 65, 1, 1408, 4096, 64, fake, 64, fake, 12288, 6,
                   None, fake, 16320, 0, 16320, 16320, 0, None)
     assert rc == -1 and "n_tab" in msg
     # gather fold: (x, x_rows, base, base_rows, indices, n_slots, top_k, x_gather, row_map, row_adapter,
-    #              a_table, b_table, scale_table, n_tab, k_in, n_out, max_rank, xa, stream)
+    #              a_table, b_table, scale_table, n_tab, n_adapters, k_in, n_out, max_rank, xa, stream)
     g = lambda **kw: _rc(L, "moe_lora_gather_fold", *[kw.get(k, v) for k, v in (
         ("x", fake), ("x_rows", 96), ("base", fake), ("base_rows", 96), ("indices", fake), ("n_slots", 96),
         ("top_k", 6), ("x_gather", 0), ("row_map", None), ("row_adapter", None), ("a", fake), ("b", fake),
-        ("s", fake), ("n_tab", 63), ("k_in", 1408), ("n_out", 2048), ("max_rank", 64), ("xa", fake),
+        ("s", fake), ("n_tab", 63), ("n_adapters", 1), ("k_in", 1408), ("n_out", 2048), ("max_rank", 64), ("xa", fake),
         ("stream", None))])
     assert g(x_gather=2)[0] == -1 and "x_gather" in g(x_gather=2)[1]
     assert g(n_slots=95)[0] == -1 and "n_slots" in g(n_slots=95)[1]
@@ -151,7 +151,8 @@ def test_argument_validation_rejects_before_launch(L):
     assert g(row_map=P((1 << 20) + 4))[0] == -1 and "aligned" in g(row_map=P((1 << 20) + 4))[1]
     assert g(n_slots=0, x=None, base=None, indices=None)[0] == 0   # no slots: nothing to do
     assert g(n_tab=0, x=None)[0] == 0                               # no adapted expert: nothing to do
-    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1408, 4096, 64, fake, 64, fake, 12288, 6,
+    assert g(n_adapters=0)[0] == -1 and "n_adapters" in g(n_adapters=0)[1]
+    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 1, 1408, 4096, 64, fake, 64, fake, 12288, 6,
                   None, fake, 16320, 0, 16320, 16320, 2, None)
     assert rc == -1 and "x_gather" in msg
     rc, msg = _rc(L, "moe_silu_mul", fake, fake, fake, None, 0, 16, 100, None)
@@ -185,14 +186,18 @@ def test_argument_validation_rejects_before_launch(L):
                   256, 16, 256, None, 0, None)
     assert rc == -1 and "unsupported type" in msg
     # fused gate/up LoRA: (x, w_gate, w_up, hs, sorted_ids, offsets, P, top_k, E, n, k, bs, max_pad,
-    #                      a_g, b_g, s_g, n_g, a_u, b_u, s_u, n_u, max_rank, row_adapter, xa, ws, ws_bytes, stream)
+    #                      a_g, b_g, s_g, n_g, a_u, b_u, s_u, n_u, n_adapters, max_rank, row_adapter, xa, ws,
+    #                      ws_bytes, stream)
     lg = lambda wg, rank: _rc(L, "moe_grouped_gemm_gate_up_lora", fake, ctypes.byref(wg), ctypes.byref(wg), fake, fake,
-                              fake, 128, 2, 8, 128, 256, 16, 256, fake, fake, fake, 8, fake, fake, fake, 8, rank, None,
+                              fake, 128, 2, 8, 128, 256, 16, 256, fake, fake, fake, 8, fake, fake, fake, 8, 1, rank, None,
                               fake, None, 0, None)
     rc, msg = lg(w4, 64)
     assert rc == -2 and "bf16" in msg
     rc, msg = lg(w, 48)
     assert rc == -1 and "max_rank" in msg
+    rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 0, 1408, 4096, 64, fake, 64, fake, 12288, 6,
+                  None, fake, 16320, 0, 16320, 16320, 0, None)
+    assert rc == -1 and "n_adapters" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 100, 8, None)
     assert rc == -1 and "hidden" in msg
     rc, msg = _rc(L, "moe_combine", fake, None, fake, fake, 4, 2, 128, 7, None)

@@ -95,3 +95,20 @@ def test_lora_fold_rejects_mismatched_buffers():
     with pytest.raises(ValueError, match="row_adapter"):
         m.moe_lora_fold(bf(r.max_pad, I), bf(r.max_pad, H), tabs, r, xa=xa,
                         row_adapter=torch.zeros(T - 1, dtype=torch.int32))
+
+
+def test_stack_lora_tables_layout():
+    """Adapter a's tables land in row a of the [n_adapters, n_tab] stack; shorter tables and
+    missing adapters are padded with unadapted (zero) entries."""
+    def one(n_tab, base):
+        return m.LoraTables(torch.arange(base, base + n_tab, dtype=torch.int64),
+                            torch.arange(base + 100, base + 100 + n_tab, dtype=torch.int64),
+                            torch.full((n_tab,), float(base), dtype=torch.float32), n_tab, I, H, 32)
+    st = m.stack_lora_tables([one(3, 10), None, one(5, 20)], "cpu")
+    assert (st.n_tab, st.n_adapters) == (5, 3)
+    assert st.a_table.tolist() == [10, 11, 12, 0, 0] + [0] * 5 + [20, 21, 22, 23, 24]
+    assert st.b_table.tolist() == [110, 111, 112, 0, 0] + [0] * 5 + [120, 121, 122, 123, 124]
+    assert st.scale_table.tolist() == [10.0] * 3 + [0.0] * 7 + [20.0] * 5
+    with pytest.raises(ValueError):
+        m.stack_lora_tables([one(3, 10), m.LoraTables(torch.zeros(2, dtype=torch.int64), torch.zeros(2, dtype=torch.int64),
+                                                      torch.zeros(2), 2, I, H, 64)], "cpu")

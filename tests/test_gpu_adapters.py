@@ -1,0 +1,180 @@
+"""GPU parity of mixed-adapter batches (atlas moe_lora_grouped.rs, MoeExpertRoute: a mixed batch's
+adapter identity travels in the per-row moe_row_adapter, not in the expert tables).  The tables of
+three adapters are stacked [n_adapters, n_tab]; each token's row_adapter entry names its adapter
+(-1: the base, no fold).  Every fold form is checked against the oracle on the same inputs: the
+grouped fold and the gather fold stage by stage, the gate/up LoRA in the GEMM epilogue against the
+oracle and bit for bit against the unfused GPU path, and the whole layer."""
+import numpy as np
+import pytest
+
+import oracle
+from moe_synth import MoeConfig, make_inputs, f32_to_bf16_bits
+from _util import assert_close_rows, bf16_dev, bf16_host, bf16_ulp_diff, bits_host, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+CANARY = 0x7FC1
+
+MIX = MoeConfig("mix_small", T=300, H=512, I=256, E=16, top_k=6, block_size=64, lora_rank=16, lora_max_rank=64,
+                lora_adapters=3, seed=51)
+MIX_GU = MIX.with_(name="mix_gu_small", lora_gate_up=True, seed=52)
+MIX_GU_256 = MIX_GU.with_(name="mix_gu_256rows", T=1100, E=8, top_k=2, seed=53)   # 256-row kernel
+MIX_DECODE = MoeConfig("mix_decode", T=16, H=2048, I=1408, E=64, top_k=6, block_size=16, weights="int4_gptq",
+                       group_size=128, lora_rank=16, lora_max_rank=64, lora_adapters=3, seed=54)
+
+
+def note(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import mixture_experts_routed_route_amd as m
+    m.lib()
+    return torch.device("cuda:0")
+
+
+def _routing(cfg, d):
+    import mixture_experts_routed_route_amd as m
+    ids, w = oracle.route(d["logits"], cfg.top_k, cfg.renormalize)
+    al = oracle.align(ids, cfg.E, cfg.block_size)
+    r = m.moe_align(to_dev(ids), cfg.E, cfg.block_size)
+    return ids, al, r
+
+
+def _real(al, P):
+    return np.flatnonzero(al["sorted_ids"] < P)
+
+
+def _adapter_of_rows(al, ra, k, rows):
+    return np.array([ra[al["sorted_ids"][rr] // k] for rr in rows])
+
+
+def test_mixed_adapters_grouped_fold_stage(dev):
+    import mixture_experts_routed_route_amd as m
+    cfg = MIX
+    note(f"mixed adapters grouped fold {cfg.name}")
+    d = make_inputs(cfg)
+    ra = d["row_adapter"]
+    ids, al, r = _routing(cfg, d)
+    real = _real(al, cfg.P)
+    rng = np.random.default_rng(5)
+    x = np.full((r.max_pad, cfg.I), CANARY, np.uint16)
+    x[real] = f32_to_bf16_bits(rng.standard_normal((real.size, cfg.I)).astype(np.float32))
+    base = np.full((r.max_pad, cfg.H), CANARY, np.uint16)
+    base[real] = f32_to_bf16_bits((rng.standard_normal((real.size, cfg.H)) * 0.05).astype(np.float32))
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    assert layer.lora.n_adapters == 3
+    tabs = oracle.moe_oracle._lora_tables(d)
+    ref = oracle.lora_fold(oracle.bf16_bits_to_f64(base), oracle.bf16_bits_to_f64(x), tabs, al, cfg.top_k,
+                           row_adapter=ra)
+    got = bf16_dev(base)
+    m.moe_lora_fold(bf16_dev(x), got, layer.lora, r, row_adapter=to_dev(ra))
+    gb = bits_host(got)
+    pad = np.setdiff1d(np.arange(r.max_pad), real)
+    assert (gb[pad] == CANARY).all(), "padding rows of the base written"
+    ref_bits = f32_to_bf16_bits(ref[real].astype(np.float32))
+    ulp = bf16_ulp_diff(gb[real], ref_bits)
+    note(f"  exact {(ulp == 0).mean():.5f}, max ulp of the result {ulp.max()}")
+    # the bar of the fold where base and scale * delta may cancel: within 3 bf16 ulps of the largest
+    # of |base|, |result| and |scale * delta|, and >= 99.9% bit-exact
+    from test_gpu_parity import _gather_check
+    sd = oracle.lora_fold(np.zeros(base.shape), oracle.bf16_bits_to_f64(x), tabs, al, cfg.top_k, row_adapter=ra,
+                          bf16_base=False)
+    _gather_check(gb, ref, sd, base, real, "mixed adapters grouped fold")
+    # rows the oracle leaves alone are bit-identical; each adapter folds some rows
+    same = np.all(ref_bits == base[real], axis=1)
+    assert np.array_equal(gb[real][same], base[real][same])
+    changed_by = _adapter_of_rows(al, ra, cfg.top_k, real[~same])
+    assert set(np.unique(changed_by)) == {0, 1, 2}, np.unique(changed_by)
+    assert (_adapter_of_rows(al, ra, cfg.top_k, real[same]) >= -1).all()
+
+
+def test_mixed_adapters_gather_fold_on_sorted_rows(dev):
+    import mixture_experts_routed_route_amd as m
+    from test_gpu_parity import _gather_check
+    cfg = MIX_DECODE
+    note(f"mixed adapters gather fold {cfg.name}")
+    d = make_inputs(cfg)
+    ra = d["row_adapter"]
+    ids, al, r = _routing(cfg, d)
+    real = _real(al, cfg.P)
+    rng = np.random.default_rng(6)
+    x = np.zeros((r.max_pad, cfg.I), np.uint16)
+    x[real] = f32_to_bf16_bits(rng.standard_normal((real.size, cfg.I)).astype(np.float32))
+    base = np.full((r.max_pad, cfg.H), CANARY, np.uint16)
+    base[real] = f32_to_bf16_bits((rng.standard_normal((real.size, cfg.H)) * 0.05).astype(np.float32))
+    layer = m.MoeLayer.from_arrays(d, "cuda")
+    tabs = oracle.moe_oracle._lora_tables(d)
+    xf, bf = oracle.bf16_bits_to_f64(x), oracle.bf16_bits_to_f64(base)
+    want = oracle.lora_gather_fold(bf, xf, tabs, ids.reshape(-1), cfg.top_k, row_adapter=ra, row_map=al["inv"])
+    sd = oracle.lora_gather_fold(np.zeros(bf.shape), xf, tabs, ids.reshape(-1), cfg.top_k, row_adapter=ra,
+                                 row_map=al["inv"])
+    got = bf16_dev(base)
+    m.moe_lora_gather_fold(bf16_dev(x), got, layer.lora, to_dev(ids), cfg.top_k, row_map=r.inv_sorted,
+                           row_adapter=to_dev(ra))
+    gb = bits_host(got)
+    folded = np.flatnonzero(np.any(sd != 0, axis=1))
+    assert set(np.unique(_adapter_of_rows(al, ra, cfg.top_k, folded))) == {0, 1, 2}
+    _gather_check(gb, want, sd, base, folded, "mixed adapters gather fold")
+    others = np.setdiff1d(np.arange(r.max_pad), folded)
+    assert np.array_equal(gb[others], base[others])
+
+
+@pytest.mark.parametrize("cfg", [MIX_GU, MIX_GU_256], ids=["128rows", "256rows"])
+def test_mixed_adapters_gate_up_fused(dev, cfg):
+    import torch
+    import mixture_experts_routed_route_amd as m
+    note(f"mixed adapters gate/up fused {cfg.name}")
+    d = make_inputs(cfg)
+    ra = d["row_adapter"]
+    ids, al, r = _routing(cfg, d)
+    real = _real(al, cfg.P)
+    outs = {}
+    for name, fused in (("fused", True), ("unfused", False)):
+        lay = m.MoeLayer.from_arrays(d, "cuda", gate_up_fused=fused)
+        b = lay.plan(cfg.T, "cuda")
+        lay.route_align(to_dev(d["logits"]), b)
+        b.hs.view(torch.int16).fill_(CANARY)
+        lay.gate_up_stage(bf16_dev(d["x"]), b, to_dev(ra))
+        torch.cuda.synchronize()
+        outs[name] = bits_host(b.hs)
+    pad = np.setdiff1d(np.arange(al["sorted_ids"].size), real)
+    assert (outs["fused"][pad] == CANARY).all(), "padding rows of Hs written"
+    exact = (outs["fused"][real] == outs["unfused"][real]).mean()
+    note(f"  fused == unfused bits on {exact:.5f} of the values")
+    wg, wu, wd = oracle.moe_oracle._weights(d)
+    tg, tu = oracle.moe_oracle._lora_tables(d, "gate"), oracle.moe_oracle._lora_tables(d, "up")
+    h = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu, ra)
+    h0 = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, None, None)
+    fused = oracle.bf16_bits_to_f64(outs["fused"][real])
+    assert_close_rows(fused, h[real], TOL, f"fused vs oracle {cfg.name}")
+    assert_close_rows(oracle.bf16_bits_to_f64(outs["unfused"][real]), h[real], TOL, f"unfused vs oracle {cfg.name}")
+    # the folds show: rows whose adapter adapts their expert differ from the unfolded result
+    moved = np.linalg.norm(h[real] - h0[real], axis=1) > 0
+    assert set(np.unique(_adapter_of_rows(al, ra, cfg.top_k, real[moved]))) == {0, 1, 2}
+    assert exact >= 0.999
+
+
+@pytest.mark.parametrize("cfg,fold", [(MIX, "grouped"), (MIX, "gather"), (MIX_GU, "grouped"),
+                                      (MIX_DECODE, "gather")], ids=["mix_grouped", "mix_gather", "mix_gu",
+                                                                    "mix_decode"])
+def test_layer_mixed_adapters(dev, cfg, fold):
+    import torch
+    import mixture_experts_routed_route_amd as m
+    note(f"layer mixed adapters {cfg.name} {fold}")
+    d = make_inputs(cfg)
+    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold)
+    b = layer.plan(cfg.T, "cuda")
+    out = layer.forward(to_dev(d["logits"]), bf16_dev(d["x"]), b, row_adapter=to_dev(d["row_adapter"]))
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(d)
+    assert_close_rows(bf16_host(out), ref["out"], TOL, f"layer {cfg.name} {fold}")
+    # the same layer with every token on the base differs (the adapters are not below the tolerance
+    # everywhere): checked on the oracle side, where it is exact
+    plain = dict(d, row_adapter=np.full_like(d["row_adapter"], -1))
+    diff = np.linalg.norm(oracle.moe_layer(plain)["out"] - ref["out"], axis=1)
+    assert (diff > 0).sum() > cfg.T // 4

@@ -199,7 +199,7 @@ def gather_no_delta_round(y, x, tables, indices, top_k, x_gather=False, row_adap
         om.round_bf16 = real
 
 
-def gate_up_lora_gate_unrounded(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up):
+def gate_up_lora_gate_unrounded(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up, row_adapter=None):
     real = om.round_bf16
     calls = {"n": 0}
 
@@ -208,13 +208,13 @@ def gate_up_lora_gate_unrounded(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs
         return v if calls["n"] == 1 else real(v)  # the first expert's gate values stay unrounded
     om.round_bf16 = rb
     try:
-        return om._orig_gate_up_lora(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up)
+        return om._orig_gate_up_lora(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up, row_adapter)
     finally:
         om.round_bf16 = real
 
 
-def gate_up_lora_tables_swapped(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up):
-    return om._orig_gate_up_lora(x_bits, w_gate, w_up, al, top_k, tabs_up, tabs_gate)
+def gate_up_lora_tables_swapped(x_bits, w_gate, w_up, al, top_k, tabs_gate, tabs_up, row_adapter=None):
+    return om._orig_gate_up_lora(x_bits, w_gate, w_up, al, top_k, tabs_up, tabs_gate, row_adapter)
 
 
 def fold_x_gather_by_row(y, x, tables, al, top_k, row_adapter=None, row_offset=0, row_end=None, bf16_base=True,
@@ -258,6 +258,15 @@ def gptq_dequant_always_first(w, e):
     return om._orig_gptq_dequant(w, 0)
 
 
+def adapter_tables_ignores_id(tables, a):
+    # every non-negative adapter id gets adapter 0's tables
+    return om._orig_adapter_tables(tables, 0 if a >= 0 else a)
+
+
+def token_adapter_ignores_map(row_adapter, t):
+    return 0
+
+
 om._orig_route = om.route
 om._orig_align = om.align
 om._orig_gate_up = om.grouped_gate_up
@@ -268,6 +277,7 @@ om._orig_gate_up_lora = om.grouped_gate_up_lora
 om._orig_e4m3 = om.e4m3_to_f64
 om._orig_fp8_gate_up = om.grouped_gate_up_fp8
 om._orig_expert_matrix = om.expert_matrix
+om._orig_adapter_tables = om.adapter_tables
 om._orig_gptq_dequant = om.gptq_dequant_expert
 
 ROUTE_PINS = [pins.test_route_worked_examples, pins.test_route_special_cases, pins.test_route_brute_force_ids_and_sum]
@@ -280,6 +290,8 @@ FP8_PINS = [pins.test_e4m3_decode_against_torch, pins.test_quantize_rows_fp8_clo
             pins.test_fp8_gemms_match_dequantised_definition]
 INT4_PINS = [pins.test_gptq_unpack_and_dequant, pins.test_layer_int4_matches_dense_brute_force]
 # pins that build the stacked expert slabs by hand and never read them through the oracle
+ADAPTER_PINS = [pins.test_two_adapters_closed_form_grouped_and_gather,
+                pins.test_layer_two_adapters_matches_dense_brute_force]
 SELECTION_PINS = [lambda: pins.test_expert_selection_bf16_hand_built_stacks(5, 2),
                   pins.test_expert_selection_int4_hand_built_stacks]
 
@@ -295,6 +307,8 @@ MUTANTS = [
     ("expert_matrix", expert_matrix_always_first, SELECTION_PINS),
     ("expert_matrix", expert_matrix_next_expert, SELECTION_PINS),
     ("gptq_dequant_expert", gptq_dequant_always_first, SELECTION_PINS),
+    ("adapter_tables", adapter_tables_ignores_id, ADAPTER_PINS),
+    ("token_adapter", token_adapter_ignores_map, ADAPTER_PINS),
     ("grouped_gate_up", gate_up_token_mod, LAYER_PINS),
     ("grouped_gate_up", gate_up_swapped, LAYER_PINS),
     ("combine", combine_ignores_inv, [pins.test_combine_worked_example] + LAYER_PINS),

@@ -454,9 +454,11 @@ def test_lora_gather_fold_identity_closed_forms():
     assert np.array_equal(down, expect(lambda s, r: r))
     gate_up = oracle.lora_gather_fold(zero, xs[:T], tabs, ids, k, x_gather=True)
     assert np.array_equal(gate_up, expect(lambda s, r: s // k))
+    # adapter ids: 0 is the one installed adapter; a negative id is the base; id 3 names no
+    # installed adapter, so its token is not folded either
     adapter = np.array([0, -1, 3, -2, 0], np.int32)
     skipped = oracle.lora_gather_fold(zero, xs, tabs, ids, k, row_adapter=adapter)
-    assert np.array_equal(skipped, expect(lambda s, r: r, skip_tok=(1, 3)))
+    assert np.array_equal(skipped, expect(lambda s, r: r, skip_tok=(1, 2, 3)))
     perm = rng.permutation(n).astype(np.int32)
     perm[[2, 9]] = -1
     mapped = oracle.lora_gather_fold(zero, xs, tabs, ids, k, row_map=perm)
@@ -659,3 +661,104 @@ def test_expert_selection_int4_hand_built_stacks():
     r = oracle.moe_layer(d)
     assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
     assert np.allclose(oracle.moe_tokens(d, range(T)), ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- several adapters in one batch
+# atlas moe_lora_grouped.rs, MoeExpertRoute: the adapter of a mixed batch's token comes from the per-row
+# moe_row_adapter (< 0: base), not from the tables.  Reading: row a of the stacked tables is adapter a.
+
+def _two_adapter_tables(R, E):
+    """A_e = B_e = I for both adapters; adapter 0 adapts even experts with scale 2^-(e+1), adapter 1
+    adapts experts 1, 2 (mod 3 != 0) with scale 2^-(e+8), so a folded value names its adapter and
+    its expert (powers of two keep the bf16 fold exact)."""
+    eye = bf16(np.eye(R))
+    t0 = oracle.pack_expert_tables([(e, eye, eye, 2.0 ** -(e + 1)) for e in range(0, E, 2)])
+    t1 = oracle.pack_expert_tables([(e, eye, eye, 2.0 ** -(e + 8)) for e in range(E) if e % 3])
+    return [t0, t1]
+
+
+def _scale_of(a, e):
+    if a == 0 and e % 2 == 0:
+        return 2.0 ** -(e + 1)
+    if a == 1 and e % 3:
+        return 2.0 ** -(e + 8)
+    return None
+
+
+def test_two_adapters_closed_form_grouped_and_gather():
+    T, k, R, E, bs = 12, 2, 8, 6, 16
+    rng = np.random.default_rng(21)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ra = np.array([0, 1, -1, 1, 0, 7, 1, 0, -3, 1, 1, 0], np.int32)   # 7: no such adapter
+    tabs = _two_adapter_tables(R, E)
+    al = oracle.align(ids, E, bs)
+    P = T * k
+    xs = oracle.round_bf16(rng.standard_normal((len(al["sorted_ids"]), R)))   # bf16 values: exact fold
+    got = oracle.lora_fold(np.zeros(xs.shape), xs, tabs, al, k, row_adapter=ra)
+    want = np.zeros(xs.shape)
+    for r, p in enumerate(al["sorted_ids"]):
+        if p >= P:
+            continue
+        e, a = ids.reshape(-1)[p], ra[p // k]
+        sc = _scale_of(a, e) if a >= 0 else None
+        if sc is not None:
+            want[r] = sc * xs[r]
+    assert np.array_equal(got, want)
+    assert (want != 0).any(axis=1).sum() > 4          # both adapters fold some rows
+    # the slot-major gather fold: the same rule per slot
+    xs2 = oracle.round_bf16(rng.standard_normal((P, R)))
+    got2 = oracle.lora_gather_fold(np.zeros((P, R)), xs2, tabs, ids.reshape(-1), k, row_adapter=ra)
+    want2 = np.zeros((P, R))
+    for s in range(P):
+        a = ra[s // k]
+        sc = _scale_of(a, ids.reshape(-1)[s]) if a >= 0 else None
+        if sc is not None:
+            want2[s] = sc * xs2[s]
+    assert np.array_equal(got2, want2)
+    # without a map every token is adapter 0
+    got3 = oracle.lora_gather_fold(np.zeros((P, R)), xs2, tabs, ids.reshape(-1), k)
+    want3 = np.array([(_scale_of(0, e) or 0.0) * xs2[s] for s, e in enumerate(ids.reshape(-1))])
+    assert np.array_equal(got3, want3)
+
+
+def _dense_brute_force_adapters(d, ids, w):
+    """Every token through every expert, the folds of its own adapter (read straight from the adapter
+    dicts), no sorting."""
+    cfg = d["cfg"]
+    X = oracle.bf16_bits_to_f64(d["x"])
+    rb, f64 = oracle.round_bf16, oracle.bf16_bits_to_f64
+    Wg, Wu, Wd = (f64(d[key]) for key in ("wg", "wu", "wd"))
+    out = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        a = int(d["row_adapter"][t])
+        ad = d["lora_adapters"][a] if a >= 0 else None
+        lids = list(ad["lora_ids"]) if ad is not None else []
+        for j in range(cfg.top_k):
+            e = int(ids[t, j])
+            i = lids.index(e) if e in lids else None
+            proj = []
+            for Wm, pre in ((Wg, "lora_gate"), (Wu, "lora_up")):
+                v = rb(Wm[e] @ X[t])
+                if i is not None and f"{pre}_a" in ad:
+                    v = rb(v + float(ad[f"{pre}_scale"][i]) * rb(f64(ad[f"{pre}_b"][i]) @ rb(f64(ad[f"{pre}_a"][i]) @ X[t])))
+                proj.append(v)
+            h = rb(proj[0] / (1 + np.exp(-proj[0])) * proj[1])
+            y = Wd[e] @ h
+            if i is not None:
+                y = y + float(ad["lora_scale"][i]) * rb(f64(ad["lora_b"][i]) @ rb(f64(ad["lora_a"][i]) @ h))
+            out[t] += float(w[t, j]) * y
+    return out
+
+
+def test_layer_two_adapters_matches_dense_brute_force():
+    cfg = MoeConfig("t", T=36, H=64, I=48, E=6, top_k=2, block_size=16, lora_rank=4, lora_max_rank=8,
+                    lora_gate_up=True, lora_adapters=3, seed=23)
+    d = make_inputs(cfg)
+    assert set(np.unique(d["row_adapter"])) == {-1, 0, 1, 2}
+    r = oracle.moe_layer(d)
+    ref = _dense_brute_force_adapters(d, r["ids"], r["w"])
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+    assert np.allclose(oracle.moe_tokens(d, range(cfg.T)), ref, rtol=1e-12, atol=1e-14)
+    # each adapter matters: relabelling the tokens changes the result
+    d2 = dict(d, row_adapter=np.where(d["row_adapter"] == 1, 2, np.where(d["row_adapter"] == 2, 1, d["row_adapter"])))
+    assert not np.allclose(oracle.moe_layer(d2)["out"], ref, rtol=1e-6, atol=1e-9)
