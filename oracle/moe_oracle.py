@@ -427,24 +427,27 @@ def fp8_expert_matrix(w: Dict[str, np.ndarray], e: int) -> np.ndarray:
 
 
 def grouped_gate_up_fp8(xq: np.ndarray, sx: np.ndarray, w_gate, w_up, al: Dict[str, np.ndarray],
-                        top_k: int) -> np.ndarray:
+                        top_k: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
     """FP8 gate/up with SiLU * up over the sorted rows: for real row r (token t, expert e),
     g = s_x[t] * sum_k x(t, k) Wg(e, n, k) with x = e4m3 values of the quantised token row and W
-    the dequantised weights; likewise u; h = silu(g) * u.  Sentinel rows are NaN."""
+    the dequantised weights; likewise u; h = silu(g) * u.  Sentinel rows are NaN.  ``rows``
+    restricts the evaluation to a subset."""
     sid = al["sorted_ids"]
     h = np.full((len(sid), w_gate["codes"].shape[1]), np.nan)
     X = e4m3_to_f64(xq) * np.asarray(sx, np.float64)[:, None]
-    for e, rr in _rows_by_expert(al).items():
+    for e, rr in _rows_by_expert(al, rows).items():
         xt = X[sid[rr] // top_k]
         h[rr] = silu(xt @ fp8_expert_matrix(w_gate, e).T) * (xt @ fp8_expert_matrix(w_up, e).T)
     return h
 
 
-def grouped_down_fp8(hq: np.ndarray, sh: np.ndarray, w_down, al: Dict[str, np.ndarray]) -> np.ndarray:
-    """FP8 down over the sorted rows: y[r] = s_h[r] * (values of hq[r]) Wd(e)^T, dequantised."""
+def grouped_down_fp8(hq: np.ndarray, sh: np.ndarray, w_down, al: Dict[str, np.ndarray],
+                     rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """FP8 down over the sorted rows: y[r] = s_h[r] * (values of hq[r]) Wd(e)^T, dequantised.
+    ``rows`` restricts the evaluation to a subset."""
     y = np.full((hq.shape[0], w_down["codes"].shape[1]), np.nan)
     H = e4m3_to_f64(hq) * np.asarray(sh, np.float64)[:, None]
-    for e, rr in _rows_by_expert(al).items():
+    for e, rr in _rows_by_expert(al, rows).items():
         y[rr] = H[rr] @ fp8_expert_matrix(w_down, e).T
     return y
 

@@ -151,8 +151,9 @@ def test_mixed_adapters_gate_up_fused(dev, cfg):
     h = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, tg, tu, ra)
     h0 = oracle.grouped_gate_up_lora(d["x"], wg, wu, al, cfg.top_k, None, None)
     fused = oracle.bf16_bits_to_f64(outs["fused"][real])
-    assert_close_rows(fused, h[real], TOL, f"fused vs oracle {cfg.name}")
-    assert_close_rows(oracle.bf16_bits_to_f64(outs["unfused"][real]), h[real], TOL, f"unfused vs oracle {cfg.name}")
+    assert_close_rows(fused, h[real], TOL, f"fused vs oracle {cfg.name}", ulps=4)
+    assert_close_rows(oracle.bf16_bits_to_f64(outs["unfused"][real]), h[real], TOL, f"unfused vs oracle {cfg.name}",
+                      ulps=4)
     # the folds show: rows whose adapter adapts their expert differ from the unfolded result
     moved = np.linalg.norm(h[real] - h0[real], axis=1) > 0
     assert set(np.unique(_adapter_of_rows(al, ra, cfg.top_k, real[moved]))) == {0, 1, 2}
