@@ -1,0 +1,353 @@
+"""CPU models of the addressing of every kernel that computes addresses from device-resident ids
+(besides the bf16 GEMM, modelled in test_gemm_addressing): the int4 GEMM, the fp8 GEMM (tile heights
+and split tail), the gate/up LoRA epilogue of the bf16 GEMM, the grouped fold's shrink and expand,
+and the gather fold.  Each model restates the kernel's integer arithmetic and yields every
+(buffer, index, extent) a launch can address; the tests show all of them in bounds on the routings of
+the workloads and on tight routings whose padded total reaches the sorted capacity.  CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+from moe_synth import CONFIGS, make_router_logits
+
+
+def _spans(al, E, max_pad):
+    off = al["offsets"]
+    lo = [min(max(int(off[e]), 0), max_pad) for e in range(E)]
+    hi = [min(max(int(off[e + 1]), lo[e]), max_pad) for e in range(E)]
+    return lo, hi
+
+
+# ----------------------------------------------------------------------------- int4 GEMM
+def int4_touched(al, P, top_k, E, N, K, G, bs, gate_up, a_tok=False):
+    """gemm_int4_kernel: grid (max_pad/16, N/64); workgroup = 16 sorted rows x 64 columns; the
+    tile's expert from expert_ids[r0 / bs]; wave (proj, part) streams its K groups; lane
+    (m = lane % 16, kq = lane / 16) loads qweight rows g*G/8 + kq + 4*st at columns ncol..ncol+3."""
+    max_pad = len(al["sorted_ids"])
+    sid, eid = al["sorted_ids"], al["expert_ids"]
+    T = P // top_k
+    STEPS = G // 32
+    nsplit = 2 if gate_up else 4
+    ngroups = K // G
+    per = -(-ngroups // nsplit)
+    for bx in range(max_pad // 16):
+        r0 = bx * 16
+        yield "expert_ids", r0 // bs, len(eid)
+        e = int(eid[r0 // bs])
+        for m in range(16):
+            yield "sorted_ids", min(r0 + m, max_pad - 1), max_pad
+        if e < 0 or e >= E:
+            continue
+        srcs = []
+        for m in range(16):
+            p = int(sid[min(r0 + m, max_pad - 1)]) if r0 + m < max_pad else -1
+            srcs.append((p // top_k if (gate_up or a_tok) else r0 + m) if 0 <= p < P else -1)
+        for by in range(N // 64):
+            n0 = by * 64
+            for wave in range(4):
+                part = wave & 1 if gate_up else wave
+                g_begin, g_end = part * per, min(ngroups, part * per + per)
+                g0 = min(g_begin, ngroups - 1)
+                groups = range(g0, g0 + max(1, g_end - g_begin))   # a wave without groups loads g0 once
+                for lane in range(0, 64, 15):                         # lanes 0, 15, 30, 45, 60 cover m, kq ends
+                    m, kq = lane & 15, lane >> 4
+                    ncol = n0 + 4 * m
+                    for g in groups:
+                        for st in range(STEPS):
+                            krow = g * (G // 8) + kq + 4 * st
+                            yield "qweight", (e * (K // 8) + krow) * N + ncol + 3, E * (K // 8) * N
+                        yield "scales", (e * (K // G) + g) * N + ncol + 3, E * (K // G) * N
+                        yield "qzeros", (e * (K // G) + g) * (N // 8) + ncol // 8, E * (K // G) * (N // 8)
+                        if any(s >= 0 for s in srcs):
+                            src = srcs[m]
+                            arow = src if src >= 0 else (0 if (gate_up or a_tok) else r0)
+                            for st in range(STEPS):
+                                yield "A", arow * K + g * G + st * 32 + kq * 8 + 7, (T if (gate_up or a_tok) else max_pad) * K
+            for row in range(16):
+                if srcs[row] >= 0:
+                    yield "C", (r0 + row) * N + n0 + 63, max_pad * N
+
+
+# ----------------------------------------------------------------------------- fp8 GEMM
+def fp8_touched(al, P, top_k, E, N, K, BM, NW, slots, gate_up, split_max_rounds=4, min_stages=8):
+    """gemm_fp8_kernel: row tiles of BM rows per expert span; logical tile L = n_t * m_real + m_t;
+    XCD x takes [x*Tw/8, (x+1)*Tw/8) of the first Tw tiles; with a workspace and fewer than
+    split_max_rounds rounds, the rest = T mod slots tiles are cut along K into pieces that run on the
+    workgroups past each XCD's share.  Yields A rows, a_scale entries, weight rows, channel scales,
+    C rows, partial slots and tile counters."""
+    max_pad = len(al["sorted_ids"])
+    sid = al["sorted_ids"]
+    T_tok = P // top_k
+    lo, hi = _spans(al, E, max_pad)
+    nt = [-(-(hi[e] - lo[e]) // BM) for e in range(E)]
+    tb = np.concatenate([[0], np.cumsum(nt)]).astype(int)
+    m_real = int(tb[-1])
+    BP = BM
+    ncol = BP // 2 if gate_up else BP
+    n_tiles = -(-N // ncol)
+    nk = -(-K // 128)
+    m_bound = -(-max_pad // BM) + E
+    grid = ((m_bound * n_tiles + 7) // 8 + 1 + (slots + 7) // 8) * 8
+    T = m_real * n_tiles
+    Tw, split = T, 1
+    split_on = slots > 0 and m_bound * n_tiles < split_max_rounds * slots
+    if split_on and T < split_max_rounds * slots:
+        rest = T % slots
+        s_max = min(slots // rest, nk // min_stages) if rest > 0 else 1
+        if s_max >= 2:
+            Tw, split = T - rest, s_max
+    covered = np.zeros((T, nk), np.int32)
+    for bid in range(grid):
+        xcd, slot = bid & 7, bid >> 3
+        lo_x = Tw * xcd // 8
+        share = Tw * (xcd + 1) // 8 - lo_x
+        if slot < share:
+            L, kb, ke = lo_x + slot, 0, nk
+        else:
+            piece = (slot - share) * 8 + xcd
+            if piece >= (T - Tw) * split:
+                continue
+            tail_u = piece // split
+            j = piece - tail_u * split
+            L, kb, ke = Tw + tail_u, j * nk // split, (j + 1) * nk // split
+            yield "partial", piece, slots
+            yield "counter", tail_u, 1024
+            yield "partial", tail_u * split + split - 1, slots
+        assert 0 <= L < T
+        covered[L, kb:ke] += 1
+        n_t, m_t = L // m_real, L % m_real
+        e = max(i for i in range(E) if tb[i] <= m_t)
+        r0 = lo[e] + (m_t - tb[e]) * BM
+        r_end = min(r0 + BM, hi[e])
+        n0 = n_t * ncol
+        rows = []
+        for t in range(BM):
+            r = r0 + t
+            src = -1
+            if r < r_end:
+                yield "sorted_ids", r, max_pad
+                p = int(sid[r])
+                if 0 <= p < P:
+                    src = p // top_k if gate_up else r
+                    yield "a_scale", src, T_tok if gate_up else max_pad
+            rows.append(src)
+        for t in range(BM):
+            srow = rows[t] if rows[t] >= 0 else (0 if gate_up else r0)
+            yield "A", srow * K + K - 1, (T_tok if gate_up else max_pad) * K
+        for prow in range(BP):
+            n = min((n0 + (prow & (BP // 2 - 1))) if gate_up else (n0 + prow), N - 1)
+            yield "W", (e * N + n) * K + K - 1, E * N * K
+        for c in range(n0, n0 + ncol):
+            yield "w_scale", e * N + min(c, N - 1), E * N
+        for t in range(BM):
+            if rows[t] >= 0:
+                yield "C", (r0 + t) * N + min(n0 + ncol, N) - 1, max_pad * N
+    assert (covered == 1).all(), "every (tile, K stage) once"
+
+
+# ----------------------------------------------------------------------------- gate/up LoRA epilogue
+def lora_epilogue_touched(al, P, top_k, E, N, BM, rank, n_tab, n_ad, ra):
+    """The LoRA epilogue of gemm_bf16_kernel (gate/up, 2 x 4 wave grid of 64 x 128 per wave in a
+    256-row tile, 2 x 2 of 64 x 64 in a 128-row tile): xa rows min(r0 + wm*WM + i*32 + fr, max_pad - 1)
+    of [2, max_pad, rank], B_e rows min(n0 + wn*64 + jj*32 + fr, N - 1) of [N, rank], table entries
+    a * n_tab + e for the adapters of the tile's rows, and row_adapter at each row's token."""
+    max_pad = len(al["sorted_ids"])
+    sid = al["sorted_ids"]
+    lo, hi = _spans(al, E, max_pad)
+    NW = 8 if BM == 256 else 4
+    WM = BM // (NW // 2)
+    for e in range(E):
+        for t in range(-(-(hi[e] - lo[e]) // BM)):
+            r0 = lo[e] + t * BM
+            r_end = min(r0 + BM, hi[e])
+            ads = set()
+            for i in range(BM):
+                r = r0 + i
+                if r < r_end and 0 <= sid[r] < P:
+                    tok = int(sid[r]) // top_k
+                    yield "row_adapter", tok, P // top_k
+                    a = int(ra[tok]) if ra is not None else 0
+                    if 0 <= a < n_ad:
+                        ads.add(a)
+            for n_t in range(-(-N // 128)):
+                n0 = n_t * 128
+                for wm in range(NW // 2):
+                    for i in range(2):
+                        for fr in (0, 31):
+                            yield "xa", min(r0 + wm * WM + i * 32 + fr, max_pad - 1), max_pad
+                for wn in range(2):
+                    for jj in range(2):
+                        for fr in (0, 31):
+                            yield "B_e", min(n0 + wn * 64 + jj * 32 + fr, N - 1) * rank + rank - 1, N * rank
+                if e < n_tab:
+                    for a in ads:
+                        yield "table", a * n_tab + e, n_ad * n_tab
+
+
+# ----------------------------------------------------------------------------- grouped fold
+def grouped_fold_touched(al, P, top_k, E, k_in, n_out, max_rank, n_tab, n_ad, ra, row_offset, row_end, cap,
+                         x_gather, x_rows):
+    """lora_shrink_kernel (one workgroup per 16-row sub-tile from base16 = row_offset rounded down to
+    16) and lora_expand_fold_kernel (64-row tiles x 256 columns, a 16-row sub-tile per wave): only
+    rows inside the window and the expert span are read through sorted_ids; active rows read x,
+    write and read xa at r - row_offset, read and write base; A_e rows < max_rank, B_e rows < n_out."""
+    max_pad = len(al["sorted_ids"])
+    sid, off = al["sorted_ids"], al["offsets"]
+    base16 = row_offset // 16 * 16
+    for sub0 in range(base16, row_end, 16):
+        yield "offsets", E, E + 1
+        if off[0] > sub0 or off[E] <= sub0:
+            continue
+        e = max(i for i in range(E) if off[i] <= sub0)
+        if e >= n_tab:
+            continue
+        span_end = int(off[e + 1])
+        for m in range(16):
+            r = sub0 + m
+            if r < row_offset or r >= row_end or r >= span_end:
+                continue
+            yield "sorted_ids", r, max_pad
+            p = int(sid[r])
+            if not 0 <= p < P:
+                continue
+            yield "row_adapter", p // top_k, P // top_k
+            a = int(ra[p // top_k]) if ra is not None else 0
+            if not 0 <= a < n_ad:
+                continue
+            yield "table", a * n_tab + e, n_ad * n_tab
+            xrow = p // top_k if x_gather else r
+            yield "x", xrow * k_in + k_in - 1, x_rows * k_in
+            yield "A_e", (max_rank - 1) * k_in + k_in - 1, max_rank * k_in
+            yield "xa", (r - row_offset) * max_rank + max_rank - 1, cap * max_rank
+            yield "base", r * n_out + n_out - 1, max_pad * n_out
+            yield "B_e", (n_out - 1) * max_rank + max_rank - 1, n_out * max_rank
+
+
+# ----------------------------------------------------------------------------- gather fold
+def gather_touched(indices, n_slots, top_k, x_gather, row_map, ra, n_tab, n_ad, x_rows, base_rows, k_in, n_out,
+                   max_rank):
+    """gather_shrink_kernel / gather_expand_kernel: one workgroup per (slot, chunk); a slot whose id,
+    adapter, map entry or x row falls outside its table or buffer is skipped before any other access."""
+    for s in range(n_slots):
+        yield "indices", s, n_slots
+        e = int(indices[s])
+        if e < 0 or e >= n_tab:
+            continue
+        yield "row_adapter" if ra is not None else "none", s // top_k, n_slots // top_k
+        a = int(ra[s // top_k]) if ra is not None else 0
+        if a < 0 or a >= n_ad:
+            continue
+        yield "table", a * n_tab + e, n_ad * n_tab
+        row = int(row_map[s]) if row_map is not None else s
+        if row < 0 or row >= base_rows:
+            continue
+        xrow = s // top_k if x_gather else row
+        if xrow >= x_rows:
+            continue
+        yield "x", xrow * k_in + k_in - 1, x_rows * k_in
+        yield "xa", s * max_rank + max_rank - 1, n_slots * max_rank
+        for jb in range(max_rank // 16):
+            yield "A_e", (jb * 16 + 15) * k_in + k_in - 1, max_rank * k_in
+        for by in range(-(-n_out // 256)):
+            for wave in range(4):
+                n0 = by * 256 + wave * 64
+                if n0 >= n_out:
+                    continue
+                yield "base", row * n_out + min(n0 + 63, n_out - 1), base_rows * n_out
+                yield "B_e", min(n0 + 63, n_out - 1) * max_rank + max_rank - 1, n_out * max_rank
+
+
+# ----------------------------------------------------------------------------- routings
+def _routings():
+    out = []
+    for name in ("tiny", "decode_int4", "lora_prefill"):
+        cfg = CONFIGS[name]
+        ids, _ = oracle.route(make_router_logits(cfg), cfg.top_k)
+        out.append((name, cfg.top_k, cfg.E, cfg.block_size, ids))
+    # padded total exactly at the capacity: every expert holds a multiple of bs plus one pair
+    for E, bs, per in ((2, 64, 8 * 64 + 1), (3, 16, 5 * 16 + 1), (8, 16, 7 * 16 + 1), (5, 128, 3 * 128 + 1)):
+        out.append((f"tight_E{E}_bs{bs}", 1, E, bs, np.repeat(np.arange(E), per).reshape(-1, 1)))
+    # ids outside [0, E) are dropped by the alignment
+    rng = np.random.default_rng(3)
+    ids = rng.integers(-2, 10, (50, 2)).astype(np.int32)
+    out.append(("dropped_ids", 2, 8, 16, ids))
+    return out
+
+
+def _check(gen, what):
+    n = 0
+    for kind, idx, lim in gen:
+        assert 0 <= idx < lim, f"{what}: {kind} index {idx} outside [0, {lim})"
+        n += 1
+    return n
+
+
+@pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
+def test_int4_gemm_addresses_in_bounds(case):
+    name, top_k, E, bs, ids = case
+    al = oracle.align(ids, E, bs)
+    P = ids.size
+    for gate_up, N, K in ((True, 128, 256), (False, 64, 128)):
+        for G in (32, 64, 128):
+            if K % G == 0:
+                assert _check(int4_touched(al, P, top_k, E, N, K, G, bs, gate_up), f"{name} int4 G={G}") > 0
+    _check(int4_touched(al, P, top_k, E, 64, 128, 64, bs, False, a_tok=True), f"{name} int4 gathered")
+
+
+@pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
+@pytest.mark.parametrize("BM,NW", [(256, 8), (128, 4)])
+def test_fp8_gemm_addresses_in_bounds(case, BM, NW):
+    name, top_k, E, bs, ids = case
+    al = oracle.align(ids, E, bs)
+    P = ids.size
+    for gate_up, N, K in ((True, 264, 2048), (False, 136, 1024)):
+        for slots in (0, 256, 512):   # no workspace; one or two workgroups per compute unit
+            assert _check(fp8_touched(al, P, top_k, E, N, K, BM, NW, slots, gate_up),
+                          f"{name} fp8 BM={BM} slots={slots}") > 0
+
+
+@pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
+def test_gate_up_lora_epilogue_addresses_in_bounds(case):
+    name, top_k, E, bs, ids = case
+    al = oracle.align(ids, E, bs)
+    P = ids.size
+    T = P // top_k
+    ra = np.random.default_rng(1).integers(-1, 4, T).astype(np.int32)   # ids past n_ad included
+    for BM in (128, 256):
+        for n_tab, n_ad, rmap in ((E, 1, None), (max(1, E - 1), 3, ra)):
+            _check(lora_epilogue_touched(al, P, top_k, E, 200, BM, 64, n_tab, n_ad, rmap), f"{name} epilogue")
+
+
+@pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
+def test_grouped_fold_addresses_in_bounds(case):
+    name, top_k, E, bs, ids = case
+    al = oracle.align(ids, E, bs)
+    P = ids.size
+    T = P // top_k
+    max_pad = len(al["sorted_ids"])
+    ra = np.random.default_rng(2).integers(-1, 4, T).astype(np.int32)
+    for x_gather in (False, True):
+        x_rows = T if x_gather else max_pad
+        for cap in (max_pad, 100, 17):
+            for s, e in oracle.lora_windows(max_pad, cap):
+                for n_tab, n_ad, rmap in ((E, 1, None), (max(1, E // 2), 3, ra)):
+                    _check(grouped_fold_touched(al, P, top_k, E, 96, 136, 64, n_tab, n_ad, rmap, s, e, cap, x_gather,
+                                                x_rows), f"{name} fold window {s}-{e}")
+
+
+@pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
+def test_gather_fold_addresses_in_bounds(case):
+    name, top_k, E, bs, ids = case
+    al = oracle.align(ids, E, bs)
+    P = ids.size
+    T = P // top_k
+    flat = ids.reshape(-1)
+    ra = np.random.default_rng(4).integers(-1, 4, T).astype(np.int32)
+    max_pad = len(al["sorted_ids"])
+    for x_gather in (False, True):
+        # slot-major buffers, and the sorted buffers through the inverse map
+        for row_map, base_rows in ((None, P), (al["inv"], max_pad)):
+            x_rows = T if x_gather else base_rows
+            for n_tab, n_ad, rmap in ((E, 1, None), (E + 3, 2, ra)):
+                _check(gather_touched(flat, P, top_k, x_gather, row_map, rmap, n_tab, n_ad, x_rows, base_rows, 96,
+                                      520, 64), f"{name} gather")
