@@ -81,45 +81,6 @@ constexpr int BP = 256;
 #endif
 constexpr int kMaxE = 256;
 
-__device__ __attribute__((aligned(16))) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// 16 bytes per lane from global memory straight into LDS at m0 + lane*16 (one 1 KB row block
-// per wave).  Emitted as inline asm so that the compiler does not treat every later LDS read
-// as dependent on it (it would drain all loads in flight before each read); completion is
-// tracked with explicit vmcnt waits instead.  m0 is written inside the statement itself.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory");
-}
-
-// The same with the source as a scalar base plus a 32-bit per-lane byte offset (saddr form).
-__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
-                 : "memory");
-}
-
-// A wave-uniform pointer held in scalar registers (a select between two uniform pointers may
-// otherwise be formed in vector registers, which an "s" operand cannot take).
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-    const uint64_t v = reinterpret_cast<uintptr_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-    return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(p))));
-}
-
 template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
 struct Cfg {
     static constexpr int NT = 64 * NW;                  // threads

@@ -58,15 +58,6 @@ struct F8Cfg {
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
-__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
-
-// 16 bytes per lane from global memory into LDS at m0 + lane*16 (see gemm_bf16.hip: inline asm
-// keeps the compiler from draining the loads before every LDS read; completion is tracked with
-// explicit vmcnt waits)
-__device__ __forceinline__ void dma16_f8(const void* g, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory");
-}
-
 __device__ __forceinline__ int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 // ------------------------------------------------------------------ per-row quantisation
@@ -266,14 +257,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_fp8_kernel(
 #pragma unroll
             for (int q = 0; q < F::B_INST; ++q) {
                 const void* g = b_src[j][q] + k0;
-                if (!full && k0 + b_kc[j][q] * 16 >= K) g = kZeroChunk;
-                dma16_f8(g, sb + BM * F8_BK + (bw * F::B_INST + q) * 1024);
+                if (!full && k0 + b_kc[j][q] * 16 >= K) g = kZero16;
+                dma16(g, sb + BM * F8_BK + (bw * F::B_INST + q) * 1024);
             }
 #pragma unroll
             for (int q = 0; q < F::A_INST; ++q) {
                 const void* g = a_src[j][q] + k0;
-                if (!full && k0 + a_kc[j][q] * 16 >= K) g = kZeroChunk;
-                dma16_f8(g, sb + (bw * F::A_INST + q) * 1024);
+                if (!full && k0 + a_kc[j][q] * 16 >= K) g = kZero16;
+                dma16(g, sb + (bw * F::A_INST + q) * 1024);
             }
         }
     };

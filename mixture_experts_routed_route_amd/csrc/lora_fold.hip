@@ -13,12 +13,13 @@
 // Two launches like the page: the shrink writes the bf16 xa scratch at the local row
 // r - row_offset, the expand reads it.  The expert of a row is read on the device from
 // expert_offsets (the row's span), so the grid is fixed by host scalars: a window is cut
-// into 64-row tiles aligned to 16-row boundaries (one 16-row sub-tile per wave; block
-// sizes are multiples of 16, so a sub-tile never straddles two experts' spans), and
-// sub-tiles of unadapted experts, sentinel rows and rows outside the window do nothing.
-// Both stages use 16x16x32 bf16 MFMA with fp32 accumulation.  The shrink gives each 16-row
-// sub-tile a workgroup whose 4 waves split k_in.  The expand stages its bf16
-// delta tile in LDS and then updates the base rows with 16-byte coalesced accesses.
+// into 16-row sub-tiles (block sizes are multiples of 16, so a sub-tile never straddles two
+// experts' spans), and sub-tiles of unadapted experts, sentinel rows and rows outside the
+// window do nothing.  Both stages use 16x16x32 bf16 MFMA with fp32 accumulation.  The shrink
+// gives each 16-row sub-tile a workgroup whose 4 waves split k_in.  The expand takes 64-row
+// tiles (four sub-tiles), each wave a column slab of all four, so that it reads B_e once per
+// tile; it stages its bf16 delta tile in LDS and then updates the base rows with 16-byte
+// coalesced accesses.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -26,21 +27,12 @@ namespace moe {
 namespace {
 
 constexpr int NT = 256;
-#ifndef MOE_LORA_EXP_COLS
-#define MOE_LORA_EXP_COLS 64
+constexpr int EXP_COLS = 64;  // expand: output columns per wave and slab
+#ifndef MOE_LORA_EXP_SLABS
+#define MOE_LORA_EXP_SLABS 4
 #endif
-// expand output columns per workgroup (32 to 256; 64 measured best: 4 accumulators per wave keep
-// 4 waves per SIMD and the base-row loads in flight)
-constexpr int EXP_COLS = MOE_LORA_EXP_COLS;
-static_assert(EXP_COLS >= 32 && EXP_COLS <= 256 && (EXP_COLS & (EXP_COLS - 1)) == 0, "expand tile width");
-constexpr int FOLD_LPR = EXP_COLS / 8;       // fold: lanes per row (8 columns each)
-constexpr int FOLD_RPS = 64 / FOLD_LPR;      // fold: rows per step
-constexpr int FOLD_STEPS = 16 / FOLD_RPS;    // fold: steps over a 16-row sub-tile
+constexpr int EXP_SLABS = MOE_LORA_EXP_SLABS;  // expand: slabs of 4 * EXP_COLS columns per workgroup
 constexpr int MAX_RANK_BLOCKS = 8;  // max_rank <= 128
-#ifndef MOE_LORA_EXP_BLOCKS
-#define MOE_LORA_EXP_BLOCKS 4
-#endif
-constexpr int EXP_BLOCKS = MOE_LORA_EXP_BLOCKS;  // column blocks of EXP_COLS per expand wave
 
 // expert_offsets [E+1] (E <= 256) into LDS, so that each sub-tile's binary search over the
 // expert spans costs LDS reads instead of a chain of dependent global loads
@@ -96,13 +88,48 @@ __device__ __forceinline__ int wave_next_adapter(int mine, int after) {
         const int w = __shfl_xor(v, o);
         v = w < v ? w : v;
     }
-    return v;
+    return __builtin_amdgcn_readfirstlane(v);  // the same in every lane: let the compiler know
 }
 
-// Shrink: one workgroup per 16-row sub-tile; its 4 waves take a quarter of k_in each and add
-// their partial sums in LDS, so one row's k loop is split over 4 waves.  NB = rank blocks of 16
-// (max_rank / 16, up to 8); KU k-steps per round: every load of a round is issued before its
-// MFMAs, so a wave waits for one memory round trip per KU steps.
+constexpr int kNoKey = 0x7fffffff;  // "no (expert, adapter) pair": above every real key
+constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range used here
+
+// Smallest key above `after` held by any lane of the wave (kNoKey if none), the same in every lane.
+__device__ __forceinline__ int wave_next_key(int mine, int after) {
+    int v = mine > after ? mine : kNoKey;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const int w = __shfl_xor(v, o);
+        v = w < v ? w : v;
+    }
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Shrink LDS: each wave's ring of R k-steps (x of the 64 rows, then A_e's 16 NB rank rows, 32 k each,
+// in 1 KB blocks of 16 rows: block byte (c * 16 + r) * 16 holds chunk c (k 8c..8c+7) of row r, so
+// that lane L of a fragment read takes bytes 16 L..16 L + 15); after the K loop the same memory holds
+// one sub-tile's partial sums of the four waves.
+template <int NB>
+struct ShrinkLds {
+    static constexpr int R = NB <= 4 ? 4 : 3;  // k-steps in flight per wave
+    static constexpr int X_BYTES = 4 * 1024;
+    static constexpr int STAGE = X_BYTES + NB * 1024;
+    static constexpr int WAVE = R * STAGE;
+    static constexpr int RING = 4 * WAVE;
+    static constexpr int RED = 4 * NB * 4 * 64 * 4;
+    static constexpr int BYTES = RING > RED ? RING : RED;
+    static constexpr int LOADS = 4 + NB;  // load instructions per k-step and wave
+};
+
+// Shrink: one workgroup per 64-row tile (four 16-row sub-tiles); its 4 waves take a quarter of k_in
+// each and add their partial sums in LDS.  A tile's rows are taken one (expert, adapter) pair at a
+// time (a uniform loop over the pairs present, usually one); in the pass of a pair, a wave streams
+// its k range of x (the tile's 64 rows) and of the pair's A_e through its LDS ring with direct
+// global->LDS loads, R k-steps ahead, and each k-step's A_e fragments serve all four sub-tiles.
+// The loads are not tracked by the compiler (see dma16): each k-step waits with an explicit vmcnt
+// for its own loads only.  Chunks past the wave's k range load zeros; x rows of other passes (or not
+// folded) give results in their own output rows only, which this pass does not store.
+// NB = rank blocks of 16 (max_rank / 16, up to 8).
 template <int NB>
 __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restrict__ x, const uint64_t* a_tab,
                                                          const uint64_t* b_tab, int n_tab, int n_ad, int k_in,
@@ -112,83 +139,136 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ row_adapter,
                                                          uint16_t* __restrict__ xa, int64_t row_offset,
                                                          int64_t row_end, int64_t base16, int x_gather) {
-    constexpr int KU = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
-    __shared__ float red[4][NB][4][64];  // [wave][rank block][v][lane]
+    using L = ShrinkLds<NB>;
+    constexpr int R = L::R;
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     __shared__ int s_off[257];
+    __shared__ int s_key[64];       // (expert << 16) | adapter of each row of the tile, kNoKey: not folded
+    __shared__ int64_t s_xrow[64];  // its x row
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.x) * 16;
-    if (sub0 >= row_end) return;  // uniform over the workgroup
+    const int64_t tile0 = base16 + static_cast<int64_t>(blockIdx.x) * 64;
+    if (tile0 >= row_end) return;  // uniform over the workgroup
     stage_offsets(off, E, s_off);
-    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
-    if (st.e < 0) return;  // uniform over the workgroup
+    if (threadIdx.x < 64) {
+        const int64_t r = tile0 + threadIdx.x;
+        const int64_t sub0 = tile0 + (threadIdx.x & ~15);
+        SubTile st{-1, 0};
+        if (sub0 < row_end) st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
+        const int a = st.e >= 0 ? row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k,
+                                                 row_adapter, n_ad, n_tab, st.e, a_tab, b_tab)
+                                : kNoAdapter;
+        s_key[threadIdx.x] = a != kNoAdapter ? (st.e << 16) | a : kNoKey;
+        // x row: the sorted row (down), or the row's token in the token-major input (gate/up form)
+        s_xrow[threadIdx.x] = a != kNoAdapter ? (x_gather ? static_cast<int64_t>(sorted_ids[r] / top_k) : r) : 0;
+    }
+    __syncthreads();
 
     const int m = lane & 15, kq = lane >> 4;
-    const int64_t r = sub0 + m;
-    const int ad = row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter, n_ad,
-                                  n_tab, st.e, a_tab, b_tab);
-    const bool act = ad != kNoAdapter;
-    // x row: the sorted row (down), or the row's token in the token-major input (gate/up form)
-    const int64_t xrow = act && x_gather ? static_cast<int64_t>(sorted_ids[r] / top_k) : r;
-    const uint16_t* xr = act ? x + xrow * k_in + kq * 8 : nullptr;
+    const int key_l = s_key[lane];  // lane l holds row l's key, for the pass loop
+    // this lane's load sources: chunk kq of row m of x block q (sub-tile q), of rank row 16 j + m
+    const uint16_t* xsrc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xsrc[q] = x + s_xrow[q * 16 + m] * k_in + kq * 8;
     const int kpart = ((k_in + 127) / 128) * 32;  // this wave's k range, a multiple of 32
     const int kb = wave * kpart, ke = min(k_in, kb + kpart);
-    // the rows' adapters, one pass each (every wave holds the same 16 rows: the passes are uniform over
-    // the workgroup); a row of another adapter is computed with this pass's A and not stored
-    for (int cur = wave_next_adapter(ad, -1); cur != kNoAdapter; cur = wave_next_adapter(ad, cur)) {
-    const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[static_cast<int64_t>(cur) * n_tab + st.e]);
+    const int nsteps = ke > kb ? (ke - kb + 31) / 32 : 0;  // uniform over the wave
+    const uint32_t ring = lds_u32(smem) + wave * L::WAVE;
+    const char* ring_p = smem + wave * L::WAVE;
 
-    f32x4 acc[NB];
+    for (int cur = wave_next_key(key_l, -1); cur != kNoKey; cur = wave_next_key(key_l, cur)) {
+        const int e = cur >> 16, a = cur & 0xffff;
+        const uint16_t* Ae = reinterpret_cast<const uint16_t*>(a_tab[static_cast<int64_t>(a) * n_tab + e]) +
+                             static_cast<int64_t>(m) * k_in + kq * 8;
+        // k-step t (k = kb + 32 t) into ring slot t % R
+        auto issue = [&](int t) {
+            const int k = kb + 32 * t;
+            const bool in = k + kq * 8 < ke;
+            const uint32_t slot = __builtin_amdgcn_readfirstlane(ring + (t % R) * L::STAGE);  // m0 takes a scalar
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kb; k0 < ke; k0 += 32 * KU) {
-        u32x4 av[KU], bv[KU][NB];
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int kk = k0 + u * 32;
-            const bool kin = kk + kq * 8 < ke;
-            av[u] = (xr && kin) ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                bv[u][j] = kin ? *reinterpret_cast<const u32x4*>(Ae + static_cast<int64_t>(j * 16 + m) * k_in + kk + kq * 8)
-                               : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const bf16x8 afr = __builtin_bit_cast(bf16x8, av[u]);
+            for (int q = 0; q < 4; ++q) dma16(in ? static_cast<const void*>(xsrc[q] + k) : kZero16, slot + q * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bv[u][j]), acc[j], 0, 0, 0);
+                dma16(in ? static_cast<const void*>(Ae + static_cast<int64_t>(j * 16) * k_in + k) : kZero16,
+                      slot + L::X_BYTES + j * 1024);
+        };
+        f32x4 acc[4][NB];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[s][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < R && t < nsteps; ++t) issue(t);
+        for (int t = 0; t < nsteps; ++t) {
+            // k-step t has landed once at most `ahead` later k-steps' loads are still in flight
+            const int ahead = min(R - 1, nsteps - 1 - t);
+            if (ahead >= 3) wait_vmcnt<3 * L::LOADS>();
+            else if (ahead == 2) wait_vmcnt<2 * L::LOADS>();
+            else if (ahead == 1) wait_vmcnt<L::LOADS>();
+            else wait_vmcnt<0>();
+            asm volatile("" ::: "memory");  // the LDS reads stay below the wait
+            const char* st = ring_p + (t % R) * L::STAGE + lane * 16;
+            u32x4 xv[4], av[NB];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xv[q] = *reinterpret_cast<const u32x4*>(st + q * 1024);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) av[j] = *reinterpret_cast<const u32x4*>(st + L::X_BYTES + j * 1024);
+            // the slot's reads are done before it is refilled (the clobber keeps them above this point)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (t + R < nsteps) issue(t + R);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[s][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[s]),
+                                                                        __builtin_bit_cast(bf16x8, av[j]),
+                                                                        acc[s][j], 0, 0, 0);
         }
-    }
+        // the four waves' partial sums, one sub-tile at a time (in the ring's memory, once every wave
+        // is past its K loop); wave w stores rank blocks w, w + 4
+        float (*red)[NB][4][64] = reinterpret_cast<float (*)[NB][4][64]>(smem);
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[j][v];
-    __syncthreads();
-    if (wave == 0) {
-        // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t rr = sub0 + 4 * kq + v;
-            if (row_adapter_of(rr, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter, n_ad, n_tab,
-                               st.e, a_tab, b_tab) != cur)
-                continue;
-            uint16_t* dst = xa + (rr - row_offset) * max_rank;
+        for (int s = 0; s < 4; ++s) {
+            __syncthreads();
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                dst[j * 16 + m] = f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
-                                              (red[2][j][v][lane] + red[3][j][v][lane]));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[s][j][v];
+            __syncthreads();
+            // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
+#pragma unroll
+            for (int j = wave; j < NB; j += 4)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int rl = s * 16 + 4 * kq + v;
+                    if (s_key[rl] != cur) continue;
+                    xa[(tile0 + rl - row_offset) * max_rank + j * 16 + m] =
+                        f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
+                                    (red[2][j][v][lane] + red[3][j][v][lane]));
+                }
         }
-    }
-    __syncthreads();  // red[] is rewritten by the next pass
+        __syncthreads();  // the ring is refilled by the next pass
     }
 }
 
-// Expand + fold: each wave takes one 16-row sub-tile and EXP_COLS * EXP_BLOCKS columns, one
-// block of EXP_COLS at a time.  The row state (which rows fold, their xa fragments) is read once;
-// the base rows and B_e columns of the next block are loaded while the current one is computed
-// and written, so a wave keeps a block's loads in flight instead of paying its row lookups and
-// a memory round trip per EXP_COLS columns.
+// Expand + fold: a workgroup takes a 64-row tile (four 16-row sub-tiles) and EXP_SLABS slabs of
+// 4 * EXP_COLS columns; in each slab wave w owns EXP_COLS columns of all four sub-tiles.  The tile's
+// row adapters are looked up once (a chain of dependent loads: offsets, sorted id, token adapter,
+// table entry) and its xa rows loaded once, for all slabs.  The MFMA takes B_e as its first operand,
+// delta^T = B_e xa^T, with B_e's rows permuted so that each lane ends up holding 8 consecutive
+// columns of one row: the fold runs on the accumulators directly, with 16-byte loads and stores of
+// the base rows.
+//   16x16x32 block c (of 4) of a k-step, operand row i (lane i + 16 * kq) <- B_e row
+//   n0 + 32 * (c >> 1) + 8 * (i >> 2) + 4 * (c & 1) + (i & 3); accumulator v of lane (j, kq) of block c
+//   is then delta[row j][n0 + 32 * (c >> 1) + 8 * kq + 4 * (c & 1) + v].
+// Two paths:
+//  * one expert and one adapter in the tile (the usual case): straight-line code.  Base rows and B_e
+//    are read and written with buffer instructions whose offsets are pushed out of range for lanes
+//    and columns with nothing to do (out-of-range loads return 0, stores are dropped), and the next
+//    slab's B_e and base rows are loaded before the current slab is computed.  With no branches
+//    between a load and its use, the wait before each slab covers only that slab's loads, not the
+//    stores of the slab before it (the vector memory counter is one in-order count of loads and
+//    stores).
+//  * otherwise (sub-tiles of several experts, rows of several adapters): per sub-tile, one pass per
+//    adapter present, each loading that (expert, adapter)'s B_e.
 template <int NKS>  // k-steps of 32 over max_rank
 __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __restrict__ xa,
                                                               const uint64_t* a_tab, const uint64_t* b_tab,
@@ -198,110 +278,218 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
                                                               const int32_t* __restrict__ sorted_ids, int P,
                                                               int top_k, const int32_t* __restrict__ row_adapter,
                                                               uint16_t* __restrict__ base, int64_t row_offset,
-                                                              int64_t row_end, int64_t base16) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_delta[4][16][EXP_COLS];
+                                                              int64_t row_end, int64_t base16, int n_groups,
+                                                              int fast_ok) {
     __shared__ int s_off[257];
+    __shared__ int s_rad[64];  // adapter of each row of the tile (kNoAdapter: not folded)
+    __shared__ int s_e[4];     // expert of each sub-tile (-1: nothing to do)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t sub0 = base16 + static_cast<int64_t>(blockIdx.y) * 64 + wave * 16;
-    const int slab0 = blockIdx.x * (EXP_COLS * EXP_BLOCKS);
-    if (base16 + static_cast<int64_t>(blockIdx.y) * 64 >= row_end) return;  // uniform over the workgroup
+    const int tile = blockIdx.x / n_groups, grp = blockIdx.x - tile * n_groups;
+    const int64_t tile0 = base16 + static_cast<int64_t>(tile) * 64;
+    if (tile0 >= row_end) return;  // uniform over the workgroup
     stage_offsets(off, E, s_off);
-    if (sub0 >= row_end) return;
-    const SubTile st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
-    if (st.e < 0) return;
-
+    // the 64 rows' adapters, one row per thread of the first wave, so that their chains of dependent
+    // loads are in flight together
+    if (threadIdx.x < 64) {
+        const int64_t sub0 = tile0 + (threadIdx.x & ~15);
+        SubTile st{-1, 0};
+        if (sub0 < row_end) st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
+        s_rad[threadIdx.x] = st.e >= 0 ? row_adapter_of(tile0 + threadIdx.x, row_offset, row_end, st.span_end,
+                                                        sorted_ids, P, top_k, row_adapter, n_ad, n_tab, st.e,
+                                                        a_tab, b_tab)
+                                       : kNoAdapter;
+        if ((threadIdx.x & 15) == 0) s_e[threadIdx.x >> 4] = st.e;
+    }
+    __syncthreads();
+    // no workgroup barrier after this point: a wave with nothing to do leaves on its own
+    constexpr int SLAB = 4 * EXP_COLS;
+    const int cw = grp * (SLAB * EXP_SLABS) + wave * EXP_COLS;  // this wave's first column in slab 0
+    if (cw >= n_out) return;
     const int m = lane & 15, kq = lane >> 4;
-    const int64_t r = sub0 + m;
-    const int ad = row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k, row_adapter, n_ad, n_tab,
-                                  st.e, a_tab, b_tab);
-    const bool act = ad != kNoAdapter;
-    if (__ballot(act) == 0) return;
-    u32x4 av[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        av[ks] = act ? *reinterpret_cast<const u32x4*>(xa + (r - row_offset) * max_rank + ks * 32 + kq * 8)
-                                   : u32x4{0, 0, 0, 0};
-    // fold rows of this lane (FOLD_RPS rows x FOLD_LPR lanes x 8 columns per step)
-    const int col = (lane % FOLD_LPR) * 8;
-    int row_ad[FOLD_STEPS];
-#pragma unroll
-    for (int it = 0; it < FOLD_STEPS; ++it)
-        row_ad[it] = row_adapter_of(sub0 + it * FOLD_RPS + lane / FOLD_LPR, row_offset, row_end, st.span_end,
-                                    sorted_ids, P, top_k, row_adapter, n_ad, n_tab, st.e, a_tab, b_tab);
-    // one pass per adapter present in the sub-tile (every row's xa already holds its own adapter's
-    // shrink): the pass computes the delta with that adapter's B_e and folds only its rows
-    for (int cur = wave_next_adapter(ad, -1); cur != kNoAdapter; cur = wave_next_adapter(ad, cur)) {
-    const int64_t tix = static_cast<int64_t>(cur) * n_tab + st.e;
-    const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[tix]);
-    const float scale = s_tab[tix];
-    bool row_ok[FOLD_STEPS];
-#pragma unroll
-    for (int it = 0; it < FOLD_STEPS; ++it) row_ok[it] = row_ad[it] == cur;
 
-    u32x4 bvs[2][FOLD_STEPS], bw[2][NKS][EXP_COLS / 16];
-    auto load_block = [&](int cb, int set) __attribute__((always_inline)) {
-        const int n0 = slab0 + cb * EXP_COLS;
+    // the four sub-tiles: expert, and for this lane the adapter and xa fragments of its row m; the
+    // tile's first (expert, adapter) pair, and whether it is the only one
+    int e_s[4], ad[4];
+    u32x4 av[4][NKS];
+    int pe = -1, pa = kNoAdapter;
+    bool mixed = false;
 #pragma unroll
-        for (int it = 0; it < FOLD_STEPS; ++it) {
-            const int64_t rr = sub0 + it * FOLD_RPS + lane / FOLD_LPR;
-            bvs[set][it] = (row_ok[it] && n0 + col < n_out)
-                               ? *reinterpret_cast<const u32x4*>(base + rr * n_out + n0 + col)
-                               : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < 4; ++s) {
+        e_s[s] = __builtin_amdgcn_readfirstlane(s_e[s]);  // one value per sub-tile
+        ad[s] = s_rad[s * 16 + m];
+        // xa row (row 0 when not folded: a valid address whose values reach only output rows that
+        // are not stored)
+        const int64_t xrow = ad[s] != kNoAdapter ? tile0 + s * 16 + m - row_offset : 0;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            av[s][ks] = *reinterpret_cast<const u32x4*>(xa + xrow * max_rank + ks * 32 + kq * 8);
+        if (e_s[s] < 0) continue;
+        const int a0 = wave_next_adapter(ad[s], -1);
+        if (a0 == kNoAdapter) continue;
+        if (pe < 0) {
+            pe = e_s[s];
+            pa = a0;
         }
+        mixed = mixed || e_s[s] != pe || a0 != pa || wave_next_adapter(ad[s], a0) != kNoAdapter;
+    }
+    if (pe < 0) return;  // nothing folded in this tile (uniform over the workgroup)
+
+    if (!mixed && fast_ok) {
+        // ---- one (expert, adapter) pair: straight-line, software-pipelined over the slabs
+        const int64_t pix = static_cast<int64_t>(pa) * n_tab + pe;
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void*>(b_tab[pix]), 0, n_out * max_rank * 2, 0x00020000);
+        const float scale = s_tab[pix];
+        const int rows_here = static_cast<int>(min<int64_t>(64, row_end - tile0));
+        const __amdgpu_buffer_rsrc_t rc =
+            __builtin_amdgcn_make_buffer_rsrc(base + tile0 * n_out, 0, rows_here * n_out * 2, 0x00020000);
+        // byte offsets: B_e fragment (ks, c) at column base n0 = bo[ks][c] + 2 * n0 * max_rank (columns
+        // past n_out fall past the range); base row of sub-tile s, column n: ro[s] + 2 n, or out of range
+        int bo[NKS][4], ro[4];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int c = 0; c < EXP_COLS / 16; ++c) {
-                const int n = n0 + c * 16 + m;
-                bw[set][ks][c] = n < n_out
-                                     ? *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(n) * max_rank +
-                                                                       ks * 32 + kq * 8)
-                                     : u32x4{0, 0, 0, 0};
+            for (int c = 0; c < 4; ++c)
+                bo[ks][c] = ((32 * (c >> 1) + 8 * (m >> 2) + 4 * (c & 1) + (m & 3)) * max_rank + ks * 32 + kq * 8) * 2;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ro[s] = ad[s] == pa ? (s * 16 + m) * n_out * 2 : -1;
+        auto load_b = [&](u32x4 (&w)[NKS][4], int n0) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    w[ks][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             rb, bo[ks][c] + 2 * n0 * max_rank, 0, 0));
+        };
+        auto c_off = [&](int s, int n) -> int {
+            return (ro[s] >= 0 && n < n_out) ? ro[s] + 2 * n : static_cast<int>(kOob);
+        };
+        auto load_c = [&](u32x4 (&v)[4][2], int n0) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    v[s][h] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, c_off(s, n0 + 32 * h + 8 * kq), 0, 0));
+        };
+        u32x4 bw[NKS][4], bwn[NKS][4], bv[4][2], bvn[4][2];
+        load_b(bwn, cw);
+        load_c(bvn, cw);
+#pragma unroll
+        for (int j = 0; j < EXP_SLABS; ++j) {
+            const int n0 = cw + j * SLAB;
+            if (n0 >= n_out) break;  // uniform over the wave
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bw[ks][c] = bwn[ks][c];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) bv[s][h] = bvn[s][h];
+            if (j + 1 < EXP_SLABS) {  // the next slab's loads go out before this slab's work
+                load_b(bwn, n0 + SLAB);
+                load_c(bvn, n0 + SLAB);
             }
-    };
-    load_block(0, 0);
 #pragma unroll
-    for (int cb = 0; cb < EXP_BLOCKS; ++cb) {
-        const int set = cb & 1;
-        const int n0 = slab0 + cb * EXP_COLS;
-        if (cb + 1 < EXP_BLOCKS) load_block(cb + 1, set ^ 1);
-        f32x4 acc[EXP_COLS / 16];
+            for (int s = 0; s < 4; ++s) {
+                f32x4 acc[4];
 #pragma unroll
-        for (int c = 0; c < EXP_COLS / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const bf16x8 afr = __builtin_bit_cast(bf16x8, av[ks]);
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int c = 0; c < EXP_COLS / 16; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(bf16x8, bw[set][ks][c]),
-                                                                 acc[c], 0, 0, 0);
-        }
-        // bf16 delta tile to LDS (rows 4*(lane/16)+v, column 16*c + lane%16)
+                    for (int c = 0; c < 4; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw[ks][c]),
+                                                                         __builtin_bit_cast(bf16x8, av[s][ks]),
+                                                                         acc[c], 0, 0, 0);
 #pragma unroll
-        for (int c = 0; c < EXP_COLS / 16; ++c)
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 b = bv[s][h];
+                    u32x4 o;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) s_delta[wave][4 * kq + v][c * 16 + m] = f32_to_bf16(acc[c][v]);
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        // coalesced fold of the delta into the base rows
-#pragma unroll
-        for (int it = 0; it < FOLD_STEPS; ++it) {
-            if (!row_ok[it] || n0 + col >= n_out) continue;
-            const int rl = it * FOLD_RPS + lane / FOLD_LPR;
-            const int64_t rr = sub0 + rl;
-            const u32x4 bv = bvs[set][it];
-            const u32x4 dv = *reinterpret_cast<const u32x4*>(&s_delta[wave][rl][col]);
-            u32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float b_lo = __uint_as_float(bv[i] << 16), b_hi = __uint_as_float(bv[i] & 0xffff0000u);
-                const float d_lo = __uint_as_float(dv[i] << 16), d_hi = __uint_as_float(dv[i] & 0xffff0000u);
-                o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
+                    for (int i = 0; i < 4; ++i) {
+                        // columns 2i, 2i + 1 of the chunk: accumulators 2(i & 1), 2(i & 1) + 1 of block 2h + (i >> 1)
+                        const f32x4& a4 = acc[2 * h + (i >> 1)];
+                        const uint32_t dv = pack_bf16x2(a4[2 * (i & 1)], a4[2 * (i & 1) + 1]);  // bf16 delta
+                        const float d_lo = __uint_as_float(dv << 16), d_hi = __uint_as_float(dv & 0xffff0000u);
+                        const float b_lo = __uint_as_float(b[i] << 16), b_hi = __uint_as_float(b[i] & 0xffff0000u);
+                        o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rc,
+                                                           c_off(s, n0 + 32 * h + 8 * kq), 0, 0);
+                }
             }
-            *reinterpret_cast<u32x4*>(base + rr * n_out + n0 + col) = o;
         }
-        __builtin_amdgcn_wave_barrier();  // this block's LDS reads before the next block's writes
+        return;
     }
+
+    // ---- general tile: per sub-tile, one pass per adapter present
+    for (int j = 0; j < EXP_SLABS; ++j) {
+        const int n0 = cw + j * SLAB;
+        if (n0 >= n_out) break;  // uniform over the wave
+        u32x4 bv[4][2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int n = n0 + 32 * h + 8 * kq;
+                bv[s][h] = (ad[s] != kNoAdapter && n < n_out)
+                               ? *reinterpret_cast<const u32x4*>(base + (tile0 + s * 16 + m) * n_out + n)
+                               : u32x4{0, 0, 0, 0};
+            }
+        u32x4 bw[NKS][4];
+        int have_e = -1, have_a = -1;
+        float scale = 0.f;
+        for (int s = 0; s < 4; ++s) {
+            if (e_s[s] < 0) continue;  // uniform over the wave
+            for (int cur = wave_next_adapter(ad[s], -1); cur != kNoAdapter; cur = wave_next_adapter(ad[s], cur)) {
+                if (e_s[s] != have_e || cur != have_a) {  // B_e of this expert and adapter, this slab
+                    const int64_t tix = static_cast<int64_t>(cur) * n_tab + e_s[s];
+                    const uint16_t* Be = reinterpret_cast<const uint16_t*>(b_tab[tix]);
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int n = n0 + 32 * (c >> 1) + 8 * (m >> 2) + 4 * (c & 1) + (m & 3);
+                            bw[ks][c] = n < n_out ? *reinterpret_cast<const u32x4*>(
+                                                        Be + static_cast<int64_t>(n) * max_rank + ks * 32 + kq * 8)
+                                                  : u32x4{0, 0, 0, 0};
+                        }
+                    scale = s_tab[tix];
+                    have_e = e_s[s];
+                    have_a = cur;
+                }
+                f32x4 acc[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw[ks][c]),
+                                                                         __builtin_bit_cast(bf16x8, av[s][ks]),
+                                                                         acc[c], 0, 0, 0);
+                if (ad[s] != cur) continue;  // this lane's row belongs to another pass (or is not folded)
+                const int64_t row = tile0 + s * 16 + m;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int n = n0 + 32 * h + 8 * kq;
+                    if (n >= n_out) continue;
+                    const u32x4 b = bv[s][h];
+                    u32x4 o;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x4& a4 = acc[2 * h + (i >> 1)];
+                        const uint32_t dv = pack_bf16x2(a4[2 * (i & 1)], a4[2 * (i & 1) + 1]);  // bf16 delta
+                        const float d_lo = __uint_as_float(dv << 16), d_hi = __uint_as_float(dv & 0xffff0000u);
+                        const float b_lo = __uint_as_float(b[i] << 16), b_hi = __uint_as_float(b[i] & 0xffff0000u);
+                        o[i] = pack_bf16x2(fmaf(scale, d_lo, b_lo), fmaf(scale, d_hi, b_hi));
+                    }
+                    *reinterpret_cast<u32x4*>(base + row * n_out + n) = o;
+                }
+            }
+        }
     }
 }
 
@@ -475,19 +663,14 @@ hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const ui
                               int64_t row_end, int x_gather, hipStream_t s) {
     if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
     const int64_t base16 = (row_offset / 16) * 16;
-    const int64_t subs = (row_end - base16 + 15) / 16;
-    const dim3 sgrid(static_cast<unsigned>(subs));
+    const dim3 sgrid(static_cast<unsigned>((row_end - base16 + 63) / 64));
 #define MOE_SHRINK(NB_)                                                                                          \
     lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, sorted_ids, \
                                                  P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
-    switch (max_rank / 16) {
-        case 1: MOE_SHRINK(1); break;
-        case 2: MOE_SHRINK(2); break;
-        case 3: MOE_SHRINK(3); break;
-        case 4: MOE_SHRINK(4); break;
-        case 5: MOE_SHRINK(5); break;
-        case 6: MOE_SHRINK(6); break;
-        case 7: MOE_SHRINK(7); break;
+    switch (max_rank / 32) {  // max_rank is 32, 64, 96 or 128
+        case 1: MOE_SHRINK(2); break;
+        case 2: MOE_SHRINK(4); break;
+        case 3: MOE_SHRINK(6); break;
         default: MOE_SHRINK(8); break;
     }
 #undef MOE_SHRINK
@@ -502,29 +685,27 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
     const int64_t base16 = (row_offset / 16) * 16;
     const int64_t tiles = (row_end - base16 + 63) / 64;
-    const int64_t subs = (row_end - base16 + 15) / 16;
-    const dim3 sgrid(static_cast<unsigned>(subs));
+    const dim3 sgrid(static_cast<unsigned>(tiles));
 #define MOE_SHRINK(NB_)                                                                                          \
     lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, sorted_ids, \
                                                  P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
-    switch (max_rank / 16) {
-        case 1: MOE_SHRINK(1); break;
-        case 2: MOE_SHRINK(2); break;
-        case 3: MOE_SHRINK(3); break;
-        case 4: MOE_SHRINK(4); break;
-        case 5: MOE_SHRINK(5); break;
-        case 6: MOE_SHRINK(6); break;
-        case 7: MOE_SHRINK(7); break;
+    switch (max_rank / 32) {  // max_rank is 32, 64, 96 or 128
+        case 1: MOE_SHRINK(2); break;
+        case 2: MOE_SHRINK(4); break;
+        case 3: MOE_SHRINK(6); break;
         default: MOE_SHRINK(8); break;
     }
 #undef MOE_SHRINK
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid((n_out + EXP_COLS * EXP_BLOCKS - 1) / (EXP_COLS * EXP_BLOCKS), static_cast<unsigned>(tiles));
+    const int n_groups = (n_out + 4 * EXP_COLS * EXP_SLABS - 1) / (4 * EXP_COLS * EXP_SLABS);
+    const dim3 grid(static_cast<unsigned>(tiles * n_groups));
+    // the one-pair path addresses a tile's base rows and a B_e with 32-bit buffer offsets
+    const int fast_ok = static_cast<int64_t>(64) * n_out * 2 < kOob && static_cast<int64_t>(n_out) * max_rank * 2 < kOob;
 #define MOE_EXPAND(NKS_)                                                                                        \
     lora_expand_fold_kernel<NKS_><<<grid, NT, 0, s>>>(xa, a_tab, b_tab, s_tab, n_tab, n_ad, n_out, max_rank, offsets, E, \
-                                                      sorted_ids, P, top_k, row_adapter, base, row_offset, row_end, \
-                                                      base16)
+                                                      sorted_ids, P, top_k, row_adapter, base, row_offset, row_end,  \
+                                                      base16, n_groups, fast_ok)
     switch (max_rank / 32) {
         case 1: MOE_EXPAND(1); break;
         case 2: MOE_EXPAND(2); break;

@@ -188,7 +188,8 @@ def lora_epilogue_touched(al, P, top_k, E, N, BM, rank, n_tab, n_ad, ra):
 def grouped_fold_touched(al, P, top_k, E, k_in, n_out, max_rank, n_tab, n_ad, ra, row_offset, row_end, cap,
                          x_gather, x_rows):
     """lora_shrink_kernel (one workgroup per 16-row sub-tile from base16 = row_offset rounded down to
-    16) and lora_expand_fold_kernel (64-row tiles x 256 columns, a 16-row sub-tile per wave): only
+    16) and lora_expand_fold_kernel (64-row tiles x 256 columns, a wave per 64 columns of all four
+    16-row sub-tiles): only
     rows inside the window and the expert span are read through sorted_ids; active rows read x,
     write and read xa at r - row_offset, read and write base; A_e rows < max_rank, B_e rows < n_out."""
     max_pad = len(al["sorted_ids"])
