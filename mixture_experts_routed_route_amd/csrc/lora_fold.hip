@@ -41,6 +41,74 @@ __device__ __forceinline__ void stage_offsets(const int32_t* off, int E, int* s_
     __syncthreads();
 }
 
+// ------------------------------------------------------------------ active tiles first
+// A window's 64-row tiles (from base16) are taken in this order: the tiles that hold a row of an
+// adapted expert first, in row order, then the rest.  Workgroups are dispatched in index order and
+// a tile of an unadapted expert has nothing to do, so with this order the work starts at once
+// instead of waiting for CU slots held by such tiles.  Every workgroup stages the expert offsets and
+// a per-expert "adapted by some adapter" flag and maps its ordinal k to the k-th such tile (-1 past
+// the last): each adapted expert's span sets its tiles' bits in an LDS bitmap (tiles shared by two
+// experts are set twice), and one wave counts them.  Windows of more than kMapTiles tiles keep the
+// plain order.
+constexpr int kMapTiles = 2048;
+
+struct TileMapLds {
+    int off[257];
+    int bits[kMapTiles / 32];
+    unsigned char pres[256];
+    int tile;
+};
+
+__device__ int stage_and_map_tile(int k, const int32_t* off, int E, const uint64_t* a_tab, const uint64_t* b_tab,
+                                  int n_tab, int n_ad, int64_t row_offset, int64_t row_end, int64_t base16,
+                                  TileMapLds& L) {
+    const int t = threadIdx.x;
+    for (int i = t; i <= E; i += blockDim.x) L.off[i] = off[i];
+    // an expert is adapted if some adapter holds both of its tables (every expert below n_tab when
+    // the tables are too many to look at here: a tile taken for nothing finds no row to fold)
+    const bool look = static_cast<int64_t>(n_ad) * n_tab <= 4096;
+    for (int e = t; e < E; e += blockDim.x) {
+        bool p = false;
+        if (e < n_tab) {
+            if (!look) p = true;
+            for (int a = 0; look && a < n_ad && !p; ++a) {
+                const int64_t ix = static_cast<int64_t>(a) * n_tab + e;
+                p = a_tab[ix] != 0 && b_tab[ix] != 0;
+            }
+        }
+        L.pres[e] = p;
+    }
+    if (t < kMapTiles / 32) L.bits[t] = 0;
+    if (t == 0) L.tile = -1;
+    __syncthreads();
+    const int64_t T = (row_end - base16 + 63) / 64;
+    if (T > kMapTiles) return k < T ? k : -1;  // uniform over the workgroup
+    for (int e = t; e < E; e += blockDim.x) {
+        if (!L.pres[e]) continue;
+        // the span's rows inside the window (offsets are device data: clamp to the window)
+        const int64_t lo = max<int64_t>(L.off[e], row_offset), hi = min<int64_t>(L.off[e + 1], row_end);
+        if (lo >= hi) continue;
+        const int t0 = static_cast<int>((lo - base16) / 64), t1 = static_cast<int>((hi - 1 - base16) / 64);
+        for (int w = t0 >> 5; w <= (t1 >> 5); ++w) {
+            const int b0 = max(t0 - w * 32, 0), b1 = min(t1 - w * 32, 31);
+            const uint32_t mask = (b1 == 31 ? 0xffffffffu : ((1u << (b1 + 1)) - 1u)) & ~((1u << b0) - 1u);
+            atomicOr(reinterpret_cast<unsigned int*>(&L.bits[w]), mask);
+        }
+    }
+    __syncthreads();
+    if (t < 64) {  // the first wave: word t holds tiles 32 t .. 32 t + 31
+        uint32_t word = t < kMapTiles / 32 ? static_cast<uint32_t>(L.bits[t]) : 0u;
+        const int c = __builtin_popcount(word);
+        const int incl = wave_inclusive_scan(c);
+        if (k >= incl - c && k < incl) {
+            for (int i = k - (incl - c); i > 0; --i) word &= word - 1;  // drop the lower set bits
+            L.tile = t * 32 + __builtin_ctz(word);
+        }
+    }
+    __syncthreads();
+    return L.tile;
+}
+
 struct SubTile {
     int e;          // expert of the 16-row sub-tile (-1: nothing to do)
     int span_end;   // end of that expert's padded span
@@ -105,32 +173,38 @@ __device__ __forceinline__ int wave_next_key(int mine, int after) {
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Shrink LDS: each wave's ring of R k-steps (x of the 64 rows, then A_e's 16 NB rank rows, 32 k each,
-// in 1 KB blocks of 16 rows: block byte (c * 16 + r) * 16 holds chunk c (k 8c..8c+7) of row r, so
-// that lane L of a fragment read takes bytes 16 L..16 L + 15); after the K loop the same memory holds
-// one sub-tile's partial sums of the four waves.
-template <int NB>
+// Shrink LDS: each wave's ring of R k-steps (x of the workgroup's SUBS * 16 rows, then A_e's 16 NB
+// rank rows, 32 k each, in 1 KB blocks of 16 rows: block byte (c * 16 + r) * 16 holds chunk c (k
+// 8c..8c+7) of row r, so that lane L of a fragment read takes bytes 16 L..16 L + 15); after the K
+// loop the same memory holds one sub-tile's partial sums of the four waves.
+template <int NB, int SUBS>
 struct ShrinkLds {
-    static constexpr int R = NB <= 4 ? 4 : 3;  // k-steps in flight per wave
-    static constexpr int X_BYTES = 4 * 1024;
+    static constexpr int R = SUBS == 4 ? (NB <= 4 ? 4 : 3) : (NB <= 4 ? 3 : 2);  // k-steps in flight per wave
+    static constexpr int X_BYTES = SUBS * 1024;
     static constexpr int STAGE = X_BYTES + NB * 1024;
     static constexpr int WAVE = R * STAGE;
     static constexpr int RING = 4 * WAVE;
     static constexpr int RED = 4 * NB * 4 * 64 * 4;
     static constexpr int BYTES = RING > RED ? RING : RED;
-    static constexpr int LOADS = 4 + NB;  // load instructions per k-step and wave
+    static constexpr int LOADS = SUBS + NB;  // load instructions per k-step and wave
 };
 
-// Shrink: one workgroup per 64-row tile (four 16-row sub-tiles); its 4 waves take a quarter of k_in
-// each and add their partial sums in LDS.  A tile's rows are taken one (expert, adapter) pair at a
-// time (a uniform loop over the pairs present, usually one); in the pass of a pair, a wave streams
-// its k range of x (the tile's 64 rows) and of the pair's A_e through its LDS ring with direct
-// global->LDS loads, R k-steps ahead, and each k-step's A_e fragments serve all four sub-tiles.
+#ifndef MOE_LORA_SHRINK_SUBS
+#define MOE_LORA_SHRINK_SUBS 2
+#endif
+constexpr int SHRINK_SUBS = MOE_LORA_SHRINK_SUBS;  // 16-row sub-tiles per shrink workgroup (2 or 4)
+
+// Shrink: a workgroup takes SUBS 16-row sub-tiles of a 64-row tile (SUBS = 2: the tile's two halves
+// go to workgroups 8 ids apart, which run on the same XCD and share A_e in its L2); its 4 waves take
+// a quarter of k_in each and add their partial sums in LDS.  The rows are taken one (expert,
+// adapter) pair at a time (a uniform loop over the pairs present, usually one); in the pass of a
+// pair, a wave streams its k range of x and of the pair's A_e through its LDS ring with direct
+// global->LDS loads, R k-steps ahead, and each k-step's A_e fragments serve all SUBS sub-tiles.
 // The loads are not tracked by the compiler (see dma16): each k-step waits with an explicit vmcnt
 // for its own loads only.  Chunks past the wave's k range load zeros; x rows of other passes (or not
 // folded) give results in their own output rows only, which this pass does not store.
-// NB = rank blocks of 16 (max_rank / 16, up to 8).
-template <int NB>
+// NB = rank blocks of 16 (max_rank / 16).
+template <int NB, int SUBS>
 __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restrict__ x, const uint64_t* a_tab,
                                                          const uint64_t* b_tab, int n_tab, int n_ad, int k_in,
                                                          int max_rank,
@@ -139,19 +213,26 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ row_adapter,
                                                          uint16_t* __restrict__ xa, int64_t row_offset,
                                                          int64_t row_end, int64_t base16, int x_gather) {
-    using L = ShrinkLds<NB>;
+    static_assert(SUBS == 2 || SUBS == 4, "sub-tiles per workgroup");
+    constexpr int ROWS = SUBS * 16;
+    using L = ShrinkLds<NB, SUBS>;
     constexpr int R = L::R;
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-    __shared__ int s_off[257];
-    __shared__ int s_key[64];       // (expert << 16) | adapter of each row of the tile, kNoKey: not folded
-    __shared__ int64_t s_xrow[64];  // its x row
+    __shared__ TileMapLds tm;
+    __shared__ int s_key[ROWS];       // (expert << 16) | adapter of each row, kNoKey: not folded
+    __shared__ int64_t s_xrow[ROWS];  // its x row
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t tile0 = base16 + static_cast<int64_t>(blockIdx.x) * 64;
-    if (tile0 >= row_end) return;  // uniform over the workgroup
-    stage_offsets(off, E, s_off);
-    if (threadIdx.x < 64) {
-        const int64_t r = tile0 + threadIdx.x;
-        const int64_t sub0 = tile0 + (threadIdx.x & ~15);
+    // tile ordinal and part: with two parts, ids 16 q + p and 16 q + 8 + p (p < 8) share tile 8 q + p
+    const int b = blockIdx.x;
+    const int kt = SUBS == 4 ? b : (b >> 4) * 8 + (b & 7);
+    const int part = SUBS == 4 ? 0 : (b >> 3) & 1;
+    const int tile = stage_and_map_tile(kt, off, E, a_tab, b_tab, n_tab, n_ad, row_offset, row_end, base16, tm);
+    if (tile < 0) return;  // uniform over the workgroup
+    const int64_t row0 = base16 + static_cast<int64_t>(tile) * 64 + part * ROWS;
+    const int* s_off = tm.off;
+    if (threadIdx.x < ROWS) {
+        const int64_t r = row0 + threadIdx.x;
+        const int64_t sub0 = row0 + (threadIdx.x & ~15);
         SubTile st{-1, 0};
         if (sub0 < row_end) st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
         const int a = st.e >= 0 ? row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k,
@@ -164,11 +245,11 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
     __syncthreads();
 
     const int m = lane & 15, kq = lane >> 4;
-    const int key_l = s_key[lane];  // lane l holds row l's key, for the pass loop
+    const int key_l = lane < ROWS ? s_key[lane] : kNoKey;  // lane l holds row l's key, for the pass loop
     // this lane's load sources: chunk kq of row m of x block q (sub-tile q), of rank row 16 j + m
-    const uint16_t* xsrc[4];
+    const uint16_t* xsrc[SUBS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xsrc[q] = x + s_xrow[q * 16 + m] * k_in + kq * 8;
+    for (int q = 0; q < SUBS; ++q) xsrc[q] = x + s_xrow[q * 16 + m] * k_in + kq * 8;
     const int kpart = ((k_in + 127) / 128) * 32;  // this wave's k range, a multiple of 32
     const int kb = wave * kpart, ke = min(k_in, kb + kpart);
     const int nsteps = ke > kb ? (ke - kb + 31) / 32 : 0;  // uniform over the wave
@@ -185,17 +266,18 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
             const bool in = k + kq * 8 < ke;
             const uint32_t slot = __builtin_amdgcn_readfirstlane(ring + (t % R) * L::STAGE);  // m0 takes a scalar
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dma16(in ? static_cast<const void*>(xsrc[q] + k) : kZero16, slot + q * 1024);
+            for (int q = 0; q < SUBS; ++q)
+                dma16(in ? static_cast<const void*>(xsrc[q] + k) : kZero16, slot + q * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j)
                 dma16(in ? static_cast<const void*>(Ae + static_cast<int64_t>(j * 16) * k_in + k) : kZero16,
                       slot + L::X_BYTES + j * 1024);
         };
-        f32x4 acc[4][NB];
+        f32x4 acc[SUBS][NB];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int q = 0; q < SUBS; ++q)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[s][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NB; ++j) acc[q][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int t = 0; t < R && t < nsteps; ++t) issue(t);
         for (int t = 0; t < nsteps; ++t) {
             // k-step t has landed once at most `ahead` later k-steps' loads are still in flight
@@ -206,41 +288,41 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
             else wait_vmcnt<0>();
             asm volatile("" ::: "memory");  // the LDS reads stay below the wait
             const char* st = ring_p + (t % R) * L::STAGE + lane * 16;
-            u32x4 xv[4], av[NB];
+            u32x4 xv[SUBS], av[NB];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xv[q] = *reinterpret_cast<const u32x4*>(st + q * 1024);
+            for (int q = 0; q < SUBS; ++q) xv[q] = *reinterpret_cast<const u32x4*>(st + q * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j) av[j] = *reinterpret_cast<const u32x4*>(st + L::X_BYTES + j * 1024);
             // the slot's reads are done before it is refilled (the clobber keeps them above this point)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (t + R < nsteps) issue(t + R);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int q = 0; q < SUBS; ++q)
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
-                    acc[s][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[s]),
+                    acc[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[q]),
                                                                         __builtin_bit_cast(bf16x8, av[j]),
-                                                                        acc[s][j], 0, 0, 0);
+                                                                        acc[q][j], 0, 0, 0);
         }
         // the four waves' partial sums, one sub-tile at a time (in the ring's memory, once every wave
         // is past its K loop); wave w stores rank blocks w, w + 4
         float (*red)[NB][4][64] = reinterpret_cast<float (*)[NB][4][64]>(smem);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int q = 0; q < SUBS; ++q) {
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[s][j][v];
+                for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[q][j][v];
             __syncthreads();
             // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
 #pragma unroll
             for (int j = wave; j < NB; j += 4)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int rl = s * 16 + 4 * kq + v;
+                    const int rl = q * 16 + 4 * kq + v;
                     if (s_key[rl] != cur) continue;
-                    xa[(tile0 + rl - row_offset) * max_rank + j * 16 + m] =
+                    xa[(row0 + rl - row_offset) * max_rank + j * 16 + m] =
                         f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
                                     (red[2][j][v][lane] + red[3][j][v][lane]));
                 }
@@ -280,14 +362,15 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ base, int64_t row_offset,
                                                               int64_t row_end, int64_t base16, int n_groups,
                                                               int fast_ok) {
-    __shared__ int s_off[257];
+    __shared__ TileMapLds tm;
     __shared__ int s_rad[64];  // adapter of each row of the tile (kNoAdapter: not folded)
     __shared__ int s_e[4];     // expert of each sub-tile (-1: nothing to do)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tile = blockIdx.x / n_groups, grp = blockIdx.x - tile * n_groups;
+    const int k = blockIdx.x / n_groups, grp = blockIdx.x - k * n_groups;
+    const int tile = stage_and_map_tile(k, off, E, a_tab, b_tab, n_tab, n_ad, row_offset, row_end, base16, tm);
+    if (tile < 0) return;  // uniform over the workgroup
     const int64_t tile0 = base16 + static_cast<int64_t>(tile) * 64;
-    if (tile0 >= row_end) return;  // uniform over the workgroup
-    stage_offsets(off, E, s_off);
+    const int* s_off = tm.off;
     // the 64 rows' adapters, one row per thread of the first wave, so that their chains of dependent
     // loads are in flight together
     if (threadIdx.x < 64) {
@@ -655,6 +738,10 @@ __global__ __launch_bounds__(NT) void gather_expand_kernel(const uint16_t* __res
     }
 }
 
+// shrink workgroups for a window of `tiles` 64-row tiles: one per tile, or with two per tile, 16 per
+// group of 8 tiles (the last group whole; its ids past the window find no tile)
+int64_t shrink_blocks(int64_t tiles) { return SHRINK_SUBS == 4 ? tiles : (tiles + 7) / 8 * 16; }
+
 }  // namespace
 
 hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const uint64_t* b_tab, int n_tab, int n_ad, int k_in,
@@ -663,10 +750,11 @@ hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const ui
                               int64_t row_end, int x_gather, hipStream_t s) {
     if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
     const int64_t base16 = (row_offset / 16) * 16;
-    const dim3 sgrid(static_cast<unsigned>((row_end - base16 + 63) / 64));
+    const dim3 sgrid(static_cast<unsigned>(shrink_blocks((row_end - base16 + 63) / 64)));
 #define MOE_SHRINK(NB_)                                                                                          \
-    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, sorted_ids, \
-                                                 P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
+    lora_shrink_kernel<NB_, SHRINK_SUBS><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, \
+                                                              sorted_ids, P, top_k, row_adapter, xa, row_offset,   \
+                                                              row_end, base16, x_gather)
     switch (max_rank / 32) {  // max_rank is 32, 64, 96 or 128
         case 1: MOE_SHRINK(2); break;
         case 2: MOE_SHRINK(4); break;
@@ -685,10 +773,11 @@ hipError_t launch_lora_fold(const uint16_t* x, uint16_t* base, const uint64_t* a
     if (row_end <= row_offset || n_tab <= 0) return hipSuccess;
     const int64_t base16 = (row_offset / 16) * 16;
     const int64_t tiles = (row_end - base16 + 63) / 64;
-    const dim3 sgrid(static_cast<unsigned>(tiles));
+    const dim3 sgrid(static_cast<unsigned>(shrink_blocks(tiles)));
 #define MOE_SHRINK(NB_)                                                                                          \
-    lora_shrink_kernel<NB_><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, sorted_ids, \
-                                                 P, top_k, row_adapter, xa, row_offset, row_end, base16, x_gather)
+    lora_shrink_kernel<NB_, SHRINK_SUBS><<<sgrid, NT, 0, s>>>(x, a_tab, b_tab, n_tab, n_ad, k_in, max_rank, offsets, E, \
+                                                              sorted_ids, P, top_k, row_adapter, xa, row_offset,   \
+                                                              row_end, base16, x_gather)
     switch (max_rank / 32) {  // max_rank is 32, 64, 96 or 128
         case 1: MOE_SHRINK(2); break;
         case 2: MOE_SHRINK(4); break;
