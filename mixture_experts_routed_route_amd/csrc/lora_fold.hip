@@ -132,16 +132,19 @@ __device__ __forceinline__ SubTile sub_tile_expert(int sub0, const int32_t* off,
 constexpr int kNoAdapter = 0x7fffffff;  // "no adapter" key: above every real adapter id
 
 // Adapter of sorted row r if it is folded (inside the window and the expert span, real, its token's
-// adapter in [0, n_ad) and that adapter adapts expert e), else kNoAdapter.
+// adapter in [0, n_ad) and that adapter adapts expert e), else kNoAdapter.  With one adapter, `pres`
+// (LDS: expert e adapted, staged with the tile map) stands for the table lookup.
 __device__ __forceinline__ int row_adapter_of(int64_t r, int64_t row_offset, int64_t row_end, int span_end,
                                               const int32_t* sorted_ids, int P, int top_k,
                                               const int32_t* row_adapter, int n_ad, int n_tab, int e,
-                                              const uint64_t* a_tab, const uint64_t* b_tab) {
+                                              const uint64_t* a_tab, const uint64_t* b_tab,
+                                              const unsigned char* pres = nullptr) {
     if (r < row_offset || r >= row_end || r >= span_end) return kNoAdapter;
     const int p = sorted_ids[r];
     if (p < 0 || p >= P) return kNoAdapter;
     const int a = row_adapter ? row_adapter[p / top_k] : 0;
     if (a < 0 || a >= n_ad) return kNoAdapter;
+    if (pres && n_ad == 1) return pres[e] ? a : kNoAdapter;
     const int64_t ix = static_cast<int64_t>(a) * n_tab + e;
     if (a_tab[ix] == 0 || b_tab[ix] == 0) return kNoAdapter;
     return a;
@@ -176,7 +179,7 @@ __device__ __forceinline__ int wave_next_key(int mine, int after) {
 // Shrink LDS: each wave's ring of R k-steps (x of the workgroup's SUBS * 16 rows, then A_e's 16 NB
 // rank rows, 32 k each, in 1 KB blocks of 16 rows: block byte (c * 16 + r) * 16 holds chunk c (k
 // 8c..8c+7) of row r, so that lane L of a fragment read takes bytes 16 L..16 L + 15); after the K
-// loop the same memory holds one sub-tile's partial sums of the four waves.
+// loop the same memory holds the partial sums of the four waves.
 template <int NB, int SUBS>
 struct ShrinkLds {
     static constexpr int R = SUBS == 4 ? (NB <= 4 ? 4 : 3) : (NB <= 4 ? 3 : 2);  // k-steps in flight per wave
@@ -184,7 +187,7 @@ struct ShrinkLds {
     static constexpr int STAGE = X_BYTES + NB * 1024;
     static constexpr int WAVE = R * STAGE;
     static constexpr int RING = 4 * WAVE;
-    static constexpr int RED = 4 * NB * 4 * 64 * 4;
+    static constexpr int RED = 4 * SUBS * NB * 4 * 64 * 4;
     static constexpr int BYTES = RING > RED ? RING : RED;
     static constexpr int LOADS = SUBS + NB;  // load instructions per k-step and wave
 };
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
         SubTile st{-1, 0};
         if (sub0 < row_end) st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
         const int a = st.e >= 0 ? row_adapter_of(r, row_offset, row_end, st.span_end, sorted_ids, P, top_k,
-                                                 row_adapter, n_ad, n_tab, st.e, a_tab, b_tab)
+                                                 row_adapter, n_ad, n_tab, st.e, a_tab, b_tab, tm.pres)
                                 : kNoAdapter;
         s_key[threadIdx.x] = a != kNoAdapter ? (st.e << 16) | a : kNoKey;
         // x row: the sorted row (down), or the row's token in the token-major input (gate/up form)
@@ -304,18 +307,20 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                                                                         __builtin_bit_cast(bf16x8, av[j]),
                                                                         acc[q][j], 0, 0, 0);
         }
-        // the four waves' partial sums, one sub-tile at a time (in the ring's memory, once every wave
-        // is past its K loop); wave w stores rank blocks w, w + 4
-        float (*red)[NB][4][64] = reinterpret_cast<float (*)[NB][4][64]>(smem);
+        // the four waves' partial sums (in the ring's memory, once every wave is past its K loop);
+        // wave w adds and stores rank blocks w, w + 4
+        float (*red)[SUBS][NB][4][64] = reinterpret_cast<float (*)[SUBS][NB][4][64]>(smem);
+        __syncthreads();
 #pragma unroll
-        for (int q = 0; q < SUBS; ++q) {
-            __syncthreads();
+        for (int q = 0; q < SUBS; ++q)
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[q][j][v];
-            __syncthreads();
-            // C fragment: rows 4*(lane/16)+v of the sub-tile, rank column 16*j + lane%16
+                for (int v = 0; v < 4; ++v) red[wave][q][j][v][lane] = acc[q][j][v];
+        __syncthreads();
+        // C fragment: rows 4*(lane/16)+v of sub-tile q, rank column 16*j + lane%16
+#pragma unroll
+        for (int q = 0; q < SUBS; ++q)
 #pragma unroll
             for (int j = wave; j < NB; j += 4)
 #pragma unroll
@@ -323,10 +328,9 @@ __global__ __launch_bounds__(NT) void lora_shrink_kernel(const uint16_t* __restr
                     const int rl = q * 16 + 4 * kq + v;
                     if (s_key[rl] != cur) continue;
                     xa[(row0 + rl - row_offset) * max_rank + j * 16 + m] =
-                        f32_to_bf16((red[0][j][v][lane] + red[1][j][v][lane]) +
-                                    (red[2][j][v][lane] + red[3][j][v][lane]));
+                        f32_to_bf16((red[0][q][j][v][lane] + red[1][q][j][v][lane]) +
+                                    (red[2][q][j][v][lane] + red[3][q][j][v][lane]));
                 }
-        }
         __syncthreads();  // the ring is refilled by the next pass
     }
 }
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(NT) void lora_expand_fold_kernel(const uint16_t* __
         if (sub0 < row_end) st = sub_tile_expert(static_cast<int>(sub0), s_off, E, n_tab);
         s_rad[threadIdx.x] = st.e >= 0 ? row_adapter_of(tile0 + threadIdx.x, row_offset, row_end, st.span_end,
                                                         sorted_ids, P, top_k, row_adapter, n_ad, n_tab, st.e,
-                                                        a_tab, b_tab)
+                                                        a_tab, b_tab, tm.pres)
                                        : kNoAdapter;
         if ((threadIdx.x & 15) == 0) s_e[threadIdx.x >> 4] = st.e;
     }
