@@ -27,7 +27,8 @@
 namespace moe {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NW = 4;  // waves per workgroup (8, with half as many K groups each, measured slower)
+constexpr int NT = NW * 64;
 constexpr int NCOL = 64;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -65,20 +66,23 @@ struct GroupRegs {
 };
 
 template <bool GATE_UP, int STEPS>
-__global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
+__global__ __launch_bounds__(NT, (STEPS <= 4 ? 16 : 8) / NW) void gemm_int4_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ qw0, const uint16_t* __restrict__ sc0,
     const int32_t* __restrict__ qz0, const int32_t* __restrict__ qw1, const uint16_t* __restrict__ sc1,
     const int32_t* __restrict__ qz1, uint16_t* __restrict__ C, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ expert_ids, int P, int top_k, int E, int N, int K, int bs, int max_pad,
-    int a_tok) {
-    constexpr int NSPLIT = GATE_UP ? 2 : 4;    // waves sharing one projection's K groups
+    int a_tok, int col_fast) {
+    constexpr int NSPLIT = GATE_UP ? NW / 2 : NW;  // waves sharing one projection's K groups
     constexpr int G = STEPS * 32;
     __shared__ int s_row[16];
-    __shared__ float red[4][4][64][4];  // [wave][v][lane][j]
+    __shared__ float red[NW][4][64][4];  // [wave][v][lane][j]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r0 = blockIdx.x * 16;
-    const int n0 = blockIdx.y * NCOL;
+    // with col_fast the column blocks are the grid's fast index: the workgroups of one tile,
+    // dispatched together, read the whole rows of its expert's qweight (N * 4 bytes per k-octet)
+    // at about the same time (grids too tall for the y dimension keep the tiles fast)
+    const int r0 = (col_fast ? blockIdx.y : blockIdx.x) * 16;
+    const int n0 = (col_fast ? blockIdx.x : blockIdx.y) * NCOL;
     const int m = lane & 15, kq = lane >> 4;  // A fragment row; k-octet within a k32 step
 
     // The tile's rows: every wave reads the 16 sorted ids itself (no barrier before the first
@@ -91,8 +95,8 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     if (e < 0 || e >= E) return;
 
     // this wave's projection and quantisation groups
-    const int proj = GATE_UP ? wave >> 1 : 0;
-    const int part = GATE_UP ? wave & 1 : wave;
+    const int proj = GATE_UP ? wave / NSPLIT : 0;
+    const int part = GATE_UP ? wave % NSPLIT : wave;
     const int ngroups = K / G;
     const int per = (ngroups + NSPLIT - 1) / NSPLIT;
     const int g_begin = part * per;
@@ -100,29 +104,25 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     const int ncol = n0 + 4 * m;              // first of this lane's 4 columns
     const int zshift = 16 * (m & 1);          // nibble of column ncol inside its qzeros word
 
-    // per-lane weight cursors at group g_begin (clamped to the last group for a wave without
-    // groups, whose loads are then unused); every group moves them by a fixed stride
-    const int g0 = min(g_begin, ngroups - 1);
-    const int32_t* q_cur = (proj ? qw1 : qw0) + static_cast<size_t>(e) * (K / 8) * N +
-                           static_cast<size_t>(g0 * (G / 8) + kq) * N + ncol;
-    const uint16_t* s_cur = (proj ? sc1 : sc0) + static_cast<size_t>(e) * (K / G) * N +
-                            static_cast<size_t>(g0) * N + ncol;
-    const int32_t* z_cur = (proj ? qz1 : qz0) + static_cast<size_t>(e) * (K / G) * (N / 8) +
-                           static_cast<size_t>(g0) * (N / 8) + ncol / 8;
-    auto load_w = [&](GroupRegs<STEPS>& R) {
+    // per-lane weight and x sources of group g (g in [g0, g_last]: a wave without groups, or the
+    // prefetch past its last group, reads its last group again, in bounds and unused)
+    const int g0 = __builtin_amdgcn_readfirstlane(min(g_begin, ngroups - 1));  // wave-uniform
+    const int g_last = __builtin_amdgcn_readfirstlane(max(g_end - 1, g0));
+    const int32_t* q_base = (proj ? qw1 : qw0) + static_cast<size_t>(e) * (K / 8) * N + static_cast<size_t>(kq) * N + ncol;
+    const uint16_t* s_base = (proj ? sc1 : sc0) + static_cast<size_t>(e) * (K / G) * N + ncol;
+    const int32_t* z_base = (proj ? qz1 : qz0) + static_cast<size_t>(e) * (K / G) * (N / 8) + ncol / 8;
+    auto load_w = [&](GroupRegs<STEPS>& R, int g) {
+        const int32_t* q = q_base + static_cast<size_t>(g) * (G / 8) * N;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
-            R.q[st] = *reinterpret_cast<const u32x4*>(q_cur + static_cast<size_t>(st) * 4 * N);
-        R.s = *reinterpret_cast<const uint2*>(s_cur);
-        R.z = static_cast<uint32_t>(*z_cur);
-        q_cur += static_cast<size_t>(G / 8) * N;
-        s_cur += N;
-        z_cur += N / 8;
+            R.q[st] = *reinterpret_cast<const u32x4*>(q + static_cast<size_t>(st) * 4 * N);
+        R.s = *reinterpret_cast<const uint2*>(s_base + static_cast<size_t>(g) * N);
+        R.z = static_cast<uint32_t>(z_base[static_cast<size_t>(g) * (N / 8)]);
     };
     // the first group's weights depend only on the expert: they stream while the rows resolve
-    const int ng = g_end - g_begin;
-    GroupRegs<STEPS> nxt;
-    load_w(nxt);
+    const int ng = __builtin_amdgcn_readfirstlane(max(g_end - g_begin, 0));
+    GroupRegs<STEPS> ra, rb;  // two register sets, groups alternating between them
+    load_w(ra, g0);
 
     const int src = (p >= 0 && p < P) ? ((GATE_UP || a_tok) ? p / top_k : r0 + m) : -1;
     if (wave == 0 && lane < 16) s_row[lane] = src;  // read by the epilogue after the reduction barrier
@@ -131,17 +131,13 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
     // a row without a token reads a row that is always in bounds (token 0, or the tile's first
     // sorted row); its results are never stored
     const int arow_ok = src >= 0 ? src : ((GATE_UP || a_tok) ? 0 : r0);
-    const uint16_t* a_cur = A + static_cast<size_t>(arow_ok) * K + kq * 8 + static_cast<size_t>(g0) * G;
-    auto load_a = [&](GroupRegs<STEPS>& R) {
+    const uint16_t* a_base = A + static_cast<size_t>(arow_ok) * K + kq * 8;
+    auto load_a = [&](GroupRegs<STEPS>& R, int g) {
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) R.a[st] = *reinterpret_cast<const u32x4*>(a_cur + st * 32);
-        a_cur += G;
+        for (int st = 0; st < STEPS; ++st)
+            R.a[st] = *reinterpret_cast<const u32x4*>(a_base + static_cast<size_t>(g) * G + st * 32);
     };
-    auto load_group = [&](GroupRegs<STEPS>& R) {
-        load_w(R);
-        load_a(R);
-    };
-    load_a(nxt);
+    load_a(ra, g0);
 
     f32x4 out[4];
 #pragma unroll
@@ -174,12 +170,26 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
         }
     };
 
-    // group g+1 loads while group g is computed
-    for (int i = 0; i < ng; ++i) {
-        const GroupRegs<STEPS> cur = nxt;
-        if (i + 1 < ng) load_group(nxt);
-        compute_group(cur);
+    // group g+1 loads while group g is computed, two groups per trip in fixed register sets (no
+    // copies of registers with loads in flight); the loads are issued unconditionally (past the
+    // wave's last group they re-read it) so that no branch separates a load from its use and the
+    // wait before a group's MFMAs covers that group's loads only
+    // (scheduling fences keep each group's loads together, ahead of the other group's MFMAs)
+    int i = 0;
+    for (; i + 1 < ng; i += 2) {
+        load_w(rb, g0 + i + 1);
+        load_a(rb, g0 + i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_group(ra);
+        __builtin_amdgcn_sched_barrier(0);
+        const int gn = min(g0 + i + 2, g_last);
+        load_w(ra, gn);
+        load_a(ra, gn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_group(rb);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (i < ng) compute_group(ra);  // an odd count: the last group is in ra
 
     // split-K reduction over the waves, then the epilogue: 256 threads = 16 rows x 16 column quads
 #pragma unroll
@@ -187,6 +197,11 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) red[wave][v][lane][j] = out[j][v];
     __syncthreads();
+    // the partial sums of waves w0 .. w0 + n - 1 (n = 2 or 4), added pairwise in a fixed order
+    auto wsum = [&](int w0, int n, int v, int sl, int j) {
+        if (n == 2) return red[w0][v][sl][j] + red[w0 + 1][v][sl][j];
+        return (red[w0][v][sl][j] + red[w0 + 1][v][sl][j]) + (red[w0 + 2][v][sl][j] + red[w0 + 3][v][sl][j]);
+    };
     {
         const int sl = tid & 63, v = tid >> 6;  // source lane and row-in-quad of the C fragment
         const int row = 4 * (sl >> 4) + v;
@@ -196,13 +211,8 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float res_j;
-            if (GATE_UP) {
-                const float g = red[0][v][sl][j] + red[1][v][sl][j];
-                const float u = red[2][v][sl][j] + red[3][v][sl][j];
-                res_j = silu_mul(g, u);
-            } else {
-                res_j = (red[0][v][sl][j] + red[1][v][sl][j]) + (red[2][v][sl][j] + red[3][v][sl][j]);
-            }
+            if (GATE_UP) res_j = silu_mul(wsum(0, NSPLIT, v, sl, j), wsum(NSPLIT, NSPLIT, v, sl, j));
+            else res_j = wsum(0, NSPLIT, v, sl, j);
             res[j] = res_j;
         }
         uint2 o;
@@ -213,17 +223,17 @@ __global__ __launch_bounds__(NT, STEPS <= 4 ? 4 : 2) void gemm_int4_kernel(
 }
 
 template <int STEPS>
-void launch_int4_steps(int op, dim3 grid, hipStream_t s, const uint16_t* a, const int32_t* qw0,
+void launch_int4_steps(int op, dim3 grid, int col_fast, hipStream_t s, const uint16_t* a, const int32_t* qw0,
                        const uint16_t* sc0, const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1,
                        const int32_t* qz1, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids, int P,
                        int top_k, int E, int N, int K, int bs, int max_pad) {
     if (op == kOpGateUpSilu)
         gemm_int4_kernel<true, STEPS><<<grid, NT, 0, s>>>(a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids,
-                                                          P, top_k, E, N, K, bs, max_pad, 1);
+                                                          P, top_k, E, N, K, bs, max_pad, 1, col_fast);
     else  // one projection: rows of a in sorted order (down) or by token (gather)
         gemm_int4_kernel<false, STEPS><<<grid, NT, 0, s>>>(a, qw0, sc0, qz0, nullptr, nullptr, nullptr, c,
                                                            sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad,
-                                                           op == kOpGather ? 1 : 0);
+                                                           op == kOpGather ? 1 : 0, col_fast);
 }
 
 }  // namespace
@@ -232,12 +242,13 @@ hipError_t launch_gemm_int4(int op, const uint16_t* a, const int32_t* qw0, const
                             const int32_t* qz0, const int32_t* qw1, const uint16_t* sc1, const int32_t* qz1,
                             int group_size, uint16_t* c, const int32_t* sorted_ids, const int32_t* expert_ids,
                             int P, int top_k, int E, int N, int K, int bs, int max_pad, hipStream_t s) {
-    const dim3 grid(max_pad / 16, N / NCOL);
+    const int col_fast = max_pad / 16 <= 65535;  // column blocks fastest (see the kernel) when y can hold the tiles
+    const dim3 grid = col_fast ? dim3(N / NCOL, max_pad / 16) : dim3(max_pad / 16, N / NCOL);
     switch (group_size) {
-        case 32: launch_int4_steps<1>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
-        case 64: launch_int4_steps<2>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
-        case 128: launch_int4_steps<4>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
-        case 256: launch_int4_steps<8>(op, grid, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 32: launch_int4_steps<1>(op, grid, col_fast, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 64: launch_int4_steps<2>(op, grid, col_fast, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 128: launch_int4_steps<4>(op, grid, col_fast, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
+        case 256: launch_int4_steps<8>(op, grid, col_fast, s, a, qw0, sc0, qz0, qw1, sc1, qz1, c, sorted_ids, expert_ids, P, top_k, E, N, K, bs, max_pad); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
