@@ -136,7 +136,9 @@ def measured_traffic(workload: str, role: str):
         if ":" in line and not line.startswith((" ", "#")):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    files, want = kv.get("source_files", "").split(), kv.get("source_sha256")
+    # a role's own source list and hash when the summary gives them, else the file-wide ones
+    files = kv.get(f"{role}.source_files", kv.get("source_files", "")).split()
+    want = kv.get(f"{role}.source_sha256", kv.get("source_sha256"))
     if not files or not want or f"{role}.traffic_bytes" not in kv:
         return None
     h = hashlib.sha256()

@@ -95,6 +95,31 @@ def test_traffic_figure_only_for_the_profiled_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("w", "gate_up") is None
 
 
+def test_traffic_figure_per_role_sources(tmp_path, monkeypatch):
+    """A role with its own source list is judged by those files alone: changing another role's
+    kernel does not void it."""
+    tmp = str(tmp_path)
+    csrc = os.path.join(tmp, "mixture_experts_routed_route_amd", "csrc")
+    os.makedirs(csrc)
+    for name, body in (("g.hip", b"gemm v1"), ("f.hip", b"fold v1")):
+        with open(os.path.join(csrc, name), "wb") as f:
+            f.write(body)
+    os.makedirs(os.path.join(tmp, "profiles"))
+    with open(os.path.join(tmp, "profiles", "traffic_w.txt"), "w") as f:
+        f.write("# test\n")
+        f.write(f"gate_up.source_files: g.hip\ngate_up.source_sha256: {hashlib.sha256(b'gemm v1').hexdigest()}\n")
+        f.write("gate_up.traffic_bytes: 111\n")
+        f.write(f"lora_fold.source_files: f.hip\nlora_fold.source_sha256: {hashlib.sha256(b'fold v1').hexdigest()}\n")
+        f.write("lora_fold.traffic_bytes: 222\n")
+    monkeypatch.setattr(bench, "ROOT", tmp)
+    assert bench.measured_traffic("w", "gate_up") == 111.0
+    assert bench.measured_traffic("w", "lora_fold") == 222.0
+    with open(os.path.join(csrc, "f.hip"), "wb") as f:
+        f.write(b"fold v2")
+    assert bench.measured_traffic("w", "lora_fold") is None
+    assert bench.measured_traffic("w", "gate_up") == 111.0
+
+
 def test_cpu_baseline_object():
     cfg = MoeConfig("bench_tiny", T=48, H=64, I=32, E=4, top_k=2, block_size=16, seed=3)
     d = make_inputs(cfg)

@@ -187,22 +187,31 @@ def lora_epilogue_touched(al, P, top_k, E, N, BM, rank, n_tab, n_ad, ra):
 # ----------------------------------------------------------------------------- grouped fold
 def grouped_fold_touched(al, P, top_k, E, k_in, n_out, max_rank, n_tab, n_ad, ra, row_offset, row_end, cap,
                          x_gather, x_rows):
-    """lora_shrink_kernel (one workgroup per 16-row sub-tile from base16 = row_offset rounded down to
-    16) and lora_expand_fold_kernel (64-row tiles x 256 columns, a wave per 64 columns of all four
-    16-row sub-tiles): only
-    rows inside the window and the expert span are read through sorted_ids; active rows read x,
-    write and read xa at r - row_offset, read and write base; A_e rows < max_rank, B_e rows < n_out."""
+    """lora_shrink_kernel and lora_expand_fold_kernel over the window's 64-row tiles from base16 =
+    row_offset rounded down to 16 (every workgroup first stages the offsets and, when n_ad * n_tab <=
+    4096, every adapter's table entries of the experts below n_tab, to take the tiles of adapted
+    experts first; each tile is then cut into 16-row sub-tiles, the shrink taking a 32-row half per
+    workgroup): only rows inside the window and the expert span are read through sorted_ids; folded
+    rows read their x row, write and read xa at r - row_offset, read and write base; x row 0 and xa
+    row 0 stand in for the rows of a sub-tile that are not folded; A_e rows < max_rank, B_e rows <
+    n_out."""
     max_pad = len(al["sorted_ids"])
     sid, off = al["sorted_ids"], al["offsets"]
+    yield "offsets", E, E + 1
+    if n_ad * n_tab <= 4096:
+        for a in range(n_ad):
+            for e in range(min(n_tab, E)):
+                yield "table", a * n_tab + e, n_ad * n_tab
     base16 = row_offset // 16 * 16
     for sub0 in range(base16, row_end, 16):
-        yield "offsets", E, E + 1
         if off[0] > sub0 or off[E] <= sub0:
             continue
         e = max(i for i in range(E) if off[i] <= sub0)
         if e >= n_tab:
             continue
         span_end = int(off[e + 1])
+        yield "x", k_in - 1, x_rows * k_in              # row 0: the rows that are not folded
+        yield "xa", max_rank - 1, cap * max_rank
         for m in range(16):
             r = sub0 + m
             if r < row_offset or r >= row_end or r >= span_end:
