@@ -147,8 +147,9 @@ moe_status moe_align(const int32_t* topk_ids, int64_t num_pairs, int32_t num_exp
  * capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, results and
  * error behaviour as moe_align, minus workspace/workspace_bytes: the per-chunk histogram table
  * lives in a static device array of the library (1 MiB per GPU, 2^18 int32 cells, held until the
- * process ends).  ceil(num_pairs / 2048) * num_experts must not exceed 2^18 (for example 2^21
- * pairs at 256 experts); above that the call returns MOE_EUNSUPPORTED before anything is enqueued.
+ * process ends).  Batches of more than 2048 pairs are cut into chunks of 512 pairs, and
+ * ceil(num_pairs / 512) * num_experts must not exceed 2^18 (for example 2^19 pairs at 256 experts,
+ * 2^21 at 64); above that the call returns MOE_EUNSUPPORTED before anything is enqueued.
  * The call allocates nothing.  Every call on one GPU uses that GPU's one table and overwrites the
  * cells it reads, so calls ordered on one stream are independent, while calls that overlap on one
  * GPU (concurrent streams) race.  The first call on a device looks up the table's address; make it
@@ -160,7 +161,7 @@ moe_status moe_align_noalloc(const int32_t* topk_ids, int64_t num_pairs, int32_t
 /* A1+A2 — moe_route followed by moe_align on its topk_ids, with the same
  * arguments, results and error behaviour as the two calls (topk_ids is both the
  * routing output and the alignment input; num_pairs = num_tokens*top_k).  When
- * the pairs fit one alignment chunk (num_pairs <= 2048, decode batches) both
+ * the pairs fit one alignment workgroup (num_pairs <= 2048, decode batches) both
  * steps run in one single-workgroup launch; otherwise it enqueues the launches
  * of the two calls.  num_tokens == 0 aligns zero pairs (fills the sentinels). */
 moe_status moe_route_align(const float* logits, int32_t num_tokens, int32_t num_experts, int32_t top_k,

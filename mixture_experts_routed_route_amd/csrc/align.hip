@@ -2,7 +2,9 @@
 // moe_build_pairs_by_token, moe_align_block_size_pair_ids): a stable counting sort.
 //
 // The pairs are cut into chunks of kChunk ids; one 256-thread workgroup owns a chunk.  When
-// all pairs fit one chunk (decode batches), step 1 is folded into step 2: one launch.
+// all pairs fit the kChunkOne ids one workgroup can hold (decode batches), step 1 is folded into
+// step 2: one launch.  Otherwise the chunks are small (512 ids), so that even a mid-size batch
+// spreads its serial per-workgroup work (table sums, scan, fills, two passes) over many workgroups.
 //   1. align_count: each workgroup builds its chunk's expert histogram in LDS and
 //      writes it to the workspace row ws[chunk][0..E).
 //   2. align_scatter: each workgroup reads the whole [chunks, E] table, derives the
@@ -24,8 +26,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kIters = 8;                            // 64-pair steps per wave
-constexpr int kChunk = kThreads * kIters;            // pairs per workgroup
+constexpr int kIters = 2;                            // 64-pair steps per wave, several chunks
+constexpr int kChunk = kThreads * kIters;            // pairs per workgroup, several chunks
+constexpr int kItersOne = 8;                         // 64-pair steps per wave, one workgroup
+constexpr int kChunkOne = kThreads * kItersOne;      // pairs one workgroup aligns alone
 constexpr int kMaxE = 256;
 
 __global__ __launch_bounds__(kThreads) void align_count_kernel(const int32_t* __restrict__ ids, int P, int E,
@@ -58,10 +62,11 @@ __device__ __forceinline__ uint64_t peer_mask(int key, bool active) {
     return m;
 }
 
-// SINGLE: all pairs fit one chunk (G == 1); the workgroup builds the histogram itself, so the
-// alignment is one launch with no workspace round trip.  g = this workgroup's chunk.  NWAVES:
-// waves of the workgroup (4, or 16 in the fused route+align kernel); pairs are held by the first
-// kWaves waves only, the others take part in the scan, the fills and the barriers.
+// SINGLE: all pairs fit one workgroup (at most kChunkOne); the workgroup builds the histogram
+// itself, so the alignment is one launch with no workspace round trip.  Otherwise g = this
+// workgroup's chunk of kChunk pairs.  NWAVES: waves of the workgroup (4, or 16 in the fused
+// route+align kernel); pairs are held by the first kWaves waves only, the others take part in the
+// scan, the fills and the barriers.
 template <bool SINGLE, int NWAVES = kWaves>
 __device__ __forceinline__ void align_scatter_body(
     const int32_t* __restrict__ ids, int P, int E, int bs, const int32_t* __restrict__ ws, int G,
@@ -76,13 +81,15 @@ __device__ __forceinline__ void align_scatter_body(
     static_assert(SINGLE || NWAVES == kWaves, "several chunks: 4 waves per workgroup");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int ITERS = SINGLE ? kItersOne : kIters;  // 64-pair steps per wave
+    constexpr int CHUNK = kWaves * 64 * ITERS;
 
     // this wave's run of pairs, loaded once (expert id, or -1 past the end / out of range); waves
-    // past the first kWaves start past kChunk >= P and hold none
-    const int run0 = g * kChunk + wave * (64 * kIters);
-    int e_reg[kIters];
+    // past the first kWaves start past CHUNK >= P and hold none
+    const int run0 = g * CHUNK + wave * (64 * ITERS);
+    int e_reg[ITERS];
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
+    for (int it = 0; it < ITERS; ++it) {
         const int p = run0 + it * 64 + lane;
         const int e = p < P ? ids[p] : -1;
         e_reg[it] = (e >= 0 && e < E) ? e : -1;
@@ -94,14 +101,27 @@ __device__ __forceinline__ void align_scatter_body(
         for (int e = tid; e < E; e += NT) s_cnt[e] = 0;
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < kIters; ++it)
+        for (int it = 0; it < ITERS; ++it)
             if (e_reg[it] >= 0) atomicAdd(&s_cnt[e_reg[it]], 1);
         __syncthreads();
         if (tid < E) tot = s_cnt[tid];
         __syncthreads();
     } else {
         if (tid < E) {
-            for (int c = 0; c < G; ++c) {
+            // eight chunks' counts per round, loaded together: one memory round trip per eight
+            // chunks instead of one per chunk
+            int c = 0;
+            for (; c + 8 <= G; c += 8) {
+                int v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = ws[static_cast<size_t>(c + u) * E + tid];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    before += (c + u < g) ? v[u] : 0;
+                    tot += v[u];
+                }
+            }
+            for (; c < G; ++c) {
                 const int v = ws[static_cast<size_t>(c) * E + tid];
                 before += (c < g) ? v : 0;
                 tot += v;
@@ -154,7 +174,7 @@ __device__ __forceinline__ void align_scatter_body(
 
     // pass A: per-wave counts of each expert over the wave's run of pairs
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
+    for (int it = 0; it < ITERS; ++it) {
         if (run0 + it * 64 >= P) break;  // wave-uniform
         const int p = run0 + it * 64 + lane;
         const bool in = p < P;
@@ -178,7 +198,7 @@ __device__ __forceinline__ void align_scatter_body(
     __syncthreads();
     // pass B: place the pairs
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
+    for (int it = 0; it < ITERS; ++it) {
         if (run0 + it * 64 >= P) break;  // wave-uniform
         const int p = run0 + it * 64 + lane;
         const bool in = p < P;
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(
                                max_pad, blockIdx.x);
 }
 
-// Routing and alignment of a small batch (pairs fit one chunk, at most kFusedTokens tokens) in one
+// Routing and alignment of a small batch (at most kChunkOne pairs and kFusedTokens tokens) in one
 // workgroup and one launch: 16 waves route the tokens (one wave per token, up to four tokens per
 // wave interleaved), then the workgroup aligns the pairs they wrote.
 constexpr int kFusedWaves = 16;
@@ -217,7 +237,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void route_align_kernel(
     const float* __restrict__ logits, int T, int E, int top_k, int renorm, int32_t* topk_ids, float* topk_w,
     int bs, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad) {
-    __shared__ int s_ids[kChunk];  // the routed expert ids, handed to the alignment in LDS
+    __shared__ int s_ids[kChunkOne];  // the routed expert ids, handed to the alignment in LDS
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (T <= kFusedWaves) {
         if (wave < T) route_tokens<EPL, 1>(logits, wave, 0, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
@@ -269,12 +289,12 @@ int align_num_chunks(int64_t num_pairs) {
 hipError_t launch_align(const int32_t* topk_ids, int P, int E, int bs, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* total, int32_t* inv, int max_pad,
                         int32_t* workspace, hipStream_t s) {
-    const int G = align_num_chunks(P);
-    if (G == 1) {
+    if (P <= kChunkOne) {
         align_scatter_kernel<true><<<1, kThreads, 0, s>>>(topk_ids, P, E, bs, workspace, 1, counts, offsets,
                                                           sorted_ids, expert_ids, total, inv, max_pad);
         return hipGetLastError();
     }
+    const int G = align_num_chunks(P);
     align_count_kernel<<<G, kThreads, 0, s>>>(topk_ids, P, E, workspace);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -287,7 +307,7 @@ hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int 
                               int bs, int32_t* counts, int32_t* offsets, int32_t* sorted_ids, int32_t* expert_ids,
                               int32_t* total, int32_t* inv, int max_pad, int32_t* workspace, hipStream_t s) {
     const int P = T * top_k;
-    if (align_num_chunks(P) > 1 || T > kFusedTokens) {
+    if (P > kChunkOne || T > kFusedTokens) {
         hipError_t err = launch_route(logits, T, E, top_k, renorm, ids, w, s);
         if (err != hipSuccess) return err;
         return launch_align(ids, P, E, bs, counts, offsets, sorted_ids, expert_ids, total, inv, max_pad, workspace, s);

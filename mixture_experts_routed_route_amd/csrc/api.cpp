@@ -201,7 +201,7 @@ moe_status moe_align_noalloc(const int32_t* topk_ids, int64_t num_pairs, int32_t
     const int64_t cells = static_cast<int64_t>(moe::align_num_chunks(num_pairs)) * num_experts;
     if (cells > moe::kAlignScratchCells)
         return fail(MOE_EUNSUPPORTED,
-                    "%s: ceil(num_pairs/2048)*num_experts = %lld histogram cells exceed the static table of %lld "
+                    "%s: ceil(num_pairs/512)*num_experts = %lld histogram cells exceed the static table of %lld "
                     "(use moe_align with a workspace)",
                     who, static_cast<long long>(cells), static_cast<long long>(moe::kAlignScratchCells));
     REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);

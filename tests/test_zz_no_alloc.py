@@ -27,8 +27,8 @@ def _arrays(r, P):
             "total": r.total_padded.cpu().numpy(), "inv": r.inv_sorted.cpu().numpy()[:P]}
 
 
-# the first call uses 32 chunks x 128 experts of the table, the second 3 chunks x 64 experts;
-# the last case is one chunk (the table is not used at all)
+# the first call uses 128 chunks (of 512 pairs) x 128 experts of the table, the second 12 chunks x
+# 64 experts; the last case fits one workgroup (the table is not used at all)
 CASES = [
     (MoeConfig("big", T=8192, H=8, I=8, E=128, top_k=8, block_size=64, logits="zipf", seed=41),
      MoeConfig("small", T=1000, H=8, I=8, E=64, top_k=6, block_size=16, seed=42)),
@@ -59,8 +59,8 @@ def test_align_noalloc_refuses_oversized_table(dev):
     import torch
     import mixture_experts_routed_route_amd as m
     from mixture_experts_routed_route_amd._lib import MOE_EUNSUPPORTED
-    # 2^18 cells / 256 experts = 1024 chunks of 2048 pairs; one pair more needs 1025 chunks
-    P = 1024 * 2048 + 1
+    # 2^18 cells / 256 experts = 1024 chunks of 512 pairs; one pair more needs 1025 chunks
+    P = 1024 * 512 + 1
     ids = torch.zeros(P, dtype=torch.int32, device=dev)
     r = m.Routing.allocate(P, 1, 256, 16, dev)
     with pytest.raises(m.MoeError) as ei:
