@@ -8,18 +8,19 @@
 // Adapters (atlas MoeExpertRoute: adapter identity of a mixed batch comes from the per-row
 // moe_row_adapter, not from the tables): the tables hold n_adapters rows of n_tab entries, and a row
 // of token t uses row a = row_adapter[t] (0 without a map; < 0 or >= n_adapters folds nothing).  The
-// rows of one sub-tile may belong to several adapters: the kernels take the adapters present one at
-// a time (a uniform loop, usually one pass) and write only that adapter's rows in each pass.
+// rows of a tile may belong to several (expert, adapter) pairs: the kernels take the pairs present
+// one at a time (a uniform loop, usually one pass) and write only that pair's rows in each pass.
 // Two launches like the page: the shrink writes the bf16 xa scratch at the local row
 // r - row_offset, the expand reads it.  The expert of a row is read on the device from
-// expert_offsets (the row's span), so the grid is fixed by host scalars: a window is cut
-// into 16-row sub-tiles (block sizes are multiples of 16, so a sub-tile never straddles two
-// experts' spans), and sub-tiles of unadapted experts, sentinel rows and rows outside the
-// window do nothing.  Both stages use 16x16x32 bf16 MFMA with fp32 accumulation.  The shrink
-// gives each 16-row sub-tile a workgroup whose 4 waves split k_in.  The expand takes 64-row
-// tiles (four sub-tiles), each wave a column slab of all four, so that it reads B_e once per
-// tile; it stages its bf16 delta tile in LDS and then updates the base rows with 16-byte
-// coalesced accesses.
+// expert_offsets (the row's span), so the grid is fixed by host scalars: a window is cut into
+// 64-row tiles of four 16-row sub-tiles (block sizes are multiples of 16, so a sub-tile never
+// straddles two experts' spans), taken with the tiles of adapted experts first; sentinel rows,
+// rows of unadapted experts and rows outside the window do nothing.  Both stages use 16x16x32
+// bf16 MFMA with fp32 accumulation.  The shrink gives each half tile a workgroup whose 4 waves
+// split k_in and stream x and A_e through per-wave LDS rings; the expand gives each tile and 1024
+// columns a workgroup, folds straight from the accumulators (B_e is the MFMA's first operand, its
+// rows permuted so that a lane holds 8 consecutive columns of one row) and, for a tile of one
+// (expert, adapter) pair, runs a branch-free path that prefetches the next slab.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -32,14 +33,6 @@ constexpr int EXP_COLS = 64;  // expand: output columns per wave and slab
 #define MOE_LORA_EXP_SLABS 4
 #endif
 constexpr int EXP_SLABS = MOE_LORA_EXP_SLABS;  // expand: slabs of 4 * EXP_COLS columns per workgroup
-constexpr int MAX_RANK_BLOCKS = 8;  // max_rank <= 128
-
-// expert_offsets [E+1] (E <= 256) into LDS, so that each sub-tile's binary search over the
-// expert spans costs LDS reads instead of a chain of dependent global loads
-__device__ __forceinline__ void stage_offsets(const int32_t* off, int E, int* s_off) {
-    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = off[i];
-    __syncthreads();
-}
 
 // ------------------------------------------------------------------ active tiles first
 // A window's 64-row tiles (from base16) are taken in this order: the tiles that hold a row of an
