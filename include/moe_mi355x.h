@@ -257,9 +257,12 @@ moe_status moe_quantize_fp8(const uint16_t* x, int64_t rows, int32_t k, const in
  *            g[r, n] = a_scale[row] * scales[e, n] * sum_k a(row, k) W(n, k)
  *            (exact fp8 products, fp32 sums)
  * Sentinel and padding rows are not written.  op is MOE_OP_GATE_UP_SILU or
- * MOE_OP_DOWN; K % 16 == 0; N % 8 == 0.  workspace: as for moe_grouped_gemm (the
- * same buffer serves both; the tiles of a last partial round are split along K,
- * with results deterministic and equal to those without it up to fp32 order). */
+ * MOE_OP_DOWN; K % 16 == 0; N % 8 == 0.  As for the bf16 form, a (its rows:
+ * num_pairs/top_k for gate/up, max_pad for down) and each expert's [N, K] matrix
+ * must each be under 4 GiB (else MOE_EUNSUPPORTED).  workspace: as for
+ * moe_grouped_gemm (the same buffer serves both; the tiles of a last partial round
+ * are split along K, with results deterministic and equal to those without it up
+ * to fp32 order). */
 moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_scale, const moe_weight* w0,
                                 const moe_weight* w1, uint16_t* c, const int32_t* sorted_ids,
                                 const int32_t* expert_offsets, int64_t num_pairs, int32_t top_k,

@@ -541,6 +541,11 @@ moe_status moe_grouped_gemm_fp8(int32_t op, const uint8_t* a, const float* a_sca
         REQUIRE_PTR(who, w1->data);
         REQUIRE_PTR(who, w1->scales);
     }
+    // the kernel addresses a's rows and each expert matrix with 32-bit byte offsets
+    const int64_t a_rows = gate_up ? num_pairs / top_k : max_pad;
+    if (a_rows * k > INT64_C(0xffffffff) || static_cast<int64_t>(n) * k > INT64_C(0xffffffff))
+        return fail(MOE_EUNSUPPORTED, "%s: fp8 a (%lld rows) or an expert matrix (%d x %d) exceeds 4 GiB", who,
+                    static_cast<long long>(a_rows), n, k);
     return launched(who, moe::launch_gemm_fp8(
                              gate_up, a, a_scale, static_cast<const uint8_t*>(w0->data),
                              static_cast<const float*>(w0->scales), w1 ? static_cast<const uint8_t*>(w1->data) : nullptr,

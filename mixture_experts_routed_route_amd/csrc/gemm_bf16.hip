@@ -1,4 +1,4 @@
-// Grouped expert GEMM, bf16 weights, one launch for all experts (the grouped gate/up and
+// Grouped expert GEMM, bf16 (or fp8) weights, one launch for all experts (the grouped gate/up and
 // down roles of metrale cutlass/grouped.rs; gather through sorted ids and sentinel masking
 // as in ferrum-kernels triton_fused_moe.rs).
 //
@@ -49,6 +49,15 @@
 // Epilogue.  Straight from the accumulators, no LDS: neighbouring lanes (columns c, c+1) swap
 // one value through DPP so that each lane holds two adjacent columns of one row, converts them
 // with one v_cvt_pk_bf16_f32 and stores 4 bytes.
+//
+// fp8 form (FP8 = true; the quantised prefill variant, codes from gemm_fp8.hip).  A and the
+// weights are OCP E4M3 codes, one byte each, so the same tiles and LDS rows hold 128 k per
+// stage instead of 64: a row is still 128 bytes with the same swizzle, and a load instruction
+// still fills 1 KB.  The MFMA is the CDNA4 32x32x64 fp8 one (unit block scales), whose operand is
+// two 16-byte chunks of a row; A and B take the same lane -> k map, so every product pairs the
+// same k.  Its 32-byte fragments do not fit twice beside the accumulators of an 8-wave tile, so
+// there a wave reads each k-step's fragments just before its MFMAs.  The epilogue multiplies by
+// the row's activation scale and the column's weight scale before SiLU * up.
 #include <type_traits>
 
 #include "device_common.h"
@@ -70,6 +79,9 @@ constexpr int BP = 256;
 #ifndef MOE_GEMM_A_LATE
 #define MOE_GEMM_A_LATE 1  // asymmetric issue: activation-row loads of a stage issued at this k-step
 #endif
+#ifndef MOE_FP8_A_LATE
+#define MOE_FP8_A_LATE 1  // the same for the fp8 form (two k-steps per stage)
+#endif
 #ifndef MOE_GEMM_ASYM
 #define MOE_GEMM_ASYM 1  // 8 waves, 2 stages: waves 0-3 issue all of a stage's loads
 #endif
@@ -81,16 +93,18 @@ constexpr int BP = 256;
 #endif
 constexpr int kMaxE = 256;
 
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW>
+// BK: k per stage in elements of ES bytes (bf16: 2, fp8: 1); an LDS row is BK * ES bytes.
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int ES = 2>
 struct Cfg {
     static constexpr int NT = 64 * NW;                  // threads
     static constexpr int WAVES_M = NW / 2;              // wave grid WAVES_M x 2
-    static constexpr int CPR = BK / 8;                  // 16-byte chunks per LDS row
-    static constexpr int RP = 256 / (BK * 2);           // LDS rows per 256-byte line of the 64 banks
+    static constexpr int CE = 16 / ES;                  // elements per 16-byte chunk
+    static constexpr int CPR = BK / CE;                 // 16-byte chunks per LDS row
+    static constexpr int RP = 256 / (BK * ES);          // LDS rows per 256-byte line of the 64 banks
     static constexpr int A_ELEMS = BM * BK;
     static constexpr int B_ELEMS = BP * BK;
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-    static constexpr int ROWS_PER_INST = 1024 / (BK * 2);  // rows one wave-wide 1 KB load fills
+    static constexpr int ROWS_PER_INST = 1024 / (BK * ES);  // rows one wave-wide 1 KB load fills
     static constexpr int A_INST = BM / ROWS_PER_INST / NW;  // load instructions per wave per stage
     static constexpr int B_INST = BP / ROWS_PER_INST / NW;
     static constexpr int LOADS = A_INST + B_INST;
@@ -116,28 +130,46 @@ __device__ __forceinline__ void decode_tile(int L, int gm, int m_real, int n_til
     m_t = band * gm + (in_band - n_t * gm_b);
 }
 
+// Element type of A and the weights: bf16 bits, or OCP E4M3 codes in the fp8 form.
+template <bool FP8>
+using Elem = std::conditional_t<FP8, uint8_t, uint16_t>;
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));  // a 32-byte fp8 MFMA operand
+
+// fp8 form: dequantisation scales of the activation rows ([rows of A]) and of the weight rows
+// ([E, N], one per output channel, for w0 and w1)
+struct Fp8Scales {
+    const float* a;
+    const float* w0;
+    const float* w1;
+};
+
 // LORA: 0 no gate/up LoRA; 1 one adapter (every folded row is adapter 0); 2 several adapters (the
 // rows of one fragment may belong to different adapters: one pass per adapter present).  The
 // one-adapter form is the common case and keeps the lean epilogue, which the loop of the general
 // form would cost registers in the main loop.
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                          const uint16_t* __restrict__ W0,
-                                                          const uint16_t* __restrict__ W1,
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0, bool FP8 = false>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* __restrict__ A,
+                                                          const Elem<FP8>* __restrict__ W0,
+                                                          const Elem<FP8>* __restrict__ W1,
                                                           uint16_t* __restrict__ C,
                                                           const int32_t* __restrict__ sorted_ids,
                                                           const int32_t* __restrict__ offsets, int P, int top_k,
                                                           int E, int N, int K, int max_pad, int n_tiles,
                                                           float* __restrict__ sk_part, int32_t* __restrict__ sk_cnt,
-                                                          int sk_on, int a_tok, GateUpLora lora) {
+                                                          int sk_on, int a_tok, GateUpLora lora, Fp8Scales f8) {
     static_assert(!LORA || GATE_UP, "the LoRA epilogue is the gate/up one");
-    using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
+    static_assert(!(LORA && FP8), "no LoRA epilogue in the fp8 form");
+    using TE = Elem<FP8>;
+    constexpr int ES = sizeof(TE);
+    using F = Cfg<GATE_UP, BM, BK, STAGES, NW, ES>;
     constexpr int NT = F::NT;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[F::SMEM];
+    constexpr int CE = F::CE;
+    __shared__ __attribute__((aligned(1024))) TE smem[F::SMEM];
     __shared__ int s_scan[NW];
     __shared__ int s_lo[kMaxE], s_hi[kMaxE], s_tb[kMaxE + 1];  // expert span, first row tile
     __shared__ int s_row[2][BM];                                  // A source row per tile row
     __shared__ int s_rad[LORA ? 2 : 1][LORA ? BM : 1];            // LoRA: adapter id per tile row (-1: none)
+    __shared__ float s_as[FP8 ? 2 : 1][FP8 ? BM : 1];             // fp8: dequantisation scale per tile row
     __shared__ int s_h[2];                                        // rows up to the last token
     __shared__ int s_arrived;                                     // split tile: the other side's count
 
@@ -240,6 +272,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 if (p >= 0 && p < P) src = (GATE_UP || a_tok) ? p / top_k : r;
             }
             s_row[buf][i] = src;
+            if constexpr (FP8) s_as[buf][i] = src >= 0 ? f8.a[src] : 0.f;
             if constexpr (LORA) {
                 // the token's adapter (atlas: a mixed batch's adapter comes from the per-row map); 0
                 // without a map; -1 for rows without a token or with an id outside [0, n_ad)
@@ -267,10 +300,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     const bool issuer = !ASYM || wave < NW / 2;
     const int lrow = lane / F::CPR;   // row within the instruction's block
     const int pc = lane % F::CPR;     // physical chunk this lane's 16 bytes land in
-    using Src = std::conditional_t<ASYM, uint32_t, const uint16_t*>;
+    using Src = std::conditional_t<ASYM, uint32_t, const TE*>;
     Src a_o[NBLK][F::A_INST], b_o[NBLK][F::B_INST];
-    const uint16_t* b_base0 = W0;     // the tile's expert matrices (uniform)
-    const uint16_t* b_base1 = W1;
+    const TE* b_base0 = W0;     // the tile's expert matrices (uniform)
+    const TE* b_base1 = W1;
     auto block_wave = [&](int j) __attribute__((always_inline)) { return wave + j * (NW / 2); };
     auto set_sources = [&](int bf, int e_, int r0_, int n0_) __attribute__((always_inline)) {
         b_base0 = W0 + static_cast<size_t>(e_) * N * K;
@@ -287,8 +320,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 // a row without a token reads a row that is always in bounds (token 0, or the
                 // tile's first sorted row r0 < max_pad); its results are never stored
                 const int srow = src >= 0 ? src : ((GATE_UP || a_tok) ? 0 : r0_);
-                if constexpr (ASYM) a_o[j][q] = (static_cast<uint32_t>(srow) * K + kc * 8) * 2;
-                else a_o[j][q] = A + static_cast<size_t>(srow) * K + kc * 8;
+                if constexpr (ASYM) a_o[j][q] = (static_cast<uint32_t>(srow) * K + kc * CE) * ES;
+                else a_o[j][q] = A + static_cast<size_t>(srow) * K + kc * CE;
             }
 #pragma unroll
             for (int q = 0; q < F::B_INST; ++q) {
@@ -297,10 +330,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 int n = GATE_UP ? n0_ + (row & (BP / 2 - 1)) : n0_ + row;
                 n = min(n, N - 1);  // columns past N are computed from a valid row and never stored
                 if constexpr (ASYM) {
-                    b_o[j][q] = (static_cast<uint32_t>(n) * K + kc * 8) * 2;
+                    b_o[j][q] = (static_cast<uint32_t>(n) * K + kc * CE) * ES;
                 } else {
-                    const uint16_t* bb = (GATE_UP && row >= BP / 2) ? b_base1 : b_base0;
-                    b_o[j][q] = bb + static_cast<size_t>(n) * K + kc * 8;
+                    const TE* bb = (GATE_UP && row >= BP / 2) ? b_base1 : b_base0;
+                    b_o[j][q] = bb + static_cast<size_t>(n) * K + kc * CE;
                 }
             }
         }
@@ -312,7 +345,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     auto stage_ptr = [&](int t) __attribute__((always_inline)) { return smem + ((sb + t) % STAGES) * F::STAGE_ELEMS; };
     // LDS byte addresses of the A and B parts of stage buffer 0 (scalar)
     const uint32_t lds_a0 = lds_u32(smem);
-    const uint32_t lds_b0 = lds_a0 + F::A_ELEMS * 2;
+    const uint32_t lds_b0 = lds_a0 + F::A_ELEMS * ES;
     // loads of segment stage t (K stage kbase + t) into its LDS buffer.  The stage's 16-byte
     // chunk of each lane is k0 + kc*8 with kc = swz_chunk(row, pc); only the stage that runs past
     // K (uniform test) recomputes kc to load zeros for k >= K.
@@ -320,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     auto issue_at = [&](int t, int kbase, int parts = 3) __attribute__((always_inline)) {  // 1: A rows, 2: B rows
         if (!issuer) return;
         const int k0 = (kbase + t) * BK;
-        const uint32_t sbuf = static_cast<uint32_t>((sb + t) % STAGES) * (F::STAGE_ELEMS * 2);
+        const uint32_t sbuf = static_cast<uint32_t>((sb + t) % STAGES) * (F::STAGE_ELEMS * ES);
         // B instruction q of block j: its 8 rows lie on one side of the gate/up boundary
         auto b_base = [&](int bw, int q) __attribute__((always_inline)) {
             const int row0 = (bw * F::B_INST + q) * F::ROWS_PER_INST;
@@ -358,7 +391,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                     const void* src;
                     if constexpr (ASYM) src = reinterpret_cast<const char*>(A + k0) + a_o[j][q];
                     else src = a_o[j][q] + k0;
-                    const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+                    const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * CE < K;
                     dma16(in ? src : static_cast<const void*>(kZero16), dst);
                 }
 #pragma unroll
@@ -369,16 +402,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                     const void* src;
                     if constexpr (ASYM) src = reinterpret_cast<const char*>(b_base(bw, q) + k0) + b_o[j][q];
                     else src = b_o[j][q] + k0;
-                    const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * 8 < K;
+                    const bool in = k0 + swz_chunk(row, pc, F::RP, F::CPR) * CE < K;
                     dma16(in ? src : static_cast<const void*>(kZero16), dst);
                 }
             }
         }
     };
-    // With the asymmetric issue and MOE_GEMM_A_LATE > 0, a stage's weight-panel loads (the long
-    // ones, from HBM) go out right after the barrier and its activation-row loads (mostly L2
-    // hits) at k-step MOE_GEMM_A_LATE, which halves the burst of loads landing in LDS meanwhile.
-    constexpr bool A_LATE = ASYM && MOE_GEMM_A_LATE > 0 && MOE_GEMM_A_LATE < BK / 16;
+    // MFMA k-steps per stage: 32x32x16 bf16 (16 k), or 32x32x64 fp8 (64 k)
+    constexpr int KK = FP8 ? BK / 64 : BK / 16;
+    // With the asymmetric issue and A_LATE_K > 0, a stage's weight-panel loads (the long ones,
+    // from HBM) go out right after the barrier and its activation-row loads (mostly L2 hits) at
+    // k-step A_LATE_K, which halves the burst of loads landing in LDS meanwhile.
+    constexpr int A_LATE_K = FP8 ? MOE_FP8_A_LATE : MOE_GEMM_A_LATE;
+    constexpr bool A_LATE = ASYM && A_LATE_K > 0 && A_LATE_K < KK;
     auto issue = [&](int t) __attribute__((always_inline)) { issue_at(t, kb, A_LATE ? 2 : 3); };
 
     const int wm = wave >> 1, wn = wave & 1;  // wave grid WAVES_M x 2
@@ -400,18 +436,39 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // every fragment starts on a multiple of 32 rows, so its swizzle depends on the lane only
     const int fswz = (fr / F::RP) % F::CPR;
 
-    constexpr int KK = BK / 16;  // 32x32x16 MFMA k-steps per stage (even)
-    bf16x8 fa[2][F::FI], fb[2][4];
+    using Frag = std::conditional_t<FP8, i32x8, bf16x8>;
+    // Fragment register sets: two (the next k-step's fragments are read while the current one's
+    // MFMAs run), or one for the 8-wave fp8 form, whose 32-byte fragments would not fit twice
+    // beside 128 accumulators in 256 registers; there the other wave of the SIMD covers the reads.
+    constexpr int NSET = (FP8 && NW == 8) ? 1 : 2;
+    Frag fa[NSET][F::FI], fb[NSET][4];
     // fragments of k-step kk of stage s into register set `set` (the first NF A fragments)
     auto read = [&](auto nf_c, int s, int kk, int set) __attribute__((always_inline)) {
         constexpr int NF = decltype(nf_c)::value;
         if constexpr (NF > 0) {
-            const uint16_t* st = stage_ptr(s);
-            const int cx = ((kk * 2 + fc) ^ fswz) << 3;
+            const TE* st = stage_ptr(s);
+            if constexpr (FP8) {
+                // a 32-byte operand: logical chunks c0 and c0 + 1 of the row (A and B take the
+                // same lane -> k map, so every product pairs the same k)
+                const int c0 = kk * 4 + fc * 2;
+                const int x0 = (c0 ^ fswz) * CE, x1 = ((c0 + 1) ^ fswz) * CE;
+                auto frag = [&](int off) __attribute__((always_inline)) {
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(st + off + x0);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(st + off + x1);
+                    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                };
 #pragma unroll
-            for (int i = 0; i < NF; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
+                for (int i = 0; i < NF; ++i) fa[set][i] = frag(a_off[i]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + cx);
+                for (int j = 0; j < 4; ++j) fb[set][j] = frag(b_off[j]);
+            } else {
+                const int cx = ((kk * 2 + fc) ^ fswz) << 3;
+#pragma unroll
+                for (int i = 0; i < NF; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + cx);
+            }
         }
     };
     auto mfma = [&](auto nf_c, int set) __attribute__((always_inline)) {
@@ -420,7 +477,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         for (int i = 0; i < NF; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+                if constexpr (FP8)  // E4M3 operands (format 0), unit block scales (127 = 2^0)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j],
+                                                                               0, 0, 0, 127, 0, 127);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     };
     // Stage t becomes readable: this thread's loads of t have landed (at most `ahead` later stages
     // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
@@ -445,19 +506,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
     // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
     // NF = A fragments of this wave that hold tokens; every wave still loads and meets the barriers.
     auto main_loop = [&](auto nf_c) __attribute__((always_inline)) {
-        ready(0);
-        read(nf_c, 0, 0, 0);
-        for (int s = 0; s < nseg; ++s) {
+        if constexpr (NSET == 2) {
+            ready(0);
+            read(nf_c, 0, 0, 0);
+            for (int s = 0; s < nseg; ++s) {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                if (A_LATE && kk == MOE_GEMM_A_LATE && s + 1 < nseg) issue_at(s + 1, kb, 1);
-                if (kk + 1 < KK) {
-                    read(nf_c, s, kk + 1, (kk + 1) & 1);
-                } else if (s + 1 < nseg) {
-                    ready(s + 1);
-                    read(nf_c, s + 1, 0, 0);
+                for (int kk = 0; kk < KK; ++kk) {
+                    if (A_LATE && kk == A_LATE_K && s + 1 < nseg) issue_at(s + 1, kb, 1);
+                    if (kk + 1 < KK) {
+                        read(nf_c, s, kk + 1, (kk + 1) & 1);
+                    } else if (s + 1 < nseg) {
+                        ready(s + 1);
+                        read(nf_c, s + 1, 0, 0);
+                    }
+                    mfma(nf_c, kk & 1);
                 }
-                mfma(nf_c, kk & 1);
+            }
+        } else {
+            // one set: each k-step's reads, then its MFMAs; the stage barrier opens each stage
+            for (int s = 0; s < nseg; ++s) {
+                ready(s);
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    if (A_LATE && kk == A_LATE_K && s + 1 < nseg) issue_at(s + 1, kb, 1);
+                    read(nf_c, s, kk, 0);
+                    mfma(nf_c, 0);
+                }
             }
         }
     };
@@ -645,6 +719,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
         // value so that each lane stores two adjacent bf16 columns of one row as 4 bytes
         const bool odd = (lane & 1) != 0;
         const int ccol = n0 + (fr & ~1);
+        constexpr int NO = GATE_UP ? 2 : 4;  // output column blocks of this wave
+        // fp8: the weight scales of this lane's accumulator column in each block (gate, up)
+        float wsc[NO], wsu[NO];
+        if constexpr (FP8) {
+#pragma unroll
+            for (int j = 0; j < NO; ++j) {
+                const int cj = min(n0 + (GATE_UP ? wn * 64 : wn * 128) + j * 32 + fr, N - 1);
+                wsc[j] = f8.w0[static_cast<size_t>(e) * N + cj];
+                if constexpr (GATE_UP) wsu[j] = f8.w1[static_cast<size_t>(e) * N + cj];
+            }
+        }
         if (store)
 #pragma unroll
         for (int i = 0; i < F::FI; ++i)
@@ -654,16 +739,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const uint16_t* _
                 const int row_l = rl + (odd ? 1 : 0);
                 const bool ok = s_row[buf][row_l] >= 0;
                 uint16_t* crow = C + static_cast<size_t>(r0 + row_l) * N;
-                constexpr int NJ = GATE_UP ? 2 : 4;
+                float sa0 = 1.f, sa1 = 1.f;  // fp8: the rows' activation scales
+                if constexpr (FP8) { sa0 = s_as[buf][rl]; sa1 = s_as[buf][rl + 1]; }
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
+                for (int j = 0; j < NO; ++j) {
                     float h0, h1;  // values v (row rl) and v+1 (row rl+1) of this lane's column
-                    if (GATE_UP) {
-                        h0 = silu_mul(acc[i][j][v], acc[i][j + 2][v]);
-                        h1 = silu_mul(acc[i][j][v + 1], acc[i][j + 2][v + 1]);
+                    float g0 = acc[i][j][v], g1 = acc[i][j][v + 1];
+                    if constexpr (FP8) { g0 = g0 * sa0 * wsc[j]; g1 = g1 * sa1 * wsc[j]; }
+                    if constexpr (GATE_UP) {
+                        float u0 = acc[i][j + 2][v], u1 = acc[i][j + 2][v + 1];
+                        if constexpr (FP8) { u0 = u0 * sa0 * wsu[j]; u1 = u1 * sa1 * wsu[j]; }
+                        h0 = silu_mul(g0, u0);
+                        h1 = silu_mul(g1, u1);
                     } else {
-                        h0 = acc[i][j][v];
-                        h1 = acc[i][j][v + 1];
+                        h0 = g0;
+                        h1 = g1;
                     }
                     const float send = odd ? h0 : h1;
                     const float got = __int_as_float(__builtin_amdgcn_update_dpp(
@@ -706,12 +796,12 @@ constexpr int64_t kSkPartBytes = 512LL * 2 * 64 * 4;    // largest partial: 512 
 constexpr int64_t kSkWorkspaceBytes = kSkCounterBytes + kSkMaxGrid * kSkPartBytes;
 static_assert(kSkMaxGrid * 4 <= kSkCounterBytes, "split-tail counters overflow their area");
 
-template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0>
-hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
+template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0, bool FP8 = false>
+hipError_t launch_cfg(const Elem<FP8>* a, const Elem<FP8>* w0, const Elem<FP8>* w1, uint16_t* c,
                       const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N, int K,
                       int max_pad, void* ws, int64_t ws_bytes, int a_tok, hipStream_t s,
-                      const GateUpLora& lora = GateUpLora{}) {
-    using F = Cfg<GATE_UP, BM, BK, STAGES, NW>;
+                      const GateUpLora& lora = GateUpLora{}, const Fp8Scales& f8 = Fp8Scales{}) {
+    using F = Cfg<GATE_UP, BM, BK, STAGES, NW, sizeof(Elem<FP8>)>;
     static_assert(F::NT * F::FI * 64 * 4 <= kSkPartBytes, "partial accumulators larger than their workspace slot");
     const int n_tiles = (N + F::NCOL - 1) / F::NCOL;
     hipError_t err = hipSuccess;
@@ -734,8 +824,9 @@ hipError_t launch_cfg(const uint16_t* a, const uint16_t* w0, const uint16_t* w1,
     }
     int32_t* cnt = sk ? static_cast<int32_t*>(ws) : nullptr;
     float* part = sk ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSkCounterBytes) : nullptr;
-    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW, LORA><<<static_cast<int>(grid), F::NT, 0, s>>>(
-        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0, a_tok, lora);
+    gemm_bf16_kernel<GATE_UP, BM, BK, STAGES, NW, LORA, FP8><<<static_cast<int>(grid), F::NT, 0, s>>>(
+        a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, n_tiles, part, cnt, sk ? 1 : 0, a_tok, lora,
+        f8);
     return hipGetLastError();
 }
 
@@ -765,6 +856,21 @@ hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const
     const int a_tok = op == kOpGather ? 1 : 0;
     if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, a_tok, s);
     return launch_cfg<false, 128, 64, 3, 4>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, a_tok, s);
+}
+
+hipError_t launch_gemm_fp8(bool gate_up, const uint8_t* a, const float* a_scale, const uint8_t* w0,
+                           const float* ws0, const uint8_t* w1, const float* ws1, uint16_t* c,
+                           const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,
+                           int K, int max_pad, void* ws, int64_t ws_bytes, hipStream_t s) {
+    // the bf16 tiles in bytes: a stage is 128 k of 1-byte codes, one 128-byte LDS row per tile row
+    const Fp8Scales f8{a_scale, ws0, ws1};
+    const bool big = static_cast<long long>(P) >= static_cast<long long>(MOE_GEMM_BIG_ROWS) * E;
+    if (gate_up) {
+        if (big) return launch_cfg<true, 256, 128, 2, 8, 0, true>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, GateUpLora{}, f8);
+        return launch_cfg<true, 128, 128, 3, 4, 0, true>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, GateUpLora{}, f8);
+    }
+    if (big) return launch_cfg<false, 256, 128, 2, 8, 0, true>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 0, s, GateUpLora{}, f8);
+    return launch_cfg<false, 128, 128, 3, 4, 0, true>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 0, s, GateUpLora{}, f8);
 }
 
 }  // namespace moe

@@ -76,10 +76,11 @@ hipError_t launch_lora_shrink(const uint16_t* x, const uint64_t* a_tab, const ui
                               int max_rank, const int32_t* offsets, int E, const int32_t* sorted_ids, int P,
                               int top_k, const int32_t* row_adapter, uint16_t* xa, int64_t row_offset,
                               int64_t row_end, int x_gather, hipStream_t s);
-// gemm_fp8.hip: per-row fp8 quantisation of bf16 rows (only real sorted rows with sorted_ids), and
-// the fp8 grouped GEMM (gate/up + SiLU, or down) with per-row and per-channel scales
+// gemm_fp8.hip: per-row fp8 quantisation of bf16 rows (only real sorted rows with sorted_ids)
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int K, const int32_t* sorted_ids, int P,
                                uint8_t* q, float* scale, hipStream_t s);
+// gemm_bf16.hip, fp8 form: the grouped GEMM (gate/up + SiLU, or down) on E4M3 codes with per-row
+// and per-channel scales (ws: the same optional split-tail workspace)
 hipError_t launch_gemm_fp8(bool gate_up, const uint8_t* a, const float* a_scale, const uint8_t* w0,
                            const float* ws0, const uint8_t* w1, const float* ws1, uint16_t* c,
                            const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,

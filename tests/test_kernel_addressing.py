@@ -1,6 +1,6 @@
 """CPU models of the addressing of every kernel that computes addresses from device-resident ids
-(besides the bf16 GEMM, modelled in test_gemm_addressing): the int4 GEMM, the fp8 GEMM (tile heights
-and split tail), the gate/up LoRA epilogue of the bf16 GEMM, the grouped fold's shrink and expand,
+(besides the bf16 GEMM, modelled in test_gemm_addressing): the int4 GEMM, the fp8 form of the bf16
+GEMM (byte addressing and scales; its schedule is the bf16 one), the gate/up LoRA epilogue of the bf16 GEMM, the grouped fold's shrink and expand,
 and the gather fold.  Each model restates the kernel's integer arithmetic and yields every
 (buffer, index, extent) a launch can address; the tests show all of them in bounds on the routings of
 the workloads and on tight routings whose padded total reaches the sorted capacity.  CPU only."""
@@ -69,80 +69,49 @@ def int4_touched(al, P, top_k, E, N, K, G, bs, gate_up, a_tok=False):
 
 
 # ----------------------------------------------------------------------------- fp8 GEMM
-def fp8_touched(al, P, top_k, E, N, K, BM, NW, slots, gate_up, split_max_rounds=4, min_stages=8):
-    """gemm_fp8_kernel: row tiles of BM rows per expert span; logical tile L = n_t * m_real + m_t;
-    XCD x takes [x*Tw/8, (x+1)*Tw/8) of the first Tw tiles; with a workspace and fewer than
-    split_max_rounds rounds, the rest = T mod slots tiles are cut along K into pieces that run on the
-    workgroups past each XCD's share.  Yields A rows, a_scale entries, weight rows, channel scales,
-    C rows, partial slots and tile counters."""
+def fp8_touched(al, P, top_k, E, N, K, BM, gate_up):
+    """The fp8 form of gemm_bf16_kernel: the bf16 tiles in bytes (BM-row tiles of each expert span x
+    a 256-row weight panel; the persistent schedule and split tail are the bf16 ones, modelled in
+    test_gemm_addressing).  Per tile: the sorted ids, the rows' activation scales (s_as), the A rows
+    (a row without a token reads token 0 or the tile's first sorted row), the panel's weight rows
+    (clamped to N - 1), the channel scales of the wave columns (clamped to N - 1) and the stored C
+    rows.  A and W are 1-byte codes, so the last byte of a row is at row * K + K - 1."""
     max_pad = len(al["sorted_ids"])
     sid = al["sorted_ids"]
     T_tok = P // top_k
     lo, hi = _spans(al, E, max_pad)
-    nt = [-(-(hi[e] - lo[e]) // BM) for e in range(E)]
-    tb = np.concatenate([[0], np.cumsum(nt)]).astype(int)
-    m_real = int(tb[-1])
-    BP = BM
+    BP = 256
     ncol = BP // 2 if gate_up else BP
-    n_tiles = -(-N // ncol)
-    nk = -(-K // 128)
-    m_bound = -(-max_pad // BM) + E
-    grid = ((m_bound * n_tiles + 7) // 8 + 1 + (slots + 7) // 8) * 8
-    T = m_real * n_tiles
-    Tw, split = T, 1
-    split_on = slots > 0 and m_bound * n_tiles < split_max_rounds * slots
-    if split_on and T < split_max_rounds * slots:
-        rest = T % slots
-        s_max = min(slots // rest, nk // min_stages) if rest > 0 else 1
-        if s_max >= 2:
-            Tw, split = T - rest, s_max
-    covered = np.zeros((T, nk), np.int32)
-    for bid in range(grid):
-        xcd, slot = bid & 7, bid >> 3
-        lo_x = Tw * xcd // 8
-        share = Tw * (xcd + 1) // 8 - lo_x
-        if slot < share:
-            L, kb, ke = lo_x + slot, 0, nk
-        else:
-            piece = (slot - share) * 8 + xcd
-            if piece >= (T - Tw) * split:
-                continue
-            tail_u = piece // split
-            j = piece - tail_u * split
-            L, kb, ke = Tw + tail_u, j * nk // split, (j + 1) * nk // split
-            yield "partial", piece, slots
-            yield "counter", tail_u, 1024
-            yield "partial", tail_u * split + split - 1, slots
-        assert 0 <= L < T
-        covered[L, kb:ke] += 1
-        n_t, m_t = L // m_real, L % m_real
-        e = max(i for i in range(E) if tb[i] <= m_t)
-        r0 = lo[e] + (m_t - tb[e]) * BM
-        r_end = min(r0 + BM, hi[e])
-        n0 = n_t * ncol
-        rows = []
-        for t in range(BM):
-            r = r0 + t
-            src = -1
-            if r < r_end:
-                yield "sorted_ids", r, max_pad
-                p = int(sid[r])
-                if 0 <= p < P:
-                    src = p // top_k if gate_up else r
-                    yield "a_scale", src, T_tok if gate_up else max_pad
-            rows.append(src)
-        for t in range(BM):
-            srow = rows[t] if rows[t] >= 0 else (0 if gate_up else r0)
-            yield "A", srow * K + K - 1, (T_tok if gate_up else max_pad) * K
-        for prow in range(BP):
-            n = min((n0 + (prow & (BP // 2 - 1))) if gate_up else (n0 + prow), N - 1)
-            yield "W", (e * N + n) * K + K - 1, E * N * K
-        for c in range(n0, n0 + ncol):
-            yield "w_scale", e * N + min(c, N - 1), E * N
-        for t in range(BM):
-            if rows[t] >= 0:
-                yield "C", (r0 + t) * N + min(n0 + ncol, N) - 1, max_pad * N
-    assert (covered == 1).all(), "every (tile, K stage) once"
+    a_rows = T_tok if gate_up else max_pad
+    for e in range(E):
+        for t in range(-(-(hi[e] - lo[e]) // BM)):
+            r0 = lo[e] + t * BM
+            r_end = min(r0 + BM, hi[e])
+            rows = []
+            for i in range(BM):
+                r = r0 + i
+                src = -1
+                if r < r_end:
+                    yield "sorted_ids", r, max_pad
+                    p = int(sid[r])
+                    if 0 <= p < P:
+                        src = p // top_k if gate_up else r
+                        yield "a_scale", src, a_rows
+                rows.append(src)
+                srow = src if src >= 0 else (0 if gate_up else r0)
+                yield "A", srow * K + K - 1, a_rows * K
+            for n0 in range(0, -(-N // ncol) * ncol, ncol):
+                for prow in range(BP):
+                    n = min((n0 + (prow & (BP // 2 - 1))) if gate_up else (n0 + prow), N - 1)
+                    yield "W", (e * N + n) * K + K - 1, E * N * K
+                for wn in range(2):
+                    for j in range(2 if gate_up else 4):
+                        for fr in range(32):
+                            cj = min(n0 + (wn * 64 if gate_up else wn * 128) + j * 32 + fr, N - 1)
+                            yield "w_scale", e * N + cj, E * N
+                for i in range(BM):
+                    if rows[i] >= 0:
+                        yield "C", (r0 + i) * N + min(n0 + ncol, N) - 1, max_pad * N
 
 
 # ----------------------------------------------------------------------------- gate/up LoRA epilogue
@@ -305,15 +274,13 @@ def test_int4_gemm_addresses_in_bounds(case):
 
 
 @pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
-@pytest.mark.parametrize("BM,NW", [(256, 8), (128, 4)])
-def test_fp8_gemm_addresses_in_bounds(case, BM, NW):
+@pytest.mark.parametrize("BM", [256, 128])
+def test_fp8_gemm_addresses_in_bounds(case, BM):
     name, top_k, E, bs, ids = case
     al = oracle.align(ids, E, bs)
     P = ids.size
-    for gate_up, N, K in ((True, 264, 2048), (False, 136, 1024)):
-        for slots in (0, 256, 512):   # no workspace; one or two workgroups per compute unit
-            assert _check(fp8_touched(al, P, top_k, E, N, K, BM, NW, slots, gate_up),
-                          f"{name} fp8 BM={BM} slots={slots}") > 0
+    for gate_up, N, K in ((True, 264, 2048), (False, 136, 1040)):
+        assert _check(fp8_touched(al, P, top_k, E, N, K, BM, gate_up), f"{name} fp8 BM={BM}") > 0
 
 
 @pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
