@@ -17,6 +17,10 @@ namespace {
 // ------------------------------------------------------------------ per-row quantisation
 constexpr int kQThreads = 256;
 
+// NC > 0: each thread holds its NC 16-byte chunks of the row in registers (rows of at most
+// NC * 2048 elements), all loaded at once, so the row is read once and every load of a workgroup is
+// in flight together; NC == 0: any K, the row read twice (the second pass mostly from L2).
+template <int NC>
 __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, float* __restrict__ scale,
                                                                  const int32_t* __restrict__ sorted_ids, int P,
@@ -28,14 +32,40 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t*
         if (p < 0 || p >= P) return;  // uniform over the workgroup
     }
     const uint16_t* xr = x + r * K;
-    float amax = 0.f;
-    for (int c = threadIdx.x * 8; c < K; c += kQThreads * 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    auto absmax8 = [](float m, const u32x4& v) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
+            m = fmaxf(m, fabsf(__uint_as_float(v[i] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
         }
+        return m;
+    };
+    // codes of 8 elements, element 0 in the lowest byte
+    auto codes8 = [](const u32x4& v, float f) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(v[2 * h] << 16) * f,
+                                                     __uint_as_float(v[2 * h] & 0xffff0000u) * f, 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(v[2 * h + 1] << 16) * f,
+                                                 __uint_as_float(v[2 * h + 1] & 0xffff0000u) * f, pk, true);
+            w[h] = static_cast<uint32_t>(pk);
+        }
+        return make_uint2(w[0], w[1]);
+    };
+    float amax = 0.f;
+    u32x4 v[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = (threadIdx.x + i * kQThreads) * 8;
+            v[i] = c < K ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) amax = absmax8(amax, v[i]);
+    } else {
+        for (int c = threadIdx.x * 8; c < K; c += kQThreads * 8)
+            amax = absmax8(amax, *reinterpret_cast<const u32x4*>(xr + c));
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -45,19 +75,15 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t*
     const float f = amax > 0.f ? 448.0f / amax : 1.0f;
     if (threadIdx.x == 0) scale[r] = amax > 0.f ? amax / 448.0f : 1.0f;
     uint8_t* qr = q + r * K;
-    for (int c = threadIdx.x * 8; c < K; c += kQThreads * 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-        uint32_t w[2];
+    if constexpr (NC > 0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // codes of elements 4h .. 4h+3, element 4h in the lowest byte
-            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(v[2 * h] << 16) * f,
-                                                     __uint_as_float(v[2 * h] & 0xffff0000u) * f, 0, false);
-            pk = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(v[2 * h + 1] << 16) * f,
-                                                 __uint_as_float(v[2 * h + 1] & 0xffff0000u) * f, pk, true);
-            w[h] = static_cast<uint32_t>(pk);
+        for (int i = 0; i < NC; ++i) {
+            const int c = (threadIdx.x + i * kQThreads) * 8;
+            if (c < K) *reinterpret_cast<uint2*>(qr + c) = codes8(v[i], f);
         }
-        *reinterpret_cast<uint2*>(qr + c) = make_uint2(w[0], w[1]);
+    } else {
+        for (int c = threadIdx.x * 8; c < K; c += kQThreads * 8)
+            *reinterpret_cast<uint2*>(qr + c) = codes8(*reinterpret_cast<const u32x4*>(xr + c), f);
     }
 }
 
@@ -66,7 +92,13 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(const uint16_t*
 hipError_t launch_quantize_fp8(const uint16_t* x, int64_t rows, int K, const int32_t* sorted_ids, int P,
                                uint8_t* q, float* scale, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    quantize_fp8_kernel<<<static_cast<unsigned>(rows), kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
+    const int chunks = (K + kQThreads * 8 - 1) / (kQThreads * 8);  // 16-byte chunks per thread
+    const dim3 g(static_cast<unsigned>(rows));
+    if (chunks <= 1) quantize_fp8_kernel<1><<<g, kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
+    else if (chunks <= 2) quantize_fp8_kernel<2><<<g, kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
+    else if (chunks <= 4) quantize_fp8_kernel<4><<<g, kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
+    else if (chunks <= 8) quantize_fp8_kernel<8><<<g, kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
+    else quantize_fp8_kernel<0><<<g, kQThreads, 0, s>>>(x, q, scale, sorted_ids, P, K);
     return hipGetLastError();
 }
 

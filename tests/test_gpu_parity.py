@@ -461,13 +461,16 @@ FP8_SMALL = {
 }
 
 
-def test_quantize_fp8_bit_exact(dev):
+@pytest.mark.parametrize("k", [1040, 3088, 6160, 14336, 16400])
+def test_quantize_fp8_bit_exact(dev, k):
     """Codes and scales equal the oracle's bit for bit (every code is decided from the same fp32
-    product); with sorted ids only real rows are written."""
+    product); with sorted ids only real rows are written.  The widths select each form of the
+    kernel: 1, 2, 4 and 8 chunks of 16 bytes held per thread (partly filled at 3088, 6160 and
+    14336), and the two-pass form past 16384."""
     import torch
     m = ops()
     rng = np.random.default_rng(61)
-    rows, k = 77, 1040
+    rows = 77
     x = f32_to_bf16_bits((rng.standard_normal((rows, k)) * np.exp(rng.uniform(-8, 8, (rows, 1)))).astype(np.float32))
     x[3] = 0                                        # all-zero row
     x[5, :] = f32_to_bf16_bits(np.float32(1.5))     # constant row: every code is +448
