@@ -357,15 +357,23 @@ def test_lora_fold_gate_up_form(dev, scale_mult):
     assert np.array_equal(gb[others], base[others])
 
 
-@pytest.mark.parametrize("case", ["lora_all_small", "lora_all_256rows", "x100", "adapter"])
+@pytest.mark.parametrize("case", ["lora_all_small", "lora_all_256rows", "x100", "adapter",
+                                  "max_rank_32_256rows", "max_rank_128_256rows", "max_rank_96"])
 def test_gate_up_lora_fused_epilogue(dev, shared_ws, case):
     """The gate/up LoRA folded in the GEMM's epilogue against the oracle and against the
-    unfused GPU path (gathered gate and up, folds, SiLU * up) on the same inputs."""
+    unfused GPU path (gathered gate and up, folds, SiLU * up) on the same inputs, with max_rank
+    32, 64, 96 and 128 (the epilogue's loop over the rank) on the 128- and 256-row kernels."""
     import torch
     m = ops()
     cfg = SMALL["lora_all_small"]
-    if case == "lora_all_256rows":   # >= 128 rows per expert: the 8-wave 256-row kernel
-        cfg = cfg.with_(T=1100, E=8, top_k=2, seed=9)
+    if case in ("lora_all_256rows", "max_rank_32_256rows", "max_rank_128_256rows"):
+        cfg = cfg.with_(T=1100, E=8, top_k=2, seed=9)   # >= 128 rows per expert: 256-row tiles
+    if case == "max_rank_32_256rows":
+        cfg = cfg.with_(lora_rank=24, lora_max_rank=32)
+    elif case == "max_rank_128_256rows":
+        cfg = cfg.with_(lora_rank=100, lora_max_rank=128)
+    elif case == "max_rank_96":
+        cfg = cfg.with_(lora_rank=80, lora_max_rank=96)
     note(f"gate/up lora fused {case}")
     d = make_inputs(cfg)
     if case == "x100":
