@@ -116,6 +116,12 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t
                  : "memory");
 }
 
+// 4 bytes per lane from global memory straight into LDS at m0 + lane*4 (256 bytes per wave), for
+// small staging that the compiler must not track (see dma16).
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr) : "memory");
+}
+
 // A wave-uniform pointer held in scalar registers (a select between two uniform pointers may
 // otherwise be formed in vector registers, which an "s" operand cannot take).
 template <typename T>

@@ -172,6 +172,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     __shared__ float s_as[FP8 ? 2 : 1][FP8 ? BM : 1];             // fp8: dequantisation scale per tile row
     __shared__ int s_h[2];                                        // rows up to the last token
     __shared__ int s_arrived;                                     // split tile: the other side's count
+    __shared__ int s_pf[STAGES == 2 && LORA == 0 && !FP8 ? BM : 1];  // next segment's sorted ids
+    __shared__ int s_nx[4];                                       // next segment: e, r0, r_end, n0
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in a scalar register
@@ -486,6 +488,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     // Stage t becomes readable: this thread's loads of t have landed (at most `ahead` later stages
     // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
     // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
+    // The next segment's rows, prepared inside this segment's main loop (pf: 2 stages, at least 3
+    // stages in the segment, a next segment exists; plain bf16 tiles): after the barrier of stage
+    // 0 the waves of threads tid < BM locate it and load its sorted ids into LDS; after the
+    // barrier of stage 1 (whose vmcnt(0) covered those loads) they write its rows to LDS buffer
+    // buf ^ 1 (free: the previous segment's epilogue, its last reader, is behind both barriers).
+    // Later stage barriers order those writes before the issuing waves read them for the next
+    // segment's sources at this segment's end.  So the segment end no longer waits for the
+    // expert search, a barrier and the sorted-id loads.
+    constexpr bool PF = STAGES == 2 && LORA == 0 && !FP8 && BM <= NT && BM % 64 == 0;
+    int L_next = 0, kb2 = 0, ke2 = nk, e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
+    bool more = false, pf = false;
     auto ready = [&](int t) __attribute__((always_inline)) {
         const int ahead = min(STAGES - 2, nseg - 1 - t);
         if constexpr (STAGES >= 4) {
@@ -502,12 +515,42 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
         __builtin_amdgcn_s_barrier();
         if (t + STAGES - 1 < nseg) issue(t + STAGES - 1);
     };
+    // after the barrier of stage 0: locate the next segment, load its sorted ids
+    auto pf_load = [&]() __attribute__((always_inline)) {
+        if constexpr (PF) {
+            // only the waves that hold its rows (with the asymmetric issue, the issuing waves,
+            // which have slack in the main loop); wave 0 hands the result to the others in LDS
+            if (pf && wave < BM / 64) {
+                locate(L_next, e2, r02, r_end2, n02);
+                if (tid == 0) {
+                    s_h[buf ^ 1] = 0;
+                    s_nx[0] = e2; s_nx[1] = r02; s_nx[2] = r_end2; s_nx[3] = n02;
+                }
+                // straight into LDS, untracked by the compiler: a tracked load here would be
+                // waited for (vmcnt(0), draining the stage loads) where the loop variants join;
+                // rows past the segment read its first row, never used
+                dma4(sorted_ids + (r02 + tid < r_end2 ? r02 + tid : r02), lds_u32(s_pf) + wave * 256);
+            }
+        }
+    };
+    // after the barrier of stage 1: its rows into LDS
+    auto pf_rows = [&]() __attribute__((always_inline)) {
+        if constexpr (PF) {
+            if (pf && tid < BM) {
+                const int p = r02 + tid < r_end2 ? s_pf[tid] : -1;
+                const int src = (p >= 0 && p < P) ? ((GATE_UP || a_tok) ? p / top_k : r02 + tid) : -1;
+                s_row[buf ^ 1][tid] = src;
+                if (src >= 0) atomicMax(&s_h[buf ^ 1], tid + 1);
+            }
+        }
+    };
     // Each k-step's MFMAs are issued after the next k-step's fragment reads (and, at a stage
     // boundary, after the barrier), so queued MFMAs cover both LDS latency and barrier waits.
     // NF = A fragments of this wave that hold tokens; every wave still loads and meets the barriers.
     auto main_loop = [&](auto nf_c) __attribute__((always_inline)) {
         if constexpr (NSET == 2) {
             ready(0);
+            pf_load();
             read(nf_c, 0, 0, 0);
             for (int s = 0; s < nseg; ++s) {
 #pragma unroll
@@ -517,6 +560,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                         read(nf_c, s, kk + 1, (kk + 1) & 1);
                     } else if (s + 1 < nseg) {
                         ready(s + 1);
+                        if (s == 0) pf_rows();
                         read(nf_c, s + 1, 0, 0);
                     }
                     mfma(nf_c, kk & 1);
@@ -544,6 +588,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
         if (t < nseg) issue_at(t, kb);
 
     while (true) {
+        // the next segment: this XCD's next whole tile, else this workgroup's tail piece
+        L_next = L + per_xcd; kb2 = 0; ke2 = nk;
+        more = L != tail_L && L_next < l_hi;
+        if (!more && L != tail_L && tail_L >= 0) {
+            more = true;
+            L_next = tail_L; kb2 = tail_kb; ke2 = tail_ke;
+        }
+        pf = PF && more && nseg >= 3;
         // rows up to the last token of this tile (an expert's sentinels follow its tokens): a wave
         // whose 32-row fragments all lie past it skips their MFMAs
         const int h_rows = s_h[buf];
@@ -624,20 +676,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                     off += F::NT * 16;
                 }
 
-        // ---- next segment: its rows, sources and first stage, before this segment's epilogue
-        int L_next = L + per_xcd, kb2 = 0, ke2 = nk;
-        bool more = L != tail_L && L_next < l_hi;
-        if (!more && L != tail_L && tail_L >= 0) {
-            more = true;
-            L_next = tail_L; kb2 = tail_kb; ke2 = tail_ke;
-        }
-        int e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
+        // ---- next segment: its rows (unless prepared in the main loop), sources and first stage,
+        // before this segment's epilogue
         if (more) {
-            locate(L_next, e2, r02, r_end2, n02);
-            if (tid == 0) s_h[buf ^ 1] = 0;
-            __syncthreads();  // every wave is past this segment's last stage reads and s_h is reset
-            load_rows(buf ^ 1, r02, r_end2);
-            __syncthreads();
+            if (pf && wave >= BM / 64) {  // located by wave 0 in the main loop
+                e2 = __builtin_amdgcn_readfirstlane(s_nx[0]);
+                r02 = __builtin_amdgcn_readfirstlane(s_nx[1]);
+                r_end2 = __builtin_amdgcn_readfirstlane(s_nx[2]);
+                n02 = __builtin_amdgcn_readfirstlane(s_nx[3]);
+            }
+            if (!pf) {
+                locate(L_next, e2, r02, r_end2, n02);
+                if (tid == 0) s_h[buf ^ 1] = 0;
+                __syncthreads();  // every wave is past this segment's last stage reads and s_h is reset
+                load_rows(buf ^ 1, r02, r_end2);
+                __syncthreads();
+            }
             set_sources(buf ^ 1, e2, r02, n02);
             // stage 0 of the next segment goes to buffer (sb + nseg) % STAGES, which held stage
             // nseg-STAGES+1 .. of this segment at the latest and is no longer read by any wave
