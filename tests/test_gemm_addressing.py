@@ -164,16 +164,21 @@ def test_split_tail_covers_each_stage_once(T, nk, grid):
 
 def test_expert_of_row_tile_binary_search():
     """Largest expert whose first row tile is <= m_t, with empty experts in between (the kernel's
-    binary search over the inclusive tile scan)."""
-    nt = [0, 3, 0, 0, 2, 0, 1, 0]
-    tb = np.concatenate([[0], np.cumsum(nt)])
-    E = len(nt)
-    for m_t in range(int(tb[-1])):
-        a, b = 0, E - 1
-        while a < b:
-            mid = (a + b + 1) >> 1
-            if tb[mid] <= m_t:
-                a = mid
-            else:
-                b = mid - 1
-        assert tb[a] <= m_t < tb[a + 1] and nt[a] > 0
+    binary search over the inclusive tile scan): the expert found owns tile m_t, and it is the
+    count of experts with tb[e] <= m_t, minus one."""
+    rng = np.random.default_rng(5)
+    cases = [[0, 3, 0, 0, 2, 0, 1, 0]]
+    cases += [list(rng.integers(0, 3, size=E) * (rng.random(E) < 0.6)) for E in (1, 7, 64, 65, 200, 256)]
+    for nt in cases:
+        E = len(nt)
+        tb = np.concatenate([[0], np.cumsum(nt)])
+        for m_t in range(int(tb[-1])):
+            a, b = 0, E - 1
+            while a < b:
+                mid = (a + b + 1) >> 1
+                if tb[mid] <= m_t:
+                    a = mid
+                else:
+                    b = mid - 1
+            assert tb[a] <= m_t < tb[a + 1] and nt[a] > 0
+            assert a == int(np.sum(tb[:E] <= m_t)) - 1
