@@ -32,9 +32,11 @@
 // takes the contiguous range [x*T/8, (x+1)*T/8) of the T real tiles and its workgroups stride
 // through it; the ~32 tiles an XCD runs at once then cover a few panels x GM row tiles and share
 // A tiles and weight panels in that XCD's L2.  With more than 4 tiles per compute unit the grid
-// is persistent (one workgroup per compute unit): before a tile's epilogue the workgroup loads the
-// next tile's rows and issues its first stage into the free LDS buffer, so the next tile's setup
-// and first load latency hide behind this epilogue.  With fewer tiles, one workgroup per tile.
+// is persistent (one workgroup per compute unit): before a tile's epilogue the workgroup takes the
+// next tile's rows and issues its first stage into the free LDS buffer, so the next tile's first
+// load latency hides behind this epilogue; with 2 stages, the next tile's expert search and
+// sorted-id loads already run inside this tile's main loop (see pf below).  With fewer tiles
+// (and no workspace), one workgroup per tile.
 //
 // Split tail (only with a caller workspace).  When the tiles do not fill a whole number of
 // rounds of the persistent grid, the last partial round would leave most compute units idle
