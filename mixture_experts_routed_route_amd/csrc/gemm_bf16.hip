@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     __shared__ float s_as[FP8 ? 2 : 1][FP8 ? BM : 1];             // fp8: dequantisation scale per tile row
     __shared__ int s_h[2];                                        // rows up to the last token
     __shared__ int s_arrived;                                     // split tile: the other side's count
-    __shared__ int s_pf[STAGES == 2 && LORA == 0 && !FP8 ? BM : 1];  // next segment's sorted ids
+    __shared__ int s_pf[STAGES == 2 && LORA == 0 ? BM : 1];       // next segment's sorted ids
     __shared__ int s_nx[4];                                       // next segment: e, r0, r_end, n0
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -491,14 +491,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
     // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
     // The next segment's rows, prepared inside this segment's main loop (pf: 2 stages, at least 3
-    // stages in the segment, a next segment exists; plain bf16 tiles): after the barrier of stage
+    // stages in the segment, a next segment exists; no LoRA epilogue): after the barrier of stage
     // 0 the waves of threads tid < BM locate it and load its sorted ids into LDS; after the
     // barrier of stage 1 (whose vmcnt(0) covered those loads) they write its rows to LDS buffer
     // buf ^ 1 (free: the previous segment's epilogue, its last reader, is behind both barriers).
     // Later stage barriers order those writes before the issuing waves read them for the next
     // segment's sources at this segment's end.  So the segment end no longer waits for the
     // expert search, a barrier and the sorted-id loads.
-    constexpr bool PF = STAGES == 2 && LORA == 0 && !FP8 && BM <= NT && BM % 64 == 0;
+    constexpr bool PF = STAGES == 2 && LORA == 0 && BM <= NT && BM % 64 == 0;
     int L_next = 0, kb2 = 0, ke2 = nk, e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
     bool more = false, pf = false;
     auto ready = [&](int t) __attribute__((always_inline)) {
@@ -543,6 +543,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                 const int src = (p >= 0 && p < P) ? ((GATE_UP || a_tok) ? p / top_k : r02 + tid) : -1;
                 s_row[buf ^ 1][tid] = src;
                 if (src >= 0) atomicMax(&s_h[buf ^ 1], tid + 1);
+                // fp8: the rows' activation scales, straight into LDS as well (a row without a
+                // token takes row 0's, never used); the later stage waits cover the loads
+                if constexpr (FP8) dma4(f8.a + (src >= 0 ? src : 0), lds_u32(s_as[buf ^ 1]) + wave * 256);
             }
         }
     };
@@ -572,6 +575,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
             // one set: each k-step's reads, then its MFMAs; the stage barrier opens each stage
             for (int s = 0; s < nseg; ++s) {
                 ready(s);
+                if (s == 0) pf_load();
+                else if (s == 1) pf_rows();
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
                     if (A_LATE && kk == A_LATE_K && s + 1 < nseg) issue_at(s + 1, kb, 1);
