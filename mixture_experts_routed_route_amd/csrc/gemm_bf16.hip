@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     __shared__ float s_as[FP8 ? 2 : 1][FP8 ? BM : 1];             // fp8: dequantisation scale per tile row
     __shared__ int s_h[2];                                        // rows up to the last token
     __shared__ int s_arrived;                                     // split tile: the other side's count
-    __shared__ int s_pf[STAGES == 2 && LORA == 0 ? BM : 1];       // next segment's sorted ids
+    __shared__ int s_pf[STAGES == 2 ? BM : 1];                    // next segment's sorted ids
     __shared__ int s_nx[4];                                       // next segment: e, r0, r_end, n0
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -491,14 +491,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
     // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
     // The next segment's rows, prepared inside this segment's main loop (pf: 2 stages, at least 3
-    // stages in the segment, a next segment exists; no LoRA epilogue): after the barrier of stage
+    // stages in the segment (4 with LoRA), a next segment exists): after the barrier of stage
     // 0 the waves of threads tid < BM locate it and load its sorted ids into LDS; after the
     // barrier of stage 1 (whose vmcnt(0) covered those loads) they write its rows to LDS buffer
     // buf ^ 1 (free: the previous segment's epilogue, its last reader, is behind both barriers).
     // Later stage barriers order those writes before the issuing waves read them for the next
     // segment's sources at this segment's end.  So the segment end no longer waits for the
     // expert search, a barrier and the sorted-id loads.
-    constexpr bool PF = STAGES == 2 && LORA == 0 && BM <= NT && BM % 64 == 0;
+    constexpr bool PF = STAGES == 2 && BM <= NT && BM % 64 == 0;
     int L_next = 0, kb2 = 0, ke2 = nk, e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
     bool more = false, pf = false;
     auto ready = [&](int t) __attribute__((always_inline)) {
@@ -546,6 +546,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                 // fp8: the rows' activation scales, straight into LDS as well (a row without a
                 // token takes row 0's, never used); the later stage waits cover the loads
                 if constexpr (FP8) dma4(f8.a + (src >= 0 ? src : 0), lds_u32(s_as[buf ^ 1]) + wave * 256);
+                // LoRA: the tokens' adapter ids, raw, straight into LDS (checked after the next
+                // barrier, below); without a map every row with a token is adapter 0
+                if constexpr (LORA) {
+                    if (lora.row_adapter != nullptr)
+                        dma4(lora.row_adapter + (src >= 0 ? src : 0), lds_u32(s_rad[buf ^ 1]) + wave * 256);
+                    else
+                        s_rad[buf ^ 1][tid] = src >= 0 ? 0 : -1;
+                }
+            }
+        }
+    };
+    // LoRA, after the barrier of stage 2 (whose vmcnt(0) covered the id loads): -1 for rows without
+    // a token and for ids outside [0, n_ad), as load_rows does
+    auto pf_fix = [&]() __attribute__((always_inline)) {
+        if constexpr (PF && LORA) {
+            if (pf && tid < BM && lora.row_adapter != nullptr) {
+                const int a = s_rad[buf ^ 1][tid];
+                s_rad[buf ^ 1][tid] = (s_row[buf ^ 1][tid] >= 0 && a >= 0 && a < lora.n_ad) ? a : -1;
             }
         }
     };
@@ -566,6 +584,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                     } else if (s + 1 < nseg) {
                         ready(s + 1);
                         if (s == 0) pf_rows();
+                        else if (s == 1) pf_fix();
                         read(nf_c, s + 1, 0, 0);
                     }
                     mfma(nf_c, kk & 1);
@@ -602,7 +621,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
             more = true;
             L_next = tail_L; kb2 = tail_kb; ke2 = tail_ke;
         }
-        pf = PF && more && nseg >= 3;
+        pf = PF && more && nseg >= (LORA ? 4 : 3);
         // rows up to the last token of this tile (an expert's sentinels follow its tokens): a wave
         // whose 32-row fragments all lie past it skips their MFMAs
         const int h_rows = s_h[buf];
