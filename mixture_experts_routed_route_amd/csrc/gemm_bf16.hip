@@ -487,20 +487,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                 else
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     };
-    // Stage t becomes readable: this thread's loads of t have landed (at most `ahead` later stages
-    // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
-    // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
     // The next segment's rows, prepared inside this segment's main loop (pf: 2 stages, at least 3
     // stages in the segment (4 with LoRA), a next segment exists): after the barrier of stage
     // 0 the waves of threads tid < BM locate it and load its sorted ids into LDS; after the
     // barrier of stage 1 (whose vmcnt(0) covered those loads) they write its rows to LDS buffer
-    // buf ^ 1 (free: the previous segment's epilogue, its last reader, is behind both barriers).
-    // Later stage barriers order those writes before the issuing waves read them for the next
-    // segment's sources at this segment's end.  So the segment end no longer waits for the
-    // expert search, a barrier and the sorted-id loads.
+    // buf ^ 1 (free: the previous segment's epilogue, its last reader, is behind both barriers),
+    // with the fp8 activation scales or the LoRA adapter ids of those rows.  Later stage
+    // barriers order those writes before the issuing waves read them for the next segment's
+    // sources at this segment's end.  So the segment end no longer waits for the expert search,
+    // a barrier and the sorted-id loads.
     constexpr bool PF = STAGES == 2 && BM <= NT && BM % 64 == 0;
     int L_next = 0, kb2 = 0, ke2 = nk, e2 = 0, r02 = 0, r_end2 = 0, n02 = 0;
     bool more = false, pf = false;
+    // Stage t becomes readable: this thread's loads of t have landed (at most `ahead` later stages
+    // still in flight), its own LDS reads of earlier stages are done, and after the barrier every
+    // wave is past stage t-1, whose buffer is refilled with stage t+STAGES-1.
     auto ready = [&](int t) __attribute__((always_inline)) {
         const int ahead = min(STAGES - 2, nseg - 1 - t);
         if constexpr (STAGES >= 4) {
