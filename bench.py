@@ -311,13 +311,14 @@ def run_workload(name: str, args, dev) -> dict:
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if has_fold else None
 
-    wt = {"bf16": "gemm_bf16_kernel", "fp8": "gemm_fp8_kernel", "int4_gptq": "gemm_int4_kernel"}[cfg.weights]
+    wt = {"bf16": "gemm_bf16_kernel", "fp8": "gemm_bf16_kernel (fp8 form)", "int4_gptq": "gemm_int4_kernel"}[cfg.weights]
     gu_what = ("gemm_bf16_kernel<gate_up> with the gate/up LoRA epilogue (+ 2 shrinks)"
                if layer.gate_up_lora and layer.gate_up_fused
                else "gate/up stage: 2 gathered GEMMs, 2 LoRA folds, SiLU*up" if layer.gate_up_lora
-               else "gate/up stage: x quantisation + gemm_fp8_kernel<gate_up>" if cfg.weights == "fp8"
+               else "gate/up stage: x quantisation + gemm_bf16_kernel<gate_up> (fp8 form)" if cfg.weights == "fp8"
                else f"{wt}<gate_up>")
-    dn_what = ("down stage: Hs quantisation + gemm_fp8_kernel<down>" if cfg.weights == "fp8" else f"{wt}<down>")
+    dn_what = ("down stage: Hs quantisation + gemm_bf16_kernel<down> (fp8 form)" if cfg.weights == "fp8"
+               else f"{wt}<down>")
     peak_mfma = PEAK_FP8_TFLOPS if cfg.weights == "fp8" else PEAK_BF16_TFLOPS
     counts = b.routing.counts.cpu().numpy()
     active = int((counts > 0).sum())

@@ -182,6 +182,10 @@ def test_argument_validation_rejects_before_launch(L):
     rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8, 128,
                   256, 16, 256, fake, 64, None)
     assert rc == -1 and "workspace_bytes" in msg
+    # an expert matrix of 65536 x 65552 codes is over 4 GiB: the 32-bit load offsets cannot reach it
+    rc, msg = _rc(L, "moe_grouped_gemm_fp8", 1, fake, fake, ctypes.byref(w8), None, fake, fake, fake, 128, 2, 8,
+                  65536, 65552, 16, 256, None, 0, None)
+    assert rc == -2 and "4 GiB" in msg
     rc, msg = _rc(L, "moe_grouped_gemm", 1, fake, ctypes.byref(w8), None, fake, fake, fake, fake, 128, 2, 8, 128,
                   256, 16, 256, None, 0, None)
     assert rc == -1 and "unsupported type" in msg
