@@ -215,6 +215,12 @@ SPLIT_K = {
     "rows256_min_pieces": MoeConfig("sk_256b", T=1536, H=4104, I=1032, E=8, top_k=2, block_size=64, seed=34),
     # less than a round: every tile is a tail tile, gate/up 128 tiles and down 80, in 2 pieces
     "all_tail": MoeConfig("sk_tail", T=1536, H=1032, I=1000, E=8, top_k=2, block_size=64, seed=35),
+    # over 512 tiles on the 256-workgroup grid, so workgroups run several tiles and prepare the next
+    # one inside the main loop, with segments of 3, 4 and 5 stages (the shortest that do):
+    # gate/up 16 row tiles x 33 panels with K = 192 and 256; down 16 x 33 panels with K = 320
+    "prefetch_k3": MoeConfig("pf_k3", T=1200, H=192, I=4104, E=8, top_k=2, block_size=64, seed=38),
+    "prefetch_k4": MoeConfig("pf_k4", T=1200, H=256, I=4104, E=8, top_k=2, block_size=64, seed=39),
+    "prefetch_down_k5": MoeConfig("pf_dn5", T=1200, H=8200, I=320, E=8, top_k=2, block_size=64, seed=40),
     # GPTQ int4 takes the workspace (size-checked) and does not use it: results as without it
     "int4_decode_g128": CONFIGS["decode_int4"],
     "int4_decode_g256": MoeConfig("sk_i4_256", T=16, H=2048, I=1536, E=64, top_k=6, block_size=16,
@@ -358,7 +364,8 @@ def test_lora_fold_gate_up_form(dev, scale_mult):
 
 
 @pytest.mark.parametrize("case", ["lora_all_small", "lora_all_256rows", "x100", "adapter",
-                                  "max_rank_32_256rows", "max_rank_128_256rows", "max_rank_96"])
+                                  "max_rank_32_256rows", "max_rank_128_256rows", "max_rank_96",
+                                  "prefetch_256rows"])
 def test_gate_up_lora_fused_epilogue(dev, shared_ws, case):
     """The gate/up LoRA folded in the GEMM's epilogue against the oracle and against the
     unfused GPU path (gathered gate and up, folds, SiLU * up) on the same inputs, with max_rank
@@ -368,6 +375,8 @@ def test_gate_up_lora_fused_epilogue(dev, shared_ws, case):
     cfg = SMALL["lora_all_small"]
     if case in ("lora_all_256rows", "max_rank_32_256rows", "max_rank_128_256rows"):
         cfg = cfg.with_(T=1100, E=8, top_k=2, seed=9)   # >= 128 rows per expert: 256-row tiles
+    elif case == "prefetch_256rows":   # 16 row tiles x 33 panels, K = 256: 4-stage segments, several
+        cfg = cfg.with_(T=1100, E=8, top_k=2, H=256, I=4104, seed=10)   # tiles per workgroup
     if case == "max_rank_32_256rows":
         cfg = cfg.with_(lora_rank=24, lora_max_rank=32)
     elif case == "max_rank_128_256rows":
@@ -463,6 +472,12 @@ FP8_SMALL = {
     # tile cut in 2 pieces (gate/up here: 9 column panels, K = 2176)
     "fp8_split_gate_up": MoeConfig("fp8_split_gu", T=1024, H=2176, I=1040, E=4, top_k=2, block_size=64,
                                    weights="fp8", seed=54),
+    # several tiles per workgroup, the next prepared inside the main loop: gate/up 16 row tiles x
+    # 33 panels with K = 384 (3 stages of 128), down 16 x 33 panels with K = 384
+    "fp8_prefetch_gate_up": MoeConfig("fp8_pf_gu", T=1200, H=384, I=4112, E=8, top_k=2, block_size=64,
+                                      weights="fp8", seed=57),
+    "fp8_prefetch_down": MoeConfig("fp8_pf_dn", T=1200, H=8208, I=384, E=8, top_k=2, block_size=64,
+                                   weights="fp8", seed=58),
     # ... and down here (5 column panels of 256, K = 2176)
     "fp8_split_down": MoeConfig("fp8_split_dn", T=1024, H=1040, I=2176, E=4, top_k=2, block_size=64,
                                 weights="fp8", seed=55),
