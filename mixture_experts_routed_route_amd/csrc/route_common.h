@@ -3,10 +3,11 @@
 // experts, keep the top_k, optionally renormalise over them.
 //
 // One wave64 per token.  Each lane holds up to four logits (E <= 256) in registers.
-// Selection takes top_k rounds of a wave arg-max over a 64-bit key (order-preserving image
-// of the fp32 logit, then the complement of the expert index, so equal logits pick the
-// lower index).  Selection j is kept by lane j % 64 in its slot j / 64, so top_k may reach
-// E (up to 256).  The weights are computed in fp64 and rounded once to fp32.
+// Selection takes top_k rounds of a wave arg-max: a 32-bit wave max of an order-preserving
+// image of the fp32 logit, then a ballot of the lanes that hold it, slot by slot, whose lowest
+// set bit is the lowest expert index (so equal logits pick the lower index).  Selection j is
+// kept by lane j % 64 in its slot j / 64, so top_k may reach E (up to 256).  The weights are
+// computed in fp64 and rounded once to fp32.
 #pragma once
 
 #include "device_common.h"
@@ -42,17 +43,16 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    uint64_t o;
-    o = row_ror_u64<1>(v); v = o > v ? o : v;
-    o = row_ror_u64<2>(v); v = o > v ? o : v;
-    o = row_ror_u64<4>(v); v = o > v ? o : v;
-    o = row_ror_u64<8>(v); v = o > v ? o : v;
-    uint64_t m = readlane_u64(v, 0);
-    o = readlane_u64(v, 16); m = o > m ? o : m;
-    o = readlane_u64(v, 32); m = o > m ? o : m;
-    o = readlane_u64(v, 48); m = o > m ? o : m;
-    return m;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x121, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x122, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+    const uint32_t a = max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)),
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)));
+    const uint32_t b = max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)),
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48)));
+    return max(a, b);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -75,7 +75,7 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
                                              int top_k, int renorm, int32_t* __restrict__ ids,
                                              float* __restrict__ w, int lane, int* lds_ids = nullptr) {
     float v[NTOK][EPL];
-    uint64_t key[NTOK][EPL];
+    uint32_t key[NTOK][EPL];  // order bits of the logit; 0: not a candidate (taken, or past E)
 #pragma unroll
     for (int n = 0; n < NTOK; ++n) {
         const int t = t0 + n * dt;
@@ -84,7 +84,7 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
             const int e = lane + 64 * i;
             if (t < T && e < E) {
                 v[n][i] = logits[static_cast<size_t>(t) * E + e];
-                key[n][i] = (static_cast<uint64_t>(order_bits(v[n][i])) << 32) | static_cast<uint32_t>(0xffff - e);
+                key[n][i] = order_bits(v[n][i]);  // > 0 for every finite logit
             } else {
                 v[n][i] = 0.0f;
                 key[n][i] = 0;  // below every real key
@@ -102,19 +102,25 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
         for (int i = 0; i < EPL; ++i) { my_e[n][i] = 0; my_l[n][i] = 0.0f; }
     }
     for (int j = 0; j < top_k; ++j) {
-        uint64_t best[NTOK];
+        uint32_t best[NTOK];
 #pragma unroll
         for (int n = 0; n < NTOK; ++n) {
             best[n] = key[n][0];
 #pragma unroll
-            for (int i = 1; i < EPL; ++i) best[n] = key[n][i] > best[n] ? key[n][i] : best[n];
+            for (int i = 1; i < EPL; ++i) best[n] = max(best[n], key[n][i]);
         }
 #pragma unroll
-        for (int n = 0; n < NTOK; ++n) best[n] = wave_max_u64(best[n]);
+        for (int n = 0; n < NTOK; ++n) best[n] = wave_max_u32(best[n]);
 #pragma unroll
         for (int n = 0; n < NTOK; ++n) {
-            const int e = 0xffff - static_cast<int>(best[n] & 0xffffu);
-            const float l = from_order_bits(static_cast<uint32_t>(best[n] >> 32));
+            // the lowest expert holding the largest key: slot i holds experts 64 i + lane
+            int e = 0x7fffffff;
+#pragma unroll
+            for (int i = EPL - 1; i >= 0; --i) {
+                const uint64_t hit = __ballot(key[n][i] == best[n]);
+                if (hit) e = 64 * i + __ffsll(static_cast<unsigned long long>(hit)) - 1;
+            }
+            const float l = from_order_bits(best[n]);
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
                 if (lane + 64 * i == e) key[n][i] = 0;
