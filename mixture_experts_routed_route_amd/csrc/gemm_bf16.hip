@@ -137,6 +137,12 @@ template <bool FP8>
 using Elem = std::conditional_t<FP8, uint8_t, uint16_t>;
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));  // a 32-byte fp8 MFMA operand
 
+// 16 bytes from global memory as a global (not flat) load: a flat load is also counted by
+// lgkmcnt, so waiting for it waits for LDS traffic too
+__device__ __forceinline__ bf16x8 gload_bf16x8(const uint16_t* p) {
+    return *(const __attribute__((address_space(1))) bf16x8*)(p);
+}
+
 // fp8 form: dequantisation scales of the activation rows ([rows of A]) and of the weight rows
 // ([E, N], one per output channel, for w0 and w1)
 struct Fp8Scales {
@@ -729,70 +735,140 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
 
         // ---- gate/up LoRA (the page's order: bf16 gate and up outputs, each folded, then SiLU * up):
         // every accumulator becomes a bf16 value, bf16(bf16(acc) + scale * bf16(xa . B_e^T)) where
-        // the row is folded.  The delta blocks are 32x32x16 MFMAs over the rank, with the xa and
-        // B_e fragments read straight from memory.
+        // the row is folded.  The bf16 values are held two to a register while the deltas are formed,
+        // which leaves the registers for a projection's whole delta: its four 32x32 blocks as 32x32x16
+        // MFMAs over the rank, fed by xa and B_e fragments read straight from memory, up to 64 of the
+        // rank at a time.  A chunk's fragment loads are all issued before its MFMAs (the scheduling
+        // barrier keeps the compiler from sinking each load to its MFMA), so a projection waits for
+        // one or two memory latencies rather than one per MFMA.
         if constexpr (LORA) {
             if (store) {
                 auto bf16r = [](float x) __attribute__((always_inline)) {
                     return __uint_as_float(static_cast<uint32_t>(f32_to_bf16(x)) << 16);
                 };
+                auto lo16 = [](uint32_t w) __attribute__((always_inline)) { return __uint_as_float(w << 16); };
+                auto hi16 = [](uint32_t w) __attribute__((always_inline)) { return __uint_as_float(w & 0xffff0000u); };
+                // values 2h and 2h+1 of block [i][j]: the same rounding as bf16r
+                uint32_t pk[F::FI][4][8];
 #pragma unroll
-                for (int i = 0; i < F::FI; ++i) {
-                    // this lane's xa row (clamped: rows past the span are computed and never stored)
-                    const int rowf = min(r0 + wm * F::WM + i * 32 + fr, max_pad - 1);
+                for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-                    for (int pj = 0; pj < 2; ++pj) {  // 0: gate (blocks 0, 1), 1: up (blocks 2, 3)
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int jj = 0; jj < 2; ++jj)
+                        for (int h = 0; h < 8; ++h) pk[i][j][h] = pack_bf16x2(acc[i][j][2 * h], acc[i][j][2 * h + 1]);
+                // adapter id of the row of value v of fragment i (-1: not folded)
+                auto row_ad = [&](int i, int v) __attribute__((always_inline)) {
+                    return s_rad[buf][wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3)];
+                };
+                // the adapters present among the wave's rows, smallest first: one pass each
+                auto next_ad = [&](int after) __attribute__((always_inline)) {
+                    int m = 0x7fffffff;
+                    for (int i = 0; i < F::FI; ++i)
+                        for (int v = 0; v < 16; ++v) {
+                            const int a = row_ad(i, v);
+                            if (a > after && a < m) m = a;
+                        }
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) acc[i][pj * 2 + jj][v] = bf16r(acc[i][pj * 2 + jj][v]);
-                        if (e >= lora.n_tab[pj]) continue;  // past every adapter's table: not adapted
-                        // adapter id of the row of value v (-1: not folded)
-                        auto row_ad = [&](int v) __attribute__((always_inline)) {
-                            return s_rad[buf][wm * F::WM + i * 32 + (v >> 2) * 8 + fc * 4 + (v & 3)];
-                        };
-                        // the adapters present among the 32 rows, smallest first: one pass each
-                        auto next_ad = [&](int after) __attribute__((always_inline)) {
-                            int m = 0x7fffffff;
-                            for (int v = 0; v < 16; ++v) {
-                                const int a = row_ad(v);
-                                if (a > after && a < m) m = a;
+                    for (int o = 32; o >= 1; o >>= 1) m = min(m, __shfl_xor(m, o));
+                    return m;
+                };
+                // adapter `cur`'s B_e and scale_e of projection pj (Be = nullptr: e not adapted by it)
+                auto table = [&](int pj, int cur, const uint16_t*& Be, float& sc) __attribute__((always_inline)) {
+                    Be = nullptr;
+                    sc = 0.f;
+                    if (e >= lora.n_tab[pj]) return;
+                    const int64_t tix = static_cast<int64_t>(cur) * lora.n_tab[pj] + e;
+                    if (lora.a_tab[pj][tix] == 0 || lora.b_tab[pj][tix] == 0) return;
+                    Be = reinterpret_cast<const uint16_t*>(lora.b_tab[pj][tix]);
+                    sc = lora.s_tab[pj][tix];
+                };
+                // one adapter: its tables for both projections, looked up once per tile
+                const uint16_t* ad0_b[2] = {nullptr, nullptr};
+                float ad0_s[2] = {0.f, 0.f};
+                if constexpr (LORA == 1) {
+                    table(0, 0, ad0_b[0], ad0_s[0]);
+                    table(1, 0, ad0_b[1], ad0_s[1]);
+                }
+#pragma unroll
+                for (int pj = 0; pj < 2; ++pj) {  // 0: gate (blocks 0, 1), 1: up (blocks 2, 3)
+                    if (e >= lora.n_tab[pj]) continue;  // past every adapter's table: not adapted
+                    // this lane's xa rows (clamped: rows past the span are computed and never stored)
+                    const uint16_t* xr[F::FI];
+#pragma unroll
+                    for (int i = 0; i < F::FI; ++i) {
+                        const int rowf = min(r0 + wm * F::WM + i * 32 + fr, max_pad - 1);
+                        xr[i] = lora.xa[pj] + static_cast<size_t>(rowf) * lora.rank + fc * 8;
+                    }
+                    // one pass per adapter: the delta of adapter `cur`, folded into its rows
+                    auto pass = [&](int cur, const uint16_t* Be, float sc) __attribute__((always_inline)) {
+                        if (Be == nullptr) return;
+                        const uint16_t* br[2];
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const int col = min(n0 + wn * 64 + jj * 32 + fr, N - 1);
+                            br[jj] = Be + static_cast<size_t>(col) * lora.rank + fc * 8;
+                        }
+                        f32x16 d[F::FI][2];
+#pragma unroll
+                        for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) d[i][jj][v] = 0.f;
+                        // NTK 16-deep steps of the rank from k0; each delta block sums in rank order
+                        auto chunk = [&](int k0, auto ntk_c) __attribute__((always_inline)) {
+                            constexpr int NTK = decltype(ntk_c)::value;
+                            bf16x8 xf[F::FI][NTK], bw[2][NTK];
+#pragma unroll
+                            for (int t = 0; t < NTK; ++t) {
+#pragma unroll
+                                for (int i = 0; i < F::FI; ++i) xf[i][t] = gload_bf16x8(xr[i] + k0 + t * 16);
+#pragma unroll
+                                for (int jj = 0; jj < 2; ++jj) bw[jj][t] = gload_bf16x8(br[jj] + k0 + t * 16);
                             }
+                            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                            for (int o = 32; o >= 1; o >>= 1) m = min(m, __shfl_xor(m, o));
-                            return m;
+                            for (int t = 0; t < NTK; ++t)
+#pragma unroll
+                                for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                                    for (int jj = 0; jj < 2; ++jj)
+                                        d[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[i][t], bw[jj][t], d[i][jj], 0, 0, 0);
                         };
-                        const uint16_t* xr = lora.xa[pj] + static_cast<size_t>(rowf) * lora.rank + fc * 8;
-                        // one pass per adapter: the delta of adapter `cur`, folded into its rows
-                        auto pass = [&](int cur) __attribute__((always_inline)) {
-                            const int64_t tix = static_cast<int64_t>(cur) * lora.n_tab[pj] + e;
-                            if (lora.a_tab[pj][tix] == 0 || lora.b_tab[pj][tix] == 0) return;  // e not adapted
-                            const uint16_t* Be = reinterpret_cast<const uint16_t*>(lora.b_tab[pj][tix]);
-                            const float sc = lora.s_tab[pj][tix];
+                        for (int k0 = 0; k0 < lora.rank; k0 += 32) chunk(k0, std::integral_constant<int, 2>{});
 #pragma unroll
-                            for (int jj = 0; jj < 2; ++jj) {  // one 32x32 delta block at a time
-                                const int col = min(n0 + wn * 64 + jj * 32 + fr, N - 1);
-                                const uint16_t* br = Be + static_cast<size_t>(col) * lora.rank + fc * 8;
-                                f32x16 d;
+                        for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-                                for (int v = 0; v < 16; ++v) d[v] = 0.f;
-                                for (int k0 = 0; k0 < lora.rank; k0 += 16)
-                                    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                        *reinterpret_cast<const bf16x8*>(xr + k0), *reinterpret_cast<const bf16x8*>(br + k0),
-                                        d, 0, 0, 0);
+                            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                                for (int v = 0; v < 16; ++v)
-                                    if (row_ad(v) == cur)
-                                        acc[i][pj * 2 + jj][v] = bf16r(fmaf(sc, bf16r(d[v]), acc[i][pj * 2 + jj][v]));
-                            }
-                        };
-                        if constexpr (LORA == 1) {
-                            pass(0);
-                        } else {
-                            for (int cur = next_ad(-1); cur != 0x7fffffff; cur = next_ad(cur)) pass(cur);
+                                for (int h = 0; h < 8; ++h) {
+                                    uint32_t& w = pk[i][pj * 2 + jj][h];
+                                    float lo = lo16(w), hi = hi16(w);
+                                    if (row_ad(i, 2 * h) == cur) lo = bf16r(fmaf(sc, bf16r(d[i][jj][2 * h]), lo));
+                                    if (row_ad(i, 2 * h + 1) == cur) hi = bf16r(fmaf(sc, bf16r(d[i][jj][2 * h + 1]), hi));
+                                    w = pack_bf16x2(lo, hi);  // exact: both are bf16 values
+                                }
+                    };
+                    if constexpr (LORA == 1) {
+                        pass(0, ad0_b[pj], ad0_s[pj]);
+                    } else {
+                        for (int cur = next_ad(-1); cur != 0x7fffffff; cur = next_ad(cur)) {
+                            const uint16_t* Be;
+                            float sc;
+                            table(pj, cur, Be, sc);
+                            pass(cur, Be, sc);
                         }
                     }
                 }
+#pragma unroll
+                for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int h = 0; h < 8; ++h) {
+                            acc[i][j][2 * h] = lo16(pk[i][j][h]);
+                            acc[i][j][2 * h + 1] = hi16(pk[i][j][h]);
+                        }
             }
         }
 
