@@ -76,15 +76,17 @@ def gemm_bytes(cfg, op: str, active_experts: int) -> float:
     return w + act
 
 
-def fold_work(cfg, counts, lora_ids):
+def fold_work(cfg, counts, lora_ids, fused=False):
     """Algorithmic work of the down-projection LoRA fold: per adapted real row, the Hs row read,
-    the Ys row read and written and the bf16 xa row written and read back (at the padded rank the
-    kernels run), plus the A_e and B_e of every adapted expert that has rows; FLOPs at the real
-    rank (2 * rank * (I + H) per adapted real row)."""
+    the Ys row read and written (not when the fold runs in the down GEMM's epilogue, which writes
+    Ys once anyway) and the bf16 xa row written and read back (at the padded rank the kernels run),
+    plus the A_e and B_e of every adapted expert that has rows; FLOPs at the real rank
+    (2 * rank * (I + H) per adapted real row)."""
     R, r = cfg.lora_max_rank, cfg.lora_rank
     ad = [int(e) for e in lora_ids if int(e) < len(counts) and counts[int(e)] > 0]
     rows = int(sum(int(counts[e]) for e in ad))
-    bytes_ = rows * (cfg.I * 2 + 2 * cfg.H * 2 + 2 * R * 2) + len(ad) * (R * cfg.I * 2 + cfg.H * R * 2)
+    ys = 0 if fused else 2 * cfg.H * 2
+    bytes_ = rows * (cfg.I * 2 + ys + 2 * R * 2) + len(ad) * (R * cfg.I * 2 + cfg.H * R * 2)
     return float(2 * r * (cfg.I + cfg.H) * rows), float(bytes_), rows
 
 
@@ -242,7 +244,8 @@ def run_workload(name: str, args, dev) -> dict:
     cfg = CONFIGS[name]
     log(f"[bench] {name}: generating inputs")
     d = make_inputs(cfg)
-    layer = m.MoeLayer.from_arrays(d, dev, fold=args.fold, gate_up_fused=args.gate_up_lora == "fused")
+    layer = m.MoeLayer.from_arrays(d, dev, fold=args.fold, gate_up_fused=args.gate_up_lora == "fused",
+                                   down_fused=args.down_lora == "fused")
     b = layer.plan(cfg.T, dev)
     wbytes = sum(expert_weight_bytes(cfg, op) for op in ("gate_up", "down")) * cfg.E
     rot = args.rotate or max(1, min(4, int(-(-(1 << 30) // wbytes))))
@@ -260,7 +263,7 @@ def run_workload(name: str, args, dev) -> dict:
         ly.gate_up_stage(x, b)
         if ev is not None:
             ev[1].record()
-        ly.down_stage(b)
+        ly.down_stage(b)  # with the fused down fold: the LoRA shrink and the down GEMM that folds
         if ev is not None:
             ev[2].record()
         ly.lora_fold(b)
@@ -268,10 +271,17 @@ def run_workload(name: str, args, dev) -> dict:
             ev[3].record()
         ly.combine(b)
 
-    log(f"[bench] {name}: warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
+    # warmup: at least W steps and at least --warmup-seconds of GPU work, so that the timed steps run at
+    # the steady state (clocks, caches and page tables settle after tens of milliseconds of work on
+    # some workloads, not within a few steps)
+    n_warm, t0 = 0, time.perf_counter()
+    while n_warm < args.warmup or (time.perf_counter() - t0 < args.warmup_seconds and n_warm < 20000):
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log(f"[bench] {name}: warmup {n_warm} steps in {time.perf_counter() - t0:.2f} s")
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     if args.graph:
@@ -310,6 +320,42 @@ def run_workload(name: str, args, dev) -> dict:
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     fold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if has_fold else None
+    fused_fold = has_fold and layer.down_fold_fused(b)
+    unfused = None
+    if fused_fold:
+        # the fused fold's cost: steps with the fold in the down GEMM's epilogue and steps with the
+        # separate fold kernels after a plain down GEMM, alternating (so that clock and cache drift
+        # fall on both alike); the fused fold's added time is its down stage over that plain GEMM
+        def ab_step(i, fused, ev):
+            for ly in layers:
+                ly.down_fused = fused
+            step(i, ev)
+        for i in range(args.warmup):
+            ab_step(i, False, None)
+        torch.cuda.synchronize()
+        ev_ab = {True: [], False: []}
+        for i in range(2 * args.steps):
+            fused = (i % 4) in (0, 3)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev[4].record()
+            ab_step(i // 2, fused, ev)
+            ev[5].record()
+            ev_ab[fused].append(ev)
+        torch.cuda.synchronize()
+        for ly in layers:
+            ly.down_fused = True
+
+        def mean(evs, a, c):
+            return float(np.mean([e[a].elapsed_time(e[c]) for e in evs]))
+        fused_down = mean(ev_ab[True], 1, 3)
+        unfused = {"ms_per_step": mean(ev_ab[False], 4, 5), "down": mean(ev_ab[False], 1, 2),
+                   "lora_fold": mean(ev_ab[False], 2, 3), "fused_ms_per_step": mean(ev_ab[True], 4, 5),
+                   "fused_down_stage": fused_down,
+                   "how": f"{args.steps} fused and {args.steps} unfused steps alternating, HIP events"}
+        fold_ms = fused_down - unfused["down"]
+        log(f"[bench] {name}: A/B of the down fold: fused step {unfused['fused_ms_per_step']:.3f} ms, unfused step "
+            f"{unfused['ms_per_step']:.3f} ms; fused down stage {fused_down:.3f} ms against a plain down GEMM "
+            f"{unfused['down']:.3f} ms + fold kernels {1e3 * unfused['lora_fold']:.1f} us")
 
     wt = {"bf16": "gemm_bf16_kernel", "fp8": "gemm_bf16_kernel (fp8 form)", "int4_gptq": "gemm_int4_kernel"}[cfg.weights]
     gu_what = ("gemm_bf16_kernel<gate_up> with the gate/up LoRA epilogue (+ 2 shrinks)"
@@ -318,28 +364,36 @@ def run_workload(name: str, args, dev) -> dict:
                else "gate/up stage: x quantisation + gemm_bf16_kernel<gate_up> (fp8 form)" if cfg.weights == "fp8"
                else f"{wt}<gate_up>")
     dn_what = ("down stage: Hs quantisation + gemm_bf16_kernel<down> (fp8 form)" if cfg.weights == "fp8"
+               else "down stage: lora_shrink_kernel + gemm_bf16_kernel<down> with the LoRA epilogue" if fused_fold
                else f"{wt}<down>")
     peak_mfma = PEAK_FP8_TFLOPS if cfg.weights == "fp8" else PEAK_BF16_TFLOPS
     counts = b.routing.counts.cpu().numpy()
     active = int((counts > 0).sum())
+    if has_fold:
+        ff, fb, frows = fold_work(cfg, counts, d["lora_ids"], fused=fused_fold)
+    dn_flops, dn_bytes = gemm_flops(cfg, "down"), gemm_bytes(cfg, "down", active)
+    if fused_fold:   # the down stage also runs the shrink and the fold
+        dn_flops, dn_bytes = dn_flops + ff, dn_bytes + fb
     roofs = {
         "gate_up": roofline(gemm_flops(cfg, "gate_up"), gemm_bytes(cfg, "gate_up", active), gu_ms, peak_mfma,
                             gu_what, measured_traffic(cfg.name, "gate_up")),
-        "down": roofline(gemm_flops(cfg, "down"), gemm_bytes(cfg, "down", active), dn_ms, peak_mfma, dn_what,
-                         measured_traffic(cfg.name, "down")),
+        "down": roofline(dn_flops, dn_bytes, dn_ms, peak_mfma, dn_what,
+                         None if fused_fold else measured_traffic(cfg.name, "down")),
     }
     if has_fold:
-        ff, fb, frows = fold_work(cfg, counts, d["lora_ids"])
         mode = layer.fold_mode(b)
-        roofs["lora_fold"] = roofline(ff, fb, fold_ms, peak_mfma,
-                                      "lora_shrink_kernel + lora_expand_fold_kernel" if mode == "grouped"
-                                      else "gather_shrink_kernel + gather_expand_kernel",
-                                      measured_traffic(cfg.name, "lora_fold"))
+        what = ("the fold in the down GEMM's epilogue and lora_shrink_kernel: the fused down stage's time over "
+                "the plain down GEMM's in the unfused steps of the same run" if fused_fold
+                else "lora_shrink_kernel + lora_expand_fold_kernel" if mode == "grouped"
+                else "gather_shrink_kernel + gather_expand_kernel")
+        roofs["lora_fold"] = roofline(ff, fb, fold_ms, peak_mfma, what,
+                                      None if fused_fold else measured_traffic(cfg.name, "lora_fold"))
         roofs["lora_fold"]["adapted_rows"] = frows
     gemm_tflops = (gemm_flops(cfg, "gate_up") + gemm_flops(cfg, "down")) / ((gu_ms + dn_ms) / 1e3) / 1e12
     log(f"[bench] {name}: step {ms:.3f} ms ({cfg.T / (ms / 1e3):.4g} tokens/s); gate/up {gu_ms:.3f} ms; "
         f"down {dn_ms:.3f} ms; grouped GEMMs {gemm_tflops:.1f} TFLOP/s"
-        + (f"; LoRA fold ({layer.fold_mode(b)}) {1e3 * fold_ms:.1f} us" if fold_ms is not None else ""))
+        + (f"; LoRA fold ({'fused, added time' if fused_fold else layer.fold_mode(b)}) {1e3 * fold_ms:.1f} us"
+           if fold_ms is not None else ""))
     for k, r in roofs.items():
         log(f"[bench] {name}: {k} roofline {r['bound']} {r['achieved']:.1f} {r['unit']} "
             f"({100 * r['frac']:.1f}% of peak), AI {r['algorithmic']['flop_per_byte']:.1f} flop/B")
@@ -355,12 +409,13 @@ def run_workload(name: str, args, dev) -> dict:
     res = {
         "workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
         "top_k": cfg.top_k, "block_size": cfg.block_size, "weights": cfg.weights, "lora_rank": cfg.lora_rank,
-        **({"lora_fold": layer.fold_mode(b)} if has_fold else {}),
+        **({"lora_fold": "fused" if fused_fold else layer.fold_mode(b)} if has_fold else {}),
         **({"lora_gate_up": "fused" if layer.gate_up_fused else "unfused"} if layer.gate_up_lora else {}),
-        "launch": "hip_graph" if args.graph else "eager", "weight_copies_rotated": rot,
+        "launch": "hip_graph" if args.graph else "eager", "weight_copies_rotated": rot, "warmup_steps_run": n_warm,
         "active_experts": active,
         "tokens_per_s": cfg.T / (ms / 1e3), "ms_per_step": ms,
         "kernels_ms": {"gate_up": gu_ms, "down": dn_ms, **({"lora_fold": fold_ms} if has_fold else {})},
+        **({"unfused_fold": unfused} if unfused else {}),
         "grouped_gemm_tflops": gemm_tflops,
         "roofline": roofs,
         "cpu_baseline": None,
@@ -384,7 +439,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=3, help="warmup steps per workload, at least")
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="warmup per workload lasts at least this long (more steps than --warmup if needed)")
     ap.add_argument("--config", default="all", help="'all' (the five workloads, mixtral_prefill headline) or one name")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="token sample of the CPU oracle leg (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -395,6 +452,9 @@ def main():
                          "per-kernel figures then come from an eager pass of the same steps")
     ap.add_argument("--fold", default="auto", choices=["auto", "grouped", "gather"],
                     help="LoRA fold over the sorted rows or slot by slot (auto: by the padding share)")
+    ap.add_argument("--down-lora", default="fused", choices=["fused", "unfused"],
+                    help="down-projection LoRA fold in the down GEMM's epilogue where the fold runs over the sorted "
+                         "rows (default), or the separate shrink and expand kernels")
     ap.add_argument("--gate-up-lora", default="fused", choices=["fused", "unfused"],
                     help="gate/up LoRA folded in the gate/up GEMM's epilogue, or the page's unfused order")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / stream-read / MFMA-loop ceilings")
@@ -427,6 +487,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_seconds": args.warmup_seconds,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",

@@ -14,6 +14,8 @@
  *   moe_silu_mul      SiLU(gate)*up when gate and up are folded separately
  *   moe_quantize_fp8, moe_grouped_gemm_fp8   the fp8 prefill variant of the GEMMs
  *   moe_lora_fold     optional per-expert down-projection LoRA fold, in place
+ *   moe_grouped_gemm_down_lora, moe_grouped_gemm_gate_up_lora   the LoRA folds run
+ *                     in the grouped GEMMs' epilogues
  *   moe_lora_gather_fold  the same fold on slot-major rows (decode, no sorting)
  *   moe_combine       top-k weighted sum of the expert outputs per token
  *
@@ -328,6 +330,31 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
                                          const int32_t* row_adapter,
                                          uint16_t* xa, void* workspace, int64_t workspace_bytes,
                                          moe_stream stream);
+
+/* The down-projection LoRA fold fused into the down GEMM (bf16 weights): the same
+ * result as moe_grouped_gemm with MOE_OP_DOWN followed by moe_lora_fold (x_gather = 0)
+ * over all sorted rows, with the expand and the fold run in the GEMM's epilogue, so
+ * the folded Ys rows are written once instead of written, read back and written again
+ * (atlas moe_lora_grouped.rs, moe_lora_grouped_down: shrink, then expand and fold in
+ * place into the sorted BF16 expert_down_out).  For each real sorted row r of expert e
+ * (token t = sorted_ids[r] / top_k, adapter a = row_adapter[t], 0 without a map):
+ *   y = bf16(Hs[r] Wd[e]^T); if adapter a adapts e (e < n_tab, non-zero entries at [a, e]):
+ *   y = bf16(y + scale[a,e] * bf16(bf16(Hs[r] A[a,e]^T) B[a,e]^T)); ys[r] = y,
+ * fp32 sums.  Sentinel and padding rows are not written.
+ *   hs, w_down, ys, sorted ids ... max_pad, workspace: as moe_grouped_gemm with
+ *   MOE_OP_DOWN (n = hidden, k = intermediate)
+ *   a_table, b_table, scale_table, n_tab, n_adapters, row_adapter: as for moe_lora_fold,
+ *   [n_adapters, n_tab] (A [max_rank, k], B [n, max_rank]); n_tab 0 = plain down GEMM
+ *   xa           bf16 [max_pad, max_rank] scratch (the shrink's results, by sorted row)
+ * Launches the shrink and the GEMM.  MOE_EUNSUPPORTED for non-bf16 weights.
+ * max_rank in {32, 64, 96, 128}. */
+moe_status moe_grouped_gemm_down_lora(const uint16_t* hs, const moe_weight* w_down, uint16_t* ys,
+                                      const int32_t* sorted_ids, const int32_t* expert_offsets, int64_t num_pairs,
+                                      int32_t top_k, int32_t num_experts, int32_t n, int32_t k, int32_t block_size,
+                                      int64_t max_pad, const uint64_t* a_table, const uint64_t* b_table,
+                                      const float* scale_table, int32_t n_tab, int32_t n_adapters, int32_t max_rank,
+                                      const int32_t* row_adapter, uint16_t* xa, void* workspace,
+                                      int64_t workspace_bytes, moe_stream stream);
 
 /* SiLU(gate) * up of the gate/up LoRA path (atlas moe_lora_grouped.rs,
  * moe_lora_gather_bgmv: the caller's moe_silu_mul writes the BF16 activations

@@ -47,6 +47,10 @@ SIGNATURES = {
                                                 c_int32, c_int32, c_int32, c_int32, c_int32, c_int64, c_void_p,
                                                 c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
                                                 c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
+    "moe_grouped_gemm_down_lora": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                                             c_int32, c_int32, c_int32, c_int32, c_int64, c_void_p, c_void_p,
+                                             c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                             c_int64, c_void_p]),
     "moe_quantize_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
     "moe_grouped_gemm_fp8": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int64,

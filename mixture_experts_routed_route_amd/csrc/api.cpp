@@ -482,6 +482,79 @@ moe_status moe_grouped_gemm_gate_up_lora(const uint16_t* x, const moe_weight* w_
                                                static_cast<int>(max_pad), workspace, workspace_bytes, s, &lora));
 }
 
+moe_status moe_grouped_gemm_down_lora(const uint16_t* hs, const moe_weight* w_down, uint16_t* ys,
+                                      const int32_t* sorted_ids, const int32_t* expert_offsets, int64_t num_pairs,
+                                      int32_t top_k, int32_t num_experts, int32_t n, int32_t k, int32_t block_size,
+                                      int64_t max_pad, const uint64_t* a_table, const uint64_t* b_table,
+                                      const float* scale_table, int32_t n_tab, int32_t n_adapters, int32_t max_rank,
+                                      const int32_t* row_adapter, uint16_t* xa, void* workspace,
+                                      int64_t workspace_bytes, moe_stream stream) {
+    const char* who = "moe_grouped_gemm_down_lora";
+    REQUIRE(num_pairs >= 0 && num_pairs < INT32_MAX, "%s: num_pairs out of range", who);
+    REQUIRE(top_k >= 1 && num_pairs % top_k == 0, "%s: num_pairs %lld is not a multiple of top_k %d", who,
+            static_cast<long long>(num_pairs), top_k);
+    REQUIRE(num_experts >= 1, "%s: num_experts %d < 1", who, num_experts);
+    if (num_experts > 256) return fail(MOE_EUNSUPPORTED, "%s: num_experts=%d > 256", who, num_experts);
+    REQUIRE(valid_block_size(block_size), "%s: block_size %d not in {16,32,64,128}", who, block_size);
+    REQUIRE(n >= 8 && n % 8 == 0, "%s: n %d must be a positive multiple of 8", who, n);
+    REQUIRE(k >= 8 && k % 8 == 0, "%s: k %d must be a positive multiple of 8", who, k);
+    REQUIRE(max_pad >= max_padded(num_pairs, num_experts, block_size) && max_pad % block_size == 0 &&
+                max_pad < INT32_MAX,
+            "%s: max_pad %lld must be >= %lld and a multiple of block_size", who, static_cast<long long>(max_pad),
+            static_cast<long long>(max_padded(num_pairs, num_experts, block_size)));
+    REQUIRE(w_down != nullptr, "%s: w_down is required", who);
+    if (w_down->type != MOE_W_BF16)
+        return fail(MOE_EUNSUPPORTED, "%s: the fused down LoRA takes bf16 weights only", who);
+    REQUIRE(max_rank >= 32 && max_rank <= 128 && max_rank % 32 == 0, "%s: max_rank %d not in {32,64,96,128}", who,
+            max_rank);
+    REQUIRE(n_tab >= 0 && n_tab <= num_experts, "%s: n_tab %d not in [0, num_experts=%d]", who, n_tab, num_experts);
+    REQUIRE(n_adapters >= 1 && n_adapters <= 65536, "%s: n_adapters %d not in [1, 65536]", who, n_adapters);
+    if (workspace != nullptr) {
+        const int64_t need = moe_grouped_gemm_workspace_bytes();
+        REQUIRE_PTR(who, workspace);
+        REQUIRE(workspace_bytes >= need, "%s: workspace_bytes %lld < required %lld", who,
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+    }
+    if (num_pairs == 0) return ok();
+    REQUIRE_PTR(who, hs);
+    REQUIRE_PTR(who, ys);
+    REQUIRE_PTR(who, sorted_ids);
+    REQUIRE_PTR(who, expert_offsets);
+    REQUIRE_PTR(who, w_down->data);
+    REQUIRE_PTR(who, xa);
+    if (n_tab > 0) {
+        REQUIRE_PTR(who, a_table);
+        REQUIRE_PTR(who, b_table);
+        REQUIRE_PTR(who, scale_table);
+    }
+    if (row_adapter) REQUIRE_PTR(who, row_adapter);
+    // the kernel addresses Hs rows and each expert matrix with 32-bit byte offsets
+    if (max_pad * k * 2 > INT64_C(0xffffffff) || static_cast<int64_t>(n) * k * 2 > INT64_C(0xffffffff))
+        return fail(MOE_EUNSUPPORTED, "%s: hs or an expert matrix exceeds 4 GiB", who);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int P = static_cast<int>(num_pairs);
+    hipError_t err = hipSuccess;
+    if (n_tab > 0)
+        err = moe::launch_lora_shrink(hs, a_table, b_table, n_tab, n_adapters, k, max_rank, expert_offsets,
+                                      num_experts, sorted_ids, P, top_k, row_adapter, xa, 0, max_pad, 0, s);
+    if (err != hipSuccess) return launched(who, err);
+    moe::GateUpLora lora{};
+    for (int i = 0; i < 2; ++i) {  // the one projection's tables in both slots (the two column halves)
+        lora.xa[i] = xa;
+        lora.a_tab[i] = a_table;
+        lora.b_tab[i] = b_table;
+        lora.s_tab[i] = scale_table;
+        lora.n_tab[i] = n_tab;
+    }
+    lora.n_ad = n_adapters;
+    lora.rank = max_rank;
+    lora.row_adapter = row_adapter;
+    return launched(who, moe::launch_gemm_bf16(moe::kOpDown, hs, static_cast<const uint16_t*>(w_down->data), nullptr,
+                                               ys, sorted_ids, expert_offsets, P, top_k, num_experts, n, k,
+                                               static_cast<int>(max_pad), workspace, workspace_bytes, s,
+                                               n_tab > 0 ? &lora : nullptr));
+}
+
 moe_status moe_quantize_fp8(const uint16_t* x, int64_t rows, int32_t k, const int32_t* sorted_ids,
                             int64_t num_pairs, uint8_t* q, float* scale, moe_stream stream) {
     const char* who = "moe_quantize_fp8";

@@ -151,8 +151,9 @@ struct Fp8Scales {
     const float* w1;
 };
 
-// LORA: 0 no gate/up LoRA; 1 one adapter (every folded row is adapter 0); 2 several adapters (the
-// rows of one fragment may belong to different adapters: one pass per adapter present).  The
+// LORA: 0 no LoRA epilogue (gate/up, or with GATE_UP false the down projection); 1 one adapter (every
+// folded row is adapter 0; down: only at rank == BK, folded from LDS); 2 any adapters (the rows of one
+// fragment may belong to different adapters: one pass per adapter present; down: any rank).  The
 // one-adapter form is the common case and keeps the lean epilogue, which the loop of the general
 // form would cost registers in the main loop.
 template <bool GATE_UP, int BM, int BK, int STAGES, int NW, int LORA = 0, bool FP8 = false>
@@ -165,7 +166,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                                                           int E, int N, int K, int max_pad, int n_tiles,
                                                           float* __restrict__ sk_part, int32_t* __restrict__ sk_cnt,
                                                           int sk_on, int a_tok, GateUpLora lora, Fp8Scales f8) {
-    static_assert(!LORA || GATE_UP, "the LoRA epilogue is the gate/up one");
     static_assert(!(LORA && FP8), "no LoRA epilogue in the fp8 form");
     using TE = Elem<FP8>;
     constexpr int ES = sizeof(TE);
@@ -276,17 +276,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
     auto load_rows = [&](int buf, int r0, int r_end) __attribute__((always_inline)) {
         for (int i = tid; i < BM; i += NT) {
             const int r = r0 + i;
-            int src = -1;
+            int src = -1, tok = -1;
             if (r < r_end) {
                 const int p = sorted_ids[r];
-                if (p >= 0 && p < P) src = (GATE_UP || a_tok) ? p / top_k : r;
+                if (p >= 0 && p < P) {
+                    tok = p / top_k;
+                    src = (GATE_UP || a_tok) ? tok : r;
+                }
             }
             s_row[buf][i] = src;
             if constexpr (FP8) s_as[buf][i] = src >= 0 ? f8.a[src] : 0.f;
             if constexpr (LORA) {
                 // the token's adapter (atlas: a mixed batch's adapter comes from the per-row map); 0
                 // without a map; -1 for rows without a token or with an id outside [0, n_ad)
-                int a = src >= 0 ? (lora.row_adapter ? lora.row_adapter[src] : 0) : -1;
+                int a = tok >= 0 ? (lora.row_adapter ? lora.row_adapter[tok] : 0) : -1;
                 s_rad[buf][i] = (a >= 0 && a < lora.n_ad) ? a : -1;
             }
             if (src >= 0) atomicMax(&s_h[buf], i + 1);
@@ -547,7 +550,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
         if constexpr (PF) {
             if (pf && tid < BM) {
                 const int p = r02 + tid < r_end2 ? s_pf[tid] : -1;
-                const int src = (p >= 0 && p < P) ? ((GATE_UP || a_tok) ? p / top_k : r02 + tid) : -1;
+                const int tok = (p >= 0 && p < P) ? p / top_k : -1;
+                const int src = tok >= 0 ? ((GATE_UP || a_tok) ? tok : r02 + tid) : -1;
                 s_row[buf ^ 1][tid] = src;
                 if (src >= 0) atomicMax(&s_h[buf ^ 1], tid + 1);
                 // fp8: the rows' activation scales, straight into LDS as well (a row without a
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                 // barrier, below); without a map every row with a token is adapter 0
                 if constexpr (LORA) {
                     if (lora.row_adapter != nullptr)
-                        dma4(lora.row_adapter + (src >= 0 ? src : 0), lds_u32(s_rad[buf ^ 1]) + wave * 256);
+                        dma4(lora.row_adapter + (tok >= 0 ? tok : 0), lds_u32(s_rad[buf ^ 1]) + wave * 256);
                     else
                         s_rad[buf ^ 1][tid] = src >= 0 ? 0 : -1;
                 }
@@ -733,9 +737,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
             sb -= nseg;
         }
 
-        // ---- gate/up LoRA (the page's order: bf16 gate and up outputs, each folded, then SiLU * up):
+        // ---- LoRA epilogue (the page's order: the bf16 GEMM output, folded, then for gate/up SiLU * up):
         // every accumulator becomes a bf16 value, bf16(bf16(acc) + scale * bf16(xa . B_e^T)) where
-        // the row is folded.  The bf16 values are held two to a register while the deltas are formed,
+        // the row is folded.  Gate/up: pass pj = 0 folds the gate blocks 0, 1 with the gate tables and
+        // pj = 1 the up blocks 2, 3 with the up tables, over the same output columns.  Down (the
+        // down-projection fold of the expert outputs): the host passes the one set of tables in both
+        // slots, and pass pj folds blocks 2 pj, 2 pj + 1, the wave's columns 64 pj .. 64 pj + 63.  The bf16 values are held two to a register while the deltas are formed,
         // which leaves the registers for a projection's whole delta: its four 32x32 blocks as 32x32x16
         // MFMAs over the rank, fed by xa and B_e fragments read straight from memory, up to 64 of the
         // rank at a time.  A chunk's fragment loads are all issued before its MFMAs (the scheduling
@@ -789,8 +796,102 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                     table(0, 0, ad0_b[0], ad0_s[0]);
                     table(1, 0, ad0_b[1], ad0_s[1]);
                 }
+                // Down, one adapter (the host launches this form only with rank == BK): the delta is one
+                // more K stage of the tile, with the xa rows as A and the B_e rows of the panel as the
+                // weight panel.  The last stage's LDS buffer is free once every wave is past its reads
+                // (the next tile's first stage went to another buffer), so the whole workgroup loads
+                // that stage straight into it, in the main loop's layout and swizzle, and each wave's
+                // delta blocks then run from LDS with the main loop's fragment reads: one memory round
+                // trip per tile instead of one per column half and rank chunk, and no register form
+                // beside it, whose pressure spilled into the main loop.  Uniform over the workgroup:
+                // e and the tables are.
+                if constexpr (LORA == 1 && !GATE_UP && !FP8) {
+                    if (ad0_b[0] != nullptr) {
+                        const int lb = (sb + nseg - 1) % STAGES;  // the last stage's buffer
+                        const uint32_t lds_st = lds_u32(smem) + static_cast<uint32_t>(lb) * (F::STAGE_ELEMS * ES);
+                        __syncthreads();  // every wave is past its reads of the last stage
+                        constexpr int INSTS = (BM + BP) / F::ROWS_PER_INST;  // 1 KB loads for the stage
+                        const uint16_t* Be = ad0_b[0];
+                        for (int g = wave; g < INSTS; g += NW) {
+                            const int row = g * F::ROWS_PER_INST + lrow;
+                            const int kc = swz_chunk(row, pc, F::RP, F::CPR);
+                            // rows past the span or past N read a row in bounds; never stored
+                            const uint16_t* src =
+                                row < BM ? lora.xa[0] + static_cast<size_t>(min(r0 + row, max_pad - 1)) * BK + kc * CE
+                                         : Be + static_cast<size_t>(min(n0 + row - BM, N - 1)) * BK + kc * CE;
+                            dma16(src, lds_st + g * 1024);
+                        }
+                        wait_vmcnt<0>();
+                        __syncthreads();
+                        const TE* st = smem + lb * F::STAGE_ELEMS;
+                        const float sc = ad0_s[0];
+                        // with a row map: bit i * 16 + v set when value v of fragment i is in a folded row
+                        const bool has_map = lora.row_adapter != nullptr;
+                        uint32_t fmask = 0;
+                        if (has_map) {
 #pragma unroll
-                for (int pj = 0; pj < 2; ++pj) {  // 0: gate (blocks 0, 1), 1: up (blocks 2, 3)
+                            for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) fmask |= (row_ad(i, v) == 0 ? 1u : 0u) << (i * 16 + v);
+                        }
+                        // k-step kk's fragments of column half pj into register set `set`
+                        bf16x8 xf[2][F::FI], bw[2][2];
+                        auto lread = [&](int pj, int kk, int set) __attribute__((always_inline)) {
+                            const int cx = ((kk * 2 + fc) ^ fswz) << 3;
+#pragma unroll
+                            for (int i = 0; i < F::FI; ++i) xf[set][i] = *reinterpret_cast<const bf16x8*>(st + a_off[i] + cx);
+#pragma unroll
+                            for (int jj = 0; jj < 2; ++jj)
+                                bw[set][jj] = *reinterpret_cast<const bf16x8*>(st + b_off[2 * pj + jj] + cx);
+                        };
+#pragma unroll
+                        for (int pj = 0; pj < 2; ++pj) {  // the wave's column halves: blocks 2 pj, 2 pj + 1
+                            f32x16 d[F::FI][2];
+#pragma unroll
+                            for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                                    for (int v = 0; v < 16; ++v) d[i][jj][v] = 0.f;
+                            // rank order, as the register form: every delta block sums k 0, 16, 32, 48;
+                            // the next k-step's fragments are read while this one's MFMAs run
+                            lread(pj, 0, 0);
+#pragma unroll
+                            for (int kk = 0; kk < KK; ++kk) {
+                                if (kk + 1 < KK) lread(pj, kk + 1, (kk + 1) & 1);
+#pragma unroll
+                                for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                                    for (int jj = 0; jj < 2; ++jj)
+                                        d[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[kk & 1][i], bw[kk & 1][jj],
+                                                                                          d[i][jj], 0, 0, 0);
+                            }
+                            // a pair of values (rows rl, rl + 1 of one column): the bf16 deltas in one
+                            // conversion, the two folds, and the results rounded in one more; without a
+                            // row map every row with a token is folded, and rows without one are never
+                            // stored, so only a map needs the per-row choice
+#pragma unroll
+                            for (int i = 0; i < F::FI; ++i)
+#pragma unroll
+                                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                                    for (int h = 0; h < 8; ++h) {
+                                        uint32_t& w = pk[i][pj * 2 + jj][h];
+                                        const uint32_t dv = pack_bf16x2(d[i][jj][2 * h], d[i][jj][2 * h + 1]);
+                                        uint32_t nw = pack_bf16x2(fmaf(sc, lo16(dv), lo16(w)), fmaf(sc, hi16(dv), hi16(w)));
+                                        if (has_map) {
+                                            const uint32_t keep = ((fmask >> (i * 16 + 2 * h)) & 1u ? 0u : 0xffffu) |
+                                                                  ((fmask >> (i * 16 + 2 * h + 1)) & 1u ? 0u : 0xffff0000u);
+                                            nw = (nw & ~keep) | (w & keep);
+                                        }
+                                        w = nw;
+                                    }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int pj = 0; pj < 2; ++pj) {  // gate/up: 0 gate (blocks 0, 1), 1 up (blocks 2, 3); down: halves
+                    if constexpr (LORA == 1 && !GATE_UP) break;  // folded from LDS above
                     if (e >= lora.n_tab[pj]) continue;  // past every adapter's table: not adapted
                     // this lane's xa rows (clamped: rows past the span are computed and never stored)
                     const uint16_t* xr[F::FI];
@@ -805,7 +906,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                         const uint16_t* br[2];
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
-                            const int col = min(n0 + wn * 64 + jj * 32 + fr, N - 1);
+                            const int col = min(n0 + (GATE_UP ? wn * 64 : wn * 128 + pj * 64) + jj * 32 + fr, N - 1);
                             br[jj] = Be + static_cast<size_t>(col) * lora.rank + fc * 8;
                         }
                         f32x16 d[F::FI][2];
@@ -997,6 +1098,15 @@ hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const
     // 256-row tiles (8 waves) when experts average at least MOE_GEMM_BIG_ROWS rows, where a 128-row
     // tiling would read most weight panels twice; 128-row tiles (4 waves) for fewer rows
     const bool big = static_cast<long long>(P) >= static_cast<long long>(MOE_GEMM_BIG_ROWS) * E;
+    // down, one adapter at a rank equal to the stage depth: the delta as one more LDS stage
+    if (op == kOpDown && lora && lora->n_ad == 1 && lora->rank == (big ? MOE_GEMM_BIG_BK : 64)) {
+        if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, 1>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 0, s, *lora);
+        return launch_cfg<false, 128, 64, 3, 4, 1>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 0, s, *lora);
+    }
+    if (op == kOpDown && lora) {
+        if (big) return launch_cfg<false, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, 2>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 0, s, *lora);
+        return launch_cfg<false, 128, 64, 3, 4, 2>(a, w0, nullptr, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 0, s, *lora);
+    }
     if (op == kOpGateUpSilu && lora && lora->n_ad == 1) {
         if (big) return launch_cfg<true, 256, MOE_GEMM_BIG_BK, MOE_GEMM_BIG_STAGES, 8, 1>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);
         return launch_cfg<true, 128, 64, 3, 4, 1>(a, w0, w1, c, sorted_ids, offsets, P, top_k, E, N, K, max_pad, ws, ws_bytes, 1, s, *lora);

@@ -36,10 +36,10 @@ hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int 
 hipError_t launch_combine(const uint16_t* ys, const int32_t* inv, const float* w, uint16_t* out, int T, int k,
                           int H, int64_t ys_rows, hipStream_t s);
 
-// LoRA of the gate and up projections folded in the bf16 gate/up GEMM's epilogue.  For each
-// projection p (0 gate, 1 up): xa[p] = bf16 shrink results [max_pad, rank] of the sorted rows, and
-// the expert tables, n_ad rows of n_tab[p] entries, row a for the tokens of adapter a (n_tab[p] == 0:
-// no tables, the projection is only rounded to bf16).
+// LoRA folded in the bf16 grouped GEMM's epilogue.  Gate/up: for each projection p (0 gate, 1 up):
+// xa[p] = bf16 shrink results [max_pad, rank] of the sorted rows, and the expert tables, n_ad rows of
+// n_tab[p] entries, row a for the tokens of adapter a (n_tab[p] == 0: no tables, the projection is
+// only rounded to bf16).  Down: the one projection's shrink results and tables in both slots.
 struct GateUpLora {
     const uint16_t* xa[2];
     const uint64_t* a_tab[2];
@@ -52,7 +52,7 @@ struct GateUpLora {
 };
 
 // gemm_bf16.hip (ws: optional split-tail workspace, zero-filled before first use; NULL = none;
-// lora: gate/up op only, NULL = plain SiLU(gate) * up)
+// lora: gate/up or down op, NULL = no fold)
 int64_t gemm_bf16_workspace_bytes();
 hipError_t launch_gemm_bf16(int op, const uint16_t* a, const uint16_t* w0, const uint16_t* w1, uint16_t* c,
                             const int32_t* sorted_ids, const int32_t* offsets, int P, int top_k, int E, int N,

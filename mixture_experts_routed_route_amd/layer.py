@@ -13,7 +13,9 @@ never writes.
 A LoRA fold runs either over the sorted rows, window by window (``moe_lora_fold``), or
 slot by slot through the inverse map (``moe_lora_gather_fold``).  The second has a grid of one
 workgroup per (token, slot) pair instead of one per 16 sorted rows of the worst-case layout,
-which is what decode batches want: there the sorted layout is mostly padding.
+which is what decode batches want: there the sorted layout is mostly padding.  Over the sorted
+rows with bf16 weights, the down-projection fold runs by default in the down GEMM's epilogue
+(``moe_grouped_gemm_down_lora``), as the gate and up folds run in the gate/up GEMM's.
 
 Buffers are allocated once per token count (``plan``) so a forward pass allocates
 nothing and its launch grids depend on host scalars only.
@@ -30,7 +32,7 @@ from ._lib import MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER
 from .ops import (Bf16Weight, Fp8Weight, GptqWeight, LoraTables, Routing, gemm_workspace, lora_windows,
                   moe_align, moe_combine, moe_grouped_gemm, moe_grouped_gemm_fp8, moe_lora_fold, moe_lora_gather_fold,
                   moe_quantize_fp8, moe_route, moe_route_align, moe_silu_mul, pack_lora_tables, stack_lora_tables,
-                  moe_grouped_gemm_gate_up_lora)
+                  moe_grouped_gemm_gate_up_lora, moe_grouped_gemm_down_lora)
 
 FOLD_MODES = ("auto", "grouped", "gather")
 
@@ -58,7 +60,7 @@ class MoeLayer:
     def __init__(self, num_experts: int, hidden: int, inter: int, top_k: int, block_size: int, gate, up, down,
                  lora: Optional[LoraTables] = None, renormalize: bool = True, lora_cap: Optional[int] = None,
                  fold: str = "auto", lora_gate: Optional[LoraTables] = None, lora_up: Optional[LoraTables] = None,
-                 gate_up_fused: bool = True):
+                 gate_up_fused: bool = True, down_fused: bool = True):
         if fold not in FOLD_MODES:
             raise ValueError(f"fold must be one of {FOLD_MODES}")
         if isinstance(gate, Fp8Weight) and (lora_gate is not None or lora_up is not None):
@@ -72,6 +74,9 @@ class MoeLayer:
         # gate/up LoRA folded in the gate/up GEMM's epilogue (bf16 weights), else the page's order:
         # gathered gate and up, a fold into each, SiLU * up
         self.gate_up_fused = gate_up_fused and isinstance(gate, Bf16Weight)
+        # down-projection LoRA folded in the down GEMM's epilogue where the fold runs over the sorted
+        # rows (bf16 weights), else the shrink and expand kernels after the down GEMM
+        self.down_fused = down_fused and isinstance(down, Bf16Weight)
 
     @property
     def fp8(self) -> bool:
@@ -87,7 +92,7 @@ class MoeLayer:
     # ------------------------------------------------------------------ construction from host arrays
     @staticmethod
     def from_arrays(d: Dict[str, object], device, lora_cap: Optional[int] = None, fold: str = "auto",
-                    gate_up_fused: bool = True) -> "MoeLayer":
+                    gate_up_fused: bool = True, down_fused: bool = True) -> "MoeLayer":
         """Build from host numpy arrays (bf16 / fp16 as uint16 bit patterns, GPTQ words as int32)."""
         cfg = d["cfg"]
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
@@ -123,7 +128,7 @@ class MoeLayer:
         lora_gate = tables("lora_gate")
         lora_up = tables("lora_up")
         return MoeLayer(cfg.E, cfg.H, cfg.I, cfg.top_k, cfg.block_size, gate, up, down, lora, cfg.renormalize,
-                        lora_cap, fold, lora_gate, lora_up, gate_up_fused)
+                        lora_cap, fold, lora_gate, lora_up, gate_up_fused, down_fused)
 
     # ------------------------------------------------------------------ buffers
     def plan(self, T: int, device) -> Buffers:
@@ -178,16 +183,28 @@ class MoeLayer:
             self._fold(self.lora_up, x, b.u, b, row_adapter, x_gather=True)
         moe_silu_mul(b.g, b.u, b.hs, b.routing)
 
-    def down_stage(self, b: Buffers) -> None:
+    def down_stage(self, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
+        """Ys from Hs; with the fused down fold, the LoRA shrink and the down GEMM whose epilogue folds."""
         if self.fp8:  # the real rows of Hs quantised per row, then the fp8 down GEMM
             moe_quantize_fp8(b.hs, b.hq, b.sh, b.routing)
             moe_grouped_gemm_fp8(MOE_OP_DOWN, b.hq, b.sh, self.down, None, b.routing, out=b.ys, workspace=b.ws)
             return
+        if self.down_fold_fused(b):
+            R, mp = self.lora.max_rank, b.routing.max_pad
+            moe_grouped_gemm_down_lora(b.hs, self.down, b.routing, self.lora, b.xa[: mp * R].view(mp, R), out=b.ys,
+                                       row_adapter=row_adapter, workspace=b.ws)
+            return
         moe_grouped_gemm(MOE_OP_DOWN, b.hs, self.down, None, b.routing, out=b.ys, workspace=b.ws)
+
+    def down_fold_fused(self, b: Buffers) -> bool:
+        """Whether the down-projection fold runs in the down GEMM's epilogue for these buffers: down
+        tables, bf16 weights, the fold over the sorted rows, and a shrink scratch for every sorted row."""
+        return (self.lora is not None and self.down_fused and self.fold_mode(b) == "grouped"
+                and b.xa.numel() >= b.routing.max_pad * self.lora.max_rank)
 
     def experts(self, x: torch.Tensor, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
         self.gate_up_stage(x, b, row_adapter)
-        self.down_stage(b)
+        self.down_stage(b, row_adapter)
         self.lora_fold(b, row_adapter)
 
     def fold_mode(self, b: Buffers) -> str:
@@ -212,8 +229,8 @@ class MoeLayer:
             moe_lora_fold(x, base, tables, b.routing, row_adapter, xa, s, e, x_gather=x_gather)
 
     def lora_fold(self, b: Buffers, row_adapter: Optional[torch.Tensor] = None) -> None:
-        """The down-projection fold into Ys (none without down tables)."""
-        if self.lora is not None:
+        """The down-projection fold into Ys (none without down tables, or when the down GEMM folded)."""
+        if self.lora is not None and not self.down_fold_fused(b):
             self._fold(self.lora, b.hs, b.ys, b, row_adapter, x_gather=False)
 
     def combine(self, b: Buffers) -> torch.Tensor:

@@ -16,7 +16,7 @@ from ._lib import (MOE_OP_DOWN, MOE_OP_GATE_UP_SILU, MOE_OP_GATHER, MOE_W_BF16, 
 
 __all__ = [
     "Bf16Weight", "GptqWeight", "Fp8Weight", "Routing", "moe_quantize_fp8", "moe_grouped_gemm_fp8", "LoraTables", "max_padded", "align_workspace_bytes",
-    "moe_route", "moe_align", "moe_align_noalloc", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "stack_lora_tables", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_combine", "pack_lora_tables",
+    "moe_route", "moe_align", "moe_align_noalloc", "moe_route_align", "moe_grouped_gemm", "gemm_workspace", "moe_lora_fold", "moe_lora_gather_fold", "stack_lora_tables", "moe_silu_mul", "moe_grouped_gemm_gate_up_lora", "moe_grouped_gemm_down_lora", "moe_combine", "pack_lora_tables",
     "lora_windows", "lora_window_tiles", "check_group_arrays",
 ]
 
@@ -470,6 +470,33 @@ def moe_grouped_gemm_gate_up_lora(x: torch.Tensor, gate: Bf16Weight, up: Bf16Wei
         _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
         _dev(xa, torch.bfloat16, "xa"), _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream(x)))
+    return out
+
+
+def moe_grouped_gemm_down_lora(hs: torch.Tensor, down: Bf16Weight, routing: Routing, tables: LoraTables,
+                               xa: torch.Tensor, out: Optional[torch.Tensor] = None,
+                               row_adapter: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Ys with the down-projection LoRA folded in the down GEMM's epilogue; xa: bf16 [max_pad, max_rank]."""
+    E, N, K = down.shape
+    who = "moe_grouped_gemm_down_lora"
+    _need(tables.k_in == K and tables.n_out == N,
+          f"{who}: tables are [{tables.n_out} x {tables.k_in}], the weights [{N} x {K}]")
+    _need(tuple(xa.shape) == (routing.max_pad, tables.max_rank), f"{who}: xa must be [{routing.max_pad}, {tables.max_rank}]")
+    if out is None:
+        out = torch.empty((routing.max_pad, N), dtype=torch.bfloat16, device=hs.device)
+    _check_gemm_shapes(MOE_OP_DOWN, hs, down, None, routing, out, who)
+    _numel_at_least(row_adapter, routing.num_pairs // routing.top_k, f"{who}: row_adapter")
+    sd = down.struct()
+    check(lib().moe_grouped_gemm_down_lora(
+        _dev(hs, torch.bfloat16, "hs"), ctypes.byref(sd), _dev(out, torch.bfloat16, "out"),
+        _dev(routing.sorted_ids, torch.int32, "sorted_ids"), _dev(routing.offsets, torch.int32, "offsets"),
+        routing.num_pairs, routing.top_k, routing.num_experts, N, K, routing.block_size, routing.max_pad,
+        _dev(tables.a_table, torch.int64, "a_table"), _dev(tables.b_table, torch.int64, "b_table"),
+        _dev(tables.scale_table, torch.float32, "scale_table"), tables.n_tab, tables.n_adapters, tables.max_rank,
+        _dev(row_adapter, torch.int32, "row_adapter") if row_adapter is not None else None,
+        _dev(xa, torch.bfloat16, "xa"), _dev(workspace, torch.uint8, "workspace") if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream(hs)))
     return out
 
 

@@ -24,7 +24,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     from mixture_experts_routed_route_amd import _lib
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
@@ -199,6 +199,19 @@ def test_argument_validation_rejects_before_launch(L):
     assert rc == -2 and "bf16" in msg
     rc, msg = lg(w, 48)
     assert rc == -1 and "max_rank" in msg
+    # fused down LoRA: (hs, w_down, ys, sorted_ids, offsets, P, top_k, E, n, k, bs, max_pad, a, b, s, n_tab,
+    #                    n_adapters, max_rank, row_adapter, xa, ws, ws_bytes, stream)
+    ld = lambda wd, rank, n_tab=8, n_ad=1: _rc(L, "moe_grouped_gemm_down_lora", fake, ctypes.byref(wd), fake, fake,
+                                               fake, 128, 2, 8, 256, 128, 16, 256, fake, fake, fake, n_tab, n_ad,
+                                               rank, None, fake, None, 0, None)
+    rc, msg = ld(w4, 64)
+    assert rc == -2 and "bf16" in msg
+    rc, msg = ld(w, 48)
+    assert rc == -1 and "max_rank" in msg
+    rc, msg = ld(w, 64, n_tab=9)
+    assert rc == -1 and "n_tab" in msg
+    rc, msg = ld(w, 64, n_ad=0)
+    assert rc == -1 and "n_adapters" in msg
     rc, msg = _rc(L, "moe_lora_fold", fake, fake, fake, fake, fake, 63, 0, 1408, 4096, 64, fake, 64, fake, 12288, 6,
                   None, fake, 16320, 0, 16320, 16320, 0, None)
     assert rc == -1 and "n_adapters" in msg

@@ -97,6 +97,25 @@ def test_lora_fold_rejects_mismatched_buffers():
                         row_adapter=torch.zeros(T - 1, dtype=torch.int32))
 
 
+def test_down_lora_rejects_mismatched_buffers():
+    r = routing()
+    tabs = m.LoraTables(torch.zeros(E, dtype=torch.int64), torch.zeros(E, dtype=torch.int64),
+                        torch.zeros(E, dtype=torch.float32), E, I, H, 32)
+    xa = bf(r.max_pad, 32)
+    wd = w(n=H, k=I)
+    with pytest.raises(ValueError, match="xa must be"):
+        m.moe_grouped_gemm_down_lora(bf(r.max_pad, I), wd, r, tabs, bf(r.max_pad - 16, 32), out=bf(r.max_pad, H))
+    with pytest.raises(ValueError, match="tables are"):
+        m.moe_grouped_gemm_down_lora(bf(r.max_pad, I), w(n=H, k=I + 8), r, tabs, xa, out=bf(r.max_pad, H))
+    with pytest.raises(ValueError, match="rows"):
+        m.moe_grouped_gemm_down_lora(bf(r.max_pad - 1, I), wd, r, tabs, xa, out=bf(r.max_pad, H))
+    with pytest.raises(ValueError, match="out is"):
+        m.moe_grouped_gemm_down_lora(bf(r.max_pad, I), wd, r, tabs, xa, out=bf(r.max_pad - 16, H))
+    with pytest.raises(ValueError, match="row_adapter"):
+        m.moe_grouped_gemm_down_lora(bf(r.max_pad, I), wd, r, tabs, xa, out=bf(r.max_pad, H),
+                                     row_adapter=torch.zeros(T - 1, dtype=torch.int32))
+
+
 def test_stack_lora_tables_layout():
     """Adapter a's tables land in row a of the [n_adapters, n_tab] stack; shorter tables and
     missing adapters are padded with unadapted (zero) entries."""

@@ -959,7 +959,7 @@ def test_grouped_gemms_full_size_rows(dev, name):
     note(f"full-size GEMM rows {name}")
     d = make_inputs(cfg)
     m = ops()
-    layer = m.MoeLayer.from_arrays(d, "cuda")
+    layer = m.MoeLayer.from_arrays(d, "cuda", down_fused=False)   # the plain down GEMM first
     b = layer.plan(cfg.T, "cuda")
     x = bf16_dev(d["x"])
     layer.route_align(to_dev(d["logits"]), b)
@@ -992,6 +992,25 @@ def test_grouped_gemms_full_size_rows(dev, name):
         y = oracle.grouped_down(hs_gpu, wd, al, rows=rows_dn)
     assert_close_rows(hs_gpu[rows_gu], h[rows_gu], TOL, f"{name} gate/up rows")
     assert_close_rows(ys_gpu[rows_dn], y[rows_dn], TOL, f"{name} down rows")
+    if layer.lora is not None and not fp8:
+        # the down-projection fold in the down GEMM's epilogue, as the bench runs it: on the selected
+        # rows against the oracle's fold of this plain down output; rows it does not fold unchanged
+        plain = bits_host(b.ys)
+        layer.down_fused = True
+        assert layer.down_fold_fused(b)
+        layer.down_stage(b)
+        torch.cuda.synchronize()
+        fb = bits_host(b.ys)
+        tabs = oracle.moe_oracle._lora_tables(d)
+        H = oracle.bf16_bits_to_f64(bits_host(b.hs))
+        ref = oracle.lora_fold(oracle.bf16_bits_to_f64(plain), H, tabs, al, cfg.top_k)
+        sd = oracle.lora_fold(np.zeros(ref.shape), H, tabs, al, cfg.top_k, bf16_base=False)
+        ref_bits = f32_to_bf16_bits(ref[rows_dn].astype(np.float32))
+        same = np.all(ref_bits == plain[rows_dn], axis=1)
+        assert np.array_equal(fb[rows_dn][same], plain[rows_dn][same])
+        folded = rows_dn[~same]
+        assert folded.size > 0
+        _gather_check(fb, ref, sd, plain, folded, f"{name} fused down fold, {folded.size} selected rows")
 
 
 @pytest.mark.parametrize("name,fold", [("lora_small", "grouped"), ("lora_small", "gather"),
@@ -1004,7 +1023,7 @@ def test_layer_lora_fold_modes(dev, name, fold):
     cfg = SMALL[name]
     note(f"layer fold {name} {fold}")
     d = make_inputs(cfg)
-    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold)
+    layer = m.MoeLayer.from_arrays(d, "cuda", fold=fold, down_fused=False)   # the fold kernels after the GEMMs
     b = layer.plan(cfg.T, "cuda")
     assert layer.fold_mode(b) == fold
     layer.route_align(to_dev(d["logits"]), b)

@@ -1,6 +1,6 @@
 """CPU models of the addressing of every kernel that computes addresses from device-resident ids
 (besides the bf16 GEMM, modelled in test_gemm_addressing): the int4 GEMM, the fp8 form of the bf16
-GEMM (byte addressing and scales; its schedule is the bf16 one), the gate/up LoRA epilogue of the bf16 GEMM, the grouped fold's shrink and expand,
+GEMM (byte addressing and scales; its schedule is the bf16 one), the LoRA epilogue of the bf16 GEMM (gate/up and down), the grouped fold's shrink and expand,
 and the gather fold.  Each model restates the kernel's integer arithmetic and yields every
 (buffer, index, extent) a launch can address; the tests show all of them in bounds on the routings of
 the workloads and on tight routings whose padded total reaches the sorted capacity.  CPU only."""
@@ -115,11 +115,14 @@ def fp8_touched(al, P, top_k, E, N, K, BM, gate_up):
 
 
 # ----------------------------------------------------------------------------- gate/up LoRA epilogue
-def lora_epilogue_touched(al, P, top_k, E, N, BM, rank, n_tab, n_ad, ra):
-    """The LoRA epilogue of gemm_bf16_kernel (gate/up, 2 x 4 wave grid of 64 x 128 per wave in a
-    256-row tile, 2 x 2 of 64 x 64 in a 128-row tile): xa rows min(r0 + wm*WM + i*32 + fr, max_pad - 1)
-    of [2, max_pad, rank], B_e rows min(n0 + wn*64 + jj*32 + fr, N - 1) of [N, rank], table entries
-    a * n_tab + e for the adapters of the tile's rows, and row_adapter at each row's token."""
+def lora_epilogue_touched(al, P, top_k, E, N, BM, rank, n_tab, n_ad, ra, gate_up=True):
+    """The LoRA epilogue of gemm_bf16_kernel (a 4 x 2 wave grid of 64 x 128 per wave in a 256-row
+    tile, 2 x 2 in a 128-row tile; a 256-row weight panel): xa rows min(r0 + wm*WM + i*32 + fr,
+    max_pad - 1) of [max_pad, rank], B_e rows of [N, rank] at min(n0 + wn*64 + jj*32 + fr, N - 1) for
+    gate/up (128 output columns per panel, each projection's two blocks) or min(n0 + wn*128 + pj*64 +
+    jj*32 + fr, N - 1) for down (256 output columns per panel, pass pj folding blocks 2 pj, 2 pj + 1),
+    table entries a * n_tab + e for the adapters of the tile's rows, and row_adapter at each row's
+    token."""
     max_pad = len(al["sorted_ids"])
     sid = al["sorted_ids"]
     lo, hi = _spans(al, E, max_pad)
@@ -138,16 +141,19 @@ def lora_epilogue_touched(al, P, top_k, E, N, BM, rank, n_tab, n_ad, ra):
                     a = int(ra[tok]) if ra is not None else 0
                     if 0 <= a < n_ad:
                         ads.add(a)
-            for n_t in range(-(-N // 128)):
-                n0 = n_t * 128
+            ncol = 128 if gate_up else 256
+            for n_t in range(-(-N // ncol)):
+                n0 = n_t * ncol
                 for wm in range(NW // 2):
                     for i in range(2):
                         for fr in (0, 31):
                             yield "xa", min(r0 + wm * WM + i * 32 + fr, max_pad - 1), max_pad
                 for wn in range(2):
-                    for jj in range(2):
-                        for fr in (0, 31):
-                            yield "B_e", min(n0 + wn * 64 + jj * 32 + fr, N - 1) * rank + rank - 1, N * rank
+                    for pj in range(2):
+                        for jj in range(2):
+                            for fr in (0, 31):
+                                col = n0 + (wn * 64 if gate_up else wn * 128 + pj * 64) + jj * 32 + fr
+                                yield "B_e", min(col, N - 1) * rank + rank - 1, N * rank
                 if e < n_tab:
                     for a in ads:
                         yield "table", a * n_tab + e, n_ad * n_tab
@@ -284,7 +290,7 @@ def test_fp8_gemm_addresses_in_bounds(case, BM):
 
 
 @pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
-def test_gate_up_lora_epilogue_addresses_in_bounds(case):
+def test_lora_epilogue_addresses_in_bounds(case):
     name, top_k, E, bs, ids = case
     al = oracle.align(ids, E, bs)
     P = ids.size
@@ -292,7 +298,9 @@ def test_gate_up_lora_epilogue_addresses_in_bounds(case):
     ra = np.random.default_rng(1).integers(-1, 4, T).astype(np.int32)   # ids past n_ad included
     for BM in (128, 256):
         for n_tab, n_ad, rmap in ((E, 1, None), (max(1, E - 1), 3, ra)):
-            _check(lora_epilogue_touched(al, P, top_k, E, 200, BM, 64, n_tab, n_ad, rmap), f"{name} epilogue")
+            for gate_up, N in ((True, 200), (False, 200), (False, 520)):
+                _check(lora_epilogue_touched(al, P, top_k, E, N, BM, 64, n_tab, n_ad, rmap, gate_up),
+                       f"{name} epilogue gate_up={gate_up} N={N}")
 
 
 @pytest.mark.parametrize("case", _routings(), ids=lambda c: c[0])
