@@ -284,7 +284,9 @@ def run_workload(name: str, args, dev) -> dict:
     log(f"[bench] {name}: warmup {n_warm} steps in {time.perf_counter() - t0:.2f} s")
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    if args.graph:
+    # small batches are launch-bound: by default their steps replay from HIP graphs
+    use_graph = args.graph or args.launch == "graph" or (args.launch == "auto" and cfg.T <= 64)
+    if use_graph:
         # the path allocates nothing and issues no memset, so a step captures as it runs eagerly
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
@@ -411,7 +413,7 @@ def run_workload(name: str, args, dev) -> dict:
         "top_k": cfg.top_k, "block_size": cfg.block_size, "weights": cfg.weights, "lora_rank": cfg.lora_rank,
         **({"lora_fold": "fused" if fused_fold else layer.fold_mode(b)} if has_fold else {}),
         **({"lora_gate_up": "fused" if layer.gate_up_fused else "unfused"} if layer.gate_up_lora else {}),
-        "launch": "hip_graph" if args.graph else "eager", "weight_copies_rotated": rot, "warmup_steps_run": n_warm,
+        "launch": "hip_graph" if use_graph else "eager", "weight_copies_rotated": rot, "warmup_steps_run": n_warm,
         "active_experts": active,
         "tokens_per_s": cfg.T / (ms / 1e3), "ms_per_step": ms,
         "kernels_ms": {"gate_up": gu_ms, "down": dn_ms, **({"lora_fold": fold_ms} if has_fold else {})},
@@ -447,9 +449,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0,
                     help="independent weight copies cycled through (0: enough for >= 1 GiB of weights, max 4)")
-    ap.add_argument("--graph", action="store_true",
-                    help="time steps replayed from HIP graphs (one captured step per weight copy); the "
-                         "per-kernel figures then come from an eager pass of the same steps")
+    ap.add_argument("--launch", default="auto", choices=["auto", "eager", "graph"],
+                    help="time steps launched eagerly or replayed from HIP graphs (one captured step per weight "
+                         "copy; the per-kernel figures then come from an eager pass of the same steps); auto: "
+                         "graphs for batches of at most 64 tokens, whose steps are launch-bound")
+    ap.add_argument("--graph", action="store_true", help="the same as --launch graph")
     ap.add_argument("--fold", default="auto", choices=["auto", "grouped", "gather"],
                     help="LoRA fold over the sorted rows or slot by slot (auto: by the padding share)")
     ap.add_argument("--down-lora", default="fused", choices=["fused", "unfused"],
