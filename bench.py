@@ -380,7 +380,7 @@ def run_workload(name: str, args, dev) -> dict:
         "gate_up": roofline(gemm_flops(cfg, "gate_up"), gemm_bytes(cfg, "gate_up", active), gu_ms, peak_mfma,
                             gu_what, measured_traffic(cfg.name, "gate_up")),
         "down": roofline(dn_flops, dn_bytes, dn_ms, peak_mfma, dn_what,
-                         None if fused_fold else measured_traffic(cfg.name, "down")),
+                         measured_traffic(cfg.name, "down_fused" if fused_fold else "down")),
     }
     if has_fold:
         mode = layer.fold_mode(b)
