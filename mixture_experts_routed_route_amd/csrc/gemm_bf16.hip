@@ -691,27 +691,28 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
                     __hip_atomic_store(&sk_cnt[L - static_cast<int>(Tw)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        // runs for every segment (nothing added when np == 0), so the accumulators are not merged
-        // from two branches, which costs registers
-        const uint32_t pstride = static_cast<uint32_t>(tail_n) * PART * 4;
+        // only the last piece of a split tile (np > 0, and then its own accumulators are not kept):
+        // the tile is the sum of every piece's partial, in piece order
+        (void)keep;
+        if (np > 0) {
+            const uint32_t pstride = static_cast<uint32_t>(tail_n) * PART * 4;
 #pragma unroll
-        for (int i = 0; i < F::FI; ++i)
+            for (int i = 0; i < F::FI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f32x4 t;
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                        uint32_t o = off;
+                        for (int jp = 0; jp < np; ++jp) {
+                            t += __builtin_amdgcn_raw_buffer_load_b128(part, o, 0, kSc1);
+                            o += pstride;
+                        }
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) t[v] = keep ? acc[i][j][4 * q + v] : 0.f;
-                    uint32_t o = off;
-                    for (int jp = 0; jp < np; ++jp) {
-                        t += __builtin_amdgcn_raw_buffer_load_b128(part, o, 0, kSc1);
-                        o += pstride;
+                        for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] = t[v];
+                        off += F::NT * 16;
                     }
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] = t[v];
-                    off += F::NT * 16;
-                }
+        }
 
         // ---- next segment: its rows (unless prepared in the main loop), sources and first stage,
         // before this segment's epilogue
