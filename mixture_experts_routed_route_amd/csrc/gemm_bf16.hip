@@ -657,8 +657,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
         constexpr int kSc1 = 16;                      // cache policy: device scope
         const bool split = L == tail_L && tail_s > 1;
         bool store = true;
-        bool keep = true;  // the sum starts from acc ...
-        int np = 0;        // ... plus np partials
+        int np = 0;  // partials that make up the tile (the last piece of a split tile only)
         const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
             sk_part, 0, static_cast<int>(gridDim.x) * PART * 4, 0x00020000);
         uint32_t off = 0;  // byte offset of this thread's first 16 bytes in partial 0 to add
@@ -684,16 +683,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_kernel(const Elem<FP8>* 
             __syncthreads();
             store = s_arrived == tail_s - 1;
             if (store) {
-                keep = false;  // the tile is the sum of all pieces' partials, in piece order
                 off = (static_cast<uint32_t>(tail_first) * PART + tid * 4) * 4;
                 np = tail_s;
                 if (tid == 0)
                     __hip_atomic_store(&sk_cnt[L - static_cast<int>(Tw)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        // only the last piece of a split tile (np > 0, and then its own accumulators are not kept):
-        // the tile is the sum of every piece's partial, in piece order
-        (void)keep;
+        // only the last piece of a split tile (np > 0): the tile is the sum of every piece's partial
+        // (its own included, from the workspace), in piece order, not its own accumulators
         if (np > 0) {
             const uint32_t pstride = static_cast<uint32_t>(tail_n) * PART * 4;
 #pragma unroll
