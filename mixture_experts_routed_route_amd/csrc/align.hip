@@ -239,7 +239,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) void route_align_kernel(
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ total_out, int32_t* __restrict__ inv, int max_pad) {
     __shared__ int s_ids[kChunkOne];  // the routed expert ids, handed to the alignment in LDS
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (T <= kFusedWaves) {
+    if (E <= 16 && T > kFusedWaves) {
+        // one token per 16-lane row: the 64 tokens in one pass
+        route_row_token(logits, wave * 4 + (lane >> 4), T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
+    } else if (T <= kFusedWaves) {
         if (wave < T) route_tokens<EPL, 1>(logits, wave, 0, T, E, top_k, renorm, topk_ids, topk_w, lane, s_ids);
     } else {
         // four tokens per wave interleaved; two when each lane holds four logits (registers)

@@ -7,7 +7,8 @@
 // image of the fp32 logit, then a ballot of the lanes that hold it, slot by slot, whose lowest
 // set bit is the lowest expert index (so equal logits pick the lower index).  Selection j is
 // kept by lane j % 64 in its slot j / 64, so top_k may reach E (up to 256).  The weights are
-// computed in fp64 and rounded once to fp32.
+// computed in fp64 and rounded once to fp32.  With at most 16 experts, route_row_token takes one
+// token per 16-lane row instead, with the same results.
 #pragma once
 
 #include "device_common.h"
@@ -160,6 +161,59 @@ __device__ __forceinline__ void route_tokens(const float* __restrict__ logits, i
                 if (lds_ids != nullptr) lds_ids[t * top_k + j] = my_e[n][i];
             }
         }
+    }
+}
+
+// Route one token per 16-lane row (E <= 16): four tokens per wave at once, called by all 64 lanes
+// (row r of the wave takes token t_row; rows with t_row >= T only take part in the cross-lane
+// steps).  Every reduction stays inside the row: DPP row rotations by 1, 2, 4 and 8 leave the
+// row's result in each of its lanes.  The softmax sum is the same sequence of additions as in
+// route_tokens, whose other three rows hold zeros when E <= 16, and the kept weights are summed
+// in slot order as there, so the results are bit-identical to it.
+__device__ __forceinline__ void route_row_token(const float* __restrict__ logits, int t_row, int T, int E,
+                                                int top_k, int renorm, int32_t* __restrict__ ids,
+                                                float* __restrict__ w, int lane, int* lds_ids = nullptr) {
+    const int c = lane & 15, row = lane >> 4;
+    const bool tok = t_row < T;
+    float v = 0.0f;
+    uint32_t key = 0;  // order bits of the logit; 0: not a candidate (taken, past E, or no token)
+    if (tok && c < E) {
+        v = logits[static_cast<size_t>(t_row) * E + c];
+        key = order_bits(v);
+    }
+    int my_e = 0;
+    float my_l = 0.0f, top = 0.0f;
+    for (int j = 0; j < top_k; ++j) {
+        uint32_t best = key;
+        best = max(best, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(best), 0x121, 0xF, 0xF, false)));
+        best = max(best, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(best), 0x122, 0xF, 0xF, false)));
+        best = max(best, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(best), 0x124, 0xF, 0xF, false)));
+        best = max(best, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(best), 0x128, 0xF, 0xF, false)));
+        // the lowest expert of the row holding the largest key (ties: the lower index)
+        const uint64_t hit = __ballot(key == best);
+        const uint32_t rh = static_cast<uint32_t>(hit >> (16 * row)) & 0xffffu;
+        const int e = rh ? __builtin_ctz(rh) : 0;
+        const float l = from_order_bits(best);
+        if (c == e) key = 0;
+        if (j == 0) top = l;
+        if (c == j) { my_e = e; my_l = l; }
+    }
+    // softmax denominator over every expert of the row's token, fp64
+    const double m = static_cast<double>(top);
+    double S = (tok && c < E) ? exp(static_cast<double>(v) - m) : 0.0;
+    S += __builtin_bit_cast(double, row_ror_u64<1>(__builtin_bit_cast(uint64_t, S)));
+    S += __builtin_bit_cast(double, row_ror_u64<2>(__builtin_bit_cast(uint64_t, S)));
+    S += __builtin_bit_cast(double, row_ror_u64<4>(__builtin_bit_cast(uint64_t, S)));
+    S += __builtin_bit_cast(double, row_ror_u64<8>(__builtin_bit_cast(uint64_t, S)));
+    const double p = exp(static_cast<double>(my_l) - m) / S;
+    // the kept probabilities summed in slot order j = 0 .. top_k-1 (lane j of the row holds slot j)
+    double den = 0.0;
+    for (int j = 0; j < top_k; ++j) den += __shfl(p, row * 16 + j);
+    if (tok && c < top_k) {
+        const double wj = renorm ? p / den : p;
+        ids[static_cast<size_t>(t_row) * top_k + c] = my_e;
+        w[static_cast<size_t>(t_row) * top_k + c] = static_cast<float>(wj);
+        if (lds_ids != nullptr) lds_ids[t_row * top_k + c] = my_e;
     }
 }
 

@@ -74,7 +74,19 @@ ROUTE_CASES = [(name, cfg) for name, cfg in CONFIGS.items()] + [
                                       renormalize=False, seed=17)),
     ("E256_k256", MoeConfig("E256k256", T=9, H=8, I=8, E=256, top_k=256, block_size=16, seed=18)),
     ("E128_k65", MoeConfig("E128k65", T=40, H=8, I=8, E=128, top_k=65, block_size=32, seed=19)),
+    # at most 16 experts: one token per 16-lane row, a partial last block of rows
+    ("E16_k4_ties", MoeConfig("E16", T=101, H=8, I=8, E=16, top_k=4, block_size=16, seed=41)),
+    ("E13_k13_no_renorm", MoeConfig("E13", T=35, H=8, I=8, E=13, top_k=13, block_size=16, renormalize=False,
+                                    seed=42)),
+    ("E9_k3", MoeConfig("E9", T=18, H=8, I=8, E=9, top_k=3, block_size=16, seed=43)),
 ]
+
+
+def _plant_ties(logits, E):
+    """Exact ties, all-equal rows and -0.0 logits in the first rows."""
+    logits[:20, min(7, E - 1)] = logits[:20, min(3, E - 1)]
+    logits[20:30] = 0.0
+    logits[30:35, : max(1, E // 2)] = -0.0
 
 
 @pytest.mark.parametrize("name,cfg", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
@@ -85,6 +97,8 @@ def test_route_bit_exact(dev, name, cfg):
         logits[:40, 7] = logits[:40, 3]           # exact ties
         logits[40:60] = 0.0                       # all equal
         logits[60:70, :128] = -0.0
+    elif name.endswith("_ties"):
+        _plant_ties(logits, cfg.E)
     ids_ref, w_ref = oracle.route(logits, cfg.top_k, cfg.renormalize)
     ids, w = ops().moe_route(to_dev(logits), cfg.top_k, cfg.renormalize)
     ids, w = ids.cpu().numpy(), w.cpu().numpy()
@@ -1165,6 +1179,11 @@ ROUTE_ALIGN_CASES = [
     ("T65_two_calls", MoeConfig("t65", T=65, H=8, I=8, E=32, top_k=2, block_size=16, seed=29)),
     ("E256_k96_one_launch", MoeConfig("k96", T=20, H=8, I=8, E=256, top_k=96, block_size=16, seed=30)),
     ("E192_k100_two_calls", MoeConfig("k100", T=30, H=8, I=8, E=192, top_k=100, block_size=16, seed=31)),
+    # at most 16 experts and more than 16 tokens: one token per 16-lane row
+    ("T64_E16_ties", MoeConfig("t64e16", T=64, H=8, I=8, E=16, top_k=4, block_size=16, seed=32)),
+    ("T17_E16", MoeConfig("t17e16", T=17, H=8, I=8, E=16, top_k=2, block_size=16, seed=33)),
+    ("T50_E9_k9_no_renorm", MoeConfig("t50e9", T=50, H=8, I=8, E=9, top_k=9, block_size=32, renormalize=False,
+                                      seed=34)),
 ]
 
 
@@ -1176,6 +1195,8 @@ def test_route_align_matches_oracle(dev, name, cfg):
     note(f"route_align {name} T={cfg.T} E={cfg.E} k={cfg.top_k} P={cfg.P}")
     m = ops()
     logits = make_router_logits(cfg)
+    if name.endswith("_ties"):
+        _plant_ties(logits, cfg.E)
     ids_ref, w_ref = oracle.route(logits, cfg.top_k, cfg.renormalize)
     ref = oracle.align(ids_ref, cfg.E, cfg.block_size)
     ids = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
