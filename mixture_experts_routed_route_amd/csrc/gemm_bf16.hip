@@ -60,6 +60,12 @@
 // same k.  Its 32-byte fragments do not fit twice beside the accumulators of an 8-wave tile, so
 // there a wave reads each k-step's fragments just before its MFMAs.  The epilogue multiplies by
 // the row's activation scale and the column's weight scale before SiLU * up.
+//
+// LoRA epilogue (LORA > 0; atlas moe_lora_grouped.rs): before the stores, rows of adapted experts
+// get bf16(bf16(acc) + scale * bf16(xa . B_e^T)), from the shrink's xa rows (by sorted row) and the
+// adapter's B_e.  Gate/up folds the gate and up blocks with their own tables before SiLU * up;
+// down folds the expert output.  The one-adapter down form at rank BK runs the delta as one more
+// K stage through the last stage's LDS buffer; the other forms fetch the fragments from memory.
 #include <type_traits>
 
 #include "device_common.h"
